@@ -1,0 +1,205 @@
+/*
+ * sla.h -- C ABI of the sparse-linear attention forward library (libsla.so).
+ *
+ * What is computed (one attention head at a time, every head independent):
+ *
+ *   route          Q and K are mean-pooled over blocks of 64 consecutive
+ *                  tokens; the block logits s_ij = qbar_i . kbar_j / sqrt(d)
+ *                  are ranked per query block i (descending, equal logits by
+ *                  ascending j); the first k_crit KV blocks are critical, the
+ *                  next k_marg marginal, the rest negligible.
+ *                  [SLA2 technical summary, section 2.B (router on pooled Q
+ *                  and K, hard top-k at inference); SLA abstract (critical /
+ *                  marginal / negligible classes)]
+ *   linear states  per KV block j: H_j = phi(K_j)^T V_j (d x d) and
+ *                  z_j = sum over the block's tokens of phi(k), phi = softmax
+ *                  over the d features.
+ *                  [PISA technical summary, "Algoritmo Central" (per-block
+ *                  first-order matrices); SPLA technical summary, section 2.2
+ *                  (compact linear-attention state of unselected blocks)]
+ *   forward        O_s = softmax attention of each query over the tokens of
+ *                  its query block's critical KV blocks only (renormalised
+ *                  over those keys); O_l = phi(q) (sum_{j marginal} H_j) /
+ *                  (phi(q) . sum_{j marginal} z_j); negligible blocks are
+ *                  skipped; O = alpha_h O_s + (1 - alpha_h) O_l.
+ *                  [SLA abstract (O(N^2) on critical, O(N) on marginal,
+ *                  skip negligible, one fused kernel); SLA2 technical
+ *                  summary, section 1 item 1 (renormalised sparse softmax)
+ *                  and section 2.A (the alpha mixing equation)]
+ *   fp8 variant    the sparse branch with Q, K, V quantised per 64-token
+ *                  block to OCP E4M3 with a float32 scale, QK^T and PV on
+ *                  fp8 matrix cores.
+ *                  [SLA2 technical summary, section 2.C (low-bit sparse
+ *                  branch)]
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every function returns an int status: SLA_OK (0) or a negative
+ *   sla_status.  On error a thread-local message is available from
+ *   sla_last_error_message().  No function throws or aborts.
+ * - Device pointers are HIP device addresses on the current device; host
+ *   pointers are marked "host".  The caller owns and allocates every buffer
+ *   (outputs and workspace included); the library allocates no device
+ *   memory and keeps no per-call state.
+ * - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *   All work is enqueued on it asynchronously; the library never
+ *   synchronises.  A returned SLA_OK covers argument validation and kernel
+ *   launch; faults inside a kernel surface at the caller's next sync.
+ * - Q, K, V and O share the problem's element strides (stride_d == 1):
+ *   element (b, h, n, c) is at b*stride_b + h*stride_h + n*stride_n + c.
+ *   Their base pointers must be 16-byte aligned and stride_n * elem_size a
+ *   multiple of 16.  O has the input dtype.
+ * - Every other array is dense row-major in the shape given, owned by the
+ *   caller: index lists int32, class map int8, states bf16 / float32.
+ * - Functions are reentrant; concurrent calls on different streams with
+ *   disjoint outputs and workspaces are safe.
+ * - The library only runs on gfx950 (MI355X); on any other device, or with
+ *   no device, compute entry points return SLA_ERR_NO_DEVICE after argument
+ *   validation.
+ */
+#ifndef SLA_H_
+#define SLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SLA_VERSION_MAJOR 0
+#define SLA_VERSION_MINOR 1
+#define SLA_VERSION_PATCH 0
+
+/* Status codes. */
+typedef enum sla_status {
+  SLA_OK = 0,
+  SLA_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad count, misalignment  */
+  SLA_ERR_UNSUPPORTED = -2,      /* valid but not implemented: d, block, dtype, size */
+  SLA_ERR_WORKSPACE = -3,        /* workspace pointer null or too small     */
+  SLA_ERR_DEVICE = -4,           /* a HIP call or kernel launch failed      */
+  SLA_ERR_NO_DEVICE = -5         /* no HIP device, or it is not gfx950      */
+} sla_status;
+
+/* Element type of Q, K, V and O. */
+typedef enum sla_dtype { SLA_F32 = 0, SLA_BF16 = 1 } sla_dtype;
+
+/* Operation selector for sla_workspace_size. */
+typedef enum sla_op {
+  SLA_OP_ROUTE = 0,
+  SLA_OP_LINEAR_STATES = 1,
+  SLA_OP_FORWARD = 2,
+  SLA_OP_QUANTIZE_FP8 = 3,
+  SLA_OP_FORWARD_FP8 = 4
+} sla_op;
+
+/* Problem description (host struct, read only during the call).
+ * batch, heads, seq_len >= 1; head_dim in {64, 128}; block == 64;
+ * k_crit >= 0, k_marg >= 0, 1 <= k_crit + k_marg <= nkb where
+ * nkb = ceil(seq_len / 64); dtype is an sla_dtype; strides are in elements. */
+typedef struct sla_problem {
+  int32_t batch, heads, seq_len, head_dim;
+  int32_t block;
+  int32_t k_crit, k_marg;
+  int32_t dtype;
+  int64_t stride_b, stride_h, stride_n;
+} sla_problem;
+
+/* Host-only checks of a problem (no HIP call).  SLA_OK,
+ * SLA_ERR_INVALID_ARGUMENT (null, sizes < 1, bad counts, strides that
+ * overlap rows) or SLA_ERR_UNSUPPORTED (head_dim, block, dtype, or more than
+ * 4096 KV blocks). */
+int sla_validate(const sla_problem* problem);
+
+/* Host: number of query blocks and KV blocks (both ceil(seq_len / 64)). */
+int sla_num_blocks(const sla_problem* problem, int32_t* nq, int32_t* nkb);
+
+/* Host: bytes of device workspace the operation needs (0 if none).  The
+ * workspace passed to a call must be at least this large and 256-byte
+ * aligned.  SLA_OP_FORWARD needs a bf16 [B,H,nq,d,d] marginal-state sum
+ * plus a float32 [B,H,nq,d] normaliser sum; SLA_OP_ROUTE needs float64
+ * pooled Q and K. */
+int sla_workspace_size(const sla_problem* problem, int op, size_t* bytes);
+
+/* Block routing.  [SLA2 summary 2.B; SLA abstract]
+ * q, k         input [B,H,N,d] (problem strides, problem dtype)
+ * crit_idx     out int32 [B,H,nq,k_crit], ascending KV block indices
+ * marg_idx     out int32 [B,H,nq,k_marg], ascending
+ * block_class  out int8  [B,H,nq,nkb] or NULL: 0 negligible, 1 marginal,
+ *              2 critical
+ * block_logits out float [B,H,nq,nkb] or NULL: s_ij rounded to float32
+ * pooled_q,
+ * pooled_k     out float [B,H,nb,d] or NULL: block means rounded to float32
+ * ws           workspace of sla_workspace_size(SLA_OP_ROUTE) bytes.
+ * Pooling and logits are evaluated in float64, so the ranking follows the
+ * exact block means up to summation order. */
+int sla_route(const sla_problem* problem, const void* q, const void* k,
+              int32_t* crit_idx, int32_t* marg_idx, int8_t* block_class,
+              float* block_logits, float* pooled_q, float* pooled_k, void* ws,
+              size_t ws_bytes, void* stream);
+
+/* Per-block linear-attention states.  [PISA summary; SPLA summary 2.2]
+ * k, v      input [B,H,N,d]
+ * h_states  out bf16 [B,H,nkb,d,d]: H_j[a][c] = sum_n phi(k_n)[a] v_n[c]
+ * z_states  out float [B,H,nkb,d]: z_j[a] = sum_n phi(k_n)[a]
+ * A short last block sums its valid tokens only.  phi is evaluated in
+ * float32, H is accumulated in float32 from bf16 operands. */
+int sla_linear_states(const sla_problem* problem, const void* k, const void* v,
+                      void* h_states, float* z_states, void* stream);
+
+/* Fused sparse + linear forward.  [SLA abstract; SLA2 summary 1 and 2.A]
+ * q, k, v    input [B,H,N,d]
+ * crit_idx,
+ * marg_idx   as written by sla_route (any ascending lists with valid,
+ *            distinct indices are accepted)
+ * h_states,
+ * z_states   as written by sla_linear_states
+ * alpha      float [H] mixing weight per head
+ * o          out [B,H,N,d], problem dtype
+ * o_sparse,
+ * o_linear   out float [B,H,N,d] contiguous, or NULL (branch outputs)
+ * ws         workspace of sla_workspace_size(SLA_OP_FORWARD) bytes.
+ * A query block with k_crit == 0 has O_s = 0; with k_marg == 0, O_l = 0. */
+int sla_forward(const sla_problem* problem, const void* q, const void* k,
+                const void* v, const int32_t* crit_idx, const int32_t* marg_idx,
+                const void* h_states, const float* z_states, const float* alpha,
+                void* o, float* o_sparse, float* o_linear, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* Per-block E4M3 quantiser.  [SLA2 summary 2.C]
+ * x        input [B,H,N,d] (problem strides and dtype)
+ * x_e4m3   out uint8 [B,H,N,d] contiguous OCP E4M3 codes
+ * scales   out float [B,H,nb]: scale_j = absmax_j / 448 (1 if absmax_j = 0)
+ * code = e4m3_rne_saturate(fl32(x * fl32(448 / absmax_j))). */
+int sla_quantize_fp8(const sla_problem* problem, const void* x, uint8_t* x_e4m3,
+                     float* scales, void* stream);
+
+/* Forward with the fp8 sparse branch.  [SLA2 summary 2.C]
+ * q          bf16/f32 input [B,H,N,d] (phi(Q) of the linear branch)
+ * q8,k8,v8   uint8 [B,H,N,d] contiguous codes from sla_quantize_fp8
+ * q_s,k_s,v_s float [B,H,nb] their scales
+ * the remaining arguments as for sla_forward.  P is quantised per query
+ * row of each KV tile with scale rowmax/448 before the PV product. */
+int sla_forward_fp8(const sla_problem* problem, const void* q,
+                    const uint8_t* q8, const float* q_s, const uint8_t* k8,
+                    const float* k_s, const uint8_t* v8, const float* v_s,
+                    const int32_t* crit_idx, const int32_t* marg_idx,
+                    const void* h_states, const float* z_states,
+                    const float* alpha, void* o, float* o_sparse,
+                    float* o_linear, void* ws, size_t ws_bytes, void* stream);
+
+/* Host: static text of a status code. */
+const char* sla_status_string(int status);
+
+/* Host: thread-local detail of the last error raised on this thread
+ * ("" if none). */
+const char* sla_last_error_message(void);
+
+/* Host: library version (host pointers). */
+int sla_version(int* major, int* minor, int* patch);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA_H_ */

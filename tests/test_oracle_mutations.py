@@ -1,0 +1,89 @@
+"""The oracle's pins have teeth: plant a plausible mistake in the oracle and
+check that the pin meant to catch it fails (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import sla
+import tests.test_oracle_pins as pins
+
+
+def _fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_pool_dividing_by_full_block(monkeypatch):
+    def bad(x, block=64):
+        n, d = x.shape
+        out = np.empty((sla.n_blocks(n, block), d))
+        for j, (a, b) in enumerate(sla.block_ranges(n, block)):
+            out[j] = x[a:b].sum(0) / block
+        return out
+    monkeypatch.setattr(sla, "pool", bad)
+    _fails(pins.test_pool_tail_divides_by_valid_count)
+
+
+def test_logits_without_scale(monkeypatch):
+    monkeypatch.setattr(sla, "block_logits", lambda qp, kp: qp @ kp.T)
+    _fails(pins.test_logits_brute_force)
+
+
+def test_ties_to_higher_index(monkeypatch):
+    orig = sla.select
+
+    def bad(logits, kc, km):
+        flipped = logits[:, ::-1]
+        c, m, cls = orig(flipped, kc, km)
+        nkb = logits.shape[1]
+        return np.sort(nkb - 1 - c, 1), np.sort(nkb - 1 - m, 1), cls[:, ::-1]
+    monkeypatch.setattr(sla, "select", bad)
+    _fails(pins.test_select_matches_brute_force, 3, 5, True)
+
+
+def test_sparse_without_scale(monkeypatch):
+    def bad(q, k, v, crit_idx, block=64, q_blocks=None):
+        return sla.__dict__["_orig_sparse"](q * math.sqrt(q.shape[1]), k, v, crit_idx, block, q_blocks)
+    sla.__dict__["_orig_sparse"] = sla.sparse_branch
+    monkeypatch.setattr(sla, "sparse_branch", bad)
+    try:
+        _fails(pins.test_all_critical_is_dense_attention, 200)
+    finally:
+        del sla.__dict__["_orig_sparse"]
+
+
+def test_phi_over_tokens(monkeypatch):
+    def bad(x):
+        e = np.exp(x - x.max(axis=0, keepdims=True))
+        return e / e.sum(axis=0, keepdims=True)
+    monkeypatch.setattr(sla, "phi", bad)
+    _fails(pins.test_phi_is_feature_softmax)
+    _fails(pins.test_states_invariants, 150)
+
+
+def test_transposed_states(monkeypatch):
+    orig = sla.linear_states
+
+    def bad(k, v, block=64):
+        H, z = orig(k, v, block)
+        return np.transpose(H, (0, 2, 1)).copy(), z
+    monkeypatch.setattr(sla, "linear_states", bad)
+    _fails(pins.test_states_invariants, 192)
+
+
+def test_linear_without_denominator(monkeypatch):
+    def bad(q, H, z, marg_idx, block=64, q_blocks=None):
+        out = np.zeros((q.shape[0], H.shape[2]))
+        fq = sla.phi(q)
+        for i, (a, b) in enumerate(sla.block_ranges(q.shape[0], block)):
+            if len(marg_idx[i]):
+                out[a:b] = fq[a:b] @ H[marg_idx[i]].sum(0)
+        return out
+    monkeypatch.setattr(sla, "linear_branch", bad)
+    _fails(pins.test_all_marginal_is_closed_form_linear_attention, 256)
+
+
+def test_mix_swapped(monkeypatch):
+    monkeypatch.setattr(sla, "mix", lambda o_s, o_l, a: (1 - a) * o_s + a * o_l)
+    _fails(pins.test_mix_endpoints_and_affinity)
