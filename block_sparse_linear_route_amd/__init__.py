@@ -1,0 +1,19 @@
+"""Sparse-linear attention forward for MI355X (gfx950).
+
+The computation lives in ``lib/libsla.so`` (hand-written HIP kernels behind
+the C ABI declared in ``include/sla.h``); this package is its thin Python
+binding.  Importing it fails if the library has not been built.
+"""
+from .ops import (  # noqa: F401
+    SlaError,
+    forward,
+    forward_fp8,
+    linear_states,
+    make_problem,
+    num_blocks,
+    quantize_fp8,
+    route,
+    sla_attention,
+    version,
+    workspace_size,
+)

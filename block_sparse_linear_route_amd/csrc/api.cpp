@@ -1,0 +1,338 @@
+// C ABI of libsla: argument validation, workspace sizing, device checks and
+// kernel dispatch.  Declarations and the contract live in include/sla.h.
+#include "sla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "sla_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+constexpr int kMaxKvBlocks = 4096;
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int validate_problem(const sla_problem* p) {
+  if (!p) return fail(SLA_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->batch < 1 || p->heads < 1 || p->seq_len < 1)
+    return fail(SLA_ERR_INVALID_ARGUMENT, "batch, heads and seq_len must be >= 1 (got %d, %d, %d)",
+                p->batch, p->heads, p->seq_len);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(SLA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", p->head_dim);
+  if (p->block != 64) return fail(SLA_ERR_UNSUPPORTED, "block %d unsupported (64)", p->block);
+  if (p->dtype != SLA_F32 && p->dtype != SLA_BF16)
+    return fail(SLA_ERR_UNSUPPORTED, "dtype %d unsupported", p->dtype);
+  const int64_t nkb = (static_cast<int64_t>(p->seq_len) + 63) / 64;
+  if (nkb > kMaxKvBlocks)
+    return fail(SLA_ERR_UNSUPPORTED, "%lld KV blocks exceed the supported %d",
+                static_cast<long long>(nkb), kMaxKvBlocks);
+  if (p->k_crit < 0 || p->k_marg < 0)
+    return fail(SLA_ERR_INVALID_ARGUMENT, "k_crit and k_marg must be >= 0");
+  const int64_t sum = static_cast<int64_t>(p->k_crit) + p->k_marg;
+  if (sum < 1 || sum > nkb)
+    return fail(SLA_ERR_INVALID_ARGUMENT, "need 1 <= k_crit + k_marg <= nkb (%lld), got %lld",
+                static_cast<long long>(nkb), static_cast<long long>(sum));
+  if (p->stride_b < 0 || p->stride_h < 0 || p->stride_n < p->head_dim)
+    return fail(SLA_ERR_INVALID_ARGUMENT, "strides must be >= 0 and stride_n >= head_dim");
+  const int64_t esz = p->dtype == SLA_BF16 ? 2 : 4;
+  if ((p->stride_n * esz) % 16 || (p->stride_h * esz) % 16 || (p->stride_b * esz) % 16)
+    return fail(SLA_ERR_INVALID_ARGUMENT, "strides must be multiples of 16 bytes");
+  const int64_t nq_total = static_cast<int64_t>(p->batch) * p->heads * nkb;
+  if (nq_total > (1ll << 31) - 1)
+    return fail(SLA_ERR_UNSUPPORTED, "batch * heads * blocks exceeds the grid limit");
+  return SLA_OK;
+}
+
+sla::Geometry geometry(const sla_problem* p) {
+  sla::Geometry g;
+  g.B = p->batch;
+  g.H = p->heads;
+  g.N = p->seq_len;
+  g.D = p->head_dim;
+  g.nq = g.nkb = (p->seq_len + 63) / 64;
+  g.k_crit = p->k_crit;
+  g.k_marg = p->k_marg;
+  g.dtype = p->dtype;
+  g.sb = p->stride_b;
+  g.sh = p->stride_h;
+  g.sn = p->stride_n;
+  return g;
+}
+
+// -1 unknown, 0 not gfx950, 1 gfx950; indexed by device id.
+std::atomic<int> g_dev_ok[64];
+std::atomic<bool> g_dev_init{false};
+
+int check_device() {
+  if (!g_dev_init.load(std::memory_order_acquire)) {
+    for (auto& x : g_dev_ok) x.store(-1, std::memory_order_relaxed);
+    g_dev_init.store(true, std::memory_order_release);
+  }
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
+    (void)hipGetLastError();
+    return fail(SLA_ERR_NO_DEVICE, "no HIP device available");
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SLA_ERR_NO_DEVICE, "hipGetDevice failed");
+  }
+  if (dev < 0 || dev >= 64) return fail(SLA_ERR_NO_DEVICE, "device id %d out of range", dev);
+  int ok = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (ok < 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(SLA_ERR_NO_DEVICE, "hipGetDeviceProperties failed");
+    }
+    ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    g_dev_ok[dev].store(ok, std::memory_order_relaxed);
+  }
+  if (!ok) return fail(SLA_ERR_NO_DEVICE, "device %d is not gfx950", dev);
+  return SLA_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SLA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return SLA_OK;
+}
+
+#define SLA_TRY(x)                 \
+  do {                             \
+    const int _st = (x);           \
+    if (_st != SLA_OK) return _st; \
+  } while (0)
+
+#define SLA_REQ(ptr, align)                                                              \
+  do {                                                                                   \
+    if (!(ptr)) return fail(SLA_ERR_INVALID_ARGUMENT, "%s is NULL", #ptr);               \
+    if (!aligned((ptr), (align)))                                                        \
+      return fail(SLA_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", #ptr, (align)); \
+  } while (0)
+
+#define SLA_OPT(ptr, align)                                                              \
+  do {                                                                                   \
+    if ((ptr) && !aligned((ptr), (align)))                                               \
+      return fail(SLA_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", #ptr, (align)); \
+  } while (0)
+
+size_t forward_ws(const sla::Geometry& g) {
+  const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
+  return align_up(rows * g.D * g.D * 2) + align_up(rows * g.D * 4);
+}
+
+size_t route_ws(const sla::Geometry& g) {
+  const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
+  return 2 * align_up(rows * g.D * 8);
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return SLA_OK;
+  if (!ws) return fail(SLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(ws, kWsAlign)) return fail(SLA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+  return SLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sla_validate(const sla_problem* problem) {
+  const int st = validate_problem(problem);
+  if (st == SLA_OK) g_last_error.clear();
+  return st;
+}
+
+int sla_num_blocks(const sla_problem* problem, int32_t* nq, int32_t* nkb) {
+  SLA_TRY(validate_problem(problem));
+  if (!nq || !nkb) return fail(SLA_ERR_INVALID_ARGUMENT, "output pointers are NULL");
+  *nq = *nkb = (problem->seq_len + 63) / 64;
+  return SLA_OK;
+}
+
+int sla_workspace_size(const sla_problem* problem, int op, size_t* bytes) {
+  SLA_TRY(validate_problem(problem));
+  if (!bytes) return fail(SLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  const sla::Geometry g = geometry(problem);
+  switch (op) {
+    case SLA_OP_ROUTE: *bytes = route_ws(g); return SLA_OK;
+    case SLA_OP_LINEAR_STATES: *bytes = 0; return SLA_OK;
+    case SLA_OP_FORWARD: *bytes = forward_ws(g); return SLA_OK;
+    case SLA_OP_QUANTIZE_FP8: *bytes = 0; return SLA_OK;
+    case SLA_OP_FORWARD_FP8: *bytes = forward_ws(g); return SLA_OK;
+    default: return fail(SLA_ERR_INVALID_ARGUMENT, "unknown op %d", op);
+  }
+}
+
+int sla_route(const sla_problem* problem, const void* q, const void* k, int32_t* crit_idx,
+              int32_t* marg_idx, int8_t* block_class, float* block_logits, float* pooled_q,
+              float* pooled_k, void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(q, 16);
+  SLA_REQ(k, 16);
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  if (problem->k_marg > 0) SLA_REQ(marg_idx, 4);
+  SLA_OPT(block_logits, 4);
+  SLA_OPT(pooled_q, 4);
+  SLA_OPT(pooled_k, 4);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, route_ws(g)));
+  SLA_TRY(check_device());
+  double* qpool = static_cast<double*>(ws);
+  double* kpool_t = reinterpret_cast<double*>(static_cast<char*>(ws) + route_ws(g) / 2);
+  return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
+                                    pooled_q, pooled_k, qpool, kpool_t,
+                                    static_cast<hipStream_t>(stream)),
+                  "sla_route launch");
+}
+
+int sla_linear_states(const sla_problem* problem, const void* k, const void* v, void* h_states,
+                      float* z_states, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(k, 16);
+  SLA_REQ(v, 16);
+  SLA_REQ(h_states, 16);
+  SLA_REQ(z_states, 16);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_device());
+  return launched(sla::launch_states(g, k, v, static_cast<uint16_t*>(h_states), z_states,
+                                     static_cast<hipStream_t>(stream)),
+                  "sla_linear_states launch");
+}
+
+int sla_forward(const sla_problem* problem, const void* q, const void* k, const void* v,
+                const int32_t* crit_idx, const int32_t* marg_idx, const void* h_states,
+                const float* z_states, const float* alpha, void* o, float* o_sparse,
+                float* o_linear, void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(q, 16);
+  SLA_REQ(k, 16);
+  SLA_REQ(v, 16);
+  SLA_REQ(alpha, 4);
+  SLA_REQ(o, 16);
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  if (problem->k_marg > 0) {
+    SLA_REQ(marg_idx, 4);
+    SLA_REQ(h_states, 16);
+    SLA_REQ(z_states, 16);
+  }
+  SLA_OPT(o_sparse, 16);
+  SLA_OPT(o_linear, 16);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, forward_ws(g)));
+  SLA_TRY(check_device());
+  const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
+  uint16_t* s_sum = static_cast<uint16_t*>(ws);
+  float* sigma = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(rows * g.D * g.D * 2));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.k_marg > 0)
+    SLA_TRY(launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
+                                               z_states, s_sum, sigma, s),
+                     "marginal-sum launch"));
+  return launched(sla::launch_attention(g, q, k, v, crit_idx, s_sum, sigma, alpha, o, o_sparse,
+                                        o_linear, s),
+                  "attention launch");
+}
+
+int sla_quantize_fp8(const sla_problem* problem, const void* x, uint8_t* x_e4m3, float* scales,
+                     void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(x, 16);
+  SLA_REQ(x_e4m3, 16);
+  SLA_REQ(scales, 4);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_device());
+  return launched(sla::launch_quantize_fp8(g, x, x_e4m3, scales, static_cast<hipStream_t>(stream)),
+                  "sla_quantize_fp8 launch");
+}
+
+int sla_forward_fp8(const sla_problem* problem, const void* q, const uint8_t* q8, const float* q_s,
+                    const uint8_t* k8, const float* k_s, const uint8_t* v8, const float* v_s,
+                    const int32_t* crit_idx, const int32_t* marg_idx, const void* h_states,
+                    const float* z_states, const float* alpha, void* o, float* o_sparse,
+                    float* o_linear, void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  if (problem->dtype != SLA_BF16)
+    return fail(SLA_ERR_UNSUPPORTED, "the fp8 forward takes bf16 Q and O");
+  if (problem->head_dim != 128)
+    return fail(SLA_ERR_UNSUPPORTED, "the fp8 forward supports head_dim 128");
+  SLA_REQ(q, 16);
+  SLA_REQ(q8, 16);
+  SLA_REQ(k8, 16);
+  SLA_REQ(v8, 16);
+  SLA_REQ(q_s, 4);
+  SLA_REQ(k_s, 4);
+  SLA_REQ(v_s, 4);
+  SLA_REQ(alpha, 4);
+  SLA_REQ(o, 16);
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  if (problem->k_marg > 0) {
+    SLA_REQ(marg_idx, 4);
+    SLA_REQ(h_states, 16);
+    SLA_REQ(z_states, 16);
+  }
+  SLA_OPT(o_sparse, 16);
+  SLA_OPT(o_linear, 16);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, forward_ws(g)));
+  SLA_TRY(check_device());
+  const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
+  uint16_t* s_sum = static_cast<uint16_t*>(ws);
+  float* sigma = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(rows * g.D * g.D * 2));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.k_marg > 0)
+    SLA_TRY(launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
+                                               z_states, s_sum, sigma, s),
+                     "marginal-sum launch"));
+  return launched(sla::launch_attention_fp8(g, q, q8, q_s, k8, k_s, v8, v_s, crit_idx, s_sum,
+                                            sigma, alpha, o, o_sparse, o_linear, s),
+                  "fp8 attention launch");
+}
+
+const char* sla_status_string(int status) {
+  switch (status) {
+    case SLA_OK: return "ok";
+    case SLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SLA_ERR_UNSUPPORTED: return "unsupported";
+    case SLA_ERR_WORKSPACE: return "workspace too small";
+    case SLA_ERR_DEVICE: return "device error";
+    case SLA_ERR_NO_DEVICE: return "no gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+const char* sla_last_error_message(void) { return g_last_error.c_str(); }
+
+int sla_version(int* major, int* minor, int* patch) {
+  if (!major || !minor || !patch) return fail(SLA_ERR_INVALID_ARGUMENT, "NULL output pointer");
+  *major = SLA_VERSION_MAJOR;
+  *minor = SLA_VERSION_MINOR;
+  *patch = SLA_VERSION_PATCH;
+  return SLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+// Device-side helpers shared by the gfx950 kernels of libsla.
+//
+// Conventions used by every kernel:
+//  * 256-thread workgroups = 4 waves of 64 lanes (CDNA wavefront).
+//  * bf16 tensors are carried as raw uint16_t bit patterns in memory and as
+//    __bf16 vectors in registers for the matrix-core builtins.
+//  * Matrix-core tiles use v_mfma_f32_32x32x16_bf16: lane l holds row/column
+//    (l % 32) of an A/B operand and 8 consecutive k-slots chosen by (l / 32);
+//    the 32x32 float accumulator gives lane l column (l % 32) and rows
+//    8*(r/4) + 4*(l/32) + (r%4) for its 16 registers r.  A and B operands use
+//    the same k-slot mapping, so any assignment of k indices to slots that is
+//    applied identically to both operands yields the full dot product.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kBlock = 64;
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 (the gfx950 conversion instruction).
+__device__ __forceinline__ __bf16 f32_to_bf16(float f) { return static_cast<__bf16>(f); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float bf16v_to_f32(__bf16 h) {
+  return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h)) << 16);
+}
+
+// 8 consecutive elements as a bf16 vector (pointer 16-byte aligned for bf16,
+// 32-byte aligned for float).
+__device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ bf16x8 load8(const float* p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  bf16x8 r;
+  r[0] = f32_to_bf16(a[0]); r[1] = f32_to_bf16(a[1]);
+  r[2] = f32_to_bf16(a[2]); r[3] = f32_to_bf16(a[3]);
+  r[4] = f32_to_bf16(b[0]); r[5] = f32_to_bf16(b[1]);
+  r[6] = f32_to_bf16(b[2]); r[7] = f32_to_bf16(b[3]);
+  return r;
+}
+
+// 8 consecutive elements widened to float.
+__device__ __forceinline__ void load8_f32(const uint16_t* p, float* out) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8_f32(const float* p, float* out) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { out[i] = a[i]; out[4 + i] = b[i]; }
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = f32_to_bf16(0.0f);
+  return r;
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = 0.0f;
+  return r;
+}
+
+// Lane-crossing helpers (wave64).
+__device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Workgroup id remapped so that each XCD (the hardware dispatches workgroups
+// round-robin over 8 XCDs) owns one contiguous range of logical work items,
+// which keeps neighbouring query blocks of one head in the same L2.
+__device__ __forceinline__ int xcd_remap(int wg, int n) {
+  constexpr int kXcd = 8;
+  const int xcd = wg % kXcd;
+  const int idx = wg / kXcd;
+  const int per = n / kXcd;
+  const int rem = n % kXcd;
+  return (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+}  // namespace sla

@@ -1,0 +1,49 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel
+// translation units.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sla {
+
+// Validated problem geometry (all sizes checked by the API layer).
+struct Geometry {
+  int B, H, N, D;        // batch, heads, tokens, head dim
+  int nq, nkb;           // query blocks, KV blocks (both ceil(N / 64))
+  int k_crit, k_marg;    // critical / marginal blocks per query block
+  int dtype;             // 0 = float32, 1 = bfloat16 (Q, K, V, O)
+  int64_t sb, sh, sn;    // element strides of Q, K, V, O
+};
+
+hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t* crit,
+                        int32_t* marg, int8_t* cls, float* logits, float* pooled_q,
+                        float* pooled_k, double* ws_qpool, double* ws_kpool_t,
+                        hipStream_t stream);
+
+hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16_t* h_states,
+                         float* z_states, hipStream_t stream);
+
+// Marginal-state sums S_i = sum_{j in M_i} H_j (bf16, [B,H,nq,d,d]) and
+// sigma_i = sum_{j in M_i} z_j (float, [B,H,nq,d]).
+hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const uint16_t* h_states,
+                                const float* z_states, uint16_t* s_sum, float* sigma_sum,
+                                hipStream_t stream);
+
+hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,
+                            const int32_t* crit, const uint16_t* s_sum, const float* sigma_sum,
+                            const float* alpha, void* o, float* o_sparse, float* o_linear,
+                            hipStream_t stream);
+
+hipError_t launch_quantize_fp8(const Geometry& g, const void* x, uint8_t* codes, float* scales,
+                               hipStream_t stream);
+
+hipError_t launch_attention_fp8(const Geometry& g, const void* q, const uint8_t* q8,
+                                const float* q_s, const uint8_t* k8, const float* k_s,
+                                const uint8_t* v8, const float* v_s, const int32_t* crit,
+                                const uint16_t* s_sum, const float* sigma_sum,
+                                const float* alpha, void* o, float* o_sparse, float* o_linear,
+                                hipStream_t stream);
+
+}  // namespace sla

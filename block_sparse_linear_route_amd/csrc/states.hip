@@ -1,0 +1,214 @@
+// Per-block linear-attention states.
+//
+// [PISA technical summary, "Algoritmo Central"] each KV block j has a
+// first-order matrix built from its keys and values; [SPLA technical
+// summary, section 2.2] blocks outside the exact set are compressed into a
+// compact linear-attention state.  Here:
+//   H_j = phi(K_j)^T V_j   (d x d, bf16 out, float32 accumulation)
+//   z_j = sum over the block's tokens of phi(k)   (d, float32)
+// with phi = softmax over the d features, evaluated in float32.
+//
+// One workgroup per (b, h, j): the 64 x d tiles of K and V are read once
+// (coalesced 16-byte loads), phi(K)^T and V^T are staged token-contiguous in
+// LDS as bf16, and the d x d product runs on v_mfma_f32_32x32x16_bf16 with
+// the 64 tokens as the contraction dimension.  The kernel is HBM-bound: it
+// reads 2*64*d and writes d*d elements per block.
+#include "device_common.hpp"
+#include "sla_internal.hpp"
+
+namespace sla {
+namespace {
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads)
+states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
+              uint16_t* __restrict__ h_out, float* __restrict__ z_out) {
+  constexpr int TS = kBlock + 8;        // token stride of the transposed tiles
+  constexpr int HS = D + 8;             // row stride of the staged output tile
+  constexpr int CW = D / 4;             // features per thread (4 threads per token)
+  constexpr int TA = D / 32;            // 32-row tiles per dimension
+  constexpr int NT = TA * TA / 4;       // output tiles per wave
+  constexpr int SMEM = (2 * D * TS > D * HS) ? 2 * D * TS : D * HS;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
+  __shared__ float zpart[4][D];
+  uint16_t* phi_t = smem;               // [D][TS]: phi(K)^T
+  uint16_t* v_t = smem + D * TS;        // [D][TS]: V^T
+
+  const int j = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / g.H, h = bh % g.H;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int row = t >> 2, part = t & 3;
+  const int nj = min(kBlock, g.N - j * kBlock);
+  const bool valid = row < nj;
+  const int64_t off = b * g.sb + h * g.sh + static_cast<int64_t>(j * kBlock + row) * g.sn + part * CW;
+
+  float kv[CW], vv[CW];
+#pragma unroll
+  for (int c = 0; c < CW / 8; ++c) {
+    if (valid) {
+      load8_f32(k + off + 8 * c, kv + 8 * c);
+      load8_f32(v + off + 8 * c, vv + 8 * c);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { kv[8 * c + e] = 0.0f; vv[8 * c + e] = 0.0f; }
+    }
+  }
+
+  // phi(k) = softmax over the d features of the token (4 lanes per token).
+  float mx = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < CW; ++c) mx = fmaxf(mx, kv[c]);
+  mx = fmaxf(mx, xor_lane(mx, 1));
+  mx = fmaxf(mx, xor_lane(mx, 2));
+  float sum = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    kv[c] = expf(kv[c] - mx);
+    sum += kv[c];
+  }
+  sum += xor_lane(sum, 1);
+  sum += xor_lane(sum, 2);
+#pragma unroll
+  for (int c = 0; c < CW; ++c) kv[c] = valid ? kv[c] / sum : 0.0f;
+
+  // z: column sums over the wave's 16 tokens, then over the 4 waves.
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    float zc = kv[c];
+    zc += xor_lane(zc, 4);
+    zc += xor_lane(zc, 8);
+    zc += xor_lane(zc, 16);
+    zc += xor_lane(zc, 32);
+    if (lane < 4) zpart[wave][part * CW + c] = zc;
+  }
+
+  // token-contiguous bf16 operands: phi_t[a][token], v_t[c][token]
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    phi_t[(part * CW + c) * TS + row] = f32_to_bf16_bits(kv[c]);
+    v_t[(part * CW + c) * TS + row] = f32_to_bf16_bits(vv[c]);
+  }
+  __syncthreads();
+
+  const int64_t blk = static_cast<int64_t>(bh) * g.nkb + j;
+  if (t < D) z_out[blk * D + t] = zpart[0][t] + zpart[1][t] + zpart[2][t] + zpart[3][t];
+
+  const int l32 = lane & 31, hh = lane >> 5;
+  f32x16 acc[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int ti = wave * NT + u;
+    const int at = ti / TA, ct = ti % TA;
+    acc[u] = zero16();
+#pragma unroll
+    for (int s = 0; s < kBlock / 16; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&phi_t[(at * 32 + l32) * TS + 16 * s + 8 * hh]);
+      const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&v_t[(ct * 32 + l32) * TS + 16 * s + 8 * hh]);
+      acc[u] = mfma32(a, bb, acc[u]);
+    }
+  }
+  __syncthreads();   // operands consumed; reuse smem as the output tile
+
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int ti = wave * NT + u;
+    const int at = ti / TA, ct = ti % TA;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int a = at * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      smem[a * HS + ct * 32 + l32] = f32_to_bf16_bits(acc[u][r]);
+    }
+  }
+  __syncthreads();
+  uint16_t* dst = h_out + blk * D * D;
+  for (int e = t; e < D * D / 8; e += kThreads) {
+    const int a = e / (D / 8), c8 = e % (D / 8);
+    *reinterpret_cast<u32x4*>(dst + a * D + c8 * 8) =
+        *reinterpret_cast<const u32x4*>(&smem[a * HS + c8 * 8]);
+  }
+}
+
+// Marginal-state sums for the forward pass: S_i = sum_{j in M_i} H_j and
+// sigma_i = sum_{j in M_i} z_j, float32 accumulation, S_i stored as bf16 in
+// the layout of H.  One workgroup per (b, h, i); thread t owns a fixed
+// contiguous slice of the d*d elements so every load is a coalesced 16-byte
+// load.
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+marginal_sum_kernel(Geometry g, const int32_t* __restrict__ marg, const uint16_t* __restrict__ hs,
+                    const float* __restrict__ zs, uint16_t* __restrict__ s_out,
+                    float* __restrict__ sigma_out) {
+  constexpr int NCH = D * D / 8 / kThreads;   // 16-byte chunks per thread
+  const int i = blockIdx.x, bh = blockIdx.y;
+  const int t = threadIdx.x;
+  const int64_t row = static_cast<int64_t>(bh) * g.nq + i;
+  const int32_t* m = marg + row * g.k_marg;
+  const uint16_t* hb = hs + static_cast<int64_t>(bh) * g.nkb * D * D;
+  const float* zb = zs + static_cast<int64_t>(bh) * g.nkb * D;
+
+  float acc[NCH * 8];
+#pragma unroll
+  for (int e = 0; e < NCH * 8; ++e) acc[e] = 0.0f;
+  float sg = 0.0f;
+#pragma unroll 2
+  for (int u = 0; u < g.k_marg; ++u) {
+    const int j = __builtin_amdgcn_readfirstlane(m[u]);
+    const uint16_t* src = hb + static_cast<int64_t>(j) * D * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      float f[8];
+      load8_f32(src + (t + kThreads * c) * 8, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[c * 8 + e] += f[e];
+    }
+    if (t < D) sg += zb[static_cast<int64_t>(j) * D + t];
+  }
+  uint16_t* dst = s_out + row * D * D;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = static_cast<uint32_t>(f32_to_bf16_bits(acc[c * 8 + 2 * e])) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(acc[c * 8 + 2 * e + 1])) << 16);
+    *reinterpret_cast<u32x4*>(dst + (t + kThreads * c) * 8) = w;
+  }
+  if (t < D) sigma_out[row * D + t] = sg;
+}
+
+template <typename T, int D>
+void launch_states_t(const Geometry& g, const void* k, const void* v, uint16_t* hs, float* zs,
+                     hipStream_t stream) {
+  dim3 grid(g.nkb, g.B * g.H);
+  hipLaunchKernelGGL((states_kernel<T, D>), grid, dim3(kThreads), 0, stream,
+                     static_cast<const T*>(k), static_cast<const T*>(v), g, hs, zs);
+}
+
+}  // namespace
+
+hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16_t* h_states,
+                         float* z_states, hipStream_t stream) {
+  if (g.dtype == 1) {
+    if (g.D == 128) launch_states_t<uint16_t, 128>(g, k, v, h_states, z_states, stream);
+    else launch_states_t<uint16_t, 64>(g, k, v, h_states, z_states, stream);
+  } else {
+    if (g.D == 128) launch_states_t<float, 128>(g, k, v, h_states, z_states, stream);
+    else launch_states_t<float, 64>(g, k, v, h_states, z_states, stream);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const uint16_t* h_states,
+                                const float* z_states, uint16_t* s_sum, float* sigma_sum,
+                                hipStream_t stream) {
+  dim3 grid(g.nq, g.B * g.H);
+  if (g.D == 128)
+    hipLaunchKernelGGL((marginal_sum_kernel<128>), grid, dim3(kThreads), 0, stream, g, marg,
+                       h_states, z_states, s_sum, sigma_sum);
+  else
+    hipLaunchKernelGGL((marginal_sum_kernel<64>), grid, dim3(kThreads), 0, stream, g, marg,
+                       h_states, z_states, s_sum, sigma_sum);
+  return hipGetLastError();
+}
+
+}  // namespace sla

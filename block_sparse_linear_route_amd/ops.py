@@ -1,0 +1,202 @@
+"""Torch-facing wrappers of the libsla C ABI (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels behind the C ABI;
+these functions only allocate outputs and workspaces with torch, pass raw
+device pointers and the current HIP stream, and turn status codes into
+``SlaError``.  Shapes follow include/sla.h: Q, K, V, O are [B, H, N, d]
+with a unit stride on d and equal strides for all four.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import lib
+
+BLOCK = 64
+
+
+class SlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{lib.sla_status_string(status).decode()} ({status}): {message}")
+        self.status = status
+        self.message = message
+
+
+def _check(status: int) -> None:
+    if status != _lib.SLA_OK:
+        raise SlaError(status, lib.sla_last_error_message().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.SLA_BF16
+    if t.dtype == torch.float32:
+        return _lib.SLA_F32
+    raise SlaError(_lib.SLA_ERR_UNSUPPORTED, f"dtype {t.dtype} (bfloat16 or float32)")
+
+
+def num_blocks(n: int) -> int:
+    return (n + BLOCK - 1) // BLOCK
+
+
+def make_problem(x: torch.Tensor, k_crit: int, k_marg: int) -> _lib.Problem:
+    if x.dim() != 4:
+        raise SlaError(_lib.SLA_ERR_INVALID_ARGUMENT, "expected a [B, H, N, d] tensor")
+    B, H, N, d = x.shape
+    sb, sh, sn, sd = x.stride()
+    if sd != 1:
+        raise SlaError(_lib.SLA_ERR_UNSUPPORTED, "the last dimension must have stride 1")
+    return _lib.Problem(B, H, N, d, BLOCK, int(k_crit), int(k_marg), _dtype_code(x), sb, sh, sn)
+
+
+def _same_layout(ref: torch.Tensor, *others: torch.Tensor):
+    """Return tensors sharing ``ref``'s strides (copy the others if needed)."""
+    out = []
+    for t in others:
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise SlaError(_lib.SLA_ERR_INVALID_ARGUMENT, "Q, K, V must share shape and dtype")
+        if t.stride() != ref.stride():
+            t = torch.empty_strided(ref.shape, ref.stride(), dtype=ref.dtype, device=ref.device).copy_(t)
+        out.append(t)
+    return out
+
+
+def workspace_size(problem: _lib.Problem, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.sla_workspace_size(ctypes.byref(problem), op, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _workspace(problem: _lib.Problem, op: int, device) -> Optional[torch.Tensor]:
+    n = workspace_size(problem, op)
+    if n == 0:
+        return None
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
+
+
+def route(q: torch.Tensor, k: torch.Tensor, k_crit: int, k_marg: int, *, want_class: bool = False,
+          want_logits: bool = False, want_pooled: bool = False, stream=None) -> dict:
+    """Pool, score and split: returns crit_idx, marg_idx (+ optional intermediates)."""
+    (k,) = _same_layout(q, k)
+    p = make_problem(q, k_crit, k_marg)
+    B, H, N, d = q.shape
+    nb = num_blocks(N)
+    dev = q.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(crit_idx=torch.empty((B, H, nb, k_crit), **i32),
+               marg_idx=torch.empty((B, H, nb, k_marg), **i32))
+    if want_class:
+        out["block_class"] = torch.empty((B, H, nb, nb), dtype=torch.int8, device=dev)
+    if want_logits:
+        out["block_logits"] = torch.empty((B, H, nb, nb), dtype=torch.float32, device=dev)
+    if want_pooled:
+        out["pooled_q"] = torch.empty((B, H, nb, d), dtype=torch.float32, device=dev)
+        out["pooled_k"] = torch.empty((B, H, nb, d), dtype=torch.float32, device=dev)
+    ws = _workspace(p, _lib.OP_ROUTE, dev)
+    _check(lib.sla_route(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(out["crit_idx"]),
+                         _ptr(out["marg_idx"]), _ptr(out.get("block_class")),
+                         _ptr(out.get("block_logits")), _ptr(out.get("pooled_q")),
+                         _ptr(out.get("pooled_k")), _ptr(ws), 0 if ws is None else ws.numel(),
+                         _stream(stream)))
+    out["_workspace"] = ws   # keeps the buffer alive until the caller drops the dict
+    return out
+
+
+def linear_states(k: torch.Tensor, v: torch.Tensor, stream=None):
+    """Per-block states: H bf16 [B,H,nkb,d,d], z float32 [B,H,nkb,d]."""
+    (v,) = _same_layout(k, v)
+    p = make_problem(k, 0, 1)
+    B, H, N, d = k.shape
+    nb = num_blocks(N)
+    Hs = torch.empty((B, H, nb, d, d), dtype=torch.bfloat16, device=k.device)
+    zs = torch.empty((B, H, nb, d), dtype=torch.float32, device=k.device)
+    _check(lib.sla_linear_states(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(Hs), _ptr(zs),
+                                 _stream(stream)))
+    return Hs, zs
+
+
+def forward(q, k, v, crit_idx, marg_idx, h_states, z_states, alpha, *, branches: bool = False,
+            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Fused sparse + linear forward.  Returns O (and O_s, O_l if ``branches``)."""
+    k, v = _same_layout(q, k, v)
+    kc, km = int(crit_idx.shape[-1]), int(marg_idx.shape[-1])
+    p = make_problem(q, kc, km)
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    o_s = o_l = None
+    if branches:
+        o_s = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        o_l = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    ws = workspace if workspace is not None else _workspace(p, _lib.OP_FORWARD, q.device)
+    alpha = alpha.to(device=q.device, dtype=torch.float32).contiguous()
+    _check(lib.sla_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                           _ptr(crit_idx.contiguous()), _ptr(marg_idx.contiguous()),
+                           _ptr(h_states), _ptr(z_states), _ptr(alpha), _ptr(out), _ptr(o_s),
+                           _ptr(o_l), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return (out, o_s, o_l) if branches else out
+
+
+def quantize_fp8(x: torch.Tensor, stream=None):
+    """Per-block E4M3 codes (uint8 [B,H,N,d]) and float32 scales [B,H,nb]."""
+    p = make_problem(x, 0, 1)
+    B, H, N, d = x.shape
+    codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, H, num_blocks(N)), dtype=torch.float32, device=x.device)
+    _check(lib.sla_quantize_fp8(ctypes.byref(p), _ptr(x), _ptr(codes), _ptr(scales),
+                                _stream(stream)))
+    return codes, scales
+
+
+def forward_fp8(q, q8, q_s, k8, k_s, v8, v_s, crit_idx, marg_idx, h_states, z_states, alpha, *,
+                branches: bool = False, out=None, workspace=None, stream=None):
+    """Forward with the fp8 sparse branch (codes and scales from ``quantize_fp8``)."""
+    kc, km = int(crit_idx.shape[-1]), int(marg_idx.shape[-1])
+    p = make_problem(q, kc, km)
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    o_s = o_l = None
+    if branches:
+        o_s = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        o_l = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    ws = workspace if workspace is not None else _workspace(p, _lib.OP_FORWARD_FP8, q.device)
+    alpha = alpha.to(device=q.device, dtype=torch.float32).contiguous()
+    _check(lib.sla_forward_fp8(ctypes.byref(p), _ptr(q), _ptr(q8), _ptr(q_s), _ptr(k8), _ptr(k_s),
+                               _ptr(v8), _ptr(v_s), _ptr(crit_idx.contiguous()),
+                               _ptr(marg_idx.contiguous()), _ptr(h_states), _ptr(z_states),
+                               _ptr(alpha), _ptr(out), _ptr(o_s), _ptr(o_l), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(stream)))
+    return (out, o_s, o_l) if branches else out
+
+
+def sla_attention(q, k, v, alpha, k_crit: int, k_marg: int, *, fp8: bool = False, stream=None):
+    """Route + linear states + forward in one call (returns O)."""
+    r = route(q, k, k_crit, k_marg, stream=stream)
+    Hs, zs = linear_states(k, v, stream=stream)
+    if fp8:
+        q8, qs = quantize_fp8(q, stream=stream)
+        k8, ks = quantize_fp8(k, stream=stream)
+        v8, vs = quantize_fp8(v, stream=stream)
+        return forward_fp8(q, q8, qs, k8, ks, v8, vs, r["crit_idx"], r["marg_idx"], Hs, zs, alpha,
+                           stream=stream)
+    return forward(q, k, v, r["crit_idx"], r["marg_idx"], Hs, zs, alpha, stream=stream)
+
+
+def version():
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib.sla_version(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value

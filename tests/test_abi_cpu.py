@@ -1,0 +1,121 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/sla.h declares, and validates arguments on the host."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_linear_route_amd import _lib
+from block_sparse_linear_route_amd._lib import Problem, lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sla.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(sla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 11
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_problem_struct_layout():
+    assert ctypes.sizeof(Problem) == 8 * 4 + 3 * 8
+    assert Problem.stride_b.offset == 32
+
+
+def P(**kw):
+    base = dict(batch=1, heads=2, seq_len=1000, head_dim=128, block=64, k_crit=2, k_marg=3,
+                dtype=_lib.SLA_BF16, stride_b=2 * 1000 * 128, stride_h=1000 * 128, stride_n=128)
+    base.update(kw)
+    return Problem(**base)
+
+
+def validate(p):
+    return lib.sla_validate(ctypes.byref(p))
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, _lib.SLA_OK),
+    (dict(head_dim=64, stride_n=64), _lib.SLA_OK),
+    (dict(dtype=_lib.SLA_F32), _lib.SLA_OK),
+    (dict(head_dim=96), _lib.SLA_ERR_UNSUPPORTED),
+    (dict(block=128), _lib.SLA_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.SLA_ERR_UNSUPPORTED),
+    (dict(seq_len=64 * 4097), _lib.SLA_ERR_UNSUPPORTED),
+    (dict(batch=0), _lib.SLA_ERR_INVALID_ARGUMENT),
+    (dict(seq_len=0), _lib.SLA_ERR_INVALID_ARGUMENT),
+    (dict(k_crit=0, k_marg=0), _lib.SLA_ERR_INVALID_ARGUMENT),
+    (dict(k_crit=10, k_marg=7), _lib.SLA_ERR_INVALID_ARGUMENT),   # 17 > 16 blocks
+    (dict(k_crit=16, k_marg=0), _lib.SLA_OK),
+    (dict(k_crit=0, k_marg=16), _lib.SLA_OK),
+    (dict(k_crit=-1), _lib.SLA_ERR_INVALID_ARGUMENT),
+    (dict(stride_n=100), _lib.SLA_ERR_INVALID_ARGUMENT),          # row overlap
+    (dict(stride_n=132), _lib.SLA_ERR_INVALID_ARGUMENT),          # 264 B rows: not 16-B multiple
+])
+def test_validate(kw, status):
+    assert validate(P(**kw)) == status
+    if status != _lib.SLA_OK:
+        assert len(lib.sla_last_error_message()) > 0
+
+
+def test_validate_null():
+    assert lib.sla_validate(None) == _lib.SLA_ERR_INVALID_ARGUMENT
+
+
+def test_num_blocks_and_workspace():
+    p = P(seq_len=32760)
+    nq, nkb = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.sla_num_blocks(ctypes.byref(p), ctypes.byref(nq), ctypes.byref(nkb)) == 0
+    assert nq.value == nkb.value == 512
+    n = ctypes.c_size_t()
+    assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_FORWARD, ctypes.byref(n)) == 0
+    assert n.value >= 2 * 512 * 128 * 128 * 2 + 2 * 512 * 128 * 4
+    assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_ROUTE, ctypes.byref(n)) == 0
+    assert n.value >= 2 * 2 * 512 * 128 * 8
+    assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_LINEAR_STATES, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.sla_workspace_size(ctypes.byref(p), 99, ctypes.byref(n)) == _lib.SLA_ERR_INVALID_ARGUMENT
+
+
+def test_status_strings_and_version():
+    for s in range(0, -6, -1):
+        assert lib.sla_status_string(s)
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert lib.sla_version(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 0
+    assert (a.value, b.value, c.value) == (0, 1, 0)
+
+
+def test_entry_points_reject_bad_arguments_before_any_device_call():
+    p = P()
+    fake = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: validation fails first
+    odd = ctypes.c_void_p(0x10008)
+    st = lib.sla_route(ctypes.byref(p), None, fake, fake, fake, None, None, None, None, fake, 1 << 30, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT
+    st = lib.sla_route(ctypes.byref(p), odd, fake, fake, fake, None, None, None, None, fake, 1 << 30, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT
+    st = lib.sla_route(ctypes.byref(p), fake, fake, fake, fake, None, None, None, None, fake, 16, None)
+    assert st == _lib.SLA_ERR_WORKSPACE
+    st = lib.sla_route(ctypes.byref(p), fake, fake, fake, fake, None, None, None, None, None, 0, None)
+    assert st == _lib.SLA_ERR_WORKSPACE
+    st = lib.sla_linear_states(ctypes.byref(p), fake, None, fake, fake, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT
+    st = lib.sla_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None, fake,
+                         None, None, fake, 1 << 40, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT      # alpha missing
+    bad = P(head_dim=96)
+    st = lib.sla_forward(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                         None, None, fake, 1 << 40, None)
+    assert st == _lib.SLA_ERR_UNSUPPORTED
+    st = lib.sla_quantize_fp8(ctypes.byref(p), fake, None, fake, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT
+    f32 = P(dtype=_lib.SLA_F32)
+    st = lib.sla_forward_fp8(ctypes.byref(f32), *([fake] * 12), None, None, None, fake, 1 << 40, None)
+    assert st == _lib.SLA_ERR_UNSUPPORTED

@@ -1,0 +1,294 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Masks are compared bit-exactly, disagreements being excused only at a class
+boundary where the oracle logits tie within 1e-5 (their count is printed).
+Outputs are compared against the oracle run under the GPU's own index lists
+(so output parity never depends on how ties were resolved), with the bf16
+tolerances: relative L2 <= 1e-2 and max-abs <= 2e-2, on the mixed output and
+on each branch.  Large workloads are checked on sampled query blocks the
+oracle evaluates one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8 as ofp8
+from oracle import sla as ora
+from tests.parity_utils import (MAX_ABS_BF16, REL_L2_BF16, check_index_lists,
+                                classes_from_lists, compare_classes, max_abs, rel_l2, to64)
+from workloads import make_custom, make_workload
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _s():
+    import block_sparse_linear_route_amd as s
+    return s
+
+
+def _gpu(w):
+    return w.q.to(DEV), w.k.to(DEV), w.v.to(DEV)
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ routing
+
+def _route_check(w, heads=None):
+    s = _s()
+    q, k, _ = _gpu(w)
+    B, H, N, d = w.shape
+    nkb = ora.n_blocks(N)
+    r = s.route(q, k, w.k_crit, w.k_marg, want_class=True, want_logits=True, want_pooled=True)
+    torch.cuda.synchronize()
+    q64, k64 = to64(w.q), to64(w.k)
+    exc = unexc = rows = 0
+    heads = heads or [(b, h) for b in range(B) for h in range(H)]
+    for b, h in heads:
+        o = ora.route(q64[b, h], k64[b, h], w.k_crit, w.k_marg)
+        crit = r["crit_idx"][b, h].cpu().numpy()
+        marg = r["marg_idx"][b, h].cpu().numpy()
+        assert crit.shape == (nkb, w.k_crit) and marg.shape == (nkb, w.k_marg)
+        check_index_lists(crit, marg, nkb)
+        cls = r["block_class"][b, h].cpu().numpy()
+        np.testing.assert_array_equal(cls, classes_from_lists(crit, marg, nkb))
+        e, u, rr = compare_classes(cls, o["block_class"], o["logits"], w.k_crit, w.k_marg)
+        exc, unexc, rows = exc + e, unexc + u, rows + rr
+        pq = r["pooled_q"][b, h].cpu().numpy()
+        pk = r["pooled_k"][b, h].cpu().numpy()
+        if w.q.dtype == torch.bfloat16:     # exact float64 sums: the means match to the bit
+            np.testing.assert_array_equal(pq, o["pooled_q"].astype(np.float32))
+            np.testing.assert_array_equal(pk, o["pooled_k"].astype(np.float32))
+        else:
+            np.testing.assert_allclose(pq, o["pooled_q"], rtol=1e-6, atol=1e-7)
+            np.testing.assert_allclose(pk, o["pooled_k"], rtol=1e-6, atol=1e-7)
+        np.testing.assert_allclose(r["block_logits"][b, h].cpu().numpy(), o["logits"],
+                                   rtol=1e-6, atol=1e-6)
+    _say(f"[route {w.name} N={N} kc={w.k_crit} km={w.k_marg}] excused ties {exc} "
+         f"(rows {rows}), unexcused {unexc}")
+    assert unexc == 0
+    return r
+
+
+@pytest.mark.parametrize("name", ["tiny", "seq8k", "video32k"])
+def test_route_parity(name):
+    _route_check(make_workload(name))
+
+
+@pytest.mark.timeout(900)
+def test_route_parity_video75k():
+    w = make_workload("video75k", cache=False)
+    _route_check(w)
+
+
+@pytest.mark.parametrize("N,kc,km,H,seed", [
+    (65, 1, 1, 2, 0), (127, 1, 0, 1, 1), (1000, 3, 5, 2, 2), (4095, 0, 64, 1, 3),
+    (8190, 128, 0, 1, 4), (3000, 10, 37, 3, 5), (64 * 300 + 1, 30, 60, 1, 6),
+])
+def test_route_parity_shapes(N, kc, km, H, seed):
+    w = make_custom(1, H, N, 128, dtype="bf16", kind="fourier1d", seed=seed, k_crit=kc, k_marg=km)
+    _route_check(w)
+
+
+def test_route_ties_break_to_lower_index():
+    # identical blocks give identical logits: the lowest KV indices must win
+    base = torch.randn(1, 1, 64, 128)
+    q = base.repeat(1, 1, 8, 1).to(torch.bfloat16)
+    k = torch.zeros(1, 1, 512, 128, dtype=torch.bfloat16)
+    k[:, :, 128:256] = 1.0             # blocks 2, 3 score highest, blocks 0,1,4..7 tie
+    s = _s()
+    r = s.route(q.to(DEV), k.to(DEV), 3, 2, want_class=True)
+    crit = r["crit_idx"][0, 0].cpu().numpy()
+    marg = r["marg_idx"][0, 0].cpu().numpy()
+    o = ora.route(to64(q[0, 0]), to64(k[0, 0]), 3, 2)
+    np.testing.assert_array_equal(crit, o["crit_idx"])
+    np.testing.assert_array_equal(marg, o["marg_idx"])
+
+
+# ------------------------------------------------------------------ states
+
+@pytest.mark.parametrize("name,heads", [("tiny", None), ("seq8k", [(0, 0), (0, 7)]),
+                                        ("video32k", [(0, 3)])])
+def test_states_parity(name, heads):
+    s = _s()
+    w = make_workload(name)
+    _, k, v = _gpu(w)
+    Hs, zs = s.linear_states(k, v)
+    torch.cuda.synchronize()
+    B, H, N, d = w.shape
+    heads = heads or [(b, h) for b in range(B) for h in range(H)]
+    k64, v64 = to64(w.k), to64(w.v)
+    for b, h in heads:
+        H64, z64 = ora.linear_states(k64[b, h], v64[b, h])
+        hg = to64(Hs[b, h])
+        zg = zs[b, h].cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(zg, z64, rtol=2e-5, atol=1e-6)
+        err = rel_l2(hg, H64)
+        _say(f"[states {name} b{b}h{h}] H rel L2 {err:.2e} max-abs {max_abs(hg, H64):.2e}")
+        assert err < 5e-3
+        assert max_abs(hg, H64) < 2e-2 * max(1.0, np.abs(H64).max())
+        n_j = np.array([min(64, N - 64 * j) for j in range(ora.n_blocks(N))], dtype=np.float64)
+        np.testing.assert_allclose(zg.sum(axis=1), n_j, rtol=1e-5)
+
+
+# ------------------------------------------------------------------ forward
+
+def _forward_check(w, heads=None, n_sample=None, seed=0, tol_rel=REL_L2_BF16, tol_abs=MAX_ABS_BF16):
+    s = _s()
+    q, k, v = _gpu(w)
+    B, H, N, d = w.shape
+    nb = ora.n_blocks(N)
+    r = s.route(q, k, w.k_crit, w.k_marg)
+    Hs, zs = s.linear_states(k, v)
+    o, o_s, o_l = s.forward(q, k, v, r["crit_idx"], r["marg_idx"], Hs, zs, w.alpha, branches=True)
+    torch.cuda.synchronize()
+    q64, k64, v64 = to64(w.q), to64(w.k), to64(w.v)
+    heads = heads or [(b, h) for b in range(B) for h in range(H)]
+    rng = np.random.default_rng(seed)
+    got = {"o": [], "s": [], "l": []}
+    ref = {"o": [], "s": [], "l": []}
+    og, osg, olg = to64(o), o_s.cpu().numpy(), o_l.cpu().numpy()
+    for b, h in heads:
+        crit = r["crit_idx"][b, h].cpu().numpy().astype(np.int64)
+        marg = r["marg_idx"][b, h].cpu().numpy().astype(np.int64)
+        if n_sample is None or n_sample >= nb:
+            qb = list(range(nb))
+        else:
+            qb = sorted(set(rng.choice(nb - 1, n_sample - 1, replace=False).tolist()) | {nb - 1})
+        H64, z64 = ora.linear_states(k64[b, h], v64[b, h])
+        ro, rs, rl = ora.forward_head(q64[b, h], k64[b, h], v64[b, h], crit, marg, H64, z64,
+                                      float(w.alpha[h]), q_blocks=qb)
+        rows = np.concatenate([np.arange(64 * i, min(64 * i + 64, N)) for i in qb])
+        got["o"].append(og[b, h][rows]); ref["o"].append(ro[rows])
+        got["s"].append(osg[b, h][rows]); ref["s"].append(rs[rows])
+        got["l"].append(olg[b, h][rows]); ref["l"].append(rl[rows])
+    res = {}
+    for key in ("o", "s", "l"):
+        a, bb = np.concatenate(got[key]), np.concatenate(ref[key])
+        res[key] = (rel_l2(a, bb), max_abs(a, bb))
+    _say(f"[forward {w.name} N={N} d={d} kc={w.k_crit} km={w.k_marg} {w.q.dtype}] "
+         + " ".join(f"{k_}: relL2 {v_[0]:.2e} maxabs {v_[1]:.2e}" for k_, v_ in res.items()))
+    for key in ("o", "s", "l"):
+        if key == "s" and w.k_crit == 0 or key == "l" and w.k_marg == 0:
+            assert res[key][1] == 0.0
+            continue
+        assert res[key][0] <= tol_rel, (key, res[key])
+        assert res[key][1] <= tol_abs, (key, res[key])
+    return res
+
+
+@pytest.mark.parametrize("name,heads,n_sample", [
+    ("tiny", None, None), ("seq8k", None, 24), ("video32k", [(0, 0), (0, 5), (0, 11)], 24)])
+def test_forward_parity(name, heads, n_sample):
+    _forward_check(make_workload(name), heads=heads, n_sample=n_sample)
+
+
+@pytest.mark.parametrize("N,d,dtype,kc,km,H,B,seed", [
+    (1000, 128, "bf16", 16, 0, 2, 1, 10),       # all critical: dense softmax attention
+    (1000, 128, "bf16", 0, 16, 2, 1, 11),       # all marginal: closed-form linear attention
+    (1000, 64, "bf16", 3, 5, 2, 1, 12),
+    (777, 128, "fp32", 2, 4, 1, 2, 13),
+    (64, 128, "bf16", 1, 0, 1, 1, 14),
+    (65, 64, "fp32", 1, 1, 3, 1, 15),
+    (4095, 128, "bf16", 1, 20, 2, 1, 16),       # one critical block: one idle stream
+    (4096, 128, "bf16", 7, 9, 1, 1, 17),
+    (2500, 64, "bf16", 39, 0, 1, 1, 18),
+])
+def test_forward_parity_shapes(N, d, dtype, kc, km, H, B, seed):
+    w = make_custom(B, H, N, d, dtype=dtype, kind="fourier1d", seed=seed, k_crit=kc, k_marg=km)
+    _forward_check(w)
+
+
+@pytest.mark.parametrize("alpha", [0.0, 1.0])
+def test_forward_alpha_endpoints(alpha):
+    w = make_custom(1, 2, 1500, 128, seed=21, k_crit=4, k_marg=8, alpha=[alpha, alpha])
+    s = _s()
+    q, k, v = _gpu(w)
+    r = s.route(q, k, 4, 8)
+    Hs, zs = s.linear_states(k, v)
+    o, o_s, o_l = s.forward(q, k, v, r["crit_idx"], r["marg_idx"], Hs, zs, w.alpha, branches=True)
+    torch.cuda.synchronize()
+    want = o_s if alpha == 1.0 else o_l
+    np.testing.assert_allclose(to64(o), want.double().cpu().numpy(), rtol=1e-2, atol=4e-3)
+    _forward_check(w)
+
+
+def test_forward_dense_matches_torch_attention():
+    w = make_custom(1, 2, 1000, 128, seed=22, k_crit=16, k_marg=0, alpha=[1.0, 1.0])
+    s = _s()
+    q, k, v = _gpu(w)
+    o = s.sla_attention(q, k, v, w.alpha, 16, 0)
+    torch.cuda.synchronize()
+    ref = torch.nn.functional.scaled_dot_product_attention(w.q.double(), w.k.double(), w.v.double())
+    a, b = to64(o), ref.numpy()
+    assert rel_l2(a, b) < REL_L2_BF16 and max_abs(a, b) < MAX_ABS_BF16
+
+
+def test_forward_strided_layout():
+    # [B, N, H, d] storage viewed as [B, H, N, d]
+    w = make_custom(2, 3, 900, 128, seed=23, k_crit=3, k_marg=4)
+    s = _s()
+    qs, ks, vs = (x.transpose(1, 2).contiguous().to(DEV).transpose(1, 2) for x in (w.q, w.k, w.v))
+    assert qs.stride()[2] == 3 * 128
+    r = s.route(qs, ks, 3, 4)
+    Hs, zs = s.linear_states(ks, vs)
+    o = s.forward(qs, ks, vs, r["crit_idx"], r["marg_idx"], Hs, zs, w.alpha)
+    q, k, v = _gpu(w)
+    r2 = s.route(q, k, 3, 4)
+    Hs2, zs2 = s.linear_states(k, v)
+    o2 = s.forward(q, k, v, r2["crit_idx"], r2["marg_idx"], Hs2, zs2, w.alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(r["crit_idx"], r2["crit_idx"]) and torch.equal(r["marg_idx"], r2["marg_idx"])
+    assert torch.equal(o.contiguous(), o2)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_forward_fuzz(seed):
+    g = np.random.default_rng(100 + seed)
+    N = int(g.integers(1, 40)) * 64 + int(g.integers(1, 65))
+    nkb = ora.n_blocks(N)
+    kc = int(g.integers(0, nkb + 1))
+    km = int(g.integers(0 if kc else 1, nkb - kc + 1))
+    d = int(g.choice([64, 128]))
+    w = make_custom(1, int(g.integers(1, 4)), N, d, dtype=str(g.choice(["bf16", "fp32"])),
+                    kind="fourier1d", seed=200 + seed, k_crit=kc, k_marg=km)
+    _route_check(w)
+    _forward_check(w)
+
+
+# ------------------------------------------------------------------ fp8 quantiser
+
+def _quant_check(x: torch.Tensor):
+    s = _s()
+    codes, scales = s.quantize_fp8(x.to(DEV))
+    torch.cuda.synchronize()
+    x32 = x.float().numpy()
+    B, H = x.shape[:2]
+    for b in range(B):
+        for h in range(H):
+            c, sc = ofp8.quantize_blocks(x32[b, h])
+            np.testing.assert_array_equal(codes[b, h].cpu().numpy(), c)
+            np.testing.assert_array_equal(scales[b, h].cpu().numpy(), sc)
+
+
+def test_quantize_fp8_bit_exact_workload():
+    w = make_workload("video32k")
+    for t in (w.q, w.k, w.v):
+        _quant_check(t[:, :2])
+
+
+def test_quantize_fp8_exhaustive_bf16():
+    bits = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    vals = bits[np.isfinite(bits)]
+    vals = vals[np.argsort(np.abs(vals), kind="stable")]          # blocks of similar magnitude
+    n = (len(vals) // 128) * 128
+    x = torch.from_numpy(vals[:n].copy()).reshape(1, 1, -1, 128).to(torch.bfloat16)
+    _quant_check(x)
+    rng = np.random.default_rng(0)
+    perm = torch.from_numpy(rng.permutation(vals)[:n].copy()).reshape(1, 1, -1, 128).to(torch.bfloat16)
+    _quant_check(perm)
+    _quant_check(torch.zeros(1, 1, 100, 128, dtype=torch.bfloat16))
+    _quant_check(torch.randn(1, 2, 1000, 64))
