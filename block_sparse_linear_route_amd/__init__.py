@@ -7,9 +7,12 @@ binding.  Importing it fails if the library has not been built.
 from .ops import (  # noqa: F401
     SlaError,
     forward,
+    forward_attend,
     forward_fp8,
+    forward_workspace,
     linear_states,
     make_problem,
+    marginal_sums,
     num_blocks,
     quantize_fp8,
     route,

@@ -45,6 +45,9 @@ SIGNATURES = {
     "sla_linear_states": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp]),
     "sla_forward": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _sz, _vp]),
+    "sla_marginal_sums": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sla_forward_attend": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                          _vp]),
     "sla_quantize_fp8": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp]),
     "sla_forward_fp8": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -57,7 +60,7 @@ SIGNATURES = {
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libsla.so not found at {LIB_PATH}; build it with "
-                          "`python -m block_sparse_linear_route_amd.build`")
+                          "`python block_sparse_linear_route_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

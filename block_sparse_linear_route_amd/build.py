@@ -1,6 +1,7 @@
 """Build libsla.so (gfx950 HIP kernels + the C ABI) in-tree with hipcc.
 
-Usage: ``python -m block_sparse_linear_route_amd.build`` or ``build()``.
+Usage: ``python block_sparse_linear_route_amd/build.py`` (run it by path: importing
+the package loads the library this script builds).
 Every translation unit is compiled for gfx950 only, in parallel, into
 ``_build/`` and linked into ``lib/libsla.so`` next to this file.
 """

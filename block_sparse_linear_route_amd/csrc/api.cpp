@@ -258,6 +258,50 @@ int sla_forward(const sla_problem* problem, const void* q, const void* k, const 
                   "attention launch");
 }
 
+int sla_marginal_sums(const sla_problem* problem, const int32_t* marg_idx, const void* h_states,
+                      const float* z_states, void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  if (problem->k_marg > 0) {
+    SLA_REQ(marg_idx, 4);
+    SLA_REQ(h_states, 16);
+    SLA_REQ(z_states, 16);
+  }
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, forward_ws(g)));
+  SLA_TRY(check_device());
+  if (g.k_marg == 0) return SLA_OK;
+  const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
+  uint16_t* s_sum = static_cast<uint16_t*>(ws);
+  float* sigma = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(rows * g.D * g.D * 2));
+  return launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
+                                            z_states, s_sum, sigma, static_cast<hipStream_t>(stream)),
+                  "marginal-sum launch");
+}
+
+int sla_forward_attend(const sla_problem* problem, const void* q, const void* k, const void* v,
+                       const int32_t* crit_idx, const float* alpha, void* o, float* o_sparse,
+                       float* o_linear, const void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(q, 16);
+  SLA_REQ(k, 16);
+  SLA_REQ(v, 16);
+  SLA_REQ(alpha, 4);
+  SLA_REQ(o, 16);
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  SLA_OPT(o_sparse, 16);
+  SLA_OPT(o_linear, 16);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(const_cast<void*>(ws), ws_bytes, forward_ws(g)));
+  SLA_TRY(check_device());
+  const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
+  const uint16_t* s_sum = static_cast<const uint16_t*>(ws);
+  const float* sigma =
+      reinterpret_cast<const float*>(static_cast<const char*>(ws) + align_up(rows * g.D * g.D * 2));
+  return launched(sla::launch_attention(g, q, k, v, crit_idx, s_sum, sigma, alpha, o, o_sparse,
+                                        o_linear, static_cast<hipStream_t>(stream)),
+                  "attention launch");
+}
+
 int sla_quantize_fp8(const sla_problem* problem, const void* x, uint8_t* x_e4m3, float* scales,
                      void* stream) {
   SLA_TRY(validate_problem(problem));

@@ -151,6 +151,39 @@ def forward(q, k, v, crit_idx, marg_idx, h_states, z_states, alpha, *, branches:
     return (out, o_s, o_l) if branches else out
 
 
+def forward_workspace(q: torch.Tensor, k_crit: int, k_marg: int, fp8: bool = False) -> torch.Tensor:
+    """A workspace for ``forward`` / ``marginal_sums`` / ``forward_attend``."""
+    p = make_problem(q, k_crit, k_marg)
+    return _workspace(p, _lib.OP_FORWARD_FP8 if fp8 else _lib.OP_FORWARD, q.device)
+
+
+def marginal_sums(q, marg_idx, h_states, z_states, workspace, *, k_crit: int, stream=None):
+    """First phase of ``forward``: marginal-state sums into ``workspace``."""
+    km = int(marg_idx.shape[-1])
+    p = make_problem(q, k_crit, km)
+    _check(lib.sla_marginal_sums(ctypes.byref(p), _ptr(marg_idx.contiguous()), _ptr(h_states),
+                                 _ptr(z_states), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def forward_attend(q, k, v, crit_idx, alpha, workspace, *, k_marg: int, branches: bool = False,
+                   out=None, stream=None):
+    """Second phase of ``forward``: fused attention using the sums in ``workspace``."""
+    k, v = _same_layout(q, k, v)
+    kc = int(crit_idx.shape[-1])
+    p = make_problem(q, kc, k_marg)
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    o_s = o_l = None
+    if branches:
+        o_s = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        o_l = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    alpha = alpha.to(device=q.device, dtype=torch.float32).contiguous()
+    _check(lib.sla_forward_attend(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(crit_idx.contiguous()), _ptr(alpha), _ptr(out), _ptr(o_s),
+                                  _ptr(o_l), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (out, o_s, o_l) if branches else out
+
+
 def quantize_fp8(x: torch.Tensor, stream=None):
     """Per-block E4M3 codes (uint8 [B,H,N,d]) and float32 scales [B,H,nb]."""
     p = make_problem(x, 0, 1)

@@ -166,6 +166,24 @@ int sla_forward(const sla_problem* problem, const void* q, const void* k,
                 void* o, float* o_sparse, float* o_linear, void* ws,
                 size_t ws_bytes, void* stream);
 
+/* The two phases of sla_forward, for callers that schedule or time them
+ * separately.  sla_marginal_sums writes, into the forward workspace, the
+ * marginal-state sums S_i = sum_{j marginal} H_j (bf16 [B,H,nq,d,d]) and
+ * sigma_i = sum_{j marginal} z_j (float [B,H,nq,d]); sla_forward_attend then
+ * runs the fused sparse + linear attention reading them from the same
+ * workspace.  Arguments mean what they mean for sla_forward; with
+ * k_marg == 0 sla_marginal_sums does nothing.  sla_forward is exactly
+ * sla_marginal_sums followed by sla_forward_attend on one stream.
+ * [SLA abstract; PISA summary (per-block matrices); SLA2 summary 2.A] */
+int sla_marginal_sums(const sla_problem* problem, const int32_t* marg_idx,
+                      const void* h_states, const float* z_states, void* ws,
+                      size_t ws_bytes, void* stream);
+int sla_forward_attend(const sla_problem* problem, const void* q, const void* k,
+                       const void* v, const int32_t* crit_idx,
+                       const float* alpha, void* o, float* o_sparse,
+                       float* o_linear, const void* ws, size_t ws_bytes,
+                       void* stream);
+
 /* Per-block E4M3 quantiser.  [SLA2 summary 2.C]
  * x        input [B,H,N,d] (problem strides and dtype)
  * x_e4m3   out uint8 [B,H,N,d] contiguous OCP E4M3 codes
