@@ -6,21 +6,27 @@
 // is renormalised over the kept keys; [SLA2 summary, section 2.A equation]
 // O = alpha O_s + (1 - alpha) O_l with alpha per head.
 //
-// One workgroup per (b, h, query block i), 4 waves:
-//   wave = qh + 2*kh; qh picks 32 of the 64 query rows, kh picks the stream
-//   of critical blocks c = kh, kh+2, kh+4, ... of the query block's list.
-// Each iteration stages two gathered KV blocks (one per stream) in LDS:
-//   K tile [64 keys][d] row-major (row padded by 16 bytes), and
-//   V^T tile [d][64 keys] with the key order permuted to match the P
-//   operand that comes straight out of the S^T accumulator registers.
-// Per wave and block: S^T = K Q^T (keys x queries, 32x32x16 bf16 MFMA),
-// online softmax on the S^T registers (row max across the lane pair l,
-// l^32), then O^T += V^T P^T.  The two streams are merged through LDS at
-// the end (each wave finalises half of the d output dims), then the linear
-// branch O_l^T = S_i^T phi(Q)^T / (phi(Q) . sigma_i) uses the marginal-state
-// sum S_i precomputed by the marginal-sum kernel, and the mixed output is
-// written.  phi(Q) uses exp(q - max q) without its row normaliser, which
-// cancels between the linear branch's numerator and denominator.
+// One workgroup per (b, h, query block i), 4 waves: wave = qh + 2*kh, where
+// qh picks 32 of the 64 query rows and kh picks 32 of the 64 keys of every
+// gathered KV block.  Per critical block (one loop iteration):
+//   * the block's K tile [64 keys][d] and V^T tile [d][64 keys] sit in LDS
+//     (double-buffered: block t+1 is written while block t is consumed, and
+//     the global loads for block t+2 are in flight meanwhile);
+//   * each wave computes S^T = K Q^T for its 32 keys x 32 queries on
+//     v_mfma_f32_32x32x16_bf16, runs the online-softmax update on the S^T
+//     registers (query = lane % 32, so a row max is a reduction over the
+//     lane's own registers plus the partner lane l ^ 32), and accumulates
+//     O^T += V^T P^T with P^T taken straight from the S^T registers;
+//   * the V^T tile stores keys in a permuted order (bits 2 and 3 of the key
+//     index swapped inside every 16-key group) so that the 8 keys a lane
+//     holds in P^T at each 16-key step are 8 consecutive LDS slots.
+// The two key halves keep separate running max / sum / output (no per-block
+// cross-wave reduction) and are merged once through LDS at the end, each
+// wave finalising half of the d output dims.  The linear branch then
+// computes O_l^T = S_i^T phi(Q)^T / (phi(Q) . sigma_i) from the
+// marginal-state sum S_i precomputed by the marginal-sum kernel (phi(Q)
+// uses exp(q - max q); the row normaliser cancels), and the alpha mix is
+// stored.
 #include "device_common.hpp"
 #include "sla_internal.hpp"
 
@@ -53,31 +59,39 @@ __device__ __forceinline__ void store4(float* p, const float* x) {
   *reinterpret_cast<f32x4*>(p) = w;
 }
 
-// Key slot of the V^T tile for key 4*grp + x: within each group of 16 keys,
-// bits 2 and 3 of the key index are swapped, so that the 8 keys a lane's
-// P^T operand covers at each 16-key step are 8 consecutive slots.
+// LDS slot of key 4*grp .. 4*grp+3 in a V^T row (bits 2 and 3 of the key
+// index swapped within each group of 16 keys).
 __device__ __forceinline__ int vt_slot(int grp) {
   return 16 * (grp >> 2) + 8 * (grp & 1) + 4 * ((grp >> 1) & 1);
 }
 
 template <typename T, int D>
+struct Tile {
+  static constexpr int CH = D / 8;                 // 8-element chunks per row
+  static constexpr int KS = D + 8;                 // K row stride (elements)
+  static constexpr int VS = kBlock + 8;            // V^T row stride
+  static constexpr int KT = kBlock * KS;           // K tile elements
+  static constexpr int VT = D * VS;                // V^T tile elements
+  static constexpr int BUF = KT + VT;              // one buffer
+  static constexpr int KPT = kBlock * CH / kThreads;       // K chunks per thread
+  static constexpr int VSUB = 16 * CH;                      // V 4x8 sub-tiles per block
+  static constexpr int VPT = (VSUB + kThreads - 1) / kThreads;
+};
+
+template <typename T, int D>
 __global__ void __launch_bounds__(kThreads, 2)
 attention_kernel(AttnArgs A) {
-  constexpr int KS = D + 8;            // K tile row stride (elements)
-  constexpr int VS = kBlock + 8;       // V^T tile row stride
-  constexpr int KT = kBlock * KS;      // elements per K tile
-  constexpr int VT = D * VS;           // elements per V^T tile
+  using TL = Tile<T, D>;
+  constexpr int CH = TL::CH, KS = TL::KS, VS = TL::VS, KT = TL::KT, BUF = TL::BUF;
+  constexpr int KPT = TL::KPT, VSUB = TL::VSUB, VPT = TL::VPT;
   constexpr int NS = D / 16;           // 16-wide k-steps over the features
   constexpr int DT = D / 32;           // 32-row tiles over the value dims
   constexpr int DTH = DT / 2;          // tiles each wave finalises
-  constexpr int CH = D / 8;            // 8-element chunks per row
-  constexpr int KPT = 2 * kBlock * CH / kThreads;   // K chunks per thread
-  constexpr int VPT = 2 * 16 * CH / kThreads;       // V 4x8 sub-tiles per thread
   constexpr int SS = D + 8;            // S^T row stride
-  static_assert(KPT >= 1 && VPT >= 1, "tile split");
-  static_assert(2 * VT >= D * SS + D * 2, "S^T and sigma fit in the V region");
-  static_assert(2 * KT * 2 >= 4 * (256 + 4 * DTH * 16 * 64), "merge buffer fits in the K region");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * KT + 2 * VT];
+  static_assert(KPT >= 1, "tile split");
+  static_assert(BUF >= D * SS + 2 * D, "S^T and sigma fit in the second buffer");
+  static_assert(BUF * 2 >= 4 * (256 + 4 * DTH * 16 * 64), "merge data fits in the first buffer");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF];
 
   const Geometry& g = A.g;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -90,163 +104,146 @@ attention_kernel(AttnArgs A) {
   const int bh = logical / g.nq;
   const int b = bh / g.H, h = bh % g.H;
   const int64_t hoff = b * g.sb + h * g.sh;
-  const T* qp = static_cast<const T*>(A.q) + hoff;
-  const T* kp = static_cast<const T*>(A.k) + hoff;
-  const T* vp = static_cast<const T*>(A.v) + hoff;
+  const T* __restrict__ qp = static_cast<const T*>(A.q) + hoff;
+  const T* __restrict__ kp = static_cast<const T*>(A.k) + hoff;
+  const T* __restrict__ vp = static_cast<const T*>(A.v) + hoff;
   const int n_i = min(kBlock, g.N - kBlock * i);
   const float cl = A.c_log2;
+  const int64_t sn = g.sn;
 
   // Q fragments (B operand of S^T = K Q^T): query 32*qh + l32, features
   // 16*s + 8*hh .. +7.
   bf16x8 qf[NS];
   const int qrow = 32 * qh + l32;
-  if (qrow < n_i) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      qf[s] = load8(qp + static_cast<int64_t>(kBlock * i + qrow) * g.sn + 16 * s + 8 * hh);
-  } else {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) qf[s] = zero_bf16x8();
-  }
-
-  uint16_t* kbuf = smem;
-  uint16_t* vbuf = smem + 2 * KT;
-  const int32_t* crow = A.crit + (static_cast<int64_t>(bh) * g.nq + i) * g.k_crit;
-  const int kc = g.k_crit;
-  const int iters = (kc + 1) / 2;
-
-  bf16x8 kreg[KPT];
-  bf16x8 vreg[VPT][4];
-  auto load_regs = [&](int it) {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int id = t + kThreads * u;
-      const int kb = id / (kBlock * CH);
-      const int rem = id % (kBlock * CH);
-      const int row = rem / CH, chk = rem % CH;
-      const int c = 2 * it + kb;
-      kreg[u] = zero_bf16x8();
-      if (c < kc) {
-        const int j = crow[c];
-        if (row < g.N - kBlock * j)
-          kreg[u] = load8(kp + static_cast<int64_t>(kBlock * j + row) * g.sn + 8 * chk);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int id = t + kThreads * u;
-      const int kb = id / (16 * CH);
-      const int rem = id % (16 * CH);
-      const int grp = rem / CH, chk = rem % CH;
-      const int c = 2 * it + kb;
-      const int j = (c < kc) ? crow[c] : 0;
-      const int nj = (c < kc) ? min(kBlock, g.N - kBlock * j) : 0;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int row = 4 * grp + x;
-        vreg[u][x] = (row < nj)
-                         ? load8(vp + static_cast<int64_t>(kBlock * j + row) * g.sn + 8 * chk)
+  for (int s = 0; s < NS; ++s)
+    qf[s] = (qrow < n_i) ? load8(qp + static_cast<int64_t>(kBlock * i + qrow) * sn + 16 * s + 8 * hh)
                          : zero_bf16x8();
-      }
-    }
-  };
-  auto store_lds = [&]() {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int id = t + kThreads * u;
-      const int kb = id / (kBlock * CH);
-      const int rem = id % (kBlock * CH);
-      const int row = rem / CH, chk = rem % CH;
-      *reinterpret_cast<bf16x8*>(&kbuf[kb * KT + row * KS + 8 * chk]) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int id = t + kThreads * u;
-      const int kb = id / (16 * CH);
-      const int rem = id % (16 * CH);
-      const int grp = rem / CH, chk = rem % CH;
-      const int slot = vt_slot(grp);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x4 w;
-        w[0] = vreg[u][0][e]; w[1] = vreg[u][1][e]; w[2] = vreg[u][2][e]; w[3] = vreg[u][3][e];
-        *reinterpret_cast<bf16x4*>(&vbuf[kb * VT + (8 * chk + e) * VS + slot]) = w;
-      }
-    }
-  };
+
+  const int32_t* __restrict__ crow = A.crit + (static_cast<int64_t>(bh) * g.nq + i) * g.k_crit;
+  const int kc = g.k_crit;
+
+  // staging registers for one block: K chunks and one V 4x8 sub-tile
+  bf16x8 kr[KPT];
+  bf16x8 vr[VPT][4];
+
+#define SLA_LOAD_BLOCK(c_)                                                              \
+  do {                                                                                  \
+    const int jb_ = crow[(c_)];                                                         \
+    const int nj_ = min(kBlock, g.N - kBlock * jb_);                                    \
+    const T* kb_ = kp + static_cast<int64_t>(kBlock * jb_) * sn;                        \
+    const T* vb_ = vp + static_cast<int64_t>(kBlock * jb_) * sn;                        \
+    _Pragma("unroll") for (int u = 0; u < KPT; ++u) {                                   \
+      const int id = t + kThreads * u;                                                  \
+      const int row = id / CH, chk = id % CH;                                           \
+      kr[u] = (row < nj_) ? load8(kb_ + row * sn + 8 * chk) : zero_bf16x8();            \
+    }                                                                                   \
+    _Pragma("unroll") for (int u = 0; u < VPT; ++u) {                                   \
+      const int id = t + kThreads * u;                                                  \
+      const int grp = id % 16, chk = id / 16;                                           \
+      _Pragma("unroll") for (int x = 0; x < 4; ++x) {                                   \
+        const int row = 4 * grp + x;                                                    \
+        vr[u][x] = (id < VSUB && row < nj_) ? load8(vb_ + row * sn + 8 * chk)           \
+                                            : zero_bf16x8();                            \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
+
+#define SLA_STORE_BLOCK(buf_)                                                           \
+  do {                                                                                  \
+    uint16_t* kd_ = smem + (buf_) * BUF;                                                \
+    uint16_t* vd_ = kd_ + KT;                                                           \
+    _Pragma("unroll") for (int u = 0; u < KPT; ++u) {                                   \
+      const int id = t + kThreads * u;                                                  \
+      const int row = id / CH, chk = id % CH;                                           \
+      *reinterpret_cast<bf16x8*>(&kd_[row * KS + 8 * chk]) = kr[u];                     \
+    }                                                                                   \
+    _Pragma("unroll") for (int u = 0; u < VPT; ++u) {                                   \
+      const int id = t + kThreads * u;                                                  \
+      if (id < VSUB) {                                                                  \
+        const int grp = id % 16, chk = id / 16;                                         \
+        const int slot = vt_slot(grp);                                                  \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                 \
+          bf16x4 w4;                                                                    \
+          w4[0] = vr[u][0][e]; w4[1] = vr[u][1][e];                                     \
+          w4[2] = vr[u][2][e]; w4[3] = vr[u][3][e];                                     \
+          *reinterpret_cast<bf16x4*>(&vd_[(8 * chk + e) * VS + slot]) = w4;             \
+        }                                                                               \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = zero16();
 
-  if (iters > 0) load_regs(0);
-  for (int it = 0; it < iters; ++it) {
+  if (kc > 0) {
+    SLA_LOAD_BLOCK(0);
+    SLA_STORE_BLOCK(0);
+    if (kc > 1) SLA_LOAD_BLOCK(1);
     __syncthreads();
-    store_lds();
-    __syncthreads();
-    if (it + 1 < iters) load_regs(it + 1);
-    const int c = 2 * it + kh;
-    if (c < kc) {
-      const int j = crow[c];
-      const int nj = min(kBlock, g.N - kBlock * j);
-      const uint16_t* kt = kbuf + kh * KT;
-      const uint16_t* vt = vbuf + kh * VT;
-      f32x16 sacc[2];
+  }
+  for (int it = 0; it < kc; ++it) {
+    const int buf = it & 1;
+    const int jb = crow[it];
+    const int nj = min(kBlock, g.N - kBlock * jb);
+    const uint16_t* kt = smem + buf * BUF;
+    const uint16_t* vt = kt + KT;
+
+    // S^T for keys 32*kh .. +31 and queries 32*qh .. +31
+    f32x16 sacc = zero16();
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        sacc[mt] = zero16();
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[(32 * kh + l32) * KS + 16 * s + 8 * hh]);
+      sacc = mfma32(a, qf[s], sacc);
+    }
+    if (nj < kBlock) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[(32 * mt + l32) * KS + 16 * s + 8 * hh]);
-          sacc[mt] = mfma32(a, qf[s], sacc[mt]);
-        }
-      }
-      if (nj < kBlock) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key >= nj) sacc[mt][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
-      mx = fmaxf(mx, xor_lane(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = exp2f((m_run - m_new) * cl);
-      const float mb = m_new * cl;
-      float ps = 0.0f;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(fmaf(sacc[mt][r], cl, -mb));
-          ps += p;
-          pb[2 * mt + (r >> 3)][r & 7] = f32_to_bf16(p);
-        }
-      l_run = l_run * corr + ps;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vt[(32 * dt + l32) * VS + 16 * s + 8 * hh]);
-          oacc[dt] = mfma32(a, pb[s], oacc[dt]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key >= nj) sacc[r] = -INFINITY;
       }
     }
-  }
+    float mx = sacc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;   // all keys masked so far
+    const float corr = __builtin_amdgcn_exp2f((m_run - m_use) * cl);
+    const float mb = m_use * cl;
+    float ps = 0.0f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], cl, -mb));
+      ps += p;
+      pb[r >> 3][r & 7] = f32_to_bf16(p);
+    }
+    l_run = l_run * corr + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vt[(32 * dt + l32) * VS + 32 * kh + 16 * s + 8 * hh]);
+        oacc[dt] = mfma32(a, pb[s], oacc[dt]);
+      }
+    }
 
-  // ---- merge the two block streams; stage the linear-branch operands ----
-  __syncthreads();
+    if (it + 1 < kc) {
+      SLA_STORE_BLOCK(buf ^ 1);          // block it+1 (its loads were issued last iteration)
+      if (it + 2 < kc) SLA_LOAD_BLOCK(it + 2);
+    }
+    __syncthreads();
+  }
+#undef SLA_LOAD_BLOCK
+#undef SLA_STORE_BLOCK
+
+  // ---- merge the two key halves; stage the linear-branch operands ----
   float* mbuf = reinterpret_cast<float*>(smem);   // [4][32]
   float* lbuf = mbuf + 128;                        // [4][32]
   float* obuf = mbuf + 256;                        // [4][DTH][16][64]
@@ -255,20 +252,28 @@ attention_kernel(AttnArgs A) {
     mbuf[wave * 32 + l32] = m_run;
     lbuf[wave * 32 + l32] = l_full;
   }
-  const int own0 = kh * DTH, oth0 = (1 - kh) * DTH;
+  const int own0 = kh * DTH;
+  // the wave keeps dims [32*own0, +32*DTH); select with static indices so the
+  // accumulators stay in registers
+  f32x16 o_own[DTH], o_oth[DTH];
+#pragma unroll
+  for (int u = 0; u < DTH; ++u) {
+    o_own[u] = kh ? oacc[DTH + u] : oacc[u];
+    o_oth[u] = kh ? oacc[u] : oacc[DTH + u];
+  }
 #pragma unroll
   for (int u = 0; u < DTH; ++u)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) obuf[((wave * DTH + u) * 16 + r) * 64 + lane] = oacc[oth0 + u][r];
+    for (int r = 0; r < 16; ++r) obuf[((wave * DTH + u) * 16 + r) * 64 + lane] = o_oth[u][r];
 
   const bool has_lin = g.k_marg > 0;
-  uint16_t* st = vbuf;                                         // S_i^T [D][SS]
-  float* sg = reinterpret_cast<float*>(vbuf + D * SS);         // sigma_i [D]
+  uint16_t* st = smem + BUF;                                   // S_i^T [D][SS] (second buffer)
+  float* sg = reinterpret_cast<float*>(st + D * SS);           // sigma_i [D]
   if (has_lin) {
     const int64_t row = static_cast<int64_t>(bh) * g.nq + i;
     const uint16_t* sgl = A.s_sum + row * D * D;
     for (int e = t; e < (D / 4) * CH; e += kThreads) {
-      const int ag = e / CH, bc = e % CH;
+      const int ag = e % (D / 4), bc = e / (D / 4);
       bf16x8 w[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) w[x] = load8(sgl + (4 * ag + x) * D + 8 * bc);
@@ -287,8 +292,8 @@ attention_kernel(AttnArgs A) {
   const float m_p = mbuf[partner * 32 + l32];
   const float l_p = lbuf[partner * 32 + l32];
   const float m_tot = fmaxf(m_run, m_p);
-  const float w_me = (m_run == -INFINITY) ? 0.0f : exp2f((m_run - m_tot) * cl);
-  const float w_p = (m_p == -INFINITY) ? 0.0f : exp2f((m_p - m_tot) * cl);
+  const float w_me = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_run - m_tot) * cl);
+  const float w_p = (m_p == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_p - m_tot) * cl);
   const float den = l_full * w_me + l_p * w_p;
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   f32x16 os[DTH];
@@ -296,7 +301,7 @@ attention_kernel(AttnArgs A) {
   for (int u = 0; u < DTH; ++u)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      os[u][r] = (oacc[own0 + u][r] * w_me + obuf[((partner * DTH + u) * 16 + r) * 64 + lane] * w_p) * inv;
+      os[u][r] = (o_own[u][r] * w_me + obuf[((partner * DTH + u) * 16 + r) * 64 + lane] * w_p) * inv;
 
   f32x16 ol[DTH];
 #pragma unroll
@@ -308,25 +313,23 @@ attention_kernel(AttnArgs A) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, bf16v_to_f32(qf[s][e]));
     qmax = fmaxf(qmax, xor_lane(qmax, 32));
-    bf16x8 pf[NS];
     float dpart = 0.0f;
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < NS; ++s) {
+      bf16x8 pf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const __bf16 pv = f32_to_bf16(exp2f((bf16v_to_f32(qf[s][e]) - qmax) * kLog2e));
-        pf[s][e] = pv;
+        const __bf16 pv = f32_to_bf16(__builtin_amdgcn_exp2f((bf16v_to_f32(qf[s][e]) - qmax) * kLog2e));
+        pf[e] = pv;
         dpart += bf16v_to_f32(pv) * sg[16 * s + 8 * hh + e];
       }
-    const float dsum = dpart + xor_lane(dpart, 32);
 #pragma unroll
-    for (int u = 0; u < DTH; ++u) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
+      for (int u = 0; u < DTH; ++u) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&st[(32 * (own0 + u) + l32) * SS + 16 * s + 8 * hh]);
-        ol[u] = mfma32(a, pf[s], ol[u]);
+        ol[u] = mfma32(a, pf, ol[u]);
       }
     }
+    const float dsum = dpart + xor_lane(dpart, 32);
     const float dinv = 1.0f / dsum;
 #pragma unroll
     for (int u = 0; u < DTH; ++u)
@@ -338,7 +341,7 @@ attention_kernel(AttnArgs A) {
   const float al = A.alpha[h];
   if (qrow < n_i) {
     const int tok = kBlock * i + qrow;
-    T* orow = static_cast<T*>(A.o) + hoff + static_cast<int64_t>(tok) * g.sn;
+    T* orow = static_cast<T*>(A.o) + hoff + static_cast<int64_t>(tok) * sn;
     const int64_t dbg = (static_cast<int64_t>(bh) * g.N + tok) * D;
 #pragma unroll
     for (int u = 0; u < DTH; ++u)
