@@ -138,9 +138,29 @@ int launched(hipError_t e, const char* what) {
       return fail(SLA_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", #ptr, (align)); \
   } while (0)
 
+// Forward workspace: [S bf16 B*H*nq*d*d][sigma f32 B*H*nq*d][mask bits u32 B*H*nq*nw]
+struct FwdWs {
+  uint16_t* s_sum;
+  float* sigma;
+  uint32_t* bits;
+};
+
 size_t forward_ws(const sla::Geometry& g) {
   const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
-  return align_up(rows * g.D * g.D * 2) + align_up(rows * g.D * 4);
+  return align_up(rows * g.D * g.D * 2) + align_up(rows * g.D * 4) +
+         align_up(rows * sla::marginal_bit_words(g) * 4);
+}
+
+FwdWs carve_forward_ws(const sla::Geometry& g, void* ws) {
+  const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
+  char* p = static_cast<char*>(ws);
+  FwdWs w;
+  w.s_sum = reinterpret_cast<uint16_t*>(p);
+  p += align_up(rows * g.D * g.D * 2);
+  w.sigma = reinterpret_cast<float*>(p);
+  p += align_up(rows * g.D * 4);
+  w.bits = reinterpret_cast<uint32_t*>(p);
+  return w;
 }
 
 size_t route_ws(const sla::Geometry& g) {
@@ -245,15 +265,13 @@ int sla_forward(const sla_problem* problem, const void* q, const void* k, const 
   const sla::Geometry g = geometry(problem);
   SLA_TRY(check_ws(ws, ws_bytes, forward_ws(g)));
   SLA_TRY(check_device());
-  const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
-  uint16_t* s_sum = static_cast<uint16_t*>(ws);
-  float* sigma = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(rows * g.D * g.D * 2));
+  const FwdWs w = carve_forward_ws(g, ws);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.k_marg > 0)
     SLA_TRY(launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
-                                               z_states, s_sum, sigma, s),
+                                               z_states, w.s_sum, w.sigma, w.bits, s),
                      "marginal-sum launch"));
-  return launched(sla::launch_attention(g, q, k, v, crit_idx, s_sum, sigma, alpha, o, o_sparse,
+  return launched(sla::launch_attention(g, q, k, v, crit_idx, w.s_sum, w.sigma, alpha, o, o_sparse,
                                         o_linear, s),
                   "attention launch");
 }
@@ -270,11 +288,10 @@ int sla_marginal_sums(const sla_problem* problem, const int32_t* marg_idx, const
   SLA_TRY(check_ws(ws, ws_bytes, forward_ws(g)));
   SLA_TRY(check_device());
   if (g.k_marg == 0) return SLA_OK;
-  const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
-  uint16_t* s_sum = static_cast<uint16_t*>(ws);
-  float* sigma = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(rows * g.D * g.D * 2));
+  const FwdWs w = carve_forward_ws(g, ws);
   return launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
-                                            z_states, s_sum, sigma, static_cast<hipStream_t>(stream)),
+                                            z_states, w.s_sum, w.sigma, w.bits,
+                                            static_cast<hipStream_t>(stream)),
                   "marginal-sum launch");
 }
 
@@ -293,11 +310,8 @@ int sla_forward_attend(const sla_problem* problem, const void* q, const void* k,
   const sla::Geometry g = geometry(problem);
   SLA_TRY(check_ws(const_cast<void*>(ws), ws_bytes, forward_ws(g)));
   SLA_TRY(check_device());
-  const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
-  const uint16_t* s_sum = static_cast<const uint16_t*>(ws);
-  const float* sigma =
-      reinterpret_cast<const float*>(static_cast<const char*>(ws) + align_up(rows * g.D * g.D * 2));
-  return launched(sla::launch_attention(g, q, k, v, crit_idx, s_sum, sigma, alpha, o, o_sparse,
+  const FwdWs w = carve_forward_ws(g, const_cast<void*>(ws));
+  return launched(sla::launch_attention(g, q, k, v, crit_idx, w.s_sum, w.sigma, alpha, o, o_sparse,
                                         o_linear, static_cast<hipStream_t>(stream)),
                   "attention launch");
 }
@@ -344,16 +358,14 @@ int sla_forward_fp8(const sla_problem* problem, const void* q, const uint8_t* q8
   const sla::Geometry g = geometry(problem);
   SLA_TRY(check_ws(ws, ws_bytes, forward_ws(g)));
   SLA_TRY(check_device());
-  const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
-  uint16_t* s_sum = static_cast<uint16_t*>(ws);
-  float* sigma = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(rows * g.D * g.D * 2));
+  const FwdWs w = carve_forward_ws(g, ws);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.k_marg > 0)
     SLA_TRY(launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
-                                               z_states, s_sum, sigma, s),
+                                               z_states, w.s_sum, w.sigma, w.bits, s),
                      "marginal-sum launch"));
-  return launched(sla::launch_attention_fp8(g, q, q8, q_s, k8, k_s, v8, v_s, crit_idx, s_sum,
-                                            sigma, alpha, o, o_sparse, o_linear, s),
+  return launched(sla::launch_attention_fp8(g, q, q8, q_s, k8, k_s, v8, v_s, crit_idx, w.s_sum,
+                                            w.sigma, alpha, o, o_sparse, o_linear, s),
                   "fp8 attention launch");
 }
 

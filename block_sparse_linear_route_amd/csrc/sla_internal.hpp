@@ -26,10 +26,12 @@ hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16
                          float* z_states, hipStream_t stream);
 
 // Marginal-state sums S_i = sum_{j in M_i} H_j (bf16, [B,H,nq,d,d]) and
-// sigma_i = sum_{j in M_i} z_j (float, [B,H,nq,d]).
+// sigma_i = sum_{j in M_i} z_j (float, [B,H,nq,d]); bits is scratch of
+// B*H*nq*marginal_bit_words(g) 32-bit words for the mask rows.
+inline int marginal_bit_words(const Geometry& g) { return (g.nkb + 31) / 32; }
 hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const uint16_t* h_states,
                                 const float* z_states, uint16_t* s_sum, float* sigma_sum,
-                                hipStream_t stream);
+                                uint32_t* bits, hipStream_t stream);
 
 hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,
                             const int32_t* crit, const uint16_t* s_sum, const float* sigma_sum,

@@ -128,54 +128,6 @@ states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
   }
 }
 
-// Marginal-state sums for the forward pass: S_i = sum_{j in M_i} H_j and
-// sigma_i = sum_{j in M_i} z_j, float32 accumulation, S_i stored as bf16 in
-// the layout of H.  One workgroup per (b, h, i); thread t owns a fixed
-// contiguous slice of the d*d elements so every load is a coalesced 16-byte
-// load.
-template <int D>
-__global__ void __launch_bounds__(kThreads)
-marginal_sum_kernel(Geometry g, const int32_t* __restrict__ marg, const uint16_t* __restrict__ hs,
-                    const float* __restrict__ zs, uint16_t* __restrict__ s_out,
-                    float* __restrict__ sigma_out) {
-  constexpr int NCH = D * D / 8 / kThreads;   // 16-byte chunks per thread
-  const int i = blockIdx.x, bh = blockIdx.y;
-  const int t = threadIdx.x;
-  const int64_t row = static_cast<int64_t>(bh) * g.nq + i;
-  const int32_t* m = marg + row * g.k_marg;
-  const uint16_t* hb = hs + static_cast<int64_t>(bh) * g.nkb * D * D;
-  const float* zb = zs + static_cast<int64_t>(bh) * g.nkb * D;
-
-  float acc[NCH * 8];
-#pragma unroll
-  for (int e = 0; e < NCH * 8; ++e) acc[e] = 0.0f;
-  float sg = 0.0f;
-#pragma unroll 2
-  for (int u = 0; u < g.k_marg; ++u) {
-    const int j = __builtin_amdgcn_readfirstlane(m[u]);
-    const uint16_t* src = hb + static_cast<int64_t>(j) * D * D;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      float f[8];
-      load8_f32(src + (t + kThreads * c) * 8, f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[c * 8 + e] += f[e];
-    }
-    if (t < D) sg += zb[static_cast<int64_t>(j) * D + t];
-  }
-  uint16_t* dst = s_out + row * D * D;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    u32x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = static_cast<uint32_t>(f32_to_bf16_bits(acc[c * 8 + 2 * e])) |
-             (static_cast<uint32_t>(f32_to_bf16_bits(acc[c * 8 + 2 * e + 1])) << 16);
-    *reinterpret_cast<u32x4*>(dst + (t + kThreads * c) * 8) = w;
-  }
-  if (t < D) sigma_out[row * D + t] = sg;
-}
-
 template <typename T, int D>
 void launch_states_t(const Geometry& g, const void* k, const void* v, uint16_t* hs, float* zs,
                      hipStream_t stream) {
@@ -195,19 +147,6 @@ hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16
     if (g.D == 128) launch_states_t<float, 128>(g, k, v, h_states, z_states, stream);
     else launch_states_t<float, 64>(g, k, v, h_states, z_states, stream);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const uint16_t* h_states,
-                                const float* z_states, uint16_t* s_sum, float* sigma_sum,
-                                hipStream_t stream) {
-  dim3 grid(g.nq, g.B * g.H);
-  if (g.D == 128)
-    hipLaunchKernelGGL((marginal_sum_kernel<128>), grid, dim3(kThreads), 0, stream, g, marg,
-                       h_states, z_states, s_sum, sigma_sum);
-  else
-    hipLaunchKernelGGL((marginal_sum_kernel<64>), grid, dim3(kThreads), 0, stream, g, marg,
-                       h_states, z_states, s_sum, sigma_sum);
   return hipGetLastError();
 }
 

@@ -292,3 +292,42 @@ def test_quantize_fp8_exhaustive_bf16():
     _quant_check(perm)
     _quant_check(torch.zeros(1, 1, 100, 128, dtype=torch.bfloat16))
     _quant_check(torch.randn(1, 2, 1000, 64))
+
+
+# ------------------------------------------------------------------ marginal sums
+
+def _align256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("N,d,km,H,seed", [(1000, 64, 5, 2, 30), (1024, 64, 8, 1, 31),
+                                           (5000, 128, 20, 2, 32), (33 * 64 + 5, 128, 1, 1, 33),
+                                           (300 * 64, 128, 150, 1, 34)])
+def test_marginal_sums_parity(N, d, km, H, seed):
+    """Phase one of the forward: S_i and sigma_i in the workspace equal the
+    float64 sums of the same bf16 / float32 states over each marginal set."""
+    s = _s()
+    g = np.random.default_rng(seed)
+    nb = ora.n_blocks(N)
+    Hs = torch.from_numpy(g.standard_normal((1, H, nb, d, d)) * 0.1).to(torch.bfloat16)
+    zs = torch.from_numpy(g.uniform(0, 2, (1, H, nb, d))).float()
+    marg = np.stack([np.stack([np.sort(g.choice(nb, km, replace=False)) for _ in range(nb)])
+                     for _ in range(H)])[None].astype(np.int32)
+    q = torch.zeros(1, H, N, d, dtype=torch.bfloat16, device=DEV)
+    ws = s.forward_workspace(q, 0, km)
+    s.marginal_sums(q, torch.from_numpy(marg).to(DEV), Hs.to(DEV), zs.to(DEV), ws, k_crit=0)
+    torch.cuda.synchronize()
+    rows = H * nb
+    S = ws[:rows * d * d * 2].view(torch.bfloat16).view(1, H, nb, d, d).double().cpu().numpy()
+    off = _align256(rows * d * d * 2)
+    sig = ws[off:off + rows * d * 4].view(torch.float32).view(1, H, nb, d).double().cpu().numpy()
+    H64, z64 = Hs.double().numpy(), zs.double().numpy()
+    for h in range(H):
+        for i in range(nb):
+            m = marg[0, h, i]
+            want_s = H64[0, h, m].sum(0)
+            want_z = z64[0, h, m].sum(0)
+            np.testing.assert_allclose(S[0, h, i], want_s, rtol=2 ** -8, atol=1e-6,
+                                       err_msg=f"S head {h} row {i}")
+            np.testing.assert_allclose(sig[0, h, i], want_z, rtol=1e-5, atol=1e-6,
+                                       err_msg=f"sigma head {h} row {i}")
