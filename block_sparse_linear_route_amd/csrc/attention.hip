@@ -65,33 +65,33 @@ __device__ __forceinline__ int vt_slot(int grp) {
   return 16 * (grp >> 2) + 8 * (grp & 1) + 4 * ((grp >> 1) & 1);
 }
 
-template <typename T, int D>
-struct Tile {
-  static constexpr int CH = D / 8;                 // 8-element chunks per row
-  static constexpr int KS = D + 8;                 // K row stride (elements)
-  static constexpr int VS = kBlock + 8;            // V^T row stride
-  static constexpr int KT = kBlock * KS;           // K tile elements
-  static constexpr int VT = D * VS;                // V^T tile elements
-  static constexpr int BUF = KT + VT;              // one buffer
-  static constexpr int KPT = kBlock * CH / kThreads;       // K chunks per thread
-  static constexpr int VSUB = 16 * CH;                      // V 4x8 sub-tiles per block
-  static constexpr int VPT = (VSUB + kThreads - 1) / kThreads;
-};
+// XOR swizzle of the 16-byte chunks of a tile row: both the K-row operand
+// reads (16 consecutive rows, one chunk) and the transposing V reads (4
+// consecutive keys x 4 chunks) hit distinct LDS banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return (r >> 1) & 7;
+}
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads, 2)
 attention_kernel(AttnArgs A) {
-  using TL = Tile<T, D>;
-  constexpr int CH = TL::CH, KS = TL::KS, VS = TL::VS, KT = TL::KT, BUF = TL::BUF;
-  constexpr int KPT = TL::KPT, VSUB = TL::VSUB, VPT = TL::VPT;
-  constexpr int NS = D / 16;           // 16-wide k-steps over the features
-  constexpr int DT = D / 32;           // 32-row tiles over the value dims
-  constexpr int DTH = DT / 2;          // tiles each wave finalises
-  constexpr int SS = D + 8;            // S^T row stride
-  static_assert(KPT >= 1, "tile split");
-  static_assert(BUF >= D * SS + 2 * D, "S^T and sigma fit in the second buffer");
-  static_assert(BUF * 2 >= 4 * (256 + 4 * DTH * 16 * 64), "merge data fits in the first buffer");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF];
+  constexpr int CH = D / 8;                    // 16-byte chunks per row
+  constexpr int TILE = kBlock * D;             // elements per K or V tile
+  constexpr int NSTAGE = 4;                    // two K buffers, two V buffers
+  constexpr int RPI = 64 / CH;                 // rows per 64-lane load instruction
+  constexpr int IPW = (kBlock / 4) / RPI;      // load instructions per wave per tile
+  constexpr int NS = D / 16;                   // 16-wide k-steps over the features
+  constexpr int DT = D / 32;                   // 32-row tiles over the value dims
+  constexpr int DTH = DT / 2;                  // tiles each wave finalises
+  constexpr int SS = D + 8;                    // S^T row stride (linear branch)
+  constexpr int MERGE_BYTES = 4 * (256 + 4 * DTH * 16 * 64);
+  constexpr int ST_BYTES = D * SS * 2 + D * 4;
+  constexpr int LOOP_BYTES = NSTAGE * TILE * 2;
+  constexpr int SMEM_BYTES = (LOOP_BYTES > MERGE_BYTES + ST_BYTES ? LOOP_BYTES : MERGE_BYTES + ST_BYTES);
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM_BYTES];
+  uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
 
   const Geometry& g = A.g;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -109,144 +109,205 @@ attention_kernel(AttnArgs A) {
   const T* __restrict__ vp = static_cast<const T*>(A.v) + hoff;
   const int n_i = min(kBlock, g.N - kBlock * i);
   const float cl = A.c_log2;
+  constexpr float kLazy = 8.0f;
   const int64_t sn = g.sn;
 
   // Q fragments (B operand of S^T = K Q^T): query 32*qh + l32, features
-  // 16*s + 8*hh .. +7.
+  // 16*s + 8*hh .. +7.  Rows past the last query are clamped (not stored).
   bf16x8 qf[NS];
   const int qrow = 32 * qh + l32;
+  {
+    const int qr = qrow < n_i ? qrow : n_i - 1;
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    qf[s] = (qrow < n_i) ? load8(qp + static_cast<int64_t>(kBlock * i + qrow) * sn + 16 * s + 8 * hh)
-                         : zero_bf16x8();
+    for (int s = 0; s < NS; ++s)
+      qf[s] = load8(qp + static_cast<int64_t>(kBlock * i + qr) * sn + 16 * s + 8 * hh);
+  }
 
   const int32_t* __restrict__ crow = A.crit + (static_cast<int64_t>(bh) * g.nq + i) * g.k_crit;
   const int kc = g.k_crit;
+  // The critical list is read once into registers, 64 entries per register
+  // (lane l holds entry base + l), and entries are taken with v_readlane, so
+  // the loop issues no index loads: a vector load there would make the
+  // compiler's vmcnt wait cover the in-flight K/V tile loads as well.
+  int cl0 = lane < kc ? crow[lane] : 0;
+  int cl1 = 64 + lane < kc ? crow[64 + lane] : 0;
+  int cbase = 0;
+  auto crit_at = [&](int c) -> int {
+    const int o = c - cbase;
+    return o < 64 ? __builtin_amdgcn_readlane(cl0, o) : __builtin_amdgcn_readlane(cl1, o - 64);
+  };
 
-  // staging registers for one block: K chunks and one V 4x8 sub-tile
-  bf16x8 kr[KPT];
-  bf16x8 vr[VPT][4];
+  // LDS ring: K buffers kbuf[2] and V buffers vbuf[2] (16 KB each at d=128).
+  // Iteration it reads K of block it+1 (for the next S) and V of block it;
+  // right after its barrier it issues K of block it+2 and V of block it+1
+  // straight into LDS (no staging registers), which land while it computes.
+  //
+  // Wave w fills rows 16w .. 16w+15 of a tile; lane l of instruction u writes
+  // row 16w + RPI*u + l/CH at chunk slot l%CH, which holds global chunk
+  // (l%CH) ^ swz(row).  Rows past the end of a short last block repeat its
+  // last row (those keys are masked to -inf in S).
+  const int lrow = lane / CH, lslot = lane % CH;
+  uint16_t* kbuf0 = smem;
+  uint16_t* vbuf0 = smem + 2 * TILE;
+  const uint32_t rowb = static_cast<uint32_t>(sn * sizeof(T));
+  uint32_t toff[IPW], tcol[IPW];
+#pragma unroll
+  for (int u = 0; u < IPW; ++u) {
+    const int r = 16 * wave + RPI * u + lrow;
+    tcol[u] = static_cast<uint32_t>(8 * (lslot ^ swz<D>(r)) * sizeof(T));
+    toff[u] = static_cast<uint32_t>(r) * rowb + tcol[u];
+  }
+  auto issue_tile = [&](const T* base, int c, uint16_t* dst) {
+    const int jb = crit_at(c);
+    const int nj = min(kBlock, g.N - kBlock * jb);
+    const T* tb = base + static_cast<int64_t>(kBlock * jb) * sn;
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      const int r0 = 16 * wave + RPI * u;
+      uint32_t off = toff[u];
+      if (nj < kBlock) {
+        const int r = r0 + lrow;
+        off = static_cast<uint32_t>(r < nj ? r : nj - 1) * rowb + tcol[u];
+      }
+      const T* src = reinterpret_cast<const T*>(reinterpret_cast<const char*>(tb) + off);
+      if constexpr (sizeof(T) == 2) {
+        load_lds16(src, dst + r0 * D);
+      } else {
+        *reinterpret_cast<bf16x8*>(dst + r0 * D + 8 * lane) = load8(src);
+      }
+    }
+  };
 
-#define SLA_LOAD_BLOCK(c_)                                                              \
-  do {                                                                                  \
-    const int jb_ = crow[(c_)];                                                         \
-    const int nj_ = min(kBlock, g.N - kBlock * jb_);                                    \
-    const T* kb_ = kp + static_cast<int64_t>(kBlock * jb_) * sn;                        \
-    const T* vb_ = vp + static_cast<int64_t>(kBlock * jb_) * sn;                        \
-    _Pragma("unroll") for (int u = 0; u < KPT; ++u) {                                   \
-      const int id = t + kThreads * u;                                                  \
-      const int row = id / CH, chk = id % CH;                                           \
-      kr[u] = (row < nj_) ? load8(kb_ + row * sn + 8 * chk) : zero_bf16x8();            \
-    }                                                                                   \
-    _Pragma("unroll") for (int u = 0; u < VPT; ++u) {                                   \
-      const int id = t + kThreads * u;                                                  \
-      const int grp = id % 16, chk = id / 16;                                           \
-      _Pragma("unroll") for (int x = 0; x < 4; ++x) {                                   \
-        const int row = 4 * grp + x;                                                    \
-        vr[u][x] = (id < VSUB && row < nj_) ? load8(vb_ + row * sn + 8 * chk)           \
-                                            : zero_bf16x8();                            \
-      }                                                                                 \
-    }                                                                                   \
-  } while (0)
+  // S^T of keys 32*kh .. +31 (of the block in kt) and queries 32*qh .. +31
+  const int krow = 32 * kh + l32;
+  const int ksw = swz<D>(krow);
+  auto qk = [&](const uint16_t* kt) {
+    bf16x8 kf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      kf[s] = *reinterpret_cast<const bf16x8*>(&kt[krow * D + 8 * ((2 * s + hh) ^ ksw)]);
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc = mfma32(kf[s], qf[s], acc);
+    return acc;
+  };
 
-#define SLA_STORE_BLOCK(buf_)                                                           \
-  do {                                                                                  \
-    uint16_t* kd_ = smem + (buf_) * BUF;                                                \
-    uint16_t* vd_ = kd_ + KT;                                                           \
-    _Pragma("unroll") for (int u = 0; u < KPT; ++u) {                                   \
-      const int id = t + kThreads * u;                                                  \
-      const int row = id / CH, chk = id % CH;                                           \
-      *reinterpret_cast<bf16x8*>(&kd_[row * KS + 8 * chk]) = kr[u];                     \
-    }                                                                                   \
-    _Pragma("unroll") for (int u = 0; u < VPT; ++u) {                                   \
-      const int id = t + kThreads * u;                                                  \
-      if (id < VSUB) {                                                                  \
-        const int grp = id % 16, chk = id / 16;                                         \
-        const int slot = vt_slot(grp);                                                  \
-        _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                 \
-          bf16x4 w4;                                                                    \
-          w4[0] = vr[u][0][e]; w4[1] = vr[u][1][e];                                     \
-          w4[2] = vr[u][2][e]; w4[3] = vr[u][3][e];                                     \
-          *reinterpret_cast<bf16x4*>(&vd_[(8 * chk + e) * VS + slot]) = w4;             \
-        }                                                                               \
-      }                                                                                 \
-    }                                                                                   \
-  } while (0)
+  // transposing V reads: source role of this lane within its 16-lane group
+  const int g16 = lane >> 4, li = lane & 15;
+  const int ep = li >> 2, q4 = li & 3, gm = g16 & 1;
+  const int key1 = 32 * kh + 4 * hh + ep;                 // + 16 s, and + 8 for the second read
+  const int sw1 = swz<D>(key1), sw2 = swz<D>(key1 + 8);   // independent of s (16 s keeps bits 0..3)
+  // byte offsets inside a V tile of the (s = 0) transposing reads for each
+  // 32-dim tile; s = 1 adds 16 rows
+  uint32_t vofs1[DT], vofs2[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int c = 4 * dt + 2 * gm + (q4 >> 1);
+    vofs1[dt] = static_cast<uint32_t>((key1 * D + 8 * (c ^ sw1) + 4 * (q4 & 1)) * 2);
+    vofs2[dt] = static_cast<uint32_t>(((key1 + 8) * D + 8 * (c ^ sw2) + 4 * (q4 & 1)) * 2);
+  }
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = zero16();
 
+  f32x16 s_cur = zero16();
   if (kc > 0) {
-    SLA_LOAD_BLOCK(0);
-    SLA_STORE_BLOCK(0);
-    if (kc > 1) SLA_LOAD_BLOCK(1);
+    issue_tile(kp, 0, kbuf0);
+    issue_tile(vp, 0, vbuf0);
+    if (kc > 1) issue_tile(kp, 1, kbuf0 + TILE);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    s_cur = qk(kbuf0);
   }
   for (int it = 0; it < kc; ++it) {
-    const int buf = it & 1;
-    const int jb = crow[it];
-    const int nj = min(kBlock, g.N - kBlock * jb);
-    const uint16_t* kt = smem + buf * BUF;
-    const uint16_t* vt = kt + KT;
+    const int cur = it & 1;
+    // K(it+2) -> kbuf[cur] (K(it) was read last iteration); V(it+1) -> vbuf[cur^1]
+    if (it + 2 < kc) issue_tile(kp, it + 2, kbuf0 + cur * TILE);
+    if (it + 1 < kc) issue_tile(vp, it + 1, vbuf0 + (cur ^ 1) * TILE);
+    // next S on the matrix cores while this block's softmax runs on the VALU
+    f32x16 s_next = zero16();
+    if (it + 1 < kc) s_next = qk(kbuf0 + (cur ^ 1) * TILE);
 
-    // S^T for keys 32*kh .. +31 and queries 32*qh .. +31
-    f32x16 sacc = zero16();
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[(32 * kh + l32) * KS + 16 * s + 8 * hh]);
-      sacc = mfma32(a, qf[s], sacc);
-    }
+    const int jb = crit_at(it);
+    const int nj = min(kBlock, g.N - kBlock * jb);
     if (nj < kBlock) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (key >= nj) sacc[r] = -INFINITY;
+        if (key >= nj) s_cur[r] = -INFINITY;
       }
     }
-    float mx = sacc[0];
+    float mx = s_cur[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
     mx = fmaxf(mx, xor_lane(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;   // all keys masked so far
-    const float corr = __builtin_amdgcn_exp2f((m_run - m_use) * cl);
-    const float mb = m_use * cl;
+    // The running reference max m_run only moves when some query's tile max
+    // exceeds it by more than kLazy (in log2 units), so p <= 2^kLazy and the
+    // output / sum rescale is skipped on most blocks; O and l always share
+    // the same reference, so the final O / l is unchanged.
+    const bool grow = __ballot((mx - m_run) * cl > kLazy) != 0ull;
+    if (grow) {
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * cl);
+      l_run *= corr;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
+      m_run = m_new;
+    }
+    const float mb = (m_run == -INFINITY ? 0.0f : m_run) * cl;
     float ps = 0.0f;
     bf16x8 pb[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], cl, -mb));
+      const float p = __builtin_amdgcn_exp2f(fmaf(s_cur[r], cl, -mb));
       ps += p;
       pb[r >> 3][r & 7] = f32_to_bf16(p);
     }
-    l_run = l_run * corr + ps;
-    m_run = m_new;
+    l_run += ps;
+
+    // O^T += V^T P^T; the V^T operand comes from the row-major V tile through
+    // transposing reads: lane l gets dim 32*dt + l%32 at keys
+    // 32*kh + 16*s + 8*(e/4) + 4*hh + e%4, matching P^T's k-slots.
+    // LDS byte address of this lane's first transposing read in the V tile
+    const uint32_t vt_addr = lds_addr(vbuf0 + cur * TILE);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vt[(32 * dt + l32) * VS + 32 * kh + 16 * s + 8 * hh]);
-        oacc[dt] = mfma32(a, pb[s], oacc[dt]);
-      }
+      u32x2 a0, a1, b0, b1;
+      // the 4 reads of one 32-dim tile and their wait sit in one asm block
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %4\n\t"
+          "ds_read_b64_tr_b16 %1, %5\n\t"
+          "ds_read_b64_tr_b16 %2, %4 offset:%6\n\t"
+          "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
+          : "v"(vt_addr + vofs1[dt]), "v"(vt_addr + vofs2[dt]), "i"(16 * D * 2)
+          : "memory");
+      u32x4 w0, w1;
+      w0[0] = a0[0]; w0[1] = a0[1]; w0[2] = a1[0]; w0[3] = a1[1];
+      w1[0] = b0[0]; w1[1] = b0[1]; w1[2] = b1[0]; w1[3] = b1[1];
+      oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, w0), pb[0], oacc[dt]);
+      oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, w1), pb[1], oacc[dt]);
     }
-
-    if (it + 1 < kc) {
-      SLA_STORE_BLOCK(buf ^ 1);          // block it+1 (its loads were issued last iteration)
-      if (it + 2 < kc) SLA_LOAD_BLOCK(it + 2);
+    s_cur = s_next;
+    if (it + 1 - cbase == 64) {            // entries it+1 .. it+64 now start at register 1
+      cbase += 64;
+      cl0 = cl1;
+      cl1 = cbase + 64 + lane < kc ? crow[cbase + 64 + lane] : 0;
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads for the next step
     __syncthreads();
   }
-#undef SLA_LOAD_BLOCK
-#undef SLA_STORE_BLOCK
+  __syncthreads();
 
   // ---- merge the two key halves; stage the linear-branch operands ----
-  float* mbuf = reinterpret_cast<float*>(smem);   // [4][32]
-  float* lbuf = mbuf + 128;                        // [4][32]
-  float* obuf = mbuf + 256;                        // [4][DTH][16][64]
+  float* mbuf = reinterpret_cast<float*>(smem_raw);   // [4][32]
+  float* lbuf = mbuf + 128;                            // [4][32]
+  float* obuf = mbuf + 256;                            // [4][DTH][16][64]
   const float l_full = l_run + xor_lane(l_run, 32);
   if (hh == 0) {
     mbuf[wave * 32 + l32] = m_run;
@@ -267,12 +328,12 @@ attention_kernel(AttnArgs A) {
     for (int r = 0; r < 16; ++r) obuf[((wave * DTH + u) * 16 + r) * 64 + lane] = o_oth[u][r];
 
   const bool has_lin = g.k_marg > 0;
-  uint16_t* st = smem + BUF;                                   // S_i^T [D][SS] (second buffer)
-  float* sg = reinterpret_cast<float*>(st + D * SS);           // sigma_i [D]
+  uint16_t* st = reinterpret_cast<uint16_t*>(smem_raw + MERGE_BYTES);   // S_i^T [D][SS]
+  float* sg = reinterpret_cast<float*>(st + D * SS);                      // sigma_i [D]
   if (has_lin) {
     const int64_t row = static_cast<int64_t>(bh) * g.nq + i;
     const uint16_t* sgl = A.s_sum + row * D * D;
-    for (int e = t; e < (D / 4) * CH; e += kThreads) {
+    for (int e = t; e < (D / 4) * (D / 8); e += kThreads) {
       const int ag = e % (D / 4), bc = e / (D / 4);
       bf16x8 w[4];
 #pragma unroll

@@ -61,6 +61,13 @@ __device__ __forceinline__ bf16x8 load8(const float* p) {
   return r;
 }
 
+// 8 consecutive elements at a 32-bit byte offset from a uniform base, so the
+// load can use the scalar-base + vector-offset addressing form.
+template <typename T>
+__device__ __forceinline__ bf16x8 load8_at(const T* base, uint32_t byte_off) {
+  return load8(reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off));
+}
+
 // 8 consecutive elements widened to float.
 __device__ __forceinline__ void load8_f32(const uint16_t* p, float* out) {
   const u32x4 w = *reinterpret_cast<const u32x4*>(p);
@@ -93,6 +100,28 @@ __device__ __forceinline__ f32x16 zero16() {
 #pragma unroll
   for (int i = 0; i < 16; ++i) r[i] = 0.0f;
   return r;
+}
+
+// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16 * l (lds_base must be uniform across the wave).
+__device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Transposing LDS read of 4 bf16 (gfx950 ds_read_b64_tr_b16): within each
+// group of 16 lanes, lane i receives element (i % 4) of the 8-byte rows
+// addressed by lanes 4e + i/4 of the group, for e = 0..3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// 32-bit LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) void*)(p)));
 }
 
 // Lane-crossing helpers (wave64).

@@ -89,209 +89,188 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 }
 
 // ---------------------------------------------------------------- selection
-// grid (ceil(nq / R), B*H).  Thread t owns KV blocks j = jj*256 + t for
-// jj < J, for each of the workgroup's R query blocks.
-template <int J, int R>
+// grid (ceil(nq / R), B*H), dynamic LDS: q rows [R][D] f64, keys [R][nkbp]
+// u64, per-wave histograms [4][256] u32.
+//
+// Phase 1 (whole workgroup): float64 logits of the R query blocks against
+// every KV block, thread t owning KV blocks j = t, t + 256, ... so each
+// pooled-K column read serves all R rows; stored as 64-bit descending keys.
+// Phase 2 (one wave per row, no further workgroup barriers): an 8-pass radix
+// select finds, for each of the two cut counts k_crit and k_crit + k_marg,
+// the key of the element at that rank and how many elements equal to it
+// fall inside the cut (equal keys are taken in ascending j); classes follow,
+// then ballot prefix counts compact each class in ascending j.
+
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int D>
 __global__ void __launch_bounds__(kThreads)
-select_kernel(Geometry g, const double* __restrict__ qpool, const double* __restrict__ kpool_t,
-              double sqrt_d, int32_t* __restrict__ crit, int32_t* __restrict__ marg,
-              int8_t* __restrict__ cls, float* __restrict__ logits_out) {
-  __shared__ double qs[R][128];
-  __shared__ uint32_t hist[R][2][256];
-  __shared__ uint64_t pref[R][2];
-  __shared__ uint32_t remk[R][2];
-  __shared__ uint32_t cnt[R][2][J][4];
+select_kernel(Geometry g, int R, int nkbp, const double* __restrict__ qpool,
+              const double* __restrict__ kpool_t, double sqrt_d, int32_t* __restrict__ crit,
+              int32_t* __restrict__ marg, int8_t* __restrict__ cls,
+              float* __restrict__ logits_out) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+  double* qs = reinterpret_cast<double*>(dyn);                       // [R][D]
+  uint64_t* keys = reinterpret_cast<uint64_t*>(qs + R * D);           // [R][nkbp]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(keys + R * nkbp);      // [4][256]
 
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * R;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int D = g.D, nq = g.nq, nkb = g.nkb;
-  const int target[2] = {g.k_crit, g.k_crit + g.k_marg};
+  const int nq = g.nq, nkb = g.nkb;
 
   for (int e = t; e < R * D; e += kThreads) {
     const int r = e / D, a = e % D;
     const int i = i0 + r;
-    qs[r][a] = (i < nq) ? qpool[(static_cast<int64_t>(bh) * nq + i) * D + a] : 0.0;
-  }
-  if (t < 2 * R) {
-    pref[t >> 1][t & 1] = 0ull;
-    remk[t >> 1][t & 1] = target[t & 1] > 0 ? static_cast<uint32_t>(target[t & 1] - 1) : 0u;
+    qs[e] = (i < nq) ? qpool[(static_cast<int64_t>(bh) * nq + i) * D + a] : 0.0;
   }
   __syncthreads();
 
-  uint64_t key[R][J];
+  // ---- phase 1: logits -> keys
   const double* kt = kpool_t + static_cast<int64_t>(bh) * D * nkb;
+  for (int j = t; j < nkbp; j += kThreads) {
+    if (j >= nkb) {
+      for (int r = 0; r < R; ++r) keys[r * nkbp + j] = ~0ull;
+      continue;
+    }
+    double acc[8];
 #pragma unroll
-  for (int jj = 0; jj < J; ++jj) {
-    const int j = jj * kThreads + t;
-    double acc[R];
+    for (int r = 0; r < 8; ++r) acc[r] = 0.0;
+#pragma unroll 1
+    for (int a0 = 0; a0 < D; a0 += 16) {
+      double kv[16];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0;
-    if (j < nkb) {
-      for (int a = 0; a < D; ++a) {
-        const double kv = kt[static_cast<int64_t>(a) * nkb + j];
+      for (int u = 0; u < 16; ++u) kv[u] = kt[static_cast<int64_t>(a0 + u) * nkb + j];
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = fma(qs[r][a], kv, acc[r]);
-      }
+      for (int u = 0; u < 16; ++u)
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          if (r < R) acc[r] = fma(qs[r * D + a0 + u], kv[u], acc[r]);
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const double s = acc[r] / sqrt_d;
-      const bool ok = (j < nkb) && (i0 + r < nq);
-      key[r][jj] = ok ? desc_key(s) : ~0ull;
+    for (int r = 0; r < 8; ++r) {
+      if (r >= R) break;
+      const double sv = acc[r] / sqrt_d;
+      const bool ok = i0 + r < nq;
+      keys[r * nkbp + j] = ok ? desc_key(sv) : ~0ull;
       if (ok && logits_out)
-        logits_out[(static_cast<int64_t>(bh) * nq + i0 + r) * nkb + j] = static_cast<float>(s);
+        logits_out[(static_cast<int64_t>(bh) * nq + i0 + r) * nkb + j] = static_cast<float>(sv);
     }
   }
+  __syncthreads();
 
-  // 8 radix passes of 8 bits, most significant first, for both targets.
-  // Lanes whose key matches the prefix so far are counted with one LDS
-  // atomic per distinct digit in the wave (early passes put most keys of a
-  // row in the same bin).
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    for (int e = t; e < R * 2 * 256; e += kThreads) (&hist[0][0][0])[e] = 0u;
-    __syncthreads();
+  // ---- phase 2: one wave per query block
+  uint32_t* wh = hist + wave * 256;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const int nu = nkbp / 64;
+  const int target[2] = {g.k_crit, g.k_crit + g.k_marg};
+  for (int r = wave; r < R; r += 4) {
+    const int i = i0 + r;
+    if (i >= nq) break;
+    const uint64_t* rk = keys + r * nkbp;
+    uint64_t pref[2] = {0ull, 0ull};
+    uint32_t rem[2] = {target[0] > 0 ? static_cast<uint32_t>(target[0] - 1) : 0u,
+                       target[1] > 0 ? static_cast<uint32_t>(target[1] - 1) : 0u};
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      // while both cuts share their prefix they share the histogram
+      const bool shared = pref[0] == pref[1];
+      for (int w = 0; w < (shared ? 1 : 2); ++w) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const uint64_t p = pref[r][w];
-#pragma unroll
-        for (int jj = 0; jj < J; ++jj) {
-          const uint64_t kk = key[r][jj];
-          const bool match = (pass == 0) || (((kk ^ p) >> (shift + 8)) == 0ull);
+        for (int x = 0; x < 4; ++x) wh[4 * lane + x] = 0u;
+        lds_wait();
+        for (int u = 0; u < nu; ++u) {
+          const uint64_t kk = rk[lane + 64 * u];
+          const bool match = (pass == 0) || (((kk ^ pref[w]) >> (shift + 8)) == 0ull);
           const uint32_t digit = static_cast<uint32_t>(kk >> shift) & 255u;
-          uint64_t active = __ballot(match);
-          while (active) {
-            const int leader = __builtin_ctzll(active);
-            const uint32_t d = __builtin_amdgcn_readlane(digit, leader);
-            const uint64_t same = __ballot(match && digit == d);
-            if (lane == leader) atomicAdd(&hist[r][w][d], static_cast<uint32_t>(__popcll(same)));
-            active &= ~same;
+          if (pass == 0) {
+            // the leading byte takes few values: one atomic per distinct digit
+            uint64_t active = __ballot(true);
+            while (active) {
+              const int leader = __builtin_ctzll(active);
+              const uint32_t dd = __builtin_amdgcn_readlane(digit, leader);
+              const uint64_t same = __ballot(digit == dd);
+              if (lane == leader) atomicAdd(&wh[dd], static_cast<uint32_t>(__popcll(same)));
+              active &= ~same;
+            }
+          } else if (match) {
+            atomicAdd(&wh[digit], 1u);
           }
         }
-      }
-    }
-    __syncthreads();
-    for (int pr = wave; pr < 2 * R; pr += 4) {
-      const int r = pr >> 1, w = pr & 1;
-      const uint32_t* hs = hist[r][w];
-      const uint32_t c0 = hs[4 * lane], c1 = hs[4 * lane + 1], c2 = hs[4 * lane + 2],
-                     c3 = hs[4 * lane + 3];
-      const uint32_t tot = c0 + c1 + c2 + c3;
-      const uint32_t incl = wave_incl_scan(tot, lane);
-      const uint32_t excl = incl - tot;
-      const uint32_t rem = remk[r][w];
-      if (rem >= excl && rem < incl) {
-        uint32_t cum = excl;
-        int bin = 4 * lane;
-        const uint32_t cs[4] = {c0, c1, c2, c3};
+        lds_wait();
+        const uint32_t c0 = wh[4 * lane], c1 = wh[4 * lane + 1], c2 = wh[4 * lane + 2],
+                       c3 = wh[4 * lane + 3];
+        const uint32_t tot = c0 + c1 + c2 + c3;
+        const uint32_t incl = wave_incl_scan(tot, lane);
+        const uint32_t excl = incl - tot;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (rem < cum + cs[u]) { bin = 4 * lane + u; break; }
-          cum += cs[u];
+        for (int ww = 0; ww < 2; ++ww) {
+          if (!shared && ww != w) continue;
+          const bool mine = rem[ww] >= excl && rem[ww] < incl;
+          uint32_t bin = 4u * lane, cum = excl;
+          if (mine) {
+            if (rem[ww] >= cum + c0) { cum += c0; ++bin;
+              if (rem[ww] >= cum + c1) { cum += c1; ++bin;
+                if (rem[ww] >= cum + c2) { cum += c2; ++bin; } } }
+          }
+          const uint64_t who = __ballot(mine);
+          const int src = __builtin_ctzll(who);
+          const uint32_t b_bin = __builtin_amdgcn_readlane(bin, src);
+          const uint32_t b_cum = __builtin_amdgcn_readlane(cum, src);
+          pref[ww] |= static_cast<uint64_t>(b_bin) << shift;
+          rem[ww] -= b_cum;
         }
-        pref[r][w] = pref[r][w] | (static_cast<uint64_t>(bin) << shift);
-        remk[r][w] = rem - cum;
+        lds_wait();
       }
     }
-    __syncthreads();
-  }
 
-  // Ties at a threshold: an element whose key equals the threshold key is in
-  // iff its rank among the equal keys (ascending j) is <= remk.  Ballots are
-  // recomputed after the barrier rather than kept live across it.
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int w = 0; w < 2; ++w)
-#pragma unroll
-      for (int jj = 0; jj < J; ++jj) {
-        const uint64_t bal = __ballot(key[r][jj] == pref[r][w]);
-        if (lane == 0) cnt[r][w][jj][wave] = static_cast<uint32_t>(__popcll(bal));
-      }
-  __syncthreads();
-  uint8_t cls_v[R][J];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    bool in_w[2][J];
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const uint64_t v = pref[r][w];
-      const uint32_t rk = remk[r][w];
-      uint32_t base = 0;
-#pragma unroll
-      for (int jj = 0; jj < J; ++jj) {
-        const uint64_t kk = key[r][jj];
-        const uint64_t bal = __ballot(kk == v);
-        uint32_t before = base;
-        for (int ww = 0; ww < wave; ++ww) before += cnt[r][w][jj][ww];
-        const uint32_t tie_rank = before + static_cast<uint32_t>(__popcll(bal & lt_mask));
-        in_w[w][jj] = target[w] > 0 && (kk < v || (kk == v && tie_rank <= rk));
-        base += cnt[r][w][jj][0] + cnt[r][w][jj][1] + cnt[r][w][jj][2] + cnt[r][w][jj][3];
-      }
-    }
-#pragma unroll
-    for (int jj = 0; jj < J; ++jj)
-      cls_v[r][jj] = in_w[0][jj] ? 2 : (in_w[1][jj] ? 1 : 0);
-  }
-  __syncthreads();   // cnt is reused below
-
-  // Compaction in ascending j: counts of critical / marginal per chunk and wave.
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int jj = 0; jj < J; ++jj) {
-      const bool ok = jj * kThreads + t < nkb;
-      const uint64_t b2 = __ballot(ok && cls_v[r][jj] == 2);
-      const uint64_t b1 = __ballot(ok && cls_v[r][jj] == 1);
-      if (lane == 0) {
-        cnt[r][0][jj][wave] = static_cast<uint32_t>(__popcll(b2));
-        cnt[r][1][jj][wave] = static_cast<uint32_t>(__popcll(b1));
-      }
-    }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int i = i0 + r;
-    if (i >= nq) continue;
+    // classes (equal keys ranked by ascending j) and compaction
     const int64_t row = static_cast<int64_t>(bh) * nq + i;
-    uint32_t base[2] = {0u, 0u};
-#pragma unroll
-    for (int jj = 0; jj < J; ++jj) {
-      const int j = jj * kThreads + t;
-      const bool ok = j < nkb;
-      const int c = cls_v[r][jj];
-      const uint64_t bal[2] = {__ballot(ok && c == 2), __ballot(ok && c == 1)};
-      uint32_t pos[2];
+    uint32_t eq_base[2] = {0u, 0u};
+    uint32_t out_base[2] = {0u, 0u};
+    for (int u = 0; u < nu; ++u) {
+      const int j = lane + 64 * u;
+      const uint64_t kk = rk[j];
+      bool in_w[2];
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        uint32_t before = base[w];
-        for (int ww = 0; ww < wave; ++ww) before += cnt[r][w][jj][ww];
-        pos[w] = before + static_cast<uint32_t>(__popcll(bal[w] & lt_mask));
-        base[w] += cnt[r][w][jj][0] + cnt[r][w][jj][1] + cnt[r][w][jj][2] + cnt[r][w][jj][3];
+        const uint64_t eqb = __ballot(kk == pref[w]);
+        const uint32_t tie_rank = eq_base[w] + static_cast<uint32_t>(__popcll(eqb & lt_mask));
+        in_w[w] = target[w] > 0 && (kk < pref[w] || (kk == pref[w] && tie_rank <= rem[w]));
+        eq_base[w] += static_cast<uint32_t>(__popcll(eqb));
       }
+      const bool ok = j < nkb;
+      const int c = !ok ? 0 : (in_w[0] ? 2 : (in_w[1] ? 1 : 0));
+      const uint64_t b2 = __ballot(c == 2);
+      const uint64_t b1 = __ballot(c == 1);
+      const uint32_t p2 = out_base[0] + static_cast<uint32_t>(__popcll(b2 & lt_mask));
+      const uint32_t p1 = out_base[1] + static_cast<uint32_t>(__popcll(b1 & lt_mask));
+      out_base[0] += static_cast<uint32_t>(__popcll(b2));
+      out_base[1] += static_cast<uint32_t>(__popcll(b1));
       if (ok) {
         if (cls) cls[row * nkb + j] = static_cast<int8_t>(c);
-        if (c == 2 && pos[0] < static_cast<uint32_t>(g.k_crit)) crit[row * g.k_crit + pos[0]] = j;
-        else if (c == 1 && pos[1] < static_cast<uint32_t>(g.k_marg)) marg[row * g.k_marg + pos[1]] = j;
+        if (c == 2 && p2 < static_cast<uint32_t>(g.k_crit)) crit[row * g.k_crit + p2] = j;
+        else if (c == 1 && p1 < static_cast<uint32_t>(g.k_marg)) marg[row * g.k_marg + p1] = j;
       }
     }
   }
 }
 
-constexpr int rows_for(int J) { return (32 / J) > 16 ? 16 : ((32 / J) < 1 ? 1 : 32 / J); }
-
-template <int J>
-hipError_t launch_select_j(const Geometry& g, const double* qpool, const double* kpool_t,
-                           int32_t* crit, int32_t* marg, int8_t* cls, float* logits,
-                           hipStream_t stream) {
-  constexpr int R = rows_for(J);
+hipError_t launch_select(const Geometry& g, const double* qpool, const double* kpool_t,
+                         int32_t* crit, int32_t* marg, int8_t* cls, float* logits,
+                         hipStream_t stream) {
+  const int nkbp = (g.nkb + 63) / 64 * 64;
+  int R = static_cast<int>(40960 / (static_cast<size_t>(nkbp) * 8));
+  R = R < 1 ? 1 : (R > 8 ? 8 : R);
+  const size_t lds = static_cast<size_t>(R) * g.D * 8 + static_cast<size_t>(R) * nkbp * 8 + 4 * 256 * 4;
   dim3 grid((g.nq + R - 1) / R, g.B * g.H);
-  hipLaunchKernelGGL((select_kernel<J, R>), grid, dim3(kThreads), 0, stream, g, qpool, kpool_t,
-                     __builtin_sqrt(static_cast<double>(g.D)), crit, marg, cls, logits);
+  const double sqrt_d = __builtin_sqrt(static_cast<double>(g.D));
+  if (g.D == 128)
+    hipLaunchKernelGGL((select_kernel<128>), grid, dim3(kThreads), lds, stream, g, R, nkbp, qpool,
+                       kpool_t, sqrt_d, crit, marg, cls, logits);
+  else
+    hipLaunchKernelGGL((select_kernel<64>), grid, dim3(kThreads), lds, stream, g, R, nkbp, qpool,
+                       kpool_t, sqrt_d, crit, marg, cls, logits);
   return hipGetLastError();
 }
 
@@ -318,13 +297,7 @@ hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int J = (g.nkb + kThreads - 1) / kThreads;
-  if (J <= 1) return launch_select_j<1>(g, ws_qpool, ws_kpool_t, crit, marg, cls, logits, stream);
-  if (J <= 2) return launch_select_j<2>(g, ws_qpool, ws_kpool_t, crit, marg, cls, logits, stream);
-  if (J <= 4) return launch_select_j<4>(g, ws_qpool, ws_kpool_t, crit, marg, cls, logits, stream);
-  if (J <= 8) return launch_select_j<8>(g, ws_qpool, ws_kpool_t, crit, marg, cls, logits, stream);
-  if (J <= 16) return launch_select_j<16>(g, ws_qpool, ws_kpool_t, crit, marg, cls, logits, stream);
-  return hipErrorInvalidValue;
+  return launch_select(g, ws_qpool, ws_kpool_t, crit, marg, cls, logits, stream);
 }
 
 }  // namespace sla
