@@ -9,7 +9,10 @@ Inputs are resident in HBM before timing starts.  Prints one JSON line.
 value     executed TFLOP/s of the whole step (executed FLOPs / step time)
 roofline  the attention kernel (the dominant one): executed FLOPs per launch
           divided by its mean duration from HIP events on the launch stream,
-          against the bf16 dense MFMA peak
+          against the dense MFMA peak of its dtype (bf16, or fp8 for the
+          video32k_fp8 workload, whose step also quantises Q, K and V)
+fp8_sparse_branch  (bf16 workloads with d = 128) the same step with the fp8
+          sparse branch, timed on the same inputs
 cpu_baseline  the fp64 numpy oracle timed on the host cores over a bounded
           sample of the same workload, scaled to the whole step
 
@@ -38,7 +41,11 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 ATTN_SOURCES = ["block_sparse_linear_route_amd/csrc/attention.hip",
+                "block_sparse_linear_route_amd/csrc/attention_epilogue.hpp",
                 "block_sparse_linear_route_amd/csrc/device_common.hpp"]
+ATTN_FP8_SOURCES = ["block_sparse_linear_route_amd/csrc/attention_fp8.hip",
+                    "block_sparse_linear_route_amd/csrc/attention_epilogue.hpp",
+                    "block_sparse_linear_route_amd/csrc/device_common.hpp"]
 
 
 def block_sizes(N: int):
@@ -79,7 +86,7 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, fp8: bool = False):
     """HBM traffic of the attention kernel from committed PMC summaries, if
     they were taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"attention_{workload}_traffic.json")
@@ -87,7 +94,7 @@ def load_traffic(workload: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256_16") != source_hash(ATTN_SOURCES):
+    if t.get("kernel_source_sha256_16") != source_hash(ATTN_FP8_SOURCES if fp8 else ATTN_SOURCES):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -148,45 +155,55 @@ def main():
     w = make_workload(args.workload)
     B, H, N, d = w.shape
     kc, km = w.k_crit, w.k_marg
+    fp8 = bool(CONFIGS[args.workload].get("fp8"))
     dev = torch.device("cuda:0")
     q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
     alpha = w.alpha.to(dev)
     ws = sla_gpu.forward_workspace(q, kc, km)
     torch.cuda.synchronize()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+    # Every op runs on torch's current stream, which the events below record
+    # on, so each event pair brackets exactly that op's kernels.
+    def step(ev=None, fp8_step=fp8):
+        def mark(n):
+            if ev is not None:
+                ev[n].record()
+        mark(0)
         r = sla_gpu.route(q, k, kc, km)
-        if ev is not None:
-            ev[1].record()
+        mark(1)
         Hs, zs = sla_gpu.linear_states(k, v)
-        if ev is not None:
-            ev[2].record()
+        mark(2)
+        if fp8_step:
+            (q8, qs), (k8, ks), (v8, vs) = (sla_gpu.quantize_fp8(x) for x in (q, k, v))
+        mark(3)
         sla_gpu.marginal_sums(q, r["marg_idx"], Hs, zs, ws, k_crit=kc)
-        if ev is not None:
-            ev[3].record()
-        o = sla_gpu.forward_attend(q, k, v, r["crit_idx"], alpha, ws, k_marg=km)
-        if ev is not None:
-            ev[4].record()
+        mark(4)
+        if fp8_step:
+            o = sla_gpu.forward_attend_fp8(q, q8, qs, k8, ks, v8, vs, r["crit_idx"], alpha, ws,
+                                           k_marg=km)
+        else:
+            o = sla_gpu.forward_attend(q, k, v, r["crit_idx"], alpha, ws, k_marg=km)
+        mark(5)
         return r, o
+
+    def timed(n_steps, fp8_step):
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n_steps):
+            r, o = step(events[i], fp8_step)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        parts = np.array([[events[i][p].elapsed_time(events[i][p + 1]) for p in range(5)]
+                          for i in range(n_steps)])
+        return r, (t1 - t0) * 1e3 / n_steps, parts.mean(axis=0)
 
     for _ in range(args.warmup):
         r, o = step()
     torch.cuda.synchronize()
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        r, o = step(events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    parts = np.array([[events[i][p].elapsed_time(events[i][p + 1]) for p in range(4)]
-                      for i in range(args.steps)])
-    route_ms, states_ms, msum_ms, attn_ms = parts.mean(axis=0)
-    fwd_ms = msum_ms + attn_ms
+    r, ms_step, parts = timed(args.steps, fp8)
+    route_ms, states_ms, quant_ms, msum_ms, attn_ms = parts
+    fwd_ms = quant_ms + msum_ms + attn_ms
 
     crit = r["crit_idx"].cpu().numpy()
     marg = r["marg_idx"].cpu().numpy()
@@ -196,6 +213,25 @@ def main():
     attn_flops = f_crit + f_lin
     achieved = attn_flops / (attn_ms * 1e-3) / 1e12
     dense_equiv = 4.0 * B * H * N * N * d
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+
+    fp8_variant = None
+    if not fp8 and d == 128 and w.q.dtype == torch.bfloat16:
+        # the fp8 sparse branch on the same inputs (reported beside the bf16 path)
+        for _ in range(2):
+            step(None, True)
+        _, ms8, parts8 = timed(max(3, args.steps // 2), True)
+        _, _, q8_ms, ms8_sum, ms8_attn = parts8
+        fwd8 = q8_ms + ms8_sum + ms8_attn
+        fp8_variant = {
+            "ms_per_step": ms8,
+            "forward_ms": fwd8,
+            "breakdown_ms": {"quantize_qkv": q8_ms, "marginal_sums": ms8_sum, "attention_fp8": ms8_attn},
+            "attention_fp8_tflops": attn_flops / (ms8_attn * 1e-3) / 1e12,
+            "attention_fp8_frac_fp8_peak": attn_flops / (ms8_attn * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+            "note": "sla_quantize_fp8 on Q, K, V, then marginal sums and the fp8 attention kernel; "
+                    "same routing, states and executed FLOPs as the bf16 step",
+        }
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * (1 << 20) // 4
@@ -217,10 +253,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 sparse branch, bf16/f32 rest" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: B={B} H={H} N={N} d={d} bf16, block 64, "
+            "workload": f"{args.workload}: B={B} H={H} N={N} d={d} bf16"
+                        + (" (E4M3 codes for the sparse branch)" if fp8 else "") + ", block 64, "
                         f"k_crit={kc} k_marg={km} of {(N + 63) // 64} KV blocks"
                         + (f", (t,y,x) grid {c['grid']}" if c.get("grid") else ""),
             "global_batch": B, "seq_len": N, "heads": H, "head_dim": d,
@@ -230,6 +267,7 @@ def main():
         "forward_tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
         "forward_frac_bf16_peak": f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "breakdown_ms": {"route": route_ms, "linear_states": states_ms,
+                         **({"quantize_qkv": quant_ms} if fp8 else {}),
                          "marginal_sums": msum_ms, "attention": attn_ms},
         "executed_gflop": {"step": f_step / 1e9, "forward": f_fwd / 1e9,
                            "critical_qk_pv": f_crit / 1e9, "linear_apply": f_lin / 1e9,
@@ -238,17 +276,20 @@ def main():
                              "note": "4 H N^2 d of full attention; its rate at the forward's time",
                              "tflops": dense_equiv / (fwd_ms * 1e-3) / 1e12},
         "roofline": {
-            "kernel": "attention_kernel (fused critical online-softmax + linear apply + mix)",
+            "kernel": ("attention_fp8_kernel (fp8 critical online-softmax + linear apply + mix)" if fp8
+                       else "attention_kernel (fused critical online-softmax + linear apply + mix)"),
             "bound": "mfma",
             "achieved": achieved,
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": load_traffic(args.workload),
+            "frac": achieved / peak,
+            "traffic": load_traffic(args.workload, fp8),
             "flops_per_launch": attn_flops,
             "mean_launch_ms": attn_ms,
         },
     }
+    if fp8_variant is not None:
+        out["fp8_sparse_branch"] = fp8_variant
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, kc, km, f_step, args.cpu_heads)
     print(json.dumps(out), flush=True)

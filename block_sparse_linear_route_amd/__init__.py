@@ -8,6 +8,7 @@ from .ops import (  # noqa: F401
     SlaError,
     forward,
     forward_attend,
+    forward_attend_fp8,
     forward_fp8,
     forward_workspace,
     linear_states,

@@ -51,6 +51,8 @@ SIGNATURES = {
     "sla_quantize_fp8": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp]),
     "sla_forward_fp8": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sla_forward_attend_fp8": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _vp, _vp, _vp, _vp, _sz, _vp]),
     "sla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sla_last_error_message": (ctypes.c_char_p, []),
     "sla_version": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int)] * 3),

@@ -328,11 +328,14 @@ int sla_quantize_fp8(const sla_problem* problem, const void* x, uint8_t* x_e4m3,
                   "sla_quantize_fp8 launch");
 }
 
-int sla_forward_fp8(const sla_problem* problem, const void* q, const uint8_t* q8, const float* q_s,
-                    const uint8_t* k8, const float* k_s, const uint8_t* v8, const float* v_s,
-                    const int32_t* crit_idx, const int32_t* marg_idx, const void* h_states,
-                    const float* z_states, const float* alpha, void* o, float* o_sparse,
-                    float* o_linear, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// Checks shared by the two fp8 forward entry points (everything but the
+// marginal-state arguments).
+int check_fp8_args(const sla_problem* problem, const void* q, const uint8_t* q8, const float* q_s,
+                   const uint8_t* k8, const float* k_s, const uint8_t* v8, const float* v_s,
+                   const int32_t* crit_idx, const float* alpha, void* o, float* o_sparse,
+                   float* o_linear) {
   SLA_TRY(validate_problem(problem));
   if (problem->dtype != SLA_BF16)
     return fail(SLA_ERR_UNSUPPORTED, "the fp8 forward takes bf16 Q and O");
@@ -348,13 +351,25 @@ int sla_forward_fp8(const sla_problem* problem, const void* q, const uint8_t* q8
   SLA_REQ(alpha, 4);
   SLA_REQ(o, 16);
   if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  SLA_OPT(o_sparse, 16);
+  SLA_OPT(o_linear, 16);
+  return SLA_OK;
+}
+
+}  // namespace
+
+int sla_forward_fp8(const sla_problem* problem, const void* q, const uint8_t* q8, const float* q_s,
+                    const uint8_t* k8, const float* k_s, const uint8_t* v8, const float* v_s,
+                    const int32_t* crit_idx, const int32_t* marg_idx, const void* h_states,
+                    const float* z_states, const float* alpha, void* o, float* o_sparse,
+                    float* o_linear, void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(check_fp8_args(problem, q, q8, q_s, k8, k_s, v8, v_s, crit_idx, alpha, o, o_sparse,
+                         o_linear));
   if (problem->k_marg > 0) {
     SLA_REQ(marg_idx, 4);
     SLA_REQ(h_states, 16);
     SLA_REQ(z_states, 16);
   }
-  SLA_OPT(o_sparse, 16);
-  SLA_OPT(o_linear, 16);
   const sla::Geometry g = geometry(problem);
   SLA_TRY(check_ws(ws, ws_bytes, forward_ws(g)));
   SLA_TRY(check_device());
@@ -366,6 +381,23 @@ int sla_forward_fp8(const sla_problem* problem, const void* q, const uint8_t* q8
                      "marginal-sum launch"));
   return launched(sla::launch_attention_fp8(g, q, q8, q_s, k8, k_s, v8, v_s, crit_idx, w.s_sum,
                                             w.sigma, alpha, o, o_sparse, o_linear, s),
+                  "fp8 attention launch");
+}
+
+int sla_forward_attend_fp8(const sla_problem* problem, const void* q, const uint8_t* q8,
+                           const float* q_s, const uint8_t* k8, const float* k_s,
+                           const uint8_t* v8, const float* v_s, const int32_t* crit_idx,
+                           const float* alpha, void* o, float* o_sparse, float* o_linear,
+                           const void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(check_fp8_args(problem, q, q8, q_s, k8, k_s, v8, v_s, crit_idx, alpha, o, o_sparse,
+                         o_linear));
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(const_cast<void*>(ws), ws_bytes, forward_ws(g)));
+  SLA_TRY(check_device());
+  const FwdWs w = carve_forward_ws(g, const_cast<void*>(ws));
+  return launched(sla::launch_attention_fp8(g, q, q8, q_s, k8, k_s, v8, v_s, crit_idx, w.s_sum,
+                                            w.sigma, alpha, o, o_sparse, o_linear,
+                                            static_cast<hipStream_t>(stream)),
                   "fp8 attention launch");
 }
 

@@ -9,26 +9,21 @@
 // One workgroup per (b, h, query block i), 4 waves: wave = qh + 2*kh, where
 // qh picks 32 of the 64 query rows and kh picks 32 of the 64 keys of every
 // gathered KV block.  Per critical block (one loop iteration):
-//   * the block's K tile [64 keys][d] and V^T tile [d][64 keys] sit in LDS
-//     (double-buffered: block t+1 is written while block t is consumed, and
-//     the global loads for block t+2 are in flight meanwhile);
+//   * the block's K and V tiles [64 keys][d] sit in LDS, row-major with a
+//     16-byte-chunk XOR swizzle; two K and two V buffers form a ring that the
+//     direct global->LDS loads for the next blocks fill while this one
+//     computes;
 //   * each wave computes S^T = K Q^T for its 32 keys x 32 queries on
 //     v_mfma_f32_32x32x16_bf16, runs the online-softmax update on the S^T
 //     registers (query = lane % 32, so a row max is a reduction over the
 //     lane's own registers plus the partner lane l ^ 32), and accumulates
-//     O^T += V^T P^T with P^T taken straight from the S^T registers;
-//   * the V^T tile stores keys in a permuted order (bits 2 and 3 of the key
-//     index swapped inside every 16-key group) so that the 8 keys a lane
-//     holds in P^T at each 16-key step are 8 consecutive LDS slots.
+//     O^T += V^T P^T with P^T taken straight from the S^T registers and the
+//     V^T operand read from the row-major V tile by transposing LDS reads
+//     (ds_read_b64_tr_b16).
 // The two key halves keep separate running max / sum / output (no per-block
-// cross-wave reduction) and are merged once through LDS at the end, each
-// wave finalising half of the d output dims.  The linear branch then
-// computes O_l^T = S_i^T phi(Q)^T / (phi(Q) . sigma_i) from the
-// marginal-state sum S_i precomputed by the marginal-sum kernel (phi(Q)
-// uses exp(q - max q); the row normaliser cancels), and the alpha mix is
-// stored.
-#include "device_common.hpp"
-#include "sla_internal.hpp"
+// cross-wave reduction); the shared epilogue merges them, adds the linear
+// branch from the precomputed marginal-state sums and stores the alpha mix.
+#include "attention_epilogue.hpp"
 
 namespace sla {
 namespace {
@@ -47,23 +42,6 @@ struct AttnArgs {
   Geometry g;
   float c_log2;      // log2(e) / sqrt(d)
 };
-
-__device__ __forceinline__ void store4(uint16_t* p, const float* x) {
-  u32x2 w;
-  w[0] = static_cast<uint32_t>(f32_to_bf16_bits(x[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(x[1])) << 16);
-  w[1] = static_cast<uint32_t>(f32_to_bf16_bits(x[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(x[3])) << 16);
-  *reinterpret_cast<u32x2*>(p) = w;
-}
-__device__ __forceinline__ void store4(float* p, const float* x) {
-  f32x4 w = {x[0], x[1], x[2], x[3]};
-  *reinterpret_cast<f32x4*>(p) = w;
-}
-
-// LDS slot of key 4*grp .. 4*grp+3 in a V^T row (bits 2 and 3 of the key
-// index swapped within each group of 16 keys).
-__device__ __forceinline__ int vt_slot(int grp) {
-  return 16 * (grp >> 2) + 8 * (grp & 1) + 4 * ((grp >> 1) & 1);
-}
 
 // XOR swizzle of the 16-byte chunks of a tile row: both the K-row operand
 // reads (16 consecutive rows, one chunk) and the transposing V reads (4
@@ -84,12 +62,9 @@ attention_kernel(AttnArgs A) {
   constexpr int IPW = (kBlock / 4) / RPI;      // load instructions per wave per tile
   constexpr int NS = D / 16;                   // 16-wide k-steps over the features
   constexpr int DT = D / 32;                   // 32-row tiles over the value dims
-  constexpr int DTH = DT / 2;                  // tiles each wave finalises
-  constexpr int SS = D + 8;                    // S^T row stride (linear branch)
-  constexpr int MERGE_BYTES = 4 * (256 + 4 * DTH * 16 * 64);
-  constexpr int ST_BYTES = D * SS * 2 + D * 4;
   constexpr int LOOP_BYTES = NSTAGE * TILE * 2;
-  constexpr int SMEM_BYTES = (LOOP_BYTES > MERGE_BYTES + ST_BYTES ? LOOP_BYTES : MERGE_BYTES + ST_BYTES);
+  constexpr int EPI_BYTES = epilogue_smem_bytes<D>();
+  constexpr int SMEM_BYTES = (LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES);
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM_BYTES];
   uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
 
@@ -304,123 +279,8 @@ attention_kernel(AttnArgs A) {
   }
   __syncthreads();
 
-  // ---- merge the two key halves; stage the linear-branch operands ----
-  float* mbuf = reinterpret_cast<float*>(smem_raw);   // [4][32]
-  float* lbuf = mbuf + 128;                            // [4][32]
-  float* obuf = mbuf + 256;                            // [4][DTH][16][64]
-  const float l_full = l_run + xor_lane(l_run, 32);
-  if (hh == 0) {
-    mbuf[wave * 32 + l32] = m_run;
-    lbuf[wave * 32 + l32] = l_full;
-  }
-  const int own0 = kh * DTH;
-  // the wave keeps dims [32*own0, +32*DTH); select with static indices so the
-  // accumulators stay in registers
-  f32x16 o_own[DTH], o_oth[DTH];
-#pragma unroll
-  for (int u = 0; u < DTH; ++u) {
-    o_own[u] = kh ? oacc[DTH + u] : oacc[u];
-    o_oth[u] = kh ? oacc[u] : oacc[DTH + u];
-  }
-#pragma unroll
-  for (int u = 0; u < DTH; ++u)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) obuf[((wave * DTH + u) * 16 + r) * 64 + lane] = o_oth[u][r];
-
-  const bool has_lin = g.k_marg > 0;
-  uint16_t* st = reinterpret_cast<uint16_t*>(smem_raw + MERGE_BYTES);   // S_i^T [D][SS]
-  float* sg = reinterpret_cast<float*>(st + D * SS);                      // sigma_i [D]
-  if (has_lin) {
-    const int64_t row = static_cast<int64_t>(bh) * g.nq + i;
-    const uint16_t* sgl = A.s_sum + row * D * D;
-    for (int e = t; e < (D / 4) * (D / 8); e += kThreads) {
-      const int ag = e % (D / 4), bc = e / (D / 4);
-      bf16x8 w[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) w[x] = load8(sgl + (4 * ag + x) * D + 8 * bc);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        bf16x4 p4;
-        p4[0] = w[0][x]; p4[1] = w[1][x]; p4[2] = w[2][x]; p4[3] = w[3][x];
-        *reinterpret_cast<bf16x4*>(&st[(8 * bc + x) * SS + 4 * ag]) = p4;
-      }
-    }
-    if (t < D) sg[t] = A.sigma_sum[row * D + t];
-  }
-  __syncthreads();
-
-  const int partner = wave ^ 2;
-  const float m_p = mbuf[partner * 32 + l32];
-  const float l_p = lbuf[partner * 32 + l32];
-  const float m_tot = fmaxf(m_run, m_p);
-  const float w_me = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_run - m_tot) * cl);
-  const float w_p = (m_p == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_p - m_tot) * cl);
-  const float den = l_full * w_me + l_p * w_p;
-  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  f32x16 os[DTH];
-#pragma unroll
-  for (int u = 0; u < DTH; ++u)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      os[u][r] = (o_own[u][r] * w_me + obuf[((partner * DTH + u) * 16 + r) * 64 + lane] * w_p) * inv;
-
-  f32x16 ol[DTH];
-#pragma unroll
-  for (int u = 0; u < DTH; ++u) ol[u] = zero16();
-  if (has_lin) {
-    float qmax = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, bf16v_to_f32(qf[s][e]));
-    qmax = fmaxf(qmax, xor_lane(qmax, 32));
-    float dpart = 0.0f;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      bf16x8 pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 pv = f32_to_bf16(__builtin_amdgcn_exp2f((bf16v_to_f32(qf[s][e]) - qmax) * kLog2e));
-        pf[e] = pv;
-        dpart += bf16v_to_f32(pv) * sg[16 * s + 8 * hh + e];
-      }
-#pragma unroll
-      for (int u = 0; u < DTH; ++u) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&st[(32 * (own0 + u) + l32) * SS + 16 * s + 8 * hh]);
-        ol[u] = mfma32(a, pf, ol[u]);
-      }
-    }
-    const float dsum = dpart + xor_lane(dpart, 32);
-    const float dinv = 1.0f / dsum;
-#pragma unroll
-    for (int u = 0; u < DTH; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ol[u][r] *= dinv;
-  }
-
-  // ---- alpha mix and store ----
-  const float al = A.alpha[h];
-  if (qrow < n_i) {
-    const int tok = kBlock * i + qrow;
-    T* orow = static_cast<T*>(A.o) + hoff + static_cast<int64_t>(tok) * sn;
-    const int64_t dbg = (static_cast<int64_t>(bh) * g.N + tok) * D;
-#pragma unroll
-    for (int u = 0; u < DTH; ++u)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int dim0 = 32 * (own0 + u) + 8 * r4 + 4 * hh;
-        float ov[4], sv[4], lv[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          sv[x] = os[u][4 * r4 + x];
-          lv[x] = ol[u][4 * r4 + x];
-          ov[x] = al * sv[x] + (1.0f - al) * lv[x];
-        }
-        store4(orow + dim0, ov);
-        if (A.o_sparse) store4(A.o_sparse + dbg + dim0, sv);
-        if (A.o_linear) store4(A.o_linear + dbg + dim0, lv);
-      }
-  }
+  attention_finish<T, D>(smem_raw, g, bh, h, i, n_i, qrow, hoff, A.s_sum, A.sigma_sum, A.alpha, A.o,
+                         A.o_sparse, A.o_linear, oacc, m_run, l_run, cl, qf);
 }
 
 template <typename T, int D>

@@ -1,0 +1,179 @@
+// Epilogue shared by the fused attention kernels (bf16 and fp8 sparse branch).
+//
+// Both kernels run 4 waves per (b, h, query block i), wave = qh + 2*kh: qh
+// picks 32 of the 64 query rows and kh one of two disjoint key subsets whose
+// online softmaxes ran separately.  Each wave arrives with the O^T tiles it
+// accumulated (lane = query, 32 dims per tile), its running reference max
+// m_run and its partial row sum l_run (this lane's keys only; the partner lane
+// l ^ 32 holds the rest of the row).  The epilogue
+//   * merges the two key subsets through LDS ([SLA2 technical summary,
+//     section 1 item 1]: the sparse softmax is renormalised over the kept keys
+//     only), each wave finalising half of the output dims;
+//   * computes the linear branch O_l = phi(Q) S_i / (phi(Q) . sigma_i) from
+//     the marginal-state sum S_i and sigma_i ([SLA2 summary, section 2.A];
+//     phi = softmax over the features, evaluated as exp(q - max q) because the
+//     row normaliser cancels between numerator and denominator);
+//   * mixes O = alpha_h O_s + (1 - alpha_h) O_l ([SLA2 summary, section 2.A
+//     equation]) and stores O, plus O_s / O_l when requested.
+// m_run is in the units of S; cl converts them to log2 units.
+#pragma once
+
+#include "device_common.hpp"
+#include "sla_internal.hpp"
+
+namespace sla {
+
+__device__ __forceinline__ void store4(uint16_t* p, const float* x) {
+  u32x2 w;
+  w[0] = static_cast<uint32_t>(f32_to_bf16_bits(x[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(x[1])) << 16);
+  w[1] = static_cast<uint32_t>(f32_to_bf16_bits(x[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(x[3])) << 16);
+  *reinterpret_cast<u32x2*>(p) = w;
+}
+__device__ __forceinline__ void store4(float* p, const float* x) {
+  f32x4 w = {x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<f32x4*>(p) = w;
+}
+
+// LDS bytes the epilogue needs at the start of the shared buffer.
+template <int D>
+constexpr int epilogue_smem_bytes() {
+  return 4 * (256 + 4 * (D / 64) * 16 * 64) + D * (D + 8) * 2 + D * 4;
+}
+
+// qf: bf16 Q fragments of query 32*qh + l32, features 16*s + 8*(lane/32) .. +7.
+template <typename T, int D>
+__device__ __forceinline__ void attention_finish(
+    unsigned char* smem_raw, const Geometry& g, int bh, int h, int i, int n_i, int qrow,
+    int64_t hoff, const uint16_t* __restrict__ s_sum, const float* __restrict__ sigma_sum,
+    const float* __restrict__ alpha, void* o, float* o_sparse, float* o_linear,
+    const f32x16 (&oacc)[D / 32], float m_run, float l_run, float cl, const bf16x8 (&qf)[D / 16]) {
+  constexpr int NS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int DTH = DT / 2;
+  constexpr int SS = D + 8;
+  constexpr int MERGE_BYTES = 4 * (256 + 4 * DTH * 16 * 64);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int kh = wave >> 1;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  // ---- merge the two key halves; stage the linear-branch operands ----
+  float* mbuf = reinterpret_cast<float*>(smem_raw);   // [4][32]
+  float* lbuf = mbuf + 128;                            // [4][32]
+  float* obuf = mbuf + 256;                            // [4][DTH][16][64]
+  const float l_full = l_run + xor_lane(l_run, 32);
+  if (hh == 0) {
+    mbuf[wave * 32 + l32] = m_run;
+    lbuf[wave * 32 + l32] = l_full;
+  }
+  const int own0 = kh * DTH;
+  // the wave keeps dims [32*own0, +32*DTH); select with static indices so the
+  // accumulators stay in registers
+  f32x16 o_own[DTH], o_oth[DTH];
+#pragma unroll
+  for (int u = 0; u < DTH; ++u) {
+    o_own[u] = kh ? oacc[DTH + u] : oacc[u];
+    o_oth[u] = kh ? oacc[u] : oacc[DTH + u];
+  }
+#pragma unroll
+  for (int u = 0; u < DTH; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) obuf[((wave * DTH + u) * 16 + r) * 64 + lane] = o_oth[u][r];
+
+  const bool has_lin = g.k_marg > 0;
+  uint16_t* st = reinterpret_cast<uint16_t*>(smem_raw + MERGE_BYTES);   // S_i^T [D][SS]
+  float* sg = reinterpret_cast<float*>(st + D * SS);                      // sigma_i [D]
+  if (has_lin) {
+    const int64_t row = static_cast<int64_t>(bh) * g.nq + i;
+    const uint16_t* sgl = s_sum + row * D * D;
+    for (int e = t; e < (D / 4) * (D / 8); e += kThreads) {
+      const int ag = e % (D / 4), bc = e / (D / 4);
+      bf16x8 w[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) w[x] = load8(sgl + (4 * ag + x) * D + 8 * bc);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        bf16x4 p4;
+        p4[0] = w[0][x]; p4[1] = w[1][x]; p4[2] = w[2][x]; p4[3] = w[3][x];
+        *reinterpret_cast<bf16x4*>(&st[(8 * bc + x) * SS + 4 * ag]) = p4;
+      }
+    }
+    if (t < D) sg[t] = sigma_sum[row * D + t];
+  }
+  __syncthreads();
+
+  const int partner = wave ^ 2;
+  const float m_p = mbuf[partner * 32 + l32];
+  const float l_p = lbuf[partner * 32 + l32];
+  const float m_tot = fmaxf(m_run, m_p);
+  const float w_me = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_run - m_tot) * cl);
+  const float w_p = (m_p == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_p - m_tot) * cl);
+  const float den = l_full * w_me + l_p * w_p;
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  f32x16 os[DTH];
+#pragma unroll
+  for (int u = 0; u < DTH; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      os[u][r] = (o_own[u][r] * w_me + obuf[((partner * DTH + u) * 16 + r) * 64 + lane] * w_p) * inv;
+
+  f32x16 ol[DTH];
+#pragma unroll
+  for (int u = 0; u < DTH; ++u) ol[u] = zero16();
+  if (has_lin) {
+    float qmax = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, bf16v_to_f32(qf[s][e]));
+    qmax = fmaxf(qmax, xor_lane(qmax, 32));
+    float dpart = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      bf16x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 pv = f32_to_bf16(__builtin_amdgcn_exp2f((bf16v_to_f32(qf[s][e]) - qmax) * kLog2e));
+        pf[e] = pv;
+        dpart += bf16v_to_f32(pv) * sg[16 * s + 8 * hh + e];
+      }
+#pragma unroll
+      for (int u = 0; u < DTH; ++u) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&st[(32 * (own0 + u) + l32) * SS + 16 * s + 8 * hh]);
+        ol[u] = mfma32(a, pf, ol[u]);
+      }
+    }
+    const float dsum = dpart + xor_lane(dpart, 32);
+    const float dinv = 1.0f / dsum;
+#pragma unroll
+    for (int u = 0; u < DTH; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ol[u][r] *= dinv;
+  }
+
+  // ---- alpha mix and store ----
+  const float al = alpha[h];
+  if (qrow < n_i) {
+    const int tok = kBlock * i + qrow;
+    T* orow = static_cast<T*>(o) + hoff + static_cast<int64_t>(tok) * g.sn;
+    const int64_t dbg = (static_cast<int64_t>(bh) * g.N + tok) * D;
+#pragma unroll
+    for (int u = 0; u < DTH; ++u)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dim0 = 32 * (own0 + u) + 8 * r4 + 4 * hh;
+        float ov[4], sv[4], lv[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          sv[x] = os[u][4 * r4 + x];
+          lv[x] = ol[u][4 * r4 + x];
+          ov[x] = al * sv[x] + (1.0f - al) * lv[x];
+        }
+        store4(orow + dim0, ov);
+        if (o_sparse) store4(o_sparse + dbg + dim0, sv);
+        if (o_linear) store4(o_linear + dbg + dim0, lv);
+      }
+  }
+}
+
+
+}  // namespace sla

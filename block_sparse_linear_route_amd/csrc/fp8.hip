@@ -107,11 +107,4 @@ hipError_t launch_quantize_fp8(const Geometry& g, const void* x, uint8_t* codes,
   return hipGetLastError();
 }
 
-hipError_t launch_attention_fp8(const Geometry&, const void*, const uint8_t*, const float*,
-                                const uint8_t*, const float*, const uint8_t*, const float*,
-                                const int32_t*, const uint16_t*, const float*, const float*,
-                                void*, float*, float*, hipStream_t) {
-  return hipErrorNotSupported;
-}
-
 }  // namespace sla

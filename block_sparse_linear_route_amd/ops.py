@@ -216,6 +216,26 @@ def forward_fp8(q, q8, q_s, k8, k_s, v8, v_s, crit_idx, marg_idx, h_states, z_st
     return (out, o_s, o_l) if branches else out
 
 
+def forward_attend_fp8(q, q8, q_s, k8, k_s, v8, v_s, crit_idx, alpha, workspace, *, k_marg: int,
+                       branches: bool = False, out=None, stream=None):
+    """Second phase of ``forward_fp8``: the fused fp8-sparse / linear attention
+    reading the marginal sums ``marginal_sums`` left in ``workspace``."""
+    kc = int(crit_idx.shape[-1])
+    p = make_problem(q, kc, k_marg)
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    o_s = o_l = None
+    if branches:
+        o_s = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        o_l = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    alpha = alpha.to(device=q.device, dtype=torch.float32).contiguous()
+    _check(lib.sla_forward_attend_fp8(ctypes.byref(p), _ptr(q), _ptr(q8), _ptr(q_s), _ptr(k8),
+                                      _ptr(k_s), _ptr(v8), _ptr(v_s), _ptr(crit_idx.contiguous()),
+                                      _ptr(alpha), _ptr(out), _ptr(o_s), _ptr(o_l),
+                                      _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (out, o_s, o_l) if branches else out
+
+
 def sla_attention(q, k, v, alpha, k_crit: int, k_marg: int, *, fp8: bool = False, stream=None):
     """Route + linear states + forward in one call (returns O)."""
     r = route(q, k, k_crit, k_marg, stream=stream)

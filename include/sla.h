@@ -197,8 +197,14 @@ int sla_quantize_fp8(const sla_problem* problem, const void* x, uint8_t* x_e4m3,
  * q          bf16/f32 input [B,H,N,d] (phi(Q) of the linear branch)
  * q8,k8,v8   uint8 [B,H,N,d] contiguous codes from sla_quantize_fp8
  * q_s,k_s,v_s float [B,H,nb] their scales
- * the remaining arguments as for sla_forward.  P is quantised per query
- * row of each KV tile with scale rowmax/448 before the PV product. */
+ * the remaining arguments as for sla_forward.
+ * The sparse branch computes S = (Q^ K^T) s_q s_k / sqrt(d) on fp8 matrix
+ * cores, keeps the online-softmax statistics and the row sum in float32, and
+ * quantises P per (query row, KV block): P s_v times a power of two 2^k that
+ * puts the row's largest entry in (224, 448] is rounded to E4M3 (nearest
+ * even) and the PV product is scaled back by 2^-k in the matrix core.  The
+ * linear branch and the alpha mix are those of sla_forward (bf16 / float32).
+ * Supported: bf16 Q and O, head_dim 128 (else SLA_ERR_UNSUPPORTED). */
 int sla_forward_fp8(const sla_problem* problem, const void* q,
                     const uint8_t* q8, const float* q_s, const uint8_t* k8,
                     const float* k_s, const uint8_t* v8, const float* v_s,
@@ -206,6 +212,18 @@ int sla_forward_fp8(const sla_problem* problem, const void* q,
                     const void* h_states, const float* z_states,
                     const float* alpha, void* o, float* o_sparse,
                     float* o_linear, void* ws, size_t ws_bytes, void* stream);
+
+/* Phase two of sla_forward_fp8, for callers that run sla_marginal_sums
+ * themselves (as sla_forward_attend is for sla_forward); ws holds that
+ * call's sums.  sla_forward_fp8 is exactly sla_marginal_sums followed by
+ * sla_forward_attend_fp8 on one stream.  [SLA2 summary 2.C] */
+int sla_forward_attend_fp8(const sla_problem* problem, const void* q,
+                           const uint8_t* q8, const float* q_s,
+                           const uint8_t* k8, const float* k_s,
+                           const uint8_t* v8, const float* v_s,
+                           const int32_t* crit_idx, const float* alpha, void* o,
+                           float* o_sparse, float* o_linear, const void* ws,
+                           size_t ws_bytes, void* stream);
 
 /* Host: static text of a status code. */
 const char* sla_status_string(int status);

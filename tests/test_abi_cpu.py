@@ -119,3 +119,15 @@ def test_entry_points_reject_bad_arguments_before_any_device_call():
     f32 = P(dtype=_lib.SLA_F32)
     st = lib.sla_forward_fp8(ctypes.byref(f32), *([fake] * 12), None, None, None, fake, 1 << 40, None)
     assert st == _lib.SLA_ERR_UNSUPPORTED
+    st = lib.sla_forward_attend_fp8(ctypes.byref(f32), *([fake] * 10), None, None, fake, 1 << 40,
+                                    None)
+    assert st == _lib.SLA_ERR_UNSUPPORTED            # fp32 Q / O
+    d64 = P(head_dim=64, stride_n=64)
+    st = lib.sla_forward_attend_fp8(ctypes.byref(d64), *([fake] * 10), None, None, fake, 1 << 40,
+                                    None)
+    assert st == _lib.SLA_ERR_UNSUPPORTED            # head_dim 64
+    st = lib.sla_forward_attend_fp8(ctypes.byref(p), fake, None, *([fake] * 8), None, None,
+                                    fake, 1 << 40, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT       # q8 missing
+    st = lib.sla_forward_attend_fp8(ctypes.byref(p), *([fake] * 10), None, None, fake, 16, None)
+    assert st == _lib.SLA_ERR_WORKSPACE

@@ -14,7 +14,7 @@ import torch
 
 from oracle import fp8 as ofp8
 from oracle import sla as ora
-from tests.parity_utils import (MAX_ABS_BF16, REL_L2_BF16, check_index_lists,
+from tests.parity_utils import (MAX_ABS_BF16, MAX_ABS_FP8, REL_L2_BF16, REL_L2_FP8, check_index_lists,
                                 classes_from_lists, compare_classes, max_abs, rel_l2, to64)
 from workloads import make_custom, make_workload
 
@@ -136,14 +136,33 @@ def test_states_parity(name, heads):
 
 # ------------------------------------------------------------------ forward
 
-def _forward_check(w, heads=None, n_sample=None, seed=0, tol_rel=REL_L2_BF16, tol_abs=MAX_ABS_BF16):
+def _deq(x32: np.ndarray) -> np.ndarray:
+    """One head's values after the CPU quantiser (bit-exact with the GPU's)."""
+    return ofp8.dequantize_blocks(*ofp8.quantize_blocks(x32))
+
+
+def _forward_check(w, heads=None, n_sample=None, seed=0, tol_rel=None, tol_abs=None, fp8=False,
+                   fp8_inputs=False):
+    """fp8: the sparse branch runs on E4M3 codes and is compared against the
+    unquantised float64 oracle with the fp8 tolerance.  fp8_inputs: the
+    oracle's sparse branch is fed the dequantised Q, K, V codes instead, so
+    only the kernel's own P quantisation and float32 arithmetic remain."""
     s = _s()
     q, k, v = _gpu(w)
     B, H, N, d = w.shape
     nb = ora.n_blocks(N)
+    if tol_rel is None:
+        tol_rel = REL_L2_FP8 if fp8 else REL_L2_BF16
+    if tol_abs is None:
+        tol_abs = MAX_ABS_FP8 if fp8 else MAX_ABS_BF16
     r = s.route(q, k, w.k_crit, w.k_marg)
     Hs, zs = s.linear_states(k, v)
-    o, o_s, o_l = s.forward(q, k, v, r["crit_idx"], r["marg_idx"], Hs, zs, w.alpha, branches=True)
+    if fp8:
+        (q8, qs), (k8, ks), (v8, vs) = (s.quantize_fp8(x) for x in (q, k, v))
+        o, o_s, o_l = s.forward_fp8(q, q8, qs, k8, ks, v8, vs, r["crit_idx"], r["marg_idx"], Hs, zs,
+                                    w.alpha, branches=True)
+    else:
+        o, o_s, o_l = s.forward(q, k, v, r["crit_idx"], r["marg_idx"], Hs, zs, w.alpha, branches=True)
     torch.cuda.synchronize()
     q64, k64, v64 = to64(w.q), to64(w.k), to64(w.v)
     heads = heads or [(b, h) for b in range(B) for h in range(H)]
@@ -161,6 +180,11 @@ def _forward_check(w, heads=None, n_sample=None, seed=0, tol_rel=REL_L2_BF16, to
         H64, z64 = ora.linear_states(k64[b, h], v64[b, h])
         ro, rs, rl = ora.forward_head(q64[b, h], k64[b, h], v64[b, h], crit, marg, H64, z64,
                                       float(w.alpha[h]), q_blocks=qb)
+        if fp8_inputs:
+            qd, kd, vd = (_deq(x[b, h].float().numpy()) for x in (w.q, w.k, w.v))
+            _, rs, _ = ora.forward_head(qd, kd, vd, crit, marg, H64, z64, float(w.alpha[h]),
+                                        q_blocks=qb)
+            ro = ora.mix(rs, rl, float(w.alpha[h]))
         rows = np.concatenate([np.arange(64 * i, min(64 * i + 64, N)) for i in qb])
         got["o"].append(og[b, h][rows]); ref["o"].append(ro[rows])
         got["s"].append(osg[b, h][rows]); ref["s"].append(rs[rows])
@@ -169,7 +193,7 @@ def _forward_check(w, heads=None, n_sample=None, seed=0, tol_rel=REL_L2_BF16, to
     for key in ("o", "s", "l"):
         a, bb = np.concatenate(got[key]), np.concatenate(ref[key])
         res[key] = (rel_l2(a, bb), max_abs(a, bb))
-    _say(f"[forward {w.name} N={N} d={d} kc={w.k_crit} km={w.k_marg} {w.q.dtype}] "
+    _say(f"[forward{' fp8' if fp8 else ''}{' vs dequantised inputs' if fp8_inputs else ''} {w.name} N={N} d={d} kc={w.k_crit} km={w.k_marg} {w.q.dtype}] "
          + " ".join(f"{k_}: relL2 {v_[0]:.2e} maxabs {v_[1]:.2e}" for k_, v_ in res.items()))
     for key in ("o", "s", "l"):
         if key == "s" and w.k_crit == 0 or key == "l" and w.k_marg == 0:
@@ -257,6 +281,50 @@ def test_forward_fuzz(seed):
                     kind="fourier1d", seed=200 + seed, k_crit=kc, k_marg=km)
     _route_check(w)
     _forward_check(w)
+
+
+# ------------------------------------------------------------------ fp8 sparse branch
+
+@pytest.mark.parametrize("name,heads,n_sample", [
+    ("seq8k", None, 24), ("video32k_fp8", [(0, 0), (0, 5), (0, 11)], 24)])
+def test_forward_fp8_parity(name, heads, n_sample):
+    w = make_workload(name)
+    _forward_check(w, heads=heads, n_sample=n_sample, fp8=True)
+    # the same blocks against the oracle on dequantised inputs: the P path alone
+    _forward_check(w, heads=heads[:1] if heads else [(0, 0)], n_sample=8, fp8=True, fp8_inputs=True)
+
+
+@pytest.mark.parametrize("N,kc,km,H,seed", [
+    (1000, 16, 0, 2, 40),        # all critical: dense softmax attention on fp8 codes
+    (1000, 0, 16, 2, 41),        # no critical block: linear branch only
+    (777, 5, 3, 1, 42),          # ragged tail block
+    (64, 1, 0, 1, 43),           # one block, one list half idle
+    (4095, 1, 20, 2, 44),
+    (4096, 7, 9, 1, 45),         # odd critical count: halves of 4 and 3
+    (300 * 64 + 17, 150, 10, 1, 46),   # half lists of 75 entries: register refill
+    (270 * 64, 260, 4, 1, 47),   # half lists of 130 entries: second refill
+])
+def test_forward_fp8_parity_shapes(N, kc, km, H, seed):
+    w = make_custom(1, H, N, 128, dtype="bf16", kind="fourier1d", seed=seed, k_crit=kc, k_marg=km)
+    nb = ora.n_blocks(N)
+    _forward_check(w, n_sample=None if nb <= 40 else 12, fp8=True, fp8_inputs=True)
+
+
+def test_forward_fp8_close_to_bf16_forward():
+    """Both sparse branches see the same routing; their outputs differ by the
+    quantisation error only."""
+    w = make_workload("seq8k")
+    s = _s()
+    q, k, v = _gpu(w)
+    r = s.route(q, k, w.k_crit, w.k_marg)
+    Hs, zs = s.linear_states(k, v)
+    o16 = s.forward(q, k, v, r["crit_idx"], r["marg_idx"], Hs, zs, w.alpha)
+    (q8, qs), (k8, ks), (v8, vs) = (s.quantize_fp8(x) for x in (q, k, v))
+    o8 = s.forward_fp8(q, q8, qs, k8, ks, v8, vs, r["crit_idx"], r["marg_idx"], Hs, zs, w.alpha)
+    torch.cuda.synchronize()
+    a, b = to64(o8), to64(o16)
+    _say(f"[fp8 vs bf16 seq8k] relL2 {rel_l2(a, b):.2e} maxabs {max_abs(a, b):.2e}")
+    assert rel_l2(a, b) < REL_L2_FP8
 
 
 # ------------------------------------------------------------------ fp8 quantiser
