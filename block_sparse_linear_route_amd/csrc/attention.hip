@@ -23,6 +23,8 @@
 // The two key halves keep separate running max / sum / output (no per-block
 // cross-wave reduction); the shared epilogue merges them, adds the linear
 // branch from the precomputed marginal-state sums and stores the alpha mix.
+#include <type_traits>
+
 #include "attention_epilogue.hpp"
 
 namespace sla {
@@ -69,7 +71,8 @@ attention_kernel(AttnArgs A) {
   uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
 
   const Geometry& g = A.g;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform (scalar)
   const int qh = wave & 1, kh = wave >> 1;
   const int l32 = lane & 31, hh = lane >> 5;
 
@@ -119,12 +122,15 @@ attention_kernel(AttnArgs A) {
   //
   // Wave w fills rows 16w .. 16w+15 of a tile; lane l of instruction u writes
   // row 16w + RPI*u + l/CH at chunk slot l%CH, which holds global chunk
-  // (l%CH) ^ swz(row).  Rows past the end of a short last block repeat its
-  // last row (those keys are masked to -inf in S).
+  // (l%CH) ^ swz(row).  bf16 tiles come through a range-checked buffer
+  // resource ending at the last token's row, so rows past the end of a short
+  // last block read as zeros (their keys are masked to -inf in S); float
+  // tiles are converted in registers with the row index clamped instead.
   const int lrow = lane / CH, lslot = lane % CH;
-  uint16_t* kbuf0 = smem;
-  uint16_t* vbuf0 = smem + 2 * TILE;
   const uint32_t rowb = static_cast<uint32_t>(sn * sizeof(T));
+  const uint32_t head_bytes = static_cast<uint32_t>((g.N - 1) * sn * sizeof(T) + D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, head_bytes);
   uint32_t toff[IPW], tcol[IPW];
 #pragma unroll
   for (int u = 0; u < IPW; ++u) {
@@ -132,54 +138,57 @@ attention_kernel(AttnArgs A) {
     tcol[u] = static_cast<uint32_t>(8 * (lslot ^ swz<D>(r)) * sizeof(T));
     toff[u] = static_cast<uint32_t>(r) * rowb + tcol[u];
   }
-  auto issue_tile = [&](const T* base, int c, uint16_t* dst) {
+  auto issue_tile = [&](bool is_k, int c, uint16_t* dst) {
     const int jb = crit_at(c);
-    const int nj = min(kBlock, g.N - kBlock * jb);
-    const T* tb = base + static_cast<int64_t>(kBlock * jb) * sn;
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t soff = static_cast<uint32_t>(kBlock * jb) * rowb;
 #pragma unroll
-    for (int u = 0; u < IPW; ++u) {
-      const int r0 = 16 * wave + RPI * u;
-      uint32_t off = toff[u];
-      if (nj < kBlock) {
+      for (int u = 0; u < IPW; ++u)
+        buffer_load_lds16(is_k ? krs : vrs, dst + (16 * wave + RPI * u) * D, toff[u], soff);
+    } else {
+      const int nj = min(kBlock, g.N - kBlock * jb);
+      const T* tb = (is_k ? kp : vp) + static_cast<int64_t>(kBlock * jb) * sn;
+#pragma unroll
+      for (int u = 0; u < IPW; ++u) {
+        const int r0 = 16 * wave + RPI * u;
         const int r = r0 + lrow;
-        off = static_cast<uint32_t>(r < nj ? r : nj - 1) * rowb + tcol[u];
-      }
-      const T* src = reinterpret_cast<const T*>(reinterpret_cast<const char*>(tb) + off);
-      if constexpr (sizeof(T) == 2) {
-        load_lds16(src, dst + r0 * D);
-      } else {
+        const uint32_t off = static_cast<uint32_t>(r < nj ? r : nj - 1) * rowb + tcol[u];
+        const T* src = reinterpret_cast<const T*>(reinterpret_cast<const char*>(tb) + off);
         *reinterpret_cast<bf16x8*>(dst + r0 * D + 8 * lane) = load8(src);
       }
     }
   };
 
-  // S^T of keys 32*kh .. +31 (of the block in kt) and queries 32*qh .. +31
+  // K operand rows: S^T of keys 32*kh .. +31 (of a K tile) and queries
+  // 32*qh .. +31; element offsets of the 8 feature chunks (loop-invariant).
   const int krow = 32 * kh + l32;
   const int ksw = swz<D>(krow);
-  auto qk = [&](const uint16_t* kt) {
-    bf16x8 kf[NS];
+  int kofs[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      kf[s] = *reinterpret_cast<const bf16x8*>(&kt[krow * D + 8 * ((2 * s + hh) ^ ksw)]);
-    f32x16 acc = zero16();
-#pragma unroll
-    for (int s = 0; s < NS; ++s) acc = mfma32(kf[s], qf[s], acc);
-    return acc;
-  };
+  for (int s = 0; s < NS; ++s) kofs[s] = krow * D + 8 * ((2 * s + hh) ^ ksw);
 
-  // transposing V reads: source role of this lane within its 16-lane group
+  // Transposing V reads (ds_read_b64_tr_b16): within each 16-lane group,
+  // output lane i receives element i % 4 of the 8-byte rows addressed by
+  // lanes 4e + i / 4 (e = 0..3).  This lane addresses key
+  // 32*kh + 16*s + 8*x + 4*hh + ep (x = 0, 1 for the two reads of a k-step)
+  // at the 4 dims from 32*dt + 16*gm + 4*q4, so that output lane l gets dim
+  // 32*dt + l % 32 at the keys its P^T k-slots hold.
   const int g16 = lane >> 4, li = lane & 15;
   const int ep = li >> 2, q4 = li & 3, gm = g16 & 1;
   const int key1 = 32 * kh + 4 * hh + ep;                 // + 16 s, and + 8 for the second read
   const int sw1 = swz<D>(key1), sw2 = swz<D>(key1 + 8);   // independent of s (16 s keeps bits 0..3)
-  // byte offsets inside a V tile of the (s = 0) transposing reads for each
-  // 32-dim tile; s = 1 adds 16 rows
-  uint32_t vofs1[DT], vofs2[DT];
+  // LDS byte addresses of the (s = 0) reads for each 32-dim tile, relative
+  // to the start of the tile area; the V buffer and s = 1 (+16 rows) are
+  // immediate offsets
+  uint32_t va1[DT], va2[DT];
+  {
+    const uint32_t base = lds_addr(smem);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const int c = 4 * dt + 2 * gm + (q4 >> 1);
-    vofs1[dt] = static_cast<uint32_t>((key1 * D + 8 * (c ^ sw1) + 4 * (q4 & 1)) * 2);
-    vofs2[dt] = static_cast<uint32_t>(((key1 + 8) * D + 8 * (c ^ sw2) + 4 * (q4 & 1)) * 2);
+    for (int dt = 0; dt < DT; ++dt) {
+      const int c = 4 * dt + 2 * gm + (q4 >> 1);
+      va1[dt] = base + static_cast<uint32_t>((key1 * D + 8 * (c ^ sw1) + 4 * (q4 & 1)) * 2);
+      va2[dt] = base + static_cast<uint32_t>(((key1 + 8) * D + 8 * (c ^ sw2) + 4 * (q4 & 1)) * 2);
+    }
   }
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -187,23 +196,25 @@ attention_kernel(AttnArgs A) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = zero16();
 
-  f32x16 s_cur = zero16();
-  if (kc > 0) {
-    issue_tile(kp, 0, kbuf0);
-    issue_tile(vp, 0, vbuf0);
-    if (kc > 1) issue_tile(kp, 1, kbuf0 + TILE);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    s_cur = qk(kbuf0);
-  }
-  for (int it = 0; it < kc; ++it) {
-    const int cur = it & 1;
-    // K(it+2) -> kbuf[cur] (K(it) was read last iteration); V(it+1) -> vbuf[cur^1]
-    if (it + 2 < kc) issue_tile(kp, it + 2, kbuf0 + cur * TILE);
-    if (it + 1 < kc) issue_tile(vp, it + 1, vbuf0 + (cur ^ 1) * TILE);
-    // next S on the matrix cores while this block's softmax runs on the VALU
-    f32x16 s_next = zero16();
-    if (it + 1 < kc) s_next = qk(kbuf0 + (cur ^ 1) * TILE);
+  // One critical block per step.  Step it (buffer parity X = it & 1) finds
+  // K(it+1) in kbuf[X^1] and V(it) in vbuf[X], sends K(it+2) into kbuf[X]
+  // and V(it+1) into vbuf[X^1], computes S(it+1) (from a stale but
+  // in-bounds buffer when there is no block it+1; the result is dropped)
+  // while the softmax of S(it) runs, then adds P V(it).
+  auto step = [&](auto xc, int it, f32x16& s_cur, f32x16& s_next) {
+    constexpr int X = decltype(xc)::value;
+    const uint16_t* kb_next = smem + (X ^ 1) * TILE;
+    // K fragments first: no direct-to-LDS load of this wave is in flight yet
+    // (the previous step ended with vmcnt(0)), so these reads need no wait
+    // on the loads issued right after them.
+    bf16x8 kf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kb_next + kofs[s]);
+    if (it + 2 < kc) issue_tile(true, it + 2, smem + X * TILE);
+    if (it + 1 < kc) issue_tile(false, it + 1, smem + (2 + (X ^ 1)) * TILE);
+    f32x16 acc = zero16();
+    acc = mfma32(kf[0], qf[0], acc);
+    acc = mfma32(kf[1], qf[1], acc);
 
     const int jb = crit_at(it);
     const int nj = min(kBlock, g.N - kBlock * jb);
@@ -214,10 +225,14 @@ attention_kernel(AttnArgs A) {
         if (key >= nj) s_cur[r] = -INFINITY;
       }
     }
-    float mx = s_cur[0];
+    float mx = fmaxf(s_cur[0], s_cur[1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
-    mx = fmaxf(mx, xor_lane(mx, 32));
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[r], s_cur[r + 1]));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // with lane l ^ 32
+    }
     // The running reference max m_run only moves when some query's tile max
     // exceeds it by more than kLazy (in log2 units), so p <= 2^kLazy and the
     // output / sum rescale is skipped on most blocks; O and l always share
@@ -233,9 +248,12 @@ attention_kernel(AttnArgs A) {
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= corr;
       m_run = m_new;
     }
+#pragma unroll
+    for (int s = 2; s < NS; ++s) acc = mfma32(kf[s], qf[s], acc);
+
     const float mb = (m_run == -INFINITY ? 0.0f : m_run) * cl;
-    float ps = 0.0f;
     bf16x8 pb[2];
+    float ps = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = __builtin_amdgcn_exp2f(fmaf(s_cur[r], cl, -mb));
@@ -243,39 +261,92 @@ attention_kernel(AttnArgs A) {
       pb[r >> 3][r & 7] = f32_to_bf16(p);
     }
     l_run += ps;
+    s_next = acc;
 
-    // O^T += V^T P^T; the V^T operand comes from the row-major V tile through
-    // transposing reads: lane l gets dim 32*dt + l%32 at keys
-    // 32*kh + 16*s + 8*(e/4) + 4*hh + e%4, matching P^T's k-slots.
-    // LDS byte address of this lane's first transposing read in the V tile
-    const uint32_t vt_addr = lds_addr(vbuf0 + cur * TILE);
+    // O^T += V^T P^T: lane l gets dim 32*dt + l%32 at keys
+    // 32*kh + 16*s + 8*(e/4) + 4*hh + e%4, matching P^T's k-slots.  All 16
+    // transposing reads and their wait sit in one asm block.
+    constexpr int VOFF0 = (2 + X) * TILE * 2;
+    constexpr int VOFF1 = VOFF0 + 16 * D * 2;
+    u32x2 rd[4 * DT];
+    if constexpr (DT == 4) {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %2, %16 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %3, %17 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %4, %18 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %5, %19 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %6, %18 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %7, %19 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %9, %21 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %10, %20 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %11, %21 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %12, %22 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %13, %23 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(rd[0]), "=&v"(rd[1]), "=&v"(rd[2]), "=&v"(rd[3]), "=&v"(rd[4]), "=&v"(rd[5]),
+            "=&v"(rd[6]), "=&v"(rd[7]), "=&v"(rd[8]), "=&v"(rd[9]), "=&v"(rd[10]), "=&v"(rd[11]),
+            "=&v"(rd[12]), "=&v"(rd[13]), "=&v"(rd[14]), "=&v"(rd[15])
+          : "v"(va1[0]), "v"(va2[0]), "v"(va1[1]), "v"(va2[1]), "v"(va1[2]), "v"(va2[2]),
+            "v"(va1[3]), "v"(va2[3]), "i"(VOFF0), "i"(VOFF1)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %2, %8 offset:%13\n\t"
+          "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+          "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %5, %11 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
+          "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(rd[0]), "=&v"(rd[1]), "=&v"(rd[2]), "=&v"(rd[3]), "=&v"(rd[4]), "=&v"(rd[5]),
+            "=&v"(rd[6]), "=&v"(rd[7])
+          : "v"(va1[0]), "v"(va2[0]), "v"(va1[1]), "v"(va2[1]), "i"(VOFF0), "i"(VOFF1)
+          : "memory");
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      u32x2 a0, a1, b0, b1;
-      // the 4 reads of one 32-dim tile and their wait sit in one asm block
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %4\n\t"
-          "ds_read_b64_tr_b16 %1, %5\n\t"
-          "ds_read_b64_tr_b16 %2, %4 offset:%6\n\t"
-          "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
-          : "v"(vt_addr + vofs1[dt]), "v"(vt_addr + vofs2[dt]), "i"(16 * D * 2)
-          : "memory");
       u32x4 w0, w1;
-      w0[0] = a0[0]; w0[1] = a0[1]; w0[2] = a1[0]; w0[3] = a1[1];
-      w1[0] = b0[0]; w1[1] = b0[1]; w1[2] = b1[0]; w1[3] = b1[1];
+      w0[0] = rd[4 * dt][0]; w0[1] = rd[4 * dt][1]; w0[2] = rd[4 * dt + 1][0]; w0[3] = rd[4 * dt + 1][1];
+      w1[0] = rd[4 * dt + 2][0]; w1[1] = rd[4 * dt + 2][1]; w1[2] = rd[4 * dt + 3][0]; w1[3] = rd[4 * dt + 3][1];
       oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, w0), pb[0], oacc[dt]);
       oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, w1), pb[1], oacc[dt]);
     }
-    s_cur = s_next;
     if (it + 1 - cbase == 64) {            // entries it+1 .. it+64 now start at register 1
       cbase += 64;
       cl0 = cl1;
       cl1 = cbase + 64 + lane < kc ? crow[cbase + 64 + lane] : 0;
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads for the next step
+    wait_vmem();   // this wave's loads for the next step
     __syncthreads();
+  };
+
+  // Q fragments and the critical list are in registers before the loop; a
+  // wait the compiler can see keeps it from guarding their first uses inside
+  // the loop with waits that would then also stall on the tile prefetches.
+  wait_vmem();
+  f32x16 sa = zero16(), sb = zero16();
+  if (kc > 0) {
+    issue_tile(true, 0, smem);
+    issue_tile(false, 0, smem + 2 * TILE);
+    if (kc > 1) issue_tile(true, 1, smem + TILE);
+    wait_vmem();
+    __syncthreads();
+    bf16x8 kf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(smem + kofs[s]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sa = mfma32(kf[s], qf[s], sa);
+  }
+  for (int it = 0; it < kc; it += 2) {
+    step(std::integral_constant<int, 0>(), it, sa, sb);
+    if (it + 1 < kc) step(std::integral_constant<int, 1>(), it + 1, sb, sa);
   }
   __syncthreads();
 

@@ -225,7 +225,7 @@ attention_fp8_kernel(AttnFp8Args A) {
     issue_tile(v8p, 0, hbase + 2 * TB);
     if (nh > 1) issue_tile(k8p, 1, hbase + TB);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_vmem();
   __syncthreads();
   if (nh > 0) qk(hbase, s_cur);
 
@@ -324,7 +324,7 @@ attention_fp8_kernel(AttnFp8Args A) {
       ej1 = ebase + 64 + lane < nh ? crow[lh + 2 * (ebase + 64 + lane)] : 0;
       load_scales();
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmem();
     __syncthreads();
   }
 

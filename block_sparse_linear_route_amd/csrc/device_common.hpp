@@ -19,6 +19,7 @@ namespace sla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -106,6 +107,28 @@ __device__ __forceinline__ f32x16 zero16() {
 // lds_base + 16 * l (lds_base must be uniform across the wave).
 __device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Wait until all of this wave's vector-memory loads (including direct-to-LDS
+// loads) have completed.  Issued through the builtin, not inline asm, so the
+// compiler's own wait-count tracking knows that nothing is outstanding after
+// it (s_waitcnt vmcnt(0) with the other counters left at their maximum).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Buffer resource over [base, base + bytes): raw (unstructured) loads through
+// it are range-checked per dword, and dwords past the end read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// Range-checked direct buffer -> LDS load of 16 bytes per lane from byte
+// offset voff + soff: lane l's bytes land at lds_base + 16 * l (lds_base
+// uniform across the wave).
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base,
+                                                  uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                           voff, soff, 0, 0);
 }
 
 // Transposing LDS read of 4 bf16 (gfx950 ds_read_b64_tr_b16): within each
