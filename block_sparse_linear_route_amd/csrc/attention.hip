@@ -45,15 +45,6 @@ struct AttnArgs {
   float c_log2;      // log2(e) / sqrt(d)
 };
 
-// XOR swizzle of the 16-byte chunks of a tile row: both the K-row operand
-// reads (16 consecutive rows, one chunk) and the transposing V reads (4
-// consecutive keys x 4 chunks) hit distinct LDS banks.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
-  else return (r >> 1) & 7;
-}
-
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads, 2)
 attention_kernel(AttnArgs A) {
@@ -66,7 +57,11 @@ attention_kernel(AttnArgs A) {
   constexpr int DT = D / 32;                   // 32-row tiles over the value dims
   constexpr int LOOP_BYTES = NSTAGE * TILE * 2;
   constexpr int EPI_BYTES = epilogue_smem_bytes<D>();
-  constexpr int SMEM_BYTES = (LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES);
+  // d = 128: the last two steps prefetch S_i^T into the two K buffers, so the
+  // merge buffers start at the V buffers; d = 64 reads S_i^T from HBM.
+  constexpr bool ST_LDS = (D == 128);
+  constexpr int EPI_OFF = ST_LDS ? 2 * TILE * 2 : 0;
+  constexpr int SMEM_BYTES = (LOOP_BYTES > EPI_OFF + EPI_BYTES ? LOOP_BYTES : EPI_OFF + EPI_BYTES);
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM_BYTES];
   uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
 
@@ -159,6 +154,21 @@ attention_kernel(AttnArgs A) {
     }
   };
 
+  // S_i^T (value-major, D rows x D) halves: rows 64*half .. +63 as a
+  // swizzled tile, same pattern as a K tile (contiguous rows of D bf16)
+  const bool has_lin = g.k_marg > 0;
+  const __amdgpu_buffer_rsrc_t srs =
+      make_rsrc(A.s_sum + (static_cast<int64_t>(bh) * g.nq + i) * D * D, D * D * 2);
+  auto issue_st = [&](int half, uint16_t* dst) {
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      const int r = 16 * wave + RPI * u + lrow;
+      const uint32_t off = static_cast<uint32_t>(r * D * 2 + 16 * (lslot ^ swz<D>(r)));
+      buffer_load_lds16(srs, dst + (16 * wave + RPI * u) * D, off,
+                        static_cast<uint32_t>(half * kBlock * D * 2));
+    }
+  };
+
   // K operand rows: S^T of keys 32*kh .. +31 (of a K tile) and queries
   // 32*qh .. +31; element offsets of the 8 feature chunks (loop-invariant).
   const int krow = 32 * kh + l32;
@@ -210,7 +220,21 @@ attention_kernel(AttnArgs A) {
     bf16x8 kf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kb_next + kofs[s]);
-    if (it + 2 < kc) issue_tile(true, it + 2, smem + X * TILE);
+    if (it + 2 < kc) {
+      issue_tile(true, it + 2, smem + X * TILE);
+    } else if constexpr (ST_LDS) {
+      // kbuf[X] (K(it), consumed last step) stays free: S_i^T half 0 goes in
+      // at step kc-2, half 1 at step kc-1 (both at step 0 when kc = 1), so
+      // half 0 ends in kbuf[kc & 1] and half 1 in kbuf[(kc & 1) ^ 1]
+      if (has_lin) {
+        if (it == kc - 2) {
+          issue_st(0, smem + X * TILE);
+        } else {
+          issue_st(1, smem + X * TILE);
+          if (kc == 1) issue_st(0, smem + (X ^ 1) * TILE);
+        }
+      }
+    }
     if (it + 1 < kc) issue_tile(false, it + 1, smem + (2 + (X ^ 1)) * TILE);
     f32x16 acc = zero16();
     acc = mfma32(kf[0], qf[0], acc);
@@ -344,14 +368,18 @@ attention_kernel(AttnArgs A) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) sa = mfma32(kf[s], qf[s], sa);
   }
+  // every wave has read kbuf[0] before step 0 refills it
+  __syncthreads();
   for (int it = 0; it < kc; it += 2) {
     step(std::integral_constant<int, 0>(), it, sa, sb);
     if (it + 1 < kc) step(std::integral_constant<int, 1>(), it + 1, sb, sa);
   }
   __syncthreads();
 
-  attention_finish<T, D>(smem_raw, g, bh, h, i, n_i, qrow, hoff, A.s_sum, A.sigma_sum, A.alpha, A.o,
-                         A.o_sparse, A.o_linear, oacc, m_run, l_run, cl, qf);
+  const uint16_t* st_half = smem + ((kc & 1) ^ kh) * TILE;
+  attention_finish<T, D, ST_LDS>(smem_raw + EPI_OFF, (ST_LDS && kc > 0) ? st_half : nullptr, g, bh,
+                                 h, i, n_i, qrow, hoff, A.s_sum, A.sigma_sum, A.alpha, A.o,
+                                 A.o_sparse, A.o_linear, oacc, m_run, l_run, cl, qf);
 }
 
 template <typename T, int D>

@@ -37,65 +37,102 @@ __device__ __forceinline__ void store4(float* p, const float* x) {
 // LDS bytes the epilogue needs at the start of the shared buffer.
 template <int D>
 constexpr int epilogue_smem_bytes() {
-  return 4 * (256 + 4 * (D / 64) * 16 * 64) + D * (D + 8) * 2 + D * 4;
+  return 4 * (256 + 4 * (D / 64) * 16 * 64) + D * 4;
 }
 
+// XOR swizzle of the 16-byte chunks of a bf16 tile row (64 rows x D): the
+// operand reads of 16 consecutive rows at one chunk, and the transposing V
+// reads (4 consecutive keys x 4 chunks), hit distinct LDS banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return (r >> 1) & 7;
+}
+
+// merge_lds: epilogue_smem_bytes<D>() bytes of LDS for the merge buffers.
+// st_half (when kStLds and not null; D = 128 only): the 64 rows
+// c = 64*kh .. +63 of the value-major sum S_i^T that this wave's key half
+// finalises, already in LDS as a swizzled 64 x D tile; otherwise S_i^T is
+// read from s_sum in HBM.
 // qf: bf16 Q fragments of query 32*qh + l32, features 16*s + 8*(lane/32) .. +7.
-template <typename T, int D>
+template <typename T, int D, bool kStLds>
 __device__ __forceinline__ void attention_finish(
-    unsigned char* smem_raw, const Geometry& g, int bh, int h, int i, int n_i, int qrow,
-    int64_t hoff, const uint16_t* __restrict__ s_sum, const float* __restrict__ sigma_sum,
-    const float* __restrict__ alpha, void* o, float* o_sparse, float* o_linear,
-    const f32x16 (&oacc)[D / 32], float m_run, float l_run, float cl, const bf16x8 (&qf)[D / 16]) {
+    unsigned char* merge_lds, const uint16_t* st_half, const Geometry& g, int bh, int h, int i,
+    int n_i, int qrow, int64_t hoff, const uint16_t* __restrict__ s_sum,
+    const float* __restrict__ sigma_sum, const float* __restrict__ alpha, void* o,
+    float* o_sparse, float* o_linear, const f32x16 (&oacc)[D / 32], float m_run, float l_run,
+    float cl, const bf16x8 (&qf)[D / 16]) {
   constexpr int NS = D / 16;
   constexpr int DT = D / 32;
   constexpr int DTH = DT / 2;
-  constexpr int SS = D + 8;
   constexpr int MERGE_BYTES = 4 * (256 + 4 * DTH * 16 * 64);
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int kh = wave >> 1;
   const int l32 = lane & 31, hh = lane >> 5;
 
   // ---- merge the two key halves; stage the linear-branch operands ----
-  float* mbuf = reinterpret_cast<float*>(smem_raw);   // [4][32]
+  float* mbuf = reinterpret_cast<float*>(merge_lds);  // [4][32]
   float* lbuf = mbuf + 128;                            // [4][32]
   float* obuf = mbuf + 256;                            // [4][DTH][16][64]
+  float* sg = reinterpret_cast<float*>(merge_lds + MERGE_BYTES);  // sigma_i [D]
+  const int own0 = kh * DTH;
+
   const float l_full = l_run + xor_lane(l_run, 32);
   if (hh == 0) {
     mbuf[wave * 32 + l32] = m_run;
     lbuf[wave * 32 + l32] = l_full;
   }
-  const int own0 = kh * DTH;
-  // the wave keeps dims [32*own0, +32*DTH); select with static indices so the
-  // accumulators stay in registers
-  f32x16 o_own[DTH], o_oth[DTH];
+  // the wave keeps dims [32*own0, +32*DTH) and hands the other half to its
+  // partner; select with static indices so the accumulators stay in registers
+  f32x16 o_own[DTH];
 #pragma unroll
   for (int u = 0; u < DTH; ++u) {
     o_own[u] = kh ? oacc[DTH + u] : oacc[u];
-    o_oth[u] = kh ? oacc[u] : oacc[DTH + u];
+    const f32x16 oth = kh ? oacc[u] : oacc[DTH + u];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) obuf[((wave * DTH + u) * 16 + r) * 64 + lane] = oth[r];
   }
-#pragma unroll
-  for (int u = 0; u < DTH; ++u)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) obuf[((wave * DTH + u) * 16 + r) * 64 + lane] = o_oth[u][r];
 
+  // phi(Q) as the B operand of O_l^T = S_i^T phi(Q)^T (exp(q - max q) per
+  // query row; the row normaliser cancels against the denominator)
   const bool has_lin = g.k_marg > 0;
-  uint16_t* st = reinterpret_cast<uint16_t*>(smem_raw + MERGE_BYTES);   // S_i^T [D][SS]
-  float* sg = reinterpret_cast<float*>(st + D * SS);                      // sigma_i [D]
+  bf16x8 pf[NS];
   if (has_lin) {
-    const int64_t row = static_cast<int64_t>(bh) * g.nq + i;
-    const uint16_t* sgl = s_sum + row * D * D;
-    for (int e = t; e < (D / 4) * (D / 8); e += kThreads) {
-      const int ag = e % (D / 4), bc = e / (D / 4);
-      bf16x8 w[4];
+    float qmax = -INFINITY;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) w[x] = load8(sgl + (4 * ag + x) * D + 8 * bc);
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        bf16x4 p4;
-        p4[0] = w[0][x]; p4[1] = w[1][x]; p4[2] = w[2][x]; p4[3] = w[3][x];
-        *reinterpret_cast<bf16x4*>(&st[(8 * bc + x) * SS + 4 * ag]) = p4;
+      for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, bf16v_to_f32(qf[s][e]));
+    qmax = fmaxf(qmax, xor_lane(qmax, 32));
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pf[s][e] = f32_to_bf16(__builtin_amdgcn_exp2f((bf16v_to_f32(qf[s][e]) - qmax) * kLog2e));
+  }
+
+  // S_i^T rows (value dim c = 32*(own0+u) + l32, features 16*s + 8*hh .. +7)
+  // of the value-major sum: from the LDS copy, or straight from HBM (their
+  // latency then overlaps the merge)
+  const int64_t row = static_cast<int64_t>(bh) * g.nq + i;
+  bf16x8 sf[DTH][NS];
+  if (has_lin) {
+    if (kStLds && st_half != nullptr) {
+#pragma unroll
+      for (int u = 0; u < DTH; ++u) {
+        const int r = 32 * u + l32;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          sf[u][s] = *reinterpret_cast<const bf16x8*>(st_half + r * D + 8 * ((2 * s + hh) ^ swz<D>(r)));
       }
+    } else {
+      const uint16_t* sgl = s_sum + row * D * D;
+#pragma unroll
+      for (int u = 0; u < DTH; ++u)
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          sf[u][s] = load8(sgl + (32 * (own0 + u) + l32) * D + 16 * s + 8 * hh);
     }
     if (t < D) sg[t] = sigma_sum[row * D + t];
   }
@@ -120,27 +157,13 @@ __device__ __forceinline__ void attention_finish(
 #pragma unroll
   for (int u = 0; u < DTH; ++u) ol[u] = zero16();
   if (has_lin) {
-    float qmax = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, bf16v_to_f32(qf[s][e]));
-    qmax = fmaxf(qmax, xor_lane(qmax, 32));
     float dpart = 0.0f;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      bf16x8 pf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 pv = f32_to_bf16(__builtin_amdgcn_exp2f((bf16v_to_f32(qf[s][e]) - qmax) * kLog2e));
-        pf[e] = pv;
-        dpart += bf16v_to_f32(pv) * sg[16 * s + 8 * hh + e];
-      }
+      for (int e = 0; e < 8; ++e) dpart += bf16v_to_f32(pf[s][e]) * sg[16 * s + 8 * hh + e];
 #pragma unroll
-      for (int u = 0; u < DTH; ++u) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&st[(32 * (own0 + u) + l32) * SS + 16 * s + 8 * hh]);
-        ol[u] = mfma32(a, pf, ol[u]);
-      }
+      for (int u = 0; u < DTH; ++u) ol[u] = mfma32(sf[u][s], pf[s], ol[u]);
     }
     const float dsum = dpart + xor_lane(dpart, 32);
     const float dinv = 1.0f / dsum;

@@ -6,7 +6,10 @@
 // compact linear-attention state.  Here:
 //   H_j = phi(K_j)^T V_j   (d x d, bf16 out, float32 accumulation)
 //   z_j = sum over the block's tokens of phi(k)   (d, float32)
-// with phi = softmax over the d features, evaluated in float32.
+// with phi = softmax over the d features, evaluated in float32.  H_j is
+// stored value-major, element [c][a] = sum_n v_n[c] phi(k_n)[a] (that is,
+// H_j^T row-major), the operand layout in which the marginal sums feed the
+// matrix cores of the attention kernel directly.
 //
 // One workgroup per (b, h, j): the 64 x d tiles of K and V are read once
 // (coalesced 16-byte loads), phi(K)^T and V^T are staged token-contiguous in
@@ -24,7 +27,7 @@ __global__ void __launch_bounds__(kThreads)
 states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
               uint16_t* __restrict__ h_out, float* __restrict__ z_out) {
   constexpr int TS = kBlock + 8;        // token stride of the transposed tiles
-  constexpr int HS = D + 8;             // row stride of the staged output tile
+  constexpr int HS = D + 8;             // row stride of the staged (value-major) output tile
   constexpr int CW = D / 4;             // features per thread (4 threads per token)
   constexpr int TA = D / 32;            // 32-row tiles per dimension
   constexpr int NT = TA * TA / 4;       // output tiles per wave
@@ -109,22 +112,27 @@ states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
   }
   __syncthreads();   // operands consumed; reuse smem as the output tile
 
+  // value-major staging: row c = ct*32 + l32, features a (pairs of
+  // consecutive a packed into one 32-bit store)
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
     const int ti = wave * NT + u;
     const int at = ti / TA, ct = ti % TA;
+    uint16_t* srow = smem + (ct * 32 + l32) * HS;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 16; r += 2) {
       const int a = at * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      smem[a * HS + ct * 32 + l32] = f32_to_bf16_bits(acc[u][r]);
+      *reinterpret_cast<uint32_t*>(srow + a) =
+          static_cast<uint32_t>(f32_to_bf16_bits(acc[u][r])) |
+          (static_cast<uint32_t>(f32_to_bf16_bits(acc[u][r + 1])) << 16);
     }
   }
   __syncthreads();
   uint16_t* dst = h_out + blk * D * D;
   for (int e = t; e < D * D / 8; e += kThreads) {
-    const int a = e / (D / 8), c8 = e % (D / 8);
-    *reinterpret_cast<u32x4*>(dst + a * D + c8 * 8) =
-        *reinterpret_cast<const u32x4*>(&smem[a * HS + c8 * 8]);
+    const int c = e / (D / 8), a8 = e % (D / 8);
+    *reinterpret_cast<u32x4*>(dst + c * D + a8 * 8) =
+        *reinterpret_cast<const u32x4*>(&smem[c * HS + a8 * 8]);
   }
 }
 

@@ -141,7 +141,8 @@ int sla_route(const sla_problem* problem, const void* q, const void* k,
 
 /* Per-block linear-attention states.  [PISA summary; SPLA summary 2.2]
  * k, v      input [B,H,N,d]
- * h_states  out bf16 [B,H,nkb,d,d]: H_j[a][c] = sum_n phi(k_n)[a] v_n[c]
+ * h_states  out bf16 [B,H,nkb,d,d], value-major: element [c][a] of block j
+ *           is H_j[a][c] = sum_n phi(k_n)[a] v_n[c] (H_j^T row-major)
  * z_states  out float [B,H,nkb,d]: z_j[a] = sum_n phi(k_n)[a]
  * A short last block sums its valid tokens only.  phi is evaluated in
  * float32, H is accumulated in float32 from bf16 operands. */
@@ -169,7 +170,8 @@ int sla_forward(const sla_problem* problem, const void* q, const void* k,
 
 /* The two phases of sla_forward, for callers that schedule or time them
  * separately.  sla_marginal_sums writes, into the forward workspace, the
- * marginal-state sums S_i = sum_{j marginal} H_j (bf16 [B,H,nq,d,d]) and
+ * marginal-state sums S_i = sum_{j marginal} H_j (bf16 [B,H,nq,d,d],
+ * value-major like h_states) and
  * sigma_i = sum_{j marginal} z_j (float [B,H,nq,d]); sla_forward_attend then
  * runs the fused sparse + linear attention reading them from the same
  * workspace.  Arguments mean what they mean for sla_forward; with

@@ -123,7 +123,7 @@ def test_states_parity(name, heads):
     k64, v64 = to64(w.k), to64(w.v)
     for b, h in heads:
         H64, z64 = ora.linear_states(k64[b, h], v64[b, h])
-        hg = to64(Hs[b, h])
+        hg = to64(Hs[b, h]).transpose(0, 2, 1)      # stored value-major: [j][c][a]
         zg = zs[b, h].cpu().numpy().astype(np.float64)
         np.testing.assert_allclose(zg, z64, rtol=2e-5, atol=1e-6)
         err = rel_l2(hg, H64)
