@@ -138,7 +138,8 @@ int launched(hipError_t e, const char* what) {
       return fail(SLA_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", #ptr, (align)); \
   } while (0)
 
-// Forward workspace: [S bf16 B*H*nq*d*d][sigma f32 B*H*nq*d][mask bits u32 B*H*nq*nw]
+// Forward workspace: [S bf16 B*H*nq*d*d][sigma f32 B*H*nq*d]
+// [mask bits u32 B*H*ceil(nkb/64)*ceil(nq/512)*512*2]
 struct FwdWs {
   uint16_t* s_sum;
   float* sigma;
@@ -147,8 +148,9 @@ struct FwdWs {
 
 size_t forward_ws(const sla::Geometry& g) {
   const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
-  return align_up(rows * g.D * g.D * 2) + align_up(rows * g.D * 4) +
-         align_up(rows * sla::marginal_bit_words(g) * 4);
+  const size_t bit_words = static_cast<size_t>(g.B) * g.H * sla::marginal_chunks(g) *
+                           sla::marginal_rows_pad(g) * 2;
+  return align_up(rows * g.D * g.D * 2) + align_up(rows * g.D * 4) + align_up(bit_words * 4);
 }
 
 FwdWs carve_forward_ws(const sla::Geometry& g, void* ws) {

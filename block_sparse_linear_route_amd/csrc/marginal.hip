@@ -1,204 +1,320 @@
-// Marginal-state sums of the linear branch on the matrix cores.
+// Marginal-state sums of the linear branch.
 //
 // [SLA abstract] marginal KV blocks get O(N) linear attention; [PISA
 // technical summary] per-block first-order matrices H_j; the linear branch of
 // query block i needs S_i = sum_{j in M_i} H_j and sigma_i = sum_{j in M_i}
-// z_j.  Per head this is a product with the 0/1 marginal mask M
-// ([nq x nkb], exact in bf16):
-//     S[i, e] = sum_j M[i, j] H[j, e]        (e runs over the d*d entries)
-//     sigma[i, a] = sum_j M[i, j] z[j, a]
-// which runs as a dense bf16 GEMM on v_mfma_f32_32x32x16_bf16 with float32
-// accumulation, so every product is exact and S is the float32 sum of the
-// bf16 states (rounded once to bf16 on store).  z is float32: it enters the
-// same GEMM as two bf16 columns per feature (hi = bf16(z), lo = bf16(z - hi))
-// whose products are added in float32, giving sigma to ~2^-17 relative.
+// z_j.
 //
-// Kernel 1 turns the ascending marginal index lists into bit rows
-// (nkb bits per query block).  Kernel 2 tiles the GEMM: 256 query blocks x
-// 128 columns per workgroup, K-loop over chunks of 32 KV blocks; the H chunk
-// is staged in LDS transposed (column-major in j) so both MFMA operands are
-// contiguous in the contraction index, and the mask operand is expanded from
-// the bit rows in registers.
+// Per head, S is a product with the 0/1 marginal mask M ([nq x nkb], exact in
+// bf16): S[i, e] = sum_j M[i, j] H[j, e], e running over the d*d entries of
+// the value-major states.  It runs as a dense bf16 GEMM on
+// v_mfma_f32_32x32x16_bf16 with float32 accumulation, so every product is
+// exact and S is the float32 sum of the bf16 states, rounded once to bf16.
+//
+// Kernel 1 (one workgroup per 64 query blocks) writes the mask as bit rows,
+// laid out chunk-major (64 KV blocks per chunk, two 32-bit words per row) so
+// that a chunk's bits for 512 rows are one contiguous 4 KB piece; a small
+// gather kernel sums sigma_i directly in float32 (ascending j) from the
+// index lists.
+//
+// Kernel 2 computes S^T tiles of 64 columns x 512 rows per workgroup, so H is
+// streamed from HBM once per head for nq <= 512.  Each 64-block chunk of H
+// (64 rows of 128 bytes) and of the bit rows reaches LDS by direct buffer
+// loads through a 6-stage ring of separate LDS arrays (the loop is unrolled
+// over the stages, so the compiler can tell the stage being read from the
+// stages being filled and needs no wait on the loads in flight).  The H^T
+// operand comes from the row-major chunk by transposing LDS reads
+// (ds_read_b64_tr_b16), and the mask operand is expanded 4 bits at a time
+// through a 16-entry LDS table of bf16 0/1 quadruples.
 #include "device_common.hpp"
 #include "sla_internal.hpp"
+
+#include <type_traits>
 
 namespace sla {
 namespace {
 
-constexpr int kTM = 256;        // query blocks per workgroup
-constexpr int kTN = 128;        // GEMM columns per workgroup
-constexpr int kTK = 32;         // KV blocks per K chunk
-constexpr int kHS = kTK + 8;    // LDS row stride of the transposed chunk (elements)
+constexpr int kGM = 512;                  // query-block rows per GEMM workgroup
+constexpr int kGN = 64;                   // S columns per GEMM workgroup
+constexpr int kGK = 64;                   // KV blocks per chunk
+constexpr int kStages = 6;
+constexpr int kHBytes = kGK * kGN * 2;    // H chunk bytes (8 KB)
+constexpr int kBBytes = kGM * 8;          // bit-row chunk bytes (4 KB)
+constexpr int kStageBytes = kHBytes + kBBytes;
 
-// grid (ceil(nq / 64), B*H): bit rows of the marginal sets.
+// grid (ceil(nq / 64), B*H).  Bit rows of the marginal sets (chunk-major).
 __global__ void __launch_bounds__(kThreads)
-marg_bits_kernel(Geometry g, const int32_t* __restrict__ marg, uint32_t* __restrict__ bits, int nw) {
-  extern __shared__ uint32_t sbits[];        // [64][nw]
+marg_bits_kernel(Geometry g, const int32_t* __restrict__ marg, uint32_t* __restrict__ bits,
+                 int nchunks, int rows_pad) {
+  extern __shared__ uint32_t sbits[];        // [64][2 * nchunks]: row r, word w
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * 64;
   const int t = threadIdx.x;
+  const int nw = 2 * nchunks;
   for (int e = t; e < 64 * nw; e += kThreads) sbits[e] = 0u;
   __syncthreads();
   const int km = g.k_marg;
+  const int32_t* __restrict__ mrow0 = marg + (static_cast<int64_t>(bh) * g.nq + i0) * km;
   for (int e = t; e < 64 * km; e += kThreads) {
-    const int r = e / km, u = e % km;
-    const int i = i0 + r;
-    if (i < g.nq) {
-      const int j = marg[(static_cast<int64_t>(bh) * g.nq + i) * km + u];
+    const int r = e / km;
+    if (i0 + r < g.nq) {
+      const int j = mrow0[e];
       atomicOr(&sbits[r * nw + (j >> 5)], 1u << (j & 31));
     }
   }
   __syncthreads();
+  // chunk-major: word w of row i lands at [(w / 2) * rows_pad + i] * 2 + w % 2
+  uint32_t* __restrict__ bout = bits + static_cast<int64_t>(bh) * nchunks * rows_pad * 2;
   for (int e = t; e < 64 * nw; e += kThreads) {
-    const int r = e / nw, w = e % nw;
-    const int i = i0 + r;
-    if (i < g.nq) bits[(static_cast<int64_t>(bh) * g.nq + i) * nw + w] = sbits[e];
+    const int c = e / 128, r = (e / 2) % 64, h = e % 2;   // consecutive threads: consecutive words
+    if (i0 + r < g.nq)
+      bout[(static_cast<int64_t>(c) * rows_pad + i0 + r) * 2 + h] = sbits[r * nw + 2 * c + h];
   }
+
 }
 
-// Eight mask bits -> eight bf16 values 0.0 / 1.0.
-__device__ __forceinline__ bf16x8 bits_to_bf16x8(uint32_t byte) {
-  u32x4 w;
+// grid (ceil(nq / (256 / D)), B*H): sigma_i = sum_{j in M_i} z_j in float32,
+// ascending j; thread (row, feature a), z rows read whole by consecutive lanes.
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+marg_sigma_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __restrict__ zs,
+                  float* __restrict__ sigma) {
+  constexpr int RPB = kThreads / D;          // rows per workgroup
+  const int bh = blockIdx.y;
+  const int i = blockIdx.x * RPB + threadIdx.x / D;
+  const int a = threadIdx.x % D;
+  if (i >= g.nq) return;
+  const int km = g.k_marg;
+  const int32_t* __restrict__ mrow = marg + (static_cast<int64_t>(bh) * g.nq + i) * km;
+  const float* __restrict__ zb = zs + static_cast<int64_t>(bh) * g.nkb * D + a;
+  float acc = 0.0f;
+  int u = 0;
+  for (; u + 8 <= km; u += 8) {
+    float v[8];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t lo = (byte >> (2 * p)) & 1u ? 0x3f80u : 0u;
-    const uint32_t hi = (byte >> (2 * p + 1)) & 1u ? 0x3f800000u : 0u;
-    w[p] = lo | hi;
+    for (int x = 0; x < 8; ++x) v[x] = zb[static_cast<int64_t>(mrow[u + x]) * D];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc += v[x];
   }
-  return __builtin_bit_cast(bf16x8, w);
+  for (; u < km; ++u) acc += zb[static_cast<int64_t>(mrow[u]) * D];
+  sigma[(static_cast<int64_t>(bh) * g.nq + i) * D + a] = acc;
 }
 
-// grid (ceil(nq / 256), D*D/128 + D/64, B*H).  Column tiles ct < D*D/128
-// take entries e in [128 ct, 128 ct + 128) of H; the last D/64 take z
-// features [64 zt, 64 zt + 64) as (hi, lo) column pairs.
+// Physical 16-byte slot of chunk-column c16 in row r of an H chunk (8 slots
+// per 128-byte row): flipping bit 2 on rows with bit 1 set makes the
+// transposing reads (rows base + 0..3, four slots) hit distinct banks.
+__device__ __forceinline__ int hslot(int r, int c16) { return c16 ^ (4 * ((r >> 1) & 1)); }
+
+// grid (rows_pad / 512, D*D / 64, B*H).  S^T tile: columns e in
+// [64 ct, 64 ct + 64) of the value-major states, rows i0 .. i0 + 511.
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2)
-marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nw,
-                 const uint16_t* __restrict__ hs, const float* __restrict__ zs,
-                 uint16_t* __restrict__ s_out, float* __restrict__ sigma_out) {
-  constexpr int HT = D * D / kTN;                  // H column tiles
-  __shared__ __attribute__((aligned(16))) uint16_t ht[2][kTN * kHS];
+marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int rows_pad,
+                 const uint16_t* __restrict__ hs, uint16_t* __restrict__ s_out) {
+  constexpr int DD = D * D;
+  __shared__ __attribute__((aligned(16))) unsigned char st0[kStageBytes], st1[kStageBytes],
+      st2[kStageBytes], st3[kStageBytes], st4[kStageBytes], st5[kStageBytes];
+  __shared__ __attribute__((aligned(16))) u32x2 lut[16];
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int bh = blockIdx.z;
-  const int ct = blockIdx.y;
-  const bool ztile = ct >= HT;
-  const int i0 = blockIdx.x * kTM;
-  const int nq = g.nq, nkb = g.nkb;
-  const int nchunks = (nkb + kTK - 1) / kTK;
-  const uint16_t* hb = hs + static_cast<int64_t>(bh) * nkb * D * D + (ztile ? 0 : ct * kTN);
-  const float* zb = zs + static_cast<int64_t>(bh) * nkb * D + (ztile ? (ct - HT) * 64 : 0);
+  const int bh = blockIdx.z, ct = blockIdx.y;
+  const int i0 = blockIdx.x * kGM;
 
-  // staging: thread loads KV blocks 2*jp, 2*jp+1 of the chunk, columns 8*ec .. +7
-  const int jp = t % 16, ec = t / 16;
-  bf16x8 st0, st1;
-#define SLA_LOAD_CHUNK(c_)                                                                   \
-  do {                                                                                       \
-    const int j = kTK * (c_) + 2 * jp;                                                       \
-    if (!ztile) {                                                                            \
-      st0 = (j < nkb) ? load8(hb + static_cast<int64_t>(j) * D * D + 8 * ec) : zero_bf16x8(); \
-      st1 = (j + 1 < nkb) ? load8(hb + static_cast<int64_t>(j + 1) * D * D + 8 * ec)         \
-                          : zero_bf16x8();                                                   \
-    } else {                                                                                 \
-      f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = z0;                                              \
-      if (j < nkb) z0 = *reinterpret_cast<const f32x4*>(zb + static_cast<int64_t>(j) * D + 4 * ec); \
-      if (j + 1 < nkb)                                                                       \
-        z1 = *reinterpret_cast<const f32x4*>(zb + static_cast<int64_t>(j + 1) * D + 4 * ec); \
-      _Pragma("unroll") for (int x = 0; x < 4; ++x) {                                        \
-        const __bf16 h0 = f32_to_bf16(z0[x]);                                                \
-        const __bf16 h1 = f32_to_bf16(z1[x]);                                                \
-        st0[2 * x] = h0;                                                                     \
-        st0[2 * x + 1] = f32_to_bf16(z0[x] - bf16v_to_f32(h0));                              \
-        st1[2 * x] = h1;                                                                     \
-        st1[2 * x + 1] = f32_to_bf16(z1[x] - bf16v_to_f32(h1));                              \
-      }                                                                                      \
-    }                                                                                        \
-  } while (0)
-
-#define SLA_STORE_CHUNK(buf_)                                                                \
-  do {                                                                                       \
-    const u32x4 a_ = __builtin_bit_cast(u32x4, st0);                                         \
-    const u32x4 b_ = __builtin_bit_cast(u32x4, st1);                                         \
-    _Pragma("unroll") for (int x = 0; x < 8; ++x) {                                          \
-      const uint32_t w = (x & 1) ? ((a_[x >> 1] >> 16) | (b_[x >> 1] & 0xffff0000u))         \
-                                 : ((a_[x >> 1] & 0xffffu) | (b_[x >> 1] << 16));            \
-      *reinterpret_cast<uint32_t*>(&ht[(buf_)][(8 * ec + x) * kHS + 2 * jp]) = w;            \
-    }                                                                                        \
-  } while (0)
-
-  // rows of this wave: i0 + 64*wave + 32*nt + l32
-  const uint32_t* brow[2];
-  bool rok[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int i = i0 + 64 * wave + 32 * nt + l32;
-    rok[nt] = i < nq;
-    brow[nt] = bits + (static_cast<int64_t>(bh) * nq + (rok[nt] ? i : 0)) * nw;
+  if (t < 16) {
+    u32x2 e;
+    e[0] = ((t & 1) ? 0x3f80u : 0u) | ((t & 2) ? 0x3f800000u : 0u);
+    e[1] = ((t & 4) ? 0x3f80u : 0u) | ((t & 8) ? 0x3f800000u : 0u);
+    lut[t] = e;
   }
 
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = zero16();
+  auto stage_mem = [&](auto sc) -> unsigned char* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return st0;
+    else if constexpr (S == 1) return st1;
+    else if constexpr (S == 2) return st2;
+    else if constexpr (S == 3) return st3;
+    else if constexpr (S == 4) return st4;
+    else return st5;
+  };
 
-  SLA_LOAD_CHUNK(0);
-  SLA_STORE_CHUNK(0);
-  if (nchunks > 1) SLA_LOAD_CHUNK(1);
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    uint32_t word[2];
+  // Chunk loads.  H: rows j = 64c + r, bytes 128 ct .. +127 of each block's
+  // d*d states; wave w loads rows 16w + 8u + lane/8 (u = 0, 1), lane slot
+  // lane%8 holding global 16-byte column (lane%8) ^ swizzle; rows past nkb
+  // read as zeros.  Bits: 4 KB, 1 KB per wave.
+  const __amdgpu_buffer_rsrc_t hrs =
+      make_rsrc(hs + static_cast<int64_t>(bh) * g.nkb * DD, static_cast<uint32_t>(g.nkb) * DD * 2);
+  const __amdgpu_buffer_rsrc_t brs =
+      make_rsrc(bits + static_cast<int64_t>(bh) * nchunks * rows_pad * 2,
+                static_cast<uint32_t>(nchunks) * rows_pad * 8);
+  uint32_t hoff[2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) word[nt] = rok[nt] ? brow[nt][c] : 0u;
+  for (int u = 0; u < 2; ++u) {
+    const int r = 16 * wave + 8 * u + (lane >> 3);
+    hoff[u] = static_cast<uint32_t>(r) * DD * 2 + 128u * ct + 16u * hslot(r, lane & 7);
+  }
+  const uint32_t boff = static_cast<uint32_t>(i0) * 8 + 1024u * wave + 16u * lane;
+  auto issue = [&](int c, unsigned char* sb) {
+    const int cc = min(c, nchunks - 1);         // past the end: reload the last chunk (unused)
+    const uint32_t hs_off = static_cast<uint32_t>(kGK * cc) * DD * 2;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 bm[2];
+    for (int u = 0; u < 2; ++u) buffer_load_lds16(hrs, sb + (16 * wave + 8 * u) * 128, hoff[u], hs_off);
+    buffer_load_lds16(brs, sb + kHBytes + 1024 * wave, boff, static_cast<uint32_t>(cc) * rows_pad * 8);
+  };
+
+  // Transposing H^T reads: output lane i of a 16-lane group (G = (lane/16)%2)
+  // receives element i%4 of the rows addressed by lanes 4q + i/4; source
+  // lane (q, p) = (li/4, li%4) addresses row 16s + 8hh + 4x + q at columns
+  // 32mt + 16G + 4p .. +3, so output lane l gets column 32mt + l%32 at the
+  // rows j = 16s + 8hh + 4x + q, k-slot 4x + q: the bit order of the mask
+  // operand below.
+  uint32_t ta[2];
+  const uint32_t bofs = static_cast<uint32_t>(kHBytes + (128 * wave + l32) * 8);
+  {
+    const int li = lane & 15, q = li >> 2, p = li & 3, G = (lane >> 4) & 1;
+    const int r = 8 * hh + q;                       // + 16 s + 4 x (bits 2, 4, 5)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) bm[nt] = bits_to_bf16x8((word[nt] >> (16 * s + 8 * hh)) & 0xffu);
+    for (int mt = 0; mt < 2; ++mt) {
+      const int c16 = 4 * mt + 2 * G + (p >> 1);
+      ta[mt] = static_cast<uint32_t>(r * 128 + 16 * hslot(r, c16) + 8 * (p & 1));
+    }
+  }
+
+  f32x16 acc[2][4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ht[buf][(32 * mt + l32) * kHS + 16 * s + 8 * hh]);
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(a, bm[nt], acc[mt][nt]);
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = zero16();
+
+  // Every wave issues 3 loads per chunk, always (clamped past the end), so
+  // "chunk c landed" is vmcnt(3 * (kStages - 2)) at the top of step c.
+  auto step = [&](auto sc, int c) {
+    constexpr int S = decltype(sc)::value;
+    constexpr int SN = (S + kStages - 1) % kStages;
+    static_assert(3 * (kStages - 2) < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * (kStages - 2)));
+    // Barrier without a memory fence: a fence here would also wait for the
+    // loads still in flight into the other stages.  Each wave has just
+    // waited for its own part of chunk c, so after the barrier the whole
+    // chunk is in LDS; the empty asm statements keep the compiler from
+    // moving LDS accesses across the barrier.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(c + kStages - 1, stage_mem(std::integral_constant<int, SN>()));
+    if (c >= nchunks) return;
+    // This stage's operands in one asm block (it carries no memory operands,
+    // so the compiler adds no wait on the loads still filling other stages;
+    // the wait for these reads sits inside the block): the 32 mask bits of
+    // rows 128w + 32nt + l32, and the H^T fragments of both k-steps.
+    const uint32_t sb = lds_addr(stage_mem(sc));
+    u32x2 wb[4];
+    u32x2 tr[16];
+    asm volatile(
+        "ds_read_b64 %0, %20\n\t"
+        "ds_read_b64 %1, %20 offset:256\n\t"
+        "ds_read_b64 %2, %20 offset:512\n\t"
+        "ds_read_b64 %3, %20 offset:768\n\t"
+        "ds_read_b64_tr_b16 %4, %21\n\t"
+        "ds_read_b64_tr_b16 %5, %21 offset:512\n\t"
+        "ds_read_b64_tr_b16 %6, %22\n\t"
+        "ds_read_b64_tr_b16 %7, %22 offset:512\n\t"
+        "ds_read_b64_tr_b16 %8, %21 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %9, %21 offset:2560\n\t"
+        "ds_read_b64_tr_b16 %10, %22 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %11, %22 offset:2560\n\t"
+        "ds_read_b64_tr_b16 %12, %21 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %13, %21 offset:4608\n\t"
+        "ds_read_b64_tr_b16 %14, %22 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %15, %22 offset:4608\n\t"
+        "ds_read_b64_tr_b16 %16, %21 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %17, %21 offset:6656\n\t"
+        "ds_read_b64_tr_b16 %18, %22 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %19, %22 offset:6656\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(wb[0]), "=&v"(wb[1]), "=&v"(wb[2]), "=&v"(wb[3]), "=&v"(tr[0]), "=&v"(tr[1]),
+          "=&v"(tr[2]), "=&v"(tr[3]), "=&v"(tr[4]), "=&v"(tr[5]), "=&v"(tr[6]), "=&v"(tr[7]),
+          "=&v"(tr[8]), "=&v"(tr[9]), "=&v"(tr[10]), "=&v"(tr[11]), "=&v"(tr[12]), "=&v"(tr[13]),
+          "=&v"(tr[14]), "=&v"(tr[15])
+        : "v"(sb + bofs), "v"(sb + ta[0]), "v"(sb + ta[1])
+        : "memory");
+    // mask operand of k-step s for row tile nt: byte 2s + hh of the row's 64
+    // chunk bits (word s / 2), one LUT quadruple per nibble
+    auto mask_op = [&](int s, int nt) {
+      const uint32_t word = wb[nt][s >> 1];
+      const uint32_t sh = 16 * (s & 1) + 8 * hh;
+      const u32x2 lo = lut[(word >> sh) & 15u];
+      const u32x2 hi = lut[(word >> (sh + 4)) & 15u];
+      u32x4 w;
+      w[0] = lo[0]; w[1] = lo[1]; w[2] = hi[0]; w[3] = hi[1];
+      return __builtin_bit_cast(bf16x8, w);
+    };
+    bf16x8 mb[2][4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) mb[0][nt] = mask_op(0, nt);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s + 1 < 4) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) mb[(s + 1) & 1][nt] = mask_op(s + 1, nt);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        u32x4 w;
+        w[0] = tr[4 * s + 2 * mt][0]; w[1] = tr[4 * s + 2 * mt][1];
+        w[2] = tr[4 * s + 2 * mt + 1][0]; w[3] = tr[4 * s + 2 * mt + 1][1];
+        const bf16x8 ha = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma32(ha, mb[s & 1][nt], acc[mt][nt]);
       }
     }
-    if (c + 1 < nchunks) {
-      SLA_STORE_CHUNK(buf ^ 1);
-      if (c + 2 < nchunks) SLA_LOAD_CHUNK(c + 2);
-    }
-    __syncthreads();
+  };
+
+  issue(0, st0);
+  issue(1, st1);
+  issue(2, st2);
+  issue(3, st3);
+  issue(4, st4);
+  for (int c = 0; c < nchunks; c += kStages) {
+    step(std::integral_constant<int, 0>(), c);
+    step(std::integral_constant<int, 1>(), c + 1);
+    step(std::integral_constant<int, 2>(), c + 2);
+    step(std::integral_constant<int, 3>(), c + 3);
+    step(std::integral_constant<int, 4>(), c + 4);
+    step(std::integral_constant<int, 5>(), c + 5);
   }
+  wait_vmem();         // the clamped tail loads also write LDS
+  __syncthreads();     // every wave is done with the stages
 
-#undef SLA_LOAD_CHUNK
-#undef SLA_STORE_CHUNK
-
-  // epilogue: acc[mt][nt][r] = C[i = i0 + 64*wave + 32*nt + l32][col = 32*mt + 8*(r/4) + 4*hh + r%4]
+  // Output: acc[mt][nt][r] = S^T[e = 64 ct + 32 mt + 8(r/4) + 4hh + r%4]
+  //                              [i = i0 + 128w + 32nt + l32].
+  // Each wave stages 32 rows x 128 bytes at a time in its own stage array
+  // (16-byte chunks XOR-swizzled by row) and writes whole 128-byte rows.
+  unsigned char* ob = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    if (!rok[nt]) continue;
-    const int64_t i = static_cast<int64_t>(i0 + 64 * wave + 32 * nt + l32);
-    const int64_t row = static_cast<int64_t>(bh) * nq + i;
+  for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int col = 32 * mt + 8 * r4 + 4 * hh;
-        if (!ztile) {
-          u32x2 w;
-          w[0] = static_cast<uint32_t>(f32_to_bf16_bits(acc[mt][nt][4 * r4])) |
-                 (static_cast<uint32_t>(f32_to_bf16_bits(acc[mt][nt][4 * r4 + 1])) << 16);
-          w[1] = static_cast<uint32_t>(f32_to_bf16_bits(acc[mt][nt][4 * r4 + 2])) |
-                 (static_cast<uint32_t>(f32_to_bf16_bits(acc[mt][nt][4 * r4 + 3])) << 16);
-          *reinterpret_cast<u32x2*>(s_out + row * D * D + ct * kTN + col) = w;
-        } else {
-          float2 sg;
-          sg.x = acc[mt][nt][4 * r4] + acc[mt][nt][4 * r4 + 1];
-          sg.y = acc[mt][nt][4 * r4 + 2] + acc[mt][nt][4 * r4 + 3];
-          *reinterpret_cast<float2*>(sigma_out + row * D + (ct - HT) * 64 + col / 2) = sg;
-        }
+        const int c = 4 * mt + r4;                         // 16-byte chunk of the row
+        u32x2 w;
+        w[0] = static_cast<uint32_t>(f32_to_bf16_bits(acc[mt][nt][4 * r4])) |
+               (static_cast<uint32_t>(f32_to_bf16_bits(acc[mt][nt][4 * r4 + 1])) << 16);
+        w[1] = static_cast<uint32_t>(f32_to_bf16_bits(acc[mt][nt][4 * r4 + 2])) |
+               (static_cast<uint32_t>(f32_to_bf16_bits(acc[mt][nt][4 * r4 + 3])) << 16);
+        *reinterpret_cast<u32x2*>(ob + l32 * 128 + 16 * (c ^ ((l32 >> 1) & 7)) + 8 * hh) = w;
       }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int qc = 64 * k + lane;
+      const int row = qc >> 3, c = qc & 7;
+      const int i = i0 + 128 * wave + 32 * nt + row;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ob + row * 128 + 16 * (c ^ ((row >> 1) & 7)));
+      if (i < g.nq)
+        *reinterpret_cast<u32x4*>(s_out + (static_cast<int64_t>(bh) * g.nq + i) * DD + kGN * ct + 8 * c) = v;
+    }
   }
 }
 
@@ -207,20 +323,32 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nw,
 hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const uint16_t* h_states,
                                 const float* z_states, uint16_t* s_sum, float* sigma_sum,
                                 uint32_t* bits, hipStream_t stream) {
-  const int nw = marginal_bit_words(g);     // one 32-bit word per chunk of 32 KV blocks
+  const int nchunks = marginal_chunks(g);
+  const int rows_pad = marginal_rows_pad(g);
   dim3 g1((g.nq + 63) / 64, g.B * g.H);
-  hipLaunchKernelGGL(marg_bits_kernel, g1, dim3(kThreads), 64 * nw * sizeof(uint32_t), stream,
-                     g, marg, bits, nw);
+  const size_t lds1 = 64 * 2 * nchunks * sizeof(uint32_t);
+  hipLaunchKernelGGL(marg_bits_kernel, g1, dim3(kThreads), lds1, stream, g, marg, bits, nchunks,
+                     rows_pad);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int rpb = kThreads / g.D;
+  dim3 gs((g.nq + rpb - 1) / rpb, g.B * g.H);
   if (g.D == 128) {
-    dim3 g2((g.nq + kTM - 1) / kTM, 128 * 128 / kTN + 2, g.B * g.H);
-    hipLaunchKernelGGL((marg_gemm_kernel<128>), g2, dim3(kThreads), 0, stream, g, bits, nw,
-                       h_states, z_states, s_sum, sigma_sum);
+    hipLaunchKernelGGL((marg_sigma_kernel<128>), gs, dim3(kThreads), 0, stream, g, marg, z_states,
+                       sigma_sum);
   } else {
-    dim3 g2((g.nq + kTM - 1) / kTM, 64 * 64 / kTN + 1, g.B * g.H);
-    hipLaunchKernelGGL((marg_gemm_kernel<64>), g2, dim3(kThreads), 0, stream, g, bits, nw,
-                       h_states, z_states, s_sum, sigma_sum);
+    hipLaunchKernelGGL((marg_sigma_kernel<64>), gs, dim3(kThreads), 0, stream, g, marg, z_states,
+                       sigma_sum);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2(rows_pad / kGM, g.D * g.D / kGN, g.B * g.H);
+  if (g.D == 128) {
+    hipLaunchKernelGGL((marg_gemm_kernel<128>), g2, dim3(kThreads), 0, stream, g, bits, nchunks,
+                       rows_pad, h_states, s_sum);
+  } else {
+    hipLaunchKernelGGL((marg_gemm_kernel<64>), g2, dim3(kThreads), 0, stream, g, bits, nchunks,
+                       rows_pad, h_states, s_sum);
   }
   return hipGetLastError();
 }

@@ -25,10 +25,12 @@ hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t
 hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16_t* h_states,
                          float* z_states, hipStream_t stream);
 
-// Marginal-state sums S_i = sum_{j in M_i} H_j (bf16, [B,H,nq,d,d]) and
-// sigma_i = sum_{j in M_i} z_j (float, [B,H,nq,d]); bits is scratch of
-// B*H*nq*marginal_bit_words(g) 32-bit words for the mask rows.
-inline int marginal_bit_words(const Geometry& g) { return (g.nkb + 31) / 32; }
+// Marginal-state sums S_i = sum_{j in M_i} H_j (bf16, [B,H,nq,d,d], value-major
+// like the states) and sigma_i = sum_{j in M_i} z_j (float, [B,H,nq,d]); bits
+// is scratch of B*H*marginal_chunks(g)*marginal_rows_pad(g)*2 32-bit words for
+// the mask rows (two words per query block and chunk of 64 KV blocks).
+inline int marginal_chunks(const Geometry& g) { return (g.nkb + 63) / 64; }
+inline int marginal_rows_pad(const Geometry& g) { return (g.nq + 511) / 512 * 512; }
 hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const uint16_t* h_states,
                                 const float* z_states, uint16_t* s_sum, float* sigma_sum,
                                 uint32_t* bits, hipStream_t stream);

@@ -118,7 +118,8 @@ int sla_num_blocks(const sla_problem* problem, int32_t* nq, int32_t* nkb);
  * workspace passed to a call must be at least this large and 256-byte
  * aligned.  SLA_OP_FORWARD (and SLA_OP_FORWARD_FP8) needs a bf16
  * [B,H,nq,d,d] marginal-state sum, a float32 [B,H,nq,d] normaliser sum and
- * B*H*nq*ceil(nkb/32) 32-bit words of marginal-mask bits; SLA_OP_ROUTE
+ * B*H*2*ceil(nkb/64)*(nq rounded up to 512) 32-bit words of marginal-mask
+ * bits, each region 256-byte aligned; SLA_OP_ROUTE
  * needs float64 pooled Q and K. */
 int sla_workspace_size(const sla_problem* problem, int op, size_t* bytes);
 
