@@ -63,6 +63,7 @@ attention_kernel(AttnArgs A) {
   constexpr int EPI_OFF = ST_LDS ? 2 * TILE * 2 : 0;
   constexpr int SMEM_BYTES = (LOOP_BYTES > EPI_OFF + EPI_BYTES ? LOOP_BYTES : EPI_OFF + EPI_BYTES);
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM_BYTES];
+  __shared__ __attribute__((aligned(16))) float sig_lds[D];     // sigma_i, loaded at the start
   uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
 
   const Geometry& g = A.g;
@@ -159,6 +160,11 @@ attention_kernel(AttnArgs A) {
   const bool has_lin = g.k_marg > 0;
   const __amdgpu_buffer_rsrc_t srs =
       make_rsrc(A.s_sum + (static_cast<int64_t>(bh) * g.nq + i) * D * D, D * D * 2);
+  if (has_lin && wave == 0 && lane < D / 4) {
+    const __amdgpu_buffer_rsrc_t sgr =
+        make_rsrc(A.sigma_sum + (static_cast<int64_t>(bh) * g.nq + i) * D, D * 4);
+    buffer_load_lds16(sgr, sig_lds, 16u * lane, 0u);
+  }
   auto issue_st = [&](int half, uint16_t* dst) {
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
@@ -377,7 +383,8 @@ attention_kernel(AttnArgs A) {
   __syncthreads();
 
   const uint16_t* st_half = smem + ((kc & 1) ^ kh) * TILE;
-  attention_finish<T, D, ST_LDS>(smem_raw + EPI_OFF, (ST_LDS && kc > 0) ? st_half : nullptr, g, bh,
+  attention_finish<T, D, ST_LDS>(smem_raw + EPI_OFF, (ST_LDS && kc > 0) ? st_half : nullptr,
+                                 has_lin ? sig_lds : nullptr, g, bh,
                                  h, i, n_i, qrow, hoff, A.s_sum, A.sigma_sum, A.alpha, A.o,
                                  A.o_sparse, A.o_linear, oacc, m_run, l_run, cl, qf);
 }

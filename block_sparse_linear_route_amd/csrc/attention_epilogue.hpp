@@ -50,6 +50,8 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 // merge_lds: epilogue_smem_bytes<D>() bytes of LDS for the merge buffers.
+// sg_lds: sigma_i already in LDS (visible to all waves), or null to load it
+// from sigma_sum here.
 // st_half (when kStLds and not null; D = 128 only): the 64 rows
 // c = 64*kh .. +63 of the value-major sum S_i^T that this wave's key half
 // finalises, already in LDS as a swizzled 64 x D tile; otherwise S_i^T is
@@ -57,7 +59,8 @@ __device__ __forceinline__ int swz(int r) {
 // qf: bf16 Q fragments of query 32*qh + l32, features 16*s + 8*(lane/32) .. +7.
 template <typename T, int D, bool kStLds>
 __device__ __forceinline__ void attention_finish(
-    unsigned char* merge_lds, const uint16_t* st_half, const Geometry& g, int bh, int h, int i,
+    unsigned char* merge_lds, const uint16_t* st_half, const float* sg_lds, const Geometry& g,
+    int bh, int h, int i,
     int n_i, int qrow, int64_t hoff, const uint16_t* __restrict__ s_sum,
     const float* __restrict__ sigma_sum, const float* __restrict__ alpha, void* o,
     float* o_sparse, float* o_linear, const f32x16 (&oacc)[D / 32], float m_run, float l_run,
@@ -134,8 +137,9 @@ __device__ __forceinline__ void attention_finish(
         for (int s = 0; s < NS; ++s)
           sf[u][s] = load8(sgl + (32 * (own0 + u) + l32) * D + 16 * s + 8 * hh);
     }
-    if (t < D) sg[t] = sigma_sum[row * D + t];
+    if (sg_lds == nullptr && t < D) sg[t] = sigma_sum[row * D + t];
   }
+  const float* sgv = sg_lds != nullptr ? sg_lds : sg;
   __syncthreads();
 
   const int partner = wave ^ 2;
@@ -161,7 +165,7 @@ __device__ __forceinline__ void attention_finish(
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dpart += bf16v_to_f32(pf[s][e]) * sg[16 * s + 8 * hh + e];
+      for (int e = 0; e < 8; ++e) dpart += bf16v_to_f32(pf[s][e]) * sgv[16 * s + 8 * hh + e];
 #pragma unroll
       for (int u = 0; u < DTH; ++u) ol[u] = mfma32(sf[u][s], pf[s], ol[u]);
     }

@@ -336,7 +336,8 @@ attention_fp8_kernel(AttnFp8Args A) {
   for (int s = 0; s < NS; ++s)
     qf[s] = load8(qp + static_cast<int64_t>(kBlock * i + qr) * g.sn + 16 * s + 8 * hh);
   __syncthreads();
-  attention_finish<uint16_t, D, false>(smem_raw, nullptr, g, bh, h, i, n_i, qrow, hoff, A.s_sum, A.sigma_sum,
+  attention_finish<uint16_t, D, false>(smem_raw, nullptr, nullptr, g, bh, h, i, n_i, qrow, hoff,
+                                       A.s_sum, A.sigma_sum,
                                 A.alpha, A.o, A.o_sparse, A.o_linear, oacc, m_run, l_run, 1.0f, qf);
 }
 
