@@ -57,10 +57,11 @@ attention_kernel(AttnArgs A) {
   constexpr int DT = D / 32;                   // 32-row tiles over the value dims
   constexpr int LOOP_BYTES = NSTAGE * TILE * 2;
   constexpr int EPI_BYTES = epilogue_smem_bytes<D>();
-  // d = 128: the last two steps prefetch S_i^T into the two K buffers, so the
-  // merge buffers start at the V buffers; d = 64 reads S_i^T from HBM.
+  // The merge buffers of the epilogue start at the V buffers; at d = 128 the
+  // last two steps prefetch S_i^T into the two K buffers (d = 64 reads S_i^T
+  // from HBM).
   constexpr bool ST_LDS = (D == 128);
-  constexpr int EPI_OFF = ST_LDS ? 2 * TILE * 2 : 0;
+  constexpr int EPI_OFF = 2 * TILE * 2;
   constexpr int SMEM_BYTES = (LOOP_BYTES > EPI_OFF + EPI_BYTES ? LOOP_BYTES : EPI_OFF + EPI_BYTES);
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM_BYTES];
   __shared__ __attribute__((aligned(16))) float sig_lds[D];     // sigma_i, loaded at the start
@@ -376,17 +377,24 @@ attention_kernel(AttnArgs A) {
   }
   // every wave has read kbuf[0] before step 0 refills it
   __syncthreads();
+  // no critical block: the idle K buffers take S_i^T right away (the
+  // epilogue then always finds it in LDS)
+  if (ST_LDS && kc == 0 && has_lin) {
+    issue_st(0, smem);
+    issue_st(1, smem + TILE);
+  }
   for (int it = 0; it < kc; it += 2) {
     step(std::integral_constant<int, 0>(), it, sa, sb);
     if (it + 1 < kc) step(std::integral_constant<int, 1>(), it + 1, sb, sa);
   }
+  wait_vmem();       // (kc = 0: the S_i^T loads above)
   __syncthreads();
 
   const uint16_t* st_half = smem + ((kc & 1) ^ kh) * TILE;
-  attention_finish<T, D, ST_LDS>(smem_raw + EPI_OFF, (ST_LDS && kc > 0) ? st_half : nullptr,
-                                 has_lin ? sig_lds : nullptr, g, bh,
-                                 h, i, n_i, qrow, hoff, A.s_sum, A.sigma_sum, A.alpha, A.o,
-                                 A.o_sparse, A.o_linear, oacc, m_run, l_run, cl, qf);
+  attention_finish<T, D, ST_LDS, false>(smem_raw + EPI_OFF, st_half, sig_lds, has_lin, g, bh, h, i,
+                                        n_i, qrow, hoff, A.s_sum, A.sigma_sum, A.alpha, A.o,
+                                        A.o_sparse, A.o_linear, oacc, m_run, l_run, cl, qf,
+                                        [](int) {});
 }
 
 template <typename T, int D>

@@ -50,21 +50,24 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 // merge_lds: epilogue_smem_bytes<D>() bytes of LDS for the merge buffers.
-// sg_lds: sigma_i already in LDS (visible to all waves), or null to load it
-// from sigma_sum here.
-// st_half (when kStLds and not null; D = 128 only): the 64 rows
-// c = 64*kh .. +63 of the value-major sum S_i^T that this wave's key half
-// finalises, already in LDS as a swizzled 64 x D tile; otherwise S_i^T is
-// read from s_sum in HBM.
+// sg_lds: sigma_i already in LDS (visible to all waves) when sg_ok, else it
+// is loaded from sigma_sum here.  (Both LDS pointers are always valid, so
+// the compiler keeps them in the LDS address space.)
+// st_half (read when kStLds; D = 128 only): the 64 rows c = 64*kh .. +63 of
+// the value-major sum S_i^T that this wave's key half finalises, already in
+// LDS as a swizzled 64 x D tile; otherwise S_i^T is read from s_sum in HBM.
 // qf: bf16 Q fragments of query 32*qh + l32, features 16*s + 8*(lane/32) .. +7.
-template <typename T, int D, bool kStLds>
+// With kHooks, hook(1) runs once the LDS below merge_lds is no longer read
+// and hook(2) once the merge buffers are no longer read (all waves, after a
+// barrier): a caller can start loads for its next block there.
+template <typename T, int D, bool kStLds, bool kHooks, typename Hook>
 __device__ __forceinline__ void attention_finish(
-    unsigned char* merge_lds, const uint16_t* st_half, const float* sg_lds, const Geometry& g,
-    int bh, int h, int i,
+    unsigned char* merge_lds, const uint16_t* st_half, const float* sg_lds, bool sg_ok,
+    const Geometry& g, int bh, int h, int i,
     int n_i, int qrow, int64_t hoff, const uint16_t* __restrict__ s_sum,
     const float* __restrict__ sigma_sum, const float* __restrict__ alpha, void* o,
     float* o_sparse, float* o_linear, const f32x16 (&oacc)[D / 32], float m_run, float l_run,
-    float cl, const bf16x8 (&qf)[D / 16]) {
+    float cl, const bf16x8 (&qf)[D / 16], Hook&& hook) {
   constexpr int NS = D / 16;
   constexpr int DT = D / 32;
   constexpr int DTH = DT / 2;
@@ -121,7 +124,7 @@ __device__ __forceinline__ void attention_finish(
   const int64_t row = static_cast<int64_t>(bh) * g.nq + i;
   bf16x8 sf[DTH][NS];
   if (has_lin) {
-    if (kStLds && st_half != nullptr) {
+    if constexpr (kStLds) {
 #pragma unroll
       for (int u = 0; u < DTH; ++u) {
         const int r = 32 * u + l32;
@@ -130,17 +133,17 @@ __device__ __forceinline__ void attention_finish(
           sf[u][s] = *reinterpret_cast<const bf16x8*>(st_half + r * D + 8 * ((2 * s + hh) ^ swz<D>(r)));
       }
     } else {
-      const uint16_t* sgl = s_sum + row * D * D;
+      const uint16_t* sgl = s_sum + row * D * D;   // uniform base, 32-bit lane offsets
 #pragma unroll
       for (int u = 0; u < DTH; ++u)
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-          sf[u][s] = load8(sgl + (32 * (own0 + u) + l32) * D + 16 * s + 8 * hh);
+          sf[u][s] = load8_at(sgl, static_cast<uint32_t>(((32 * (own0 + u) + l32) * D + 16 * s + 8 * hh) * 2));
     }
-    if (sg_lds == nullptr && t < D) sg[t] = sigma_sum[row * D + t];
+    if (!sg_ok && t < D) sg[t] = sigma_sum[row * D + t];
   }
-  const float* sgv = sg_lds != nullptr ? sg_lds : sg;
   __syncthreads();
+  if constexpr (kHooks) hook(1);   // every wave has read S_i^T: the LDS below merge_lds is free
 
   const int partner = wave ^ 2;
   const float m_p = mbuf[partner * 32 + l32];
@@ -150,12 +153,16 @@ __device__ __forceinline__ void attention_finish(
   const float w_p = (m_p == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_p - m_tot) * cl);
   const float den = l_full * w_me + l_p * w_p;
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  f32x16 os[DTH];
+  // merged O_s, in place of the wave's own partial output
 #pragma unroll
   for (int u = 0; u < DTH; ++u)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      os[u][r] = (o_own[u][r] * w_me + obuf[((partner * DTH + u) * 16 + r) * 64 + lane] * w_p) * inv;
+      o_own[u][r] = (o_own[u][r] * w_me + obuf[((partner * DTH + u) * 16 + r) * 64 + lane] * w_p) * inv;
+  if constexpr (kHooks) {
+    __syncthreads();
+    hook(2);   // the merge buffers are free (sigma stays in use when it lives there)
+  }
 
   f32x16 ol[DTH];
 #pragma unroll
@@ -165,7 +172,8 @@ __device__ __forceinline__ void attention_finish(
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dpart += bf16v_to_f32(pf[s][e]) * sgv[16 * s + 8 * hh + e];
+      for (int e = 0; e < 8; ++e)
+        dpart += bf16v_to_f32(pf[s][e]) * (sg_ok ? sg_lds[16 * s + 8 * hh + e] : sg[16 * s + 8 * hh + e]);
 #pragma unroll
       for (int u = 0; u < DTH; ++u) ol[u] = mfma32(sf[u][s], pf[s], ol[u]);
     }
@@ -180,9 +188,11 @@ __device__ __forceinline__ void attention_finish(
   // ---- alpha mix and store ----
   const float al = alpha[h];
   if (qrow < n_i) {
-    const int tok = kBlock * i + qrow;
-    T* orow = static_cast<T*>(o) + hoff + static_cast<int64_t>(tok) * g.sn;
-    const int64_t dbg = (static_cast<int64_t>(bh) * g.N + tok) * D;
+    // uniform bases of the query block, 32-bit offsets of this lane's row
+    char* obase = reinterpret_cast<char*>(static_cast<T*>(o) + hoff + static_cast<int64_t>(kBlock * i) * g.sn);
+    const uint32_t orow = static_cast<uint32_t>(qrow * g.sn * sizeof(T));
+    const int64_t dbg0 = (static_cast<int64_t>(bh) * g.N + kBlock * i) * D;
+    const uint32_t drow = static_cast<uint32_t>(qrow * D * 4);
 #pragma unroll
     for (int u = 0; u < DTH; ++u)
 #pragma unroll
@@ -191,13 +201,13 @@ __device__ __forceinline__ void attention_finish(
         float ov[4], sv[4], lv[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          sv[x] = os[u][4 * r4 + x];
+          sv[x] = o_own[u][4 * r4 + x];
           lv[x] = ol[u][4 * r4 + x];
           ov[x] = al * sv[x] + (1.0f - al) * lv[x];
         }
-        store4(orow + dim0, ov);
-        if (o_sparse) store4(o_sparse + dbg + dim0, sv);
-        if (o_linear) store4(o_linear + dbg + dim0, lv);
+        store4(reinterpret_cast<T*>(obase + orow + dim0 * sizeof(T)), ov);
+        if (o_sparse) store4(reinterpret_cast<float*>(reinterpret_cast<char*>(o_sparse + dbg0) + drow + dim0 * 4), sv);
+        if (o_linear) store4(reinterpret_cast<float*>(reinterpret_cast<char*>(o_linear + dbg0) + drow + dim0 * 4), lv);
       }
   }
 }

@@ -87,6 +87,8 @@ attention_fp8_kernel(AttnFp8Args A) {
   constexpr float kLazy = 8.0f;
   constexpr float kLog2Max = 8.807354922057604f;   // log2(448)
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM_BYTES];
+  const uint16_t* smem_u16 = reinterpret_cast<const uint16_t*>(smem_raw);   // (unused S^T slot)
+  const float* sig_dummy = reinterpret_cast<const float*>(smem_raw);         // (unused sigma slot)
 
   const Geometry& g = A.g;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -336,9 +338,10 @@ attention_fp8_kernel(AttnFp8Args A) {
   for (int s = 0; s < NS; ++s)
     qf[s] = load8(qp + static_cast<int64_t>(kBlock * i + qr) * g.sn + 16 * s + 8 * hh);
   __syncthreads();
-  attention_finish<uint16_t, D, false>(smem_raw, nullptr, nullptr, g, bh, h, i, n_i, qrow, hoff,
+  attention_finish<uint16_t, D, false, false>(smem_raw, smem_u16, sig_dummy, false, g, bh, h, i, n_i,
+                                       qrow, hoff,
                                        A.s_sum, A.sigma_sum,
-                                A.alpha, A.o, A.o_sparse, A.o_linear, oacc, m_run, l_run, 1.0f, qf);
+                                A.alpha, A.o, A.o_sparse, A.o_linear, oacc, m_run, l_run, 1.0f, qf, [](int) {});
 }
 
 }  // namespace
