@@ -7,8 +7,8 @@
 //
 // Pooling sums bf16/f32 rows in float64 (exact for bf16 blocks) and divides
 // by the valid token count; logits are float64 dot products divided by
-// sqrt(d).  The selection is an exact 8-pass radix select over a 64-bit key
-// that orders logits descending, so the split is the one the float64 logits
+// sqrt(d).  The selection is an exact radix select over a 64-bit key that
+// orders logits descending, so the split is the one the float64 logits
 // define; equal logits are ordered by ascending KV block index.  Compaction
 // writes each class's KV block indices in ascending order.
 #include "device_common.hpp"
@@ -79,198 +79,301 @@ __device__ __forceinline__ uint64_t desc_key(double s) {
   return ~u;
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(v, o, 64);
-    if (lane >= o) v += y;
-  }
-  return v;
+// DPP lane move within rows of 16 lanes; lanes whose source falls outside
+// the row read 0.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, true));
 }
 
-// ---------------------------------------------------------------- selection
-// grid (ceil(nq / R), B*H), dynamic LDS: q rows [R][D] f64, keys [R][nkbp]
-// u64, per-wave histograms [4][256] u32.
-//
-// Phase 1 (whole workgroup): float64 logits of the R query blocks against
-// every KV block, thread t owning KV blocks j = t, t + 256, ... so each
-// pooled-K column read serves all R rows; stored as 64-bit descending keys.
-// Phase 2 (one wave per row, no further workgroup barriers): an 8-pass radix
-// select finds, for each of the two cut counts k_crit and k_crit + k_marg,
-// the key of the element at that rank and how many elements equal to it
-// fall inside the cut (equal keys are taken in ascending j); classes follow,
-// then ballot prefix counts compact each class in ascending j.
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each row of 16
+// lanes (row_shr 1, 2, 4, 8), then the totals of the lower rows.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+  v += dpp_mov<0x111>(v);
+  v += dpp_mov<0x112>(v);
+  v += dpp_mov<0x114>(v);
+  v += dpp_mov<0x118>(v);
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15);
+  const uint32_t r1 = __builtin_amdgcn_readlane(v, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// Bitwise OR over the 64 lanes (quad swaps, half-row and row mirrors, then
+// the four row results).
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= dpp_mov<0xB1>(v);
+  v |= dpp_mov<0x4E>(v);
+  v |= dpp_mov<0x141>(v);
+  v |= dpp_mov<0x140>(v);
+  return __builtin_amdgcn_readlane(v, 0) | __builtin_amdgcn_readlane(v, 16) |
+         __builtin_amdgcn_readlane(v, 32) | __builtin_amdgcn_readlane(v, 48);
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), l);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int D>
+// ---------------------------------------------------------------- selection
+// One wave splits one query block's row of nkb keys (key order = descending
+// logit).  Lane l holds the keys of KV blocks l + 64u in registers.
+//
+// The two cuts sit at ranks k_crit - 1 and k_crit + k_marg - 1.  Each is
+// found by a radix select that starts at the highest bit where the row's
+// keys differ (the bits above are common to all keys) and takes 8 bits per
+// pass.  A pass histograms the digit of the keys that share the cut's prefix,
+// a prefix scan of the bins finds the bin holding the cut's rank, and the
+// search ends as soon as that bin holds a single key: that key is the cut.
+// If all 64 bits are consumed, the remaining rank counts equal keys, which
+// are taken in ascending KV block order.
+template <int KPL>
+__device__ __forceinline__ void select_row(const uint64_t* rk, int nkb, int lane, uint32_t* wh,
+                                           int k_crit, int k_marg, int64_t row, int32_t* crit,
+                                           int32_t* marg, int8_t* cls) {
+  uint64_t kk[KPL];
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    const int j = lane + 64 * u;
+    kk[u] = j < nkb ? rk[j] : ~0ull;
+  }
+  const uint64_t k0 = rk[0];
+  uint64_t dx = 0;
+#pragma unroll
+  for (int u = 0; u < KPL; ++u)
+    if (lane + 64 * u < nkb) dx |= kk[u] ^ k0;
+  const uint64_t diff = (static_cast<uint64_t>(wave_or(static_cast<uint32_t>(dx >> 32))) << 32) |
+                        wave_or(static_cast<uint32_t>(dx));
+  int hi = diff ? 63 - __builtin_clzll(diff) : -1;
+  // bits above the highest differing bit (for hi = 63: none)
+  const uint64_t common = diff ? (k0 & ~((2ull << hi) - 1ull)) : k0;
+
+  const int target[2] = {k_crit, k_crit + k_marg};
+  uint64_t pref[2] = {common, common};
+  uint32_t rem[2];
+  bool done[2];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    rem[w] = target[w] > 0 ? static_cast<uint32_t>(target[w] - 1) : 0u;
+    done[w] = target[w] <= 0;
+  }
+
+  while (hi >= 0 && !(done[0] && done[1])) {
+    const int lo = hi >= 7 ? hi - 7 : 0;
+    const uint32_t dmask = (2u << (hi - lo)) - 1u;
+    const uint64_t above = ~((2ull << hi) - 1ull);
+    const uint64_t from_lo = ~((1ull << lo) - 1ull);
+    const bool shared = !done[0] && !done[1] && pref[0] == pref[1];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      if (done[w] || (shared && w == 1)) continue;
+      *reinterpret_cast<u32x4*>(wh + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+      const uint64_t pw = pref[w];
+#pragma unroll
+      for (int u = 0; u < KPL; ++u) {
+        if (64 * u >= nkb) break;
+        if (lane + 64 * u < nkb && ((kk[u] ^ pw) & above) == 0ull)
+          atomicAdd(&wh[static_cast<uint32_t>(kk[u] >> lo) & dmask], 1u);
+      }
+      lds_wait();
+      const u32x4 c = *reinterpret_cast<const u32x4*>(wh + 4 * lane);
+      const uint32_t tot = c[0] + c[1] + c[2] + c[3];
+      const uint32_t incl = wave_incl_scan(tot, lane);
+      const uint32_t excl = incl - tot;
+#pragma unroll
+      for (int ww = 0; ww < 2; ++ww) {
+        if (ww != w && !shared) continue;
+        const uint32_t rr = rem[ww];
+        const bool mine = rr >= excl && rr < incl;
+        uint32_t bin = 4u * lane, cum = excl, cnt = c[0];
+        if (mine && rr >= cum + c[0]) {
+          cum += c[0]; ++bin; cnt = c[1];
+          if (rr >= cum + c[1]) {
+            cum += c[1]; ++bin; cnt = c[2];
+            if (rr >= cum + c[2]) { cum += c[2]; ++bin; cnt = c[3]; }
+          }
+        }
+        const int src = __builtin_ctzll(__ballot(mine));
+        const uint32_t b_bin = __builtin_amdgcn_readlane(bin, src);
+        const uint32_t b_cum = __builtin_amdgcn_readlane(cum, src);
+        const uint32_t b_cnt = __builtin_amdgcn_readlane(cnt, src);
+        pref[ww] |= static_cast<uint64_t>(b_bin) << lo;
+        rem[ww] -= b_cum;
+        if (b_cnt == 1u) {
+          // the bin holds one key: it is the cut
+          const uint64_t pv = pref[ww];
+          uint64_t key = pv;
+#pragma unroll
+          for (int u = 0; u < KPL; ++u) {
+            if (64 * u >= nkb) break;
+            const uint64_t bm = __ballot(lane + 64 * u < nkb && ((kk[u] ^ pv) & from_lo) == 0ull);
+            if (bm) key = readlane64(kk[u], __builtin_ctzll(bm));
+          }
+          pref[ww] = key;
+          rem[ww] = 0u;
+          done[ww] = true;
+        }
+      }
+      lds_wait();
+    }
+    hi = lo - 1;
+  }
+
+  // classes (equal keys ranked by ascending j) and compaction
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  uint32_t eq_base[2] = {0u, 0u};
+  uint32_t out_base[2] = {0u, 0u};
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    if (64 * u >= nkb) break;
+    const int j = lane + 64 * u;
+    const uint64_t kv = kk[u];
+    bool in_w[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const uint64_t eqb = __ballot(kv == pref[w] && j < nkb);
+      const uint32_t tie_rank = eq_base[w] + static_cast<uint32_t>(__popcll(eqb & lt_mask));
+      in_w[w] = target[w] > 0 && (kv < pref[w] || (kv == pref[w] && tie_rank <= rem[w]));
+      eq_base[w] += static_cast<uint32_t>(__popcll(eqb));
+    }
+    const bool ok = j < nkb;
+    const int c = !ok ? 0 : (in_w[0] ? 2 : (in_w[1] ? 1 : 0));
+    const uint64_t b2 = __ballot(c == 2);
+    const uint64_t b1 = __ballot(c == 1);
+    const uint32_t p2 = out_base[0] + static_cast<uint32_t>(__popcll(b2 & lt_mask));
+    const uint32_t p1 = out_base[1] + static_cast<uint32_t>(__popcll(b1 & lt_mask));
+    out_base[0] += static_cast<uint32_t>(__popcll(b2));
+    out_base[1] += static_cast<uint32_t>(__popcll(b1));
+    if (ok) {
+      if (cls) cls[row * nkb + j] = static_cast<int8_t>(c);
+      if (c == 2 && p2 < static_cast<uint32_t>(k_crit)) crit[row * k_crit + p2] = j;
+      else if (c == 1 && p1 < static_cast<uint32_t>(k_marg)) marg[row * k_marg + p1] = j;
+    }
+  }
+}
+
+// grid (ceil(nq / R), B*H), dynamic LDS: keys [R][nkbp] u64, per-wave
+// histograms [4][256] u32.
+//
+// Phase 1 (whole workgroup): thread t owns KV blocks j = t + 512 m and
+// t + 256 + 512 m and computes the float64 logits of the R query blocks
+// against them, so each pooled-K value read serves R logits; the pooled-Q
+// rows are uniform across the workgroup and are read as scalar operands,
+// each serving two logits.  Results go to LDS as keys.
+// Phase 2: one wave per query block (select_row).
+template <int R, int KPL>
 __global__ void __launch_bounds__(kThreads)
-select_kernel(Geometry g, int R, int nkbp, const double* __restrict__ qpool,
+select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
               const double* __restrict__ kpool_t, double sqrt_d, int32_t* __restrict__ crit,
               int32_t* __restrict__ marg, int8_t* __restrict__ cls,
               float* __restrict__ logits_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
-  double* qs = reinterpret_cast<double*>(dyn);                       // [R][D]
-  uint64_t* keys = reinterpret_cast<uint64_t*>(qs + R * D);           // [R][nkbp]
+  uint64_t* keys = reinterpret_cast<uint64_t*>(dyn);                 // [R][nkbp]
   uint32_t* hist = reinterpret_cast<uint32_t*>(keys + R * nkbp);      // [4][256]
 
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * R;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int nq = g.nq, nkb = g.nkb;
+  const int nq = g.nq, nkb = g.nkb, D = g.D;
 
-  for (int e = t; e < R * D; e += kThreads) {
-    const int r = e / D, a = e % D;
-    const int i = i0 + r;
-    qs[e] = (i < nq) ? qpool[(static_cast<int64_t>(bh) * nq + i) * D + a] : 0.0;
-  }
-  __syncthreads();
-
-  // ---- phase 1: logits -> keys
+  const double* qrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    qrow[r] = qpool + (static_cast<int64_t>(bh) * nq + min(i0 + r, nq - 1)) * D;
   const double* kt = kpool_t + static_cast<int64_t>(bh) * D * nkb;
-  for (int j = t; j < nkbp; j += kThreads) {
-    if (j >= nkb) {
-      for (int r = 0; r < R; ++r) keys[r * nkbp + j] = ~0ull;
-      continue;
+
+  // Two KV blocks per thread (j and j + 256); 4 features per step, the next
+  // step's pooled-K values loaded before this step's FMAs.
+  for (int j0 = t; j0 < nkbp; j0 += 2 * kThreads) {
+    const int jj[2] = {j0, j0 + kThreads};
+    const int64_t jl[2] = {jj[0] < nkb ? jj[0] : 0, jj[1] < nkb ? jj[1] : 0};
+    double acc[2][R];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[x][r] = 0.0;
+    double kv[2][4];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kv[x][e] = kt[static_cast<int64_t>(e) * nkb + jl[x]];
+#pragma unroll 2
+    for (int a0 = 0; a0 < D; a0 += 4) {
+      const int an = a0 + 4 < D ? a0 + 4 : a0;
+      double kn[2][4];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kn[x][e] = kt[static_cast<int64_t>(an + e) * nkb + jl[x]];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double qv = qrow[r][a0 + e];
+          acc[0][r] = fma(qv, kv[0][e], acc[0][r]);
+          acc[1][r] = fma(qv, kv[1][e], acc[1][r]);
+        }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kv[x][e] = kn[x][e];
     }
-    double acc[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) acc[r] = 0.0;
-#pragma unroll 1
-    for (int a0 = 0; a0 < D; a0 += 16) {
-      double kv[16];
+    for (int x = 0; x < 2; ++x) {
+      const int j = jj[x];
+      if (j >= nkbp) continue;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) kv[u] = kt[static_cast<int64_t>(a0 + u) * nkb + j];
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-          if (r < R) acc[r] = fma(qs[r * D + a0 + u], kv[u], acc[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      if (r >= R) break;
-      const double sv = acc[r] / sqrt_d;
-      const bool ok = i0 + r < nq;
-      keys[r * nkbp + j] = ok ? desc_key(sv) : ~0ull;
-      if (ok && logits_out)
-        logits_out[(static_cast<int64_t>(bh) * nq + i0 + r) * nkb + j] = static_cast<float>(sv);
+      for (int r = 0; r < R; ++r) {
+        const double sv = acc[x][r] / sqrt_d;
+        const bool ok = i0 + r < nq && j < nkb;
+        keys[r * nkbp + j] = ok ? desc_key(sv) : ~0ull;
+        if (ok && logits_out)
+          logits_out[(static_cast<int64_t>(bh) * nq + i0 + r) * nkb + j] = static_cast<float>(sv);
+      }
     }
   }
   __syncthreads();
 
-  // ---- phase 2: one wave per query block
-  uint32_t* wh = hist + wave * 256;
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-  const int nu = nkbp / 64;
-  const int target[2] = {g.k_crit, g.k_crit + g.k_marg};
   for (int r = wave; r < R; r += 4) {
     const int i = i0 + r;
     if (i >= nq) break;
-    const uint64_t* rk = keys + r * nkbp;
-    uint64_t pref[2] = {0ull, 0ull};
-    uint32_t rem[2] = {target[0] > 0 ? static_cast<uint32_t>(target[0] - 1) : 0u,
-                       target[1] > 0 ? static_cast<uint32_t>(target[1] - 1) : 0u};
-    for (int pass = 0; pass < 8; ++pass) {
-      const int shift = 56 - 8 * pass;
-      // while both cuts share their prefix they share the histogram
-      const bool shared = pref[0] == pref[1];
-      for (int w = 0; w < (shared ? 1 : 2); ++w) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) wh[4 * lane + x] = 0u;
-        lds_wait();
-        for (int u = 0; u < nu; ++u) {
-          const uint64_t kk = rk[lane + 64 * u];
-          const bool match = (pass == 0) || (((kk ^ pref[w]) >> (shift + 8)) == 0ull);
-          const uint32_t digit = static_cast<uint32_t>(kk >> shift) & 255u;
-          if (pass == 0) {
-            // the leading byte takes few values: one atomic per distinct digit
-            uint64_t active = __ballot(true);
-            while (active) {
-              const int leader = __builtin_ctzll(active);
-              const uint32_t dd = __builtin_amdgcn_readlane(digit, leader);
-              const uint64_t same = __ballot(digit == dd);
-              if (lane == leader) atomicAdd(&wh[dd], static_cast<uint32_t>(__popcll(same)));
-              active &= ~same;
-            }
-          } else if (match) {
-            atomicAdd(&wh[digit], 1u);
-          }
-        }
-        lds_wait();
-        const uint32_t c0 = wh[4 * lane], c1 = wh[4 * lane + 1], c2 = wh[4 * lane + 2],
-                       c3 = wh[4 * lane + 3];
-        const uint32_t tot = c0 + c1 + c2 + c3;
-        const uint32_t incl = wave_incl_scan(tot, lane);
-        const uint32_t excl = incl - tot;
-#pragma unroll
-        for (int ww = 0; ww < 2; ++ww) {
-          if (!shared && ww != w) continue;
-          const bool mine = rem[ww] >= excl && rem[ww] < incl;
-          uint32_t bin = 4u * lane, cum = excl;
-          if (mine) {
-            if (rem[ww] >= cum + c0) { cum += c0; ++bin;
-              if (rem[ww] >= cum + c1) { cum += c1; ++bin;
-                if (rem[ww] >= cum + c2) { cum += c2; ++bin; } } }
-          }
-          const uint64_t who = __ballot(mine);
-          const int src = __builtin_ctzll(who);
-          const uint32_t b_bin = __builtin_amdgcn_readlane(bin, src);
-          const uint32_t b_cum = __builtin_amdgcn_readlane(cum, src);
-          pref[ww] |= static_cast<uint64_t>(b_bin) << shift;
-          rem[ww] -= b_cum;
-        }
-        lds_wait();
-      }
-    }
-
-    // classes (equal keys ranked by ascending j) and compaction
-    const int64_t row = static_cast<int64_t>(bh) * nq + i;
-    uint32_t eq_base[2] = {0u, 0u};
-    uint32_t out_base[2] = {0u, 0u};
-    for (int u = 0; u < nu; ++u) {
-      const int j = lane + 64 * u;
-      const uint64_t kk = rk[j];
-      bool in_w[2];
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const uint64_t eqb = __ballot(kk == pref[w]);
-        const uint32_t tie_rank = eq_base[w] + static_cast<uint32_t>(__popcll(eqb & lt_mask));
-        in_w[w] = target[w] > 0 && (kk < pref[w] || (kk == pref[w] && tie_rank <= rem[w]));
-        eq_base[w] += static_cast<uint32_t>(__popcll(eqb));
-      }
-      const bool ok = j < nkb;
-      const int c = !ok ? 0 : (in_w[0] ? 2 : (in_w[1] ? 1 : 0));
-      const uint64_t b2 = __ballot(c == 2);
-      const uint64_t b1 = __ballot(c == 1);
-      const uint32_t p2 = out_base[0] + static_cast<uint32_t>(__popcll(b2 & lt_mask));
-      const uint32_t p1 = out_base[1] + static_cast<uint32_t>(__popcll(b1 & lt_mask));
-      out_base[0] += static_cast<uint32_t>(__popcll(b2));
-      out_base[1] += static_cast<uint32_t>(__popcll(b1));
-      if (ok) {
-        if (cls) cls[row * nkb + j] = static_cast<int8_t>(c);
-        if (c == 2 && p2 < static_cast<uint32_t>(g.k_crit)) crit[row * g.k_crit + p2] = j;
-        else if (c == 1 && p1 < static_cast<uint32_t>(g.k_marg)) marg[row * g.k_marg + p1] = j;
-      }
-    }
+    select_row<KPL>(keys + r * nkbp, nkb, lane, hist + wave * 256, g.k_crit, g.k_marg,
+                    static_cast<int64_t>(bh) * nq + i, crit, marg, cls);
   }
 }
 
+template <int R, int KPL>
+void launch_select_rk(const Geometry& g, int nkbp, const double* qpool, const double* kpool_t,
+                      int32_t* crit, int32_t* marg, int8_t* cls, float* logits,
+                      hipStream_t stream) {
+  const size_t lds = static_cast<size_t>(R) * nkbp * 8 + 4 * 256 * 4;
+  dim3 grid((g.nq + R - 1) / R, g.B * g.H);
+  const double sqrt_d = __builtin_sqrt(static_cast<double>(g.D));
+  hipLaunchKernelGGL((select_kernel<R, KPL>), grid, dim3(kThreads), lds, stream, g, nkbp, qpool,
+                     kpool_t, sqrt_d, crit, marg, cls, logits);
+}
+
+// Rows per workgroup shrink as rows grow so the key rows stay within 64 KB
+// of LDS; keys per lane cover the row (nkb <= 4096).
 hipError_t launch_select(const Geometry& g, const double* qpool, const double* kpool_t,
                          int32_t* crit, int32_t* marg, int8_t* cls, float* logits,
                          hipStream_t stream) {
   const int nkbp = (g.nkb + 63) / 64 * 64;
-  int R = static_cast<int>(40960 / (static_cast<size_t>(nkbp) * 8));
-  R = R < 1 ? 1 : (R > 8 ? 8 : R);
-  const size_t lds = static_cast<size_t>(R) * g.D * 8 + static_cast<size_t>(R) * nkbp * 8 + 4 * 256 * 4;
-  dim3 grid((g.nq + R - 1) / R, g.B * g.H);
-  const double sqrt_d = __builtin_sqrt(static_cast<double>(g.D));
-  if (g.D == 128)
-    hipLaunchKernelGGL((select_kernel<128>), grid, dim3(kThreads), lds, stream, g, R, nkbp, qpool,
-                       kpool_t, sqrt_d, crit, marg, cls, logits);
+  if (nkbp <= 128)
+    launch_select_rk<8, 2>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+  else if (nkbp <= 512)
+    launch_select_rk<8, 8>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+  else if (nkbp <= 1024)
+    launch_select_rk<8, 16>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+  else if (nkbp <= 2048)
+    launch_select_rk<4, 32>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
   else
-    hipLaunchKernelGGL((select_kernel<64>), grid, dim3(kThreads), lds, stream, g, R, nkbp, qpool,
-                       kpool_t, sqrt_d, crit, marg, cls, logits);
+    launch_select_rk<2, 64>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
   return hipGetLastError();
 }
 

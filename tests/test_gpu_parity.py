@@ -93,6 +93,45 @@ def test_route_parity_shapes(N, kc, km, H, seed):
     _route_check(w)
 
 
+@pytest.mark.parametrize("nkb,kc,km", [(700, 30, 60), (2101, 26, 51)])
+def test_route_parity_long_rows(nkb, kc, km):
+    # 16 and 64 keys per lane in the selection kernel
+    w = make_custom(1, 1, 64 * nkb - 3, 128, dtype="bf16", kind="fourier1d", seed=nkb,
+                    k_crit=kc, k_marg=km)
+    _route_check(w)
+
+
+def _integer_blocks(nb, n_patterns, seed):
+    # bf16 rows of small integers, constant inside each 64-token block, so
+    # pooled means and logits are exact in float64 whatever the summation order
+    g = torch.Generator().manual_seed(seed)
+    pats = torch.randint(-2, 3, (n_patterns, 128), generator=g).to(torch.float32)
+    which = torch.randint(0, n_patterns, (nb,), generator=g)
+    return pats[which].repeat_interleave(64, dim=0)[None, None].to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("nkb,kc,km,n_patterns", [(300, 26, 51, 5), (700, 40, 100, 3),
+                                                  (90, 1, 88, 2)])
+def test_route_heavy_exact_ties(nkb, kc, km, n_patterns):
+    # few distinct logits per row: both cuts fall inside runs of equal logits,
+    # which must be taken in ascending KV block order
+    q = _integer_blocks(nkb, 7, seed=nkb)
+    k = _integer_blocks(nkb, n_patterns, seed=nkb + 1)
+    r = _s().route(q.to(DEV), k.to(DEV), kc, km)
+    o = ora.route(to64(q[0, 0]), to64(k[0, 0]), kc, km)
+    np.testing.assert_array_equal(r["crit_idx"][0, 0].cpu().numpy(), o["crit_idx"])
+    np.testing.assert_array_equal(r["marg_idx"][0, 0].cpu().numpy(), o["marg_idx"])
+
+
+def test_route_all_logits_equal():
+    q = torch.randn(1, 1, 64 * 200, 128).to(torch.bfloat16)
+    k = torch.zeros(1, 1, 64 * 200, 128, dtype=torch.bfloat16)
+    r = _s().route(q.to(DEV), k.to(DEV), 20, 30)
+    idx = np.arange(200)
+    np.testing.assert_array_equal(r["crit_idx"][0, 0].cpu().numpy(), np.tile(idx[:20], (200, 1)))
+    np.testing.assert_array_equal(r["marg_idx"][0, 0].cpu().numpy(), np.tile(idx[20:50], (200, 1)))
+
+
 def test_route_ties_break_to_lower_index():
     # identical blocks give identical logits: the lowest KV indices must win
     base = torch.randn(1, 1, 64, 128)
