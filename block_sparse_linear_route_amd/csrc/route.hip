@@ -18,7 +18,10 @@ namespace sla {
 namespace {
 
 // ---------------------------------------------------------------- pooling
-// grid (nb, B*H, 2): z = 0 pools Q, z = 1 pools K.  One workgroup per block.
+// grid (nb, B*H, 2): z = 0 pools Q, z = 1 pools K.  One workgroup per block:
+// thread t reads the 16-byte chunk t % CH of rows t / CH + RG m (rows past
+// a ragged end load the block's last row and are zeroed, so every load is in
+// flight at once), then LDS sums the row groups in float64.
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads)
 pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g,
@@ -39,18 +42,17 @@ pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g,
   const int row0 = j * kBlock;
   const int nj = min(kBlock, g.N - row0);
 
+  float f[RPG][8];
+#pragma unroll
+  for (int rr = 0; rr < RPG; ++rr)
+    load8_f32(x + static_cast<int64_t>(row0 + min(rg + rr * RG, nj - 1)) * g.sn + ch * 8, f[rr]);
   double acc[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  for (int e = 0; e < 8; ++e) {
+    acc[e] = 0.0;
 #pragma unroll
-  for (int rr = 0; rr < RPG; ++rr) {
-    const int r = rg + rr * RG;
-    if (r < nj) {
-      float f[8];
-      load8_f32(x + static_cast<int64_t>(row0 + r) * g.sn + ch * 8, f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(f[e]);
-    }
+    for (int rr = 0; rr < RPG; ++rr)
+      acc[e] += rg + rr * RG < nj ? static_cast<double>(f[rr][e]) : 0.0;
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[rg][ch * 8 + e] = acc[e];
@@ -266,6 +268,8 @@ __device__ __forceinline__ void select_row(const uint64_t* rk, int nkb, int lane
 // rows are uniform across the workgroup and are read as scalar operands,
 // each serving two logits.  Results go to LDS as keys.
 // Phase 2: one wave per query block (select_row).
+constexpr int kFC = 4;
+
 template <int R, int KPL>
 __global__ void __launch_bounds__(kThreads)
 select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
@@ -287,7 +291,7 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
     qrow[r] = qpool + (static_cast<int64_t>(bh) * nq + min(i0 + r, nq - 1)) * D;
   const double* kt = kpool_t + static_cast<int64_t>(bh) * D * nkb;
 
-  // Two KV blocks per thread (j and j + 256); 4 features per step, the next
+  // Two KV blocks per thread (j and j + 256); kFC features per step, the next
   // step's pooled-K values loaded before this step's FMAs.
   for (int j0 = t; j0 < nkbp; j0 += 2 * kThreads) {
     const int jj[2] = {j0, j0 + kThreads};
@@ -297,31 +301,40 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
     for (int x = 0; x < 2; ++x)
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[x][r] = 0.0;
-    double kv[2][4];
+    const int qz = 0;
+    double kv[2][kFC], qv[R][kFC];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int e = 0; e < kFC; ++e) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) kv[x][e] = kt[static_cast<int64_t>(e) * nkb + jl[x]];
+      for (int x = 0; x < 2; ++x) kv[x][e] = kt[static_cast<int64_t>(e) * nkb + jl[x]];
+#pragma unroll
+      for (int r = 0; r < R; ++r) qv[r][e] = qrow[r][e + qz];
+    }
 #pragma unroll 2
-    for (int a0 = 0; a0 < D; a0 += 4) {
-      const int an = a0 + 4 < D ? a0 + 4 : a0;
-      double kn[2][4];
+    for (int a0 = 0; a0 < D; a0 += kFC) {
+      const int an = a0 + kFC < D ? a0 + kFC : a0;
+      double kn[2][kFC], qn[R][kFC];
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int e = 0; e < kFC; ++e) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kn[x][e] = kt[static_cast<int64_t>(an + e) * nkb + jl[x]];
+        for (int x = 0; x < 2; ++x) kn[x][e] = kt[static_cast<int64_t>(an + e) * nkb + jl[x]];
+#pragma unroll
+        for (int r = 0; r < R; ++r) qn[r][e] = qrow[r][an + e + qz];
+      }
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const double qv = qrow[r][a0 + e];
-          acc[0][r] = fma(qv, kv[0][e], acc[0][r]);
-          acc[1][r] = fma(qv, kv[1][e], acc[1][r]);
+        for (int e = 0; e < kFC; ++e) {
+          acc[0][r] = fma(qv[r][e], kv[0][e], acc[0][r]);
+          acc[1][r] = fma(qv[r][e], kv[1][e], acc[1][r]);
         }
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int e = 0; e < kFC; ++e) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kv[x][e] = kn[x][e];
+        for (int x = 0; x < 2; ++x) kv[x][e] = kn[x][e];
+#pragma unroll
+        for (int r = 0; r < R; ++r) qv[r][e] = qn[r][e];
+      }
     }
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
