@@ -256,9 +256,7 @@ attention_kernel(AttnArgs A) {
         if (key >= nj) s_cur[r] = -INFINITY;
       }
     }
-    float mx = fmaxf(s_cur[0], s_cur[1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[r], s_cur[r + 1]));
+    float mx = max16(s_cur);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                        false, false);

@@ -248,20 +248,25 @@ attention_fp8_kernel(AttnFp8Args A) {
       const float fb = readlane_f(efb, o);
       const float lv = readlane_f(elv, o);
       const float iv = readlane_f(eiv, o);
-      float x[2][16];
+      if (nj < kBlock) {
+        // short last block: keys past the end score -inf (p = 0)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * tt + 8 * (r >> 2) + 4 * hh + (r & 3);
-          x[tt][r] = key < nj ? s_cur[tt][r] * fb : -INFINITY;
-        }
-      float mx = x[0][0];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[tt][r]);
-      mx = fmaxf(mx, xor_lane(mx, 32));
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * tt + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key >= nj) s_cur[tt][r] = -INFINITY;
+          }
+      }
+      // the scores in log2 units are fb * s with fb > 0, so their maximum is
+      // fb times the largest raw score
+      const float m0 = max16(s_cur[0]), m1 = max16(s_cur[1]);
+      float mx = fb * vmax3(m0, m1, m1);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // with lane l ^ 32
+      }
       // lazy reference max, as in the bf16 kernel: P_true <= 2^kLazy
       const bool grow = __ballot(mx - m_run > kLazy) != 0ull;
       if (grow) {
@@ -288,7 +293,7 @@ attention_fp8_kernel(AttnFp8Args A) {
           float e[4];
 #pragma unroll
           for (int x4 = 0; x4 < 4; ++x4) {
-            e[x4] = __builtin_amdgcn_exp2f(x[tt][r + x4] + bias);
+            e[x4] = __builtin_amdgcn_exp2f(fmaf(s_cur[tt][r + x4], fb, bias));
             ps += e[x4];
           }
           const int w = 4 * tt + (r >> 2);

@@ -150,6 +150,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Lane-crossing helpers (wave64).
 __device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// max(a, b, c) as one v_max3_f32.  fmaxf on matrix-core results costs an
+// extra quieting move per input (the compiler cannot tell they are not
+// signalling NaNs); softmax row maxima only ever see finite scores or -inf.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Maximum of the 16 registers of an accumulator, as a tree of v_max3_f32.
+__device__ __forceinline__ float max16(const f32x16& s) {
+  const float a = vmax3(s[0], s[1], s[2]), b = vmax3(s[3], s[4], s[5]);
+  const float c = vmax3(s[6], s[7], s[8]), d = vmax3(s[9], s[10], s[11]);
+  const float e = vmax3(s[12], s[13], s[14]);
+  const float f = vmax3(d, e, s[15]);
+  return vmax3(vmax3(a, b, c), f, f);
+}
+
 // Workgroup id remapped so that each XCD (the hardware dispatches workgroups
 // round-robin over 8 XCDs) owns one contiguous range of logical work items,
 // which keeps neighbouring query blocks of one head in the same L2.

@@ -199,7 +199,8 @@ int sla_quantize_fp8(const sla_problem* problem, const void* x, uint8_t* x_e4m3,
 /* Forward with the fp8 sparse branch.  [SLA2 summary 2.C]
  * q          bf16/f32 input [B,H,N,d] (phi(Q) of the linear branch)
  * q8,k8,v8   uint8 [B,H,N,d] contiguous codes from sla_quantize_fp8
- * q_s,k_s,v_s float [B,H,nb] their scales
+ * q_s,k_s,v_s float [B,H,nb] their scales (positive and finite, as sla_quantize_fp8
+ *            writes them)
  * the remaining arguments as for sla_forward.
  * The sparse branch computes S = (Q^ K^T) s_q s_k / sqrt(d) on fp8 matrix
  * cores, keeps the online-softmax statistics and the row sum in float32, and
