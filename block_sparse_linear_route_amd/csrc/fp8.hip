@@ -5,7 +5,7 @@
 //   r = fl32(448 / absmax), scale = fl32(absmax / 448), code = e4m3(fl32(x * r))
 // (scale 1 and all-zero codes for an all-zero block).  The float -> E4M3
 // conversion is done in integer/float steps below (round to nearest even,
-// saturate finite values to +-448, -0 kept as 0x80) so that the bytes are
+// saturate to +-448, -0 kept as 0x80) so that the bytes are
 // fully specified by the OCP 8-bit floating-point format rather than by a
 // conversion instruction's modes.
 #include "device_common.hpp"
@@ -13,20 +13,20 @@
 
 namespace sla {
 
+// E4M3 code of x, branch-free.  |x| >= 2^-6: adding 2^19 - 1 plus the kept
+// lowest bit to the float's bits and dropping 20 mantissa bits rounds to 3
+// mantissa bits, nearest even, with any carry moving into the exponent; the
+// result minus (127 - 7) << 3 is the code (exponent bias 7), and everything
+// above 448 (0x7e), infinities and NaN included, saturates to 0x7e.  Below
+// 2^-6 the codes are the multiples of 2^-9 (code 8 being 2^-6 itself).
 __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   const uint32_t bits = __float_as_uint(x);
   const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = fabsf(x);
-  if (a < 0.015625f) {                       // below 2^-6: grid of 2^-9
-    const uint32_t m = static_cast<uint32_t>(rintf(a * 512.0f));   // 0..8, 8 = 2^-6
-    return sign | m;
-  }
-  int e = static_cast<int>((bits >> 23) & 0xffu) - 127;     // a is a normal float
-  if (e > 8) return sign | 0x7eu;
-  uint32_t m = static_cast<uint32_t>(rintf(ldexpf(a, 3 - e)));   // 8..16
-  if (m == 16u) { m = 8u; ++e; }
-  if (e > 8 || (e == 8 && m > 14u)) return sign | 0x7eu;
-  return sign | (static_cast<uint32_t>(e + 7) << 3) | (m - 8u);
+  const uint32_t ab = bits & 0x7fffffffu;
+  const uint32_t rn = (ab + 0x7ffffu + ((ab >> 20) & 1u)) >> 20;
+  const uint32_t nc = min(rn - (120u << 3), 0x7eu);
+  const uint32_t sc = static_cast<uint32_t>(rintf(__uint_as_float(ab) * 512.0f));
+  return sign | (ab < 0x3c800000u ? sc : nc);
 }
 
 namespace {
@@ -48,16 +48,20 @@ quantize_kernel(const T* __restrict__ x, Geometry g, uint8_t* __restrict__ codes
   float amax = 0.0f;
 #pragma unroll
   for (int u = 0; u < NCH; ++u) {
+    // rows past a short last block load its last row and are zeroed after
+    // the load, so all loads are in flight together
     const int id = t + kThreads * u;
     const int row = id / CH, c8 = id % CH;
-    if (row < nj) {
-      load8_f32(src + static_cast<int64_t>(j * kBlock + row) * g.sn + 8 * c8, v[u]);
-    } else {
+    load8_f32(src + static_cast<int64_t>(j * kBlock + min(row, nj - 1)) * g.sn + 8 * c8, v[u]);
+  }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
+  for (int u = 0; u < NCH; ++u) {
+    const bool in = (t + kThreads * u) / CH < nj;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[u][e] = in ? v[u][e] : 0.0f;
+      amax = fmaxf(amax, fabsf(v[u][e]));
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[u][e]));
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, xor_lane(amax, o));
