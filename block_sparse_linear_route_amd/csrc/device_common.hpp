@@ -150,6 +150,23 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Lane-crossing helpers (wave64).
 __device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// DPP lane move of a float (bound_ctrl: lanes without a source read 0).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// v + v of lane l ^ 16 (v_permlane16_swap) and v + v of lane l ^ 32
+// (v_permlane32_swap).
+__device__ __forceinline__ float swap_sum16(float v) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+__device__ __forceinline__ float swap_sum32(float v) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 // max(a, b, c) as one v_max3_f32.  fmaxf on matrix-core results costs an
 // extra quieting move per input (the compiler cannot tell they are not
 // signalling NaNs); softmax row maxima only ever see finite scores or -inf.

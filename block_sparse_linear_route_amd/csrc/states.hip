@@ -43,45 +43,49 @@ states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
   const int row = t >> 2, part = t & 3;
   const int nj = min(kBlock, g.N - j * kBlock);
   const bool valid = row < nj;
-  const int64_t off = b * g.sb + h * g.sh + static_cast<int64_t>(j * kBlock + row) * g.sn + part * CW;
 
+  // rows past a short last block load its last row (all loads in flight
+  // together); their phi is zeroed below
+  const int64_t off = b * g.sb + h * g.sh + static_cast<int64_t>(j * kBlock + min(row, nj - 1)) * g.sn +
+                      part * CW;
   float kv[CW], vv[CW];
 #pragma unroll
   for (int c = 0; c < CW / 8; ++c) {
-    if (valid) {
-      load8_f32(k + off + 8 * c, kv + 8 * c);
-      load8_f32(v + off + 8 * c, vv + 8 * c);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { kv[8 * c + e] = 0.0f; vv[8 * c + e] = 0.0f; }
-    }
+    load8_f32(k + off + 8 * c, kv + 8 * c);
+    load8_f32(v + off + 8 * c, vv + 8 * c);
   }
 
-  // phi(k) = softmax over the d features of the token (4 lanes per token).
-  float mx = -INFINITY;
+  // phi(k) = softmax over the d features of the token (4 lanes per token:
+  // quad_perm DPP moves give the partners)
+  float mx = vmax3(kv[0], kv[1], kv[2]);
 #pragma unroll
-  for (int c = 0; c < CW; ++c) mx = fmaxf(mx, kv[c]);
-  mx = fmaxf(mx, xor_lane(mx, 1));
-  mx = fmaxf(mx, xor_lane(mx, 2));
+  for (int c = 3; c + 1 < CW; c += 2) mx = vmax3(mx, kv[c], kv[c + 1]);
+  if (CW % 2 == 0) mx = vmax3(mx, kv[CW - 1], kv[CW - 1]);
+  mx = vmax3(mx, dpp_f<0xB1>(mx), dpp_f<0x4E>(mx));
+  mx = vmax3(mx, dpp_f<0x4E>(mx), dpp_f<0x4E>(mx));
+  const float mb = mx * kLog2e;
   float sum = 0.0f;
 #pragma unroll
   for (int c = 0; c < CW; ++c) {
-    kv[c] = expf(kv[c] - mx);
+    kv[c] = __builtin_amdgcn_exp2f(fmaf(kv[c], kLog2e, -mb));
     sum += kv[c];
   }
-  sum += xor_lane(sum, 1);
-  sum += xor_lane(sum, 2);
+  sum += dpp_f<0xB1>(sum);
+  sum += dpp_f<0x4E>(sum);
+  const float inv = valid ? 1.0f / sum : 0.0f;
 #pragma unroll
-  for (int c = 0; c < CW; ++c) kv[c] = valid ? kv[c] / sum : 0.0f;
+  for (int c = 0; c < CW; ++c) kv[c] *= inv;
 
-  // z: column sums over the wave's 16 tokens, then over the 4 waves.
+  // z: column sums over the wave's 16 tokens (lanes part + 4m: row_ror 4
+  // and 8 inside each row of 16, then the row and half swaps), then over
+  // the 4 waves
 #pragma unroll
   for (int c = 0; c < CW; ++c) {
     float zc = kv[c];
-    zc += xor_lane(zc, 4);
-    zc += xor_lane(zc, 8);
-    zc += xor_lane(zc, 16);
-    zc += xor_lane(zc, 32);
+    zc += dpp_f<0x124>(zc);
+    zc += dpp_f<0x128>(zc);
+    zc = swap_sum16(zc);
+    zc = swap_sum32(zc);
     if (lane < 4) zpart[wave][part * CW + c] = zc;
   }
 
