@@ -11,16 +11,15 @@
 // v_mfma_f32_32x32x16_bf16 with float32 accumulation, so every product is
 // exact and S is the float32 sum of the bf16 states, rounded once to bf16.
 //
-// Kernel 1 (one workgroup per 64 query blocks) writes the mask as bit rows,
+// Kernel 1 (a few query blocks per workgroup) writes the mask as bit rows,
 // laid out chunk-major (64 KV blocks per chunk, two 32-bit words per row) so
-// that a chunk's bits for 512 rows are one contiguous 4 KB piece; a small
-// gather kernel sums sigma_i directly in float32 (ascending j) from the
-// index lists.
+// that a chunk's bits for 512 rows are one contiguous 4 KB piece, and sums
+// sigma_i directly in float32 (ascending j) from the index lists.
 //
 // Kernel 2 computes S^T tiles of 64 columns x 512 rows per workgroup, so H is
 // streamed from HBM once per head for nq <= 512.  Each 64-block chunk of H
 // (64 rows of 128 bytes) and of the bit rows reaches LDS by direct buffer
-// loads through a 6-stage ring of separate LDS arrays (the loop is unrolled
+// loads through a 3-stage ring of separate LDS arrays (the loop is unrolled
 // over the stages, so the compiler can tell the stage being read from the
 // stages being filled and needs no wait on the loads in flight).  The H^T
 // operand comes from the row-major chunk by transposing LDS reads
@@ -34,70 +33,65 @@
 namespace sla {
 namespace {
 
-constexpr int kGM = 512;                  // query-block rows per GEMM workgroup
+constexpr int kGM = 512;                  // query-block rows per GEMM workgroup (256 or 512)
+constexpr int kNT = kGM / 128;            // 32-row tiles per wave
 constexpr int kGN = 64;                   // S columns per GEMM workgroup
 constexpr int kGK = 64;                   // KV blocks per chunk
-constexpr int kStages = 6;
+constexpr int kStages = 3;                // 3 to 6
 constexpr int kHBytes = kGK * kGN * 2;    // H chunk bytes (8 KB)
 constexpr int kBBytes = kGM * 8;          // bit-row chunk bytes (4 KB)
 constexpr int kStageBytes = kHBytes + kBBytes;
 
-// grid (ceil(nq / 64), B*H).  Bit rows of the marginal sets (chunk-major).
+// grid (ceil(nq / RPB), B*H), RPB = 256 / D query blocks per workgroup,
+// thread (row, feature a).  Two products of each row's marginal list:
+//  * sigma_i = sum_{j in M_i} z_j in float32, ascending j; the z rows are
+//    gathered 16 at a time (the list entries are uniform per wave, so they
+//    come as scalar loads) and added in list order;
+//  * the mask bit row, OR-ed together in LDS and written chunk-major: word w
+//    of row i lands at [(w / 2) * rows_pad + i] * 2 + w % 2.
+template <int D>
 __global__ void __launch_bounds__(kThreads)
-marg_bits_kernel(Geometry g, const int32_t* __restrict__ marg, uint32_t* __restrict__ bits,
-                 int nchunks, int rows_pad) {
-  extern __shared__ uint32_t sbits[];        // [64][2 * nchunks]: row r, word w
+marg_prep_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __restrict__ zs,
+                 float* __restrict__ sigma, uint32_t* __restrict__ bits, int nchunks,
+                 int rows_pad) {
+  constexpr int RPB = kThreads / D;
+  extern __shared__ uint32_t sbits[];        // [RPB][2 * nchunks]
   const int bh = blockIdx.y;
-  const int i0 = blockIdx.x * 64;
-  const int t = threadIdx.x;
+  const int r = threadIdx.x / D, a = threadIdx.x % D;
+  const int i0 = blockIdx.x * RPB;
+  const int i = i0 + r;
   const int nw = 2 * nchunks;
-  for (int e = t; e < 64 * nw; e += kThreads) sbits[e] = 0u;
+  for (int e = threadIdx.x; e < RPB * nw; e += kThreads) sbits[e] = 0u;
   __syncthreads();
+
   const int km = g.k_marg;
-  const int32_t* __restrict__ mrow0 = marg + (static_cast<int64_t>(bh) * g.nq + i0) * km;
-  for (int e = t; e < 64 * km; e += kThreads) {
-    const int r = e / km;
-    if (i0 + r < g.nq) {
-      const int j = mrow0[e];
+  const bool row_ok = i < g.nq;
+  const int32_t* __restrict__ mrow = marg + (static_cast<int64_t>(bh) * g.nq + min(i, g.nq - 1)) * km;
+  if (row_ok) {
+    for (int u = a; u < km; u += D) {
+      const int j = mrow[u];
       atomicOr(&sbits[r * nw + (j >> 5)], 1u << (j & 31));
     }
   }
-  __syncthreads();
-  // chunk-major: word w of row i lands at [(w / 2) * rows_pad + i] * 2 + w % 2
-  uint32_t* __restrict__ bout = bits + static_cast<int64_t>(bh) * nchunks * rows_pad * 2;
-  for (int e = t; e < 64 * nw; e += kThreads) {
-    const int c = e / 128, r = (e / 2) % 64, h = e % 2;   // consecutive threads: consecutive words
-    if (i0 + r < g.nq)
-      bout[(static_cast<int64_t>(c) * rows_pad + i0 + r) * 2 + h] = sbits[r * nw + 2 * c + h];
-  }
-
-}
-
-// grid (ceil(nq / (256 / D)), B*H): sigma_i = sum_{j in M_i} z_j in float32,
-// ascending j; thread (row, feature a), z rows read whole by consecutive lanes.
-template <int D>
-__global__ void __launch_bounds__(kThreads)
-marg_sigma_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __restrict__ zs,
-                  float* __restrict__ sigma) {
-  constexpr int RPB = kThreads / D;          // rows per workgroup
-  const int bh = blockIdx.y;
-  const int i = blockIdx.x * RPB + threadIdx.x / D;
-  const int a = threadIdx.x % D;
-  if (i >= g.nq) return;
-  const int km = g.k_marg;
-  const int32_t* __restrict__ mrow = marg + (static_cast<int64_t>(bh) * g.nq + i) * km;
   const float* __restrict__ zb = zs + static_cast<int64_t>(bh) * g.nkb * D + a;
   float acc = 0.0f;
-  int u = 0;
-  for (; u + 8 <= km; u += 8) {
-    float v[8];
+  for (int u0 = 0; u0 < km; u0 += 16) {
+    float v[16];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) v[x] = zb[static_cast<int64_t>(mrow[u + x]) * D];
+    for (int x = 0; x < 16; ++x) v[x] = zb[static_cast<int64_t>(mrow[min(u0 + x, km - 1)]) * D];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) acc += v[x];
+    for (int x = 0; x < 16; ++x)
+      if (u0 + x < km) acc += v[x];
   }
-  for (; u < km; ++u) acc += zb[static_cast<int64_t>(mrow[u]) * D];
-  sigma[(static_cast<int64_t>(bh) * g.nq + i) * D + a] = acc;
+  if (row_ok) sigma[(static_cast<int64_t>(bh) * g.nq + i) * D + a] = acc;
+  __syncthreads();
+
+  uint32_t* __restrict__ bout = bits + static_cast<int64_t>(bh) * nchunks * rows_pad * 2;
+  for (int e = threadIdx.x; e < RPB * nw; e += kThreads) {
+    const int rr = e / nw, w = e % nw;
+    if (i0 + rr < g.nq)
+      bout[(static_cast<int64_t>(w >> 1) * rows_pad + i0 + rr) * 2 + (w & 1)] = sbits[e];
+  }
 }
 
 // Physical 16-byte slot of chunk-column c16 in row r of an H chunk (8 slots
@@ -112,8 +106,11 @@ __global__ void __launch_bounds__(kThreads, 2)
 marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int rows_pad,
                  const uint16_t* __restrict__ hs, uint16_t* __restrict__ s_out) {
   constexpr int DD = D * D;
+  // stages past kStages get one byte (never used)
+  constexpr int B3 = kStages > 3 ? kStageBytes : 16, B4 = kStages > 4 ? kStageBytes : 16;
+  constexpr int B5 = kStages > 5 ? kStageBytes : 16;
   __shared__ __attribute__((aligned(16))) unsigned char st0[kStageBytes], st1[kStageBytes],
-      st2[kStageBytes], st3[kStageBytes], st4[kStageBytes], st5[kStageBytes];
+      st2[kStageBytes], st3[B3], st4[B4], st5[B5];
   __shared__ __attribute__((aligned(16))) u32x2 lut[16];
 
   const int t = threadIdx.x, lane = t & 63;
@@ -154,13 +151,14 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
     const int r = 16 * wave + 8 * u + (lane >> 3);
     hoff[u] = static_cast<uint32_t>(r) * DD * 2 + 128u * ct + 16u * hslot(r, lane & 7);
   }
-  const uint32_t boff = static_cast<uint32_t>(i0) * 8 + 1024u * wave + 16u * lane;
+  const uint32_t boff = static_cast<uint32_t>(i0) * 8 + (kBBytes / 4) * wave + 16u * lane;
   auto issue = [&](int c, unsigned char* sb) {
     const int cc = min(c, nchunks - 1);         // past the end: reload the last chunk (unused)
     const uint32_t hs_off = static_cast<uint32_t>(kGK * cc) * DD * 2;
 #pragma unroll
     for (int u = 0; u < 2; ++u) buffer_load_lds16(hrs, sb + (16 * wave + 8 * u) * 128, hoff[u], hs_off);
-    buffer_load_lds16(brs, sb + kHBytes + 1024 * wave, boff, static_cast<uint32_t>(cc) * rows_pad * 8);
+    if (kNT == 4 || lane < 16 * kNT)
+      buffer_load_lds16(brs, sb + kHBytes + (kBBytes / 4) * wave, boff, static_cast<uint32_t>(cc) * rows_pad * 8);
   };
 
   // Transposing H^T reads: output lane i of a 16-lane group (G = (lane/16)%2)
@@ -170,7 +168,7 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
   // rows j = 16s + 8hh + 4x + q, k-slot 4x + q: the bit order of the mask
   // operand below.
   uint32_t ta[2];
-  const uint32_t bofs = static_cast<uint32_t>(kHBytes + (128 * wave + l32) * 8);
+  const uint32_t bofs = static_cast<uint32_t>(kHBytes + (32 * kNT * wave + l32) * 8);
   {
     const int li = lane & 15, q = li >> 2, p = li & 3, G = (lane >> 4) & 1;
     const int r = 8 * hh + q;                       // + 16 s + 4 x (bits 2, 4, 5)
@@ -181,11 +179,11 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
     }
   }
 
-  f32x16 acc[2][4];
+  f32x16 acc[2][kNT];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = zero16();
+    for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = zero16();
 
   // Every wave issues 3 loads per chunk, always (clamped past the end), so
   // "chunk c landed" is vmcnt(3 * (kStages - 2)) at the top of step c.
@@ -207,15 +205,16 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
     // This stage's operands in one asm block (it carries no memory operands,
     // so the compiler adds no wait on the loads still filling other stages;
     // the wait for these reads sits inside the block): the 32 mask bits of
-    // rows 128w + 32nt + l32, and the H^T fragments of both k-steps.
+    // rows 32 kNT w + 32nt + l32 (with two row tiles the last two reads
+    // repeat the first two), and the H^T fragments of both k-steps.
     const uint32_t sb = lds_addr(stage_mem(sc));
     u32x2 wb[4];
     u32x2 tr[16];
     asm volatile(
         "ds_read_b64 %0, %20\n\t"
         "ds_read_b64 %1, %20 offset:256\n\t"
-        "ds_read_b64 %2, %20 offset:512\n\t"
-        "ds_read_b64 %3, %20 offset:768\n\t"
+        "ds_read_b64 %2, %20 offset:%23\n\t"
+        "ds_read_b64 %3, %20 offset:%24\n\t"
         "ds_read_b64_tr_b16 %4, %21\n\t"
         "ds_read_b64_tr_b16 %5, %21 offset:512\n\t"
         "ds_read_b64_tr_b16 %6, %22\n\t"
@@ -237,7 +236,8 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
           "=&v"(tr[2]), "=&v"(tr[3]), "=&v"(tr[4]), "=&v"(tr[5]), "=&v"(tr[6]), "=&v"(tr[7]),
           "=&v"(tr[8]), "=&v"(tr[9]), "=&v"(tr[10]), "=&v"(tr[11]), "=&v"(tr[12]), "=&v"(tr[13]),
           "=&v"(tr[14]), "=&v"(tr[15])
-        : "v"(sb + bofs), "v"(sb + ta[0]), "v"(sb + ta[1])
+        : "v"(sb + bofs), "v"(sb + ta[0]), "v"(sb + ta[1]), "i"(256 * (2 % kNT)),
+          "i"(256 * (3 % kNT))
         : "memory");
     // mask operand of k-step s for row tile nt: byte 2s + hh of the row's 64
     // chunk bits (word s / 2), one LUT quadruple per nibble
@@ -250,14 +250,14 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
       w[0] = lo[0]; w[1] = lo[1]; w[2] = hi[0]; w[3] = hi[1];
       return __builtin_bit_cast(bf16x8, w);
     };
-    bf16x8 mb[2][4];
+    bf16x8 mb[2][kNT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) mb[0][nt] = mask_op(0, nt);
+    for (int nt = 0; nt < kNT; ++nt) mb[0][nt] = mask_op(0, nt);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s + 1 < 4) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) mb[(s + 1) & 1][nt] = mask_op(s + 1, nt);
+        for (int nt = 0; nt < kNT; ++nt) mb[(s + 1) & 1][nt] = mask_op(s + 1, nt);
       }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
@@ -266,34 +266,35 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
         w[2] = tr[4 * s + 2 * mt + 1][0]; w[3] = tr[4 * s + 2 * mt + 1][1];
         const bf16x8 ha = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma32(ha, mb[s & 1][nt], acc[mt][nt]);
+        for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma32(ha, mb[s & 1][nt], acc[mt][nt]);
       }
     }
   };
 
   issue(0, st0);
   issue(1, st1);
-  issue(2, st2);
-  issue(3, st3);
-  issue(4, st4);
+  if constexpr (kStages > 3) issue(2, st2);
+  if constexpr (kStages > 4) issue(3, st3);
+  if constexpr (kStages > 5) issue(4, st4);
   for (int c = 0; c < nchunks; c += kStages) {
     step(std::integral_constant<int, 0>(), c);
     step(std::integral_constant<int, 1>(), c + 1);
     step(std::integral_constant<int, 2>(), c + 2);
-    step(std::integral_constant<int, 3>(), c + 3);
-    step(std::integral_constant<int, 4>(), c + 4);
-    step(std::integral_constant<int, 5>(), c + 5);
+    if constexpr (kStages > 3) step(std::integral_constant<int, 3>(), c + 3);
+    if constexpr (kStages > 4) step(std::integral_constant<int, 4>(), c + 4);
+    if constexpr (kStages > 5) step(std::integral_constant<int, 5>(), c + 5);
   }
   wait_vmem();         // the clamped tail loads also write LDS
   __syncthreads();     // every wave is done with the stages
 
   // Output: acc[mt][nt][r] = S^T[e = 64 ct + 32 mt + 8(r/4) + 4hh + r%4]
   //                              [i = i0 + 128w + 32nt + l32].
-  // Each wave stages 32 rows x 128 bytes at a time in its own stage array
-  // (16-byte chunks XOR-swizzled by row) and writes whole 128-byte rows.
-  unsigned char* ob = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
+  // Each wave stages 32 rows x 128 bytes at a time in its own 4 KB of the
+  // first two stage arrays (16-byte chunks XOR-swizzled by row) and writes
+  // whole 128-byte rows.
+  unsigned char* ob = wave < 2 ? st0 + 4096 * wave : st1 + 4096 * (wave - 2);
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < kNT; ++nt) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -310,7 +311,7 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
     for (int k = 0; k < 4; ++k) {
       const int qc = 64 * k + lane;
       const int row = qc >> 3, c = qc & 7;
-      const int i = i0 + 128 * wave + 32 * nt + row;
+      const int i = i0 + 32 * kNT * wave + 32 * nt + row;
       const u32x4 v = *reinterpret_cast<const u32x4*>(ob + row * 128 + 16 * (c ^ ((row >> 1) & 7)));
       if (i < g.nq)
         *reinterpret_cast<u32x4*>(s_out + (static_cast<int64_t>(bh) * g.nq + i) * DD + kGN * ct + 8 * c) = v;
@@ -325,22 +326,17 @@ hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const ui
                                 uint32_t* bits, hipStream_t stream) {
   const int nchunks = marginal_chunks(g);
   const int rows_pad = marginal_rows_pad(g);
-  dim3 g1((g.nq + 63) / 64, g.B * g.H);
-  const size_t lds1 = 64 * 2 * nchunks * sizeof(uint32_t);
-  hipLaunchKernelGGL(marg_bits_kernel, g1, dim3(kThreads), lds1, stream, g, marg, bits, nchunks,
-                     rows_pad);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int rpb = kThreads / g.D;
   dim3 gs((g.nq + rpb - 1) / rpb, g.B * g.H);
+  const size_t lds1 = static_cast<size_t>(rpb) * 2 * nchunks * sizeof(uint32_t);
   if (g.D == 128) {
-    hipLaunchKernelGGL((marg_sigma_kernel<128>), gs, dim3(kThreads), 0, stream, g, marg, z_states,
-                       sigma_sum);
+    hipLaunchKernelGGL((marg_prep_kernel<128>), gs, dim3(kThreads), lds1, stream, g, marg,
+                       z_states, sigma_sum, bits, nchunks, rows_pad);
   } else {
-    hipLaunchKernelGGL((marg_sigma_kernel<64>), gs, dim3(kThreads), 0, stream, g, marg, z_states,
-                       sigma_sum);
+    hipLaunchKernelGGL((marg_prep_kernel<64>), gs, dim3(kThreads), lds1, stream, g, marg,
+                       z_states, sigma_sum, bits, nchunks, rows_pad);
   }
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(rows_pad / kGM, g.D * g.D / kGN, g.B * g.H);
   if (g.D == 128) {
