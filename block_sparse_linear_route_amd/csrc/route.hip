@@ -174,16 +174,19 @@ __device__ __forceinline__ void select_row(const uint64_t* rk, int nkb, int lane
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
       if (done[w] || (shared && w == 1)) continue;
-      *reinterpret_cast<u32x4*>(wh + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x2*>(wh + 2 * lane) = u32x2{0u, 0u};
       const uint64_t pw = pref[w];
 #pragma unroll
       for (int u = 0; u < KPL; ++u) {
         if (64 * u >= nkb) break;
-        if (lane + 64 * u < nkb && ((kk[u] ^ pw) & above) == 0ull)
-          atomicAdd(&wh[static_cast<uint32_t>(kk[u] >> lo) & dmask], 1u);
+        if (lane + 64 * u < nkb && ((kk[u] ^ pw) & above) == 0ull) {
+          const uint32_t bin = static_cast<uint32_t>(kk[u] >> lo) & dmask;
+          atomicAdd(&wh[bin >> 1], 1u << (16 * (bin & 1)));
+        }
       }
       lds_wait();
-      const u32x4 c = *reinterpret_cast<const u32x4*>(wh + 4 * lane);
+      const u32x2 cw = *reinterpret_cast<const u32x2*>(wh + 2 * lane);
+      const u32x4 c = u32x4{cw[0] & 0xffffu, cw[0] >> 16, cw[1] & 0xffffu, cw[1] >> 16};
       const uint32_t tot = c[0] + c[1] + c[2] + c[3];
       const uint32_t incl = wave_incl_scan(tot, lane);
       const uint32_t excl = incl - tot;
@@ -260,7 +263,8 @@ __device__ __forceinline__ void select_row(const uint64_t* rk, int nkb, int lane
 }
 
 // grid (ceil(nq / R), B*H), dynamic LDS: keys [R][nkbp] u64, per-wave
-// histograms [4][256] u32.
+// histograms of 256 16-bit bins packed two to a word ([4][128] u32; a bin
+// never counts more than nkb <= 4096 keys).
 //
 // Phase 1 (whole workgroup): thread t owns KV blocks j = t + 512 m and
 // t + 256 + 512 m and computes the float64 logits of the R query blocks
@@ -278,7 +282,7 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
               float* __restrict__ logits_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
   uint64_t* keys = reinterpret_cast<uint64_t*>(dyn);                 // [R][nkbp]
-  uint32_t* hist = reinterpret_cast<uint32_t*>(keys + R * nkbp);      // [4][256]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(keys + R * nkbp);      // [4][128]
 
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * R;
@@ -355,39 +359,49 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
   for (int r = wave; r < R; r += 4) {
     const int i = i0 + r;
     if (i >= nq) break;
-    select_row<KPL>(keys + r * nkbp, nkb, lane, hist + wave * 256, g.k_crit, g.k_marg,
+    select_row<KPL>(keys + r * nkbp, nkb, lane, hist + wave * 128, g.k_crit, g.k_marg,
                     static_cast<int64_t>(bh) * nq + i, crit, marg, cls);
   }
 }
 
 template <int R, int KPL>
-void launch_select_rk(const Geometry& g, int nkbp, const double* qpool, const double* kpool_t,
-                      int32_t* crit, int32_t* marg, int8_t* cls, float* logits,
-                      hipStream_t stream) {
-  const size_t lds = static_cast<size_t>(R) * nkbp * 8 + 4 * 256 * 4;
+hipError_t launch_select_rk(const Geometry& g, int nkbp, const double* qpool,
+                            const double* kpool_t, int32_t* crit, int32_t* marg, int8_t* cls,
+                            float* logits, hipStream_t stream) {
+  const size_t lds = static_cast<size_t>(R) * nkbp * 8 + 4 * 128 * 4;
+  if (lds > 65536) {
+    // more than 64 KB of dynamic LDS has to be allowed for the kernel (on
+    // the current device)
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<R, KPL>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
   dim3 grid((g.nq + R - 1) / R, g.B * g.H);
   const double sqrt_d = __builtin_sqrt(static_cast<double>(g.D));
   hipLaunchKernelGGL((select_kernel<R, KPL>), grid, dim3(kThreads), lds, stream, g, nkbp, qpool,
                      kpool_t, sqrt_d, crit, marg, cls, logits);
+  return hipGetLastError();
 }
 
-// Rows per workgroup shrink as rows grow so the key rows stay within 64 KB
-// of LDS; keys per lane cover the row (nkb <= 4096).
+// Eight query rows per workgroup (every pooled-K value read serves eight
+// logits) up to nkb = 1024, then four and two, so that the key rows stay
+// within 64 KB of LDS and several workgroups share a CU (the kernel is
+// latency-bound; at nkb = 1182 four rows measured faster than eight).  Keys
+// per lane cover the row (nkb <= 4096).
 hipError_t launch_select(const Geometry& g, const double* qpool, const double* kpool_t,
                          int32_t* crit, int32_t* marg, int8_t* cls, float* logits,
                          hipStream_t stream) {
   const int nkbp = (g.nkb + 63) / 64 * 64;
   if (nkbp <= 128)
-    launch_select_rk<8, 2>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
-  else if (nkbp <= 512)
-    launch_select_rk<8, 8>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
-  else if (nkbp <= 1024)
-    launch_select_rk<8, 16>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
-  else if (nkbp <= 2048)
-    launch_select_rk<4, 32>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
-  else
-    launch_select_rk<2, 64>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
-  return hipGetLastError();
+    return launch_select_rk<8, 2>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+  if (nkbp <= 512)
+    return launch_select_rk<8, 8>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+  if (nkbp <= 1024)
+    return launch_select_rk<8, 16>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+  if (nkbp <= 2048)
+    return launch_select_rk<4, 32>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+  return launch_select_rk<2, 64>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
 }
 
 template <typename T, int D>
