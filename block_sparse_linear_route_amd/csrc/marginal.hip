@@ -33,14 +33,10 @@
 namespace sla {
 namespace {
 
-constexpr int kGM = 512;                  // query-block rows per GEMM workgroup (256 or 512)
-constexpr int kNT = kGM / 128;            // 32-row tiles per wave
 constexpr int kGN = 64;                   // S columns per GEMM workgroup
 constexpr int kGK = 64;                   // KV blocks per chunk
 constexpr int kStages = 3;                // 3 to 6
 constexpr int kHBytes = kGK * kGN * 2;    // H chunk bytes (8 KB)
-constexpr int kBBytes = kGM * 8;          // bit-row chunk bytes (4 KB)
-constexpr int kStageBytes = kHBytes + kBBytes;
 
 // grid (ceil(nq / RPB), B*H), RPB = 256 / D query blocks per workgroup,
 // thread (row, feature a).  Two products of each row's marginal list:
@@ -99,13 +95,18 @@ marg_prep_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __re
 // transposing reads (rows base + 0..3, four slots) hit distinct banks.
 __device__ __forceinline__ int hslot(int r, int c16) { return c16 ^ (4 * ((r >> 1) & 1)); }
 
-// grid (rows_pad / 512, D*D / 64, B*H).  S^T tile: columns e in
-// [64 ct, 64 ct + 64) of the value-major states, rows i0 .. i0 + 511.
-template <int D>
+// grid (row tiles, D*D / 64, B*H).  S^T tile: columns e in [64 ct, 64 ct +
+// 64) of the value-major states, rows i0 .. i0 + GM - 1 with GM = 128 NT
+// (NT 32-row tiles per wave) and i0 = row0 + GM blockIdx.x.
+template <int D, int NT>
 __global__ void __launch_bounds__(kThreads, 2)
 marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int rows_pad,
-                 const uint16_t* __restrict__ hs, uint16_t* __restrict__ s_out) {
+                 int row0, const uint16_t* __restrict__ hs, uint16_t* __restrict__ s_out) {
   constexpr int DD = D * D;
+  constexpr int kNT = NT;
+  constexpr int kGM = 128 * NT;
+  constexpr int kBBytes = kGM * 8;          // bit-row chunk bytes
+  constexpr int kStageBytes = kHBytes + kBBytes;
   // stages past kStages get one byte (never used)
   constexpr int B3 = kStages > 3 ? kStageBytes : 16, B4 = kStages > 4 ? kStageBytes : 16;
   constexpr int B5 = kStages > 5 ? kStageBytes : 16;
@@ -117,7 +118,7 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int bh = blockIdx.z, ct = blockIdx.y;
-  const int i0 = blockIdx.x * kGM;
+  const int i0 = row0 + blockIdx.x * kGM;
 
   if (t < 16) {
     u32x2 e;
@@ -338,13 +339,24 @@ hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const ui
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 g2(rows_pad / kGM, g.D * g.D / kGN, g.B * g.H);
+  // 512-row tiles, and a 256-row tile for a remainder of at most 256 rows
+  // (at nq = 1182: 1280 rows of matrix-core work instead of 1536)
+  const int full = g.nq / 512, rem = g.nq - 512 * full;
+  const int n512 = rem > 256 ? full + 1 : full;
+  auto gemm = [&](auto dc, auto ntc, int tiles, int row0) {
+    constexpr int DK = decltype(dc)::value, NTK = decltype(ntc)::value;
+    dim3 g2(tiles, DK * DK / kGN, g.B * g.H);
+    hipLaunchKernelGGL((marg_gemm_kernel<DK, NTK>), g2, dim3(kThreads), 0, stream, g, bits,
+                       nchunks, rows_pad, row0, h_states, s_sum);
+  };
   if (g.D == 128) {
-    hipLaunchKernelGGL((marg_gemm_kernel<128>), g2, dim3(kThreads), 0, stream, g, bits, nchunks,
-                       rows_pad, h_states, s_sum);
+    if (n512 > 0) gemm(std::integral_constant<int, 128>(), std::integral_constant<int, 4>(), n512, 0);
+    if (rem > 0 && rem <= 256)
+      gemm(std::integral_constant<int, 128>(), std::integral_constant<int, 2>(), 1, 512 * full);
   } else {
-    hipLaunchKernelGGL((marg_gemm_kernel<64>), g2, dim3(kThreads), 0, stream, g, bits, nchunks,
-                       rows_pad, h_states, s_sum);
+    if (n512 > 0) gemm(std::integral_constant<int, 64>(), std::integral_constant<int, 4>(), n512, 0);
+    if (rem > 0 && rem <= 256)
+      gemm(std::integral_constant<int, 64>(), std::integral_constant<int, 2>(), 1, 512 * full);
   }
   return hipGetLastError();
 }

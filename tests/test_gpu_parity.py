@@ -409,7 +409,10 @@ def _align256(x):
 
 @pytest.mark.parametrize("N,d,km,H,seed", [(1000, 64, 5, 2, 30), (1024, 64, 8, 1, 31),
                                            (5000, 128, 20, 2, 32), (33 * 64 + 5, 128, 1, 1, 33),
-                                           (300 * 64, 128, 150, 1, 34)])
+                                           (300 * 64, 128, 150, 1, 34),
+                                           # a 512-row GEMM tile plus the 256-row tail tile,
+                                           # and a remainder too long for the tail tile
+                                           (700 * 64, 128, 30, 1, 35), (812 * 64 - 7, 64, 40, 1, 36)])
 def test_marginal_sums_parity(N, d, km, H, seed):
     """Phase one of the forward: S_i and sigma_i in the workspace equal the
     float64 sums of the same bf16 / float32 states over each marginal set."""
