@@ -88,15 +88,9 @@ attention_kernel(AttnArgs A) {
   const int64_t sn = g.sn;
 
   // Q fragments (B operand of S^T = K Q^T): query 32*qh + l32, features
-  // 16*s + 8*hh .. +7.  Rows past the last query are clamped (not stored).
+  // 16*s + 8*hh .. +7, loaded once the first tiles are on their way.
   bf16x8 qf[NS];
   const int qrow = 32 * qh + l32;
-  {
-    const int qr = qrow < n_i ? qrow : n_i - 1;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      qf[s] = load8(qp + static_cast<int64_t>(kBlock * i + qr) * sn + 16 * s + 8 * hh);
-  }
 
   const int32_t* __restrict__ crow = A.crit + (static_cast<int64_t>(bh) * g.nq + i) * g.k_crit;
   const int kc = g.k_crit;
@@ -356,16 +350,27 @@ attention_kernel(AttnArgs A) {
     __syncthreads();
   };
 
-  // Q fragments and the critical list are in registers before the loop; a
-  // wait the compiler can see keeps it from guarding their first uses inside
-  // the loop with waits that would then also stall on the tile prefetches.
+  // The critical list is needed for the first tile addresses; the Q loads
+  // go out after those tiles so that both are in flight together.  Q and
+  // the list are in registers before the loop; a wait the compiler can see
+  // keeps it from guarding their first uses inside the loop with waits that
+  // would then also stall on the tile prefetches.  Q rows past the last
+  // query are clamped (not stored).
   wait_vmem();
   f32x16 sa = zero16(), sb = zero16();
   if (kc > 0) {
     issue_tile(true, 0, smem);
     issue_tile(false, 0, smem + 2 * TILE);
     if (kc > 1) issue_tile(true, 1, smem + TILE);
-    wait_vmem();
+  }
+  {
+    const int qr = qrow < n_i ? qrow : n_i - 1;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      qf[s] = load8(qp + static_cast<int64_t>(kBlock * i + qr) * sn + 16 * s + 8 * hh);
+  }
+  wait_vmem();
+  if (kc > 0) {
     __syncthreads();
     bf16x8 kf[NS];
 #pragma unroll
