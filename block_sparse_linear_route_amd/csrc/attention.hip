@@ -215,12 +215,61 @@ attention_kernel(AttnArgs A) {
   auto step = [&](auto xc, int it, f32x16& s_cur, f32x16& s_next) {
     constexpr int X = decltype(xc)::value;
     const uint16_t* kb_next = smem + (X ^ 1) * TILE;
-    // K fragments first: no direct-to-LDS load of this wave is in flight yet
-    // (the previous step ended with vmcnt(0)), so these reads need no wait
-    // on the loads issued right after them.
+    // K and V fragments first: no direct-to-LDS load of this wave is in
+    // flight yet (the previous step ended with vmcnt(0)), so these reads need
+    // no wait on the loads issued right after them.
     bf16x8 kf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kb_next + kofs[s]);
+    // V^T fragments for O^T += V^T P^T, read now (V(it) has been in LDS
+    // since the last barrier) so that one wait covers them and the K
+    // fragments: lane l gets dim 32*dt + l%32 at keys 32*kh + 16*s +
+    // 8*(e/4) + 4*hh + e%4, matching P^T's k-slots.  All 16 transposing reads
+    // and the wait sit in one asm block.
+    constexpr int VOFF0 = (2 + X) * TILE * 2;
+    constexpr int VOFF1 = VOFF0 + 16 * D * 2;
+    u32x2 rd[4 * DT];
+    if constexpr (DT == 4) {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %2, %16 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %3, %17 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %4, %18 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %5, %19 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %6, %18 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %7, %19 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %9, %21 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %10, %20 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %11, %21 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %12, %22 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %13, %23 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(rd[0]), "=&v"(rd[1]), "=&v"(rd[2]), "=&v"(rd[3]), "=&v"(rd[4]), "=&v"(rd[5]),
+            "=&v"(rd[6]), "=&v"(rd[7]), "=&v"(rd[8]), "=&v"(rd[9]), "=&v"(rd[10]), "=&v"(rd[11]),
+            "=&v"(rd[12]), "=&v"(rd[13]), "=&v"(rd[14]), "=&v"(rd[15])
+          : "v"(va1[0]), "v"(va2[0]), "v"(va1[1]), "v"(va2[1]), "v"(va1[2]), "v"(va2[2]),
+            "v"(va1[3]), "v"(va2[3]), "i"(VOFF0), "i"(VOFF1)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %2, %8 offset:%13\n\t"
+          "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+          "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %5, %11 offset:%12\n\t"
+          "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
+          "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(rd[0]), "=&v"(rd[1]), "=&v"(rd[2]), "=&v"(rd[3]), "=&v"(rd[4]), "=&v"(rd[5]),
+            "=&v"(rd[6]), "=&v"(rd[7])
+          : "v"(va1[0]), "v"(va2[0]), "v"(va1[1]), "v"(va2[1]), "i"(VOFF0), "i"(VOFF1)
+          : "memory");
+    }
     if (it + 2 < kc) {
       issue_tile(true, it + 2, smem + X * TILE);
     } else if constexpr (ST_LDS) {
@@ -286,53 +335,6 @@ attention_kernel(AttnArgs A) {
     l_run += ps;
     s_next = acc;
 
-    // O^T += V^T P^T: lane l gets dim 32*dt + l%32 at keys
-    // 32*kh + 16*s + 8*(e/4) + 4*hh + e%4, matching P^T's k-slots.  All 16
-    // transposing reads and their wait sit in one asm block.
-    constexpr int VOFF0 = (2 + X) * TILE * 2;
-    constexpr int VOFF1 = VOFF0 + 16 * D * 2;
-    u32x2 rd[4 * DT];
-    if constexpr (DT == 4) {
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
-          "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
-          "ds_read_b64_tr_b16 %2, %16 offset:%25\n\t"
-          "ds_read_b64_tr_b16 %3, %17 offset:%25\n\t"
-          "ds_read_b64_tr_b16 %4, %18 offset:%24\n\t"
-          "ds_read_b64_tr_b16 %5, %19 offset:%24\n\t"
-          "ds_read_b64_tr_b16 %6, %18 offset:%25\n\t"
-          "ds_read_b64_tr_b16 %7, %19 offset:%25\n\t"
-          "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
-          "ds_read_b64_tr_b16 %9, %21 offset:%24\n\t"
-          "ds_read_b64_tr_b16 %10, %20 offset:%25\n\t"
-          "ds_read_b64_tr_b16 %11, %21 offset:%25\n\t"
-          "ds_read_b64_tr_b16 %12, %22 offset:%24\n\t"
-          "ds_read_b64_tr_b16 %13, %23 offset:%24\n\t"
-          "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
-          "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(rd[0]), "=&v"(rd[1]), "=&v"(rd[2]), "=&v"(rd[3]), "=&v"(rd[4]), "=&v"(rd[5]),
-            "=&v"(rd[6]), "=&v"(rd[7]), "=&v"(rd[8]), "=&v"(rd[9]), "=&v"(rd[10]), "=&v"(rd[11]),
-            "=&v"(rd[12]), "=&v"(rd[13]), "=&v"(rd[14]), "=&v"(rd[15])
-          : "v"(va1[0]), "v"(va2[0]), "v"(va1[1]), "v"(va2[1]), "v"(va1[2]), "v"(va2[2]),
-            "v"(va1[3]), "v"(va2[3]), "i"(VOFF0), "i"(VOFF1)
-          : "memory");
-    } else {
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
-          "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
-          "ds_read_b64_tr_b16 %2, %8 offset:%13\n\t"
-          "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
-          "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
-          "ds_read_b64_tr_b16 %5, %11 offset:%12\n\t"
-          "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
-          "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(rd[0]), "=&v"(rd[1]), "=&v"(rd[2]), "=&v"(rd[3]), "=&v"(rd[4]), "=&v"(rd[5]),
-            "=&v"(rd[6]), "=&v"(rd[7])
-          : "v"(va1[0]), "v"(va2[0]), "v"(va1[1]), "v"(va2[1]), "i"(VOFF0), "i"(VOFF1)
-          : "memory");
-    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       u32x4 w0, w1;
