@@ -93,7 +93,7 @@ def test_route_parity_shapes(N, kc, km, H, seed):
     _route_check(w)
 
 
-@pytest.mark.parametrize("nkb,kc,km", [(700, 30, 60), (2101, 26, 51)])
+@pytest.mark.parametrize("nkb,kc,km", [(700, 30, 60), (2101, 26, 51), (4096, 40, 80)])
 def test_route_parity_long_rows(nkb, kc, km):
     # 16 and 64 keys per lane in the selection kernel
     w = make_custom(1, 1, 64 * nkb - 3, 128, dtype="bf16", kind="fourier1d", seed=nkb,
@@ -259,6 +259,8 @@ def test_forward_parity(name, heads, n_sample):
     (4095, 128, "bf16", 1, 20, 2, 1, 16),       # one critical block: one idle stream
     (4096, 128, "bf16", 7, 9, 1, 1, 17),
     (2500, 64, "bf16", 39, 0, 1, 1, 18),
+    (1, 128, "bf16", 1, 0, 1, 1, 19),           # one token: one block of one row
+    (37, 64, "fp32", 0, 1, 2, 1, 20),           # one short block, linear branch only
 ])
 def test_forward_parity_shapes(N, d, dtype, kc, km, H, B, seed):
     w = make_custom(B, H, N, d, dtype=dtype, kind="fourier1d", seed=seed, k_crit=kc, k_marg=km)
@@ -320,6 +322,13 @@ def test_forward_fuzz(seed):
                     kind="fourier1d", seed=200 + seed, k_crit=kc, k_marg=km)
     _route_check(w)
     _forward_check(w)
+
+
+@pytest.mark.timeout(900)
+def test_forward_parity_video75k():
+    # the largest workload (nq = nkb = 1182, 512-row GEMM tiles plus the
+    # 256-row tail tile); two heads, sampled query blocks
+    _forward_check(make_workload("video75k", cache=False), heads=[(0, 0), (0, 39)], n_sample=16)
 
 
 # ------------------------------------------------------------------ fp8 sparse branch
