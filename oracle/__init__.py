@@ -25,6 +25,10 @@ Sources (page titles as printed; sections as on each page):
   a compact linear-attention state; section 2.3: a parameter-free
   exponential feature map.
 
+Residual linear attention (SPLA technical summary, sections 2.2 and 2.3:
+o_rla = o_bar - o_tilde over all and over the selected blocks, an RMS norm on
+that branch, a gated sum, an exponential feature map) is in ``oracle.rla``.
+
 The block size (64), mean pooling, phi = softmax over the feature dimension,
 H_j = phi(K_j)^T V_j, z_j = column sums of phi(K_j), and the per-head alpha
 are the plain readings this build fixes where the pages leave the step open.

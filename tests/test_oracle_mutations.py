@@ -87,3 +87,45 @@ def test_linear_without_denominator(monkeypatch):
 def test_mix_swapped(monkeypatch):
     monkeypatch.setattr(sla, "mix", lambda o_s, o_l, a: (1 - a) * o_s + a * o_l)
     _fails(pins.test_mix_endpoints_and_affinity)
+
+
+# ------------------------------------------------- residual linear attention
+
+import oracle.rla as rla_mod
+import tests.test_oracle_pins_rla as rla_pins
+
+
+def test_rla_sum_instead_of_difference(monkeypatch):
+    def bad(q, H, crit_idx, block=64, q_blocks=None):
+        n, d = q.shape
+        out = np.zeros((n, H.shape[2]))
+        fq = np.exp(q - q.max(axis=1, keepdims=True))
+        S_all = H.sum(axis=0)
+        for i, (a, b) in enumerate(sla.block_ranges(n, block)):
+            c = crit_idx[i]
+            out[a:b] = fq[a:b] @ S_all + (fq[a:b] @ H[c].sum(axis=0) if len(c) else 0)
+        return out
+    monkeypatch.setattr(rla_mod, "rla_branch", bad)
+    _fails(rla_pins.test_rla_branch_brute_force_over_noncritical_tokens, 40, 4, 8, 2)
+
+
+def test_rla_states_transposed(monkeypatch):
+    orig = rla_mod.linear_states_exp
+
+    def bad(k, v, block=64):
+        H, z = orig(k, v, block)
+        return H.transpose(0, 2, 1).copy(), z
+    monkeypatch.setattr(rla_mod, "linear_states_exp", bad)
+    _fails(rla_pins.test_states_exp_brute_force, 10, 3, 4)
+
+
+def test_rla_rms_over_rows(monkeypatch):
+    monkeypatch.setattr(rla_mod, "rms_norm",
+                        lambda x, eps=1e-6: x / np.sqrt((x * x).mean(axis=0, keepdims=True) + eps))
+    _fails(rla_pins.test_rms_norm_closed_forms)
+
+
+def test_rla_rms_without_eps(monkeypatch):
+    monkeypatch.setattr(rla_mod, "rms_norm",
+                        lambda x, eps=1e-6: x / np.sqrt((x * x).mean(axis=-1, keepdims=True)))
+    _fails(rla_pins.test_rms_norm_closed_forms)
