@@ -9,13 +9,16 @@ from .ops import (  # noqa: F401
     forward,
     forward_attend,
     forward_attend_fp8,
+    forward_attend_rla,
     forward_fp8,
+    forward_rla,
     forward_workspace,
     linear_states,
     make_problem,
     marginal_sums,
     num_blocks,
     quantize_fp8,
+    residual_sums,
     route,
     sla_attention,
     version,

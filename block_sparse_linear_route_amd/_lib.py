@@ -53,6 +53,12 @@ SIGNATURES = {
                                        _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sla_forward_attend_fp8": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                               _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sla_linear_states_exp": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp]),
+    "sla_residual_sums": (ctypes.c_int, [_P, _vp, _vp, _vp, _sz, _vp]),
+    "sla_forward_attend_rla": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _sz, _vp]),
+    "sla_forward_rla": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _sz, _vp]),
     "sla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sla_last_error_message": (ctypes.c_char_p, []),
     "sla_version": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int)] * 3),

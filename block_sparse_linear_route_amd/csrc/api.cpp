@@ -241,7 +241,7 @@ int sla_linear_states(const sla_problem* problem, const void* k, const void* v, 
   SLA_REQ(z_states, 16);
   const sla::Geometry g = geometry(problem);
   SLA_TRY(check_device());
-  return launched(sla::launch_states(g, k, v, static_cast<uint16_t*>(h_states), z_states,
+  return launched(sla::launch_states(g, k, v, static_cast<uint16_t*>(h_states), z_states, false,
                                      static_cast<hipStream_t>(stream)),
                   "sla_linear_states launch");
 }
@@ -271,10 +271,10 @@ int sla_forward(const sla_problem* problem, const void* q, const void* k, const 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.k_marg > 0)
     SLA_TRY(launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
-                                               z_states, w.s_sum, w.sigma, w.bits, s),
+                                               z_states, w.s_sum, w.sigma, w.bits, false, s),
                      "marginal-sum launch"));
   return launched(sla::launch_attention(g, q, k, v, crit_idx, w.s_sum, w.sigma, alpha, o, o_sparse,
-                                        o_linear, s),
+                                        o_linear, false, s),
                   "attention launch");
 }
 
@@ -292,7 +292,7 @@ int sla_marginal_sums(const sla_problem* problem, const int32_t* marg_idx, const
   if (g.k_marg == 0) return SLA_OK;
   const FwdWs w = carve_forward_ws(g, ws);
   return launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
-                                            z_states, w.s_sum, w.sigma, w.bits,
+                                            z_states, w.s_sum, w.sigma, w.bits, false,
                                             static_cast<hipStream_t>(stream)),
                   "marginal-sum launch");
 }
@@ -314,7 +314,7 @@ int sla_forward_attend(const sla_problem* problem, const void* q, const void* k,
   SLA_TRY(check_device());
   const FwdWs w = carve_forward_ws(g, const_cast<void*>(ws));
   return launched(sla::launch_attention(g, q, k, v, crit_idx, w.s_sum, w.sigma, alpha, o, o_sparse,
-                                        o_linear, static_cast<hipStream_t>(stream)),
+                                        o_linear, false, static_cast<hipStream_t>(stream)),
                   "attention launch");
 }
 
@@ -379,7 +379,7 @@ int sla_forward_fp8(const sla_problem* problem, const void* q, const uint8_t* q8
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.k_marg > 0)
     SLA_TRY(launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
-                                               z_states, w.s_sum, w.sigma, w.bits, s),
+                                               z_states, w.s_sum, w.sigma, w.bits, false, s),
                      "marginal-sum launch"));
   return launched(sla::launch_attention_fp8(g, q, q8, q_s, k8, k_s, v8, v_s, crit_idx, w.s_sum,
                                             w.sigma, alpha, o, o_sparse, o_linear, s),
@@ -401,6 +401,81 @@ int sla_forward_attend_fp8(const sla_problem* problem, const void* q, const uint
                                             w.sigma, alpha, o, o_sparse, o_linear,
                                             static_cast<hipStream_t>(stream)),
                   "fp8 attention launch");
+}
+
+// ---------------------------------------------------------------- residual linear attention
+
+int sla_linear_states_exp(const sla_problem* problem, const void* k, const void* v,
+                          void* h_states, float* z_states, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(k, 16);
+  SLA_REQ(v, 16);
+  SLA_REQ(h_states, 16);
+  SLA_REQ(z_states, 16);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_device());
+  return launched(sla::launch_states(g, k, v, static_cast<uint16_t*>(h_states), z_states, true,
+                                     static_cast<hipStream_t>(stream)),
+                  "sla_linear_states_exp launch");
+}
+
+namespace {
+// The residual state covers every non-critical block: k_marg names that count.
+int check_rla_counts(const sla_problem* p) {
+  const int64_t nkb = (static_cast<int64_t>(p->seq_len) + 63) / 64;
+  if (p->k_marg != nkb - p->k_crit)
+    return fail(SLA_ERR_INVALID_ARGUMENT,
+                "residual linear attention sums every non-critical block: k_marg must be "
+                "nkb - k_crit = %lld, got %d", static_cast<long long>(nkb - p->k_crit), p->k_marg);
+  return SLA_OK;
+}
+}  // namespace
+
+int sla_residual_sums(const sla_problem* problem, const int32_t* crit_idx, const void* h_states,
+                      void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_TRY(check_rla_counts(problem));
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  if (problem->k_marg > 0) SLA_REQ(h_states, 16);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, forward_ws(g)));
+  SLA_TRY(check_device());
+  if (g.k_marg == 0) return SLA_OK;
+  const FwdWs w = carve_forward_ws(g, ws);
+  return launched(sla::launch_marginal_sums(g, crit_idx, static_cast<const uint16_t*>(h_states),
+                                            nullptr, w.s_sum, nullptr, w.bits, true,
+                                            static_cast<hipStream_t>(stream)),
+                  "residual-sum launch");
+}
+
+int sla_forward_attend_rla(const sla_problem* problem, const void* q, const void* k, const void* v,
+                           const int32_t* crit_idx, const float* alpha, void* o, float* o_sparse,
+                           float* o_linear, const void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_TRY(check_rla_counts(problem));
+  SLA_REQ(q, 16);
+  SLA_REQ(k, 16);
+  SLA_REQ(v, 16);
+  SLA_REQ(alpha, 4);
+  SLA_REQ(o, 16);
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  SLA_OPT(o_sparse, 16);
+  SLA_OPT(o_linear, 16);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(const_cast<void*>(ws), ws_bytes, forward_ws(g)));
+  SLA_TRY(check_device());
+  const FwdWs w = carve_forward_ws(g, const_cast<void*>(ws));
+  return launched(sla::launch_attention(g, q, k, v, crit_idx, w.s_sum, w.sigma, alpha, o, o_sparse,
+                                        o_linear, true, static_cast<hipStream_t>(stream)),
+                  "attention launch");
+}
+
+int sla_forward_rla(const sla_problem* problem, const void* q, const void* k, const void* v,
+                    const int32_t* crit_idx, const void* h_states, const float* alpha, void* o,
+                    float* o_sparse, float* o_linear, void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(sla_residual_sums(problem, crit_idx, h_states, ws, ws_bytes, stream));
+  return sla_forward_attend_rla(problem, q, k, v, crit_idx, alpha, o, o_sparse, o_linear, ws,
+                                ws_bytes, stream);
 }
 
 const char* sla_status_string(int status) {

@@ -45,7 +45,10 @@ struct AttnArgs {
   float c_log2;      // log2(e) / sqrt(d)
 };
 
-template <typename T, int D>
+// RLA: residual linear attention epilogue (the marginal sum holds every
+// non-critical block's exponential-map state; RMS norm instead of the
+// phi(Q) . sigma_i denominator, so sigma_i is not loaded).
+template <typename T, int D, bool RLA>
 __global__ void __launch_bounds__(kThreads, 2)
 attention_kernel(AttnArgs A) {
   constexpr int CH = D / 8;                    // 16-byte chunks per row
@@ -155,7 +158,7 @@ attention_kernel(AttnArgs A) {
   const bool has_lin = g.k_marg > 0;
   const __amdgpu_buffer_rsrc_t srs =
       make_rsrc(A.s_sum + (static_cast<int64_t>(bh) * g.nq + i) * D * D, D * D * 2);
-  if (has_lin && wave == 0 && lane < D / 4) {
+  if (!RLA && has_lin && wave == 0 && lane < D / 4) {
     const __amdgpu_buffer_rsrc_t sgr =
         make_rsrc(A.sigma_sum + (static_cast<int64_t>(bh) * g.nq + i) * D, D * 4);
     buffer_load_lds16(sgr, sig_lds, 16u * lane, 0u);
@@ -396,16 +399,19 @@ attention_kernel(AttnArgs A) {
   __syncthreads();
 
   const uint16_t* st_half = smem + ((kc & 1) ^ kh) * TILE;
-  attention_finish<T, D, ST_LDS, false>(smem_raw + EPI_OFF, st_half, sig_lds, has_lin, g, bh, h, i,
+  attention_finish<T, D, ST_LDS, false, RLA>(smem_raw + EPI_OFF, st_half, sig_lds, !RLA && has_lin, g, bh, h, i,
                                         n_i, qrow, hoff, A.s_sum, A.sigma_sum, A.alpha, A.o,
                                         A.o_sparse, A.o_linear, oacc, m_run, l_run, cl, qf,
                                         [](int) {});
 }
 
 template <typename T, int D>
-void launch_attn_t(const AttnArgs& a, hipStream_t stream) {
+void launch_attn_t(const AttnArgs& a, bool rla, hipStream_t stream) {
   const int total = a.g.B * a.g.H * a.g.nq;
-  hipLaunchKernelGGL((attention_kernel<T, D>), dim3(total), dim3(kThreads), 0, stream, a);
+  if (rla)
+    hipLaunchKernelGGL((attention_kernel<T, D, true>), dim3(total), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attention_kernel<T, D, false>), dim3(total), dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace
@@ -413,15 +419,15 @@ void launch_attn_t(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,
                             const int32_t* crit, const uint16_t* s_sum, const float* sigma_sum,
                             const float* alpha, void* o, float* o_sparse, float* o_linear,
-                            hipStream_t stream) {
+                            bool rla, hipStream_t stream) {
   AttnArgs a{q, k, v, crit, s_sum, sigma_sum, alpha, o, o_sparse, o_linear, g,
              static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(g.D)))};
   if (g.dtype == 1) {
-    if (g.D == 128) launch_attn_t<uint16_t, 128>(a, stream);
-    else launch_attn_t<uint16_t, 64>(a, stream);
+    if (g.D == 128) launch_attn_t<uint16_t, 128>(a, rla, stream);
+    else launch_attn_t<uint16_t, 64>(a, rla, stream);
   } else {
-    if (g.D == 128) launch_attn_t<float, 128>(a, stream);
-    else launch_attn_t<float, 64>(a, stream);
+    if (g.D == 128) launch_attn_t<float, 128>(a, rla, stream);
+    else launch_attn_t<float, 64>(a, rla, stream);
   }
   return hipGetLastError();
 }

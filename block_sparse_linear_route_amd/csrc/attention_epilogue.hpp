@@ -15,6 +15,12 @@
 //     row normaliser cancels between numerator and denominator);
 //   * mixes O = alpha_h O_s + (1 - alpha_h) O_l ([SLA2 summary, section 2.A
 //     equation]) and stores O, plus O_s / O_l when requested.
+// With kRla (residual linear attention, [SPLA technical summary, sections 2.2
+// and 2.3]) S_i sums every non-critical block's exponential-map state, the
+// linear output phi(Q) S_i is not divided by phi(Q) . sigma_i but RMS-
+// normalised over the d value features of each row (x / sqrt(mean x^2 +
+// 1e-6); the factor exp(-max q) of phi(Q) cancels there), and O_l is that
+// normalised output.
 // m_run is in the units of S; cl converts them to log2 units.
 #pragma once
 
@@ -34,11 +40,14 @@ __device__ __forceinline__ void store4(float* p, const float* x) {
   *reinterpret_cast<f32x4*>(p) = w;
 }
 
-// LDS bytes the epilogue needs at the start of the shared buffer.
+// LDS bytes the epilogue needs at the start of the shared buffer: merge
+// buffers, sigma_i, and the per-row sums of squares of the residual branch.
 template <int D>
 constexpr int epilogue_smem_bytes() {
-  return 4 * (256 + 4 * (D / 64) * 16 * 64) + D * 4;
+  return 4 * (256 + 4 * (D / 64) * 16 * 64) + D * 4 + 4 * 128;
 }
+
+constexpr float kRmsEps = 1e-6f;
 
 // XOR swizzle of the 16-byte chunks of a bf16 tile row (64 rows x D): the
 // operand reads of 16 consecutive rows at one chunk, and the transposing V
@@ -60,7 +69,7 @@ __device__ __forceinline__ int swz(int r) {
 // With kHooks, hook(1) runs once the LDS below merge_lds is no longer read
 // and hook(2) once the merge buffers are no longer read (all waves, after a
 // barrier): a caller can start loads for its next block there.
-template <typename T, int D, bool kStLds, bool kHooks, typename Hook>
+template <typename T, int D, bool kStLds, bool kHooks, bool kRla = false, typename Hook>
 __device__ __forceinline__ void attention_finish(
     unsigned char* merge_lds, const uint16_t* st_half, const float* sg_lds, bool sg_ok,
     const Geometry& g, int bh, int h, int i,
@@ -82,6 +91,7 @@ __device__ __forceinline__ void attention_finish(
   float* lbuf = mbuf + 128;                            // [4][32]
   float* obuf = mbuf + 256;                            // [4][DTH][16][64]
   float* sg = reinterpret_cast<float*>(merge_lds + MERGE_BYTES);  // sigma_i [D]
+  float* rbuf = sg + D;                                            // [4][32] row sums of squares
   const int own0 = kh * DTH;
 
   const float l_full = l_run + xor_lane(l_run, 32);
@@ -140,7 +150,7 @@ __device__ __forceinline__ void attention_finish(
         for (int s = 0; s < NS; ++s)
           sf[u][s] = load8_at(sgl, static_cast<uint32_t>(((32 * (own0 + u) + l32) * D + 16 * s + 8 * hh) * 2));
     }
-    if (!sg_ok && t < D) sg[t] = sigma_sum[row * D + t];
+    if (!kRla && !sg_ok && t < D) sg[t] = sigma_sum[row * D + t];
   }
   __syncthreads();
   if constexpr (kHooks) hook(1);   // every wave has read S_i^T: the LDS below merge_lds is free
@@ -167,7 +177,32 @@ __device__ __forceinline__ void attention_finish(
   f32x16 ol[DTH];
 #pragma unroll
   for (int u = 0; u < DTH; ++u) ol[u] = zero16();
-  if (has_lin) {
+  if constexpr (kRla) {
+    // RMS norm of phi(Q) S_i over the row's D dims: this lane's 16 * DTH, the
+    // partner lane's (l ^ 32) and the other key-half wave's (wave ^ 2) half
+    float ss = 0.0f;
+    if (has_lin) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int u = 0; u < DTH; ++u) ol[u] = mfma32(sf[u][s], pf[s], ol[u]);
+#pragma unroll
+      for (int u = 0; u < DTH; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ss = fmaf(ol[u][r], ol[u][r], ss);
+      ss = swap_sum32(ss);
+      if (hh == 0) rbuf[wave * 32 + l32] = ss;
+    }
+    __syncthreads();
+    if (has_lin) {
+      const float rinv =
+          1.0f / __builtin_sqrtf((ss + rbuf[partner * 32 + l32]) * (1.0f / D) + kRmsEps);
+#pragma unroll
+      for (int u = 0; u < DTH; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ol[u][r] *= rinv;
+    }
+  } else if (has_lin) {
     float dpart = 0.0f;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {

@@ -45,7 +45,11 @@ constexpr int kHBytes = kGK * kGN * 2;    // H chunk bytes (8 KB)
 //    come as scalar loads) and added in list order;
 //  * the mask bit row, OR-ed together in LDS and written chunk-major: word w
 //    of row i lands at [(w / 2) * rows_pad + i] * 2 + w % 2.
-template <int D>
+//
+// COMPL: the list is each row's critical list (k_crit entries) and the bit
+// row written is its complement over the valid KV blocks (the residual set of
+// residual linear attention: every block that is not critical); no sigma.
+template <int D, bool COMPL>
 __global__ void __launch_bounds__(kThreads)
 marg_prep_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __restrict__ zs,
                  float* __restrict__ sigma, uint32_t* __restrict__ bits, int nchunks,
@@ -60,7 +64,7 @@ marg_prep_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __re
   for (int e = threadIdx.x; e < RPB * nw; e += kThreads) sbits[e] = 0u;
   __syncthreads();
 
-  const int km = g.k_marg;
+  const int km = COMPL ? g.k_crit : g.k_marg;
   const bool row_ok = i < g.nq;
   const int32_t* __restrict__ mrow = marg + (static_cast<int64_t>(bh) * g.nq + min(i, g.nq - 1)) * km;
   if (row_ok) {
@@ -69,24 +73,31 @@ marg_prep_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __re
       atomicOr(&sbits[r * nw + (j >> 5)], 1u << (j & 31));
     }
   }
-  const float* __restrict__ zb = zs + static_cast<int64_t>(bh) * g.nkb * D + a;
-  float acc = 0.0f;
-  for (int u0 = 0; u0 < km; u0 += 16) {
-    float v[16];
+  if constexpr (!COMPL) {
+    const float* __restrict__ zb = zs + static_cast<int64_t>(bh) * g.nkb * D + a;
+    float acc = 0.0f;
+    for (int u0 = 0; u0 < km; u0 += 16) {
+      float v[16];
 #pragma unroll
-    for (int x = 0; x < 16; ++x) v[x] = zb[static_cast<int64_t>(mrow[min(u0 + x, km - 1)]) * D];
+      for (int x = 0; x < 16; ++x) v[x] = zb[static_cast<int64_t>(mrow[min(u0 + x, km - 1)]) * D];
 #pragma unroll
-    for (int x = 0; x < 16; ++x)
-      if (u0 + x < km) acc += v[x];
+      for (int x = 0; x < 16; ++x)
+        if (u0 + x < km) acc += v[x];
+    }
+    if (row_ok) sigma[(static_cast<int64_t>(bh) * g.nq + i) * D + a] = acc;
   }
-  if (row_ok) sigma[(static_cast<int64_t>(bh) * g.nq + i) * D + a] = acc;
   __syncthreads();
 
   uint32_t* __restrict__ bout = bits + static_cast<int64_t>(bh) * nchunks * rows_pad * 2;
   for (int e = threadIdx.x; e < RPB * nw; e += kThreads) {
     const int rr = e / nw, w = e % nw;
+    uint32_t word = sbits[e];
+    if constexpr (COMPL) {
+      const int valid = g.nkb - 32 * w;      // KV blocks 32 w .. 32 w + 31 that exist
+      word = ~word & (valid >= 32 ? ~0u : (valid <= 0 ? 0u : (1u << valid) - 1u));
+    }
     if (i0 + rr < g.nq)
-      bout[(static_cast<int64_t>(w >> 1) * rows_pad + i0 + rr) * 2 + (w & 1)] = sbits[e];
+      bout[(static_cast<int64_t>(w >> 1) * rows_pad + i0 + rr) * 2 + (w & 1)] = word;
   }
 }
 
@@ -324,18 +335,24 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
 
 hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const uint16_t* h_states,
                                 const float* z_states, uint16_t* s_sum, float* sigma_sum,
-                                uint32_t* bits, hipStream_t stream) {
+                                uint32_t* bits, bool complement, hipStream_t stream) {
   const int nchunks = marginal_chunks(g);
   const int rows_pad = marginal_rows_pad(g);
   const int rpb = kThreads / g.D;
   dim3 gs((g.nq + rpb - 1) / rpb, g.B * g.H);
   const size_t lds1 = static_cast<size_t>(rpb) * 2 * nchunks * sizeof(uint32_t);
+  auto prep = [&](auto dc, auto cc) {
+    constexpr int DK = decltype(dc)::value;
+    constexpr bool CK = decltype(cc)::value;
+    hipLaunchKernelGGL((marg_prep_kernel<DK, CK>), gs, dim3(kThreads), lds1, stream, g, marg,
+                       z_states, sigma_sum, bits, nchunks, rows_pad);
+  };
   if (g.D == 128) {
-    hipLaunchKernelGGL((marg_prep_kernel<128>), gs, dim3(kThreads), lds1, stream, g, marg,
-                       z_states, sigma_sum, bits, nchunks, rows_pad);
+    if (complement) prep(std::integral_constant<int, 128>(), std::true_type());
+    else prep(std::integral_constant<int, 128>(), std::false_type());
   } else {
-    hipLaunchKernelGGL((marg_prep_kernel<64>), gs, dim3(kThreads), lds1, stream, g, marg,
-                       z_states, sigma_sum, bits, nchunks, rows_pad);
+    if (complement) prep(std::integral_constant<int, 64>(), std::true_type());
+    else prep(std::integral_constant<int, 64>(), std::false_type());
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

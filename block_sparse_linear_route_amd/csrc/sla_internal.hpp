@@ -22,8 +22,9 @@ hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t
                         float* pooled_k, double* ws_qpool, double* ws_kpool_t,
                         hipStream_t stream);
 
+// exp_map: phi(k) = exp(k) elementwise instead of the softmax over features.
 hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16_t* h_states,
-                         float* z_states, hipStream_t stream);
+                         float* z_states, bool exp_map, hipStream_t stream);
 
 // Marginal-state sums S_i = sum_{j in M_i} H_j (bf16, [B,H,nq,d,d], value-major
 // like the states) and sigma_i = sum_{j in M_i} z_j (float, [B,H,nq,d]); bits
@@ -31,14 +32,19 @@ hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16
 // the mask rows (two words per query block and chunk of 64 KV blocks).
 inline int marginal_chunks(const Geometry& g) { return (g.nkb + 63) / 64; }
 inline int marginal_rows_pad(const Geometry& g) { return (g.nq + 511) / 512 * 512; }
+// complement: marg is the critical list (k_crit entries per query block) and
+// S_i sums every KV block outside it (the residual state of residual linear
+// attention); sigma_sum and z_states are not used.
 hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const uint16_t* h_states,
                                 const float* z_states, uint16_t* s_sum, float* sigma_sum,
-                                uint32_t* bits, hipStream_t stream);
+                                uint32_t* bits, bool complement, hipStream_t stream);
 
+// rla: residual linear attention epilogue (s_sum holds every non-critical
+// block's exponential-map state; RMS norm in place of the sigma denominator).
 hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,
                             const int32_t* crit, const uint16_t* s_sum, const float* sigma_sum,
                             const float* alpha, void* o, float* o_sparse, float* o_linear,
-                            hipStream_t stream);
+                            bool rla, hipStream_t stream);
 
 hipError_t launch_quantize_fp8(const Geometry& g, const void* x, uint8_t* codes, float* scales,
                                hipStream_t stream);

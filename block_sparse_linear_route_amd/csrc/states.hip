@@ -6,7 +6,8 @@
 // compact linear-attention state.  Here:
 //   H_j = phi(K_j)^T V_j   (d x d, bf16 out, float32 accumulation)
 //   z_j = sum over the block's tokens of phi(k)   (d, float32)
-// with phi = softmax over the d features, evaluated in float32.  H_j is
+// with phi = softmax over the d features, evaluated in float32, or (the
+// exponential map of residual linear attention) phi(k) = exp(k).  H_j is
 // stored value-major, element [c][a] = sum_n v_n[c] phi(k_n)[a] (that is,
 // H_j^T row-major), the operand layout in which the marginal sums feed the
 // matrix cores of the attention kernel directly.
@@ -22,7 +23,9 @@
 namespace sla {
 namespace {
 
-template <typename T, int D>
+// EXPMAP: phi(k) = exp(k) elementwise, with no per-token normalisation
+// ([SPLA technical summary, section 2.3] parameter-free exponential map).
+template <typename T, int D, bool EXPMAP>
 __global__ void __launch_bounds__(kThreads)
 states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
               uint16_t* __restrict__ h_out, float* __restrict__ z_out) {
@@ -55,26 +58,31 @@ states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
     load8_f32(v + off + 8 * c, vv + 8 * c);
   }
 
-  // phi(k) = softmax over the d features of the token (4 lanes per token:
-  // quad_perm DPP moves give the partners)
-  float mx = vmax3(kv[0], kv[1], kv[2]);
+  if constexpr (EXPMAP) {
 #pragma unroll
-  for (int c = 3; c + 1 < CW; c += 2) mx = vmax3(mx, kv[c], kv[c + 1]);
-  if (CW % 2 == 0) mx = vmax3(mx, kv[CW - 1], kv[CW - 1]);
-  mx = vmax3(mx, dpp_f<0xB1>(mx), dpp_f<0x4E>(mx));
-  mx = vmax3(mx, dpp_f<0x4E>(mx), dpp_f<0x4E>(mx));
-  const float mb = mx * kLog2e;
-  float sum = 0.0f;
+    for (int c = 0; c < CW; ++c) kv[c] = valid ? __builtin_amdgcn_exp2f(kv[c] * kLog2e) : 0.0f;
+  } else {
+    // phi(k) = softmax over the d features of the token (4 lanes per token:
+    // quad_perm DPP moves give the partners)
+    float mx = vmax3(kv[0], kv[1], kv[2]);
 #pragma unroll
-  for (int c = 0; c < CW; ++c) {
-    kv[c] = __builtin_amdgcn_exp2f(fmaf(kv[c], kLog2e, -mb));
-    sum += kv[c];
+    for (int c = 3; c + 1 < CW; c += 2) mx = vmax3(mx, kv[c], kv[c + 1]);
+    if (CW % 2 == 0) mx = vmax3(mx, kv[CW - 1], kv[CW - 1]);
+    mx = vmax3(mx, dpp_f<0xB1>(mx), dpp_f<0x4E>(mx));
+    mx = vmax3(mx, dpp_f<0x4E>(mx), dpp_f<0x4E>(mx));
+    const float mb = mx * kLog2e;
+    float sum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      kv[c] = __builtin_amdgcn_exp2f(fmaf(kv[c], kLog2e, -mb));
+      sum += kv[c];
+    }
+    sum += dpp_f<0xB1>(sum);
+    sum += dpp_f<0x4E>(sum);
+    const float inv = valid ? 1.0f / sum : 0.0f;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) kv[c] *= inv;
   }
-  sum += dpp_f<0xB1>(sum);
-  sum += dpp_f<0x4E>(sum);
-  const float inv = valid ? 1.0f / sum : 0.0f;
-#pragma unroll
-  for (int c = 0; c < CW; ++c) kv[c] *= inv;
 
   // z: column sums over the wave's 16 tokens (lanes part + 4m: row_ror 4
   // and 8 inside each row of 16, then the row and half swaps), then over
@@ -142,22 +150,26 @@ states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
 
 template <typename T, int D>
 void launch_states_t(const Geometry& g, const void* k, const void* v, uint16_t* hs, float* zs,
-                     hipStream_t stream) {
+                     bool exp_map, hipStream_t stream) {
   dim3 grid(g.nkb, g.B * g.H);
-  hipLaunchKernelGGL((states_kernel<T, D>), grid, dim3(kThreads), 0, stream,
-                     static_cast<const T*>(k), static_cast<const T*>(v), g, hs, zs);
+  if (exp_map)
+    hipLaunchKernelGGL((states_kernel<T, D, true>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const T*>(k), static_cast<const T*>(v), g, hs, zs);
+  else
+    hipLaunchKernelGGL((states_kernel<T, D, false>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const T*>(k), static_cast<const T*>(v), g, hs, zs);
 }
 
 }  // namespace
 
 hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16_t* h_states,
-                         float* z_states, hipStream_t stream) {
+                         float* z_states, bool exp_map, hipStream_t stream) {
   if (g.dtype == 1) {
-    if (g.D == 128) launch_states_t<uint16_t, 128>(g, k, v, h_states, z_states, stream);
-    else launch_states_t<uint16_t, 64>(g, k, v, h_states, z_states, stream);
+    if (g.D == 128) launch_states_t<uint16_t, 128>(g, k, v, h_states, z_states, exp_map, stream);
+    else launch_states_t<uint16_t, 64>(g, k, v, h_states, z_states, exp_map, stream);
   } else {
-    if (g.D == 128) launch_states_t<float, 128>(g, k, v, h_states, z_states, stream);
-    else launch_states_t<float, 64>(g, k, v, h_states, z_states, stream);
+    if (g.D == 128) launch_states_t<float, 128>(g, k, v, h_states, z_states, exp_map, stream);
+    else launch_states_t<float, 64>(g, k, v, h_states, z_states, exp_map, stream);
   }
   return hipGetLastError();
 }

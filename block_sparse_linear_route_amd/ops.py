@@ -117,16 +117,22 @@ def route(q: torch.Tensor, k: torch.Tensor, k_crit: int, k_marg: int, *, want_cl
     return out
 
 
-def linear_states(k: torch.Tensor, v: torch.Tensor, stream=None):
-    """Per-block states: H bf16 [B,H,nkb,d,d], z float32 [B,H,nkb,d]."""
+def linear_states(k: torch.Tensor, v: torch.Tensor, stream=None, *, feature_map: str = "softmax"):
+    """Per-block states: H bf16 [B,H,nkb,d,d], z float32 [B,H,nkb,d].
+
+    ``feature_map``: "softmax" (softmax over the features, the linear branch
+    of ``forward``) or "exp" (exp(k) elementwise, the residual branch of
+    ``forward_rla``)."""
+    if feature_map not in ("softmax", "exp"):
+        raise SlaError(_lib.SLA_ERR_INVALID_ARGUMENT, f"unknown feature map {feature_map!r}")
     (v,) = _same_layout(k, v)
     p = make_problem(k, 0, 1)
     B, H, N, d = k.shape
     nb = num_blocks(N)
     Hs = torch.empty((B, H, nb, d, d), dtype=torch.bfloat16, device=k.device)
     zs = torch.empty((B, H, nb, d), dtype=torch.float32, device=k.device)
-    _check(lib.sla_linear_states(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(Hs), _ptr(zs),
-                                 _stream(stream)))
+    fn = lib.sla_linear_states if feature_map == "softmax" else lib.sla_linear_states_exp
+    _check(fn(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(Hs), _ptr(zs), _stream(stream)))
     return Hs, zs
 
 
@@ -181,6 +187,60 @@ def forward_attend(q, k, v, crit_idx, alpha, workspace, *, k_marg: int, branches
     _check(lib.sla_forward_attend(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
                                   _ptr(crit_idx.contiguous()), _ptr(alpha), _ptr(out), _ptr(o_s),
                                   _ptr(o_l), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (out, o_s, o_l) if branches else out
+
+
+def residual_sums(q, crit_idx, h_states, workspace, *, stream=None):
+    """First phase of ``forward_rla``: S_i = sum of the exponential-map states
+    of every non-critical KV block, into ``workspace``."""
+    kc = int(crit_idx.shape[-1])
+    p = make_problem(q, kc, num_blocks(q.shape[2]) - kc)
+    _check(lib.sla_residual_sums(ctypes.byref(p), _ptr(crit_idx.contiguous()), _ptr(h_states),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def forward_attend_rla(q, k, v, crit_idx, alpha, workspace, *, branches: bool = False, out=None,
+                       stream=None):
+    """Second phase of ``forward_rla``: exact sparse branch, RMS-normalised
+    residual branch from the sums in ``workspace``, gated by alpha."""
+    k, v = _same_layout(q, k, v)
+    kc = int(crit_idx.shape[-1])
+    p = make_problem(q, kc, num_blocks(q.shape[2]) - kc)
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    o_s = o_l = None
+    if branches:
+        o_s = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        o_l = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    alpha = alpha.to(device=q.device, dtype=torch.float32).contiguous()
+    _check(lib.sla_forward_attend_rla(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(crit_idx.contiguous()), _ptr(alpha), _ptr(out),
+                                      _ptr(o_s), _ptr(o_l), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)))
+    return (out, o_s, o_l) if branches else out
+
+
+def forward_rla(q, k, v, crit_idx, h_states, alpha, *, branches: bool = False, out=None,
+                workspace=None, stream=None):
+    """Residual linear attention forward: O = alpha O_s + (1 - alpha) RMSNorm(phi(Q) S_i)
+    with S_i over every non-critical block (``h_states`` from ``linear_states(...,
+    feature_map="exp")``).  Returns O (and O_s, the normalised residual branch if
+    ``branches``)."""
+    k, v = _same_layout(q, k, v)
+    kc = int(crit_idx.shape[-1])
+    p = make_problem(q, kc, num_blocks(q.shape[2]) - kc)
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    o_s = o_l = None
+    if branches:
+        o_s = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        o_l = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    ws = workspace if workspace is not None else _workspace(p, _lib.OP_FORWARD, q.device)
+    alpha = alpha.to(device=q.device, dtype=torch.float32).contiguous()
+    _check(lib.sla_forward_rla(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(crit_idx.contiguous()), _ptr(h_states), _ptr(alpha),
+                               _ptr(out), _ptr(o_s), _ptr(o_l), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(stream)))
     return (out, o_s, o_l) if branches else out
 
 

@@ -68,7 +68,7 @@ extern "C" {
 #endif
 
 #define SLA_VERSION_MAJOR 0
-#define SLA_VERSION_MINOR 1
+#define SLA_VERSION_MINOR 2
 #define SLA_VERSION_PATCH 0
 
 /* Status codes. */
@@ -228,6 +228,46 @@ int sla_forward_attend_fp8(const sla_problem* problem, const void* q,
                            const int32_t* crit_idx, const float* alpha, void* o,
                            float* o_sparse, float* o_linear, const void* ws,
                            size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Residual linear attention.  [SPLA technical summary, sections 2.2 and 2.3]
+ * The blocks a query block does not select feed a linear-attention state
+ * instead of being dropped, written as o_rla = o_bar - o_tilde (linear
+ * attention over all blocks minus over the selected ones) with an
+ * exponential feature map; the output is a gated sum of the exact sparse
+ * branch and the RMS-normalised residual branch:
+ *   O = alpha_h O_s + (1 - alpha_h) RMSNorm(phi(Q) S_i),
+ *   S_i = sum over the KV blocks j not critical for query block i of H_j,
+ *   H_j = exp(K_j)^T V_j,  phi(q) = exp(q - max q) (the RMS norm removes
+ *   that per-row factor), RMSNorm(x) = x / sqrt(mean over the d features of
+ *   x^2 + 1e-6) with unit scale.
+ * The selected blocks are the critical ones; every other KV block is in the
+ * residual state, so these calls need problem->k_marg == nkb - k_crit
+ * (SLA_ERR_INVALID_ARGUMENT otherwise) and no marginal list.
+ *
+ * sla_linear_states_exp: as sla_linear_states with phi(k) = exp(k)
+ *   elementwise (no per-token normalisation; float32, so keys must stay
+ *   below about 88); h_states / z_states layouts as there.
+ * sla_residual_sums: writes S_i (bf16 [B,H,nq,d,d], value-major) into the
+ *   forward workspace (sla_workspace_size(SLA_OP_FORWARD) bytes) from the
+ *   critical lists and the exponential-map states; the sigma region is not
+ *   written.
+ * sla_forward_attend_rla: the fused forward reading S_i from that workspace;
+ *   o_linear (when not NULL) receives RMSNorm(phi(Q) S_i).
+ * sla_forward_rla: sla_residual_sums then sla_forward_attend_rla on one
+ *   stream. */
+int sla_linear_states_exp(const sla_problem* problem, const void* k, const void* v,
+                          void* h_states, float* z_states, void* stream);
+int sla_residual_sums(const sla_problem* problem, const int32_t* crit_idx,
+                      const void* h_states, void* ws, size_t ws_bytes, void* stream);
+int sla_forward_attend_rla(const sla_problem* problem, const void* q, const void* k,
+                           const void* v, const int32_t* crit_idx, const float* alpha,
+                           void* o, float* o_sparse, float* o_linear, const void* ws,
+                           size_t ws_bytes, void* stream);
+int sla_forward_rla(const sla_problem* problem, const void* q, const void* k, const void* v,
+                    const int32_t* crit_idx, const void* h_states, const float* alpha,
+                    void* o, float* o_sparse, float* o_linear, void* ws, size_t ws_bytes,
+                    void* stream);
 
 /* Host: static text of a status code. */
 const char* sla_status_string(int status);

@@ -90,7 +90,7 @@ def test_status_strings_and_version():
         assert lib.sla_status_string(s)
     a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     assert lib.sla_version(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 0
-    assert (a.value, b.value, c.value) == (0, 1, 0)
+    assert (a.value, b.value, c.value) == (0, 2, 0)
 
 
 def test_entry_points_reject_bad_arguments_before_any_device_call():
@@ -130,4 +130,26 @@ def test_entry_points_reject_bad_arguments_before_any_device_call():
                                     fake, 1 << 40, None)
     assert st == _lib.SLA_ERR_INVALID_ARGUMENT       # q8 missing
     st = lib.sla_forward_attend_fp8(ctypes.byref(p), *([fake] * 10), None, None, fake, 16, None)
+    assert st == _lib.SLA_ERR_WORKSPACE
+
+
+def test_residual_entry_points_reject_bad_arguments_before_any_device_call():
+    fake = ctypes.c_void_p(0x10000)
+    p = P()                                  # k_marg = 3 != 16 - 2: not the complement
+    st = lib.sla_forward_rla(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None, None,
+                             fake, 1 << 40, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT
+    assert b"k_marg must be" in lib.sla_last_error_message()
+    r = P(k_crit=2, k_marg=14)               # nkb = 16: every non-critical block
+    st = lib.sla_residual_sums(ctypes.byref(r), fake, fake, fake, 16, None)
+    assert st == _lib.SLA_ERR_WORKSPACE
+    st = lib.sla_residual_sums(ctypes.byref(r), None, fake, fake, 1 << 40, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT      # critical list missing
+    st = lib.sla_forward_attend_rla(ctypes.byref(r), fake, fake, fake, fake, None, fake, None, None,
+                                    fake, 1 << 40, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT      # alpha missing
+    st = lib.sla_linear_states_exp(ctypes.byref(r), fake, None, fake, fake, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT
+    all_crit = P(k_crit=16, k_marg=0)        # no residual block: no states needed
+    st = lib.sla_residual_sums(ctypes.byref(all_crit), fake, None, fake, 16, None)
     assert st == _lib.SLA_ERR_WORKSPACE
