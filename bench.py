@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=6,
                     help="heads the oracle runs for the CPU baseline (scaled to all heads)")
+    ap.add_argument("--no-rla", action="store_true",
+                    help="skip the residual-linear-attention side measurement")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this size (PMC calibration)")
     args = ap.parse_args()
@@ -233,6 +235,56 @@ def main():
                     "same routing, states and executed FLOPs as the bf16 step",
         }
 
+    rla_variant = None
+    if not fp8 and not args.no_rla:
+        # residual linear attention on the same inputs: the critical split of
+        # the step, every other block in the residual state
+        nb = (N + 63) // 64
+        ws_r = sla_gpu.forward_workspace(q, kc, nb - kc)
+
+        def rla_step(ev=None):
+            def mark(n):
+                if ev is not None:
+                    ev[n].record()
+            mark(0)
+            rr = sla_gpu.route(q, k, kc, nb - kc)
+            mark(1)
+            He, _ = sla_gpu.linear_states(k, v, feature_map="exp")
+            mark(2)
+            sla_gpu.residual_sums(q, rr["crit_idx"], He, ws_r)
+            mark(3)
+            orla = sla_gpu.forward_attend_rla(q, k, v, rr["crit_idx"], alpha, ws_r)
+            mark(4)
+            return rr, orla
+
+        for _ in range(2):
+            rla_step()
+        n_r = max(3, args.steps // 2)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_r)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n_r):
+            rr, _ = rla_step(evs[i])
+        torch.cuda.synchronize()
+        ms_r = (time.perf_counter() - t0) * 1e3 / n_r
+        pr = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
+                       for i in range(n_r)]).mean(axis=0)
+        fr_crit, fr_lin, fr_sums = executed_flops(rr["crit_idx"].cpu().numpy(),
+                                                  rr["marg_idx"].cpu().numpy(), N, d)
+        fr_fwd = fr_crit + fr_lin + fr_sums
+        rla_variant = {
+            "ms_per_step": ms_r,
+            "forward_ms": float(pr[2] + pr[3]),
+            "breakdown_ms": {"route": pr[0], "linear_states_exp": pr[1],
+                             "residual_sums": pr[2], "attention_rla": pr[3]},
+            "forward_tflops": fr_fwd / ((pr[2] + pr[3]) * 1e-3) / 1e12,
+            "attention_rla_tflops": (fr_crit + fr_lin) / (pr[3] * 1e-3) / 1e12,
+            "note": "residual linear attention: same critical split, residual state = the "
+                    f"{nb - kc} non-critical blocks, exponential feature map, RMS-normalised "
+                    "residual branch; executed FLOPs count the residual sums as k_m (d^2 + d) "
+                    "per query block",
+        }
+
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -290,6 +342,8 @@ def main():
     }
     if fp8_variant is not None:
         out["fp8_sparse_branch"] = fp8_variant
+    if rla_variant is not None:
+        out["residual_linear_attention"] = rla_variant
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, kc, km, f_step, args.cpu_heads)
     print(json.dumps(out), flush=True)
