@@ -129,3 +129,45 @@ def test_rla_rms_without_eps(monkeypatch):
     monkeypatch.setattr(rla_mod, "rms_norm",
                         lambda x, eps=1e-6: x / np.sqrt((x * x).mean(axis=-1, keepdims=True)))
     _fails(rla_pins.test_rms_norm_closed_forms)
+
+
+from oracle import taylor as taylor_mod
+import tests.test_oracle_pins_taylor as taylor_pins
+
+
+def test_taylor_without_half(monkeypatch):
+    def bad(qp, kp, kv):
+        d = qp.shape[1]
+        return (qp @ kp.T) / math.sqrt(d) + np.log1p(((qp * qp) @ kv.T) / d)
+    monkeypatch.setattr(taylor_mod, "taylor_logits", bad)
+    _fails(taylor_pins.test_score_matches_block_mass_to_fourth_order, 1e-2)
+
+
+def test_taylor_unscaled_second_order(monkeypatch):
+    def bad(qp, kp, kv):
+        d = qp.shape[1]
+        return (qp @ kp.T) / math.sqrt(d) + np.log1p(((qp * qp) @ kv.T) / 2.0)
+    monkeypatch.setattr(taylor_mod, "taylor_logits", bad)
+    _fails(taylor_pins.test_score_matches_block_mass_to_fourth_order, 1e-2)
+
+
+def test_taylor_sample_variance(monkeypatch):
+    def bad(x, block=64):
+        n, d = x.shape
+        out = np.zeros((sla.n_blocks(n, block), d))
+        for j, (a, b) in enumerate(sla.block_ranges(n, block)):
+            if b - a > 1:
+                out[j] = x[a:b].var(axis=0, ddof=1)
+        return out
+    monkeypatch.setattr(taylor_mod, "block_variance", bad)
+    _fails(taylor_pins.test_block_variance_brute_force_with_short_tail)
+
+
+def test_taylor_variance_of_queries(monkeypatch):
+    # the spread term taken over the query blocks instead of the key blocks
+    orig = taylor_mod.route_taylor
+
+    def bad(q, k, kc, km, block=64):
+        return orig(k, q, kc, km, block)
+    monkeypatch.setattr(taylor_mod, "route_taylor", bad)
+    _fails(taylor_pins.test_zero_variance_gives_the_sla_route)
