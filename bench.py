@@ -285,6 +285,27 @@ def main():
                     "per query block",
         }
 
+    # the second-order routing score on the same inputs (route only: the
+    # forward that follows is the same kernels on its index lists)
+    for _ in range(2):
+        sla_gpu.route(q, k, kc, km, score="taylor")
+    n_t = max(3, args.steps // 2)
+    evt = [torch.cuda.Event(enable_timing=True) for _ in range(n_t + 1)]
+    evt[0].record()
+    for i in range(n_t):
+        rt = sla_gpu.route(q, k, kc, km, score="taylor")
+        evt[i + 1].record()
+    torch.cuda.synchronize()
+    taylor_ms = float(np.mean([evt[i].elapsed_time(evt[i + 1]) for i in range(n_t)]))
+    same = ((rt["crit_idx"] == r["crit_idx"]).all(-1) & (rt["marg_idx"] == r["marg_idx"]).all(-1))
+    taylor_route = {
+        "route_ms": taylor_ms,
+        "mean_score_route_ms": float(route_ms),
+        "rows_split_differently": float(1.0 - same.float().mean().item()),
+        "note": "sla_route_taylor: pooled means plus per-block key variances, score "
+                "qbar.kbar/sqrt(d) + log1p(qbar^2 . var / 2d), same top-k split",
+    }
+
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -344,6 +365,7 @@ def main():
         out["fp8_sparse_branch"] = fp8_variant
     if rla_variant is not None:
         out["residual_linear_attention"] = rla_variant
+    out["taylor_routing"] = taylor_route
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, kc, km, f_step, args.cpu_heads)
     print(json.dumps(out), flush=True)

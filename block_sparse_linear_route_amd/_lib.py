@@ -19,7 +19,7 @@ SLA_ERR_DEVICE = -4
 SLA_ERR_NO_DEVICE = -5
 
 SLA_F32, SLA_BF16 = 0, 1
-OP_ROUTE, OP_LINEAR_STATES, OP_FORWARD, OP_QUANTIZE_FP8, OP_FORWARD_FP8 = range(5)
+OP_ROUTE, OP_LINEAR_STATES, OP_FORWARD, OP_QUANTIZE_FP8, OP_FORWARD_FP8, OP_ROUTE_TAYLOR = range(6)
 
 
 class Problem(ctypes.Structure):
@@ -42,6 +42,8 @@ SIGNATURES = {
     "sla_num_blocks": (ctypes.c_int, [_P, _i32p, _i32p]),
     "sla_workspace_size": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_sz)]),
     "sla_route": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sla_route_taylor": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _sz, _vp]),
     "sla_linear_states": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp]),
     "sla_forward": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _sz, _vp]),

@@ -165,10 +165,13 @@ FwdWs carve_forward_ws(const sla::Geometry& g, void* ws) {
   return w;
 }
 
-size_t route_ws(const sla::Geometry& g) {
-  const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
-  return 2 * align_up(rows * g.D * 8);
+// Route workspace: [pooled Q f64 B*H*nq*d][pooled K^T f64 B*H*d*nkb]
+// and, for the second-order score, [key variances^T f64 B*H*d*nkb].
+size_t route_region(const sla::Geometry& g) {
+  return align_up(static_cast<size_t>(g.B) * g.H * g.nq * g.D * 8);
 }
+size_t route_ws(const sla::Geometry& g) { return 2 * route_region(g); }
+size_t route_taylor_ws(const sla::Geometry& g) { return 3 * route_region(g); }
 
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return SLA_OK;
@@ -206,6 +209,7 @@ int sla_workspace_size(const sla_problem* problem, int op, size_t* bytes) {
     case SLA_OP_FORWARD: *bytes = forward_ws(g); return SLA_OK;
     case SLA_OP_QUANTIZE_FP8: *bytes = 0; return SLA_OK;
     case SLA_OP_FORWARD_FP8: *bytes = forward_ws(g); return SLA_OK;
+    case SLA_OP_ROUTE_TAYLOR: *bytes = route_taylor_ws(g); return SLA_OK;
     default: return fail(SLA_ERR_INVALID_ARGUMENT, "unknown op %d", op);
   }
 }
@@ -225,11 +229,37 @@ int sla_route(const sla_problem* problem, const void* q, const void* k, int32_t*
   SLA_TRY(check_ws(ws, ws_bytes, route_ws(g)));
   SLA_TRY(check_device());
   double* qpool = static_cast<double*>(ws);
-  double* kpool_t = reinterpret_cast<double*>(static_cast<char*>(ws) + route_ws(g) / 2);
+  double* kpool_t = reinterpret_cast<double*>(static_cast<char*>(ws) + route_region(g));
   return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
-                                    pooled_q, pooled_k, qpool, kpool_t,
+                                    pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr,
                                     static_cast<hipStream_t>(stream)),
                   "sla_route launch");
+}
+
+int sla_route_taylor(const sla_problem* problem, const void* q, const void* k, int32_t* crit_idx,
+                     int32_t* marg_idx, int8_t* block_class, float* block_logits,
+                     float* pooled_q, float* pooled_k, float* key_var, void* ws, size_t ws_bytes,
+                     void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(q, 16);
+  SLA_REQ(k, 16);
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  if (problem->k_marg > 0) SLA_REQ(marg_idx, 4);
+  SLA_OPT(block_logits, 4);
+  SLA_OPT(pooled_q, 4);
+  SLA_OPT(pooled_k, 4);
+  SLA_OPT(key_var, 4);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, route_taylor_ws(g)));
+  SLA_TRY(check_device());
+  char* p = static_cast<char*>(ws);
+  double* qpool = reinterpret_cast<double*>(p);
+  double* kpool_t = reinterpret_cast<double*>(p + route_region(g));
+  double* kvar_t = reinterpret_cast<double*>(p + 2 * route_region(g));
+  return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
+                                    pooled_q, pooled_k, qpool, kpool_t, kvar_t, key_var,
+                                    static_cast<hipStream_t>(stream)),
+                  "sla_route_taylor launch");
 }
 
 int sla_linear_states(const sla_problem* problem, const void* k, const void* v, void* h_states,

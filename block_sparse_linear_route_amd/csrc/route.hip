@@ -7,7 +7,10 @@
 //
 // Pooling sums bf16/f32 rows in float64 (exact for bf16 blocks) and divides
 // by the valid token count; logits are float64 dot products divided by
-// sqrt(d).  The selection is an exact radix select over a 64-bit key that
+// sqrt(d).  The second-order score of [SPLA technical summary, section 2.1]
+// adds log1p(sum_a qbar_a^2 var_a / (2 d)), var_a the population variance of
+// feature a over the KV block's valid keys (two passes in float64 over the
+// block held in registers).  The selection is an exact radix select over a 64-bit key that
 // orders logits descending, so the split is the one the float64 logits
 // define; equal logits are ordered by ascending KV block index.  Compaction
 // writes each class's KV block indices in ascending order.
@@ -21,16 +24,20 @@ namespace {
 // grid (nb, B*H, 2): z = 0 pools Q, z = 1 pools K.  One workgroup per block:
 // thread t reads the 16-byte chunk t % CH of rows t / CH + RG m (rows past
 // a ragged end load the block's last row and are zeroed, so every load is in
-// flight at once), then LDS sums the row groups in float64.
-template <typename T, int D>
+// flight at once), then LDS sums the row groups in float64.  VAR adds, for
+// K blocks, a second pass: squared deviations from the block mean, summed
+// the same way.
+template <typename T, int D, bool VAR>
 __global__ void __launch_bounds__(kThreads)
 pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g,
             double* __restrict__ qpool, double* __restrict__ kpool_t,
-            float* __restrict__ qout, float* __restrict__ kout) {
+            float* __restrict__ qout, float* __restrict__ kout,
+            double* __restrict__ kvar_t, float* __restrict__ vout) {
   constexpr int CH = D / 8;           // 8-element chunks per row
   constexpr int RG = kThreads / CH;   // row groups
   constexpr int RPG = kBlock / RG;    // rows per group
   __shared__ double red[RG][D];
+  __shared__ double mean_s[VAR ? D : 1];
 
   const int j = blockIdx.x;
   const int bh = blockIdx.y;
@@ -68,6 +75,32 @@ pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g,
     } else {
       kpool_t[(static_cast<int64_t>(bh) * D + t) * g.nkb + j] = m;
       if (kout) kout[(static_cast<int64_t>(bh) * g.nkb + j) * D + t] = static_cast<float>(m);
+      if constexpr (VAR) mean_s[t] = m;
+    }
+  }
+  if constexpr (VAR) {
+    if (which == 1) {          // uniform over the workgroup
+      __syncthreads();         // means visible, first-pass reads of red done
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double me = mean_s[ch * 8 + e];
+        acc[e] = 0.0;
+#pragma unroll
+        for (int rr = 0; rr < RPG; ++rr) {
+          const double dv = static_cast<double>(f[rr][e]) - me;
+          acc[e] += rg + rr * RG < nj ? dv * dv : 0.0;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[rg][ch * 8 + e] = acc[e];
+      __syncthreads();
+      if (t < D) {
+        double s = 0.0;
+        for (int r = 0; r < RG; ++r) s += red[r][t];
+        const double var = s / static_cast<double>(nj);
+        kvar_t[(static_cast<int64_t>(bh) * D + t) * g.nkb + j] = var;
+        if (vout) vout[(static_cast<int64_t>(bh) * g.nkb + j) * D + t] = static_cast<float>(var);
+      }
     }
   }
 }
@@ -271,13 +304,17 @@ __device__ __forceinline__ void select_row(const uint64_t* rk, int nkb, int lane
 // against them, so each pooled-K value read serves R logits; the pooled-Q
 // rows are uniform across the workgroup and are read as scalar operands,
 // each serving two logits.  Results go to LDS as keys.
+// TAYLOR accumulates the second-order term beside the dot product, from the
+// same scalar pooled-Q values squared and the block variances laid out like
+// the pooled K.
 // Phase 2: one wave per query block (select_row).
 constexpr int kFC = 4;
 
-template <int R, int KPL>
+template <int R, int KPL, bool TAYLOR>
 __global__ void __launch_bounds__(kThreads)
 select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
-              const double* __restrict__ kpool_t, double sqrt_d, int32_t* __restrict__ crit,
+              const double* __restrict__ kpool_t, const double* __restrict__ kvar_t,
+              double sqrt_d, double inv_2d, int32_t* __restrict__ crit,
               int32_t* __restrict__ marg, int8_t* __restrict__ cls,
               float* __restrict__ logits_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
@@ -294,23 +331,31 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
   for (int r = 0; r < R; ++r)
     qrow[r] = qpool + (static_cast<int64_t>(bh) * nq + min(i0 + r, nq - 1)) * D;
   const double* kt = kpool_t + static_cast<int64_t>(bh) * D * nkb;
+  const double* vt = TAYLOR ? kvar_t + static_cast<int64_t>(bh) * D * nkb : nullptr;
 
   // Two KV blocks per thread (j and j + 256); kFC features per step, the next
   // step's pooled-K values loaded before this step's FMAs.
   for (int j0 = t; j0 < nkbp; j0 += 2 * kThreads) {
     const int jj[2] = {j0, j0 + kThreads};
     const int64_t jl[2] = {jj[0] < nkb ? jj[0] : 0, jj[1] < nkb ? jj[1] : 0};
-    double acc[2][R];
+    double acc[2][R], acc2[TAYLOR ? 2 : 1][TAYLOR ? R : 1];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[x][r] = 0.0;
+      for (int r = 0; r < R; ++r) {
+        acc[x][r] = 0.0;
+        if constexpr (TAYLOR) acc2[x][r] = 0.0;
+      }
     const int qz = 0;
     double kv[2][kFC], qv[R][kFC];
+    double vv[TAYLOR ? 2 : 1][kFC], vn[TAYLOR ? 2 : 1][kFC];
 #pragma unroll
     for (int e = 0; e < kFC; ++e) {
 #pragma unroll
-      for (int x = 0; x < 2; ++x) kv[x][e] = kt[static_cast<int64_t>(e) * nkb + jl[x]];
+      for (int x = 0; x < 2; ++x) {
+        kv[x][e] = kt[static_cast<int64_t>(e) * nkb + jl[x]];
+        if constexpr (TAYLOR) vv[x][e] = vt[static_cast<int64_t>(e) * nkb + jl[x]];
+      }
 #pragma unroll
       for (int r = 0; r < R; ++r) qv[r][e] = qrow[r][e + qz];
     }
@@ -321,7 +366,10 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
 #pragma unroll
       for (int e = 0; e < kFC; ++e) {
 #pragma unroll
-        for (int x = 0; x < 2; ++x) kn[x][e] = kt[static_cast<int64_t>(an + e) * nkb + jl[x]];
+        for (int x = 0; x < 2; ++x) {
+          kn[x][e] = kt[static_cast<int64_t>(an + e) * nkb + jl[x]];
+          if constexpr (TAYLOR) vn[x][e] = vt[static_cast<int64_t>(an + e) * nkb + jl[x]];
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r) qn[r][e] = qrow[r][an + e + qz];
       }
@@ -331,11 +379,19 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
         for (int e = 0; e < kFC; ++e) {
           acc[0][r] = fma(qv[r][e], kv[0][e], acc[0][r]);
           acc[1][r] = fma(qv[r][e], kv[1][e], acc[1][r]);
+          if constexpr (TAYLOR) {
+            const double q2 = qv[r][e] * qv[r][e];
+            acc2[0][r] = fma(q2, vv[0][e], acc2[0][r]);
+            acc2[1][r] = fma(q2, vv[1][e], acc2[1][r]);
+          }
         }
 #pragma unroll
       for (int e = 0; e < kFC; ++e) {
 #pragma unroll
-        for (int x = 0; x < 2; ++x) kv[x][e] = kn[x][e];
+        for (int x = 0; x < 2; ++x) {
+          kv[x][e] = kn[x][e];
+          if constexpr (TAYLOR) vv[x][e] = vn[x][e];
+        }
 #pragma unroll
         for (int r = 0; r < R; ++r) qv[r][e] = qn[r][e];
       }
@@ -346,7 +402,8 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
       if (j >= nkbp) continue;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const double sv = acc[x][r] / sqrt_d;
+        double sv = acc[x][r] / sqrt_d;
+        if constexpr (TAYLOR) sv += log1p(acc2[x][r] * inv_2d);
         const bool ok = i0 + r < nq && j < nkb;
         keys[r * nkbp + j] = ok ? desc_key(sv) : ~0ull;
         if (ok && logits_out)
@@ -364,23 +421,24 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
   }
 }
 
-template <int R, int KPL>
+template <int R, int KPL, bool TAYLOR>
 hipError_t launch_select_rk(const Geometry& g, int nkbp, const double* qpool,
-                            const double* kpool_t, int32_t* crit, int32_t* marg, int8_t* cls,
-                            float* logits, hipStream_t stream) {
+                            const double* kpool_t, const double* kvar_t, int32_t* crit,
+                            int32_t* marg, int8_t* cls, float* logits, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(R) * nkbp * 8 + 4 * 128 * 4;
   if (lds > 65536) {
     // more than 64 KB of dynamic LDS has to be allowed for the kernel (on
     // the current device)
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<R, KPL>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<R, KPL, TAYLOR>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
   dim3 grid((g.nq + R - 1) / R, g.B * g.H);
   const double sqrt_d = __builtin_sqrt(static_cast<double>(g.D));
-  hipLaunchKernelGGL((select_kernel<R, KPL>), grid, dim3(kThreads), lds, stream, g, nkbp, qpool,
-                     kpool_t, sqrt_d, crit, marg, cls, logits);
+  const double inv_2d = 1.0 / (2.0 * g.D);
+  hipLaunchKernelGGL((select_kernel<R, KPL, TAYLOR>), grid, dim3(kThreads), lds, stream, g, nkbp,
+                     qpool, kpool_t, kvar_t, sqrt_d, inv_2d, crit, marg, cls, logits);
   return hipGetLastError();
 }
 
@@ -389,27 +447,34 @@ hipError_t launch_select_rk(const Geometry& g, int nkbp, const double* qpool,
 // within 64 KB of LDS and several workgroups share a CU (the kernel is
 // latency-bound; at nkb = 1182 four rows measured faster than eight).  Keys
 // per lane cover the row (nkb <= 4096).
+template <bool TAYLOR>
 hipError_t launch_select(const Geometry& g, const double* qpool, const double* kpool_t,
-                         int32_t* crit, int32_t* marg, int8_t* cls, float* logits,
-                         hipStream_t stream) {
+                         const double* kvar_t, int32_t* crit, int32_t* marg, int8_t* cls,
+                         float* logits, hipStream_t stream) {
   const int nkbp = (g.nkb + 63) / 64 * 64;
   if (nkbp <= 128)
-    return launch_select_rk<8, 2>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+    return launch_select_rk<8, 2, TAYLOR>(g, nkbp, qpool, kpool_t, kvar_t, crit, marg, cls, logits, stream);
   if (nkbp <= 512)
-    return launch_select_rk<8, 8>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+    return launch_select_rk<8, 8, TAYLOR>(g, nkbp, qpool, kpool_t, kvar_t, crit, marg, cls, logits, stream);
   if (nkbp <= 1024)
-    return launch_select_rk<8, 16>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+    return launch_select_rk<8, 16, TAYLOR>(g, nkbp, qpool, kpool_t, kvar_t, crit, marg, cls, logits, stream);
   if (nkbp <= 2048)
-    return launch_select_rk<4, 32>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
-  return launch_select_rk<2, 64>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+    return launch_select_rk<4, 32, TAYLOR>(g, nkbp, qpool, kpool_t, kvar_t, crit, marg, cls, logits, stream);
+  return launch_select_rk<2, 64, TAYLOR>(g, nkbp, qpool, kpool_t, kvar_t, crit, marg, cls, logits, stream);
 }
 
 template <typename T, int D>
 void launch_pool_t(const Geometry& g, const void* q, const void* k, double* qpool, double* kpool_t,
-                   float* qo, float* ko, hipStream_t stream) {
+                   float* qo, float* ko, double* kvar_t, float* vo, hipStream_t stream) {
   dim3 grid(g.nq, g.B * g.H, 2);
-  hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(kThreads), 0, stream,
-                     static_cast<const T*>(q), static_cast<const T*>(k), g, qpool, kpool_t, qo, ko);
+  if (kvar_t)
+    hipLaunchKernelGGL((pool_kernel<T, D, true>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const T*>(q), static_cast<const T*>(k), g, qpool, kpool_t, qo,
+                       ko, kvar_t, vo);
+  else
+    hipLaunchKernelGGL((pool_kernel<T, D, false>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const T*>(q), static_cast<const T*>(k), g, qpool, kpool_t, qo,
+                       ko, nullptr, nullptr);
 }
 
 }  // namespace
@@ -417,17 +482,23 @@ void launch_pool_t(const Geometry& g, const void* q, const void* k, double* qpoo
 hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t* crit,
                         int32_t* marg, int8_t* cls, float* logits, float* pooled_q,
                         float* pooled_k, double* ws_qpool, double* ws_kpool_t,
-                        hipStream_t stream) {
+                        double* ws_kvar_t, float* key_var, hipStream_t stream) {
   if (g.dtype == 1) {
-    if (g.D == 128) launch_pool_t<uint16_t, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, stream);
-    else launch_pool_t<uint16_t, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, stream);
+    if (g.D == 128)
+      launch_pool_t<uint16_t, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream);
+    else
+      launch_pool_t<uint16_t, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream);
   } else {
-    if (g.D == 128) launch_pool_t<float, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, stream);
-    else launch_pool_t<float, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, stream);
+    if (g.D == 128)
+      launch_pool_t<float, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream);
+    else
+      launch_pool_t<float, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_select(g, ws_qpool, ws_kpool_t, crit, marg, cls, logits, stream);
+  if (ws_kvar_t)
+    return launch_select<true>(g, ws_qpool, ws_kpool_t, ws_kvar_t, crit, marg, cls, logits, stream);
+  return launch_select<false>(g, ws_qpool, ws_kpool_t, nullptr, crit, marg, cls, logits, stream);
 }
 
 }  // namespace sla

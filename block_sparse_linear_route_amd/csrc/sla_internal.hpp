@@ -17,10 +17,12 @@ struct Geometry {
   int64_t sb, sh, sn;    // element strides of Q, K, V, O
 };
 
+// ws_kvar_t non-null: second-order routing score (block key variances pooled
+// into it, and into key_var as float32 when that is non-null).
 hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t* crit,
                         int32_t* marg, int8_t* cls, float* logits, float* pooled_q,
                         float* pooled_k, double* ws_qpool, double* ws_kpool_t,
-                        hipStream_t stream);
+                        double* ws_kvar_t, float* key_var, hipStream_t stream);
 
 // exp_map: phi(k) = exp(k) elementwise instead of the softmax over features.
 hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16_t* h_states,

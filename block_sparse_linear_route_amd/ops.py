@@ -90,8 +90,15 @@ def _workspace(problem: _lib.Problem, op: int, device) -> Optional[torch.Tensor]
 
 
 def route(q: torch.Tensor, k: torch.Tensor, k_crit: int, k_marg: int, *, want_class: bool = False,
-          want_logits: bool = False, want_pooled: bool = False, stream=None) -> dict:
-    """Pool, score and split: returns crit_idx, marg_idx (+ optional intermediates)."""
+          want_logits: bool = False, want_pooled: bool = False, score: str = "mean",
+          stream=None) -> dict:
+    """Pool, score and split: returns crit_idx, marg_idx (+ optional intermediates).
+
+    ``score``: "mean" (the pooled dot product, ``sla_route``) or "taylor"
+    (the second-order score with block key variances, ``sla_route_taylor``;
+    ``want_pooled`` then also returns ``key_var``)."""
+    if score not in ("mean", "taylor"):
+        raise SlaError(_lib.SLA_ERR_INVALID_ARGUMENT, f"unknown routing score {score!r}")
     (k,) = _same_layout(q, k)
     p = make_problem(q, k_crit, k_marg)
     B, H, N, d = q.shape
@@ -107,12 +114,22 @@ def route(q: torch.Tensor, k: torch.Tensor, k_crit: int, k_marg: int, *, want_cl
     if want_pooled:
         out["pooled_q"] = torch.empty((B, H, nb, d), dtype=torch.float32, device=dev)
         out["pooled_k"] = torch.empty((B, H, nb, d), dtype=torch.float32, device=dev)
-    ws = _workspace(p, _lib.OP_ROUTE, dev)
-    _check(lib.sla_route(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(out["crit_idx"]),
-                         _ptr(out["marg_idx"]), _ptr(out.get("block_class")),
-                         _ptr(out.get("block_logits")), _ptr(out.get("pooled_q")),
-                         _ptr(out.get("pooled_k")), _ptr(ws), 0 if ws is None else ws.numel(),
-                         _stream(stream)))
+        if score == "taylor":
+            out["key_var"] = torch.empty((B, H, nb, d), dtype=torch.float32, device=dev)
+    if score == "taylor":
+        ws = _workspace(p, _lib.OP_ROUTE_TAYLOR, dev)
+        _check(lib.sla_route_taylor(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(out["crit_idx"]),
+                                    _ptr(out["marg_idx"]), _ptr(out.get("block_class")),
+                                    _ptr(out.get("block_logits")), _ptr(out.get("pooled_q")),
+                                    _ptr(out.get("pooled_k")), _ptr(out.get("key_var")),
+                                    _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    else:
+        ws = _workspace(p, _lib.OP_ROUTE, dev)
+        _check(lib.sla_route(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(out["crit_idx"]),
+                             _ptr(out["marg_idx"]), _ptr(out.get("block_class")),
+                             _ptr(out.get("block_logits")), _ptr(out.get("pooled_q")),
+                             _ptr(out.get("pooled_k")), _ptr(ws), 0 if ws is None else ws.numel(),
+                             _stream(stream)))
     out["_workspace"] = ws   # keeps the buffer alive until the caller drops the dict
     return out
 

@@ -68,7 +68,7 @@ extern "C" {
 #endif
 
 #define SLA_VERSION_MAJOR 0
-#define SLA_VERSION_MINOR 2
+#define SLA_VERSION_MINOR 3
 #define SLA_VERSION_PATCH 0
 
 /* Status codes. */
@@ -90,7 +90,8 @@ typedef enum sla_op {
   SLA_OP_LINEAR_STATES = 1,
   SLA_OP_FORWARD = 2,
   SLA_OP_QUANTIZE_FP8 = 3,
-  SLA_OP_FORWARD_FP8 = 4
+  SLA_OP_FORWARD_FP8 = 4,
+  SLA_OP_ROUTE_TAYLOR = 5
 } sla_op;
 
 /* Problem description (host struct, read only during the call).
@@ -120,7 +121,8 @@ int sla_num_blocks(const sla_problem* problem, int32_t* nq, int32_t* nkb);
  * [B,H,nq,d,d] marginal-state sum, a float32 [B,H,nq,d] normaliser sum and
  * B*H*2*ceil(nkb/64)*(nq rounded up to 512) 32-bit words of marginal-mask
  * bits, each region 256-byte aligned; SLA_OP_ROUTE
- * needs float64 pooled Q and K. */
+ * needs float64 pooled Q and K, SLA_OP_ROUTE_TAYLOR those and float64 block
+ * key variances. */
 int sla_workspace_size(const sla_problem* problem, int op, size_t* bytes);
 
 /* Block routing.  [SLA2 summary 2.B; SLA abstract]
@@ -139,6 +141,21 @@ int sla_route(const sla_problem* problem, const void* q, const void* k,
               int32_t* crit_idx, int32_t* marg_idx, int8_t* block_class,
               float* block_logits, float* pooled_q, float* pooled_k, void* ws,
               size_t ws_bytes, void* stream);
+
+/* Block routing with the second-order score.  [SPLA summary 2.1]
+ * The block score keeps the spread of the keys around their block mean,
+ * to second order with a diagonal covariance:
+ *   s_ij = qbar_i . kbar_j / sqrt(d) + log1p(sum_a qbar_ia^2 var_ja / (2 d)),
+ * var_ja = population variance of feature a over block j's valid keys.
+ * Outputs, ordering and tie rule are those of sla_route, with s_ij in
+ * block_logits, plus
+ * key_var      out float [B,H,nb,d] or NULL: var_ja rounded to float32
+ * ws           workspace of sla_workspace_size(SLA_OP_ROUTE_TAYLOR) bytes.
+ * Means, variances and logits are evaluated in float64. */
+int sla_route_taylor(const sla_problem* problem, const void* q, const void* k,
+                     int32_t* crit_idx, int32_t* marg_idx, int8_t* block_class,
+                     float* block_logits, float* pooled_q, float* pooled_k,
+                     float* key_var, void* ws, size_t ws_bytes, void* stream);
 
 /* Per-block linear-attention states.  [PISA summary; SPLA summary 2.2]
  * k, v      input [B,H,N,d]

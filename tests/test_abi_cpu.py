@@ -80,6 +80,8 @@ def test_num_blocks_and_workspace():
     assert n.value >= 2 * 512 * 128 * 128 * 2 + 2 * 512 * 128 * 4
     assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_ROUTE, ctypes.byref(n)) == 0
     assert n.value >= 2 * 2 * 512 * 128 * 8
+    assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_ROUTE_TAYLOR, ctypes.byref(n)) == 0
+    assert n.value >= 3 * 2 * 512 * 128 * 8
     assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_LINEAR_STATES, ctypes.byref(n)) == 0
     assert n.value == 0
     assert lib.sla_workspace_size(ctypes.byref(p), 99, ctypes.byref(n)) == _lib.SLA_ERR_INVALID_ARGUMENT
@@ -90,7 +92,7 @@ def test_status_strings_and_version():
         assert lib.sla_status_string(s)
     a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     assert lib.sla_version(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 0
-    assert (a.value, b.value, c.value) == (0, 2, 0)
+    assert (a.value, b.value, c.value) == (0, 3, 0)
 
 
 def test_entry_points_reject_bad_arguments_before_any_device_call():
@@ -105,6 +107,17 @@ def test_entry_points_reject_bad_arguments_before_any_device_call():
     assert st == _lib.SLA_ERR_WORKSPACE
     st = lib.sla_route(ctypes.byref(p), fake, fake, fake, fake, None, None, None, None, None, 0, None)
     assert st == _lib.SLA_ERR_WORKSPACE
+    st = lib.sla_route_taylor(ctypes.byref(p), fake, None, fake, fake, None, None, None, None, None,
+                              fake, 1 << 30, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT       # k missing
+    st = lib.sla_route_taylor(ctypes.byref(p), fake, fake, fake, fake, None, None, None, None,
+                              ctypes.c_void_p(0x10002), fake, 1 << 30, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT       # misaligned key_var
+    n = ctypes.c_size_t()
+    lib.sla_workspace_size(ctypes.byref(p), _lib.OP_ROUTE, ctypes.byref(n))
+    st = lib.sla_route_taylor(ctypes.byref(p), fake, fake, fake, fake, None, None, None, None, None,
+                              fake, n.value, None)
+    assert st == _lib.SLA_ERR_WORKSPACE              # the plain route workspace is too small
     st = lib.sla_linear_states(ctypes.byref(p), fake, None, fake, fake, None)
     assert st == _lib.SLA_ERR_INVALID_ARGUMENT
     st = lib.sla_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None, fake,
