@@ -28,6 +28,12 @@ Sources (page titles as printed; sections as on each page):
 Residual linear attention (SPLA technical summary, sections 2.2 and 2.3:
 o_rla = o_bar - o_tilde over all and over the selected blocks, an RMS norm on
 that branch, a gated sum, an exponential feature map) is in ``oracle.rla``.
+The second-order block routing score (SPLA technical summary, section 2.1)
+is in ``oracle.taylor``.  Piecewise exact-or-approximate attention (PISA
+technical summary, section 2: exact terms on the selected blocks, a
+zero-order centroid term per unselected block and one global first-order
+correction inside a single softmax numerator and denominator) is in
+``oracle.pisa``.
 
 The block size (64), mean pooling, phi = softmax over the feature dimension,
 H_j = phi(K_j)^T V_j, z_j = column sums of phi(K_j), and the per-head alpha

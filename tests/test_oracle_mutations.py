@@ -171,3 +171,44 @@ def test_taylor_variance_of_queries(monkeypatch):
         return orig(k, q, kc, km, block)
     monkeypatch.setattr(taylor_mod, "route_taylor", bad)
     _fails(taylor_pins.test_zero_variance_gives_the_sla_route)
+
+
+from oracle import pisa as pisa_mod
+import tests.test_oracle_pins_pisa as pisa_pins
+
+
+def _patch_stats(monkeypatch, fn):
+    orig = pisa_mod.block_statistics
+    monkeypatch.setattr(pisa_mod, "block_statistics", lambda k, v, block=64: fn(*orig(k, v, block)))
+
+
+def test_pisa_denominator_without_token_count(monkeypatch):
+    _patch_stats(monkeypatch, lambda kb, vs, cnt, H: (kb, vs, np.ones_like(cnt), H))
+    _fails(pisa_pins.test_constant_key_blocks_make_the_expansion_exact, 64 * 6, 2)
+
+
+def test_pisa_value_mean_instead_of_sum(monkeypatch):
+    _patch_stats(monkeypatch, lambda kb, vs, cnt, H: (kb, vs / cnt[:, None], cnt, H))
+    _fails(pisa_pins.test_constant_key_blocks_make_the_expansion_exact, 64 * 6, 2)
+
+
+def test_pisa_uncentred_first_order(monkeypatch):
+    _patch_stats(monkeypatch, lambda kb, vs, cnt, H: (kb, vs, cnt,
+                                                       H + kb[:, :, None] * vs[:, None, :]))
+    _fails(pisa_pins.test_constant_key_blocks_make_the_expansion_exact, 64 * 6, 2)
+
+
+def test_pisa_hbar_summed_not_averaged(monkeypatch):
+    monkeypatch.setattr(pisa_mod, "global_first_order", lambda H: H.sum(axis=0))
+    _fails(pisa_pins.test_equal_first_order_matrices_leave_second_order_error)
+
+
+def test_pisa_correction_unscaled(monkeypatch):
+    # the correction taken with q_t instead of q_t / sqrt(d)
+    monkeypatch.setattr(pisa_mod, "global_first_order", lambda H: H.mean(axis=0) * math.sqrt(8))
+    _fails(pisa_pins.test_equal_first_order_matrices_leave_second_order_error)
+
+
+def test_pisa_correction_sign(monkeypatch):
+    monkeypatch.setattr(pisa_mod, "global_first_order", lambda H: -H.mean(axis=0))
+    _fails(pisa_pins.test_equal_first_order_matrices_leave_second_order_error)

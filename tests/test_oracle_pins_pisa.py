@@ -1,0 +1,148 @@
+"""Pins of piecewise exact-or-approximate attention (oracle/pisa.py), CPU only."""
+import math
+
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+from oracle import pisa
+
+rng = np.random.default_rng(17)
+
+
+def _dense(q, k, v):
+    """Textbook scaled dot-product softmax attention."""
+    return softmax(q @ k.T / math.sqrt(q.shape[1]), axis=1) @ v
+
+
+def _random_lists(nb, kc, rng_):
+    return np.stack([np.sort(rng_.choice(nb, kc, replace=False)) for _ in range(nb)]) \
+        if kc else np.zeros((nb, 0), dtype=np.int64)
+
+
+def test_block_statistics_brute_force():
+    n, d, dv, block = 21, 3, 2, 8
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, dv))
+    kbar, vsum, cnt, H = pisa.block_statistics(k, v, block)
+    starts = [0, 8, 16]
+    for j, a in enumerate(starts):
+        b = min(a + block, n)
+        assert cnt[j] == b - a
+        for f in range(d):
+            mean = sum(k[t, f] for t in range(a, b)) / (b - a)
+            assert abs(kbar[j, f] - mean) < 1e-14
+            for c in range(dv):
+                h = sum((k[t, f] - mean) * v[t, c] for t in range(a, b))
+                assert abs(H[j, f, c] - h) < 1e-13
+        for c in range(dv):
+            assert abs(vsum[j, c] - sum(v[t, c] for t in range(a, b))) < 1e-13
+    np.testing.assert_allclose(pisa.global_first_order(H), H.sum(axis=0) / 3, rtol=1e-14)
+
+
+@pytest.mark.parametrize("n", [256, 250])
+def test_nothing_unselected_is_dense_attention(n):
+    d = 16
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    nb = -(-n // 64)
+    crit = np.tile(np.arange(nb), (nb, 1))
+    o, o_sm, o_fo = pisa.pisa_head(q, k, v, crit)
+    np.testing.assert_allclose(o, _dense(q, k, v), rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(o_fo, 0.0)
+
+
+@pytest.mark.parametrize("n,kc", [(64 * 6, 0), (64 * 6, 2), (64 * 5 + 19, 1), (64 * 5 + 19, 3)])
+def test_constant_key_blocks_make_the_expansion_exact(n, kc):
+    # every key equals its block centroid: the zero-order terms are the
+    # exact block contributions and every first-order matrix is 0, so the
+    # result is dense attention whatever the selected set (the short last
+    # block checks the token count in the denominator)
+    d = 8
+    nb = -(-n // 64)
+    q = rng.standard_normal((n, d))
+    k = np.repeat(rng.standard_normal((nb, d)) * 1.5, 64, axis=0)[:n]
+    v = rng.standard_normal((n, 5))
+    crit = _random_lists(nb, kc, rng)
+    o, o_sm, o_fo = pisa.pisa_head(q, k, v, crit)
+    np.testing.assert_allclose(o, _dense(q, k, v), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(o_fo, 0.0, atol=1e-13)
+
+
+def _equal_first_order_case(eps, seed=3):
+    # K = per-block centroid + eps * a mean-zero pattern shared by all blocks;
+    # V = per-block offset + a pattern shared by all blocks.  Every block
+    # then has the same first-order matrix, so the global correction is the
+    # exact first-order term and the error left is of second order in eps.
+    r = np.random.default_rng(seed)
+    nb, d, dv = 6, 8, 4
+    pat = r.standard_normal((64, d))
+    pat -= pat.mean(axis=0)
+    wpat = r.standard_normal((64, dv))
+    k = (r.standard_normal((nb, 1, d)) + eps * pat[None]).reshape(nb * 64, d)
+    v = (r.standard_normal((nb, 1, dv)) + wpat[None]).reshape(nb * 64, dv)
+    q = r.standard_normal((nb * 64, d)) * 2.0
+    crit = np.stack([np.sort(r.choice(nb, 2, replace=False)) for _ in range(nb)])
+    o, o_sm, _ = pisa.pisa_head(q, k, v, crit)
+    ref = _dense(q, k, v)
+    return np.abs(o - ref).max(), np.abs(o_sm - ref).max()
+
+
+def test_equal_first_order_matrices_leave_second_order_error():
+    e1, z1 = _equal_first_order_case(0.02)
+    e2, z2 = _equal_first_order_case(0.01)
+    # with the correction: second order (halving eps quarters the error)
+    assert 0.18 < e2 / e1 < 0.32, (e1, e2)
+    # without it (zero order only): first order (halving eps halves it)
+    assert 0.4 < z2 / z1 < 0.6, (z1, z2)
+    assert e1 < 0.1 * z1
+
+
+def test_brute_force_tiny():
+    n, d, dv, block = 20, 3, 2, 8
+    q = rng.standard_normal((n, d)) * 0.7
+    k = rng.standard_normal((n, d)) * 0.7
+    v = rng.standard_normal((n, dv))
+    crit = np.array([[1], [0], [2]])
+    o, _, _ = pisa.pisa_head(q, k, v, crit, block)
+    blocks = [range(0, 8), range(8, 16), range(16, 20)]
+    sq = math.sqrt(d)
+    kb = [[sum(k[t, f] for t in blk) / len(blk) for f in range(d)] for blk in blocks]
+    Hs = []
+    for j, blk in enumerate(blocks):
+        Hs.append([[sum((k[t, f] - kb[j][f]) * v[t, c] for t in blk) for c in range(dv)]
+                   for f in range(d)])
+    Hbar = [[sum(Hs[j][f][c] for j in range(3)) / 3 for c in range(dv)] for f in range(d)]
+    for i, blk_i in enumerate(blocks):
+        for t in blk_i:
+            qt = [q[t, f] / sq for f in range(d)]
+            num = [0.0] * dv
+            den = 0.0
+            asum = 0.0
+            for j, blk in enumerate(blocks):
+                if j in crit[i]:
+                    for s in blk:
+                        e = math.exp(sum(qt[f] * k[s, f] for f in range(d)))
+                        den += e
+                        for c in range(dv):
+                            num[c] += e * v[s, c]
+                else:
+                    al = math.exp(sum(qt[f] * kb[j][f] for f in range(d)))
+                    asum += al
+                    den += al * len(blk)
+                    for c in range(dv):
+                        num[c] += al * sum(v[s, c] for s in blk)
+            for c in range(dv):
+                num[c] += asum * sum(qt[f] * Hbar[f][c] for f in range(d))
+                assert abs(o[t, c] - num[c] / den) < 1e-12
+
+
+def test_query_block_subset():
+    n, d = 64 * 5 + 7, 16
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    crit = _random_lists(6, 2, rng)
+    full = pisa.pisa_head(q, k, v, crit)[0]
+    part = pisa.pisa_head(q, k, v, crit, q_blocks=[1, 5])[0]
+    rows = np.r_[64:128, 320:n]
+    np.testing.assert_array_equal(part[rows], full[rows])
+    other = np.setdiff1d(np.arange(n), rows)
+    np.testing.assert_array_equal(part[other], 0.0)
