@@ -9,14 +9,18 @@ from .ops import (  # noqa: F401
     forward,
     forward_attend,
     forward_attend_fp8,
+    forward_attend_pisa,
     forward_attend_rla,
     forward_fp8,
+    forward_pisa,
     forward_rla,
     forward_workspace,
     linear_states,
     make_problem,
     marginal_sums,
     num_blocks,
+    pisa_statistics,
+    pisa_workspace,
     quantize_fp8,
     residual_sums,
     route,

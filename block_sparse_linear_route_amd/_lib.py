@@ -19,7 +19,8 @@ SLA_ERR_DEVICE = -4
 SLA_ERR_NO_DEVICE = -5
 
 SLA_F32, SLA_BF16 = 0, 1
-OP_ROUTE, OP_LINEAR_STATES, OP_FORWARD, OP_QUANTIZE_FP8, OP_FORWARD_FP8, OP_ROUTE_TAYLOR = range(6)
+(OP_ROUTE, OP_LINEAR_STATES, OP_FORWARD, OP_QUANTIZE_FP8, OP_FORWARD_FP8, OP_ROUTE_TAYLOR,
+ OP_FORWARD_PISA) = range(7)
 
 
 class Problem(ctypes.Structure):
@@ -61,6 +62,10 @@ SIGNATURES = {
                                               _sz, _vp]),
     "sla_forward_rla": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _sz, _vp]),
+    "sla_pisa_statistics": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sla_forward_attend_pisa": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                               _vp]),
+    "sla_forward_pisa": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sla_last_error_message": (ctypes.c_char_p, []),
     "sla_version": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int)] * 3),

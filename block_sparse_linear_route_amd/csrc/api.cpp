@@ -173,6 +173,37 @@ size_t route_region(const sla::Geometry& g) {
 size_t route_ws(const sla::Geometry& g) { return 2 * route_region(g); }
 size_t route_taylor_ws(const sla::Geometry& g) { return 3 * route_region(g); }
 
+// PISA workspace: [kbar bf16 B*H*npb*64*d][vbar bf16 B*H*npb*64*d]
+// [Hbar bf16 B*H*d*d][chunk partials f32 B*H*nchunks*d*d]
+struct PisaWs {
+  uint16_t* kbar;
+  uint16_t* vbar;
+  uint16_t* hbar;
+  float* part;
+};
+
+size_t pisa_ws(const sla::Geometry& g) {
+  const size_t bh = static_cast<size_t>(g.B) * g.H;
+  const size_t rows = bh * sla::pisa_pseudo_blocks(g) * 64;
+  return 2 * align_up(rows * g.D * 2) + align_up(bh * g.D * g.D * 2) +
+         align_up(bh * sla::pisa_chunks(g) * g.D * g.D * 4);
+}
+
+PisaWs carve_pisa_ws(const sla::Geometry& g, void* ws) {
+  const size_t bh = static_cast<size_t>(g.B) * g.H;
+  const size_t rows = bh * sla::pisa_pseudo_blocks(g) * 64;
+  char* p = static_cast<char*>(ws);
+  PisaWs w;
+  w.kbar = reinterpret_cast<uint16_t*>(p);
+  p += align_up(rows * g.D * 2);
+  w.vbar = reinterpret_cast<uint16_t*>(p);
+  p += align_up(rows * g.D * 2);
+  w.hbar = reinterpret_cast<uint16_t*>(p);
+  p += align_up(bh * g.D * g.D * 2);
+  w.part = reinterpret_cast<float*>(p);
+  return w;
+}
+
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return SLA_OK;
   if (!ws) return fail(SLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
@@ -210,6 +241,7 @@ int sla_workspace_size(const sla_problem* problem, int op, size_t* bytes) {
     case SLA_OP_QUANTIZE_FP8: *bytes = 0; return SLA_OK;
     case SLA_OP_FORWARD_FP8: *bytes = forward_ws(g); return SLA_OK;
     case SLA_OP_ROUTE_TAYLOR: *bytes = route_taylor_ws(g); return SLA_OK;
+    case SLA_OP_FORWARD_PISA: *bytes = pisa_ws(g); return SLA_OK;
     default: return fail(SLA_ERR_INVALID_ARGUMENT, "unknown op %d", op);
   }
 }
@@ -506,6 +538,50 @@ int sla_forward_rla(const sla_problem* problem, const void* q, const void* k, co
   SLA_TRY(sla_residual_sums(problem, crit_idx, h_states, ws, ws_bytes, stream));
   return sla_forward_attend_rla(problem, q, k, v, crit_idx, alpha, o, o_sparse, o_linear, ws,
                                 ws_bytes, stream);
+}
+
+int sla_pisa_statistics(const sla_problem* problem, const void* k, const void* v, float* hbar,
+                        void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(k, 16);
+  SLA_REQ(v, 16);
+  SLA_OPT(hbar, 16);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, pisa_ws(g)));
+  SLA_TRY(check_device());
+  const PisaWs w = carve_pisa_ws(g, ws);
+  return launched(sla::launch_pisa_stats(g, k, v, w.kbar, w.vbar, w.hbar, w.part, hbar,
+                                         static_cast<hipStream_t>(stream)),
+                  "PISA statistics launch");
+}
+
+int sla_forward_attend_pisa(const sla_problem* problem, const void* q, const void* k,
+                            const void* v, const int32_t* crit_idx, void* o, float* o_softmax,
+                            float* o_correction, const void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(q, 16);
+  SLA_REQ(k, 16);
+  SLA_REQ(v, 16);
+  SLA_REQ(o, 16);
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  SLA_OPT(o_softmax, 16);
+  SLA_OPT(o_correction, 16);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(const_cast<void*>(ws), ws_bytes, pisa_ws(g)));
+  SLA_TRY(check_device());
+  const PisaWs w = carve_pisa_ws(g, const_cast<void*>(ws));
+  return launched(sla::launch_attention_pisa(g, q, k, v, crit_idx, w.kbar, w.vbar, w.hbar, o,
+                                             o_softmax, o_correction,
+                                             static_cast<hipStream_t>(stream)),
+                  "PISA attention launch");
+}
+
+int sla_forward_pisa(const sla_problem* problem, const void* q, const void* k, const void* v,
+                     const int32_t* crit_idx, void* o, float* o_softmax, float* o_correction,
+                     void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(sla_pisa_statistics(problem, k, v, nullptr, ws, ws_bytes, stream));
+  return sla_forward_attend_pisa(problem, q, k, v, crit_idx, o, o_softmax, o_correction, ws,
+                                 ws_bytes, stream);
 }
 
 const char* sla_status_string(int status) {

@@ -23,6 +23,17 @@
 // The two key halves keep separate running max / sum / output (no per-block
 // cross-wave reduction); the shared epilogue merges them, adds the linear
 // branch from the precomputed marginal-state sums and stores the alpha mix.
+//
+// PISA instance ([PISA technical summary, "Algoritmo Central" and
+// "Implementación de Hardware"]): after the critical blocks the same loop
+// runs over pseudo-blocks of 64 block centroids (kbar rows as keys, block
+// value means as values), so the zero-order terms of every unselected block
+// enter the one online softmax: a centroid key carries log(n_j) in its score
+// (its block's n_j tokens) and selected or padding centroids are masked out.
+// A third running sum collects sum_j alpha_{t,j} over the unselected blocks,
+// and the epilogue adds the global first-order correction
+// (q_t / sqrt(d)) Hbar sum_j alpha_{t,j} to the numerator before the one
+// division.
 #include <type_traits>
 
 #include "attention_epilogue.hpp"
@@ -43,12 +54,21 @@ struct AttnArgs {
   float* o_linear;
   Geometry g;
   float c_log2;      // log2(e) / sqrt(d)
+  // PISA only: centroid tiles, pseudo-block count, the log2(n_j) score
+  // offsets in units of the raw dot product, 1 / n_j of the last block
+  const uint16_t* kbar;
+  const uint16_t* vbar;
+  int npb;
+  float bias_full;
+  float bias_last;
+  float inv_last;
 };
 
 // RLA: residual linear attention epilogue (the marginal sum holds every
 // non-critical block's exponential-map state; RMS norm instead of the
-// phi(Q) . sigma_i denominator, so sigma_i is not loaded).
-template <typename T, int D, bool RLA>
+// phi(Q) . sigma_i denominator, so sigma_i is not loaded).  PISA: piecewise
+// exact-or-approximate attention (s_sum holds Hbar per head).
+template <typename T, int D, bool RLA, bool PISA = false>
 __global__ void __launch_bounds__(kThreads, 2)
 attention_kernel(AttnArgs A) {
   constexpr int CH = D / 8;                    // 16-byte chunks per row
@@ -68,6 +88,8 @@ attention_kernel(AttnArgs A) {
   constexpr int SMEM_BYTES = (LOOP_BYTES > EPI_OFF + EPI_BYTES ? LOOP_BYTES : EPI_OFF + EPI_BYTES);
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM_BYTES];
   __shared__ __attribute__((aligned(16))) float sig_lds[D];     // sigma_i, loaded at the start
+  // PISA: excluded centroids (selected blocks and padding), one bit each
+  __shared__ uint64_t excl[PISA ? 64 : 1];
   uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
 
   const Geometry& g = A.g;
@@ -97,6 +119,17 @@ attention_kernel(AttnArgs A) {
 
   const int32_t* __restrict__ crow = A.crit + (static_cast<int64_t>(bh) * g.nq + i) * g.k_crit;
   const int kc = g.k_crit;
+  // steps of the loop: the critical blocks, then (PISA) the pseudo-blocks
+  const int nst = PISA ? kc + A.npb : kc;
+  if constexpr (PISA) {
+    for (int w = t; w < A.npb; w += kThreads)
+      excl[w] = (w == A.npb - 1 && (g.nkb & 63)) ? (~0ull << (g.nkb & 63)) : 0ull;
+    __syncthreads();
+    for (int c = t; c < kc; c += kThreads) {
+      const int jb = crow[c];
+      atomicOr(reinterpret_cast<unsigned long long*>(excl + (jb >> 6)), 1ull << (jb & 63));
+    }
+  }
   // The critical list is read once into registers, 64 entries per register
   // (lane l holds entry base + l), and entries are taken with v_readlane, so
   // the loop issues no index loads: a vector load there would make the
@@ -132,7 +165,26 @@ attention_kernel(AttnArgs A) {
     tcol[u] = static_cast<uint32_t>(8 * (lslot ^ swz<D>(r)) * sizeof(T));
     toff[u] = static_cast<uint32_t>(r) * rowb + tcol[u];
   }
+  [[maybe_unused]] __amdgpu_buffer_rsrc_t kbrs, vbrs;
+  if constexpr (PISA) {
+    const int64_t cb = static_cast<int64_t>(bh) * A.npb * kBlock * D;
+    kbrs = make_rsrc(A.kbar + cb, static_cast<uint32_t>(g.nkb * D * 2));
+    vbrs = make_rsrc(A.vbar + cb, static_cast<uint32_t>(g.nkb * D * 2));
+  }
   auto issue_tile = [&](bool is_k, int c, uint16_t* dst) {
+    if constexpr (PISA) {
+      if (c >= kc) {
+        // centroid tile: bf16 rows of D, rows past nkb read as zeros
+        const uint32_t soff = static_cast<uint32_t>((c - kc) * kBlock * D * 2);
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) {
+          const int r = 16 * wave + RPI * u + lrow;
+          const uint32_t off = static_cast<uint32_t>(r * D * 2 + 16 * (lslot ^ swz<D>(r)));
+          buffer_load_lds16(is_k ? kbrs : vbrs, dst + (16 * wave + RPI * u) * D, off, soff);
+        }
+        return;
+      }
+    }
     const int jb = crit_at(c);
     if constexpr (sizeof(T) == 2) {
       const uint32_t soff = static_cast<uint32_t>(kBlock * jb) * rowb;
@@ -155,10 +207,11 @@ attention_kernel(AttnArgs A) {
 
   // S_i^T (value-major, D rows x D) halves: rows 64*half .. +63 as a
   // swizzled tile, same pattern as a K tile (contiguous rows of D bf16)
-  const bool has_lin = g.k_marg > 0;
+  const bool has_lin = PISA || g.k_marg > 0;
   const __amdgpu_buffer_rsrc_t srs =
-      make_rsrc(A.s_sum + (static_cast<int64_t>(bh) * g.nq + i) * D * D, D * D * 2);
-  if (!RLA && has_lin && wave == 0 && lane < D / 4) {
+      make_rsrc(A.s_sum + (PISA ? static_cast<int64_t>(bh) : static_cast<int64_t>(bh) * g.nq + i) * D * D,
+                D * D * 2);
+  if (!RLA && !PISA && has_lin && wave == 0 && lane < D / 4) {
     const __amdgpu_buffer_rsrc_t sgr =
         make_rsrc(A.sigma_sum + (static_cast<int64_t>(bh) * g.nq + i) * D, D * 4);
     buffer_load_lds16(sgr, sig_lds, 16u * lane, 0u);
@@ -206,6 +259,10 @@ attention_kernel(AttnArgs A) {
   }
 
   float m_run = -INFINITY, l_run = 0.0f;
+  float a_run = 0.0f;   // PISA: sum of alpha_{t,j} over this lane's unselected centroids
+  // PISA: the exclusion words, lane w holding pseudo-block w (set below,
+  // once the bits are complete), read in the loop with v_readlane
+  uint32_t exw_lo = 0, exw_hi = 0;
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = zero16();
@@ -273,33 +330,50 @@ attention_kernel(AttnArgs A) {
           : "v"(va1[0]), "v"(va2[0]), "v"(va1[1]), "v"(va2[1]), "i"(VOFF0), "i"(VOFF1)
           : "memory");
     }
-    if (it + 2 < kc) {
+    if (it + 2 < nst) {
       issue_tile(true, it + 2, smem + X * TILE);
     } else if constexpr (ST_LDS) {
       // kbuf[X] (K(it), consumed last step) stays free: S_i^T half 0 goes in
       // at step kc-2, half 1 at step kc-1 (both at step 0 when kc = 1), so
       // half 0 ends in kbuf[kc & 1] and half 1 in kbuf[(kc & 1) ^ 1]
       if (has_lin) {
-        if (it == kc - 2) {
+        if (it == nst - 2) {
           issue_st(0, smem + X * TILE);
         } else {
           issue_st(1, smem + X * TILE);
-          if (kc == 1) issue_st(0, smem + (X ^ 1) * TILE);
+          if (nst == 1) issue_st(0, smem + (X ^ 1) * TILE);
         }
       }
     }
-    if (it + 1 < kc) issue_tile(false, it + 1, smem + (2 + (X ^ 1)) * TILE);
+    if (it + 1 < nst) issue_tile(false, it + 1, smem + (2 + (X ^ 1)) * TILE);
     f32x16 acc = zero16();
     acc = mfma32(kf[0], qf[0], acc);
     acc = mfma32(kf[1], qf[1], acc);
 
-    const int jb = crit_at(it);
-    const int nj = min(kBlock, g.N - kBlock * jb);
-    if (nj < kBlock) {
+    const bool pseudo = PISA && it >= kc;
+    [[maybe_unused]] int key0 = 0;
+    if (pseudo) {
+      // centroid 64*(it-kc) + key of this lane's registers: excluded ones
+      // drop out, the others carry log(n_j) (in units of the raw score)
+      const int pbk = it - kc;
+      const uint32_t w32 = kh ? __builtin_amdgcn_readlane(exw_hi, pbk) : __builtin_amdgcn_readlane(exw_lo, pbk);
+      const uint32_t wl = w32 >> (4 * hh);
+      key0 = kBlock * pbk + 32 * kh + 4 * hh;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (key >= nj) s_cur[r] = -INFINITY;
+        const int kk = 8 * (r >> 2) + (r & 3);
+        const float bias = key0 + kk == g.nkb - 1 ? A.bias_last : A.bias_full;
+        s_cur[r] = ((wl >> kk) & 1u) ? -INFINITY : s_cur[r] + bias;
+      }
+    } else {
+      const int jb = crit_at(it);
+      const int nj = min(kBlock, g.N - kBlock * jb);
+      if (nj < kBlock) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kh + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= nj) s_cur[r] = -INFINITY;
+        }
       }
     }
     float mx = max16(s_cur);
@@ -317,6 +391,7 @@ attention_kernel(AttnArgs A) {
       const float m_new = fmaxf(m_run, mx);
       const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * cl);
       l_run *= corr;
+      if constexpr (PISA) a_run *= corr;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -336,6 +411,14 @@ attention_kernel(AttnArgs A) {
       pb[r >> 3][r & 7] = f32_to_bf16(p);
     }
     l_run += ps;
+    if (pseudo) {
+      // alpha_{t,j} = p / n_j: 1/64 for full blocks, 1/n_last for the last
+      float plast = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (key0 + 8 * (r >> 2) + (r & 3) == g.nkb - 1) plast = __builtin_amdgcn_exp2f(fmaf(s_cur[r], cl, -mb));
+      a_run += ps * (1.0f / kBlock) + plast * (A.inv_last - 1.0f / kBlock);
+    }
     s_next = acc;
 
 #pragma unroll
@@ -346,7 +429,7 @@ attention_kernel(AttnArgs A) {
       oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, w0), pb[0], oacc[dt]);
       oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, w1), pb[1], oacc[dt]);
     }
-    if (it + 1 - cbase == 64) {            // entries it+1 .. it+64 now start at register 1
+    if ((!PISA || it + 1 < kc) && it + 1 - cbase == 64) {   // entries it+1 .. it+64 now start at register 1
       cbase += 64;
       cl0 = cl1;
       cl1 = cbase + 64 + lane < kc ? crow[cbase + 64 + lane] : 0;
@@ -363,10 +446,10 @@ attention_kernel(AttnArgs A) {
   // query are clamped (not stored).
   wait_vmem();
   f32x16 sa = zero16(), sb = zero16();
-  if (kc > 0) {
+  if (nst > 0) {
     issue_tile(true, 0, smem);
     issue_tile(false, 0, smem + 2 * TILE);
-    if (kc > 1) issue_tile(true, 1, smem + TILE);
+    if (nst > 1) issue_tile(true, 1, smem + TILE);
   }
   {
     const int qr = qrow < n_i ? qrow : n_i - 1;
@@ -375,7 +458,7 @@ attention_kernel(AttnArgs A) {
       qf[s] = load8(qp + static_cast<int64_t>(kBlock * i + qr) * sn + 16 * s + 8 * hh);
   }
   wait_vmem();
-  if (kc > 0) {
+  if (nst > 0) {
     __syncthreads();
     bf16x8 kf[NS];
 #pragma unroll
@@ -385,24 +468,32 @@ attention_kernel(AttnArgs A) {
   }
   // every wave has read kbuf[0] before step 0 refills it
   __syncthreads();
+  if constexpr (PISA) {
+    if (lane < A.npb) {
+      const uint64_t w = excl[lane];
+      exw_lo = static_cast<uint32_t>(w);
+      exw_hi = static_cast<uint32_t>(w >> 32);
+    }
+  }
   // no critical block: the idle K buffers take S_i^T right away (the
   // epilogue then always finds it in LDS)
-  if (ST_LDS && kc == 0 && has_lin) {
+  if (ST_LDS && nst == 0 && has_lin) {
     issue_st(0, smem);
     issue_st(1, smem + TILE);
   }
-  for (int it = 0; it < kc; it += 2) {
+  for (int it = 0; it < nst; it += 2) {
     step(std::integral_constant<int, 0>(), it, sa, sb);
-    if (it + 1 < kc) step(std::integral_constant<int, 1>(), it + 1, sb, sa);
+    if (it + 1 < nst) step(std::integral_constant<int, 1>(), it + 1, sb, sa);
   }
-  wait_vmem();       // (kc = 0: the S_i^T loads above)
+  wait_vmem();       // (no step: the S_i^T loads above)
   __syncthreads();
 
-  const uint16_t* st_half = smem + ((kc & 1) ^ kh) * TILE;
-  attention_finish<T, D, ST_LDS, false, RLA>(smem_raw + EPI_OFF, st_half, sig_lds, !RLA && has_lin, g, bh, h, i,
-                                        n_i, qrow, hoff, A.s_sum, A.sigma_sum, A.alpha, A.o,
-                                        A.o_sparse, A.o_linear, oacc, m_run, l_run, cl, qf,
-                                        [](int) {});
+  const uint16_t* st_half = smem + ((nst & 1) ^ kh) * TILE;
+  attention_finish<T, D, ST_LDS, false, RLA, PISA>(smem_raw + EPI_OFF, st_half, sig_lds,
+                                                   !RLA && !PISA && has_lin, g, bh, h, i, n_i, qrow,
+                                                   hoff, A.s_sum, A.sigma_sum, A.alpha, A.o,
+                                                   A.o_sparse, A.o_linear, oacc, m_run, l_run, cl,
+                                                   qf, [](int) {}, a_run);
 }
 
 template <typename T, int D>
@@ -414,14 +505,42 @@ void launch_attn_t(const AttnArgs& a, bool rla, hipStream_t stream) {
     hipLaunchKernelGGL((attention_kernel<T, D, false>), dim3(total), dim3(kThreads), 0, stream, a);
 }
 
+template <typename T, int D>
+void launch_attn_pisa_t(const AttnArgs& a, hipStream_t stream) {
+  const int total = a.g.B * a.g.H * a.g.nq;
+  hipLaunchKernelGGL((attention_kernel<T, D, false, true>), dim3(total), dim3(kThreads), 0, stream, a);
+}
+
 }  // namespace
+
+hipError_t launch_attention_pisa(const Geometry& g, const void* q, const void* k, const void* v,
+                                 const int32_t* crit, const uint16_t* kbar, const uint16_t* vbar,
+                                 const uint16_t* hbar, void* o, float* o_softmax,
+                                 float* o_correction, hipStream_t stream) {
+  const double cl = 1.4426950408889634 / __builtin_sqrt(static_cast<double>(g.D));
+  const int n_last = g.N - kBlock * (g.nkb - 1);
+  AttnArgs a{q, k, v, crit, hbar, nullptr, nullptr, o, o_softmax, o_correction, g,
+             static_cast<float>(cl), kbar, vbar, pisa_pseudo_blocks(g),
+             static_cast<float>(6.0 / cl),
+             static_cast<float>(__builtin_log2(static_cast<double>(n_last)) / cl),
+             1.0f / static_cast<float>(n_last)};
+  if (g.dtype == 1) {
+    if (g.D == 128) launch_attn_pisa_t<uint16_t, 128>(a, stream);
+    else launch_attn_pisa_t<uint16_t, 64>(a, stream);
+  } else {
+    if (g.D == 128) launch_attn_pisa_t<float, 128>(a, stream);
+    else launch_attn_pisa_t<float, 64>(a, stream);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,
                             const int32_t* crit, const uint16_t* s_sum, const float* sigma_sum,
                             const float* alpha, void* o, float* o_sparse, float* o_linear,
                             bool rla, hipStream_t stream) {
   AttnArgs a{q, k, v, crit, s_sum, sigma_sum, alpha, o, o_sparse, o_linear, g,
-             static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(g.D)))};
+             static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(g.D))),
+             nullptr, nullptr, 0, 0.0f, 0.0f, 0.0f};
   if (g.dtype == 1) {
     if (g.D == 128) launch_attn_t<uint16_t, 128>(a, rla, stream);
     else launch_attn_t<uint16_t, 64>(a, rla, stream);

@@ -21,6 +21,12 @@
 // normalised over the d value features of each row (x / sqrt(mean x^2 +
 // 1e-6); the factor exp(-max q) of phi(Q) cancels there), and O_l is that
 // normalised output.
+// With kPisa (piecewise exact-or-approximate attention, [PISA technical
+// summary, "Algoritmo Central"]) the merged softmax already holds the exact
+// and zero-order terms; the epilogue adds the global first-order term
+// (q_t / sqrt(d)) Hbar A_t to the numerator, A_t = sum of alpha_{t,j} over
+// the unselected blocks (a_run, merged like l_run), before the one division:
+// O_s is the softmax part, O_l the correction part, O = O_s + O_l.
 // m_run is in the units of S; cl converts them to log2 units.
 #pragma once
 
@@ -69,14 +75,15 @@ __device__ __forceinline__ int swz(int r) {
 // With kHooks, hook(1) runs once the LDS below merge_lds is no longer read
 // and hook(2) once the merge buffers are no longer read (all waves, after a
 // barrier): a caller can start loads for its next block there.
-template <typename T, int D, bool kStLds, bool kHooks, bool kRla = false, typename Hook>
+template <typename T, int D, bool kStLds, bool kHooks, bool kRla = false, bool kPisa = false,
+          typename Hook>
 __device__ __forceinline__ void attention_finish(
     unsigned char* merge_lds, const uint16_t* st_half, const float* sg_lds, bool sg_ok,
     const Geometry& g, int bh, int h, int i,
     int n_i, int qrow, int64_t hoff, const uint16_t* __restrict__ s_sum,
     const float* __restrict__ sigma_sum, const float* __restrict__ alpha, void* o,
     float* o_sparse, float* o_linear, const f32x16 (&oacc)[D / 32], float m_run, float l_run,
-    float cl, const bf16x8 (&qf)[D / 16], Hook&& hook) {
+    float cl, const bf16x8 (&qf)[D / 16], Hook&& hook, float a_run = 0.0f) {
   constexpr int NS = D / 16;
   constexpr int DT = D / 32;
   constexpr int DTH = DT / 2;
@@ -95,9 +102,12 @@ __device__ __forceinline__ void attention_finish(
   const int own0 = kh * DTH;
 
   const float l_full = l_run + xor_lane(l_run, 32);
+  [[maybe_unused]] float a_full = 0.0f;
+  if constexpr (kPisa) a_full = a_run + xor_lane(a_run, 32);
   if (hh == 0) {
     mbuf[wave * 32 + l32] = m_run;
     lbuf[wave * 32 + l32] = l_full;
+    if constexpr (kPisa) rbuf[wave * 32 + l32] = a_full;
   }
   // the wave keeps dims [32*own0, +32*DTH) and hands the other half to its
   // partner; select with static indices so the accumulators stay in registers
@@ -112,9 +122,9 @@ __device__ __forceinline__ void attention_finish(
 
   // phi(Q) as the B operand of O_l^T = S_i^T phi(Q)^T (exp(q - max q) per
   // query row; the row normaliser cancels against the denominator)
-  const bool has_lin = g.k_marg > 0;
+  const bool has_lin = kPisa || g.k_marg > 0;
   bf16x8 pf[NS];
-  if (has_lin) {
+  if (!kPisa && has_lin) {
     float qmax = -INFINITY;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
@@ -132,6 +142,7 @@ __device__ __forceinline__ void attention_finish(
   // of the value-major sum: from the LDS copy, or straight from HBM (their
   // latency then overlaps the merge)
   const int64_t row = static_cast<int64_t>(bh) * g.nq + i;
+  const int64_t srow = kPisa ? static_cast<int64_t>(bh) : row;   // Hbar is per head
   bf16x8 sf[DTH][NS];
   if (has_lin) {
     if constexpr (kStLds) {
@@ -143,14 +154,14 @@ __device__ __forceinline__ void attention_finish(
           sf[u][s] = *reinterpret_cast<const bf16x8*>(st_half + r * D + 8 * ((2 * s + hh) ^ swz<D>(r)));
       }
     } else {
-      const uint16_t* sgl = s_sum + row * D * D;   // uniform base, 32-bit lane offsets
+      const uint16_t* sgl = s_sum + srow * D * D;   // uniform base, 32-bit lane offsets
 #pragma unroll
       for (int u = 0; u < DTH; ++u)
 #pragma unroll
         for (int s = 0; s < NS; ++s)
           sf[u][s] = load8_at(sgl, static_cast<uint32_t>(((32 * (own0 + u) + l32) * D + 16 * s + 8 * hh) * 2));
     }
-    if (!kRla && !sg_ok && t < D) sg[t] = sigma_sum[row * D + t];
+    if (!kRla && !kPisa && !sg_ok && t < D) sg[t] = sigma_sum[row * D + t];
   }
   __syncthreads();
   if constexpr (kHooks) hook(1);   // every wave has read S_i^T: the LDS below merge_lds is free
@@ -177,7 +188,20 @@ __device__ __forceinline__ void attention_finish(
   f32x16 ol[DTH];
 #pragma unroll
   for (int u = 0; u < DTH; ++u) ol[u] = zero16();
-  if constexpr (kRla) {
+  if constexpr (kPisa) {
+    // Hbar^T Q^T on the matrix cores (raw Q: the 1/sqrt(d) goes into the
+    // row factor with A_t and the denominator)
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int u = 0; u < DTH; ++u) ol[u] = mfma32(sf[u][s], qf[s], ol[u]);
+    const float a_p = rbuf[partner * 32 + l32];
+    const float fac = (a_full * w_me + a_p * w_p) * inv * (cl * (1.0f / kLog2e));
+#pragma unroll
+    for (int u = 0; u < DTH; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ol[u][r] *= fac;
+  } else if constexpr (kRla) {
     // RMS norm of phi(Q) S_i over the row's D dims: this lane's 16 * DTH, the
     // partner lane's (l ^ 32) and the other key-half wave's (wave ^ 2) half
     float ss = 0.0f;
@@ -221,7 +245,7 @@ __device__ __forceinline__ void attention_finish(
   }
 
   // ---- alpha mix and store ----
-  const float al = alpha[h];
+  const float al = kPisa ? 1.0f : alpha[h];
   if (qrow < n_i) {
     // uniform bases of the query block, 32-bit offsets of this lane's row
     char* obase = reinterpret_cast<char*>(static_cast<T*>(o) + hoff + static_cast<int64_t>(kBlock * i) * g.sn);
@@ -238,7 +262,7 @@ __device__ __forceinline__ void attention_finish(
         for (int x = 0; x < 4; ++x) {
           sv[x] = o_own[u][4 * r4 + x];
           lv[x] = ol[u][4 * r4 + x];
-          ov[x] = al * sv[x] + (1.0f - al) * lv[x];
+          ov[x] = kPisa ? sv[x] + lv[x] : al * sv[x] + (1.0f - al) * lv[x];
         }
         store4(reinterpret_cast<T*>(obase + orow + dim0 * sizeof(T)), ov);
         if (o_sparse) store4(reinterpret_cast<float*>(reinterpret_cast<char*>(o_sparse + dbg0) + drow + dim0 * 4), sv);

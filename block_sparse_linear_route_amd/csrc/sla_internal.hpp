@@ -48,6 +48,35 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
                             const float* alpha, void* o, float* o_sparse, float* o_linear,
                             bool rla, hipStream_t stream);
 
+// Piecewise exact-or-approximate attention.  Pseudo-blocks: the centroid
+// rows are grouped 64 to a tile; the block statistics are reduced in chunks
+// of G consecutive KV blocks (fewer blocks per chunk when that leaves fewer
+// than 512 workgroups), each chunk leaving a float32 d x d partial sum.
+inline int pisa_pseudo_blocks(const Geometry& g) { return (g.nkb + 63) / 64; }
+inline int pisa_chunk_blocks(const Geometry& g) {
+  int G = 16;
+  while (G > 1 && static_cast<int64_t>(g.B) * g.H * ((g.nkb + G - 1) / G) < 512) G /= 2;
+  return G;
+}
+inline int pisa_chunks(const Geometry& g) {
+  const int G = pisa_chunk_blocks(g);
+  return (g.nkb + G - 1) / G;
+}
+// kbar / vbar: bf16 [B*H][pisa_pseudo_blocks*64][d] block means of K / V;
+// hbar: bf16 [B*H][d][d] value-major mean first-order matrix; part: float32
+// [B*H][pisa_chunks][d][d] scratch; hbar_f32: optional float32 copy of hbar.
+hipError_t launch_pisa_stats(const Geometry& g, const void* k, const void* v, uint16_t* kbar,
+                             uint16_t* vbar, uint16_t* hbar, float* part, float* hbar_f32,
+                             hipStream_t stream);
+// The fused pass: exact online softmax over the critical blocks, then the
+// centroid pseudo-blocks in the same softmax, then the first-order
+// correction; o_softmax / o_correction (float, optional) are the two parts
+// of O divided by the shared denominator.
+hipError_t launch_attention_pisa(const Geometry& g, const void* q, const void* k, const void* v,
+                                 const int32_t* crit, const uint16_t* kbar, const uint16_t* vbar,
+                                 const uint16_t* hbar, void* o, float* o_softmax,
+                                 float* o_correction, hipStream_t stream);
+
 hipError_t launch_quantize_fp8(const Geometry& g, const void* x, uint8_t* codes, float* scales,
                                hipStream_t stream);
 

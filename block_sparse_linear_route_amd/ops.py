@@ -261,6 +261,68 @@ def forward_rla(q, k, v, crit_idx, h_states, alpha, *, branches: bool = False, o
     return (out, o_s, o_l) if branches else out
 
 
+def _pisa_problem(x: torch.Tensor, k_crit: int) -> _lib.Problem:
+    # the unselected set is every non-critical block: k_marg = nkb - k_crit
+    # (the kernels do not read it; it only has to pass validation)
+    return make_problem(x, k_crit, num_blocks(x.shape[2]) - k_crit)
+
+
+def pisa_workspace(q: torch.Tensor) -> torch.Tensor:
+    """A workspace for ``pisa_statistics`` / ``forward_attend_pisa`` / ``forward_pisa``."""
+    return _workspace(_pisa_problem(q, 0), _lib.OP_FORWARD_PISA, q.device)
+
+
+def pisa_statistics(k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor, *,
+                    want_hbar: bool = False, stream=None):
+    """Block centroids, value means and Hbar into ``workspace``; returns Hbar
+    (float32 [B,H,d,d], value-major: [c][a] = Hbar[a][c]) if ``want_hbar``."""
+    (v,) = _same_layout(k, v)
+    p = _pisa_problem(k, 0)
+    B, H, N, d = k.shape
+    hb = torch.empty((B, H, d, d), dtype=torch.float32, device=k.device) if want_hbar else None
+    _check(lib.sla_pisa_statistics(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(hb), _ptr(workspace),
+                                   workspace.numel(), _stream(stream)))
+    return hb
+
+
+def forward_attend_pisa(q, k, v, crit_idx, workspace, *, branches: bool = False, out=None,
+                        stream=None):
+    """The fused pass of ``forward_pisa`` from a workspace ``pisa_statistics`` filled."""
+    k, v = _same_layout(q, k, v)
+    p = _pisa_problem(q, int(crit_idx.shape[-1]))
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    o_s = o_c = None
+    if branches:
+        o_s = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        o_c = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _check(lib.sla_forward_attend_pisa(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(crit_idx.contiguous()), _ptr(out), _ptr(o_s), _ptr(o_c),
+                                       _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (out, o_s, o_c) if branches else out
+
+
+def forward_pisa(q, k, v, crit_idx, *, branches: bool = False, out=None, workspace=None,
+                 stream=None):
+    """Piecewise exact-or-approximate attention: the critical blocks exactly,
+    every other block through its centroid (zero order) plus one global
+    first-order correction, all in one softmax.  Returns O (and the softmax
+    part and the correction part, O = their sum, if ``branches``)."""
+    k, v = _same_layout(q, k, v)
+    p = _pisa_problem(q, int(crit_idx.shape[-1]))
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    o_s = o_c = None
+    if branches:
+        o_s = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        o_c = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    ws = workspace if workspace is not None else _workspace(p, _lib.OP_FORWARD_PISA, q.device)
+    _check(lib.sla_forward_pisa(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(crit_idx.contiguous()), _ptr(out), _ptr(o_s), _ptr(o_c),
+                                _ptr(ws), ws.numel(), _stream(stream)))
+    return (out, o_s, o_c) if branches else out
+
+
 def quantize_fp8(x: torch.Tensor, stream=None):
     """Per-block E4M3 codes (uint8 [B,H,N,d]) and float32 scales [B,H,nb]."""
     p = make_problem(x, 0, 1)

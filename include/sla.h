@@ -68,7 +68,7 @@ extern "C" {
 #endif
 
 #define SLA_VERSION_MAJOR 0
-#define SLA_VERSION_MINOR 3
+#define SLA_VERSION_MINOR 4
 #define SLA_VERSION_PATCH 0
 
 /* Status codes. */
@@ -91,7 +91,8 @@ typedef enum sla_op {
   SLA_OP_FORWARD = 2,
   SLA_OP_QUANTIZE_FP8 = 3,
   SLA_OP_FORWARD_FP8 = 4,
-  SLA_OP_ROUTE_TAYLOR = 5
+  SLA_OP_ROUTE_TAYLOR = 5,
+  SLA_OP_FORWARD_PISA = 6
 } sla_op;
 
 /* Problem description (host struct, read only during the call).
@@ -122,7 +123,9 @@ int sla_num_blocks(const sla_problem* problem, int32_t* nq, int32_t* nkb);
  * B*H*2*ceil(nkb/64)*(nq rounded up to 512) 32-bit words of marginal-mask
  * bits, each region 256-byte aligned; SLA_OP_ROUTE
  * needs float64 pooled Q and K, SLA_OP_ROUTE_TAYLOR those and float64 block
- * key variances. */
+ * key variances; SLA_OP_FORWARD_PISA needs bf16 block means of K and V
+ * [B,H,64*ceil(nkb/64),d], a bf16 Hbar [B,H,d,d] and float32 per-chunk
+ * partial sums of the first-order matrices. */
 int sla_workspace_size(const sla_problem* problem, int op, size_t* bytes);
 
 /* Block routing.  [SLA2 summary 2.B; SLA abstract]
@@ -285,6 +288,41 @@ int sla_forward_rla(const sla_problem* problem, const void* q, const void* k, co
                     const int32_t* crit_idx, const void* h_states, const float* alpha,
                     void* o, float* o_sparse, float* o_linear, void* ws, size_t ws_bytes,
                     void* stream);
+
+/* Piecewise exact-or-approximate attention.  [PISA summary, section 2:
+ * "Algoritmo Central", "Implementación de Hardware"]
+ * The critical blocks of query block i (crit_idx, as written by sla_route)
+ * are attended exactly (the problem's k_marg only has to pass validation;
+ * the unselected set is every other block); every other KV block j enters
+ * the same softmax through its centroid: alpha_tj = exp(q_t . kbar_j / sqrt(d))
+ * adds alpha_tj * (sum of the block's values) to the numerator and
+ * alpha_tj * n_j to the denominator; one global first-order correction
+ * (q_t / sqrt(d)) Hbar sum_j alpha_tj joins the numerator, with
+ * Hbar = mean over all KV blocks of H_j = sum_n (k_n - kbar_j)^T v_n.
+ * o_t = numerator / denominator.
+ *
+ * sla_pisa_statistics writes kbar, the block means of V and Hbar into the
+ * workspace (sla_workspace_size(SLA_OP_FORWARD_PISA) bytes); hbar, when not
+ * NULL, receives Hbar as float [B,H,d,d] value-major (element [c][a] =
+ * Hbar[a][c], a = key feature, c = value dim).  Block means are float32
+ * sums of the valid tokens, rounded to bf16; H is accumulated in float32 on
+ * the matrix cores from bf16 block-centred K and V.
+ * sla_forward_attend_pisa runs the fused pass from that workspace:
+ * o            out [B,H,N,d], problem dtype
+ * o_softmax,
+ * o_correction out float [B,H,N,d] contiguous, or NULL: the exact and
+ *              zero-order part and the first-order part of the numerator,
+ *              each divided by the denominator (o is their sum).
+ * sla_forward_pisa is the two in order on one stream. */
+int sla_pisa_statistics(const sla_problem* problem, const void* k, const void* v,
+                        float* hbar, void* ws, size_t ws_bytes, void* stream);
+int sla_forward_attend_pisa(const sla_problem* problem, const void* q, const void* k,
+                            const void* v, const int32_t* crit_idx, void* o,
+                            float* o_softmax, float* o_correction, const void* ws,
+                            size_t ws_bytes, void* stream);
+int sla_forward_pisa(const sla_problem* problem, const void* q, const void* k,
+                     const void* v, const int32_t* crit_idx, void* o, float* o_softmax,
+                     float* o_correction, void* ws, size_t ws_bytes, void* stream);
 
 /* Host: static text of a status code. */
 const char* sla_status_string(int status);

@@ -82,6 +82,9 @@ def test_num_blocks_and_workspace():
     assert n.value >= 2 * 2 * 512 * 128 * 8
     assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_ROUTE_TAYLOR, ctypes.byref(n)) == 0
     assert n.value >= 3 * 2 * 512 * 128 * 8
+    # PISA: centroids and value means (bf16, 8 tiles of 64 rows), Hbar and partials
+    assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_FORWARD_PISA, ctypes.byref(n)) == 0
+    assert n.value >= 2 * (2 * 512 * 128 * 2) + 2 * 128 * 128 * 2 + 2 * 128 * 128 * 4
     assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_LINEAR_STATES, ctypes.byref(n)) == 0
     assert n.value == 0
     assert lib.sla_workspace_size(ctypes.byref(p), 99, ctypes.byref(n)) == _lib.SLA_ERR_INVALID_ARGUMENT
@@ -92,7 +95,7 @@ def test_status_strings_and_version():
         assert lib.sla_status_string(s)
     a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     assert lib.sla_version(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 0
-    assert (a.value, b.value, c.value) == (0, 3, 0)
+    assert (a.value, b.value, c.value) == (0, 4, 0)
 
 
 def test_entry_points_reject_bad_arguments_before_any_device_call():
@@ -166,3 +169,30 @@ def test_residual_entry_points_reject_bad_arguments_before_any_device_call():
     all_crit = P(k_crit=16, k_marg=0)        # no residual block: no states needed
     st = lib.sla_residual_sums(ctypes.byref(all_crit), fake, None, fake, 16, None)
     assert st == _lib.SLA_ERR_WORKSPACE
+
+
+def test_pisa_entry_points_reject_bad_arguments_before_any_device_call():
+    fake = ctypes.c_void_p(0x10000)
+    p = P()
+    st = lib.sla_pisa_statistics(ctypes.byref(p), fake, None, None, fake, 1 << 40, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT       # v missing
+    st = lib.sla_pisa_statistics(ctypes.byref(p), fake, fake, ctypes.c_void_p(0x10004), fake,
+                                 1 << 40, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT       # misaligned Hbar output
+    st = lib.sla_pisa_statistics(ctypes.byref(p), fake, fake, None, fake, 64, None)
+    assert st == _lib.SLA_ERR_WORKSPACE
+    st = lib.sla_forward_attend_pisa(ctypes.byref(p), fake, fake, fake, None, fake, None, None,
+                                     fake, 1 << 40, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT       # k_crit > 0 and no critical list
+    st = lib.sla_forward_attend_pisa(ctypes.byref(p), fake, fake, fake, fake, None, None, None,
+                                     fake, 1 << 40, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT       # o missing
+    n = ctypes.c_size_t()
+    lib.sla_workspace_size(ctypes.byref(p), _lib.OP_FORWARD, ctypes.byref(n))
+    st = lib.sla_forward_pisa(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, fake,
+                              64, None)
+    assert st == _lib.SLA_ERR_WORKSPACE
+    bad = P(head_dim=96)
+    st = lib.sla_forward_pisa(ctypes.byref(bad), fake, fake, fake, fake, fake, None, None, fake,
+                              1 << 40, None)
+    assert st == _lib.SLA_ERR_UNSUPPORTED
