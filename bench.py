@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=6,
                     help="heads the oracle runs for the CPU baseline (scaled to all heads)")
+    ap.add_argument("--no-pisa", action="store_true",
+                    help="skip the piecewise exact-or-approximate attention side measurement")
     ap.add_argument("--no-rla", action="store_true",
                     help="skip the residual-linear-attention side measurement")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -285,6 +287,58 @@ def main():
                     "per query block",
         }
 
+    pisa_variant = None
+    if not fp8 and not args.no_pisa:
+        # piecewise exact-or-approximate attention on the same inputs: the
+        # critical split of the step exact, every other block by centroid
+        ws_p = sla_gpu.pisa_workspace(q)
+
+        def pisa_step(ev=None):
+            def mark(n):
+                if ev is not None:
+                    ev[n].record()
+            mark(0)
+            rp = sla_gpu.route(q, k, kc, km)
+            mark(1)
+            sla_gpu.pisa_statistics(k, v, ws_p)
+            mark(2)
+            op = sla_gpu.forward_attend_pisa(q, k, v, rp["crit_idx"], ws_p)
+            mark(3)
+            return rp, op
+
+        for _ in range(2):
+            pisa_step()
+        n_p = max(3, args.steps // 2)
+        evp = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_p)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n_p):
+            rp, _ = pisa_step(evp[i])
+        torch.cuda.synchronize()
+        ms_p = (time.perf_counter() - t0) * 1e3 / n_p
+        pp = np.array([[evp[i][j].elapsed_time(evp[i][j + 1]) for j in range(3)]
+                       for i in range(n_p)]).mean(axis=0)
+        nbk = (N + 63) // 64
+        # exact blocks as in the step, one 64-key tile of centroids per 64
+        # KV blocks (only the unselected ones count), the first-order term
+        fp_crit = f_crit
+        fp_zero = 4.0 * B * H * N * d * (nbk - kc)
+        fp_corr = 2.0 * B * H * N * d * d
+        fp_stats = 2.0 * B * H * N * d * d
+        pisa_variant = {
+            "ms_per_step": ms_p,
+            "forward_ms": float(pp[1] + pp[2]),
+            "breakdown_ms": {"route": pp[0], "block_statistics": pp[1], "attention_pisa": pp[2]},
+            "attention_pisa_tflops": (fp_crit + fp_zero + fp_corr) / (pp[2] * 1e-3) / 1e12,
+            "forward_tflops": (fp_crit + fp_zero + fp_corr + fp_stats) / ((pp[1] + pp[2]) * 1e-3) / 1e12,
+            "note": "piecewise exact-or-approximate attention: the step's critical blocks exact, "
+                    f"the other {nbk - kc} blocks per query block through their centroids "
+                    f"({(nbk + 63) // 64} pseudo-blocks of 64 centroids in the same online "
+                    "softmax), one global first-order correction; FLOPs count 4 n d per "
+                    "exact key and per unselected centroid, 2 N d^2 for the correction and "
+                    "2 N d^2 for the block statistics",
+        }
+
     # the second-order routing score on the same inputs (route only: the
     # forward that follows is the same kernels on its index lists)
     for _ in range(2):
@@ -365,6 +419,8 @@ def main():
         out["fp8_sparse_branch"] = fp8_variant
     if rla_variant is not None:
         out["residual_linear_attention"] = rla_variant
+    if pisa_variant is not None:
+        out["piecewise_attention"] = pisa_variant
     out["taylor_routing"] = taylor_route
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, kc, km, f_step, args.cpu_heads)
