@@ -212,3 +212,45 @@ def test_pisa_correction_unscaled(monkeypatch):
 def test_pisa_correction_sign(monkeypatch):
     monkeypatch.setattr(pisa_mod, "global_first_order", lambda H: -H.mean(axis=0))
     _fails(pisa_pins.test_equal_first_order_matrices_leave_second_order_error)
+
+
+from oracle import backward as bwd_mod
+import tests.test_oracle_pins_backward as bwd_pins
+
+
+def test_backward_softmax_without_row_term(monkeypatch):
+    orig = bwd_mod.sparse_branch_backward
+
+    def bad(q, k, v, crit_idx, do_s, block=64):
+        # drops the rowsum(dO_s * O_s) term: dS = P * dP
+        n, d = q.shape
+        dq = np.zeros_like(q); dk = np.zeros_like(k); dv = np.zeros_like(v)
+        for i, (a, b) in enumerate(sla.block_ranges(n, block)):
+            c = crit_idx[i]
+            if len(c) == 0:
+                continue
+            toks = np.concatenate([np.arange(*sla.block_ranges(n, block)[j]) for j in c])
+            x = q[a:b] @ k[toks].T / math.sqrt(d)
+            p = np.exp(x - x.max(axis=1, keepdims=True)); p /= p.sum(axis=1, keepdims=True)
+            dv[toks] += p.T @ do_s[a:b]
+            ds = p * (do_s[a:b] @ v[toks].T)
+            dq[a:b] += ds @ k[toks] / math.sqrt(d)
+            dk[toks] += ds.T @ q[a:b] / math.sqrt(d)
+        return dq, dk, dv
+    monkeypatch.setattr(bwd_mod, "sparse_branch_backward", bad)
+    _fails(bwd_pins.test_gradients_match_finite_differences, 20, 1, 1, 0.6)
+
+
+def test_backward_phi_jacobian_dropped(monkeypatch):
+    monkeypatch.setattr(bwd_mod, "phi_backward", lambda f, df: df)
+    _fails(bwd_pins.test_gradients_match_finite_differences, 24, 0, 2, 0.5)
+
+
+def test_backward_alpha_sign(monkeypatch):
+    orig = bwd_mod.backward_head
+
+    def bad(q, k, v, crit_idx, marg_idx, alpha, do, block=64):
+        dq, dk, dv, da = orig(q, k, v, crit_idx, marg_idx, alpha, do, block)
+        return dq, dk, dv, -da
+    monkeypatch.setattr(bwd_mod, "backward_head", bad)
+    _fails(bwd_pins.test_gradients_match_finite_differences, 20, 1, 1, 0.6)
