@@ -6,6 +6,7 @@ binding.  Importing it fails if the library has not been built.
 """
 from .ops import (  # noqa: F401
     SlaError,
+    backward,
     forward,
     forward_attend,
     forward_attend_fp8,

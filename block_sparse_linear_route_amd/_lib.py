@@ -20,7 +20,7 @@ SLA_ERR_NO_DEVICE = -5
 
 SLA_F32, SLA_BF16 = 0, 1
 (OP_ROUTE, OP_LINEAR_STATES, OP_FORWARD, OP_QUANTIZE_FP8, OP_FORWARD_FP8, OP_ROUTE_TAYLOR,
- OP_FORWARD_PISA) = range(7)
+ OP_FORWARD_PISA, OP_BACKWARD) = range(8)
 
 
 class Problem(ctypes.Structure):
@@ -66,6 +66,8 @@ SIGNATURES = {
     "sla_forward_attend_pisa": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                                _vp]),
     "sla_forward_pisa": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sla_backward": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _vp, _vp, _sz, _vp]),
     "sla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sla_last_error_message": (ctypes.c_char_p, []),
     "sla_version": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int)] * 3),

@@ -204,6 +204,66 @@ PisaWs carve_pisa_ws(const sla::Geometry& g, void* ws) {
   return w;
 }
 
+// Backward workspace: [forward workspace][O scratch, problem layout]
+// [O_s f32][O_l f32][lse f32 B*H*N][D_t f32 B*H*N][dS bf16 B*H*nq*d*d]
+// [dsigma f32 B*H*nq*d][dH bf16 B*H*nkb*d*d][critical bits^T]
+// [marginal bits^T][dalpha partials f32 B*H*nq], each region 256-byte aligned
+struct BwdWs {
+  FwdWs fwd;
+  void* o;
+  sla::BackwardBuffers b;
+};
+
+size_t span_elems(const sla::Geometry& g) {
+  return static_cast<size_t>((g.B - 1) * g.sb + (g.H - 1) * g.sh + (g.N - 1) * g.sn + g.D);
+}
+
+size_t backward_ws(const sla::Geometry& g) {
+  const size_t bh = static_cast<size_t>(g.B) * g.H;
+  const size_t rows = bh * g.N;
+  const size_t blk = bh * g.nq;
+  const size_t nmt = bh * sla::marginal_chunks(g) * sla::marginal_rows_pad(g) * 2;
+  return forward_ws(g) + align_up(span_elems(g) * 2) + 2 * align_up(rows * g.D * 4) +
+         2 * align_up(rows * 4) + align_up(blk * g.D * g.D * 2) + align_up(blk * g.D * 4) +
+         align_up(bh * g.nkb * g.D * g.D * 2) +
+         align_up(bh * g.nkb * sla::backward_crit_words(g) * 4) + align_up(nmt * 4) +
+         align_up(blk * 4);
+}
+
+BwdWs carve_backward_ws(const sla::Geometry& g, void* ws) {
+  const size_t bh = static_cast<size_t>(g.B) * g.H;
+  const size_t rows = bh * g.N;
+  const size_t blk = bh * g.nq;
+  const size_t nmt = bh * sla::marginal_chunks(g) * sla::marginal_rows_pad(g) * 2;
+  BwdWs w;
+  w.fwd = carve_forward_ws(g, ws);
+  char* p = static_cast<char*>(ws) + forward_ws(g);
+  w.o = p;
+  p += align_up(span_elems(g) * 2);
+  float* o_s = reinterpret_cast<float*>(p);
+  p += align_up(rows * g.D * 4);
+  float* o_l = reinterpret_cast<float*>(p);
+  p += align_up(rows * g.D * 4);
+  float* lse = reinterpret_cast<float*>(p);
+  p += align_up(rows * 4);
+  float* dd = reinterpret_cast<float*>(p);
+  p += align_up(rows * 4);
+  uint16_t* ds = reinterpret_cast<uint16_t*>(p);
+  p += align_up(blk * g.D * g.D * 2);
+  float* dsig = reinterpret_cast<float*>(p);
+  p += align_up(blk * g.D * 4);
+  uint16_t* dh = reinterpret_cast<uint16_t*>(p);
+  p += align_up(bh * g.nkb * g.D * g.D * 2);
+  uint32_t* crit_t = reinterpret_cast<uint32_t*>(p);
+  p += align_up(bh * g.nkb * sla::backward_crit_words(g) * 4);
+  uint32_t* marg_t = reinterpret_cast<uint32_t*>(p);
+  p += align_up(nmt * 4);
+  float* dap = reinterpret_cast<float*>(p);
+  w.b = sla::BackwardBuffers{o_s, o_l, lse, dd, w.fwd.s_sum, w.fwd.sigma, ds, dsig, dh, crit_t,
+                             marg_t, dap};
+  return w;
+}
+
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return SLA_OK;
   if (!ws) return fail(SLA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
@@ -242,6 +302,7 @@ int sla_workspace_size(const sla_problem* problem, int op, size_t* bytes) {
     case SLA_OP_FORWARD_FP8: *bytes = forward_ws(g); return SLA_OK;
     case SLA_OP_ROUTE_TAYLOR: *bytes = route_taylor_ws(g); return SLA_OK;
     case SLA_OP_FORWARD_PISA: *bytes = pisa_ws(g); return SLA_OK;
+    case SLA_OP_BACKWARD: *bytes = backward_ws(g); return SLA_OK;
     default: return fail(SLA_ERR_INVALID_ARGUMENT, "unknown op %d", op);
   }
 }
@@ -582,6 +643,48 @@ int sla_forward_pisa(const sla_problem* problem, const void* q, const void* k, c
   SLA_TRY(sla_pisa_statistics(problem, k, v, nullptr, ws, ws_bytes, stream));
   return sla_forward_attend_pisa(problem, q, k, v, crit_idx, o, o_softmax, o_correction, ws,
                                  ws_bytes, stream);
+}
+
+int sla_backward(const sla_problem* problem, const void* q, const void* k, const void* v,
+                 const void* dout, const int32_t* crit_idx, const int32_t* marg_idx,
+                 const void* h_states, const float* z_states, const float* alpha, float* dq,
+                 float* dk, float* dv, float* dalpha, void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  if (problem->dtype != SLA_BF16)
+    return fail(SLA_ERR_UNSUPPORTED, "the backward pass takes bf16 inputs only");
+  SLA_REQ(q, 16);
+  SLA_REQ(k, 16);
+  SLA_REQ(v, 16);
+  SLA_REQ(dout, 16);
+  SLA_REQ(alpha, 4);
+  SLA_REQ(dq, 16);
+  SLA_REQ(dk, 16);
+  SLA_REQ(dv, 16);
+  SLA_REQ(dalpha, 4);
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  if (problem->k_marg > 0) {
+    SLA_REQ(marg_idx, 4);
+    SLA_REQ(h_states, 16);
+    SLA_REQ(z_states, 16);
+  }
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, backward_ws(g)));
+  SLA_TRY(check_device());
+  const BwdWs w = carve_backward_ws(g, ws);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (g.k_marg > 0)
+    SLA_TRY(launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
+                                               z_states, w.fwd.s_sum, w.fwd.sigma, w.fwd.bits,
+                                               false, st),
+                     "backward marginal sums"));
+  SLA_TRY(launched(sla::launch_attention(g, q, k, v, crit_idx, w.fwd.s_sum, w.fwd.sigma, alpha,
+                                         w.o, const_cast<float*>(w.b.o_s),
+                                         const_cast<float*>(w.b.o_l), false, st,
+                                         const_cast<float*>(w.b.lse)),
+                   "backward forward pass"));
+  return launched(sla::launch_backward(g, w.b, q, k, v, dout, crit_idx, marg_idx, alpha, dq, dk,
+                                       dv, dalpha, st),
+                  "backward launch");
 }
 
 const char* sla_status_string(int status) {

@@ -62,6 +62,7 @@ struct AttnArgs {
   float bias_full;
   float bias_last;
   float inv_last;
+  float* lse;        // optional log2 normaliser of the sparse softmax per row
 };
 
 // RLA: residual linear attention epilogue (the marginal sum holds every
@@ -493,7 +494,7 @@ attention_kernel(AttnArgs A) {
                                                    !RLA && !PISA && has_lin, g, bh, h, i, n_i, qrow,
                                                    hoff, A.s_sum, A.sigma_sum, A.alpha, A.o,
                                                    A.o_sparse, A.o_linear, oacc, m_run, l_run, cl,
-                                                   qf, [](int) {}, a_run);
+                                                   qf, [](int) {}, a_run, A.lse);
 }
 
 template <typename T, int D>
@@ -523,7 +524,7 @@ hipError_t launch_attention_pisa(const Geometry& g, const void* q, const void* k
              static_cast<float>(cl), kbar, vbar, pisa_pseudo_blocks(g),
              static_cast<float>(6.0 / cl),
              static_cast<float>(__builtin_log2(static_cast<double>(n_last)) / cl),
-             1.0f / static_cast<float>(n_last)};
+             1.0f / static_cast<float>(n_last), nullptr};
   if (g.dtype == 1) {
     if (g.D == 128) launch_attn_pisa_t<uint16_t, 128>(a, stream);
     else launch_attn_pisa_t<uint16_t, 64>(a, stream);
@@ -537,10 +538,10 @@ hipError_t launch_attention_pisa(const Geometry& g, const void* q, const void* k
 hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,
                             const int32_t* crit, const uint16_t* s_sum, const float* sigma_sum,
                             const float* alpha, void* o, float* o_sparse, float* o_linear,
-                            bool rla, hipStream_t stream) {
+                            bool rla, hipStream_t stream, float* lse) {
   AttnArgs a{q, k, v, crit, s_sum, sigma_sum, alpha, o, o_sparse, o_linear, g,
              static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(g.D))),
-             nullptr, nullptr, 0, 0.0f, 0.0f, 0.0f};
+             nullptr, nullptr, 0, 0.0f, 0.0f, 0.0f, lse};
   if (g.dtype == 1) {
     if (g.D == 128) launch_attn_t<uint16_t, 128>(a, rla, stream);
     else launch_attn_t<uint16_t, 64>(a, rla, stream);

@@ -27,6 +27,8 @@
 // (q_t / sqrt(d)) Hbar A_t to the numerator, A_t = sum of alpha_{t,j} over
 // the unselected blocks (a_run, merged like l_run), before the one division:
 // O_s is the softmax part, O_l the correction part, O = O_s + O_l.
+// lse (optional): float [B,H,N], log2 of each row's sparse softmax
+// normaliser in the scaled log2 units of the scores.
 // m_run is in the units of S; cl converts them to log2 units.
 #pragma once
 
@@ -83,7 +85,8 @@ __device__ __forceinline__ void attention_finish(
     int n_i, int qrow, int64_t hoff, const uint16_t* __restrict__ s_sum,
     const float* __restrict__ sigma_sum, const float* __restrict__ alpha, void* o,
     float* o_sparse, float* o_linear, const f32x16 (&oacc)[D / 32], float m_run, float l_run,
-    float cl, const bf16x8 (&qf)[D / 16], Hook&& hook, float a_run = 0.0f) {
+    float cl, const bf16x8 (&qf)[D / 16], Hook&& hook, float a_run = 0.0f,
+    float* __restrict__ lse = nullptr) {
   constexpr int NS = D / 16;
   constexpr int DT = D / 32;
   constexpr int DTH = DT / 2;
@@ -174,6 +177,11 @@ __device__ __forceinline__ void attention_finish(
   const float w_p = (m_p == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_p - m_tot) * cl);
   const float den = l_full * w_me + l_p * w_p;
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  // log2 of the sparse softmax normaliser, sum over kept keys of
+  // exp2(s * cl), for a backward pass to rebuild P (-inf when no key)
+  if (lse && kh == 0 && hh == 0 && qrow < n_i)
+    lse[static_cast<int64_t>(bh) * g.N + kBlock * i + qrow] =
+        den > 0.0f ? m_tot * cl + log2f(den) : -INFINITY;
   // merged O_s, in place of the wave's own partial output
 #pragma unroll
   for (int u = 0; u < DTH; ++u)

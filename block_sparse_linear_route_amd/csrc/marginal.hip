@@ -356,6 +356,13 @@ hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const ui
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_mask_gemm(g, bits, h_states, s_sum, stream);
+}
+
+hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint16_t* h_states,
+                            uint16_t* s_sum, hipStream_t stream) {
+  const int nchunks = marginal_chunks(g);
+  const int rows_pad = marginal_rows_pad(g);
   // 512-row tiles, and a 256-row tile for a remainder of at most 256 rows
   // (at nq = 1182: 1280 rows of matrix-core work instead of 1536)
   const int full = g.nq / 512, rem = g.nq - 512 * full;

@@ -41,12 +41,19 @@ hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const ui
                                 const float* z_states, uint16_t* s_sum, float* sigma_sum,
                                 uint32_t* bits, bool complement, hipStream_t stream);
 
+// The product S = M H alone, from mask bits already in the layout the
+// marginal sums write (chunk-major, rows padded to the 512-row tile); with
+// nq = nkb the roles of query and KV blocks can be swapped (a transposed mask).
+hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint16_t* h_states,
+                            uint16_t* s_sum, hipStream_t stream);
+
 // rla: residual linear attention epilogue (s_sum holds every non-critical
 // block's exponential-map state; RMS norm in place of the sigma denominator).
+// lse (optional, float [B,H,N]): log2 of each row's sparse softmax normaliser.
 hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,
                             const int32_t* crit, const uint16_t* s_sum, const float* sigma_sum,
                             const float* alpha, void* o, float* o_sparse, float* o_linear,
-                            bool rla, hipStream_t stream);
+                            bool rla, hipStream_t stream, float* lse = nullptr);
 
 // Piecewise exact-or-approximate attention.  Pseudo-blocks: the centroid
 // rows are grouped 64 to a tile; the block statistics are reduced in chunks
@@ -76,6 +83,33 @@ hipError_t launch_attention_pisa(const Geometry& g, const void* q, const void* k
                                  const int32_t* crit, const uint16_t* kbar, const uint16_t* vbar,
                                  const uint16_t* hbar, void* o, float* o_softmax,
                                  float* o_correction, hipStream_t stream);
+
+// Backward pass.  Buffers (all in the backward workspace): the forward's
+// float O_s, O_l [B*H][N][d] and log2 softmax normaliser [B*H][N]; the
+// forward workspace's marginal sums (s_sum, sigma); D_t [B*H][N]; dS_i bf16
+// [B*H][nq][d][d] and dsigma_i [B*H][nq][d]; dH bf16 [B*H][nkb][d][d]; the
+// transposed critical bit rows [B*H][nkb][backward_crit_words] and the
+// transposed marginal mask in the mask-product layout; dalpha partials
+// [B*H][nq].  Inputs bf16 only.
+struct BackwardBuffers {
+  const float* o_s;
+  const float* o_l;
+  const float* lse;
+  float* dd;
+  const uint16_t* s_sum;
+  const float* sigma;
+  uint16_t* ds;
+  float* dsig;
+  uint16_t* dh;
+  uint32_t* crit_t;
+  uint32_t* marg_t;
+  float* dalpha_part;
+};
+inline int backward_crit_words(const Geometry& g) { return (g.nq + 31) / 32; }
+hipError_t launch_backward(const Geometry& g, const BackwardBuffers& w, const void* q,
+                           const void* k, const void* v, const void* dout, const int32_t* crit,
+                           const int32_t* marg, const float* alpha, float* dq, float* dk,
+                           float* dv, float* dalpha, hipStream_t stream);
 
 hipError_t launch_quantize_fp8(const Geometry& g, const void* x, uint8_t* codes, float* scales,
                                hipStream_t stream);

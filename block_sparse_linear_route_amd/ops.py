@@ -323,6 +323,27 @@ def forward_pisa(q, k, v, crit_idx, *, branches: bool = False, out=None, workspa
     return (out, o_s, o_c) if branches else out
 
 
+def backward(q, k, v, dout, crit_idx, marg_idx, h_states, z_states, alpha, *, workspace=None,
+             stream=None):
+    """Gradients of ``forward`` for fixed block lists: (dq, dk, dv) float32
+    [B,H,N,d] and dalpha float32 [H].  bf16 inputs only."""
+    k, v, dout = _same_layout(q, k, v, dout)
+    kc, km = int(crit_idx.shape[-1]), int(marg_idx.shape[-1])
+    p = make_problem(q, kc, km)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32)
+    dk = torch.empty(q.shape, **f32)
+    dv = torch.empty(q.shape, **f32)
+    da = torch.empty(q.shape[1], **f32)
+    ws = workspace if workspace is not None else _workspace(p, _lib.OP_BACKWARD, q.device)
+    alpha = alpha.to(device=q.device, dtype=torch.float32).contiguous()
+    _check(lib.sla_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                            _ptr(crit_idx.contiguous()), _ptr(marg_idx.contiguous()),
+                            _ptr(h_states), _ptr(z_states), _ptr(alpha), _ptr(dq), _ptr(dk),
+                            _ptr(dv), _ptr(da), _ptr(ws), ws.numel(), _stream(stream)))
+    return dq, dk, dv, da
+
+
 def quantize_fp8(x: torch.Tensor, stream=None):
     """Per-block E4M3 codes (uint8 [B,H,N,d]) and float32 scales [B,H,nb]."""
     p = make_problem(x, 0, 1)

@@ -68,7 +68,7 @@ extern "C" {
 #endif
 
 #define SLA_VERSION_MAJOR 0
-#define SLA_VERSION_MINOR 4
+#define SLA_VERSION_MINOR 5
 #define SLA_VERSION_PATCH 0
 
 /* Status codes. */
@@ -92,7 +92,8 @@ typedef enum sla_op {
   SLA_OP_QUANTIZE_FP8 = 3,
   SLA_OP_FORWARD_FP8 = 4,
   SLA_OP_ROUTE_TAYLOR = 5,
-  SLA_OP_FORWARD_PISA = 6
+  SLA_OP_FORWARD_PISA = 6,
+  SLA_OP_BACKWARD = 7
 } sla_op;
 
 /* Problem description (host struct, read only during the call).
@@ -125,7 +126,11 @@ int sla_num_blocks(const sla_problem* problem, int32_t* nq, int32_t* nkb);
  * needs float64 pooled Q and K, SLA_OP_ROUTE_TAYLOR those and float64 block
  * key variances; SLA_OP_FORWARD_PISA needs bf16 block means of K and V
  * [B,H,64*ceil(nkb/64),d], a bf16 Hbar [B,H,d,d] and float32 per-chunk
- * partial sums of the first-order matrices. */
+ * partial sums of the first-order matrices; SLA_OP_BACKWARD needs the
+ * forward workspace, an O scratch in the problem layout, float O_s, O_l
+ * [B,H,N,d], float row statistics [B,H,N] x 2, bf16 dS [B,H,nq,d,d], float
+ * dsigma [B,H,nq,d], bf16 dH [B,H,nkb,d,d], transposed mask bits and float
+ * dalpha partials [B,H,nq]. */
 int sla_workspace_size(const sla_problem* problem, int op, size_t* bytes);
 
 /* Block routing.  [SLA2 summary 2.B; SLA abstract]
@@ -323,6 +328,35 @@ int sla_forward_attend_pisa(const sla_problem* problem, const void* q, const voi
 int sla_forward_pisa(const sla_problem* problem, const void* q, const void* k,
                      const void* v, const int32_t* crit_idx, void* o, float* o_softmax,
                      float* o_correction, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward pass of sla_forward for fixed block lists.  [SLA abstract
+ * (forward and backward); SLA2 summary 2.A (the mix)]
+ * The lists carry no gradient; alpha does.  With f = phi(q):
+ *   dalpha_h = sum over the head's rows and dims of dO * (O_s - O_l);
+ *   sparse branch (dO_s = alpha dO): the softmax backward over the critical
+ *     keys, dq += dS K / sqrt(d), dk += dS^T q / sqrt(d), dv += P^T dO_s;
+ *   linear branch (dO_l = (1 - alpha) dO): through O_l = f S_i / (f . sigma_i),
+ *     S_i = sum_{j in M_i} H_j, sigma_i = sum z_j, H_j = phi(K_j)^T V_j,
+ *     z_j = colsum phi(K_j), and the feature softmax phi.
+ * q, k, v, dout bf16 [B,H,N,d] (problem strides; float inputs are
+ *              SLA_ERR_UNSUPPORTED)
+ * crit_idx,
+ * marg_idx     as for sla_forward
+ * h_states,
+ * z_states     as written by sla_linear_states (read when k_marg > 0)
+ * alpha        float [H]
+ * dq, dk, dv   out float [B,H,N,d] contiguous
+ * dalpha       out float [H] (summed over the batch)
+ * ws           workspace of sla_workspace_size(SLA_OP_BACKWARD) bytes.
+ * The call recomputes the forward (marginal sums, then the fused kernel
+ * writing O_s, O_l and each row's log2 softmax normaliser into ws) before
+ * the gradient kernels.  P, dS and the linear-branch operands enter the
+ * matrix cores as bf16; accumulation is float32. */
+int sla_backward(const sla_problem* problem, const void* q, const void* k,
+                 const void* v, const void* dout, const int32_t* crit_idx,
+                 const int32_t* marg_idx, const void* h_states, const float* z_states,
+                 const float* alpha, float* dq, float* dk, float* dv, float* dalpha,
+                 void* ws, size_t ws_bytes, void* stream);
 
 /* Host: static text of a status code. */
 const char* sla_status_string(int status);

@@ -95,7 +95,7 @@ def test_status_strings_and_version():
         assert lib.sla_status_string(s)
     a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     assert lib.sla_version(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 0
-    assert (a.value, b.value, c.value) == (0, 4, 0)
+    assert (a.value, b.value, c.value) == (0, 5, 0)
 
 
 def test_entry_points_reject_bad_arguments_before_any_device_call():
@@ -196,3 +196,21 @@ def test_pisa_entry_points_reject_bad_arguments_before_any_device_call():
     st = lib.sla_forward_pisa(ctypes.byref(bad), fake, fake, fake, fake, fake, None, None, fake,
                               1 << 40, None)
     assert st == _lib.SLA_ERR_UNSUPPORTED
+
+
+def test_backward_entry_point_rejects_bad_arguments_before_any_device_call():
+    fake = ctypes.c_void_p(0x10000)
+    p = P()
+    st = lib.sla_backward(ctypes.byref(P(dtype=_lib.SLA_F32)), *([fake] * 14), 1 << 40, None)
+    assert st == _lib.SLA_ERR_UNSUPPORTED             # float inputs
+    st = lib.sla_backward(ctypes.byref(p), fake, fake, fake, None, *([fake] * 9), fake, 1 << 40, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT        # dO missing
+    st = lib.sla_backward(ctypes.byref(p), *([fake] * 5), None, *([fake] * 7), fake, 1 << 40, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT        # marginal list missing (k_marg > 0)
+    n = ctypes.c_size_t()
+    assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_BACKWARD, ctypes.byref(n)) == 0
+    f = ctypes.c_size_t()
+    lib.sla_workspace_size(ctypes.byref(p), _lib.OP_FORWARD, ctypes.byref(f))
+    assert n.value > f.value + 2 * 2 * 1000 * 128 * 4    # forward workspace + O_s + O_l at least
+    st = lib.sla_backward(ctypes.byref(p), *([fake] * 14), f.value, None)
+    assert st == _lib.SLA_ERR_WORKSPACE
