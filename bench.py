@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=6,
                     help="heads the oracle runs for the CPU baseline (scaled to all heads)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass side measurement")
     ap.add_argument("--no-pisa", action="store_true",
                     help="skip the piecewise exact-or-approximate attention side measurement")
     ap.add_argument("--no-rla", action="store_true",
@@ -339,6 +341,40 @@ def main():
                     "2 N d^2 for the block statistics",
         }
 
+    bwd_variant = None
+    if not fp8 and not args.no_backward and w.q.dtype == torch.bfloat16:
+        # the backward pass on the same inputs and lists (recomputes the
+        # forward, then the gradient kernels), for an upstream gradient dO
+        gdo = torch.Generator(device="cpu").manual_seed(4242)
+        dout = torch.randn(q.shape, generator=gdo).to(q.dtype).to(dev)
+        Hb, zb = sla_gpu.linear_states(k, v)
+        kb = sla_gpu.backward(q, k, v, dout, r["crit_idx"], r["marg_idx"], Hb, zb, alpha)
+        ws_b = sla_gpu.backward_workspace(q, kc, km)
+        n_b = max(3, args.steps // 2)
+        evb = [torch.cuda.Event(enable_timing=True) for _ in range(n_b + 1)]
+        torch.cuda.synchronize()
+        evb[0].record()
+        for i_ in range(n_b):
+            sla_gpu.backward(q, k, v, dout, r["crit_idx"], r["marg_idx"], Hb, zb, alpha, workspace=ws_b)
+            evb[i_ + 1].record()
+        torch.cuda.synchronize()
+        bwd_ms = float(np.mean([evb[i_].elapsed_time(evb[i_ + 1]) for i_ in range(n_b)]))
+        # executed FLOPs: the forward again, then per critical (query, key)
+        # pair 6 d (dQ kernel: S, dP, dQ) + 8 d (dK/dV kernel: S, dP, dV, dK),
+        # 4 d^2 per row on each side of the linear branch, and the marginal
+        # gradient sums like the forward's state sums
+        f_bwd = f_fwd + 3.5 * f_crit + (8.0 * d * d * N * B * H if km else 0.0) + f_sums
+        bwd_variant = {
+            "ms": bwd_ms,
+            "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12,
+            "executed_gflop": f_bwd / 1e9,
+            "note": "sla_backward for fixed lists: marginal sums and the fused forward again "
+                    "(writing O_s, O_l and the log2 softmax normaliser), then D_t, sparse dQ, "
+                    "linear query side, transposed masks, dH by the mask product, sparse dK/dV, "
+                    "linear KV side, dalpha; bf16 inputs, float32 gradients",
+        }
+        del kb
+
     # the second-order routing score on the same inputs (route only: the
     # forward that follows is the same kernels on its index lists)
     for _ in range(2):
@@ -422,6 +458,8 @@ def main():
     if pisa_variant is not None:
         out["piecewise_attention"] = pisa_variant
     out["taylor_routing"] = taylor_route
+    if bwd_variant is not None:
+        out["backward"] = bwd_variant
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, kc, km, f_step, args.cpu_heads)
     print(json.dumps(out), flush=True)

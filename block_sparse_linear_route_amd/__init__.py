@@ -7,6 +7,7 @@ binding.  Importing it fails if the library has not been built.
 from .ops import (  # noqa: F401
     SlaError,
     backward,
+    backward_workspace,
     forward,
     forward_attend,
     forward_attend_fp8,

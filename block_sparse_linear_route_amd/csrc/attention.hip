@@ -69,7 +69,7 @@ struct AttnArgs {
 // non-critical block's exponential-map state; RMS norm instead of the
 // phi(Q) . sigma_i denominator, so sigma_i is not loaded).  PISA: piecewise
 // exact-or-approximate attention (s_sum holds Hbar per head).
-template <typename T, int D, bool RLA, bool PISA = false>
+template <typename T, int D, bool RLA, bool PISA = false, bool LSE = false>
 __global__ void __launch_bounds__(kThreads, 2)
 attention_kernel(AttnArgs A) {
   constexpr int CH = D / 8;                    // 16-byte chunks per row
@@ -490,7 +490,7 @@ attention_kernel(AttnArgs A) {
   __syncthreads();
 
   const uint16_t* st_half = smem + ((nst & 1) ^ kh) * TILE;
-  attention_finish<T, D, ST_LDS, false, RLA, PISA>(smem_raw + EPI_OFF, st_half, sig_lds,
+  attention_finish<T, D, ST_LDS, false, RLA, PISA, LSE>(smem_raw + EPI_OFF, st_half, sig_lds,
                                                    !RLA && !PISA && has_lin, g, bh, h, i, n_i, qrow,
                                                    hoff, A.s_sum, A.sigma_sum, A.alpha, A.o,
                                                    A.o_sparse, A.o_linear, oacc, m_run, l_run, cl,
@@ -500,7 +500,10 @@ attention_kernel(AttnArgs A) {
 template <typename T, int D>
 void launch_attn_t(const AttnArgs& a, bool rla, hipStream_t stream) {
   const int total = a.g.B * a.g.H * a.g.nq;
-  if (rla)
+  if (a.lse)
+    hipLaunchKernelGGL((attention_kernel<T, D, false, false, true>), dim3(total), dim3(kThreads), 0,
+                       stream, a);
+  else if (rla)
     hipLaunchKernelGGL((attention_kernel<T, D, true>), dim3(total), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((attention_kernel<T, D, false>), dim3(total), dim3(kThreads), 0, stream, a);

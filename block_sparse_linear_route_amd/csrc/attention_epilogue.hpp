@@ -27,7 +27,7 @@
 // (q_t / sqrt(d)) Hbar A_t to the numerator, A_t = sum of alpha_{t,j} over
 // the unselected blocks (a_run, merged like l_run), before the one division:
 // O_s is the softmax part, O_l the correction part, O = O_s + O_l.
-// lse (optional): float [B,H,N], log2 of each row's sparse softmax
+// kLse: lse (float [B,H,N]) receives log2 of each row's sparse softmax
 // normaliser in the scaled log2 units of the scores.
 // m_run is in the units of S; cl converts them to log2 units.
 #pragma once
@@ -78,7 +78,7 @@ __device__ __forceinline__ int swz(int r) {
 // and hook(2) once the merge buffers are no longer read (all waves, after a
 // barrier): a caller can start loads for its next block there.
 template <typename T, int D, bool kStLds, bool kHooks, bool kRla = false, bool kPisa = false,
-          typename Hook>
+          bool kLse = false, typename Hook>
 __device__ __forceinline__ void attention_finish(
     unsigned char* merge_lds, const uint16_t* st_half, const float* sg_lds, bool sg_ok,
     const Geometry& g, int bh, int h, int i,
@@ -179,7 +179,7 @@ __device__ __forceinline__ void attention_finish(
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   // log2 of the sparse softmax normaliser, sum over kept keys of
   // exp2(s * cl), for a backward pass to rebuild P (-inf when no key)
-  if (lse && kh == 0 && hh == 0 && qrow < n_i)
+  if (kLse && kh == 0 && hh == 0 && qrow < n_i)
     lse[static_cast<int64_t>(bh) * g.N + kBlock * i + qrow] =
         den > 0.0f ? m_tot * cl + log2f(den) : -INFINITY;
   // merged O_s, in place of the wave's own partial output

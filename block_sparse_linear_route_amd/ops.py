@@ -323,6 +323,11 @@ def forward_pisa(q, k, v, crit_idx, *, branches: bool = False, out=None, workspa
     return (out, o_s, o_c) if branches else out
 
 
+def backward_workspace(q: torch.Tensor, k_crit: int, k_marg: int) -> torch.Tensor:
+    """A workspace for ``backward``."""
+    return _workspace(make_problem(q, k_crit, k_marg), _lib.OP_BACKWARD, q.device)
+
+
 def backward(q, k, v, dout, crit_idx, marg_idx, h_states, z_states, alpha, *, workspace=None,
              stream=None):
     """Gradients of ``forward`` for fixed block lists: (dq, dk, dv) float32
