@@ -33,10 +33,10 @@
 //   bwd_bits_kernel     the transposed critical relation as bit rows per KV
 //                       block, and the transposed marginal relation in the
 //                       mask-product layout (then dH = M^T dS by that product);
-//   bwd_dkdv_kernel     KV-major: for KV block j, the query blocks holding j
-//                       critical (from its bit row) stream Q and dO tiles
-//                       through an LDS ring; dK^T and dV^T accumulate on the
-//                       matrix cores;
+//   bwd_kv_kernel       KV-major (one instance for dV, one for dK): for KV
+//                       block j, the query blocks holding j critical (from
+//                       its bit row) stream Q and dO tiles through an LDS
+//                       ring; dV^T or dK^T accumulates on the matrix cores;
 //   bwd_lin_kv_kernel   the linear branch on the KV side (added to dk, dv);
 //   bwd_dalpha_kernel   dalpha per head, summed in a fixed order.
 // Gradients are float32; every kernel is deterministic (no atomics on
@@ -165,11 +165,13 @@ bwd_rowdot_kernel(BwdArgs A) {
 // ------------------------------------------------------------ sparse dQ
 // One workgroup per (b, h, query block i); wave = qh + 2 kh as in the
 // forward (qh: 32 of the 64 query rows, kh: 32 of the 64 keys of every
-// critical block).  Step it finds K(it), V(it) in kbuf[X], vbuf[X] (X =
-// it & 1) and sends K(it+1), V(it+1) into the other pair once its own LDS
-// reads are done.
+// critical block).  Step it finds K(it), V(it) in stage X = it & 1 of a
+// two-stage ring (one __shared__ array per stage and tensor, so reads of one
+// stage wait on nothing filling the other) and first sends K(it+1), V(it+1)
+// into the other stage.  One operand buffer serves K, then V, then K^T:
+// S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (alpha dP^T - D_t), dQ^T += K^T dS^T.
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kThreads, 2)
 bwd_dq_kernel(BwdArgs A) {
   constexpr int CH = D / 8;
   constexpr int TILE = kBlock * D;
@@ -178,7 +180,7 @@ bwd_dq_kernel(BwdArgs A) {
   constexpr int NS = D / 16;
   constexpr int DT = D / 32;
   constexpr int DTH = DT / 2;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t k0[TILE], k1[TILE], v0[TILE], v1[TILE];
 
   const Geometry& g = A.g;
   const int t = threadIdx.x, lane = t & 63;
@@ -216,11 +218,16 @@ bwd_dq_kernel(BwdArgs A) {
     const int r = 16 * wave + RPI * u + lrow;
     toff[u] = static_cast<uint32_t>(r) * rowb + static_cast<uint32_t>(16 * (lslot ^ swz<D>(r)));
   }
-  auto issue_tile = [&](bool is_k, int c, uint16_t* dst) {
+  auto issue = [&](auto xc, int c) {
+    constexpr int X = decltype(xc)::value;
     const uint32_t soff = static_cast<uint32_t>(kBlock * crit_at(c)) * rowb;
+    uint16_t* kd = (X ? k1 : k0) + 16 * wave * D;
+    uint16_t* vd = (X ? v1 : v0) + 16 * wave * D;
 #pragma unroll
-    for (int u = 0; u < IPW; ++u)
-      buffer_load_lds16(is_k ? krs : vrs, dst + (16 * wave + RPI * u) * D, toff[u], soff);
+    for (int u = 0; u < IPW; ++u) {
+      buffer_load_lds16(krs, kd + RPI * u * D, toff[u], soff);
+      buffer_load_lds16(vrs, vd + RPI * u * D, toff[u], soff);
+    }
   };
 
   const int krow = 32 * kh + l32;
@@ -240,10 +247,7 @@ bwd_dq_kernel(BwdArgs A) {
   const float al = A.alpha[h];
 
   wait_vmem();
-  if (kc > 0) {
-    issue_tile(true, 0, smem);
-    issue_tile(false, 0, smem + 2 * TILE);
-  }
+  if (kc > 0) issue(std::integral_constant<int, 0>(), 0);
   const int64_t rowg = hoff + static_cast<int64_t>(kBlock * i + qr) * sn;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -253,35 +257,24 @@ bwd_dq_kernel(BwdArgs A) {
   const int64_t rowt = static_cast<int64_t>(bh) * g.N + kBlock * i + qr;
   const float lse_t = A.lse[rowt];
   const float d_t = A.dd[rowt];
-  wait_vmem();
-  __syncthreads();
 
   auto step = [&](auto xc, int it) {
     constexpr int X = decltype(xc)::value;
-    const uint16_t* kb = smem + X * TILE;
-    const uint16_t* vb = smem + (2 + X) * TILE;
-    bf16x8 kf[NS], vf[NS];
+    wait_vmem();
+    __syncthreads();   // K(it), V(it) landed; the other stage's reads are done
+    if (it + 1 < kc) issue(std::integral_constant<int, X ^ 1>(), it + 1);
+    const uint16_t* kb = X ? k1 : k0;
+    const uint16_t* vb = X ? v1 : v0;
+    bf16x8 op[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      kf[s] = *reinterpret_cast<const bf16x8*>(kb + kofs[s]);
-      vf[s] = *reinterpret_cast<const bf16x8*>(vb + kofs[s]);
-    }
-    bf16x8 kt[DT][2];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) kt[dt][s] = tr_operand(kb + 16 * s * D, to1[dt], to2[dt]);
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this step's LDS reads are done
-    if (it + 1 < kc) {
-      issue_tile(true, it + 1, smem + (X ^ 1) * TILE);
-      issue_tile(false, it + 1, smem + (2 + (X ^ 1)) * TILE);
-    }
+    for (int s = 0; s < NS; ++s) op[s] = *reinterpret_cast<const bf16x8*>(kb + kofs[s]);
     f32x16 sc = zero16(), dp = zero16();
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      sc = mfma32(kf[s], qf[s], sc);
-      dp = mfma32(vf[s], gf[s], dp);
-    }
+    for (int s = 0; s < NS; ++s) sc = mfma32(op[s], qf[s], sc);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) op[s] = *reinterpret_cast<const bf16x8*>(vb + kofs[s]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) dp = mfma32(op[s], gf[s], dp);
     const int nj = min(kBlock, g.N - kBlock * crit_at(it));
     bf16x8 pb[2];
 #pragma unroll
@@ -292,36 +285,41 @@ bwd_dq_kernel(BwdArgs A) {
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      dqacc[dt] = mfma32(kt[dt][0], pb[0], dqacc[dt]);
-      dqacc[dt] = mfma32(kt[dt][1], pb[1], dqacc[dt]);
+      dqacc[dt] = mfma32(tr_operand(kb, to1[dt], to2[dt]), pb[0], dqacc[dt]);
+      dqacc[dt] = mfma32(tr_operand(kb + 16 * D, to1[dt], to2[dt]), pb[1], dqacc[dt]);
     }
     if (it + 1 - cbase == 64) {
       cbase += 64;
       cl0 = cl1;
       cl1 = cbase + 64 + lane < kc ? crow[cbase + 64 + lane] : 0;
     }
-    wait_vmem();
-    __syncthreads();
   };
   for (int it = 0; it < kc; it += 2) {
     step(std::integral_constant<int, 0>(), it);
     if (it + 1 < kc) step(std::integral_constant<int, 1>(), it + 1);
   }
+  wait_vmem();
+  __syncthreads();
 
   // merge the key halves: the wave keeps dims [32*own0, +32*DTH) and hands
   // the rest to the wave of the same query half
-  float* obuf = reinterpret_cast<float*>(smem);   // [4][DTH][16][64]
+  // each wave's outgoing half: [DTH][16][64] floats, waves 0-1 in k0, 2-3 in k1
+  auto wbuf = [&](int w) -> float* {
+    return reinterpret_cast<float*>(w < 2 ? k0 : k1) + (w & 1) * DTH * 16 * 64;
+  };
   const int own0 = kh * DTH;
   f32x16 own[DTH];
+  float* obuf_out = wbuf(wave);
 #pragma unroll
   for (int u = 0; u < DTH; ++u) {
     own[u] = kh ? dqacc[DTH + u] : dqacc[u];
     const f32x16 oth = kh ? dqacc[u] : dqacc[DTH + u];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) obuf[((wave * DTH + u) * 16 + r) * 64 + lane] = oth[r];
+    for (int r = 0; r < 16; ++r) obuf_out[(u * 16 + r) * 64 + lane] = oth[r];
   }
   __syncthreads();
   const int partner = wave ^ 2;
+  const float* obuf_in = wbuf(partner);
   const float rs = cl * (1.0f / kLog2e);   // 1 / sqrt(d)
   if (qrow < n_i) {
     float* dst = A.dq + (static_cast<int64_t>(bh) * g.N + kBlock * i + qrow) * D;
@@ -333,7 +331,7 @@ bwd_dq_kernel(BwdArgs A) {
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int r = 4 * r4 + x;
-          w[x] = (own[u][r] + obuf[((partner * DTH + u) * 16 + r) * 64 + lane]) * rs;
+          w[x] = (own[u][r] + obuf_in[(u * 16 + r) * 64 + lane]) * rs;
         }
         *reinterpret_cast<f32x4*>(dst + 32 * (own0 + u) + 8 * r4 + 4 * hh) = w;
       }
@@ -573,14 +571,46 @@ bwd_fill_kernel(uint32_t* __restrict__ p, int64_t n) {
 }
 
 // ------------------------------------------------------------ sparse dK, dV
+// The query blocks holding KV block j critical, ascending, from j's bit row
+// (returns the count; the list is complete after the caller's next barrier).
+__device__ __forceinline__ int bit_row_list(const uint32_t* __restrict__ brow, int W,
+                                            uint16_t* qlist, int* wcount) {
+  const int t = threadIdx.x;
+  uint32_t myword = 0;
+  if (t < W) {
+    myword = brow[t];
+    wcount[t + 1] = __builtin_popcount(myword);
+  }
+  if (t == 0) wcount[0] = 0;
+  __syncthreads();
+  if (t == 0)
+    for (int w = 1; w <= W; ++w) wcount[w] += wcount[w - 1];
+  __syncthreads();
+  if (t < W) {
+    int pos = wcount[t];
+    uint32_t word = myword;
+    while (word) {
+      qlist[pos++] = static_cast<uint16_t>(32 * t + __builtin_ctz(word));
+      word &= word - 1;
+    }
+  }
+  return wcount[W];
+}
+
 // One workgroup per (b, h, KV block j); wave = qh + 2 kh: kh picks 32 of the
-// block's 64 keys (their K and V rows stay in registers), qh 32 of the 64
-// rows of each streamed query block.  The query blocks that hold j critical
-// come from j's bit row as an ascending list in LDS; their Q and dO tiles
-// (and the rows' log2 normaliser and D_t) go through a two-stage LDS ring.
-template <int D>
-__global__ void __launch_bounds__(kThreads, 1)
-bwd_dkdv_kernel(BwdArgs A) {
+// block's 64 keys (their K rows, and V rows for dK, stay in registers as B
+// operands), qh 32 of the 64 rows of each streamed query block.  The query
+// blocks holding j critical stream their Q and dO tiles and the rows' log2
+// normaliser and D_t through a two-stage ring (one __shared__ array per
+// stage and tensor).  Per block, S = Q K^T on the matrix cores gives P (lane
+// = key), which feeds the B operand directly:
+//   GRAD_K = false: dV^T += dO^T (alpha P)          (dO^T by transposing reads)
+//   GRAD_K = true:  dP = dO V^T, dS = P (alpha dP - D_t), dK^T += Q^T dS
+// Two kernels instead of one keep each within 256 registers (two waves per
+// SIMD) at the price of computing S twice.
+template <int D, bool GRAD_K>
+__global__ void __launch_bounds__(kThreads, 2)
+bwd_kv_kernel(BwdArgs A) {
   constexpr int CH = D / 8;
   constexpr int TILE = kBlock * D;
   constexpr int RPI = 64 / CH;
@@ -588,8 +618,8 @@ bwd_dkdv_kernel(BwdArgs A) {
   constexpr int NS = D / 16;
   constexpr int DT = D / 32;
   constexpr int DTH = DT / 2;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];   // q[2], do[2]
-  __shared__ __attribute__((aligned(16))) float rowst[2][2][kBlock];  // [stage][lse, D]
+  __shared__ __attribute__((aligned(16))) uint16_t q0[TILE], q1[TILE], g0[TILE], g1[TILE];
+  __shared__ __attribute__((aligned(16))) float st0[2][kBlock], st1[2][kBlock];   // [lse, D]
   __shared__ uint16_t qlist[4096];
   __shared__ int wcount[129];
 
@@ -609,31 +639,9 @@ bwd_dkdv_kernel(BwdArgs A) {
   const int64_t sn = g.sn;
   const float al = A.alpha[h];
 
-  // the query blocks holding j critical, ascending
-  const int W = A.crit_words;
-  const uint32_t* brow = A.crit_t + (static_cast<int64_t>(bh) * g.nkb + j) * W;
-  uint32_t myword = 0;
-  if (t < W) {
-    myword = brow[t];
-    wcount[t + 1] = __builtin_popcount(myword);
-  }
-  if (t == 0) wcount[0] = 0;
-  __syncthreads();
-  if (t == 0)
-    for (int w = 1; w <= W; ++w) wcount[w] += wcount[w - 1];
-  __syncthreads();
-  if (t < W) {
-    int pos = wcount[t];
-    uint32_t word = myword;
-    while (word) {
-      const int bpos = __builtin_ctz(word);
-      qlist[pos++] = static_cast<uint16_t>(32 * t + bpos);
-      word &= word - 1;
-    }
-  }
-  const int cnt = wcount[W];
+  const int cnt = bit_row_list(A.crit_t + (static_cast<int64_t>(bh) * g.nkb + j) * A.crit_words,
+                               A.crit_words, qlist, wcount);
 
-  // ring loads of a query block's Q and dO tiles and row statistics
   const int lrow = lane / CH, lslot = lane % CH;
   const uint32_t rowb = static_cast<uint32_t>(sn * 2);
   const uint32_t head_bytes = static_cast<uint32_t>((g.N - 1) * sn * 2 + D * 2);
@@ -651,29 +659,31 @@ bwd_dkdv_kernel(BwdArgs A) {
     constexpr int X = decltype(xc)::value;
     const int qi = qlist[it];
     const uint32_t soff = static_cast<uint32_t>(kBlock * qi) * rowb;
+    uint16_t* qd = (X ? q1 : q0) + 16 * wave * D;
+    uint16_t* gd = (X ? g1 : g0) + 16 * wave * D;
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
-      buffer_load_lds16(qrs, smem + X * TILE + (16 * wave + RPI * u) * D, toff[u], soff);
-      buffer_load_lds16(grs, smem + (2 + X) * TILE + (16 * wave + RPI * u) * D, toff[u], soff);
+      buffer_load_lds16(qrs, qd + RPI * u * D, toff[u], soff);
+      buffer_load_lds16(grs, gd + RPI * u * D, toff[u], soff);
     }
+    float* stx = X ? &st1[0][0] : &st0[0][0];
     if (wave == 0 && lane < 16)
-      buffer_load_lds16(lrs, &rowst[X][0][0], 16u * lane, static_cast<uint32_t>(kBlock * qi * 4));
+      buffer_load_lds16(lrs, stx, 16u * lane, static_cast<uint32_t>(kBlock * qi * 4));
     if (wave == 1 && lane < 16)
-      buffer_load_lds16(drs, &rowst[X][1][0], 16u * lane, static_cast<uint32_t>(kBlock * qi * 4));
+      buffer_load_lds16(drs, stx + kBlock, 16u * lane, static_cast<uint32_t>(kBlock * qi * 4));
   };
 
-  // K and V rows of this wave's keys (B operands), rows past the block's
-  // end clamped (their columns are masked)
+  // B operands: this wave's keys (rows past the block's end clamped; their
+  // columns are masked)
   const int key = 32 * kh + l32;
   const int64_t krowg = hoff + static_cast<int64_t>(kBlock * j + min(key, nj - 1)) * sn;
-  bf16x8 kf[NS], vf[NS];
+  bf16x8 kf[NS];
+  [[maybe_unused]] bf16x8 vf[GRAD_K ? NS : 1];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     kf[s] = load8(A.k + krowg + 16 * s + 8 * hh);
-    vf[s] = load8(A.v + krowg + 16 * s + 8 * hh);
+    if constexpr (GRAD_K) vf[s] = load8(A.v + krowg + 16 * s + 8 * hh);
   }
-  // A operands: query rows 32 qh + l32 of the Q / dO tiles; transposing
-  // reads over those rows for dK^T and dV^T
   const int arow = 32 * qh + l32;
   int aofs[NS];
 #pragma unroll
@@ -682,9 +692,9 @@ bwd_dkdv_kernel(BwdArgs A) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) tr_offsets<D>(lane, 32 * qh, dt, to1[dt], to2[dt]);
 
-  f32x16 dkacc[DT], dvacc[DT];
+  f32x16 acc[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) dkacc[dt] = dvacc[dt] = zero16();
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
 
   wait_vmem();
   __syncthreads();   // list complete
@@ -693,54 +703,58 @@ bwd_dkdv_kernel(BwdArgs A) {
   auto step = [&](auto xc, int it) {
     constexpr int X = decltype(xc)::value;
     wait_vmem();
-    __syncthreads();   // block it in LDS; block it-1's reads done
-    const uint16_t* qt = smem + X * TILE;
-    const uint16_t* gt = smem + (2 + X) * TILE;
-    bf16x8 qa[NS], ga[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      qa[s] = *reinterpret_cast<const bf16x8*>(qt + aofs[s]);
-      ga[s] = *reinterpret_cast<const bf16x8*>(gt + aofs[s]);
-    }
-    bf16x8 qtr[DT][2], gtr[DT][2];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        qtr[dt][s] = tr_operand(qt + 16 * s * D, to1[dt], to2[dt]);
-        gtr[dt][s] = tr_operand(gt + 16 * s * D, to1[dt], to2[dt]);
-      }
+    __syncthreads();   // block it in LDS; the other stage's reads are done
+    if (it + 1 < cnt) issue(std::integral_constant<int, X ^ 1>(), it + 1);
+    const uint16_t* qt = X ? q1 : q0;
+    const uint16_t* gt = X ? g1 : g0;
+    const float* stx = X ? &st1[0][0] : &st0[0][0];
+    const int n_q = min(kBlock, g.N - kBlock * qlist[it]);
+    // row statistics of the 16 query rows in this lane's registers
     float lse_r[16], d_r[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tq = 32 * qh + 8 * (r >> 2) + 4 * hh + (r & 3);
-      lse_r[r] = rowst[X][0][tq];
-      d_r[r] = rowst[X][1][tq];
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    if (it + 1 < cnt) issue(std::integral_constant<int, X ^ 1>(), it + 1);
-    const int qi = qlist[it];
-    const int n_q = min(kBlock, g.N - kBlock * qi);
-    f32x16 sc = zero16(), dp = zero16();
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int tq = 32 * qh + 8 * r4 + 4 * hh;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(stx + tq);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      sc = mfma32(qa[s], kf[s], sc);
-      dp = mfma32(ga[s], vf[s], dp);
-    }
-    bf16x8 pvb[2], dsb[2];
+      for (int x = 0; x < 4; ++x) lse_r[4 * r4 + x] = a[x];
+      if constexpr (GRAD_K) {
+        const f32x4 dq4 = *reinterpret_cast<const f32x4*>(stx + kBlock + tq);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tq = 32 * qh + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const float p = (tq < n_q && key < nj) ? __builtin_amdgcn_exp2f(fmaf(sc[r], cl, -lse_r[r])) : 0.0f;
-      pvb[r >> 3][r & 7] = f32_to_bf16(al * p);
-      dsb[r >> 3][r & 7] = f32_to_bf16(p * fmaf(al, dp[r], -d_r[r]));
+        for (int x = 0; x < 4; ++x) d_r[4 * r4 + x] = dq4[x];
+      }
     }
+    bf16x8 op[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) op[s] = *reinterpret_cast<const bf16x8*>(qt + aofs[s]);
+    f32x16 sc = zero16();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sc = mfma32(op[s], kf[s], sc);
+    bf16x8 pb[2];
+    if constexpr (GRAD_K) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) op[s] = *reinterpret_cast<const bf16x8*>(gt + aofs[s]);
+      f32x16 dp = zero16();
+#pragma unroll
+      for (int s = 0; s < NS; ++s) dp = mfma32(op[s], vf[s], dp);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tq = 32 * qh + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const float p = (tq < n_q && key < nj) ? __builtin_amdgcn_exp2f(fmaf(sc[r], cl, -lse_r[r])) : 0.0f;
+        pb[r >> 3][r & 7] = f32_to_bf16(p * fmaf(al, dp[r], -d_r[r]));
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tq = 32 * qh + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const float p = (tq < n_q && key < nj) ? __builtin_amdgcn_exp2f(fmaf(sc[r], cl, -lse_r[r])) : 0.0f;
+        pb[r >> 3][r & 7] = f32_to_bf16(al * p);
+      }
+    }
+    const uint16_t* at = GRAD_K ? qt : gt;     // Q^T for dK, dO^T for dV
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      dvacc[dt] = mfma32(gtr[dt][0], pvb[0], dvacc[dt]);
-      dvacc[dt] = mfma32(gtr[dt][1], pvb[1], dvacc[dt]);
-      dkacc[dt] = mfma32(qtr[dt][0], dsb[0], dkacc[dt]);
-      dkacc[dt] = mfma32(qtr[dt][1], dsb[1], dkacc[dt]);
+      acc[dt] = mfma32(tr_operand(at, to1[dt], to2[dt]), pb[0], acc[dt]);
+      acc[dt] = mfma32(tr_operand(at + 16 * D, to1[dt], to2[dt]), pb[1], acc[dt]);
     }
   };
   for (int it = 0; it < cnt; it += 2) {
@@ -751,41 +765,38 @@ bwd_dkdv_kernel(BwdArgs A) {
   __syncthreads();
 
   // merge the two query halves: the wave keeps dims [32*own0, +32*DTH) and
-  // hands the rest to the wave of the same key half
-  float* obuf = reinterpret_cast<float*>(smem);   // [4][2][DTH][16][64]
+  // hands the rest to the wave of the same key half (partner = wave ^ 1;
+  // waves 0-1 exchange through q0, waves 2-3 through q1)
+  auto wbuf = [&](int w) -> float* {
+    return reinterpret_cast<float*>(w < 2 ? q0 : q1) + (w & 1) * DTH * 16 * 64;
+  };
   const int own0 = qh * DTH;
-  f32x16 okk[DTH], ovv[DTH];
+  f32x16 own[DTH];
+  float* obuf_out = wbuf(wave);
 #pragma unroll
   for (int u = 0; u < DTH; ++u) {
-    okk[u] = qh ? dkacc[DTH + u] : dkacc[u];
-    ovv[u] = qh ? dvacc[DTH + u] : dvacc[u];
-    const f32x16 ok = qh ? dkacc[u] : dkacc[DTH + u];
-    const f32x16 ov = qh ? dvacc[u] : dvacc[DTH + u];
+    own[u] = qh ? acc[DTH + u] : acc[u];
+    const f32x16 oth = qh ? acc[u] : acc[DTH + u];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      obuf[(((wave * 2 + 0) * DTH + u) * 16 + r) * 64 + lane] = ok[r];
-      obuf[(((wave * 2 + 1) * DTH + u) * 16 + r) * 64 + lane] = ov[r];
-    }
+    for (int r = 0; r < 16; ++r) obuf_out[(u * 16 + r) * 64 + lane] = oth[r];
   }
   __syncthreads();
-  const int partner = wave ^ 1;
-  const float rs = cl * (1.0f / kLog2e);
+  const float* obuf_in = wbuf(wave ^ 1);
+  const float scale = GRAD_K ? cl * (1.0f / kLog2e) : 1.0f;   // dK carries 1 / sqrt(d)
+  float* out = GRAD_K ? A.dk : A.dv;
   if (key < nj) {
     const int64_t ro = (static_cast<int64_t>(bh) * g.N + kBlock * j + key) * D;
 #pragma unroll
     for (int u = 0; u < DTH; ++u)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        f32x4 wk, wv;
+        f32x4 w;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int r = 4 * r4 + x;
-          wk[x] = (okk[u][r] + obuf[(((partner * 2 + 0) * DTH + u) * 16 + r) * 64 + lane]) * rs;
-          wv[x] = ovv[u][r] + obuf[(((partner * 2 + 1) * DTH + u) * 16 + r) * 64 + lane];
+          w[x] = (own[u][r] + obuf_in[(u * 16 + r) * 64 + lane]) * scale;
         }
-        const int a0 = 32 * (own0 + u) + 8 * r4 + 4 * hh;
-        *reinterpret_cast<f32x4*>(A.dk + ro + a0) = wk;
-        *reinterpret_cast<f32x4*>(A.dv + ro + a0) = wv;
+        *reinterpret_cast<f32x4*>(out + ro + 32 * (own0 + u) + 8 * r4 + 4 * hh) = w;
       }
   }
 }
@@ -808,6 +819,8 @@ bwd_lin_kv_kernel(BwdArgs A, int nchunks, int rows_pad) {
   __shared__ float dz[D];
   __shared__ float kstat[2][kBlock];                                  // row max, 1 / normaliser
   __shared__ float red[4][32];
+  __shared__ uint16_t mlist[4096];
+  __shared__ int mcount[129];
 
   const Geometry& g = A.g;
   const int t = threadIdx.x, lane = t & 63;
@@ -833,20 +846,44 @@ bwd_lin_kv_kernel(BwdArgs A, int nchunks, int rows_pad) {
                         static_cast<uint32_t>(r * D * 2 + 16 * (lslot ^ swz<D>(r))), 0u);
     }
   }
-  // dz_j = sum of dsigma_i over the query blocks holding j marginal
-  if (t < D) {
-    float acc = 0.0f;
+  // dz_j = sum of dsigma_i over the query blocks holding j marginal: their
+  // list first (bit words of j's row gathered into registers of a wave),
+  // then the dsigma rows summed with independent loads
+  {
     const uint32_t* br = A.marg_t + static_cast<int64_t>(bh) * nchunks * rows_pad * 2;
-    for (int ch = 0; ch < nchunks; ++ch)
-      for (int w = 0; w < 2; ++w) {
-        uint32_t word = br[(static_cast<int64_t>(ch) * rows_pad + j) * 2 + w];
-        while (word) {
-          const int qi = 64 * ch + 32 * w + __builtin_ctz(word);
-          acc += A.dsig[(static_cast<int64_t>(bh) * g.nq + qi) * D + t];
-          word &= word - 1;
-        }
+    uint32_t myword = 0;
+    if (t < 2 * nchunks) {
+      myword = br[(static_cast<int64_t>(t >> 1) * rows_pad + j) * 2 + (t & 1)];
+      mcount[t + 1] = __builtin_popcount(myword);
+    }
+    if (t == 0) mcount[0] = 0;
+    __syncthreads();
+    if (t == 0)
+      for (int w = 1; w <= 2 * nchunks; ++w) mcount[w] += mcount[w - 1];
+    __syncthreads();
+    if (t < 2 * nchunks) {
+      int pos = mcount[t];
+      uint32_t word = myword;
+      while (word) {
+        mlist[pos++] = static_cast<uint16_t>(32 * t + __builtin_ctz(word));
+        word &= word - 1;
       }
-    dz[t] = acc;
+    }
+    __syncthreads();
+    const int mc = mcount[2 * nchunks];
+    if (t < D) {
+      const float* ds0 = A.dsig + static_cast<int64_t>(bh) * g.nq * D + t;
+      float acc = 0.0f;
+      for (int u0 = 0; u0 < mc; u0 += 8) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = ds0[static_cast<int64_t>(mlist[min(u0 + e, mc - 1)]) * D];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (u0 + e < mc) acc += x[e];
+      }
+      dz[t] = acc;
+    }
   }
   // phi(K_j) and V_j as bf16 tiles: 4 threads per token (row = t/4)
   {
@@ -1011,7 +1048,8 @@ hipError_t launch_backward_t(const BwdArgs& a, hipStream_t stream) {
     e = launch_mask_gemm(g, a.marg_t, a.ds, const_cast<uint16_t*>(a.dh), stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(bh * g.nkb), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((bwd_kv_kernel<D, false>), dim3(bh * g.nkb), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((bwd_kv_kernel<D, true>), dim3(bh * g.nkb), dim3(kThreads), 0, stream, a);
   if (g.k_marg > 0)
     hipLaunchKernelGGL((bwd_lin_kv_kernel<D>), dim3(g.nkb, bh), dim3(kThreads), 0, stream, a,
                        nchunks, rows_pad);
