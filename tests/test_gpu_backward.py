@@ -128,3 +128,12 @@ def test_dalpha_is_the_sum_over_the_forward_branches():
     got = da.double().cpu().numpy()
     _say(f"[dalpha sum] got {got} ref {ref}")
     np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-3)
+
+
+@pytest.mark.timeout(900)
+def test_backward_parity_max_rows():
+    # 4096 KV blocks: 128 bit words per transposed row, lists up to 4096 long
+    # (checked on sampled rows of one head against the oracle's full head)
+    w = make_custom(1, 1, 64 * 4096 - 5, 64, dtype="bf16", kind="fourier1d", seed=99, k_crit=3,
+                    k_marg=5)
+    _bwd_check(w)

@@ -146,3 +146,17 @@ def test_forward_pisa_beats_dropping_the_unselected_blocks():
     e_sparse = rel_l2(sparse[rows], dense[rows])
     _say(f"[pisa vs dense seq8k head 0] rel L2: piecewise {e_pisa:.3e}, exact-only {e_sparse:.3e}")
     assert e_pisa < e_sparse
+
+
+@pytest.mark.timeout(900)
+def test_forward_pisa_parity_max_rows():
+    # 4096 KV blocks: 64 pseudo-blocks of centroids, a full exclusion bitmask
+    w = make_custom(1, 1, 64 * 4096 - 5, 64, dtype="bf16", kind="fourier1d", seed=100, k_crit=3,
+                    k_marg=0)
+    _pisa_check(w, 3, n_sample=12)
+
+
+@pytest.mark.timeout(900)
+def test_forward_pisa_parity_video75k():
+    w = make_workload("video75k", cache=False)
+    _pisa_check(w, w.k_crit, heads=[(0, 0)], n_sample=8)

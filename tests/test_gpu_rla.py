@@ -129,3 +129,9 @@ def test_forward_rla_phases_equal_fused_call():
     o2 = s.forward_attend_rla(q, k, v, r["crit_idx"], w.alpha, ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.timeout(900)
+def test_forward_rla_parity_video75k():
+    w = make_workload("video75k", cache=False)
+    _rla_check(w, w.k_crit, heads=[(0, 7)], n_sample=8)

@@ -115,3 +115,8 @@ def test_taylor_route_changes_the_split_on_the_workload():
     diff = rows.float().mean().item()
     _say(f"[taylor vs mean seq8k] rows with a different split: {diff:.3f}")
     assert diff > 0.0
+
+
+@pytest.mark.timeout(900)
+def test_taylor_route_parity_video75k():
+    _taylor_check(make_workload("video75k", cache=False), heads=[(0, 0), (0, 21), (0, 39)])
