@@ -205,9 +205,10 @@ PisaWs carve_pisa_ws(const sla::Geometry& g, void* ws) {
 }
 
 // Backward workspace: [forward workspace][O scratch, problem layout]
-// [O_s f32][O_l f32][lse f32 B*H*N][D_t f32 B*H*N][dS bf16 B*H*nq*d*d]
-// [dsigma f32 B*H*nq*d][dH bf16 B*H*nkb*d*d][critical bits^T]
-// [marginal bits^T][dalpha partials f32 B*H*nq], each region 256-byte aligned
+// [O_s f32][O_l f32][lse f32 B*H*N][D_t f32 B*H*N]
+// [dS|dsigma bf16 B*H*nq*(d*d + d)][dH|dz bf16 B*H*nkb*(d*d + d)]
+// [critical bits^T][marginal bits^T][dalpha partials f32 B*H*nq], each
+// region 256-byte aligned
 struct BwdWs {
   FwdWs fwd;
   void* o;
@@ -224,8 +225,8 @@ size_t backward_ws(const sla::Geometry& g) {
   const size_t blk = bh * g.nq;
   const size_t nmt = bh * sla::marginal_chunks(g) * sla::marginal_rows_pad(g) * 2;
   return forward_ws(g) + align_up(span_elems(g) * 2) + 2 * align_up(rows * g.D * 4) +
-         2 * align_up(rows * 4) + align_up(blk * g.D * g.D * 2) + align_up(blk * g.D * 4) +
-         align_up(bh * g.nkb * g.D * g.D * 2) +
+         2 * align_up(rows * 4) + align_up(blk * (g.D * g.D + g.D) * 2) +
+         align_up(bh * g.nkb * (g.D * g.D + g.D) * 2) +
          align_up(bh * g.nkb * sla::backward_crit_words(g) * 4) + align_up(nmt * 4) +
          align_up(blk * 4);
 }
@@ -249,18 +250,16 @@ BwdWs carve_backward_ws(const sla::Geometry& g, void* ws) {
   float* dd = reinterpret_cast<float*>(p);
   p += align_up(rows * 4);
   uint16_t* ds = reinterpret_cast<uint16_t*>(p);
-  p += align_up(blk * g.D * g.D * 2);
-  float* dsig = reinterpret_cast<float*>(p);
-  p += align_up(blk * g.D * 4);
+  p += align_up(blk * (g.D * g.D + g.D) * 2);
   uint16_t* dh = reinterpret_cast<uint16_t*>(p);
-  p += align_up(bh * g.nkb * g.D * g.D * 2);
+  p += align_up(bh * g.nkb * (g.D * g.D + g.D) * 2);
   uint32_t* crit_t = reinterpret_cast<uint32_t*>(p);
   p += align_up(bh * g.nkb * sla::backward_crit_words(g) * 4);
   uint32_t* marg_t = reinterpret_cast<uint32_t*>(p);
   p += align_up(nmt * 4);
   float* dap = reinterpret_cast<float*>(p);
-  w.b = sla::BackwardBuffers{o_s, o_l, lse, dd, w.fwd.s_sum, w.fwd.sigma, ds, dsig, dh, crit_t,
-                             marg_t, dap};
+  w.b = sla::BackwardBuffers{o_s, o_l, lse, dd, w.fwd.s_sum, w.fwd.sigma, ds, dh, crit_t, marg_t,
+                             dap};
   return w;
 }
 

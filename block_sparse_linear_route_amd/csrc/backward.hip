@@ -29,10 +29,12 @@
 //                       and dQ^T += K^T dS^T on the matrix cores (K^T by
 //                       transposing LDS reads, dS^T fed from registers);
 //   bwd_lin_q_kernel    the linear branch on the query side: dq (added),
-//                       dS_i (bf16, value-major like H) and dsigma_i;
+//                       dS_i (bf16, value-major like H) with dsigma_i after
+//                       it in the same row;
 //   bwd_bits_kernel     the transposed critical relation as bit rows per KV
 //                       block, and the transposed marginal relation in the
-//                       mask-product layout (then dH = M^T dS by that product);
+//                       mask-product layout (then dH = M^T dS by that product,
+//                       dz riding along as d more columns of each row);
 //   bwd_kv_kernel       KV-major (one instance for dV, one for dK): for KV
 //                       block j, the query blocks holding j critical (from
 //                       its bit row) stream Q and dO tiles through an LDS
@@ -63,9 +65,8 @@ struct BwdArgs {
   float* dd;               // float [BH][N], D_t
   const uint16_t* s_sum;   // bf16 [BH][nq][D][D] value-major (forward workspace)
   const float* sigma;      // float [BH][nq][D]
-  uint16_t* ds;            // bf16 [BH][nq][D][D] value-major
-  float* dsig;             // float [BH][nq][D]
-  const uint16_t* dh;      // bf16 [BH][nkb][D][D] value-major
+  uint16_t* ds;            // bf16 [BH][nq][D*D + D]: dS_i value-major, then dsigma_i
+  const uint16_t* dh;      // bf16 [BH][nkb][D*D + D]: dH_j value-major, then dz_j
   uint32_t* crit_t;        // [BH][nkb][crit_words]
   int crit_words;
   uint32_t* marg_t;        // mask-product bit layout, rows = KV blocks
@@ -413,6 +414,34 @@ bwd_lin_q_kernel(BwdArgs A) {
       zp += qv[s][e];
     }
   const float zinv = 1.0f / (zp + xor_lane(zp, 32));
+  // dO (kept packed, in the k-slot order of the transposing reads: c = 16 s
+  // + {4 hh + e, 8 + 4 hh + e}) and dO . O_l, before the barrier so that
+  // these loads overlap the S_i^T and sigma_i transfers
+  u32x2 graw[NS][2];
+  float gdot = 0.0f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int c0 = 16 * s + 4 * hh;
+    graw[s][0] = *reinterpret_cast<const u32x2*>(A.dout + rowg + c0);
+    graw[s][1] = *reinterpret_cast<const u32x2*>(A.dout + rowg + c0 + 8);
+    const f32x4 l0 = *reinterpret_cast<const f32x4*>(A.o_l + rowt * D + c0);
+    const f32x4 l1 = *reinterpret_cast<const f32x4*>(A.o_l + rowt * D + c0 + 8);
+    float g0[4], g1[4];
+    load4_f32(reinterpret_cast<const uint16_t*>(&graw[s][0]), g0);
+    load4_f32(reinterpret_cast<const uint16_t*>(&graw[s][1]), g1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gdot = fmaf(g0[e], l0[e], gdot);
+      gdot = fmaf(g1[e], l1[e], gdot);
+    }
+  }
+  // q at the df positions (a = 32 at + 8 r4 + 4 hh + x), packed
+  u32x2 qraw[DTH][4];
+#pragma unroll
+  for (int u = 0; u < DTH; ++u)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      qraw[u][r4] = *reinterpret_cast<const u32x2*>(A.q + rowg + 32 * (ah * DTH + u) + 8 * r4 + 4 * hh);
   wait_vmem();
   __syncthreads();
   float dpart = 0.0f;
@@ -422,23 +451,16 @@ bwd_lin_q_kernel(BwdArgs A) {
     for (int e = 0; e < 8; ++e) dpart = fmaf(qv[s][e], sig[16 * s + 8 * hh + e], dpart);
   const float den = (dpart + xor_lane(dpart, 32)) * zinv;
 
-  // dO_l / den as the B operand of df^T, in the k-slot order of the
-  // transposing reads (c = 16 s + {4 hh + e, 8 + 4 hh + e})
+  // dO_l / den as the B operand of df^T
   const float cdo = (1.0f - al) / den;
   bf16x8 dn[NS];
-  float gdot = 0.0f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const int c0 = 16 * s + 4 * hh;
     float g0[4], g1[4];
-    load4_f32(A.dout + rowg + c0, g0);
-    load4_f32(A.dout + rowg + c0 + 8, g1);
-    const f32x4 l0 = *reinterpret_cast<const f32x4*>(A.o_l + rowt * D + c0);
-    const f32x4 l1 = *reinterpret_cast<const f32x4*>(A.o_l + rowt * D + c0 + 8);
+    load4_f32(reinterpret_cast<const uint16_t*>(&graw[s][0]), g0);
+    load4_f32(reinterpret_cast<const uint16_t*>(&graw[s][1]), g1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      gdot = fmaf(g0[e], l0[e], gdot);
-      gdot = fmaf(g1[e], l1[e], gdot);
       dn[s][e] = f32_to_bf16(vrow ? g0[e] * cdo : 0.0f);
       dn[s][4 + e] = f32_to_bf16(vrow ? g1[e] * cdo : 0.0f);
     }
@@ -465,7 +487,7 @@ bwd_lin_q_kernel(BwdArgs A) {
     for (int r4 = 0; r4 < 4; ++r4) {
       const int a0 = 32 * (ah * DTH + u) + 8 * r4 + 4 * hh;
       float qa[4];
-      load4_f32(A.q + rowg + a0, qa);
+      load4_f32(reinterpret_cast<const uint16_t*>(&qraw[u][r4]), qa);
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int r = 4 * r4 + x;
@@ -516,7 +538,7 @@ bwd_lin_q_kernel(BwdArgs A) {
   }
 
   // dS_i^T[c][a] = sum_t dnum[t][c] f[t][a]: tiles (ct, at), k = the 64 rows
-  uint16_t* dso = A.ds + irow * D * D;
+  uint16_t* dso = A.ds + irow * (D * D + D);
 #pragma unroll
   for (int u = 0; u < NTW; ++u) {
     const int ti = wave * NTW + u;
@@ -535,11 +557,12 @@ bwd_lin_q_kernel(BwdArgs A) {
       dso[c * D + 32 * at + l32] = f32_to_bf16_bits(acc[r]);
     }
   }
-  // dsigma_i[a] = sum_t f[t][a] dden_t
+  // dsigma_i[a] = sum_t f[t][a] dden_t, after dS_i in the same row (the
+  // mask product then sums both)
   if (t < D) {
     float acc = 0.0f;
     for (int r = 0; r < kBlock; ++r) acc = fmaf(bf16_to_f32(ftile[tile_off<D>(r, t)]), dden_s[r], acc);
-    A.dsig[irow * D + t] = acc;
+    dso[D * D + t] = f32_to_bf16_bits(acc);
   }
 }
 
@@ -819,8 +842,6 @@ bwd_lin_kv_kernel(BwdArgs A, int nchunks, int rows_pad) {
   __shared__ float dz[D];
   __shared__ float kstat[2][kBlock];                                  // row max, 1 / normaliser
   __shared__ float red[4][32];
-  __shared__ uint16_t mlist[4096];
-  __shared__ int mcount[129];
 
   const Geometry& g = A.g;
   const int t = threadIdx.x, lane = t & 63;
@@ -836,7 +857,7 @@ bwd_lin_kv_kernel(BwdArgs A, int nchunks, int rows_pad) {
   // dH_j^T into LDS
   {
     const __amdgpu_buffer_rsrc_t hrs =
-        make_rsrc(A.dh + (static_cast<int64_t>(bh) * g.nkb + j) * D * D, D * D * 2);
+        make_rsrc(A.dh + (static_cast<int64_t>(bh) * g.nkb + j) * (D * D + D), D * D * 2);
     const int lrow = lane / CH, lslot = lane % CH;
     constexpr int RPW = D / 4;
 #pragma unroll
@@ -846,45 +867,7 @@ bwd_lin_kv_kernel(BwdArgs A, int nchunks, int rows_pad) {
                         static_cast<uint32_t>(r * D * 2 + 16 * (lslot ^ swz<D>(r))), 0u);
     }
   }
-  // dz_j = sum of dsigma_i over the query blocks holding j marginal: their
-  // list first (bit words of j's row gathered into registers of a wave),
-  // then the dsigma rows summed with independent loads
-  {
-    const uint32_t* br = A.marg_t + static_cast<int64_t>(bh) * nchunks * rows_pad * 2;
-    uint32_t myword = 0;
-    if (t < 2 * nchunks) {
-      myword = br[(static_cast<int64_t>(t >> 1) * rows_pad + j) * 2 + (t & 1)];
-      mcount[t + 1] = __builtin_popcount(myword);
-    }
-    if (t == 0) mcount[0] = 0;
-    __syncthreads();
-    if (t == 0)
-      for (int w = 1; w <= 2 * nchunks; ++w) mcount[w] += mcount[w - 1];
-    __syncthreads();
-    if (t < 2 * nchunks) {
-      int pos = mcount[t];
-      uint32_t word = myword;
-      while (word) {
-        mlist[pos++] = static_cast<uint16_t>(32 * t + __builtin_ctz(word));
-        word &= word - 1;
-      }
-    }
-    __syncthreads();
-    const int mc = mcount[2 * nchunks];
-    if (t < D) {
-      const float* ds0 = A.dsig + static_cast<int64_t>(bh) * g.nq * D + t;
-      float acc = 0.0f;
-      for (int u0 = 0; u0 < mc; u0 += 8) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = ds0[static_cast<int64_t>(mlist[min(u0 + e, mc - 1)]) * D];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (u0 + e < mc) acc += x[e];
-      }
-      dz[t] = acc;
-    }
-  }
+  if (t < D) dz[t] = bf16_to_f32(A.dh[(static_cast<int64_t>(bh) * g.nkb + j) * (D * D + D) + D * D + t]);
   // phi(K_j) and V_j as bf16 tiles: 4 threads per token (row = t/4)
   {
     const int row = t >> 2, prt = t & 3;
@@ -1045,7 +1028,7 @@ hipError_t launch_backward_t(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (g.k_marg > 0) {
-    e = launch_mask_gemm(g, a.marg_t, a.ds, const_cast<uint16_t*>(a.dh), stream);
+    e = launch_mask_gemm(g, a.marg_t, a.ds, const_cast<uint16_t*>(a.dh), stream, true);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((bwd_kv_kernel<D, false>), dim3(bh * g.nkb), dim3(kThreads), 0, stream, a);
@@ -1065,7 +1048,7 @@ hipError_t launch_backward(const Geometry& g, const BackwardBuffers& w, const vo
                            float* dv, float* dalpha, hipStream_t stream) {
   BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
             static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), crit, marg, alpha,
-            w.o_s, w.o_l, w.lse, w.dd, w.s_sum, w.sigma, w.ds, w.dsig, w.dh, w.crit_t,
+            w.o_s, w.o_l, w.lse, w.dd, w.s_sum, w.sigma, w.ds, w.dh, w.crit_t,
             backward_crit_words(g), w.marg_t, dq, dk, dv, w.dalpha_part, dalpha, g,
             static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(g.D)))};
   if (g.D == 128) return launch_backward_t<128>(a, stream);

@@ -109,11 +109,13 @@ __device__ __forceinline__ int hslot(int r, int c16) { return c16 ^ (4 * ((r >> 
 // grid (row tiles, D*D / 64, B*H).  S^T tile: columns e in [64 ct, 64 ct +
 // 64) of the value-major states, rows i0 .. i0 + GM - 1 with GM = 128 NT
 // (NT 32-row tiles per wave) and i0 = row0 + GM blockIdx.x.
-template <int D, int NT>
+// RS: elements per row of hs and s_out (d*d, or d*d + d when each row also
+// carries a d-vector summed the same way).
+template <int D, int NT, int RS = D * D>
 __global__ void __launch_bounds__(kThreads, 2)
 marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int rows_pad,
                  int row0, const uint16_t* __restrict__ hs, uint16_t* __restrict__ s_out) {
-  constexpr int DD = D * D;
+  constexpr int DD = RS;
   constexpr int kNT = NT;
   constexpr int kGM = 128 * NT;
   constexpr int kBBytes = kGM * 8;          // bit-row chunk bytes
@@ -360,7 +362,7 @@ hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const ui
 }
 
 hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint16_t* h_states,
-                            uint16_t* s_sum, hipStream_t stream) {
+                            uint16_t* s_sum, hipStream_t stream, bool with_vector) {
   const int nchunks = marginal_chunks(g);
   const int rows_pad = marginal_rows_pad(g);
   // 512-row tiles, and a 256-row tile for a remainder of at most 256 rows
@@ -369,9 +371,15 @@ hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint1
   const int n512 = rem > 256 ? full + 1 : full;
   auto gemm = [&](auto dc, auto ntc, int tiles, int row0) {
     constexpr int DK = decltype(dc)::value, NTK = decltype(ntc)::value;
-    dim3 g2(tiles, DK * DK / kGN, g.B * g.H);
-    hipLaunchKernelGGL((marg_gemm_kernel<DK, NTK>), g2, dim3(kThreads), 0, stream, g, bits,
-                       nchunks, rows_pad, row0, h_states, s_sum);
+    if (with_vector) {
+      dim3 g2(tiles, (DK * DK + DK) / kGN, g.B * g.H);
+      hipLaunchKernelGGL((marg_gemm_kernel<DK, NTK, DK * DK + DK>), g2, dim3(kThreads), 0, stream,
+                         g, bits, nchunks, rows_pad, row0, h_states, s_sum);
+    } else {
+      dim3 g2(tiles, DK * DK / kGN, g.B * g.H);
+      hipLaunchKernelGGL((marg_gemm_kernel<DK, NTK>), g2, dim3(kThreads), 0, stream, g, bits,
+                         nchunks, rows_pad, row0, h_states, s_sum);
+    }
   };
   if (g.D == 128) {
     if (n512 > 0) gemm(std::integral_constant<int, 128>(), std::integral_constant<int, 4>(), n512, 0);

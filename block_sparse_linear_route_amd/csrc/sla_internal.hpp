@@ -44,8 +44,10 @@ hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const ui
 // The product S = M H alone, from mask bits already in the layout the
 // marginal sums write (chunk-major, rows padded to the 512-row tile); with
 // nq = nkb the roles of query and KV blocks can be swapped (a transposed mask).
+// with_vector: rows of d*d + d elements (a d-vector after each matrix, summed
+// the same way).
 hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint16_t* h_states,
-                            uint16_t* s_sum, hipStream_t stream);
+                            uint16_t* s_sum, hipStream_t stream, bool with_vector = false);
 
 // rla: residual linear attention epilogue (s_sum holds every non-critical
 // block's exponential-map state; RMS norm in place of the sigma denominator).
@@ -87,7 +89,8 @@ hipError_t launch_attention_pisa(const Geometry& g, const void* q, const void* k
 // Backward pass.  Buffers (all in the backward workspace): the forward's
 // float O_s, O_l [B*H][N][d] and log2 softmax normaliser [B*H][N]; the
 // forward workspace's marginal sums (s_sum, sigma); D_t [B*H][N]; dS_i bf16
-// [B*H][nq][d][d] and dsigma_i [B*H][nq][d]; dH bf16 [B*H][nkb][d][d]; the
+// [B*H][nq][d*d + d] (the d x d matrix value-major, then dsigma_i); dH bf16
+// [B*H][nkb][d*d + d] (likewise, dz_j after the matrix); the
 // transposed critical bit rows [B*H][nkb][backward_crit_words] and the
 // transposed marginal mask in the mask-product layout; dalpha partials
 // [B*H][nq].  Inputs bf16 only.
@@ -99,7 +102,6 @@ struct BackwardBuffers {
   const uint16_t* s_sum;
   const float* sigma;
   uint16_t* ds;
-  float* dsig;
   uint16_t* dh;
   uint32_t* crit_t;
   uint32_t* marg_t;
