@@ -215,6 +215,9 @@ attention_fp8_kernel(AttnFp8Args A) {
   }
 
   float m_run = -INFINITY, l_run = 0.0f;       // log2 units
+  i32x8 ones8;                                   // e4m3 1.0 in every byte
+#pragma unroll
+  for (int w = 0; w < 8; ++w) ones8[w] = 0x38383838;
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = zero16();
@@ -282,7 +285,6 @@ attention_fp8_kernel(AttnFp8Args A) {
       // 2^kq * s_v * max_j P_true lies in (224, 448]
       const float kq = fminf(fmaxf(floorf(kLog2Max - (mx - m_run) - lv), -126.0f), 126.0f);
       const float bias = lv + kq - m_run;
-      float ps = 0.0f;
       i32x8 pk;
 #pragma unroll
       for (int w = 0; w < 8; ++w) pk[w] = 0;
@@ -294,14 +296,19 @@ attention_fp8_kernel(AttnFp8Args A) {
 #pragma unroll
           for (int x4 = 0; x4 < 4; ++x4) {
             e[x4] = __builtin_amdgcn_exp2f(fmaf(s_cur[tt][r + x4], fb, bias));
-            ps += e[x4];
           }
           const int w = 4 * tt + (r >> 2);
           pk[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], pk[w], false);
           pk[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], pk[w], true);
         }
-      l_run += ps * __builtin_ldexpf(iv, -static_cast<int>(kq));
       const int scale_b = 127 - static_cast<int>(kq);
+      // Row sums of the quantized weights on the matrix core: a ones operand
+      // times P^T puts sum_k e_k 2^-kq (this block's 64 keys) in every row
+      // of the lane's query column, so both lanes of a query hold the whole
+      // sum and each adds half (the epilogue adds the partner lane's l).
+      // The normaliser then sums exactly the weights P V uses.
+      const f32x16 lsum = mfma_fp8(ones8, pk, zero16(), scale_b);
+      l_run = fmaf(lsum[0], 0.5f * iv, l_run);
 
       const uint32_t vt_addr = lds_addr(hbase + 2 * TB + cur * TB);
 #pragma unroll
