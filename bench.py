@@ -359,6 +359,25 @@ def main():
             evb[i_ + 1].record()
         torch.cuda.synchronize()
         bwd_ms = float(np.mean([evb[i_].elapsed_time(evb[i_ + 1]) for i_ in range(n_b)]))
+        # the same gradients for a training step that runs the forward once:
+        # sla_forward_save (the forward, keeping what the backward reads) and
+        # sla_backward_saved (the gradient kernels only)
+        o_t, _ = sla_gpu.forward_save(q, k, v, r["crit_idx"], r["marg_idx"], Hb, zb, alpha,
+                                      workspace=ws_b)
+        sla_gpu.backward_saved(q, k, v, dout, r["crit_idx"], r["marg_idx"], alpha, ws_b)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_b)]
+        torch.cuda.synchronize()
+        for i_ in range(n_b):
+            evs[i_][0].record()
+            sla_gpu.forward_save(q, k, v, r["crit_idx"], r["marg_idx"], Hb, zb, alpha,
+                                 workspace=ws_b, out=o_t)
+            evs[i_][1].record()
+            sla_gpu.backward_saved(q, k, v, dout, r["crit_idx"], r["marg_idx"], alpha, ws_b)
+            evs[i_][2].record()
+        torch.cuda.synchronize()
+        fsave_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        bsaved_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        del o_t
         # executed FLOPs: the forward again, then per critical (query, key)
         # pair 6 d (dQ kernel: S, dP, dQ) + 8 d (dK/dV kernel: S, dP, dV, dK),
         # 4 d^2 per row on each side of the linear branch, and the marginal
@@ -368,6 +387,13 @@ def main():
             "ms": bwd_ms,
             "tflops": f_bwd / (bwd_ms * 1e-3) / 1e12,
             "executed_gflop": f_bwd / 1e9,
+            "forward_save_ms": fsave_ms,
+            "backward_saved_ms": bsaved_ms,
+            "backward_saved_tflops": (f_bwd - f_fwd) / (bsaved_ms * 1e-3) / 1e12,
+            "saved_note": "training step with the forward run once: sla_forward_save (marginal "
+                          "sums and the fused kernel writing O plus O_s, O_l and the normaliser "
+                          "into the backward workspace), then sla_backward_saved (gradient "
+                          "kernels only; executed FLOPs without the forward's)",
             "note": "sla_backward for fixed lists: marginal sums and the fused forward again "
                     "(writing O_s, O_l and the log2 softmax normaliser), then D_t, sparse dQ, "
                     "linear query side, transposed masks, dH by the mask product, sparse dK/dV, "

@@ -7,6 +7,7 @@ binding.  Importing it fails if the library has not been built.
 from .ops import (  # noqa: F401
     SlaError,
     backward,
+    backward_saved,
     backward_workspace,
     forward,
     forward_attend,
@@ -16,6 +17,7 @@ from .ops import (  # noqa: F401
     forward_fp8,
     forward_pisa,
     forward_rla,
+    forward_save,
     forward_workspace,
     linear_states,
     make_problem,

@@ -68,6 +68,10 @@ SIGNATURES = {
     "sla_forward_pisa": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sla_backward": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _sz, _vp]),
+    "sla_forward_save": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _sz, _vp]),
+    "sla_backward_saved": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          _vp, _vp, _sz, _vp]),
     "sla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sla_last_error_message": (ctypes.c_char_p, []),
     "sla_version": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int)] * 3),

@@ -644,25 +644,56 @@ int sla_forward_pisa(const sla_problem* problem, const void* q, const void* k, c
                                  ws_bytes, stream);
 }
 
-int sla_backward(const sla_problem* problem, const void* q, const void* k, const void* v,
-                 const void* dout, const int32_t* crit_idx, const int32_t* marg_idx,
-                 const void* h_states, const float* z_states, const float* alpha, float* dq,
-                 float* dk, float* dv, float* dalpha, void* ws, size_t ws_bytes, void* stream) {
+// The forward pass of sla_backward: marginal sums, then the fused kernel
+// writing O (to o), O_s, O_l and each row's log2 softmax normaliser into the
+// backward workspace.
+static int backward_forward_part(const sla::Geometry& g, const void* q, const void* k,
+                                 const void* v, const int32_t* crit_idx, const int32_t* marg_idx,
+                                 const void* h_states, const float* z_states, const float* alpha,
+                                 void* o, const BwdWs& w, hipStream_t st) {
+  if (g.k_marg > 0)
+    SLA_TRY(launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
+                                               z_states, w.fwd.s_sum, w.fwd.sigma, w.fwd.bits,
+                                               false, st),
+                     "backward marginal sums"));
+  return launched(sla::launch_attention(g, q, k, v, crit_idx, w.fwd.s_sum, w.fwd.sigma, alpha, o,
+                                        const_cast<float*>(w.b.o_s), const_cast<float*>(w.b.o_l),
+                                        false, st, const_cast<float*>(w.b.lse)),
+                  "backward forward pass");
+}
+
+// Argument checks shared by the backward entry points and sla_forward_save.
+static int check_backward_args(const sla_problem* problem, const void* q, const void* k,
+                               const void* v, const int32_t* crit_idx, const int32_t* marg_idx,
+                               const float* alpha) {
   SLA_TRY(validate_problem(problem));
   if (problem->dtype != SLA_BF16)
     return fail(SLA_ERR_UNSUPPORTED, "the backward pass takes bf16 inputs only");
   SLA_REQ(q, 16);
   SLA_REQ(k, 16);
   SLA_REQ(v, 16);
-  SLA_REQ(dout, 16);
   SLA_REQ(alpha, 4);
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  if (problem->k_marg > 0) SLA_REQ(marg_idx, 4);
+  return SLA_OK;
+}
+
+static int check_gradient_args(const void* dout, float* dq, float* dk, float* dv, float* dalpha) {
+  SLA_REQ(dout, 16);
   SLA_REQ(dq, 16);
   SLA_REQ(dk, 16);
   SLA_REQ(dv, 16);
   SLA_REQ(dalpha, 4);
-  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  return SLA_OK;
+}
+
+int sla_backward(const sla_problem* problem, const void* q, const void* k, const void* v,
+                 const void* dout, const int32_t* crit_idx, const int32_t* marg_idx,
+                 const void* h_states, const float* z_states, const float* alpha, float* dq,
+                 float* dk, float* dv, float* dalpha, void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(check_backward_args(problem, q, k, v, crit_idx, marg_idx, alpha));
+  SLA_TRY(check_gradient_args(dout, dq, dk, dv, dalpha));
   if (problem->k_marg > 0) {
-    SLA_REQ(marg_idx, 4);
     SLA_REQ(h_states, 16);
     SLA_REQ(z_states, 16);
   }
@@ -671,18 +702,43 @@ int sla_backward(const sla_problem* problem, const void* q, const void* k, const
   SLA_TRY(check_device());
   const BwdWs w = carve_backward_ws(g, ws);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (g.k_marg > 0)
-    SLA_TRY(launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
-                                               z_states, w.fwd.s_sum, w.fwd.sigma, w.fwd.bits,
-                                               false, st),
-                     "backward marginal sums"));
-  SLA_TRY(launched(sla::launch_attention(g, q, k, v, crit_idx, w.fwd.s_sum, w.fwd.sigma, alpha,
-                                         w.o, const_cast<float*>(w.b.o_s),
-                                         const_cast<float*>(w.b.o_l), false, st,
-                                         const_cast<float*>(w.b.lse)),
-                   "backward forward pass"));
+  SLA_TRY(backward_forward_part(g, q, k, v, crit_idx, marg_idx, h_states, z_states, alpha, w.o, w,
+                                st));
   return launched(sla::launch_backward(g, w.b, q, k, v, dout, crit_idx, marg_idx, alpha, dq, dk,
                                        dv, dalpha, st),
+                  "backward launch");
+}
+
+int sla_forward_save(const sla_problem* problem, const void* q, const void* k, const void* v,
+                     const int32_t* crit_idx, const int32_t* marg_idx, const void* h_states,
+                     const float* z_states, const float* alpha, void* o, void* ws,
+                     size_t ws_bytes, void* stream) {
+  SLA_TRY(check_backward_args(problem, q, k, v, crit_idx, marg_idx, alpha));
+  SLA_REQ(o, 16);
+  if (problem->k_marg > 0) {
+    SLA_REQ(h_states, 16);
+    SLA_REQ(z_states, 16);
+  }
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, backward_ws(g)));
+  SLA_TRY(check_device());
+  const BwdWs w = carve_backward_ws(g, ws);
+  return backward_forward_part(g, q, k, v, crit_idx, marg_idx, h_states, z_states, alpha, o, w,
+                               static_cast<hipStream_t>(stream));
+}
+
+int sla_backward_saved(const sla_problem* problem, const void* q, const void* k, const void* v,
+                       const void* dout, const int32_t* crit_idx, const int32_t* marg_idx,
+                       const float* alpha, float* dq, float* dk, float* dv, float* dalpha,
+                       void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(check_backward_args(problem, q, k, v, crit_idx, marg_idx, alpha));
+  SLA_TRY(check_gradient_args(dout, dq, dk, dv, dalpha));
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, backward_ws(g)));
+  SLA_TRY(check_device());
+  const BwdWs w = carve_backward_ws(g, ws);
+  return launched(sla::launch_backward(g, w.b, q, k, v, dout, crit_idx, marg_idx, alpha, dq, dk,
+                                       dv, dalpha, static_cast<hipStream_t>(stream)),
                   "backward launch");
 }
 

@@ -349,6 +349,44 @@ def backward(q, k, v, dout, crit_idx, marg_idx, h_states, z_states, alpha, *, wo
     return dq, dk, dv, da
 
 
+def forward_save(q, k, v, crit_idx, marg_idx, h_states, z_states, alpha, *, workspace=None,
+                 out=None, stream=None):
+    """``forward`` for a training step: returns (O, workspace), the workspace
+    (of ``backward_workspace`` size) holding what ``backward_saved`` reads
+    instead of recomputing the forward.  bf16 inputs only."""
+    k, v = _same_layout(q, k, v)
+    kc, km = int(crit_idx.shape[-1]), int(marg_idx.shape[-1])
+    p = make_problem(q, kc, km)
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    ws = workspace if workspace is not None else _workspace(p, _lib.OP_BACKWARD, q.device)
+    alpha = alpha.to(device=q.device, dtype=torch.float32).contiguous()
+    _check(lib.sla_forward_save(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(crit_idx.contiguous()), _ptr(marg_idx.contiguous()),
+                                _ptr(h_states), _ptr(z_states), _ptr(alpha), _ptr(out), _ptr(ws),
+                                ws.numel(), _stream(stream)))
+    return out, ws
+
+
+def backward_saved(q, k, v, dout, crit_idx, marg_idx, alpha, workspace, *, stream=None):
+    """``backward`` without its forward part: ``workspace`` is the one
+    ``forward_save`` filled for the same inputs, lists and alpha."""
+    k, v, dout = _same_layout(q, k, v, dout)
+    kc, km = int(crit_idx.shape[-1]), int(marg_idx.shape[-1])
+    p = make_problem(q, kc, km)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32)
+    dk = torch.empty(q.shape, **f32)
+    dv = torch.empty(q.shape, **f32)
+    da = torch.empty(q.shape[1], **f32)
+    alpha = alpha.to(device=q.device, dtype=torch.float32).contiguous()
+    _check(lib.sla_backward_saved(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                  _ptr(crit_idx.contiguous()), _ptr(marg_idx.contiguous()),
+                                  _ptr(alpha), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dq, dk, dv, da
+
+
 def quantize_fp8(x: torch.Tensor, stream=None):
     """Per-block E4M3 codes (uint8 [B,H,N,d]) and float32 scales [B,H,nb]."""
     p = make_problem(x, 0, 1)

@@ -68,7 +68,7 @@ extern "C" {
 #endif
 
 #define SLA_VERSION_MAJOR 0
-#define SLA_VERSION_MINOR 5
+#define SLA_VERSION_MINOR 6
 #define SLA_VERSION_PATCH 0
 
 /* Status codes. */
@@ -357,6 +357,29 @@ int sla_backward(const sla_problem* problem, const void* q, const void* k,
                  const int32_t* marg_idx, const void* h_states, const float* z_states,
                  const float* alpha, float* dq, float* dk, float* dv, float* dalpha,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* The backward pass split at its forward part, for a training step that
+ * runs the forward once.  [SLA abstract (forward and backward)]
+ * sla_forward_save is sla_forward (same arguments, bf16 only) that also
+ * keeps what the gradient kernels read: it writes O to o and, into ws (a
+ * workspace of sla_workspace_size(SLA_OP_BACKWARD) bytes), the marginal
+ * sums S_i and sigma_i, O_s and O_l (float) and each row's log2 softmax
+ * normaliser.  sla_backward_saved then runs only the gradient kernels of
+ * sla_backward, reading those from ws: the caller passes the ws that
+ * sla_forward_save filled for the same problem, inputs, lists and alpha,
+ * unmodified in between (nothing checks this; other contents give wrong
+ * gradients, never an out-of-range access).  Arguments mean what they mean
+ * for sla_backward; the states are not read again.  sla_backward is exactly
+ * sla_forward_save (O into ws) followed by sla_backward_saved on one stream,
+ * and both calls' results equal it bit for bit. */
+int sla_forward_save(const sla_problem* problem, const void* q, const void* k,
+                     const void* v, const int32_t* crit_idx, const int32_t* marg_idx,
+                     const void* h_states, const float* z_states, const float* alpha,
+                     void* o, void* ws, size_t ws_bytes, void* stream);
+int sla_backward_saved(const sla_problem* problem, const void* q, const void* k,
+                       const void* v, const void* dout, const int32_t* crit_idx,
+                       const int32_t* marg_idx, const float* alpha, float* dq, float* dk,
+                       float* dv, float* dalpha, void* ws, size_t ws_bytes, void* stream);
 
 /* Host: static text of a status code. */
 const char* sla_status_string(int status);

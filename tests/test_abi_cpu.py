@@ -95,7 +95,7 @@ def test_status_strings_and_version():
         assert lib.sla_status_string(s)
     a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     assert lib.sla_version(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 0
-    assert (a.value, b.value, c.value) == (0, 5, 0)
+    assert (a.value, b.value, c.value) == (0, 6, 0)
 
 
 def test_entry_points_reject_bad_arguments_before_any_device_call():
@@ -213,4 +213,29 @@ def test_backward_entry_point_rejects_bad_arguments_before_any_device_call():
     lib.sla_workspace_size(ctypes.byref(p), _lib.OP_FORWARD, ctypes.byref(f))
     assert n.value > f.value + 2 * 2 * 1000 * 128 * 4    # forward workspace + O_s + O_l at least
     st = lib.sla_backward(ctypes.byref(p), *([fake] * 14), f.value, None)
+    assert st == _lib.SLA_ERR_WORKSPACE
+
+
+def test_saved_backward_entry_points_reject_bad_arguments_before_any_device_call():
+    fake = ctypes.c_void_p(0x10000)
+    p = P()
+    n = ctypes.c_size_t()
+    assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_BACKWARD, ctypes.byref(n)) == 0
+    # sla_forward_save: q k v crit marg h z alpha o ws
+    st = lib.sla_forward_save(ctypes.byref(P(dtype=_lib.SLA_F32)), *([fake] * 10), n.value, None)
+    assert st == _lib.SLA_ERR_UNSUPPORTED             # float inputs
+    st = lib.sla_forward_save(ctypes.byref(p), *([fake] * 8), None, fake, n.value, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT        # output missing
+    st = lib.sla_forward_save(ctypes.byref(p), *([fake] * 5), None, *([fake] * 4), n.value, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT        # states missing (k_marg > 0)
+    st = lib.sla_forward_save(ctypes.byref(p), *([fake] * 10), n.value - 1, None)
+    assert st == _lib.SLA_ERR_WORKSPACE
+    # sla_backward_saved: q k v dout crit marg alpha dq dk dv dalpha ws
+    st = lib.sla_backward_saved(ctypes.byref(P(dtype=_lib.SLA_F32)), *([fake] * 12), n.value, None)
+    assert st == _lib.SLA_ERR_UNSUPPORTED
+    st = lib.sla_backward_saved(ctypes.byref(p), *([fake] * 3), None, *([fake] * 8), n.value, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT        # dO missing
+    st = lib.sla_backward_saved(ctypes.byref(p), *([fake] * 10), None, fake, n.value, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT        # dalpha missing
+    st = lib.sla_backward_saved(ctypes.byref(p), *([fake] * 12), n.value - 1, None)
     assert st == _lib.SLA_ERR_WORKSPACE

@@ -111,6 +111,31 @@ def test_backward_is_deterministic():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("kc,km", [(5, 9), (0, 7), (6, 0)])
+def test_saved_forward_and_backward_equal_the_one_call_backward(kc, km):
+    # sla_backward is sla_forward_save followed by sla_backward_saved: the
+    # split gives the same bits, O equals sla_forward's, and the saved
+    # workspace serves a second backward with another dO
+    s = _s()
+    w = make_custom(1, 2, 3000, 128, seed=101 + kc, k_crit=kc, k_marg=km)
+    q, k, v = w.q.to(DEV), w.k.to(DEV), w.v.to(DEV)
+    r = s.route(q, k, kc, km)
+    Hs, zs = s.linear_states(k, v)
+    o_ref = s.forward(q, k, v, r["crit_idx"], r["marg_idx"], Hs, zs, w.alpha)
+    o, ws = s.forward_save(q, k, v, r["crit_idx"], r["marg_idx"], Hs, zs, w.alpha)
+    torch.cuda.synchronize()
+    _say(f"[saved kc={kc} km={km}] max|O - forward O| {float((o.float() - o_ref.float()).abs().max()):.3e}")
+    assert torch.equal(o, o_ref)
+    for seed in (0, 1):
+        g = torch.Generator().manual_seed(seed)
+        do = torch.randn(w.q.shape, generator=g).bfloat16().to(DEV)
+        got = s.backward_saved(q, k, v, do, r["crit_idx"], r["marg_idx"], w.alpha, ws)
+        ref = s.backward(q, k, v, do, r["crit_idx"], r["marg_idx"], Hs, zs, w.alpha)
+        torch.cuda.synchronize()
+        for name, x, y in zip(("dq", "dk", "dv", "dalpha"), got, ref):
+            assert torch.equal(x, y), name
+
+
 def test_dalpha_is_the_sum_over_the_forward_branches():
     # dalpha_h = sum over batch, rows and dims of dO * (O_s - O_l), with the
     # branch outputs the forward itself writes: a float32 reduction of the
