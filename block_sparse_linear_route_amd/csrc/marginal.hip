@@ -106,15 +106,18 @@ marg_prep_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __re
 // transposing reads (rows base + 0..3, four slots) hit distinct banks.
 __device__ __forceinline__ int hslot(int r, int c16) { return c16 ^ (4 * ((r >> 1) & 1)); }
 
-// grid (row tiles, D*D / 64, B*H).  S^T tile: columns e in [64 ct, 64 ct +
-// 64) of the value-major states, rows i0 .. i0 + GM - 1 with GM = 128 NT
-// (NT 32-row tiles per wave) and i0 = row0 + GM blockIdx.x.
+// One-dimensional grid of row tiles x (RS / 64) column tiles x B*H, the
+// row tile fastest in the logical order and each XCD given a contiguous
+// range of it, so the row tiles of one column tile share an L2 (each reads
+// the same H slabs).  S^T tile: columns e in [64 ct, 64 ct + 64) of the
+// value-major states, rows i0 .. i0 + GM - 1 with GM = 128 NT (NT 32-row
+// tiles per wave) and i0 = row0 + GM * (row tile).
 // RS: elements per row of hs and s_out (d*d, or d*d + d when each row also
 // carries a d-vector summed the same way).
 template <int D, int NT, int RS = D * D>
 __global__ void __launch_bounds__(kThreads, 2)
 marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int rows_pad,
-                 int row0, const uint16_t* __restrict__ hs, uint16_t* __restrict__ s_out) {
+                 int row0, int tiles, const uint16_t* __restrict__ hs, uint16_t* __restrict__ s_out) {
   constexpr int DD = RS;
   constexpr int kNT = NT;
   constexpr int kGM = 128 * NT;
@@ -130,8 +133,12 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int bh = blockIdx.z, ct = blockIdx.y;
-  const int i0 = row0 + blockIdx.x * kGM;
+  constexpr int kCols = RS / kGN;
+  const int logical = xcd_remap(blockIdx.x, tiles * kCols * g.B * g.H);
+  const int rt = logical % tiles;
+  const int ct = (logical / tiles) % kCols;
+  const int bh = logical / (tiles * kCols);
+  const int i0 = row0 + rt * kGM;
 
   if (t < 16) {
     u32x2 e;
@@ -372,13 +379,13 @@ hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint1
   auto gemm = [&](auto dc, auto ntc, int tiles, int row0) {
     constexpr int DK = decltype(dc)::value, NTK = decltype(ntc)::value;
     if (with_vector) {
-      dim3 g2(tiles, (DK * DK + DK) / kGN, g.B * g.H);
+      dim3 g2(tiles * ((DK * DK + DK) / kGN) * g.B * g.H);
       hipLaunchKernelGGL((marg_gemm_kernel<DK, NTK, DK * DK + DK>), g2, dim3(kThreads), 0, stream,
-                         g, bits, nchunks, rows_pad, row0, h_states, s_sum);
+                         g, bits, nchunks, rows_pad, row0, tiles, h_states, s_sum);
     } else {
-      dim3 g2(tiles, DK * DK / kGN, g.B * g.H);
+      dim3 g2(tiles * (DK * DK / kGN) * g.B * g.H);
       hipLaunchKernelGGL((marg_gemm_kernel<DK, NTK>), g2, dim3(kThreads), 0, stream, g, bits,
-                         nchunks, rows_pad, row0, h_states, s_sum);
+                         nchunks, rows_pad, row0, tiles, h_states, s_sum);
     }
   };
   if (g.D == 128) {
