@@ -321,10 +321,16 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
   uint64_t* keys = reinterpret_cast<uint64_t*>(dyn);                 // [R][nkbp]
   uint32_t* hist = reinterpret_cast<uint32_t*>(keys + R * nkbp);      // [4][128]
 
-  const int bh = blockIdx.y;
-  const int i0 = blockIdx.x * R;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // One-dimensional grid of row groups x B*H, the row group fastest in the
+  // logical order and each XCD given a contiguous range of it: an XCD then
+  // works through its heads one at a time, and the head's pooled keys,
+  // which every row group reads in full, stay in its L2.
   const int nq = g.nq, nkb = g.nkb, D = g.D;
+  const int ngroups = (nq + R - 1) / R;
+  const int logical = xcd_remap(blockIdx.x, ngroups * g.B * g.H);
+  const int bh = logical / ngroups;
+  const int i0 = (logical % ngroups) * R;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 
   const double* qrow[R];
 #pragma unroll
@@ -434,7 +440,7 @@ hipError_t launch_select_rk(const Geometry& g, int nkbp, const double* qpool,
                                              static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  dim3 grid((g.nq + R - 1) / R, g.B * g.H);
+  dim3 grid(((g.nq + R - 1) / R) * g.B * g.H);
   const double sqrt_d = __builtin_sqrt(static_cast<double>(g.D));
   const double inv_2d = 1.0 / (2.0 * g.D);
   hipLaunchKernelGGL((select_kernel<R, KPL, TAYLOR>), grid, dim3(kThreads), lds, stream, g, nkbp,
