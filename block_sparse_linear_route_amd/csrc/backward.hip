@@ -116,49 +116,52 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int o1, int o
 }
 
 // ------------------------------------------------------------ row dots
-// grid (nq, B*H): thread (row = t/4, part = t%4) covers D/4 dims of a row.
+// grid (nq, B*H).  The block's float O_s and O_l rows are read as contiguous
+// 1 KB pieces: in pass k thread t takes the 4 values 4 (256 k + t) .. +3 of
+// the block, so a row spans D / 4 consecutive lanes and its sums reduce
+// across them (rows past the last token are clamped and not written).
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 bwd_rowdot_kernel(BwdArgs A) {
-  constexpr int CW = D / 4;
+  constexpr int LPR = D / 4;                               // lanes per row
+  constexpr int PASSES = kBlock * D / (4 * kThreads);      // rows per thread
   __shared__ float red[4];
   const Geometry& g = A.g;
   const int i = blockIdx.x, bh = blockIdx.y;
   const int b = bh / g.H, h = bh % g.H;
-  const int t = threadIdx.x, row = t >> 2, prt = t & 3;
-  const int n = kBlock * i + row;
-  const bool valid = n < g.N;
-  const int nn = valid ? n : g.N - 1;
-  const uint16_t* gp = A.dout + b * g.sb + h * g.sh + static_cast<int64_t>(nn) * g.sn + prt * CW;
-  const int64_t ob = (static_cast<int64_t>(bh) * g.N + nn) * D + prt * CW;
-  float ds = 0.0f, da = 0.0f;
+  const int t = threadIdx.x, lane = t & 63;
+  const int col = (4 * t) % D;
+  const uint16_t* gbase = A.dout + b * g.sb + h * g.sh + col;
+  f32x4 sv[PASSES], lv[PASSES];
+  float gv[PASSES][4];
+  int nrow[PASSES];
 #pragma unroll
-  for (int c = 0; c < CW; c += 8) {
-    float gv[8];
-    load8_f32(gp + c, gv);
-    const f32x4 s0 = *reinterpret_cast<const f32x4*>(A.o_s + ob + c);
-    const f32x4 s1 = *reinterpret_cast<const f32x4*>(A.o_s + ob + c + 4);
-    const f32x4 l0 = *reinterpret_cast<const f32x4*>(A.o_l + ob + c);
-    const f32x4 l1 = *reinterpret_cast<const f32x4*>(A.o_l + ob + c + 4);
+  for (int k = 0; k < PASSES; ++k) {
+    nrow[k] = kBlock * i + (kThreads * k + t) / LPR;
+    const int nn = min(nrow[k], g.N - 1);
+    const int64_t o = (static_cast<int64_t>(bh) * g.N + nn) * D + col;
+    sv[k] = *reinterpret_cast<const f32x4*>(A.o_s + o);
+    lv[k] = *reinterpret_cast<const f32x4*>(A.o_l + o);
+    load4_f32(gbase + static_cast<int64_t>(nn) * g.sn, gv[k]);
+  }
+  float da = 0.0f;
+  const float al = A.alpha[h];
+#pragma unroll
+  for (int k = 0; k < PASSES; ++k) {
+    float ds = 0.0f, dak = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      ds = fmaf(gv[e], s0[e], ds);
-      ds = fmaf(gv[4 + e], s1[e], ds);
-      da = fmaf(gv[e], s0[e] - l0[e], da);
-      da = fmaf(gv[4 + e], s1[e] - l1[e], da);
+      ds = fmaf(gv[k][e], sv[k][e], ds);
+      dak = fmaf(gv[k][e], sv[k][e] - lv[k][e], dak);
     }
+    if (nrow[k] < g.N) da += dak;
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) ds += xor_lane(ds, m);
+    if ((t % LPR) == 0 && nrow[k] < g.N) A.dd[static_cast<int64_t>(bh) * g.N + nrow[k]] = al * ds;
   }
-  ds += dpp_f<0xB1>(ds);
-  ds += dpp_f<0x4E>(ds);
-  da += dpp_f<0xB1>(da);
-  da += dpp_f<0x4E>(da);
-  if (prt == 0 && valid) A.dd[static_cast<int64_t>(bh) * g.N + n] = A.alpha[h] * ds;
-  float w = (prt == 0 && valid) ? da : 0.0f;
-  w += xor_lane(w, 32);
-  w += xor_lane(w, 16);
-  w += xor_lane(w, 8);
-  w += xor_lane(w, 4);
-  if ((t & 63) == 0) red[t >> 6] = w;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) da += xor_lane(da, m);
+  if (lane == 0) red[t >> 6] = da;
   __syncthreads();
   if (t == 0) A.dalpha_part[static_cast<int64_t>(bh) * g.nq + i] = (red[0] + red[1]) + (red[2] + red[3]);
 }
