@@ -225,7 +225,7 @@ size_t backward_ws(const sla::Geometry& g) {
   const size_t blk = bh * g.nq;
   const size_t nmt = bh * sla::marginal_chunks(g) * sla::marginal_rows_pad(g) * 2;
   return forward_ws(g) + align_up(span_elems(g) * 2) + 2 * align_up(rows * g.D * 4) +
-         2 * align_up(rows * 4) + align_up(blk * (g.D * g.D + g.D) * 2) +
+         3 * align_up(rows * 4) + align_up(blk * (g.D * g.D + g.D) * 2) +
          align_up(bh * g.nkb * (g.D * g.D + g.D) * 2) +
          align_up(bh * g.nkb * sla::backward_crit_words(g) * 4) + align_up(nmt * 4) +
          align_up(blk * 4);
@@ -249,6 +249,8 @@ BwdWs carve_backward_ws(const sla::Geometry& g, void* ws) {
   p += align_up(rows * 4);
   float* dd = reinterpret_cast<float*>(p);
   p += align_up(rows * 4);
+  float* dol = reinterpret_cast<float*>(p);
+  p += align_up(rows * 4);
   uint16_t* ds = reinterpret_cast<uint16_t*>(p);
   p += align_up(blk * (g.D * g.D + g.D) * 2);
   uint16_t* dh = reinterpret_cast<uint16_t*>(p);
@@ -258,8 +260,8 @@ BwdWs carve_backward_ws(const sla::Geometry& g, void* ws) {
   uint32_t* marg_t = reinterpret_cast<uint32_t*>(p);
   p += align_up(nmt * 4);
   float* dap = reinterpret_cast<float*>(p);
-  w.b = sla::BackwardBuffers{o_s, o_l, lse, dd, w.fwd.s_sum, w.fwd.sigma, ds, dh, crit_t, marg_t,
-                             dap};
+  w.b = sla::BackwardBuffers{o_s, o_l, lse, dd, dol, w.fwd.s_sum, w.fwd.sigma, ds, dh, crit_t,
+                             marg_t, dap};
   return w;
 }
 

@@ -22,8 +22,9 @@
 //
 // Kernels (one launch each, in this order, after the forward has written
 // O_s, O_l and the log2 normaliser into the workspace):
-//   bwd_rowdot_kernel   D_t = alpha dO . O_s per row; per-block partial sums
-//                       of dO . (O_s - O_l) for dalpha;
+//   bwd_rowdot_kernel   D_t = alpha dO . O_s and dO . O_l per row (the
+//                       linear query side reads the latter); per-block
+//                       partial sums of dO . (O_s - O_l) for dalpha;
 //   bwd_dq_kernel       query-major: the critical blocks of query block i
 //                       through the same LDS ring as the forward; S^T, dP^T
 //                       and dQ^T += K^T dS^T on the matrix cores (K^T by
@@ -63,6 +64,7 @@ struct BwdArgs {
   const float* o_l;        // float [BH][N][D]
   const float* lse;        // float [BH][N], log2 normaliser of the sparse softmax
   float* dd;               // float [BH][N], D_t
+  float* dol;              // float [BH][N], dO . O_l per row
   const uint16_t* s_sum;   // bf16 [BH][nq][D][D] value-major (forward workspace)
   const float* sigma;      // float [BH][nq][D]
   uint16_t* ds;            // bf16 [BH][nq][D*D + D]: dS_i value-major, then dsigma_i
@@ -148,16 +150,23 @@ bwd_rowdot_kernel(BwdArgs A) {
   const float al = A.alpha[h];
 #pragma unroll
   for (int k = 0; k < PASSES; ++k) {
-    float ds = 0.0f, dak = 0.0f;
+    float ds = 0.0f, dl = 0.0f, dak = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       ds = fmaf(gv[k][e], sv[k][e], ds);
+      dl = fmaf(gv[k][e], lv[k][e], dl);
       dak = fmaf(gv[k][e], sv[k][e] - lv[k][e], dak);
     }
     if (nrow[k] < g.N) da += dak;
 #pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) ds += xor_lane(ds, m);
-    if ((t % LPR) == 0 && nrow[k] < g.N) A.dd[static_cast<int64_t>(bh) * g.N + nrow[k]] = al * ds;
+    for (int m = 1; m < LPR; m <<= 1) {
+      ds += xor_lane(ds, m);
+      dl += xor_lane(dl, m);
+    }
+    if ((t % LPR) == 0 && nrow[k] < g.N) {
+      A.dd[static_cast<int64_t>(bh) * g.N + nrow[k]] = al * ds;
+      A.dol[static_cast<int64_t>(bh) * g.N + nrow[k]] = dl;
+    }
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) da += xor_lane(da, m);
@@ -418,26 +427,17 @@ bwd_lin_q_kernel(BwdArgs A) {
     }
   const float zinv = 1.0f / (zp + xor_lane(zp, 32));
   // dO (kept packed, in the k-slot order of the transposing reads: c = 16 s
-  // + {4 hh + e, 8 + 4 hh + e}) and dO . O_l, before the barrier so that
-  // these loads overlap the S_i^T and sigma_i transfers
+  // + {4 hh + e, 8 + 4 hh + e}) and the row's dO . O_l (from the row-dot
+  // pass), before the barrier so that these loads overlap the S_i^T and
+  // sigma_i transfers
   u32x2 graw[NS][2];
-  float gdot = 0.0f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int c0 = 16 * s + 4 * hh;
     graw[s][0] = *reinterpret_cast<const u32x2*>(A.dout + rowg + c0);
     graw[s][1] = *reinterpret_cast<const u32x2*>(A.dout + rowg + c0 + 8);
-    const f32x4 l0 = *reinterpret_cast<const f32x4*>(A.o_l + rowt * D + c0);
-    const f32x4 l1 = *reinterpret_cast<const f32x4*>(A.o_l + rowt * D + c0 + 8);
-    float g0[4], g1[4];
-    load4_f32(reinterpret_cast<const uint16_t*>(&graw[s][0]), g0);
-    load4_f32(reinterpret_cast<const uint16_t*>(&graw[s][1]), g1);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      gdot = fmaf(g0[e], l0[e], gdot);
-      gdot = fmaf(g1[e], l1[e], gdot);
-    }
   }
+  const float gdot = A.dol[rowt];
   // q at the df positions (a = 32 at + 8 r4 + 4 hh + x), packed
   u32x2 qraw[DTH][4];
 #pragma unroll
@@ -468,7 +468,7 @@ bwd_lin_q_kernel(BwdArgs A) {
       dn[s][4 + e] = f32_to_bf16(vrow ? g1[e] * cdo : 0.0f);
     }
   }
-  const float dden = vrow ? -(1.0f - al) * (gdot + xor_lane(gdot, 32)) / den : 0.0f;
+  const float dden = vrow ? -(1.0f - al) * gdot / den : 0.0f;
 
   // df^T for the key-feature tiles at = ah*DTH + u: S_i rows a (transposing
   // reads of S_i^T) times dn, plus sigma_i[a] dden
@@ -1051,7 +1051,7 @@ hipError_t launch_backward(const Geometry& g, const BackwardBuffers& w, const vo
                            float* dv, float* dalpha, hipStream_t stream) {
   BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
             static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout), crit, marg, alpha,
-            w.o_s, w.o_l, w.lse, w.dd, w.s_sum, w.sigma, w.ds, w.dh, w.crit_t,
+            w.o_s, w.o_l, w.lse, w.dd, w.dol, w.s_sum, w.sigma, w.ds, w.dh, w.crit_t,
             backward_crit_words(g), w.marg_t, dq, dk, dv, w.dalpha_part, dalpha, g,
             static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(g.D)))};
   if (g.D == 128) return launch_backward_t<128>(a, stream);

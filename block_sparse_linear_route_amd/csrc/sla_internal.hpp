@@ -99,6 +99,7 @@ struct BackwardBuffers {
   const float* o_l;
   const float* lse;
   float* dd;
+  float* dol;
   const uint16_t* s_sum;
   const float* sigma;
   uint16_t* ds;

@@ -128,7 +128,7 @@ int sla_num_blocks(const sla_problem* problem, int32_t* nq, int32_t* nkb);
  * [B,H,64*ceil(nkb/64),d], a bf16 Hbar [B,H,d,d] and float32 per-chunk
  * partial sums of the first-order matrices; SLA_OP_BACKWARD needs the
  * forward workspace, an O scratch in the problem layout, float O_s, O_l
- * [B,H,N,d], float row statistics [B,H,N] x 2, bf16 dS with dsigma
+ * [B,H,N,d], float row statistics [B,H,N] x 3, bf16 dS with dsigma
  * [B,H,nq,d*d+d], bf16 dH with dz [B,H,nkb,d*d+d], transposed mask bits and
  * float dalpha partials [B,H,nq]. */
 int sla_workspace_size(const sla_problem* problem, int op, size_t* bytes);
