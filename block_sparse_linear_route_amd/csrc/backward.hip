@@ -969,24 +969,77 @@ bwd_lin_kv_kernel(BwdArgs A, int nchunks, int rows_pad) {
   }
   __syncthreads();
   const float tot = rsum + red[wave ^ 2][l32];
-  if (nvalid) {
-    const int64_t ro = (static_cast<int64_t>(bh) * g.N + kBlock * j + nrow) * D;
+  if constexpr (D != 128) {
+    // (d = 64: the tiles are too small to stage the block; add in place)
+    if (nvalid) {
+      const int64_t ro = (static_cast<int64_t>(bh) * g.N + kBlock * j + nrow) * D;
 #pragma unroll
-    for (int u = 0; u < DTH; ++u)
+      for (int u = 0; u < DTH; ++u)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int a0 = 32 * (fh * DTH + u) + 8 * r4 + 4 * hh;
-        f32x4 wk = *reinterpret_cast<const f32x4*>(A.dk + ro + a0);
-        f32x4 wv = *reinterpret_cast<const f32x4*>(A.dv + ro + a0);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int a0 = 32 * (fh * DTH + u) + 8 * r4 + 4 * hh;
+          f32x4 wk = *reinterpret_cast<const f32x4*>(A.dk + ro + a0);
+          f32x4 wv = *reinterpret_cast<const f32x4*>(A.dv + ro + a0);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int r = 4 * r4 + x;
-          wk[x] += pv[u][r] * (dphi[u][r] - tot);
-          wv[x] += dvl[u][r];
+          for (int x = 0; x < 4; ++x) {
+            const int r = 4 * r4 + x;
+            wk[x] += pv[u][r] * (dphi[u][r] - tot);
+            wv[x] += dvl[u][r];
+          }
+          *reinterpret_cast<f32x4*>(A.dk + ro + a0) = wk;
+          *reinterpret_cast<f32x4*>(A.dv + ro + a0) = wv;
         }
-        *reinterpret_cast<f32x4*>(A.dk + ro + a0) = wk;
-        *reinterpret_cast<f32x4*>(A.dv + ro + a0) = wv;
+    }
+    return;
+  }
+  // d = 128: the contributions to dk and dv go through LDS (the tiles are no
+  // longer read): dk's 64 token rows in htile (32 KB), dv's rows 0-31 in
+  // vtile and 32-63 in ptile (16 KB each), each row's 16-byte chunks
+  // XOR-swizzled by the row.  All threads then add them into dk and dv with
+  // contiguous 1 KB reads and writes per instruction, where the register
+  // layout would touch 32 B of 32 rows.
+  constexpr int CPR = D / 4;                           // 16-byte chunks per row
+  float* sk = reinterpret_cast<float*>(htile);
+  auto sv_row = [&](int r) -> float* {
+    return reinterpret_cast<float*>(r < 32 ? vtile : ptile) + (r & 31) * D;
+  };
+#pragma unroll
+  for (int u = 0; u < DTH; ++u)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int a0 = 32 * (fh * DTH + u) + 8 * r4 + 4 * hh;
+      const int pc = ((a0 >> 2) ^ (nrow & (CPR - 1))) * 4;
+      f32x4 wk, wv;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 4 * r4 + x;
+        wk[x] = pv[u][r] * (dphi[u][r] - tot);
+        wv[x] = dvl[u][r];
       }
+      *reinterpret_cast<f32x4*>(sk + nrow * D + pc) = wk;
+      *reinterpret_cast<f32x4*>(sv_row(nrow) + pc) = wv;
+    }
+  __syncthreads();
+  const int64_t rb = (static_cast<int64_t>(bh) * g.N + kBlock * j) * D;
+#pragma unroll
+  for (int k = 0; k < kBlock * CPR / kThreads; ++k) {
+    const int e4 = k * kThreads + t;
+    const int row = e4 / CPR, c = e4 % CPR;
+    if (row < nj) {
+      const int pc = (c ^ (row & (CPR - 1))) * 4;
+      const f32x4 ak = *reinterpret_cast<const f32x4*>(sk + row * D + pc);
+      const f32x4 av = *reinterpret_cast<const f32x4*>(sv_row(row) + pc);
+      f32x4* gk = reinterpret_cast<f32x4*>(A.dk + rb + row * D + 4 * c);
+      f32x4* gv = reinterpret_cast<f32x4*>(A.dv + rb + row * D + 4 * c);
+      f32x4 wk = *gk, wv = *gv;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        wk[x] += ak[x];
+        wv[x] += av[x];
+      }
+      *gk = wk;
+      *gv = wv;
+    }
   }
 }
 
