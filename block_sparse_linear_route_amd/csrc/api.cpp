@@ -58,6 +58,12 @@ int validate_problem(const sla_problem* p) {
   const int64_t esz = p->dtype == SLA_BF16 ? 2 : 4;
   if ((p->stride_n * esz) % 16 || (p->stride_h * esz) % 16 || (p->stride_b * esz) % 16)
     return fail(SLA_ERR_INVALID_ARGUMENT, "strides must be multiples of 16 bytes");
+  // The tile loads address a head's rows through buffer resources with
+  // 32-bit byte offsets and sizes: one head's span must fit in them.
+  const int64_t head_span = (static_cast<int64_t>(p->seq_len) - 1) * p->stride_n * esz + p->head_dim * esz;
+  if (head_span > static_cast<int64_t>(UINT32_MAX))
+    return fail(SLA_ERR_UNSUPPORTED, "one head spans %lld bytes (seq_len x stride_n); at most 4 GiB is supported",
+                static_cast<long long>(head_span));
   const int64_t nq_total = static_cast<int64_t>(p->batch) * p->heads * nkb;
   if (nq_total > (1ll << 31) - 1)
     return fail(SLA_ERR_UNSUPPORTED, "batch * heads * blocks exceeds the grid limit");

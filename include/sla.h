@@ -110,8 +110,10 @@ typedef struct sla_problem {
 
 /* Host-only checks of a problem (no HIP call).  SLA_OK,
  * SLA_ERR_INVALID_ARGUMENT (null, sizes < 1, bad counts, strides that
- * overlap rows) or SLA_ERR_UNSUPPORTED (head_dim, block, dtype, or more than
- * 4096 KV blocks). */
+ * overlap rows) or SLA_ERR_UNSUPPORTED (head_dim, block, dtype, more than
+ * 4096 KV blocks, or one head spanning more than 4 GiB:
+ * (seq_len - 1) * stride_n * elem_size + head_dim * elem_size > 2^32 - 1,
+ * which only very wide row strides such as packed QKV of many heads reach). */
 int sla_validate(const sla_problem* problem);
 
 /* Host: number of query blocks and KV blocks (both ceil(seq_len / 64)). */

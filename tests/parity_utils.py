@@ -69,3 +69,16 @@ def compare_classes(gpu_cls: np.ndarray, ora_cls: np.ndarray, logits: np.ndarray
         else:
             unexcused += 1
     return excused, unexcused, len(rows)
+
+
+def metrics_by_head(pairs):
+    """pairs: {head label: (got, ref)} float64 arrays of one output.
+    Returns (whole-tensor (rel L2, max-abs), {label: (rel L2, max-abs)})."""
+    per = {lab: (rel_l2(a, b), max_abs(a, b)) for lab, (a, b) in pairs.items()}
+    got = np.concatenate([a.ravel() for a, _ in pairs.values()])
+    ref = np.concatenate([b.ravel() for _, b in pairs.values()])
+    return (rel_l2(got, ref), max_abs(got, ref)), per
+
+
+def format_per_head(per) -> str:
+    return " ".join(f"{lab}:{e:.1e}/{m:.1e}" for lab, (e, m) in per.items())

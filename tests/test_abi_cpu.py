@@ -59,6 +59,13 @@ def validate(p):
     (dict(k_crit=-1), _lib.SLA_ERR_INVALID_ARGUMENT),
     (dict(stride_n=100), _lib.SLA_ERR_INVALID_ARGUMENT),          # row overlap
     (dict(stride_n=132), _lib.SLA_ERR_INVALID_ARGUMENT),          # 264 B rows: not 16-B multiple
+    # packed QKV of 40 heads (row stride 3 * 40 * 128 elements): 139 811
+    # tokens span 4 294 963 456 bytes, one more row passes 2^32 - 1
+    (dict(seq_len=139811, stride_n=15360, stride_h=128, stride_b=139811 * 15360), _lib.SLA_OK),
+    (dict(seq_len=139812, stride_n=15360, stride_h=128, stride_b=139812 * 15360),
+     _lib.SLA_ERR_UNSUPPORTED),
+    (dict(seq_len=262144, stride_n=15360, stride_h=128, stride_b=0, dtype=_lib.SLA_BF16),
+     _lib.SLA_ERR_UNSUPPORTED),
 ])
 def test_validate(kw, status):
     assert validate(P(**kw)) == status
@@ -239,3 +246,28 @@ def test_saved_backward_entry_points_reject_bad_arguments_before_any_device_call
     assert st == _lib.SLA_ERR_INVALID_ARGUMENT        # dalpha missing
     st = lib.sla_backward_saved(ctypes.byref(p), *([fake] * 12), n.value - 1, None)
     assert st == _lib.SLA_ERR_WORKSPACE
+
+
+def _device_visible() -> bool:
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif(_device_visible(), reason="a HIP device is present: fake pointers would reach kernels")
+def test_valid_calls_without_a_device_return_no_device():
+    # arguments pass validation, then the device check finds no gfx950 GPU
+    fake = ctypes.c_void_p(0x10000)
+    p = P()
+    n = ctypes.c_size_t()
+    assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_ROUTE, ctypes.byref(n)) == 0
+    st = lib.sla_route(ctypes.byref(p), fake, fake, fake, fake, None, None, None, None, fake, n.value, None)
+    assert st == _lib.SLA_ERR_NO_DEVICE
+    assert lib.sla_last_error_message()
+    st = lib.sla_linear_states(ctypes.byref(p), fake, fake, fake, fake, None)
+    assert st == _lib.SLA_ERR_NO_DEVICE
+    assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_FORWARD, ctypes.byref(n)) == 0
+    st = lib.sla_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                         None, None, fake, n.value, None)
+    assert st == _lib.SLA_ERR_NO_DEVICE
+    st = lib.sla_quantize_fp8(ctypes.byref(p), fake, fake, fake, None)
+    assert st == _lib.SLA_ERR_NO_DEVICE

@@ -64,3 +64,40 @@ def test_block_quantiser_properties():
         deq = fp8.decode_e4m3(codes[a:b]) * scales[jj]
         big = np.abs(x[a:b]) >= amax * 2.0 ** -6      # normal range: relative error <= 2^-4
         assert (np.abs(deq - x[a:b])[big] <= np.abs(x[a:b])[big] * 2.0 ** -4 + 1e-12).all()
+
+
+def test_dequantize_blocks_hand_values():
+    # two blocks of 64 rows and a 3-row tail; codes with values fixed by the
+    # format: 0x38 = 1, 0x7E = 448, 0x01 = 2^-9, 0xC0 = -2, 0x00 = 0,
+    # 0x3C = 1.5; each row is multiplied by its own block's scale
+    codes = np.zeros((131, 2), dtype=np.uint8)
+    codes[0] = [0x38, 0x7E]
+    codes[63] = [0x01, 0xC0]
+    codes[64] = [0x38, 0x3C]
+    codes[130] = [0x7E, 0xC0]
+    scales = np.array([2.0, 0.25, 1.0 / 448.0], dtype=np.float32)
+    out = fp8.dequantize_blocks(codes, scales)
+    want = np.zeros((131, 2))
+    want[0] = [2.0, 896.0]
+    want[63] = [2.0 ** -8, -4.0]
+    want[64] = [0.25, 0.375]
+    want[130] = [float(np.float32(1.0 / 448.0)) * 448.0, -2.0 * float(np.float32(1.0 / 448.0))]
+    np.testing.assert_array_equal(out, want)
+
+
+def test_dequantize_inverts_quantize_within_the_format_error():
+    # x -> codes, scale -> x': each element is within half a quantum of the
+    # block-scaled grid: relative 2^-4 in the normal range, and at most
+    # 2^-10 * scale (half the subnormal step) below it
+    r = np.random.default_rng(11)
+    x = (r.standard_normal((64 * 5 + 9, 128)) * np.exp2(r.integers(-6, 6, (64 * 5 + 9, 1)))).astype(np.float32)
+    codes, scales = fp8.quantize_blocks(x)
+    deq = fp8.dequantize_blocks(codes, scales)
+    for j in range(len(scales)):
+        a, b = 64 * j, min(64 * j + 64, x.shape[0])
+        err = np.abs(deq[a:b] - x[a:b])
+        bound = np.maximum(np.abs(x[a:b]) * 2.0 ** -4, 2.0 ** -10 * float(scales[j])) * (1 + 1e-6)
+        assert (err <= bound).all(), j
+        # the block's largest magnitude is reproduced to float32 rounding
+        amax = np.abs(x[a:b]).max()
+        assert abs(np.abs(deq[a:b]).max() - amax) <= amax * 2.0 ** -20

@@ -86,6 +86,12 @@ def _bwd_check(w, heads=None, seed=0):
     (1000, 128, 0, 6, 1, 94),      # linear branch only
     (1000, 128, 7, 0, 1, 95),      # sparse branch only
     (1000, 128, 16, 0, 1, 96),     # every block critical: dense attention
+    # critical lists past the 64 entries one list register holds (forward
+    # recompute and the query-major dQ kernel refill them every 64 steps)
+    (300 * 64 + 17, 128, 64, 10, 1, 110),
+    (300 * 64 + 17, 128, 65, 20, 1, 111),
+    (300 * 64 + 17, 128, 129, 30, 1, 112),
+    (270 * 64, 64, 200, 30, 1, 113),
 ])
 def test_backward_parity_shapes(N, d, kc, km, H, seed):
     w = make_custom(1, H, N, d, dtype="bf16", kind="fourier1d", seed=seed, k_crit=kc, k_marg=km)

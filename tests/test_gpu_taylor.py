@@ -119,4 +119,4 @@ def test_taylor_route_changes_the_split_on_the_workload():
 
 @pytest.mark.timeout(900)
 def test_taylor_route_parity_video75k():
-    _taylor_check(make_workload("video75k", cache=False), heads=[(0, 0), (0, 21), (0, 39)])
+    _taylor_check(make_workload("video75k"), heads=[(0, 0), (0, 21), (0, 39)])
