@@ -28,6 +28,7 @@ from .ops import (  # noqa: F401
     quantize_fp8,
     residual_sums,
     route,
+    route_noalloc,
     sla_attention,
     version,
     workspace_size,

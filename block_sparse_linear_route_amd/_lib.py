@@ -19,6 +19,7 @@ SLA_ERR_DEVICE = -4
 SLA_ERR_NO_DEVICE = -5
 
 SLA_F32, SLA_BF16 = 0, 1
+SLA_STATIC_SCRATCH_BYTES = 64 << 20
 (OP_ROUTE, OP_LINEAR_STATES, OP_FORWARD, OP_QUANTIZE_FP8, OP_FORWARD_FP8, OP_ROUTE_TAYLOR,
  OP_FORWARD_PISA, OP_BACKWARD) = range(8)
 
@@ -43,6 +44,7 @@ SIGNATURES = {
     "sla_num_blocks": (ctypes.c_int, [_P, _i32p, _i32p]),
     "sla_workspace_size": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_sz)]),
     "sla_route": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sla_route_noalloc": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "sla_route_taylor": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _sz, _vp]),
     "sla_linear_states": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp]),

@@ -336,6 +336,35 @@ int sla_route(const sla_problem* problem, const void* q, const void* k, int32_t*
                   "sla_route launch");
 }
 
+int sla_route_noalloc(const sla_problem* problem, const void* q, const void* k, int32_t* crit_idx,
+                      int32_t* marg_idx, int8_t* block_class, float* block_logits,
+                      float* pooled_q, float* pooled_k, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(q, 16);
+  SLA_REQ(k, 16);
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  if (problem->k_marg > 0) SLA_REQ(marg_idx, 4);
+  SLA_OPT(block_logits, 4);
+  SLA_OPT(pooled_q, 4);
+  SLA_OPT(pooled_k, 4);
+  const sla::Geometry g = geometry(problem);
+  const size_t need = route_ws(g);
+  if (need > sla::kStaticScratchBytes)
+    return fail(SLA_ERR_WORKSPACE,
+                "routing needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use sla_route with a caller workspace)",
+                need, sla::kStaticScratchBytes);
+  SLA_TRY(check_device());
+  void* ws = nullptr;
+  SLA_TRY(launched(sla::static_scratch(&ws), "static scratch lookup"));
+  double* qpool = static_cast<double*>(ws);
+  double* kpool_t = reinterpret_cast<double*>(static_cast<char*>(ws) + route_region(g));
+  return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
+                                    pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr,
+                                    static_cast<hipStream_t>(stream)),
+                  "sla_route_noalloc launch");
+}
+
 int sla_route_taylor(const sla_problem* problem, const void* q, const void* k, int32_t* crit_idx,
                      int32_t* marg_idx, int8_t* block_class, float* block_logits,
                      float* pooled_q, float* pooled_k, float* key_var, void* ws, size_t ws_bytes,

@@ -17,6 +17,13 @@ struct Geometry {
   int64_t sb, sh, sn;    // element strides of Q, K, V, O
 };
 
+// Static device scratch of the allocation-free entry points (scratch.hip):
+// kStaticScratchBytes per GPU, 256-byte aligned.  static_scratch() returns
+// the current device's copy (looked up once per device); calls that use it
+// concurrently on one GPU share it.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t static_scratch(void** ptr);
+
 // ws_kvar_t non-null: second-order routing score (block key variances pooled
 // into it, and into key_var as float32 when that is non-null).
 hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t* crit,

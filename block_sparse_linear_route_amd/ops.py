@@ -134,6 +134,37 @@ def route(q: torch.Tensor, k: torch.Tensor, k_crit: int, k_marg: int, *, want_cl
     return out
 
 
+def route_noalloc(q: torch.Tensor, k: torch.Tensor, k_crit: int, k_marg: int, *,
+                  want_class: bool = False, want_logits: bool = False, want_pooled: bool = False,
+                  out: Optional[dict] = None, stream=None) -> dict:
+    """``sla_route_noalloc``: the plain route with the library's static device
+    scratch in place of a workspace.  ``out`` may hold preallocated outputs
+    (crit_idx, marg_idx and the optional ones); missing ones are allocated
+    here, so a caller that must not allocate passes all it asks for."""
+    (k,) = _same_layout(q, k)
+    p = make_problem(q, k_crit, k_marg)
+    B, H, N, d = q.shape
+    nb = num_blocks(N)
+    dev = q.device
+    out = dict(out or {})
+    shapes = dict(crit_idx=((B, H, nb, k_crit), torch.int32), marg_idx=((B, H, nb, k_marg), torch.int32))
+    if want_class:
+        shapes["block_class"] = ((B, H, nb, nb), torch.int8)
+    if want_logits:
+        shapes["block_logits"] = ((B, H, nb, nb), torch.float32)
+    if want_pooled:
+        shapes["pooled_q"] = ((B, H, nb, d), torch.float32)
+        shapes["pooled_k"] = ((B, H, nb, d), torch.float32)
+    for name, (shape, dt) in shapes.items():
+        if name not in out:
+            out[name] = torch.empty(shape, dtype=dt, device=dev)
+    _check(lib.sla_route_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(out["crit_idx"]),
+                                 _ptr(out["marg_idx"]), _ptr(out.get("block_class")),
+                                 _ptr(out.get("block_logits")), _ptr(out.get("pooled_q")),
+                                 _ptr(out.get("pooled_k")), _stream(stream)))
+    return out
+
+
 def linear_states(k: torch.Tensor, v: torch.Tensor, stream=None, *, feature_map: str = "softmax"):
     """Per-block states: H bf16 [B,H,nkb,d,d], z float32 [B,H,nkb,d].
 

@@ -152,6 +152,27 @@ int sla_route(const sla_problem* problem, const void* q, const void* k,
               float* block_logits, float* pooled_q, float* pooled_k, void* ws,
               size_t ws_bytes, void* stream);
 
+/* Bytes of device scratch the library holds per GPU for the allocation-free
+ * entry points. */
+#define SLA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* Block routing without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * sla_route, minus ws / ws_bytes: the float64 pooled sums live in a static
+ * device array of SLA_STATIC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends (its device address is looked up
+ * once per device on the first call there).  The call allocates nothing.
+ * Returns SLA_ERR_WORKSPACE when sla_workspace_size(SLA_OP_ROUTE) exceeds
+ * SLA_STATIC_SCRATCH_BYTES (at head_dim 128: B * H * nkb > 32768).  Every
+ * call on one GPU shares that GPU's array, whatever the stream: calls that
+ * overlap in time on one GPU race on it and must be serialised by the
+ * caller (one stream, or events). */
+int sla_route_noalloc(const sla_problem* problem, const void* q, const void* k,
+                      int32_t* crit_idx, int32_t* marg_idx, int8_t* block_class,
+                      float* block_logits, float* pooled_q, float* pooled_k,
+                      void* stream);
+
 /* Block routing with the second-order score.  [SPLA summary 2.1]
  * The block score keeps the spread of the keys around their block mean,
  * to second order with a diagonal covariance:

@@ -271,3 +271,19 @@ def test_valid_calls_without_a_device_return_no_device():
     assert st == _lib.SLA_ERR_NO_DEVICE
     st = lib.sla_quantize_fp8(ctypes.byref(p), fake, fake, fake, None)
     assert st == _lib.SLA_ERR_NO_DEVICE
+
+
+def test_noalloc_route_rejects_sizes_past_the_static_scratch_before_any_device_call():
+    fake = ctypes.c_void_p(0x10000)
+    assert _lib.SLA_STATIC_SCRATCH_BYTES == 64 << 20
+    # route scratch 2 * B*H*nkb*d*8 bytes: 32 * 1024 blocks fit exactly, one more head does not
+    fits = P(batch=32, heads=1, seq_len=64 * 1024, stride_h=64 * 1024 * 128, stride_b=64 * 1024 * 128)
+    n = ctypes.c_size_t()
+    assert lib.sla_workspace_size(ctypes.byref(fits), _lib.OP_ROUTE, ctypes.byref(n)) == 0
+    assert n.value == _lib.SLA_STATIC_SCRATCH_BYTES
+    big = P(batch=33, heads=1, seq_len=64 * 1024, stride_h=64 * 1024 * 128, stride_b=64 * 1024 * 128)
+    st = lib.sla_route_noalloc(ctypes.byref(big), fake, fake, fake, fake, None, None, None, None, None)
+    assert st == _lib.SLA_ERR_WORKSPACE
+    assert b"static scratch" in lib.sla_last_error_message()
+    st = lib.sla_route_noalloc(ctypes.byref(fits), None, fake, fake, fake, None, None, None, None, None)
+    assert st == _lib.SLA_ERR_INVALID_ARGUMENT
