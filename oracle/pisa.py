@@ -21,8 +21,24 @@ Readings fixed here (each is listed in the design notes):
 * the first-order term of D_t is q_t . sum_n (k_n - kbar_j) = 0 exactly, so
   D_t has exact and zero-order terms only;
 * S_i is the router's critical list; U_i is every other KV block.
-The covariance-aware selection score is not part of this reference: the
-page does not say how the block norm enters the score.
+
+Covariance-aware routing ("Enrutamiento Consciente de la Covarianza": the
+selection score of a block takes in, beside its attention score, the norm
+M_j = ||H_j - Hbar|| of its first-order matrix's deviation from the shared
+Hbar, so that blocks of high relevance or high heterogeneity are computed
+exactly) is ``route_pisa``.  Readings fixed here:
+* an unselected block j replaces its own first-order term by Hbar, so N_t
+  misses alpha_{t,j} (q_t / sqrt(d)) (H_j - Hbar), whose norm is at most
+  alpha_{t,j} (|q_t| / sqrt(d)) M_j;
+* the norm is the L2 norm of the matrix taken as a vector (Frobenius),
+  which bounds the spectral norm, so the bound above holds with it;
+* the score weighs the block's zero-order weight alpha_ij B (B = 64 tokens)
+  by one plus that first-order discrepancy per token, with the router's
+  pooled query qbar_i in place of q_t; ranking uses its logarithm
+  s_ij + log1p(|qbar_i| M_j / (sqrt(d) B)), s_ij the plain logit (the
+  constant log B is dropped).  Equal M_j for every block shift a row by a
+  constant and leave the plain router's split unchanged; the split, counts
+  and tie rule are those of ``oracle.sla``.
 
 The evaluation subtracts the row max of all the exponents involved (exact
 logits and centroid logits) from each of them, a common factor of N_t and
@@ -111,3 +127,43 @@ def pisa_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, crit_idx: np.ndarray,
         o_fo[a:b] = num_fo / den[:, None]
         o[a:b] = o_sm[a:b] + o_fo[a:b]
     return o, o_sm, o_fo
+
+
+def block_deviation(H: np.ndarray, Hbar: np.ndarray) -> np.ndarray:
+    """M_j = ||H_j - Hbar||, the L2 norm of the d x d deviation taken as a vector.
+
+    Pinned by: squared norm = sum of squared singular values (numpy SVD);
+    at least the spectral norm, so it bounds |q (H_j - Hbar)| / |q|; zero
+    when every block shares one first-order matrix; brute-force loops.
+    """
+    dev = H - Hbar[None]
+    return np.sqrt((dev * dev).sum(axis=(1, 2)))
+
+
+def covariance_logits(q_pool: np.ndarray, k_pool: np.ndarray, M: np.ndarray,
+                      block: int = BLOCK) -> np.ndarray:
+    """s_ij + log1p(|qbar_i| M_j / (sqrt(d) B)), s_ij = qbar_i . kbar_j / sqrt(d).
+
+    Pinned by: M = 0, or equal M_j for every block, gives the plain router's
+    split; the logit grows with M_j and with nothing else of block j;
+    brute-force loops.
+    """
+    d = q_pool.shape[1]
+    s = (q_pool @ k_pool.T) / math.sqrt(d)
+    c = np.sqrt((q_pool * q_pool).sum(axis=1)) / (math.sqrt(d) * block)
+    return s + np.log1p(c[:, None] * M[None, :])
+
+
+def route_pisa(q: np.ndarray, k: np.ndarray, v: np.ndarray, k_crit: int, k_marg: int,
+               block: int = BLOCK):
+    """Pool, covariance-aware score and split one head (outputs as ``sla.route``,
+    plus the block deviations M_j and Hbar)."""
+    qp = sla.pool(q, block)
+    kp = sla.pool(k, block)
+    _, _, _, H = block_statistics(k, v, block)
+    Hbar = global_first_order(H)
+    M = block_deviation(H, Hbar)
+    logits = covariance_logits(qp, kp, M, block)
+    crit, marg, cls = sla.select(logits, k_crit, k_marg)
+    return {"crit_idx": crit, "marg_idx": marg, "block_class": cls, "logits": logits,
+            "pooled_q": qp, "pooled_k": kp, "block_dev": M, "hbar": Hbar}

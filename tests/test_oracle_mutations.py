@@ -214,6 +214,28 @@ def test_pisa_correction_sign(monkeypatch):
     _fails(pisa_pins.test_equal_first_order_matrices_leave_second_order_error)
 
 
+def test_pisa_deviation_without_hbar(monkeypatch):
+    # the norm of H_j itself instead of its deviation from Hbar
+    monkeypatch.setattr(pisa_mod, "block_deviation",
+                        lambda H, Hbar: np.sqrt((H * H).sum(axis=(1, 2))))
+    _fails(pisa_pins.test_equal_deviations_give_the_plain_split)
+
+
+def test_pisa_covariance_term_unscaled(monkeypatch):
+    # |qbar| M_j without the 1 / (sqrt(d) B) factor
+    monkeypatch.setattr(pisa_mod, "covariance_logits", lambda qp, kp, M, block=64:
+                        qp @ kp.T / math.sqrt(qp.shape[1])
+                        + np.log1p(np.linalg.norm(qp, axis=1)[:, None] * M[None, :]))
+    _fails(pisa_pins.test_covariance_logits_brute_force)
+
+
+def test_pisa_covariance_term_subtracted(monkeypatch):
+    orig = pisa_mod.covariance_logits
+    monkeypatch.setattr(pisa_mod, "covariance_logits", lambda qp, kp, M, block=64:
+                        2 * (qp @ kp.T / math.sqrt(qp.shape[1])) - orig(qp, kp, M, block))
+    _fails(pisa_pins.test_logit_grows_with_the_block_deviation_alone)
+
+
 from oracle import backward as bwd_mod
 import tests.test_oracle_pins_backward as bwd_pins
 

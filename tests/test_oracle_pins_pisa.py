@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 from scipy.special import softmax
 
-from oracle import pisa
+from oracle import pisa, sla
 
 rng = np.random.default_rng(17)
 
@@ -146,3 +146,111 @@ def test_query_block_subset():
     np.testing.assert_array_equal(part[rows], full[rows])
     other = np.setdiff1d(np.arange(n), rows)
     np.testing.assert_array_equal(part[other], 0.0)
+
+
+# ---------------------------------------------------------------- covariance-aware routing
+
+def test_block_deviation_brute_force_singular_values_and_spectral_bound():
+    nb, d, dv = 5, 4, 3
+    H = rng.standard_normal((nb, d, dv))
+    Hbar = H.mean(axis=0)
+    M = pisa.block_deviation(H, Hbar)
+    for j in range(nb):
+        ss = 0.0
+        for a in range(d):
+            for c in range(dv):
+                ss += (H[j, a, c] - Hbar[a, c]) ** 2
+        assert abs(M[j] - math.sqrt(ss)) < 1e-13
+        sv = np.linalg.svd(H[j] - Hbar, compute_uv=False)
+        assert abs(M[j] ** 2 - (sv ** 2).sum()) < 1e-12 * max(1.0, M[j] ** 2)
+        assert M[j] >= sv[0] - 1e-13          # bounds the spectral norm ...
+        for _ in range(20):                    # ... hence |q (H_j - Hbar)| <= |q| M_j
+            qv = rng.standard_normal(d)
+            assert np.linalg.norm(qv @ (H[j] - Hbar)) <= np.linalg.norm(qv) * M[j] + 1e-12
+    np.testing.assert_array_equal(pisa.block_deviation(np.tile(H[:1], (nb, 1, 1)), H[0]), 0.0)
+
+
+def test_covariance_logits_brute_force():
+    nq, nkb, d = 3, 5, 8
+    qp, kp = rng.standard_normal((nq, d)), rng.standard_normal((nkb, d))
+    M = rng.uniform(0, 50, nkb)
+    got = pisa.covariance_logits(qp, kp, M)
+    for i in range(nq):
+        qn = math.sqrt(sum(x * x for x in qp[i]))
+        for j in range(nkb):
+            s = sum(qp[i, a] * kp[j, a] for a in range(d)) / math.sqrt(d)
+            want = s + math.log(1.0 + qn * M[j] / (math.sqrt(d) * 64))
+            assert abs(got[i, j] - want) < 1e-12
+
+
+def _signed_deviation_blocks(nb, d, n_last=64):
+    # every block: the same centred key pattern Dk and values U + W or
+    # U - W (half the blocks each), so H_j = Dk^T U +- Dk^T W, Hbar =
+    # Dk^T U and every M_j is the same non-zero number while |H_j| is not;
+    # the block means differ, so the plain logits do not tie
+    n = 64 * (nb - 1) + n_last
+    Dk = rng.standard_normal((64, d))
+    Dk -= Dk.mean(axis=0)
+    W = rng.standard_normal((64, d))
+    U = 2.0 * rng.standard_normal((64, d))
+    means = rng.standard_normal((nb, d))
+    k = np.concatenate([means[j] + Dk for j in range(nb)])[:n]
+    sign = np.array([1.0 if j % 2 == 0 else -1.0 for j in range(nb)])
+    v = np.concatenate([U + sign[j] * W for j in range(nb)])[:n]
+    q = rng.standard_normal((n, d))
+    return q, k, v
+
+
+def test_equal_deviations_give_the_plain_split():
+    q, k, v = _signed_deviation_blocks(12, 16)
+    r = pisa.route_pisa(q, k, v, 3, 4)
+    M = r["block_dev"]
+    assert M.min() > 1.0 and np.ptp(M) < 1e-9 * M.max()
+    p = sla.route(q, k, 3, 4)
+    np.testing.assert_array_equal(r["crit_idx"], p["crit_idx"])
+    np.testing.assert_array_equal(r["marg_idx"], p["marg_idx"])
+    # zero values: every M_j = 0 and the logits are the plain ones
+    r0 = pisa.route_pisa(q, k, np.zeros_like(v), 3, 4)
+    np.testing.assert_array_equal(r0["block_dev"], 0.0)
+    np.testing.assert_array_equal(r0["logits"], p["logits"])
+
+
+def test_logit_grows_with_the_block_deviation_alone():
+    nq, nkb, d = 4, 10, 8
+    qp, kp = rng.standard_normal((nq, d)), rng.standard_normal((nkb, d))
+    M = rng.uniform(10, 60, nkb)
+    base = pisa.covariance_logits(qp, kp, M)
+    M2 = M.copy()
+    M2[6] *= 1.5
+    up = pisa.covariance_logits(qp, kp, M2)
+    assert (up[:, 6] > base[:, 6]).all()
+    np.testing.assert_array_equal(np.delete(up, 6, axis=1), np.delete(base, 6, axis=1))
+    # raised far enough, a block enters every row's critical set
+    M2[6] = 1e9
+    crit, _, _ = sla.select(pisa.covariance_logits(qp, kp, M2), 2, 3)
+    assert all(6 in row for row in crit)
+
+
+def test_covariance_routing_lowers_the_piecewise_error_on_heterogeneous_blocks():
+    # four blocks whose values follow their (spread-out) keys carry large
+    # first-order matrices that the shared Hbar misses; the covariance-aware
+    # split computes them exactly and the piecewise output lands closer to
+    # dense attention than with the plain split
+    r_ = np.random.default_rng(0)
+    nb, d = 16, 16
+    n = 64 * nb
+    cen = r_.standard_normal((nb, d))
+    k = np.repeat(cen, 64, axis=0) + 0.5 * r_.standard_normal((n, d))
+    q = np.repeat(cen[r_.permutation(nb)], 64, axis=0) * 0.8 + 0.5 * r_.standard_normal((n, d))
+    v = r_.standard_normal((n, d))
+    W = r_.standard_normal((d, d))
+    for j in r_.choice(nb, 4, replace=False):
+        a, b = 64 * j, 64 * j + 64
+        k[a:b] += 2.0 * r_.standard_normal((64, d))
+        v[a:b] = (k[a:b] - k[a:b].mean(axis=0)) @ W * 0.5
+    ref = _dense(q, k, v)
+    plain = sla.route(q, k, 3, 0)["crit_idx"]
+    cov = pisa.route_pisa(q, k, v, 3, 0)["crit_idx"]
+    e_plain = np.linalg.norm(pisa.pisa_head(q, k, v, plain)[0] - ref) / np.linalg.norm(ref)
+    e_cov = np.linalg.norm(pisa.pisa_head(q, k, v, cov)[0] - ref) / np.linalg.norm(ref)
+    assert e_cov < 0.6 * e_plain, (e_cov, e_plain)
