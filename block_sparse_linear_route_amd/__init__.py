@@ -29,6 +29,7 @@ from .ops import (  # noqa: F401
     residual_sums,
     route,
     route_noalloc,
+    route_pisa,
     sla_attention,
     version,
     workspace_size,

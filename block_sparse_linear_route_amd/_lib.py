@@ -21,7 +21,7 @@ SLA_ERR_NO_DEVICE = -5
 SLA_F32, SLA_BF16 = 0, 1
 SLA_STATIC_SCRATCH_BYTES = 64 << 20
 (OP_ROUTE, OP_LINEAR_STATES, OP_FORWARD, OP_QUANTIZE_FP8, OP_FORWARD_FP8, OP_ROUTE_TAYLOR,
- OP_FORWARD_PISA, OP_BACKWARD) = range(8)
+ OP_FORWARD_PISA, OP_BACKWARD, OP_ROUTE_PISA) = range(9)
 
 
 class Problem(ctypes.Structure):
@@ -67,6 +67,8 @@ SIGNATURES = {
     "sla_pisa_statistics": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sla_forward_attend_pisa": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                                _vp]),
+    "sla_route_pisa": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _sz, _vp]),
     "sla_forward_pisa": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sla_backward": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _sz, _vp]),

@@ -210,6 +210,14 @@ PisaWs carve_pisa_ws(const sla::Geometry& g, void* ws) {
   return w;
 }
 
+// Covariance-aware routing workspace: [PISA workspace, so that the
+// statistics serve sla_forward_attend_pisa][route regions][Hbar f32
+// B*H*d*d][M_j f64 B*H*nkb]
+size_t route_pisa_ws(const sla::Geometry& g) {
+  const size_t bh = static_cast<size_t>(g.B) * g.H;
+  return pisa_ws(g) + route_ws(g) + align_up(bh * g.D * g.D * 4) + align_up(bh * g.nkb * 8);
+}
+
 // Backward workspace: [forward workspace][O scratch, problem layout]
 // [O_s f32][O_l f32][lse f32 B*H*N][D_t f32 B*H*N]
 // [dS|dsigma bf16 B*H*nq*(d*d + d)][dH|dz bf16 B*H*nkb*(d*d + d)]
@@ -310,6 +318,7 @@ int sla_workspace_size(const sla_problem* problem, int op, size_t* bytes) {
     case SLA_OP_ROUTE_TAYLOR: *bytes = route_taylor_ws(g); return SLA_OK;
     case SLA_OP_FORWARD_PISA: *bytes = pisa_ws(g); return SLA_OK;
     case SLA_OP_BACKWARD: *bytes = backward_ws(g); return SLA_OK;
+    case SLA_OP_ROUTE_PISA: *bytes = route_pisa_ws(g); return SLA_OK;
     default: return fail(SLA_ERR_INVALID_ARGUMENT, "unknown op %d", op);
   }
 }
@@ -650,6 +659,40 @@ int sla_pisa_statistics(const sla_problem* problem, const void* k, const void* v
   return launched(sla::launch_pisa_stats(g, k, v, w.kbar, w.vbar, w.hbar, w.part, hbar,
                                          static_cast<hipStream_t>(stream)),
                   "PISA statistics launch");
+}
+
+int sla_route_pisa(const sla_problem* problem, const void* q, const void* k, const void* v,
+                   int32_t* crit_idx, int32_t* marg_idx, int8_t* block_class, float* block_logits,
+                   float* pooled_q, float* pooled_k, float* block_dev, void* ws, size_t ws_bytes,
+                   void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(q, 16);
+  SLA_REQ(k, 16);
+  SLA_REQ(v, 16);
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  if (problem->k_marg > 0) SLA_REQ(marg_idx, 4);
+  SLA_OPT(block_logits, 4);
+  SLA_OPT(pooled_q, 4);
+  SLA_OPT(pooled_k, 4);
+  SLA_OPT(block_dev, 4);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, route_pisa_ws(g)));
+  SLA_TRY(check_device());
+  const PisaWs w = carve_pisa_ws(g, ws);
+  const size_t bh = static_cast<size_t>(g.B) * g.H;
+  char* p = static_cast<char*>(ws) + pisa_ws(g);
+  double* qpool = reinterpret_cast<double*>(p);
+  double* kpool_t = reinterpret_cast<double*>(p + route_region(g));
+  float* hbar_f32 = reinterpret_cast<float*>(p + route_ws(g));
+  double* mdev = reinterpret_cast<double*>(p + route_ws(g) + align_up(bh * g.D * g.D * 4));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  SLA_TRY(launched(sla::launch_pisa_stats(g, k, v, w.kbar, w.vbar, w.hbar, w.part, hbar_f32, st),
+                   "PISA statistics launch"));
+  SLA_TRY(launched(sla::launch_pisa_deviation(g, k, v, w.hbar, w.part, hbar_f32, mdev, block_dev, st),
+                   "PISA block deviation launch"));
+  return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
+                                    pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr, st, mdev),
+                  "sla_route_pisa launch");
 }
 
 int sla_forward_attend_pisa(const sla_problem* problem, const void* q, const void* k,

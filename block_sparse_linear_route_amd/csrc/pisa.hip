@@ -162,11 +162,17 @@ pisa_stats_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g, 
 // computes the key-sum tile its first B operand covers and the value-sum
 // tile of ct; the key sums reach the other waves through LDS one block later
 // (after the next barrier), so each block costs one barrier.
-template <int D>
+//
+// DEV (covariance-aware routing): the same per-block products, but each
+// block's H_j is finished on its own (the accumulators restart at every
+// block) and reduced to M_j = sqrt(sum (H_j - Hbar)^2) against the float32
+// Hbar of an earlier pass; nothing else is written.
+template <int D, bool DEV = false>
 __global__ void __launch_bounds__(kThreads, 2)
 pisa_stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, Geometry g,
                        int G, int npb, uint16_t* __restrict__ kbar, uint16_t* __restrict__ vbar,
-                       float* __restrict__ part) {
+                       float* __restrict__ part, const float* __restrict__ hbar_f32 = nullptr,
+                       double* __restrict__ mdev = nullptr, float* __restrict__ mdev_out = nullptr) {
   constexpr int CH = D / 8;                 // 16-byte chunks per row
   constexpr int RPI = 64 / CH;              // rows per 64-lane load instruction
   constexpr int IPW = (kBlock / 4) / RPI;   // load instructions per wave per tile
@@ -177,6 +183,7 @@ pisa_stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restric
   // carry no false dependence on the loads filling the other
   __shared__ __attribute__((aligned(16))) uint16_t k0[TILE], v0[TILE], k1[TILE], v1[TILE];
   __shared__ float ksum[2][D], vsum[2][D];
+  __shared__ float devp[4];
 
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int nch = gridDim.x;
@@ -247,6 +254,18 @@ pisa_stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restric
 #pragma unroll
   for (int u = 0; u < NT; ++u) acc[u] = zero16();
   f32x16 vs_prev = zero16();
+  // DEV: this lane's elements of Hbar, in the accumulator layout
+  [[maybe_unused]] f32x16 hb[DEV ? NT : 1];
+  if constexpr (DEV) {
+    const float* hsrc = hbar_f32 + static_cast<int64_t>(bh) * D * D;
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = ct * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        hb[u][r] = hsrc[c * D + (at0 + u) * 32 + l32];
+      }
+  }
 
   // rank-one term and means of block it (sums in LDS buffer it & 1, value
   // sums of this wave's rows in vs_prev)
@@ -260,9 +279,33 @@ pisa_stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[u][r] = fmaf(-vs_prev[r], ka, acc[u][r]);
     }
-    const int64_t orow = (static_cast<int64_t>(bh) * npb * kBlock + j) * D;
-    if (t < D) kbar[orow + t] = f32_to_bf16_bits(ks[t] * inv_n);
-    else if (t < 2 * D) vbar[orow + t - D] = f32_to_bf16_bits(vsum[it & 1][t - D] * inv_n);
+    if constexpr (DEV) {
+      // acc holds H_j of this block alone: sum of squared deviations from
+      // Hbar over the wave's tiles, then over the lanes and the four waves
+      float ss = 0.0f;
+#pragma unroll
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float dl = acc[u][r] - hb[u][r];
+          ss = fmaf(dl, dl, ss);
+          acc[u][r] = 0.0f;
+        }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+      if (lane == 0) devp[wave] = ss;
+      __syncthreads();
+      if (t == 0) {
+        const double tot = (static_cast<double>(devp[0]) + devp[1]) + (static_cast<double>(devp[2]) + devp[3]);
+        const double m = sqrt(tot);
+        mdev[static_cast<int64_t>(bh) * g.nkb + j] = m;
+        if (mdev_out) mdev_out[static_cast<int64_t>(bh) * g.nkb + j] = static_cast<float>(m);
+      }
+    } else {
+      const int64_t orow = (static_cast<int64_t>(bh) * npb * kBlock + j) * D;
+      if (t < D) kbar[orow + t] = f32_to_bf16_bits(ks[t] * inv_n);
+      else if (t < 2 * D) vbar[orow + t - D] = f32_to_bf16_bits(vsum[it & 1][t - D] * inv_n);
+    }
   };
 
   auto body = [&](auto xc, int it) {
@@ -308,6 +351,7 @@ pisa_stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restric
   }
   __syncthreads();
   if (nblk > 0) finish_block(nblk - 1);
+  if constexpr (DEV) return;
 
   float* dst = part + (static_cast<int64_t>(bh) * nch + chunk) * D * D;
 #pragma unroll
@@ -317,6 +361,116 @@ pisa_stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restric
       const int c = ct * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
       dst[c * D + (at0 + u) * 32 + l32] = acc[u][r];
     }
+  }
+}
+
+// Float32 first-order matrices for covariance-aware routing (any input
+// type, float32 arithmetic throughout, no bf16 rounding of the operands).
+// grid (chunks of G blocks, B*H); per block the K and V tiles go to LDS as
+// float32 with the keys centred on their block mean (rows past a short last
+// block are 0), and thread t accumulates the (D/16) x (D/16) elements
+// a in [a0, a0 + D/16), c in [c0, c0 + D/16) of sum_n (k_n - kbar)[a] v_n[c].
+// SUM: the chunk's sum of H_j goes to part (value-major, as the statistics
+// kernels write it) for pisa_reduce_kernel.  DEV: each block's
+// M_j = sqrt(sum (H_j - Hbar)^2) against hbar_f32 goes to mdev (float64) and
+// mdev_out (float32, optional).
+template <typename T, int D, bool DEV>
+__global__ void __launch_bounds__(kThreads)
+pisa_first_order_f32_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g, int G,
+                            float* __restrict__ part, const float* __restrict__ hbar_f32,
+                            double* __restrict__ mdev, float* __restrict__ mdev_out) {
+  constexpr int AW = D / 16;
+  __shared__ float kc[kBlock][D];
+  __shared__ float vv[kBlock][D];
+  __shared__ float mk[D];
+  __shared__ double red[4];
+  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const int nch = gridDim.x;
+  const int b = bh / g.H, h = bh % g.H;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int a0 = (t / 16) * AW, c0 = (t % 16) * AW;
+  const int j0 = chunk * G, j1 = min(j0 + G, g.nkb);
+  const T* kh = k + b * g.sb + h * g.sh;
+  const T* vh = v + b * g.sb + h * g.sh;
+  float acc[AW][AW];
+#pragma unroll
+  for (int x = 0; x < AW; ++x)
+#pragma unroll
+    for (int y = 0; y < AW; ++y) acc[x][y] = 0.0f;
+  [[maybe_unused]] float hb[DEV ? AW : 1][DEV ? AW : 1];
+  if constexpr (DEV) {
+    const float* hs = hbar_f32 + static_cast<int64_t>(bh) * D * D;
+#pragma unroll
+    for (int x = 0; x < AW; ++x)
+#pragma unroll
+      for (int y = 0; y < AW; ++y) hb[x][y] = hs[(c0 + y) * D + a0 + x];
+  }
+  for (int j = j0; j < j1; ++j) {
+    const int nj = min(kBlock, g.N - j * kBlock);
+    for (int e = t; e < kBlock * D; e += kThreads) {
+      const int n = e / D, f = e % D;
+      const int64_t off = static_cast<int64_t>(j * kBlock + n) * g.sn + f;
+      float kx = 0.0f, vx = 0.0f;
+      if (n < nj) {
+        if constexpr (sizeof(T) == 2) {
+          kx = bf16_to_f32(reinterpret_cast<const uint16_t*>(kh)[off]);
+          vx = bf16_to_f32(reinterpret_cast<const uint16_t*>(vh)[off]);
+        } else {
+          kx = kh[off];
+          vx = vh[off];
+        }
+      }
+      kc[n][f] = kx;
+      vv[n][f] = vx;
+    }
+    __syncthreads();
+    if (t < D) {
+      float sm = 0.0f;
+      for (int n = 0; n < nj; ++n) sm += kc[n][t];
+      mk[t] = sm / static_cast<float>(nj);
+    }
+    __syncthreads();
+    for (int e = t; e < nj * D; e += kThreads) kc[e / D][e % D] -= mk[e % D];
+    __syncthreads();
+    for (int n = 0; n < nj; ++n) {
+      float ka[AW], vc[AW];
+#pragma unroll
+      for (int x = 0; x < AW; ++x) ka[x] = kc[n][a0 + x];
+#pragma unroll
+      for (int y = 0; y < AW; ++y) vc[y] = vv[n][c0 + y];
+#pragma unroll
+      for (int x = 0; x < AW; ++x)
+#pragma unroll
+        for (int y = 0; y < AW; ++y) acc[x][y] = fmaf(ka[x], vc[y], acc[x][y]);
+    }
+    if constexpr (DEV) {
+      double ss = 0.0;
+#pragma unroll
+      for (int x = 0; x < AW; ++x)
+#pragma unroll
+        for (int y = 0; y < AW; ++y) {
+          const double dl = static_cast<double>(acc[x][y]) - hb[x][y];
+          ss = fma(dl, dl, ss);
+          acc[x][y] = 0.0f;
+        }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+      if (lane == 0) red[wave] = ss;
+      __syncthreads();
+      if (t == 0) {
+        const double m = sqrt((red[0] + red[1]) + (red[2] + red[3]));
+        mdev[static_cast<int64_t>(bh) * g.nkb + j] = m;
+        if (mdev_out) mdev_out[static_cast<int64_t>(bh) * g.nkb + j] = static_cast<float>(m);
+      }
+    }
+    __syncthreads();   // every thread is past this block's LDS reads
+  }
+  if constexpr (!DEV) {
+    float* dst = part + (static_cast<int64_t>(bh) * nch + chunk) * D * D;
+#pragma unroll
+    for (int x = 0; x < AW; ++x)
+#pragma unroll
+      for (int y = 0; y < AW; ++y) dst[(c0 + y) * D + a0 + x] = acc[x][y];
   }
 }
 
@@ -371,7 +525,44 @@ void launch_pisa_stats_t(const Geometry& g, const void* k, const void* v, int G,
                      part, nch, g.nkb, hbar, hbar_f32);
 }
 
+template <typename T, int D>
+void launch_pisa_dev_t(const Geometry& g, const void* k, const void* v, int G, int nch,
+                       uint16_t* hbar, float* part, float* hbar_f32, double* mdev,
+                       float* mdev_out, hipStream_t stream) {
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((pisa_stats_bf16_kernel<D, true>), dim3(nch, g.B * g.H), dim3(kThreads), 0,
+                       stream, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), g, G,
+                       pisa_pseudo_blocks(g), nullptr, nullptr, nullptr, hbar_f32, mdev, mdev_out);
+  } else {
+    // float32 inputs: Hbar again from float32 operands (the statistics
+    // kernel rounds its centred operands to bf16), then the deviations
+    hipLaunchKernelGGL((pisa_first_order_f32_kernel<T, D, false>), dim3(nch, g.B * g.H), dim3(kThreads),
+                       0, stream, static_cast<const T*>(k), static_cast<const T*>(v), g, G, part,
+                       nullptr, nullptr, nullptr);
+    hipLaunchKernelGGL((pisa_reduce_kernel<D>), dim3(D * D / 256, g.B * g.H), dim3(kThreads), 0, stream,
+                       part, nch, g.nkb, hbar, hbar_f32);
+    hipLaunchKernelGGL((pisa_first_order_f32_kernel<T, D, true>), dim3(nch, g.B * g.H), dim3(kThreads),
+                       0, stream, static_cast<const T*>(k), static_cast<const T*>(v), g, G, nullptr,
+                       hbar_f32, mdev, mdev_out);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pisa_deviation(const Geometry& g, const void* k, const void* v, uint16_t* hbar,
+                                 float* part, float* hbar_f32, double* mdev, float* mdev_out,
+                                 hipStream_t stream) {
+  const int G = pisa_chunk_blocks(g);
+  const int nch = (g.nkb + G - 1) / G;
+  if (g.dtype == 1) {
+    if (g.D == 128) launch_pisa_dev_t<uint16_t, 128>(g, k, v, G, nch, hbar, part, hbar_f32, mdev, mdev_out, stream);
+    else launch_pisa_dev_t<uint16_t, 64>(g, k, v, G, nch, hbar, part, hbar_f32, mdev, mdev_out, stream);
+  } else {
+    if (g.D == 128) launch_pisa_dev_t<float, 128>(g, k, v, G, nch, hbar, part, hbar_f32, mdev, mdev_out, stream);
+    else launch_pisa_dev_t<float, 64>(g, k, v, G, nch, hbar, part, hbar_f32, mdev, mdev_out, stream);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_pisa_stats(const Geometry& g, const void* k, const void* v, uint16_t* kbar,
                              uint16_t* vbar, uint16_t* hbar, float* part, float* hbar_f32,

@@ -304,20 +304,24 @@ __device__ __forceinline__ void select_row(const uint64_t* rk, int nkb, int lane
 // against them, so each pooled-K value read serves R logits; the pooled-Q
 // rows are uniform across the workgroup and are read as scalar operands,
 // each serving two logits.  Results go to LDS as keys.
-// TAYLOR accumulates the second-order term beside the dot product, from the
+// SCORE selects the logit: 0 the plain pooled dot product; 1 (second-order
+// score) accumulates the second-order term beside the dot product, from the
 // same scalar pooled-Q values squared and the block variances laid out like
 // the pooled K.
 // Phase 2: one wave per query block (select_row).
 constexpr int kFC = 4;
 
-template <int R, int KPL, bool TAYLOR>
+template <int R, int KPL, int SCORE>
 __global__ void __launch_bounds__(kThreads)
 select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
               const double* __restrict__ kpool_t, const double* __restrict__ kvar_t,
-              double sqrt_d, double inv_2d, int32_t* __restrict__ crit,
-              int32_t* __restrict__ marg, int8_t* __restrict__ cls,
+              const double* __restrict__ mdev, double sqrt_d, double inv_2d,
+              int32_t* __restrict__ crit, int32_t* __restrict__ marg, int8_t* __restrict__ cls,
               float* __restrict__ logits_out) {
+  constexpr bool TAYLOR = SCORE == 1;
+  constexpr bool COV = SCORE == 2;
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+  __shared__ double cq[COV ? R : 1];
   uint64_t* keys = reinterpret_cast<uint64_t*>(dyn);                 // [R][nkbp]
   uint32_t* hist = reinterpret_cast<uint32_t*>(keys + R * nkbp);      // [4][128]
 
@@ -338,6 +342,29 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
     qrow[r] = qpool + (static_cast<int64_t>(bh) * nq + min(i0 + r, nq - 1)) * D;
   const double* kt = kpool_t + static_cast<int64_t>(bh) * D * nkb;
   const double* vt = TAYLOR ? kvar_t + static_cast<int64_t>(bh) * D * nkb : nullptr;
+  if constexpr (COV) {
+    // |qbar_r| / (sqrt(d) B) per row: 256 / R threads per row, then a
+    // shuffle sum over those lanes (R = 2..8: 32..128 lanes, within a wave
+    // when R >= 4)
+    constexpr int TPR = kThreads / R;
+    const int r = t / TPR, e0 = t % TPR;
+    double ss = 0.0;
+    for (int e = e0; e < D; e += TPR) ss = fma(qrow[r][e], qrow[r][e], ss);
+    if constexpr (TPR <= 64) {
+#pragma unroll
+      for (int m = TPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+      if (e0 == 0) cq[r] = sqrt(ss) * inv_2d;
+    } else {
+      // R = 2: 128 threads per row, two waves; wave sums meet in LDS
+      __shared__ double wsum[4];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+      if (lane == 0) wsum[wave] = ss;
+      __syncthreads();
+      if (t < R) cq[t] = sqrt(wsum[2 * t] + wsum[2 * t + 1]) * inv_2d;
+    }
+    __syncthreads();
+  }
 
   // Two KV blocks per thread (j and j + 256); kFC features per step, the next
   // step's pooled-K values loaded before this step's FMAs.
@@ -410,6 +437,7 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
       for (int r = 0; r < R; ++r) {
         double sv = acc[x][r] / sqrt_d;
         if constexpr (TAYLOR) sv += log1p(acc2[x][r] * inv_2d);
+        if constexpr (COV) sv += log1p(cq[r] * mdev[static_cast<int64_t>(bh) * nkb + jl[x]]);
         const bool ok = i0 + r < nq && j < nkb;
         keys[r * nkbp + j] = ok ? desc_key(sv) : ~0ull;
         if (ok && logits_out)
@@ -427,24 +455,26 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
   }
 }
 
-template <int R, int KPL, bool TAYLOR>
+template <int R, int KPL, int SCORE>
 hipError_t launch_select_rk(const Geometry& g, int nkbp, const double* qpool,
-                            const double* kpool_t, const double* kvar_t, int32_t* crit,
-                            int32_t* marg, int8_t* cls, float* logits, hipStream_t stream) {
+                            const double* kpool_t, const double* kvar_t, const double* mdev,
+                            int32_t* crit, int32_t* marg, int8_t* cls, float* logits,
+                            hipStream_t stream) {
   const size_t lds = static_cast<size_t>(R) * nkbp * 8 + 4 * 128 * 4;
   if (lds > 65536) {
     // more than 64 KB of dynamic LDS has to be allowed for the kernel (on
     // the current device)
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<R, KPL, TAYLOR>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<R, KPL, SCORE>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
   dim3 grid(((g.nq + R - 1) / R) * g.B * g.H);
   const double sqrt_d = __builtin_sqrt(static_cast<double>(g.D));
-  const double inv_2d = 1.0 / (2.0 * g.D);
-  hipLaunchKernelGGL((select_kernel<R, KPL, TAYLOR>), grid, dim3(kThreads), lds, stream, g, nkbp,
-                     qpool, kpool_t, kvar_t, sqrt_d, inv_2d, crit, marg, cls, logits);
+  // second-order score: 1 / (2 d); covariance score: 1 / (sqrt(d) B)
+  const double inv_2d = SCORE == 2 ? 1.0 / (sqrt_d * kBlock) : 1.0 / (2.0 * g.D);
+  hipLaunchKernelGGL((select_kernel<R, KPL, SCORE>), grid, dim3(kThreads), lds, stream, g, nkbp,
+                     qpool, kpool_t, kvar_t, mdev, sqrt_d, inv_2d, crit, marg, cls, logits);
   return hipGetLastError();
 }
 
@@ -453,20 +483,20 @@ hipError_t launch_select_rk(const Geometry& g, int nkbp, const double* qpool,
 // within 64 KB of LDS and several workgroups share a CU (the kernel is
 // latency-bound; at nkb = 1182 four rows measured faster than eight).  Keys
 // per lane cover the row (nkb <= 4096).
-template <bool TAYLOR>
+template <int SCORE>
 hipError_t launch_select(const Geometry& g, const double* qpool, const double* kpool_t,
-                         const double* kvar_t, int32_t* crit, int32_t* marg, int8_t* cls,
-                         float* logits, hipStream_t stream) {
+                         const double* kvar_t, const double* mdev, int32_t* crit, int32_t* marg,
+                         int8_t* cls, float* logits, hipStream_t stream) {
   const int nkbp = (g.nkb + 63) / 64 * 64;
   if (nkbp <= 128)
-    return launch_select_rk<8, 2, TAYLOR>(g, nkbp, qpool, kpool_t, kvar_t, crit, marg, cls, logits, stream);
+    return launch_select_rk<8, 2, SCORE>(g, nkbp, qpool, kpool_t, kvar_t, mdev, crit, marg, cls, logits, stream);
   if (nkbp <= 512)
-    return launch_select_rk<8, 8, TAYLOR>(g, nkbp, qpool, kpool_t, kvar_t, crit, marg, cls, logits, stream);
+    return launch_select_rk<8, 8, SCORE>(g, nkbp, qpool, kpool_t, kvar_t, mdev, crit, marg, cls, logits, stream);
   if (nkbp <= 1024)
-    return launch_select_rk<8, 16, TAYLOR>(g, nkbp, qpool, kpool_t, kvar_t, crit, marg, cls, logits, stream);
+    return launch_select_rk<8, 16, SCORE>(g, nkbp, qpool, kpool_t, kvar_t, mdev, crit, marg, cls, logits, stream);
   if (nkbp <= 2048)
-    return launch_select_rk<4, 32, TAYLOR>(g, nkbp, qpool, kpool_t, kvar_t, crit, marg, cls, logits, stream);
-  return launch_select_rk<2, 64, TAYLOR>(g, nkbp, qpool, kpool_t, kvar_t, crit, marg, cls, logits, stream);
+    return launch_select_rk<4, 32, SCORE>(g, nkbp, qpool, kpool_t, kvar_t, mdev, crit, marg, cls, logits, stream);
+  return launch_select_rk<2, 64, SCORE>(g, nkbp, qpool, kpool_t, kvar_t, mdev, crit, marg, cls, logits, stream);
 }
 
 template <typename T, int D>
@@ -488,7 +518,8 @@ void launch_pool_t(const Geometry& g, const void* q, const void* k, double* qpoo
 hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t* crit,
                         int32_t* marg, int8_t* cls, float* logits, float* pooled_q,
                         float* pooled_k, double* ws_qpool, double* ws_kpool_t,
-                        double* ws_kvar_t, float* key_var, hipStream_t stream) {
+                        double* ws_kvar_t, float* key_var, hipStream_t stream,
+                        const double* block_dev) {
   if (g.dtype == 1) {
     if (g.D == 128)
       launch_pool_t<uint16_t, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream);
@@ -503,8 +534,10 @@ hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ws_kvar_t)
-    return launch_select<true>(g, ws_qpool, ws_kpool_t, ws_kvar_t, crit, marg, cls, logits, stream);
-  return launch_select<false>(g, ws_qpool, ws_kpool_t, nullptr, crit, marg, cls, logits, stream);
+    return launch_select<1>(g, ws_qpool, ws_kpool_t, ws_kvar_t, nullptr, crit, marg, cls, logits, stream);
+  if (block_dev)
+    return launch_select<2>(g, ws_qpool, ws_kpool_t, nullptr, block_dev, crit, marg, cls, logits, stream);
+  return launch_select<0>(g, ws_qpool, ws_kpool_t, nullptr, nullptr, crit, marg, cls, logits, stream);
 }
 
 }  // namespace sla

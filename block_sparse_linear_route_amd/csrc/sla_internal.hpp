@@ -25,11 +25,14 @@ constexpr size_t kStaticScratchBytes = size_t(64) << 20;
 hipError_t static_scratch(void** ptr);
 
 // ws_kvar_t non-null: second-order routing score (block key variances pooled
-// into it, and into key_var as float32 when that is non-null).
+// into it, and into key_var as float32 when that is non-null).  block_dev
+// non-null (and ws_kvar_t null): covariance-aware score, block_dev holding
+// the float64 deviation norms M_j [B*H][nkb].
 hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t* crit,
                         int32_t* marg, int8_t* cls, float* logits, float* pooled_q,
                         float* pooled_k, double* ws_qpool, double* ws_kpool_t,
-                        double* ws_kvar_t, float* key_var, hipStream_t stream);
+                        double* ws_kvar_t, float* key_var, hipStream_t stream,
+                        const double* block_dev = nullptr);
 
 // exp_map: phi(k) = exp(k) elementwise instead of the softmax over features.
 hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16_t* h_states,
@@ -84,6 +87,14 @@ inline int pisa_chunks(const Geometry& g) {
 hipError_t launch_pisa_stats(const Geometry& g, const void* k, const void* v, uint16_t* kbar,
                              uint16_t* vbar, uint16_t* hbar, float* part, float* hbar_f32,
                              hipStream_t stream);
+// Covariance-aware routing statistics, after launch_pisa_stats wrote
+// hbar_f32: mdev [B*H][nkb] float64 (and mdev_out float32, optional)
+// receives M_j = || H_j - Hbar || (all d x d elements).  For float32 inputs
+// Hbar (hbar, hbar_f32) is first recomputed from float32 operands through
+// part.
+hipError_t launch_pisa_deviation(const Geometry& g, const void* k, const void* v, uint16_t* hbar,
+                                 float* part, float* hbar_f32, double* mdev, float* mdev_out,
+                                 hipStream_t stream);
 // The fused pass: exact online softmax over the critical blocks, then the
 // centroid pseudo-blocks in the same softmax, then the first-order
 // correction; o_softmax / o_correction (float, optional) are the two parts

@@ -134,6 +134,40 @@ def route(q: torch.Tensor, k: torch.Tensor, k_crit: int, k_marg: int, *, want_cl
     return out
 
 
+def route_pisa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_crit: int, k_marg: int, *,
+               want_class: bool = False, want_logits: bool = False, want_pooled: bool = False,
+               want_dev: bool = False, workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """``sla_route_pisa``: covariance-aware routing for piecewise attention.
+    Returns the route's outputs (``block_dev`` = M_j when ``want_dev``) and
+    ``_workspace``, whose leading bytes hold the piecewise statistics that
+    ``forward_attend_pisa`` can run from."""
+    k, v = _same_layout(q, k, v)
+    p = make_problem(q, k_crit, k_marg)
+    B, H, N, d = q.shape
+    nb = num_blocks(N)
+    dev = q.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(crit_idx=torch.empty((B, H, nb, k_crit), **i32),
+               marg_idx=torch.empty((B, H, nb, k_marg), **i32))
+    if want_class:
+        out["block_class"] = torch.empty((B, H, nb, nb), dtype=torch.int8, device=dev)
+    if want_logits:
+        out["block_logits"] = torch.empty((B, H, nb, nb), dtype=torch.float32, device=dev)
+    if want_pooled:
+        out["pooled_q"] = torch.empty((B, H, nb, d), dtype=torch.float32, device=dev)
+        out["pooled_k"] = torch.empty((B, H, nb, d), dtype=torch.float32, device=dev)
+    if want_dev:
+        out["block_dev"] = torch.empty((B, H, nb), dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else _workspace(p, _lib.OP_ROUTE_PISA, dev)
+    _check(lib.sla_route_pisa(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out["crit_idx"]),
+                              _ptr(out["marg_idx"]), _ptr(out.get("block_class")),
+                              _ptr(out.get("block_logits")), _ptr(out.get("pooled_q")),
+                              _ptr(out.get("pooled_k")), _ptr(out.get("block_dev")), _ptr(ws),
+                              ws.numel(), _stream(stream)))
+    out["_workspace"] = ws
+    return out
+
+
 def route_noalloc(q: torch.Tensor, k: torch.Tensor, k_crit: int, k_marg: int, *,
                   want_class: bool = False, want_logits: bool = False, want_pooled: bool = False,
                   out: Optional[dict] = None, stream=None) -> dict:

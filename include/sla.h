@@ -93,7 +93,8 @@ typedef enum sla_op {
   SLA_OP_FORWARD_FP8 = 4,
   SLA_OP_ROUTE_TAYLOR = 5,
   SLA_OP_FORWARD_PISA = 6,
-  SLA_OP_BACKWARD = 7
+  SLA_OP_BACKWARD = 7,
+  SLA_OP_ROUTE_PISA = 8
 } sla_op;
 
 /* Problem description (host struct, read only during the call).
@@ -351,6 +352,35 @@ int sla_forward_attend_pisa(const sla_problem* problem, const void* q, const voi
 int sla_forward_pisa(const sla_problem* problem, const void* q, const void* k,
                      const void* v, const int32_t* crit_idx, void* o, float* o_softmax,
                      float* o_correction, void* ws, size_t ws_bytes, void* stream);
+
+/* Covariance-aware block routing for piecewise attention.  [PISA summary,
+ * section 2, "Enrutamiento Consciente de la Covarianza": the selection score
+ * of a block takes in, beside its attention score, the norm
+ * M_j = ||H_j - Hbar|| of its first-order matrix's deviation from the
+ * shared Hbar]
+ * An unselected block replaces its own first-order term by Hbar, so the
+ * numerator misses alpha_tj (q_t / sqrt(d)) (H_j - Hbar), of norm at most
+ * alpha_tj (|q_t| / sqrt(d)) M_j.  The logit weighs the block's zero-order
+ * weight by one plus that discrepancy per token of a 64-token block, with
+ * the pooled query:
+ *   s_ij = qbar_i . kbar_j / sqrt(d) + log1p(|qbar_i| M_j / (sqrt(d) * 64)),
+ * M_j the L2 norm of all d x d elements (Frobenius; it bounds the spectral
+ * norm), H_j = sum_n (k_n - kbar_j)^T v_n, Hbar their mean over all KV
+ * blocks.  The split, counts, tie rule and outputs are those of sla_route.
+ * q, k, v      input [B,H,N,d] (problem strides and dtype)
+ * crit_idx ... pooled_k   as for sla_route
+ * block_dev    out float [B,H,nkb] or NULL: M_j rounded to float32
+ * ws           workspace of sla_workspace_size(SLA_OP_ROUTE_PISA) bytes; its
+ *              first sla_workspace_size(SLA_OP_FORWARD_PISA) bytes then hold
+ *              the statistics of sla_pisa_statistics for the same k and v,
+ *              so sla_forward_attend_pisa can run from it directly.
+ * Pooled means, ||qbar_i||, M_j and the logits are float64 (H_j in float32:
+ * matrix-core sums of the exact bf16 products, or float32 arithmetic for
+ * float inputs). */
+int sla_route_pisa(const sla_problem* problem, const void* q, const void* k, const void* v,
+                   int32_t* crit_idx, int32_t* marg_idx, int8_t* block_class,
+                   float* block_logits, float* pooled_q, float* pooled_k, float* block_dev,
+                   void* ws, size_t ws_bytes, void* stream);
 
 /* Backward pass of sla_forward for fixed block lists.  [SLA abstract
  * (forward and backward); SLA2 summary 2.A (the mix)]
