@@ -145,18 +145,20 @@ int launched(hipError_t e, const char* what) {
   } while (0)
 
 // Forward workspace: [S bf16 B*H*nq*d*d][sigma f32 B*H*nq*d]
-// [mask bits u32 B*H*ceil(nkb/64)*ceil(nq/512)*512*2]
+// [mask bits u32 B*H*ceil(nkb/64)*ceil(nq/512)*512*2][z parts bf16 B*H*nkb*2d]
 struct FwdWs {
   uint16_t* s_sum;
   float* sigma;
   uint32_t* bits;
+  uint16_t* zhl;
 };
 
 size_t forward_ws(const sla::Geometry& g) {
   const size_t rows = static_cast<size_t>(g.B) * g.H * g.nq;
   const size_t bit_words = static_cast<size_t>(g.B) * g.H * sla::marginal_chunks(g) *
                            sla::marginal_rows_pad(g) * 2;
-  return align_up(rows * g.D * g.D * 2) + align_up(rows * g.D * 4) + align_up(bit_words * 4);
+  return align_up(rows * g.D * g.D * 2) + align_up(rows * g.D * 4) + align_up(bit_words * 4) +
+         align_up(static_cast<size_t>(g.B) * g.H * g.nkb * 2 * g.D * 2);
 }
 
 FwdWs carve_forward_ws(const sla::Geometry& g, void* ws) {
@@ -168,6 +170,10 @@ FwdWs carve_forward_ws(const sla::Geometry& g, void* ws) {
   w.sigma = reinterpret_cast<float*>(p);
   p += align_up(rows * g.D * 4);
   w.bits = reinterpret_cast<uint32_t*>(p);
+  const size_t bit_words = static_cast<size_t>(g.B) * g.H * sla::marginal_chunks(g) *
+                           sla::marginal_rows_pad(g) * 2;
+  p += align_up(bit_words * 4);
+  w.zhl = reinterpret_cast<uint16_t*>(p);
   return w;
 }
 
@@ -439,7 +445,7 @@ int sla_forward(const sla_problem* problem, const void* q, const void* k, const 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.k_marg > 0)
     SLA_TRY(launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
-                                               z_states, w.s_sum, w.sigma, w.bits, false, s),
+                                               z_states, w.s_sum, w.sigma, w.bits, w.zhl, false, s),
                      "marginal-sum launch"));
   return launched(sla::launch_attention(g, q, k, v, crit_idx, w.s_sum, w.sigma, alpha, o, o_sparse,
                                         o_linear, false, s),
@@ -460,7 +466,7 @@ int sla_marginal_sums(const sla_problem* problem, const int32_t* marg_idx, const
   if (g.k_marg == 0) return SLA_OK;
   const FwdWs w = carve_forward_ws(g, ws);
   return launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
-                                            z_states, w.s_sum, w.sigma, w.bits, false,
+                                            z_states, w.s_sum, w.sigma, w.bits, w.zhl, false,
                                             static_cast<hipStream_t>(stream)),
                   "marginal-sum launch");
 }
@@ -547,7 +553,7 @@ int sla_forward_fp8(const sla_problem* problem, const void* q, const uint8_t* q8
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (g.k_marg > 0)
     SLA_TRY(launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
-                                               z_states, w.s_sum, w.sigma, w.bits, false, s),
+                                               z_states, w.s_sum, w.sigma, w.bits, w.zhl, false, s),
                      "marginal-sum launch"));
   return launched(sla::launch_attention_fp8(g, q, q8, q_s, k8, k_s, v8, v_s, crit_idx, w.s_sum,
                                             w.sigma, alpha, o, o_sparse, o_linear, s),
@@ -611,7 +617,7 @@ int sla_residual_sums(const sla_problem* problem, const int32_t* crit_idx, const
   if (g.k_marg == 0) return SLA_OK;
   const FwdWs w = carve_forward_ws(g, ws);
   return launched(sla::launch_marginal_sums(g, crit_idx, static_cast<const uint16_t*>(h_states),
-                                            nullptr, w.s_sum, nullptr, w.bits, true,
+                                            nullptr, w.s_sum, nullptr, w.bits, w.zhl, true,
                                             static_cast<hipStream_t>(stream)),
                   "residual-sum launch");
 }
@@ -734,7 +740,7 @@ static int backward_forward_part(const sla::Geometry& g, const void* q, const vo
   if (g.k_marg > 0)
     SLA_TRY(launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
                                                z_states, w.fwd.s_sum, w.fwd.sigma, w.fwd.bits,
-                                               false, st),
+                                               w.fwd.zhl, false, st),
                      "backward marginal sums"));
   return launched(sla::launch_attention(g, q, k, v, crit_idx, w.fwd.s_sum, w.fwd.sigma, alpha, o,
                                         const_cast<float*>(w.b.o_s), const_cast<float*>(w.b.o_l),

@@ -13,8 +13,12 @@
 //
 // Kernel 1 (a few query blocks per workgroup) writes the mask as bit rows,
 // laid out chunk-major (64 KV blocks per chunk, two 32-bit words per row) so
-// that a chunk's bits for 512 rows are one contiguous 4 KB piece, and sums
-// sigma_i directly in float32 (ascending j) from the index lists.
+// that a chunk's bits for 512 rows are one contiguous 4 KB piece, and splits
+// each z_j into two bf16 parts hi + lo (hi = bf16(z), lo = bf16(z - hi)).
+// sigma_i = sum_j M[i, j] (hi_j + lo_j) then comes out of the same product
+// as S (the parts are exact bf16 values, the sums float32): its float32 sum
+// differs from the sum of the float32 z_j by the rounding of lo, about
+// 2^-17 of z.
 //
 // Kernel 2 computes S^T tiles of 64 columns x 512 rows per workgroup, so H is
 // streamed from HBM once per head for nq <= 512.  Each 64-block chunk of H
@@ -39,20 +43,21 @@ constexpr int kStages = 3;                // 3 to 6
 constexpr int kHBytes = kGK * kGN * 2;    // H chunk bytes (8 KB)
 
 // grid (ceil(nq / RPB), B*H), RPB = 256 / D query blocks per workgroup,
-// thread (row, feature a).  Two products of each row's marginal list:
-//  * sigma_i = sum_{j in M_i} z_j in float32, ascending j; the z rows are
-//    gathered 16 at a time (the list entries are uniform per wave, so they
-//    come as scalar loads) and added in list order;
-//  * the mask bit row, OR-ed together in LDS and written chunk-major: word w
-//    of row i lands at [(w / 2) * rows_pad + i] * 2 + w % 2.
+// thread (row, feature a):
+//  * the mask bit row of each row's marginal list, OR-ed together in LDS and
+//    written chunk-major: word w of row i lands at
+//    [(w / 2) * rows_pad + i] * 2 + w % 2;
+//  * (nq = nkb) the z row of KV block j = i as bf16 parts, laid out per
+//    32-feature group x as [hi of 32x .. 32x+31 | lo of the same], so that
+//    one 64-column tile of the product carries both parts of 32 features.
 //
 // COMPL: the list is each row's critical list (k_crit entries) and the bit
 // row written is its complement over the valid KV blocks (the residual set of
-// residual linear attention: every block that is not critical); no sigma.
+// residual linear attention: every block that is not critical); no z.
 template <int D, bool COMPL>
 __global__ void __launch_bounds__(kThreads)
 marg_prep_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __restrict__ zs,
-                 float* __restrict__ sigma, uint32_t* __restrict__ bits, int nchunks,
+                 uint16_t* __restrict__ zhl, uint32_t* __restrict__ bits, int nchunks,
                  int rows_pad) {
   constexpr int RPB = kThreads / D;
   extern __shared__ uint32_t sbits[];        // [RPB][2 * nchunks]
@@ -74,17 +79,14 @@ marg_prep_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __re
     }
   }
   if constexpr (!COMPL) {
-    const float* __restrict__ zb = zs + static_cast<int64_t>(bh) * g.nkb * D + a;
-    float acc = 0.0f;
-    for (int u0 = 0; u0 < km; u0 += 16) {
-      float v[16];
-#pragma unroll
-      for (int x = 0; x < 16; ++x) v[x] = zb[static_cast<int64_t>(mrow[min(u0 + x, km - 1)]) * D];
-#pragma unroll
-      for (int x = 0; x < 16; ++x)
-        if (u0 + x < km) acc += v[x];
+    if (i < g.nkb) {
+      const float z = zs[(static_cast<int64_t>(bh) * g.nkb + i) * D + a];
+      const uint16_t hi = f32_to_bf16_bits(z);
+      const uint16_t lo = f32_to_bf16_bits(z - bf16_to_f32(hi));
+      uint16_t* zr = zhl + (static_cast<int64_t>(bh) * g.nkb + i) * 2 * D + 64 * (a >> 5) + (a & 31);
+      zr[0] = hi;
+      zr[32] = lo;
     }
-    if (row_ok) sigma[(static_cast<int64_t>(bh) * g.nq + i) * D + a] = acc;
   }
   __syncthreads();
 
@@ -114,10 +116,14 @@ __device__ __forceinline__ int hslot(int r, int c16) { return c16 ^ (4 * ((r >> 
 // tiles per wave) and i0 = row0 + GM * (row tile).
 // RS: elements per row of hs and s_out (d*d, or d*d + d when each row also
 // carries a d-vector summed the same way).
-template <int D, int NT, int RS = D * D>
+// ZC: past the RS / 64 column tiles of the states, 2 D / 64 more tiles
+// read the bf16 hi / lo parts of z (zhl, rows of 2 D) and write
+// sigma = hi + lo sums as float32 [B,H,nq,D].
+template <int D, int NT, int RS = D * D, bool ZC = false>
 __global__ void __launch_bounds__(kThreads, 2)
 marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int rows_pad,
-                 int row0, int tiles, const uint16_t* __restrict__ hs, uint16_t* __restrict__ s_out) {
+                 int row0, int tiles, const uint16_t* __restrict__ hs, uint16_t* __restrict__ s_out,
+                 const uint16_t* __restrict__ zhl = nullptr, float* __restrict__ sigma = nullptr) {
   constexpr int DD = RS;
   constexpr int kNT = NT;
   constexpr int kGM = 128 * NT;
@@ -133,12 +139,17 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  constexpr int kCols = RS / kGN;
+  constexpr int kHCols = RS / kGN;
+  constexpr int kCols = kHCols + (ZC ? 2 * D / kGN : 0);
   const int logical = xcd_remap(blockIdx.x, tiles * kCols * g.B * g.H);
   const int rt = logical % tiles;
   const int ct = (logical / tiles) % kCols;
   const int bh = logical / (tiles * kCols);
   const int i0 = row0 + rt * kGM;
+  // this workgroup's source rows: the states, or (ZC) the z parts
+  const bool zt = ZC && ct >= kHCols;
+  const int src_row = zt ? 2 * D : DD;                 // elements per source row
+  const int cts = zt ? ct - kHCols : ct;              // column tile within the source row
 
   if (t < 16) {
     u32x2 e;
@@ -162,7 +173,8 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
   // lane%8 holding global 16-byte column (lane%8) ^ swizzle; rows past nkb
   // read as zeros.  Bits: 4 KB, 1 KB per wave.
   const __amdgpu_buffer_rsrc_t hrs =
-      make_rsrc(hs + static_cast<int64_t>(bh) * g.nkb * DD, static_cast<uint32_t>(g.nkb) * DD * 2);
+      zt ? make_rsrc(zhl + static_cast<int64_t>(bh) * g.nkb * 2 * D, static_cast<uint32_t>(g.nkb) * 2 * D * 2)
+         : make_rsrc(hs + static_cast<int64_t>(bh) * g.nkb * DD, static_cast<uint32_t>(g.nkb) * DD * 2);
   const __amdgpu_buffer_rsrc_t brs =
       make_rsrc(bits + static_cast<int64_t>(bh) * nchunks * rows_pad * 2,
                 static_cast<uint32_t>(nchunks) * rows_pad * 8);
@@ -170,12 +182,12 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int r = 16 * wave + 8 * u + (lane >> 3);
-    hoff[u] = static_cast<uint32_t>(r) * DD * 2 + 128u * ct + 16u * hslot(r, lane & 7);
+    hoff[u] = static_cast<uint32_t>(r) * src_row * 2 + 128u * cts + 16u * hslot(r, lane & 7);
   }
   const uint32_t boff = static_cast<uint32_t>(i0) * 8 + (kBBytes / 4) * wave + 16u * lane;
   auto issue = [&](int c, unsigned char* sb) {
     const int cc = min(c, nchunks - 1);         // past the end: reload the last chunk (unused)
-    const uint32_t hs_off = static_cast<uint32_t>(kGK * cc) * DD * 2;
+    const uint32_t hs_off = static_cast<uint32_t>(kGK * cc) * src_row * 2;
 #pragma unroll
     for (int u = 0; u < 2; ++u) buffer_load_lds16(hrs, sb + (16 * wave + 8 * u) * 128, hoff[u], hs_off);
     if (kNT == 4 || lane < 16 * kNT)
@@ -308,6 +320,24 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
   wait_vmem();         // the clamped tail loads also write LDS
   __syncthreads();     // every wave is done with the stages
 
+  if (zt) {
+    // sigma of features 32 cts + 8(r/4) + 4hh + r%4: hi part (mt = 0) plus
+    // lo part (mt = 1), float32, 16 bytes per lane
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const int i = i0 + 32 * kNT * wave + 32 * nt + l32;
+      if (i >= g.nq) continue;
+      float* srow = sigma + (static_cast<int64_t>(bh) * g.nq + i) * D + 32 * cts + 4 * hh;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 w;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) w[x] = acc[0][nt][4 * r4 + x] + acc[1][nt][4 * r4 + x];
+        *reinterpret_cast<f32x4*>(srow + 8 * r4) = w;
+      }
+    }
+    return;
+  }
   // Output: acc[mt][nt][r] = S^T[e = 64 ct + 32 mt + 8(r/4) + 4hh + r%4]
   //                              [i = i0 + 128w + 32nt + l32].
   // Each wave stages 32 rows x 128 bytes at a time in its own 4 KB of the
@@ -344,7 +374,7 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
 
 hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const uint16_t* h_states,
                                 const float* z_states, uint16_t* s_sum, float* sigma_sum,
-                                uint32_t* bits, bool complement, hipStream_t stream) {
+                                uint32_t* bits, uint16_t* zhl, bool complement, hipStream_t stream) {
   const int nchunks = marginal_chunks(g);
   const int rows_pad = marginal_rows_pad(g);
   const int rpb = kThreads / g.D;
@@ -354,7 +384,7 @@ hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const ui
     constexpr int DK = decltype(dc)::value;
     constexpr bool CK = decltype(cc)::value;
     hipLaunchKernelGGL((marg_prep_kernel<DK, CK>), gs, dim3(kThreads), lds1, stream, g, marg,
-                       z_states, sigma_sum, bits, nchunks, rows_pad);
+                       z_states, zhl, bits, nchunks, rows_pad);
   };
   if (g.D == 128) {
     if (complement) prep(std::integral_constant<int, 128>(), std::true_type());
@@ -365,11 +395,13 @@ hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const ui
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_mask_gemm(g, bits, h_states, s_sum, stream);
+  return launch_mask_gemm(g, bits, h_states, s_sum, stream, false, complement ? nullptr : zhl,
+                          sigma_sum);
 }
 
 hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint16_t* h_states,
-                            uint16_t* s_sum, hipStream_t stream, bool with_vector) {
+                            uint16_t* s_sum, hipStream_t stream, bool with_vector,
+                            const uint16_t* zhl, float* sigma) {
   const int nchunks = marginal_chunks(g);
   const int rows_pad = marginal_rows_pad(g);
   // 512-row tiles, and a 256-row tile for a remainder of at most 256 rows
@@ -382,6 +414,10 @@ hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint1
       dim3 g2(tiles * ((DK * DK + DK) / kGN) * g.B * g.H);
       hipLaunchKernelGGL((marg_gemm_kernel<DK, NTK, DK * DK + DK>), g2, dim3(kThreads), 0, stream,
                          g, bits, nchunks, rows_pad, row0, tiles, h_states, s_sum);
+    } else if (zhl) {
+      dim3 g2(tiles * ((DK * DK + 2 * DK) / kGN) * g.B * g.H);
+      hipLaunchKernelGGL((marg_gemm_kernel<DK, NTK, DK * DK, true>), g2, dim3(kThreads), 0, stream,
+                         g, bits, nchunks, rows_pad, row0, tiles, h_states, s_sum, zhl, sigma);
     } else {
       dim3 g2(tiles * (DK * DK / kGN) * g.B * g.H);
       hipLaunchKernelGGL((marg_gemm_kernel<DK, NTK>), g2, dim3(kThreads), 0, stream, g, bits,

@@ -44,20 +44,24 @@ hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16
 // the mask rows (two words per query block and chunk of 64 KV blocks).
 inline int marginal_chunks(const Geometry& g) { return (g.nkb + 63) / 64; }
 inline int marginal_rows_pad(const Geometry& g) { return (g.nq + 511) / 512 * 512; }
+// zhl: scratch of B*H*nkb*2*d bf16 for the hi / lo parts of z (sigma comes
+// out of the same product as S).
 // complement: marg is the critical list (k_crit entries per query block) and
 // S_i sums every KV block outside it (the residual state of residual linear
-// attention); sigma_sum and z_states are not used.
+// attention); sigma_sum, z_states and zhl are not used.
 hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const uint16_t* h_states,
                                 const float* z_states, uint16_t* s_sum, float* sigma_sum,
-                                uint32_t* bits, bool complement, hipStream_t stream);
+                                uint32_t* bits, uint16_t* zhl, bool complement, hipStream_t stream);
 
 // The product S = M H alone, from mask bits already in the layout the
 // marginal sums write (chunk-major, rows padded to the 512-row tile); with
 // nq = nkb the roles of query and KV blocks can be swapped (a transposed mask).
 // with_vector: rows of d*d + d elements (a d-vector after each matrix, summed
-// the same way).
+// the same way).  zhl (with_vector false): also the float32 sums
+// sigma = M (hi + lo) of the bf16 parts of z, rows of 2 d.
 hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint16_t* h_states,
-                            uint16_t* s_sum, hipStream_t stream, bool with_vector = false);
+                            uint16_t* s_sum, hipStream_t stream, bool with_vector = false,
+                            const uint16_t* zhl = nullptr, float* sigma = nullptr);
 
 // rla: residual linear attention epilogue (s_sum holds every non-critical
 // block's exponential-map state; RMS norm in place of the sigma denominator).

@@ -123,9 +123,10 @@ int sla_num_blocks(const sla_problem* problem, int32_t* nq, int32_t* nkb);
 /* Host: bytes of device workspace the operation needs (0 if none).  The
  * workspace passed to a call must be at least this large and 256-byte
  * aligned.  SLA_OP_FORWARD (and SLA_OP_FORWARD_FP8) needs a bf16
- * [B,H,nq,d,d] marginal-state sum, a float32 [B,H,nq,d] normaliser sum and
+ * [B,H,nq,d,d] marginal-state sum, a float32 [B,H,nq,d] normaliser sum,
  * B*H*2*ceil(nkb/64)*(nq rounded up to 512) 32-bit words of marginal-mask
- * bits, each region 256-byte aligned; SLA_OP_ROUTE
+ * bits and bf16 [B,H,nkb,2d] parts of z, each region 256-byte aligned;
+ * SLA_OP_ROUTE
  * needs float64 pooled Q and K, SLA_OP_ROUTE_TAYLOR those and float64 block
  * key variances; SLA_OP_FORWARD_PISA needs bf16 block means of K and V
  * [B,H,64*ceil(nkb/64),d], a bf16 Hbar [B,H,d,d] and float32 per-chunk
@@ -222,7 +223,9 @@ int sla_forward(const sla_problem* problem, const void* q, const void* k,
  * separately.  sla_marginal_sums writes, into the forward workspace, the
  * marginal-state sums S_i = sum_{j marginal} H_j (bf16 [B,H,nq,d,d],
  * value-major like h_states) and
- * sigma_i = sum_{j marginal} z_j (float [B,H,nq,d]); sla_forward_attend then
+ * sigma_i = sum_{j marginal} z_j (float [B,H,nq,d]; each z_j enters as the
+ * sum of two bf16 parts hi + lo, within 2^-17 of z_j, and the sums are
+ * float32, as for S_i); sla_forward_attend then
  * runs the fused sparse + linear attention reading them from the same
  * workspace.  Arguments mean what they mean for sla_forward; with
  * k_marg == 0 sla_marginal_sums does nothing.  sla_forward is exactly
