@@ -20,6 +20,7 @@ from .ops import (  # noqa: F401
     forward_save,
     forward_workspace,
     linear_states,
+    linear_states_quantize,
     make_problem,
     marginal_sums,
     num_blocks,
@@ -30,6 +31,7 @@ from .ops import (  # noqa: F401
     route,
     route_noalloc,
     route_pisa,
+    route_quantize,
     sla_attention,
     version,
     workspace_size,

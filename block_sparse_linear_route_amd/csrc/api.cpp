@@ -351,6 +351,34 @@ int sla_route(const sla_problem* problem, const void* q, const void* k, int32_t*
                   "sla_route launch");
 }
 
+int sla_route_quantize(const sla_problem* problem, const void* q, const void* k, int32_t* crit_idx,
+                       int32_t* marg_idx, int8_t* block_class, float* block_logits,
+                       float* pooled_q, float* pooled_k, uint8_t* q8, float* q_scales,
+                       uint8_t* k8, float* k_scales, void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(q, 16);
+  SLA_REQ(k, 16);
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  if (problem->k_marg > 0) SLA_REQ(marg_idx, 4);
+  SLA_OPT(block_logits, 4);
+  SLA_OPT(pooled_q, 4);
+  SLA_OPT(pooled_k, 4);
+  SLA_REQ(q8, 16);
+  SLA_REQ(k8, 16);
+  SLA_REQ(q_scales, 4);
+  SLA_REQ(k_scales, 4);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, route_ws(g)));
+  SLA_TRY(check_device());
+  double* qpool = static_cast<double*>(ws);
+  double* kpool_t = reinterpret_cast<double*>(static_cast<char*>(ws) + route_region(g));
+  const sla::Fp8Out f8{q8, q_scales, k8, k_scales};
+  return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
+                                    pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr,
+                                    static_cast<hipStream_t>(stream), nullptr, &f8),
+                  "sla_route_quantize launch");
+}
+
 int sla_route_noalloc(const sla_problem* problem, const void* q, const void* k, int32_t* crit_idx,
                       int32_t* marg_idx, int8_t* block_class, float* block_logits,
                       float* pooled_q, float* pooled_k, void* stream) {
@@ -404,6 +432,23 @@ int sla_route_taylor(const sla_problem* problem, const void* q, const void* k, i
                                     pooled_q, pooled_k, qpool, kpool_t, kvar_t, key_var,
                                     static_cast<hipStream_t>(stream)),
                   "sla_route_taylor launch");
+}
+
+int sla_linear_states_quantize(const sla_problem* problem, const void* k, const void* v,
+                               void* h_states, float* z_states, uint8_t* v8, float* v_scales,
+                               void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(k, 16);
+  SLA_REQ(v, 16);
+  SLA_REQ(h_states, 16);
+  SLA_REQ(z_states, 16);
+  SLA_REQ(v8, 16);
+  SLA_REQ(v_scales, 4);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_device());
+  return launched(sla::launch_states(g, k, v, static_cast<uint16_t*>(h_states), z_states, false,
+                                     static_cast<hipStream_t>(stream), v8, v_scales),
+                  "sla_linear_states_quantize launch");
 }
 
 int sla_linear_states(const sla_problem* problem, const void* k, const void* v, void* h_states,

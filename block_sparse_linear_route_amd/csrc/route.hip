@@ -15,6 +15,7 @@
 // define; equal logits are ordered by ascending KV block index.  Compaction
 // writes each class's KV block indices in ascending order.
 #include "device_common.hpp"
+#include "fp8_encode.hpp"
 #include "sla_internal.hpp"
 
 namespace sla {
@@ -26,13 +27,17 @@ namespace {
 // a ragged end load the block's last row and are zeroed, so every load is in
 // flight at once), then LDS sums the row groups in float64.  VAR adds, for
 // K blocks, a second pass: squared deviations from the block mean, summed
-// the same way.
-template <typename T, int D, bool VAR>
+// the same way.  QNT (low-bit sparse branch) also writes the block's E4M3
+// codes and float32 scale ([SLA2 technical summary, section 2.C]; the bytes
+// of the stand-alone quantiser) from the tile already in registers.
+template <typename T, int D, bool VAR, bool QNT = false>
 __global__ void __launch_bounds__(kThreads)
 pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g,
             double* __restrict__ qpool, double* __restrict__ kpool_t,
             float* __restrict__ qout, float* __restrict__ kout,
-            double* __restrict__ kvar_t, float* __restrict__ vout) {
+            double* __restrict__ kvar_t, float* __restrict__ vout,
+            uint8_t* __restrict__ q8 = nullptr, float* __restrict__ q_scale = nullptr,
+            uint8_t* __restrict__ k8 = nullptr, float* __restrict__ k_scale = nullptr) {
   constexpr int CH = D / 8;           // 8-element chunks per row
   constexpr int RG = kThreads / CH;   // row groups
   constexpr int RPG = kBlock / RG;    // rows per group
@@ -63,6 +68,22 @@ pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g,
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[rg][ch * 8 + e] = acc[e];
+  if constexpr (QNT) {
+    __shared__ float wmax[4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int rr = 0; rr < RPG; ++rr)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, rg + rr * RG < nj ? fabsf(f[rr][e]) : 0.0f);
+    amax = workgroup_max4(amax, wmax);     // (its barrier also publishes red)
+    const float r = e4m3_block_factor(amax);
+    uint8_t* codes = (which == 0 ? q8 : k8) + (static_cast<int64_t>(bh) * g.N + row0) * D + ch * 8;
+    if (t == 0) (which == 0 ? q_scale : k_scale)[static_cast<int64_t>(bh) * g.nq + j] = e4m3_block_scale(amax);
+#pragma unroll
+    for (int rr = 0; rr < RPG; ++rr)
+      if (rg + rr * RG < nj)
+        *reinterpret_cast<u32x2*>(codes + static_cast<int64_t>(rg + rr * RG) * D) = e4m3_pack8(f[rr], r);
+  }
   __syncthreads();
   if (t < D) {
     double s = 0.0;
@@ -501,9 +522,14 @@ hipError_t launch_select(const Geometry& g, const double* qpool, const double* k
 
 template <typename T, int D>
 void launch_pool_t(const Geometry& g, const void* q, const void* k, double* qpool, double* kpool_t,
-                   float* qo, float* ko, double* kvar_t, float* vo, hipStream_t stream) {
+                   float* qo, float* ko, double* kvar_t, float* vo, hipStream_t stream,
+                   const Fp8Out* f8) {
   dim3 grid(g.nq, g.B * g.H, 2);
-  if (kvar_t)
+  if (f8)
+    hipLaunchKernelGGL((pool_kernel<T, D, false, true>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const T*>(q), static_cast<const T*>(k), g, qpool, kpool_t, qo,
+                       ko, nullptr, nullptr, f8->q8, f8->q_scale, f8->k8, f8->k_scale);
+  else if (kvar_t)
     hipLaunchKernelGGL((pool_kernel<T, D, true>), grid, dim3(kThreads), 0, stream,
                        static_cast<const T*>(q), static_cast<const T*>(k), g, qpool, kpool_t, qo,
                        ko, kvar_t, vo);
@@ -519,17 +545,17 @@ hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t
                         int32_t* marg, int8_t* cls, float* logits, float* pooled_q,
                         float* pooled_k, double* ws_qpool, double* ws_kpool_t,
                         double* ws_kvar_t, float* key_var, hipStream_t stream,
-                        const double* block_dev) {
+                        const double* block_dev, const Fp8Out* f8) {
   if (g.dtype == 1) {
     if (g.D == 128)
-      launch_pool_t<uint16_t, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream);
+      launch_pool_t<uint16_t, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8);
     else
-      launch_pool_t<uint16_t, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream);
+      launch_pool_t<uint16_t, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8);
   } else {
     if (g.D == 128)
-      launch_pool_t<float, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream);
+      launch_pool_t<float, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8);
     else
-      launch_pool_t<float, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream);
+      launch_pool_t<float, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

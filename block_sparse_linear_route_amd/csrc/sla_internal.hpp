@@ -28,15 +28,25 @@ hipError_t static_scratch(void** ptr);
 // into it, and into key_var as float32 when that is non-null).  block_dev
 // non-null (and ws_kvar_t null): covariance-aware score, block_dev holding
 // the float64 deviation norms M_j [B*H][nkb].
+// f8 non-null (plain score only): the pooling pass also writes the E4M3
+// codes and scales of Q and K ([B,H,N,d] u8, [B,H,nb] float).
+struct Fp8Out {
+  uint8_t* q8;
+  float* q_scale;
+  uint8_t* k8;
+  float* k_scale;
+};
 hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t* crit,
                         int32_t* marg, int8_t* cls, float* logits, float* pooled_q,
                         float* pooled_k, double* ws_qpool, double* ws_kpool_t,
                         double* ws_kvar_t, float* key_var, hipStream_t stream,
-                        const double* block_dev = nullptr);
+                        const double* block_dev = nullptr, const Fp8Out* f8 = nullptr);
 
 // exp_map: phi(k) = exp(k) elementwise instead of the softmax over features.
+// v8 non-null (softmax map only): also the E4M3 codes and scales of V.
 hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16_t* h_states,
-                         float* z_states, bool exp_map, hipStream_t stream);
+                         float* z_states, bool exp_map, hipStream_t stream,
+                         uint8_t* v8 = nullptr, float* v_scale = nullptr);
 
 // Marginal-state sums S_i = sum_{j in M_i} H_j (bf16, [B,H,nq,d,d], value-major
 // like the states) and sigma_i = sum_{j in M_i} z_j (float, [B,H,nq,d]); bits

@@ -18,6 +18,7 @@
 // the 64 tokens as the contraction dimension.  The kernel is HBM-bound: it
 // reads 2*64*d and writes d*d elements per block.
 #include "device_common.hpp"
+#include "fp8_encode.hpp"
 #include "sla_internal.hpp"
 
 namespace sla {
@@ -25,10 +26,14 @@ namespace {
 
 // EXPMAP: phi(k) = exp(k) elementwise, with no per-token normalisation
 // ([SPLA technical summary, section 2.3] parameter-free exponential map).
-template <typename T, int D, bool EXPMAP>
+// QNT (low-bit sparse branch): also the V block's E4M3 codes and float32
+// scale ([SLA2 technical summary, section 2.C]; the bytes of the
+// stand-alone quantiser), from the V rows already in registers.
+template <typename T, int D, bool EXPMAP, bool QNT = false>
 __global__ void __launch_bounds__(kThreads)
 states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
-              uint16_t* __restrict__ h_out, float* __restrict__ z_out) {
+              uint16_t* __restrict__ h_out, float* __restrict__ z_out,
+              uint8_t* __restrict__ v8 = nullptr, float* __restrict__ v_scale = nullptr) {
   constexpr int TS = kBlock + 8;        // token stride of the transposed tiles
   constexpr int HS = D + 8;             // row stride of the staged (value-major) output tile
   constexpr int CW = D / 4;             // features per thread (4 threads per token)
@@ -97,6 +102,21 @@ states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
     if (lane < 4) zpart[wave][part * CW + c] = zc;
   }
 
+  if constexpr (QNT) {
+    __shared__ float wmax[4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) amax = fmaxf(amax, valid ? fabsf(vv[c]) : 0.0f);
+    amax = workgroup_max4(amax, wmax);
+    const float r = e4m3_block_factor(amax);
+    if (t == 0) v_scale[static_cast<int64_t>(bh) * g.nq + j] = e4m3_block_scale(amax);
+    if (valid) {
+      uint8_t* codes = v8 + (static_cast<int64_t>(bh) * g.N + j * kBlock + row) * D + part * CW;
+#pragma unroll
+      for (int c = 0; c < CW / 8; ++c) *reinterpret_cast<u32x2*>(codes + 8 * c) = e4m3_pack8(vv + 8 * c, r);
+    }
+  }
+
   // token-contiguous bf16 operands: phi_t[a][token], v_t[c][token]
 #pragma unroll
   for (int c = 0; c < CW; ++c) {
@@ -150,9 +170,12 @@ states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
 
 template <typename T, int D>
 void launch_states_t(const Geometry& g, const void* k, const void* v, uint16_t* hs, float* zs,
-                     bool exp_map, hipStream_t stream) {
+                     bool exp_map, hipStream_t stream, uint8_t* v8, float* vs) {
   dim3 grid(g.nkb, g.B * g.H);
-  if (exp_map)
+  if (v8)
+    hipLaunchKernelGGL((states_kernel<T, D, false, true>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const T*>(k), static_cast<const T*>(v), g, hs, zs, v8, vs);
+  else if (exp_map)
     hipLaunchKernelGGL((states_kernel<T, D, true>), grid, dim3(kThreads), 0, stream,
                        static_cast<const T*>(k), static_cast<const T*>(v), g, hs, zs);
   else
@@ -163,13 +186,14 @@ void launch_states_t(const Geometry& g, const void* k, const void* v, uint16_t* 
 }  // namespace
 
 hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16_t* h_states,
-                         float* z_states, bool exp_map, hipStream_t stream) {
+                         float* z_states, bool exp_map, hipStream_t stream, uint8_t* v8,
+                         float* v_scale) {
   if (g.dtype == 1) {
-    if (g.D == 128) launch_states_t<uint16_t, 128>(g, k, v, h_states, z_states, exp_map, stream);
-    else launch_states_t<uint16_t, 64>(g, k, v, h_states, z_states, exp_map, stream);
+    if (g.D == 128) launch_states_t<uint16_t, 128>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale);
+    else launch_states_t<uint16_t, 64>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale);
   } else {
-    if (g.D == 128) launch_states_t<float, 128>(g, k, v, h_states, z_states, exp_map, stream);
-    else launch_states_t<float, 64>(g, k, v, h_states, z_states, exp_map, stream);
+    if (g.D == 128) launch_states_t<float, 128>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale);
+    else launch_states_t<float, 64>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale);
   }
   return hipGetLastError();
 }

@@ -452,6 +452,50 @@ def backward_saved(q, k, v, dout, crit_idx, marg_idx, alpha, workspace, *, strea
     return dq, dk, dv, da
 
 
+def route_quantize(q: torch.Tensor, k: torch.Tensor, k_crit: int, k_marg: int, *,
+                   want_class: bool = False, stream=None) -> dict:
+    """``sla_route_quantize``: ``route`` (mean score) plus the E4M3 codes and
+    scales of Q and K from the pooling pass: ``q8``, ``q_scale``, ``k8``, ``k_scale``."""
+    (k,) = _same_layout(q, k)
+    p = make_problem(q, k_crit, k_marg)
+    B, H, N, d = q.shape
+    nb = num_blocks(N)
+    dev = q.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(crit_idx=torch.empty((B, H, nb, k_crit), **i32),
+               marg_idx=torch.empty((B, H, nb, k_marg), **i32),
+               q8=torch.empty((B, H, N, d), dtype=torch.uint8, device=dev),
+               q_scale=torch.empty((B, H, nb), dtype=torch.float32, device=dev),
+               k8=torch.empty((B, H, N, d), dtype=torch.uint8, device=dev),
+               k_scale=torch.empty((B, H, nb), dtype=torch.float32, device=dev))
+    if want_class:
+        out["block_class"] = torch.empty((B, H, nb, nb), dtype=torch.int8, device=dev)
+    ws = _workspace(p, _lib.OP_ROUTE, dev)
+    _check(lib.sla_route_quantize(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(out["crit_idx"]),
+                                  _ptr(out["marg_idx"]), _ptr(out.get("block_class")), None, None,
+                                  None, _ptr(out["q8"]), _ptr(out["q_scale"]), _ptr(out["k8"]),
+                                  _ptr(out["k_scale"]), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(stream)))
+    out["_workspace"] = ws
+    return out
+
+
+def linear_states_quantize(k: torch.Tensor, v: torch.Tensor, stream=None):
+    """``sla_linear_states_quantize``: (H, z) of ``linear_states`` plus the
+    E4M3 codes (uint8 [B,H,N,d]) and scales (float32 [B,H,nb]) of V."""
+    (v,) = _same_layout(k, v)
+    p = make_problem(k, 0, 1)
+    B, H, N, d = k.shape
+    nb = num_blocks(N)
+    Hs = torch.empty((B, H, nb, d, d), dtype=torch.bfloat16, device=k.device)
+    zs = torch.empty((B, H, nb, d), dtype=torch.float32, device=k.device)
+    v8 = torch.empty((B, H, N, d), dtype=torch.uint8, device=k.device)
+    vs = torch.empty((B, H, nb), dtype=torch.float32, device=k.device)
+    _check(lib.sla_linear_states_quantize(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(Hs), _ptr(zs),
+                                          _ptr(v8), _ptr(vs), _stream(stream)))
+    return Hs, zs, v8, vs
+
+
 def quantize_fp8(x: torch.Tensor, stream=None):
     """Per-block E4M3 codes (uint8 [B,H,N,d]) and float32 scales [B,H,nb]."""
     p = make_problem(x, 0, 1)

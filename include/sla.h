@@ -154,6 +154,20 @@ int sla_route(const sla_problem* problem, const void* q, const void* k,
               float* block_logits, float* pooled_q, float* pooled_k, void* ws,
               size_t ws_bytes, void* stream);
 
+/* Block routing that also quantises Q and K for the low-bit sparse branch.
+ * [SLA2 summary 2.B, 2.C]  Exactly sla_route (same arguments, results and
+ * errors) plus, from the tiles the pooling pass already reads, the E4M3
+ * codes and scales of Q and K that sla_quantize_fp8 would write:
+ * q8, k8         out uint8 [B,H,N,d] contiguous
+ * q_scales,
+ * k_scales       out float [B,H,nb]
+ * so the fp8 forward needs no separate pass over Q and K. */
+int sla_route_quantize(const sla_problem* problem, const void* q, const void* k,
+                       int32_t* crit_idx, int32_t* marg_idx, int8_t* block_class,
+                       float* block_logits, float* pooled_q, float* pooled_k, uint8_t* q8,
+                       float* q_scales, uint8_t* k8, float* k_scales, void* ws,
+                       size_t ws_bytes, void* stream);
+
 /* Bytes of device scratch the library holds per GPU for the allocation-free
  * entry points. */
 #define SLA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
@@ -199,6 +213,15 @@ int sla_route_taylor(const sla_problem* problem, const void* q, const void* k,
  * float32, H is accumulated in float32 from bf16 operands. */
 int sla_linear_states(const sla_problem* problem, const void* k, const void* v,
                       void* h_states, float* z_states, void* stream);
+
+/* Linear states that also quantise V for the low-bit sparse branch.
+ * [PISA summary; SLA2 summary 2.C]  Exactly sla_linear_states plus the E4M3
+ * codes (out uint8 [B,H,N,d] contiguous) and scales (out float [B,H,nb]) of
+ * V that sla_quantize_fp8 would write, from the V tiles the states pass
+ * already reads. */
+int sla_linear_states_quantize(const sla_problem* problem, const void* k, const void* v,
+                               void* h_states, float* z_states, uint8_t* v8,
+                               float* v_scales, void* stream);
 
 /* Fused sparse + linear forward.  [SLA abstract; SLA2 summary 1 and 2.A]
  * q, k, v    input [B,H,N,d]

@@ -471,3 +471,37 @@ def test_marginal_sums_parity(N, d, km, H, seed):
                                        err_msg=f"S head {h} row {i}")
             np.testing.assert_allclose(sig[0, h, i], want_z, rtol=1e-5, atol=1e-6,
                                        err_msg=f"sigma head {h} row {i}")
+
+
+# ------------------------------------------------------------------ fused quantisation
+
+@pytest.mark.parametrize("name,N,d,dtype,H,seed", [
+    ("video32k", None, None, None, None, None),
+    ("custom", 1000, 128, "bf16", 2, 140),      # ragged last block
+    ("custom", 777, 64, "fp32", 3, 141),
+    ("custom", 65, 128, "bf16", 1, 142),        # a one-token last block
+])
+def test_fused_quantisation_equals_the_quantiser(name, N, d, dtype, H, seed):
+    """sla_route_quantize and sla_linear_states_quantize: the route, the
+    states and the E4M3 codes / scales are bit-identical to sla_route,
+    sla_linear_states and sla_quantize_fp8 (whose bytes the oracle pins)."""
+    s = _s()
+    w = make_workload(name) if name != "custom" else make_custom(1, H, N, d, dtype=dtype, seed=seed,
+                                                                 k_crit=2, k_marg=3)
+    q, k, v = _gpu(w)
+    rq = s.route_quantize(q, k, w.k_crit, w.k_marg, want_class=True)
+    r = s.route(q, k, w.k_crit, w.k_marg, want_class=True)
+    Hq, zq, v8, vs = s.linear_states_quantize(k, v)
+    Hs, zs = s.linear_states(k, v)
+    (q8, qs), (k8, ks), (v8r, vsr) = (s.quantize_fp8(x) for x in (q, k, v))
+    torch.cuda.synchronize()
+    for key in ("crit_idx", "marg_idx", "block_class"):
+        assert torch.equal(rq[key], r[key]), key
+    assert torch.equal(Hq, Hs) and torch.equal(zq, zs)
+    for got, ref in ((rq["q8"], q8), (rq["q_scale"], qs), (rq["k8"], k8), (rq["k_scale"], ks),
+                     (v8, v8r), (vs, vsr)):
+        assert torch.equal(got, ref)
+    # and the codes are the oracle's bytes (one head)
+    c, sc = ofp8.quantize_blocks(w.v[0, 0].float().numpy())
+    np.testing.assert_array_equal(v8[0, 0].cpu().numpy(), c)
+    np.testing.assert_array_equal(vs[0, 0].cpu().numpy(), sc)
