@@ -99,6 +99,112 @@ def load_traffic(workload: str, fp8: bool = False):
     return t.get("hbm_bytes_per_launch")
 
 
+def make_step(sla_gpu, q, k, v, alpha, kc, km):
+    """(step, timed) closures over device-resident inputs.
+
+    step(ev, fp8_step) runs route -> states -> marginal sums -> attention on
+    torch's current stream; ev (6 events or None) brackets each op, so each
+    event pair times exactly that op's kernels.  timed(n, fp8_step) runs n
+    steps and returns the last routing, the wall ms per step and the mean
+    per-op ms (route, states, -, marginal sums, attention)."""
+    import numpy as np
+    import torch
+
+    ws = sla_gpu.forward_workspace(q, kc, km)
+    torch.cuda.synchronize()
+
+    def step(ev=None, fp8_step=False):
+        def mark(n):
+            if ev is not None:
+                ev[n].record()
+        mark(0)
+        if fp8_step:
+            # the pooling pass quantises Q and K, the states pass V
+            r = sla_gpu.route_quantize(q, k, kc, km)
+            q8, qs, k8, ks = r["q8"], r["q_scale"], r["k8"], r["k_scale"]
+        else:
+            r = sla_gpu.route(q, k, kc, km)
+        mark(1)
+        if fp8_step:
+            Hs, zs, v8, vs = sla_gpu.linear_states_quantize(k, v)
+        else:
+            Hs, zs = sla_gpu.linear_states(k, v)
+        mark(2)
+        mark(3)
+        sla_gpu.marginal_sums(q, r["marg_idx"], Hs, zs, ws, k_crit=kc)
+        mark(4)
+        if fp8_step:
+            o = sla_gpu.forward_attend_fp8(q, q8, qs, k8, ks, v8, vs, r["crit_idx"], alpha, ws,
+                                           k_marg=km)
+        else:
+            o = sla_gpu.forward_attend(q, k, v, r["crit_idx"], alpha, ws, k_marg=km)
+        mark(5)
+        return r, o
+
+    def timed(n_steps, fp8_step):
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n_steps):
+            r, o = step(events[i], fp8_step)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        parts = np.array([[events[i][p].elapsed_time(events[i][p + 1]) for p in range(5)]
+                          for i in range(n_steps)])
+        return r, (t1 - t0) * 1e3 / n_steps, parts.mean(axis=0)
+
+    return step, timed
+
+
+def config_record(sla_gpu, name: str, steps: int, warmup: int):
+    """The bf16 step on another named workload: step and forward time, the
+    forward's executed TFLOP/s and the attention kernel's fraction of the
+    bf16 MFMA peak (same FLOP accounting as the headline line)."""
+    import torch
+    from workloads import make_workload
+
+    t0 = time.perf_counter()
+    w = make_workload(name, cache=False)
+    gen_s = time.perf_counter() - t0
+    B, H, N, d = w.shape
+    kc, km = w.k_crit, w.k_marg
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
+    alpha = w.alpha.to(dev)
+    del w
+    step, timed = make_step(sla_gpu, q, k, v, alpha, kc, km)
+    for _ in range(warmup):
+        step(None, False)
+    torch.cuda.synchronize()
+    r, ms_step, parts = timed(steps, False)
+    route_ms, states_ms, _, msum_ms, attn_ms = (float(x) for x in parts)
+    fwd_ms = msum_ms + attn_ms
+    f_crit, f_lin, f_sums = executed_flops(r["crit_idx"].cpu().numpy(),
+                                           r["marg_idx"].cpu().numpy(), N, d)
+    f_fwd = f_crit + f_lin + f_sums
+    f_step = f_fwd + route_flops(B, H, N, d) + states_flops(B, H, N, d)
+    attn_tf = (f_crit + f_lin) / (attn_ms * 1e-3) / 1e12
+    rec = {
+        "workload": f"{name}: B={B} H={H} N={N} d={d} bf16, block 64, "
+                    f"k_crit={kc} k_marg={km} of {(N + 63) // 64} KV blocks",
+        "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_step,
+        "step_tflops": f_step / (ms_step * 1e-3) / 1e12,
+        "forward_ms": fwd_ms,
+        "forward_tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
+        "forward_frac_bf16_peak": f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "breakdown_ms": {"route": route_ms, "linear_states": states_ms,
+                         "marginal_sums": msum_ms, "attention": attn_ms},
+        "attention_tflops": attn_tf,
+        "attention_frac_bf16_peak": attn_tf / PEAK_BF16_TFLOPS,
+        "executed_gflop": {"step": f_step / 1e9, "forward": f_fwd / 1e9},
+        "input_synthesis_s": gen_s,
+    }
+    del q, k, v, r
+    torch.cuda.empty_cache()
+    return rec
+
+
 def cpu_baseline(w, k_crit, k_marg, f_step, n_heads: int):
     """Oracle timed on whole heads (route, states and forward), scaled to all
     heads of the step."""
@@ -143,6 +249,10 @@ def main():
                     help="skip the piecewise exact-or-approximate attention side measurement")
     ap.add_argument("--no-rla", action="store_true",
                     help="skip the residual-linear-attention side measurement")
+    ap.add_argument("--other-configs", default="seq8k,video75k",
+                    help="comma-separated bf16 workloads timed after the headline one "
+                         "(step, forward, attention fraction of peak); empty for none")
+    ap.add_argument("--other-steps", type=int, default=5)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this size (PMC calibration)")
     args = ap.parse_args()
@@ -165,53 +275,10 @@ def main():
     dev = torch.device("cuda:0")
     q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
     alpha = w.alpha.to(dev)
-    ws = sla_gpu.forward_workspace(q, kc, km)
-    torch.cuda.synchronize()
-
-    # Every op runs on torch's current stream, which the events below record
-    # on, so each event pair brackets exactly that op's kernels.
-    def step(ev=None, fp8_step=fp8):
-        def mark(n):
-            if ev is not None:
-                ev[n].record()
-        mark(0)
-        if fp8_step:
-            # the pooling pass quantises Q and K, the states pass V
-            r = sla_gpu.route_quantize(q, k, kc, km)
-            q8, qs, k8, ks = r["q8"], r["q_scale"], r["k8"], r["k_scale"]
-        else:
-            r = sla_gpu.route(q, k, kc, km)
-        mark(1)
-        if fp8_step:
-            Hs, zs, v8, vs = sla_gpu.linear_states_quantize(k, v)
-        else:
-            Hs, zs = sla_gpu.linear_states(k, v)
-        mark(2)
-        mark(3)
-        sla_gpu.marginal_sums(q, r["marg_idx"], Hs, zs, ws, k_crit=kc)
-        mark(4)
-        if fp8_step:
-            o = sla_gpu.forward_attend_fp8(q, q8, qs, k8, ks, v8, vs, r["crit_idx"], alpha, ws,
-                                           k_marg=km)
-        else:
-            o = sla_gpu.forward_attend(q, k, v, r["crit_idx"], alpha, ws, k_marg=km)
-        mark(5)
-        return r, o
-
-    def timed(n_steps, fp8_step):
-        events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(n_steps):
-            r, o = step(events[i], fp8_step)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        parts = np.array([[events[i][p].elapsed_time(events[i][p + 1]) for p in range(5)]
-                          for i in range(n_steps)])
-        return r, (t1 - t0) * 1e3 / n_steps, parts.mean(axis=0)
+    step, timed = make_step(sla_gpu, q, k, v, alpha, kc, km)
 
     for _ in range(args.warmup):
-        r, o = step()
+        r, o = step(None, fp8)
     torch.cuda.synchronize()
     r, ms_step, parts = timed(args.steps, fp8)
     route_ms, states_ms, _, msum_ms, attn_ms = parts
@@ -302,54 +369,58 @@ def main():
 
     pisa_variant = None
     if not fp8 and not args.no_pisa:
-        # piecewise exact-or-approximate attention on the same inputs: the
-        # critical split of the step exact, every other block by centroid
-        ws_p = sla_gpu.pisa_workspace(q)
+        # piecewise exact-or-approximate attention on the same inputs, routed
+        # by the covariance-aware score (its statistics pass also fills the
+        # piecewise statistics the fused kernel reads): the critical split
+        # exact, every other block by centroid plus the first-order term
+        ws_p = sla_gpu.route_pisa(q, k, v, kc, km)["_workspace"]
 
         def pisa_step(ev=None):
             def mark(n):
                 if ev is not None:
                     ev[n].record()
             mark(0)
-            rp = sla_gpu.route(q, k, kc, km)
+            rp = sla_gpu.route_pisa(q, k, v, kc, km, workspace=ws_p)
             mark(1)
-            sla_gpu.pisa_statistics(k, v, ws_p)
-            mark(2)
             op = sla_gpu.forward_attend_pisa(q, k, v, rp["crit_idx"], ws_p)
-            mark(3)
+            mark(2)
             return rp, op
 
         for _ in range(2):
             pisa_step()
         n_p = max(3, args.steps // 2)
-        evp = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_p)]
+        evp = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_p)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(n_p):
             rp, _ = pisa_step(evp[i])
         torch.cuda.synchronize()
         ms_p = (time.perf_counter() - t0) * 1e3 / n_p
-        pp = np.array([[evp[i][j].elapsed_time(evp[i][j + 1]) for j in range(3)]
+        pp = np.array([[evp[i][j].elapsed_time(evp[i][j + 1]) for j in range(2)]
                        for i in range(n_p)]).mean(axis=0)
+        same_p = ((rp["crit_idx"] == r["crit_idx"]).all(-1)
+                  & (rp["marg_idx"] == r["marg_idx"]).all(-1))
         nbk = (N + 63) // 64
-        # exact blocks as in the step, one 64-key tile of centroids per 64
-        # KV blocks (only the unselected ones count), the first-order term
-        fp_crit = f_crit
+        # exact blocks from the covariance-aware lists, one 64-key tile of
+        # centroids per 64 KV blocks (only the unselected ones count), the
+        # first-order term; the statistics pass as part of the route
+        fp_crit, _, _ = executed_flops(rp["crit_idx"].cpu().numpy(), rp["marg_idx"].cpu().numpy(),
+                                       N, d)
         fp_zero = 4.0 * B * H * N * d * (nbk - kc)
         fp_corr = 2.0 * B * H * N * d * d
-        fp_stats = 2.0 * B * H * N * d * d
         pisa_variant = {
             "ms_per_step": ms_p,
-            "forward_ms": float(pp[1] + pp[2]),
-            "breakdown_ms": {"route": pp[0], "block_statistics": pp[1], "attention_pisa": pp[2]},
-            "attention_pisa_tflops": (fp_crit + fp_zero + fp_corr) / (pp[2] * 1e-3) / 1e12,
-            "forward_tflops": (fp_crit + fp_zero + fp_corr + fp_stats) / ((pp[1] + pp[2]) * 1e-3) / 1e12,
-            "note": "piecewise exact-or-approximate attention: the step's critical blocks exact, "
-                    f"the other {nbk - kc} blocks per query block through their centroids "
+            "breakdown_ms": {"route_pisa": pp[0], "attention_pisa": pp[1]},
+            "attention_pisa_ms": float(pp[1]),
+            "attention_pisa_tflops": (fp_crit + fp_zero + fp_corr) / (pp[1] * 1e-3) / 1e12,
+            "rows_split_differently_from_mean_score": float(1.0 - same_p.float().mean().item()),
+            "note": "sla_route_pisa (pooling, block statistics with the deviations "
+                    "M_j = ||H_j - Hbar||_F, covariance-aware top-k) then the fused piecewise "
+                    "kernel: critical blocks exact, the other "
+                    f"{nbk - kc} blocks per query block through their centroids "
                     f"({(nbk + 63) // 64} pseudo-blocks of 64 centroids in the same online "
                     "softmax), one global first-order correction; FLOPs count 4 n d per "
-                    "exact key and per unselected centroid, 2 N d^2 for the correction and "
-                    "2 N d^2 for the block statistics",
+                    "exact key and per unselected centroid and 2 N d^2 for the correction",
         }
 
     bwd_variant = None
@@ -497,6 +568,10 @@ def main():
     out["taylor_routing"] = taylor_route
     if bwd_variant is not None:
         out["backward"] = bwd_variant
+    others = [x for x in args.other_configs.split(",") if x and x != args.workload]
+    if others:
+        out["other_configs"] = {name: config_record(sla_gpu, name, args.other_steps, 2)
+                                for name in others}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, kc, km, f_step, args.cpu_heads)
     print(json.dumps(out), flush=True)

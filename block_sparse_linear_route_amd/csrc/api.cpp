@@ -65,8 +65,8 @@ int validate_problem(const sla_problem* p) {
     return fail(SLA_ERR_UNSUPPORTED, "one head spans %lld bytes (seq_len x stride_n); at most 4 GiB is supported",
                 static_cast<long long>(head_span));
   const int64_t nq_total = static_cast<int64_t>(p->batch) * p->heads * nkb;
-  if (nq_total > (1ll << 31) - 1)
-    return fail(SLA_ERR_UNSUPPORTED, "batch * heads * blocks exceeds the grid limit");
+  if (2 * nq_total > (1ll << 31) - 1)
+    return fail(SLA_ERR_UNSUPPORTED, "2 * batch * heads * blocks exceeds the grid limit");
   return SLA_OK;
 }
 

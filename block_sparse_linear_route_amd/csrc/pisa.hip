@@ -269,7 +269,7 @@ pisa_stats_bf16_kernel(const uint16_t* __restrict__ k, const uint16_t* __restric
 
   // rank-one term and means of block it (sums in LDS buffer it & 1, value
   // sums of this wave's rows in vs_prev)
-  auto finish_block = [&](int it) {
+  auto finish_block = [&](int it) __attribute__((always_inline)) {
     const int j = j0 + it;
     const float inv_n = 1.0f / static_cast<float>(min(kBlock, g.N - j * kBlock));
     const float* ks = ksum[it & 1];

@@ -22,7 +22,11 @@ namespace sla {
 namespace {
 
 // ---------------------------------------------------------------- pooling
-// grid (nb, B*H, 2): z = 0 pools Q, z = 1 pools K.  One workgroup per block:
+// One-dimensional grid of nb x B*H x 2 (Q, then K) blocks, the block index
+// fastest in the logical order and each XCD given a contiguous range of it,
+// so that neighbouring blocks of one head run on one XCD and their 8-byte
+// entries of each transposed pooled-K row meet in the same L2 lines before
+// those are written back.  One workgroup per block:
 // thread t reads the 16-byte chunk t % CH of rows t / CH + RG m (rows past
 // a ragged end load the block's last row and are zeroed, so every load is in
 // flight at once), then LDS sums the row groups in float64.  VAR adds, for
@@ -44,9 +48,11 @@ pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g,
   __shared__ double red[RG][D];
   __shared__ double mean_s[VAR ? D : 1];
 
-  const int j = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int which = blockIdx.z;
+  const int bhn = g.B * g.H;
+  const int logical = xcd_remap(blockIdx.x, g.nq * bhn * 2);
+  const int j = logical % g.nq;
+  const int bh = (logical / g.nq) % bhn;
+  const int which = logical / (g.nq * bhn);
   const int b = bh / g.H, h = bh % g.H;
   const T* x = (which == 0 ? q : k) + b * g.sb + h * g.sh;
   const int t = threadIdx.x;
@@ -524,7 +530,7 @@ template <typename T, int D>
 void launch_pool_t(const Geometry& g, const void* q, const void* k, double* qpool, double* kpool_t,
                    float* qo, float* ko, double* kvar_t, float* vo, hipStream_t stream,
                    const Fp8Out* f8) {
-  dim3 grid(g.nq, g.B * g.H, 2);
+  dim3 grid(g.nq * g.B * g.H * 2);
   if (f8)
     hipLaunchKernelGGL((pool_kernel<T, D, false, true>), grid, dim3(kThreads), 0, stream,
                        static_cast<const T*>(q), static_cast<const T*>(k), g, qpool, kpool_t, qo,

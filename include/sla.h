@@ -114,7 +114,8 @@ typedef struct sla_problem {
  * overlap rows) or SLA_ERR_UNSUPPORTED (head_dim, block, dtype, more than
  * 4096 KV blocks, or one head spanning more than 4 GiB:
  * (seq_len - 1) * stride_n * elem_size + head_dim * elem_size > 2^32 - 1,
- * which only very wide row strides such as packed QKV of many heads reach). */
+ * which only very wide row strides such as packed QKV of many heads reach,
+ * or 2 * batch * heads * ceil(seq_len / 64) > 2^31 - 1, the launch grid). */
 int sla_validate(const sla_problem* problem);
 
 /* Host: number of query blocks and KV blocks (both ceil(seq_len / 64)). */
