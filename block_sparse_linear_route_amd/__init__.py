@@ -30,6 +30,7 @@ from .ops import (  # noqa: F401
     residual_sums,
     route,
     route_noalloc,
+    validate_lists,
     route_pisa,
     route_quantize,
     sla_attention,

@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libsla.so")
 SOURCES = ["api.cpp", "route.hip", "states.hip", "marginal.hip", "attention.hip", "attention_fp8.hip", "fp8.hip",
-           "pisa.hip", "backward.hip", "scratch.hip"]
+           "pisa.hip", "backward.hip", "scratch.hip", "lists.hip"]
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -26,7 +26,7 @@ int fail(int status, const char* fmt, ...) {
   return status;
 }
 
-constexpr int kMaxKvBlocks = 4096;
+using sla::kMaxKvBlocks;
 constexpr size_t kWsAlign = 256;
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
@@ -406,6 +406,26 @@ int sla_route_noalloc(const sla_problem* problem, const void* q, const void* k, 
                                     pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr,
                                     static_cast<hipStream_t>(stream)),
                   "sla_route_noalloc launch");
+}
+
+int sla_validate_lists(const sla_problem* problem, const int32_t* crit_idx,
+                       const int32_t* marg_idx, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  if (problem->k_marg > 0) SLA_REQ(marg_idx, 4);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_device());
+  unsigned int bad = 0, first = 0;
+  SLA_TRY(launched(sla::validate_lists(g, crit_idx, marg_idx, static_cast<hipStream_t>(stream),
+                                       &bad, &first),
+                   "sla_validate_lists"));
+  if (bad == 0) return SLA_OK;
+  const int i = static_cast<int>(first % static_cast<unsigned int>(g.nq));
+  const int bh = static_cast<int>(first / static_cast<unsigned int>(g.nq));
+  return fail(SLA_ERR_INVALID_ARGUMENT,
+              "%u of %lld rows hold an index outside [0, %d), a repeat or a block in both lists; "
+              "first at batch %d, head %d, query block %d",
+              bad, static_cast<long long>(g.B) * g.H * g.nq, g.nkb, bh / g.H, bh % g.H, i);
 }
 
 int sla_route_taylor(const sla_problem* problem, const void* q, const void* k, int32_t* crit_idx,

@@ -127,7 +127,7 @@ attention_kernel(AttnArgs A) {
       excl[w] = (w == A.npb - 1 && (g.nkb & 63)) ? (~0ull << (g.nkb & 63)) : 0ull;
     __syncthreads();
     for (int c = t; c < kc; c += kThreads) {
-      const int jb = crow[c];
+      const int jb = list_block(crow[c], g.nkb);
       atomicOr(reinterpret_cast<unsigned long long*>(excl + (jb >> 6)), 1ull << (jb & 63));
     }
   }
@@ -135,8 +135,8 @@ attention_kernel(AttnArgs A) {
   // (lane l holds entry base + l), and entries are taken with v_readlane, so
   // the loop issues no index loads: a vector load there would make the
   // compiler's vmcnt wait cover the in-flight K/V tile loads as well.
-  int cl0 = lane < kc ? crow[lane] : 0;
-  int cl1 = 64 + lane < kc ? crow[64 + lane] : 0;
+  int cl0 = lane < kc ? list_block(crow[lane], g.nkb) : 0;
+  int cl1 = 64 + lane < kc ? list_block(crow[64 + lane], g.nkb) : 0;
   int cbase = 0;
   auto crit_at = [&](int c) -> int {
     const int o = c - cbase;
@@ -433,7 +433,7 @@ attention_kernel(AttnArgs A) {
     if ((!PISA || it + 1 < kc) && it + 1 - cbase == 64) {   // entries it+1 .. it+64 now start at register 1
       cbase += 64;
       cl0 = cl1;
-      cl1 = cbase + 64 + lane < kc ? crow[cbase + 64 + lane] : 0;
+      cl1 = cbase + 64 + lane < kc ? list_block(crow[cbase + 64 + lane], g.nkb) : 0;
     }
     wait_vmem();   // this wave's loads for the next step
     __syncthreads();

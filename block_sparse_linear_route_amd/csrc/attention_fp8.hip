@@ -126,8 +126,8 @@ attention_fp8_kernel(AttnFp8Args A) {
   const float* __restrict__ ksb = A.k_s + static_cast<int64_t>(bh) * g.nkb;
   const float* __restrict__ vsb = A.v_s + static_cast<int64_t>(bh) * g.nkb;
   int ebase = 0;
-  int ej0 = lane < nh ? crow[lh + 2 * lane] : 0;
-  int ej1 = 64 + lane < nh ? crow[lh + 2 * (64 + lane)] : 0;
+  int ej0 = lane < nh ? list_block(crow[lh + 2 * lane], g.nkb) : 0;
+  int ej1 = 64 + lane < nh ? list_block(crow[lh + 2 * (64 + lane)], g.nkb) : 0;
   float efb = 0.0f, elv = 0.0f, eiv = 1.0f;    // s_q s_k c, log2 s_v, 1 / s_v
   auto load_scales = [&]() {
     if (ebase + lane < nh) {
@@ -336,7 +336,7 @@ attention_fp8_kernel(AttnFp8Args A) {
     if (it + 1 - ebase == 64) {          // half-list entries it+1 .. now start at register 1
       ebase += 64;
       ej0 = ej1;
-      ej1 = ebase + 64 + lane < nh ? crow[lh + 2 * (ebase + 64 + lane)] : 0;
+      ej1 = ebase + 64 + lane < nh ? list_block(crow[lh + 2 * (ebase + 64 + lane)], g.nkb) : 0;
       load_scales();
     }
     wait_vmem();

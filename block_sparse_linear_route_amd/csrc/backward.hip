@@ -212,8 +212,8 @@ bwd_dq_kernel(BwdArgs A) {
 
   const int32_t* __restrict__ crow = A.crit + (static_cast<int64_t>(bh) * g.nq + i) * g.k_crit;
   const int kc = g.k_crit;
-  int cl0 = lane < kc ? crow[lane] : 0;
-  int cl1 = 64 + lane < kc ? crow[64 + lane] : 0;
+  int cl0 = lane < kc ? list_block(crow[lane], g.nkb) : 0;
+  int cl1 = 64 + lane < kc ? list_block(crow[64 + lane], g.nkb) : 0;
   int cbase = 0;
   auto crit_at = [&](int c) -> int {
     const int o = c - cbase;
@@ -304,7 +304,7 @@ bwd_dq_kernel(BwdArgs A) {
     if (it + 1 - cbase == 64) {
       cbase += 64;
       cl0 = cl1;
-      cl1 = cbase + 64 + lane < kc ? crow[cbase + 64 + lane] : 0;
+      cl1 = cbase + 64 + lane < kc ? list_block(crow[cbase + 64 + lane], g.nkb) : 0;
     }
   };
   for (int it = 0; it < kc; it += 2) {
@@ -579,12 +579,12 @@ bwd_bits_kernel(BwdArgs A, int nchunks, int rows_pad) {
   const int64_t irow = static_cast<int64_t>(bh) * g.nq + i;
   const uint32_t bit = 1u << (i & 31);
   for (int u = threadIdx.x; u < g.k_crit; u += kThreads) {
-    const int j = A.crit[irow * g.k_crit + u];
+    const int j = list_block(A.crit[irow * g.k_crit + u], g.nkb);
     atomicOr(A.crit_t + (static_cast<int64_t>(bh) * g.nkb + j) * A.crit_words + (i >> 5), bit);
   }
   const int w = i >> 5;
   for (int u = threadIdx.x; u < g.k_marg; u += kThreads) {
-    const int j = A.marg[irow * g.k_marg + u];
+    const int j = list_block(A.marg[irow * g.k_marg + u], g.nkb);
     atomicOr(A.marg_t + ((static_cast<int64_t>(bh) * nchunks + (w >> 1)) * rows_pad + j) * 2 + (w & 1), bit);
   }
 }

@@ -185,6 +185,12 @@ __device__ __forceinline__ float max16(const f32x16& s) {
   return vmax3(vmax3(a, b, c), f, f);
 }
 
+// A KV block index read from a caller's list, clamped into [0, nkb): every
+// address formed from a list entry then stays inside the tensors whatever
+// the list holds (entries outside the range give meaningless results, not
+// out-of-bounds accesses; sla_validate_lists reports them).
+__device__ __forceinline__ int list_block(int j, int nkb) { return min(max(j, 0), nkb - 1); }
+
 // Workgroup id remapped so that each XCD (the hardware dispatches workgroups
 // round-robin over 8 XCDs) owns one contiguous range of logical work items,
 // which keeps neighbouring query blocks of one head in the same L2.

@@ -74,7 +74,7 @@ marg_prep_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __re
   const int32_t* __restrict__ mrow = marg + (static_cast<int64_t>(bh) * g.nq + min(i, g.nq - 1)) * km;
   if (row_ok) {
     for (int u = a; u < km; u += D) {
-      const int j = mrow[u];
+      const int j = list_block(mrow[u], g.nkb);
       atomicOr(&sbits[r * nw + (j >> 5)], 1u << (j & 31));
     }
   }

@@ -146,6 +146,15 @@ hipError_t launch_backward(const Geometry& g, const BackwardBuffers& w, const vo
                            const int32_t* marg, const float* alpha, float* dq, float* dk,
                            float* dv, float* dalpha, hipStream_t stream);
 
+// Largest KV block count the library accepts (validated on the host).
+constexpr int kMaxKvBlocks = 4096;
+
+// Checks the index lists of every row (range, repeats, overlap); waits on
+// the stream and returns the number of bad rows and the smallest bad row
+// index (0xffffffff when none).
+hipError_t validate_lists(const Geometry& g, const int32_t* crit, const int32_t* marg,
+                          hipStream_t stream, unsigned int* bad_rows, unsigned int* first_bad);
+
 hipError_t launch_quantize_fp8(const Geometry& g, const void* x, uint8_t* codes, float* scales,
                                hipStream_t stream);
 

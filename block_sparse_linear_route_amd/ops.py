@@ -168,6 +168,18 @@ def route_pisa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_crit: int, k
     return out
 
 
+def validate_lists(q: torch.Tensor, crit_idx: Optional[torch.Tensor],
+                   marg_idx: Optional[torch.Tensor], stream=None) -> None:
+    """``sla_validate_lists``: raise SlaError if any row's lists hold an index
+    outside [0, nkb), a repeat, or a block in both lists (q gives the shape)."""
+    kc = int(crit_idx.shape[-1]) if crit_idx is not None else 0
+    km = int(marg_idx.shape[-1]) if marg_idx is not None else 0
+    p = make_problem(q, kc, km)
+    c = crit_idx.contiguous() if crit_idx is not None and kc > 0 else None
+    m = marg_idx.contiguous() if marg_idx is not None and km > 0 else None
+    _check(lib.sla_validate_lists(ctypes.byref(p), _ptr(c), _ptr(m), _stream(stream)))
+
+
 def route_noalloc(q: torch.Tensor, k: torch.Tensor, k_crit: int, k_marg: int, *,
                   want_class: bool = False, want_logits: bool = False, want_pooled: bool = False,
                   out: Optional[dict] = None, stream=None) -> dict:

@@ -190,6 +190,22 @@ int sla_route_noalloc(const sla_problem* problem, const void* q, const void* k,
                       float* block_logits, float* pooled_q, float* pooled_k,
                       void* stream);
 
+/* Check of caller-supplied index lists.  [SLA abstract: each KV block of a
+ * row is critical, marginal or negligible, one class each]
+ * crit_idx     in int32 [B,H,nq,k_crit] (NULL allowed when k_crit = 0)
+ * marg_idx     in int32 [B,H,nq,k_marg] (NULL allowed when k_marg = 0)
+ * Every entry must lie in [0, nkb), no list may repeat an index and no index
+ * may be in both lists of a row (ascending order is not required).  The
+ * compute entry points do not check lists: they clamp each entry into
+ * [0, nkb) before forming an address, so no list makes them access memory
+ * outside their arguments, but an invalid list gives meaningless results.
+ * Returns SLA_OK, or SLA_ERR_INVALID_ARGUMENT naming the number of bad rows
+ * and the first one.  The call waits for `stream` (the lists are read after
+ * the work already queued on it).  It uses a small report array that the
+ * library holds per GPU; calls on one GPU take turns on a host lock. */
+int sla_validate_lists(const sla_problem* problem, const int32_t* crit_idx,
+                       const int32_t* marg_idx, void* stream);
+
 /* Block routing with the second-order score.  [SPLA summary 2.1]
  * The block score keeps the spread of the keys around their block mean,
  * to second order with a diagonal covariance:

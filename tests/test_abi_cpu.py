@@ -287,3 +287,20 @@ def test_noalloc_route_rejects_sizes_past_the_static_scratch_before_any_device_c
     assert b"static scratch" in lib.sla_last_error_message()
     st = lib.sla_route_noalloc(ctypes.byref(fits), None, fake, fake, fake, None, None, None, None, None)
     assert st == _lib.SLA_ERR_INVALID_ARGUMENT
+
+
+def test_list_validator_rejects_bad_arguments_before_any_device_call():
+    fake = ctypes.c_void_p(0x10000)
+    p = P()
+    assert lib.sla_validate_lists(ctypes.byref(p), None, fake, None) == _lib.SLA_ERR_INVALID_ARGUMENT
+    assert lib.sla_validate_lists(ctypes.byref(p), fake, None, None) == _lib.SLA_ERR_INVALID_ARGUMENT
+    assert lib.sla_validate_lists(ctypes.byref(P(head_dim=96)), fake, fake, None) == _lib.SLA_ERR_UNSUPPORTED
+    assert lib.sla_validate_lists(None, fake, fake, None) == _lib.SLA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.skipif(_device_visible(), reason="a HIP device is present: fake pointers would reach kernels")
+def test_list_validator_without_a_device_returns_no_device():
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.sla_validate_lists(ctypes.byref(P()), fake, fake, None) == _lib.SLA_ERR_NO_DEVICE
+    # a list the count makes unnecessary may be NULL
+    assert lib.sla_validate_lists(ctypes.byref(P(k_crit=0)), None, fake, None) == _lib.SLA_ERR_NO_DEVICE
