@@ -459,7 +459,26 @@ def main():
         torch.cuda.synchronize()
         fsave_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
         bsaved_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-        del o_t
+        # quantisation-aware training step: the fp8 forward keeps its
+        # statistics, the bf16 gradient kernels read them
+        rq = sla_gpu.route_quantize(q, k, kc, km)
+        _, _, v8q, vsq = sla_gpu.linear_states_quantize(k, v)
+        codes = (rq["q8"], rq["q_scale"], rq["k8"], rq["k_scale"], v8q, vsq)
+        sla_gpu.forward_save_fp8(q, k, v, *codes, r["crit_idx"], r["marg_idx"], Hb, zb, alpha,
+                                 workspace=ws_b, out=o_t)
+        evq = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_b)]
+        torch.cuda.synchronize()
+        for i_ in range(n_b):
+            evq[i_][0].record()
+            sla_gpu.forward_save_fp8(q, k, v, *codes, r["crit_idx"], r["marg_idx"], Hb, zb, alpha,
+                                     workspace=ws_b, out=o_t)
+            evq[i_][1].record()
+            sla_gpu.backward_saved(q, k, v, dout, r["crit_idx"], r["marg_idx"], alpha, ws_b)
+            evq[i_][2].record()
+        torch.cuda.synchronize()
+        fsave8_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evq]))
+        bsaved8_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evq]))
+        del o_t, rq, codes, v8q, vsq
         # executed FLOPs: the forward again, then per critical (query, key)
         # pair 6 d (dQ kernel: S, dP, dQ) + 8 d (dK/dV kernel: S, dP, dV, dK),
         # 4 d^2 per row on each side of the linear branch, and the marginal
@@ -472,6 +491,11 @@ def main():
             "forward_save_ms": fsave_ms,
             "backward_saved_ms": bsaved_ms,
             "backward_saved_tflops": (f_bwd - f_fwd) / (bsaved_ms * 1e-3) / 1e12,
+            "qat_forward_save_fp8_ms": fsave8_ms,
+            "qat_backward_saved_ms": bsaved8_ms,
+            "qat_note": "quantisation-aware training step: sla_forward_save_fp8 (the fp8 "
+                        "sparse branch, keeping its O_s, O_l and normalisers) then "
+                        "sla_backward_saved (bf16 gradient kernels); codes made once",
             "saved_note": "training step with the forward run once: sla_forward_save (marginal "
                           "sums and the fused kernel writing O plus O_s, O_l and the normaliser "
                           "into the backward workspace), then sla_backward_saved (gradient "

@@ -18,6 +18,7 @@ from .ops import (  # noqa: F401
     forward_pisa,
     forward_rla,
     forward_save,
+    forward_save_fp8,
     forward_workspace,
     linear_states,
     linear_states_quantize,

@@ -78,6 +78,7 @@ SIGNATURES = {
                                     _vp, _vp, _vp, _sz, _vp]),
     "sla_forward_save": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _sz, _vp]),
+    "sla_forward_save_fp8": (ctypes.c_int, [_P] + [_vp] * 16 + [_sz, _vp]),
     "sla_backward_saved": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                           _vp, _vp, _sz, _vp]),
     "sla_status_string": (ctypes.c_char_p, [ctypes.c_int]),

@@ -878,6 +878,35 @@ int sla_forward_save(const sla_problem* problem, const void* q, const void* k, c
                                static_cast<hipStream_t>(stream));
 }
 
+int sla_forward_save_fp8(const sla_problem* problem, const void* q, const void* k, const void* v,
+                         const uint8_t* q8, const float* q_s, const uint8_t* k8, const float* k_s,
+                         const uint8_t* v8, const float* v_s, const int32_t* crit_idx,
+                         const int32_t* marg_idx, const void* h_states, const float* z_states,
+                         const float* alpha, void* o, void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(check_backward_args(problem, q, k, v, crit_idx, marg_idx, alpha));
+  SLA_TRY(check_fp8_args(problem, q, q8, q_s, k8, k_s, v8, v_s, crit_idx, alpha, o, nullptr,
+                         nullptr));
+  if (problem->k_marg > 0) {
+    SLA_REQ(h_states, 16);
+    SLA_REQ(z_states, 16);
+  }
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, backward_ws(g)));
+  SLA_TRY(check_device());
+  const BwdWs w = carve_backward_ws(g, ws);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (g.k_marg > 0)
+    SLA_TRY(launched(sla::launch_marginal_sums(g, marg_idx, static_cast<const uint16_t*>(h_states),
+                                               z_states, w.fwd.s_sum, w.fwd.sigma, w.fwd.bits,
+                                               w.fwd.zhl, false, st),
+                     "marginal sums"));
+  return launched(sla::launch_attention_fp8(g, q, q8, q_s, k8, k_s, v8, v_s, crit_idx, w.fwd.s_sum,
+                                            w.fwd.sigma, alpha, o, const_cast<float*>(w.b.o_s),
+                                            const_cast<float*>(w.b.o_l), st,
+                                            const_cast<float*>(w.b.lse)),
+                  "fp8 forward (saved)");
+}
+
 int sla_backward_saved(const sla_problem* problem, const void* q, const void* k, const void* v,
                        const void* dout, const int32_t* crit_idx, const int32_t* marg_idx,
                        const float* alpha, float* dq, float* dk, float* dv, float* dalpha,

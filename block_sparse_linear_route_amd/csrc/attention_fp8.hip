@@ -46,6 +46,7 @@ struct AttnFp8Args {
   float* o_linear;
   Geometry g;
   float c_log2;      // log2(e) / sqrt(d)
+  float* lse;        // LSE: log2 normaliser of the sparse softmax per row
 };
 
 // XOR swizzle of the 16-byte chunks of a 128-byte fp8 tile row.  With
@@ -74,6 +75,9 @@ __device__ __forceinline__ i32x8 load32b(const uint8_t* p) {
   return r;
 }
 
+// LSE: also write each row's log2 sparse-softmax normaliser (for a bf16
+// backward pass that rebuilds P from the unquantised scores).
+template <bool LSE>
 __global__ void __launch_bounds__(kThreads, 2)
 attention_fp8_kernel(AttnFp8Args A) {
   constexpr int D = 128;
@@ -350,10 +354,9 @@ attention_fp8_kernel(AttnFp8Args A) {
   for (int s = 0; s < NS; ++s)
     qf[s] = load8(qp + static_cast<int64_t>(kBlock * i + qr) * g.sn + 16 * s + 8 * hh);
   __syncthreads();
-  attention_finish<uint16_t, D, false, false>(smem_raw, smem_u16, sig_dummy, false, g, bh, h, i, n_i,
-                                       qrow, hoff,
-                                       A.s_sum, A.sigma_sum,
-                                A.alpha, A.o, A.o_sparse, A.o_linear, oacc, m_run, l_run, 1.0f, qf, [](int) {});
+  attention_finish<uint16_t, D, false, false, false, false, LSE>(
+      smem_raw, smem_u16, sig_dummy, false, g, bh, h, i, n_i, qrow, hoff, A.s_sum, A.sigma_sum,
+      A.alpha, A.o, A.o_sparse, A.o_linear, oacc, m_run, l_run, 1.0f, qf, [](int) {}, 0.0f, A.lse);
 }
 
 }  // namespace
@@ -363,13 +366,17 @@ hipError_t launch_attention_fp8(const Geometry& g, const void* q, const uint8_t*
                                 const uint8_t* v8, const float* v_s, const int32_t* crit,
                                 const uint16_t* s_sum, const float* sigma_sum,
                                 const float* alpha, void* o, float* o_sparse, float* o_linear,
-                                hipStream_t stream) {
+                                hipStream_t stream, float* lse) {
   if (g.D != 128 || g.dtype != 1) return hipErrorNotSupported;
   AttnFp8Args a{static_cast<const uint16_t*>(q), q8, q_s, k8, k_s, v8, v_s, crit, s_sum, sigma_sum,
                 alpha, o, o_sparse, o_linear, g,
-                static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(g.D)))};
+                static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(g.D))),
+                lse};
   const int total = g.B * g.H * g.nq;
-  hipLaunchKernelGGL(attention_fp8_kernel, dim3(total), dim3(kThreads), 0, stream, a);
+  if (lse)
+    hipLaunchKernelGGL(attention_fp8_kernel<true>, dim3(total), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attention_fp8_kernel<false>, dim3(total), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -163,6 +163,6 @@ hipError_t launch_attention_fp8(const Geometry& g, const void* q, const uint8_t*
                                 const uint8_t* v8, const float* v_s, const int32_t* crit,
                                 const uint16_t* s_sum, const float* sigma_sum,
                                 const float* alpha, void* o, float* o_sparse, float* o_linear,
-                                hipStream_t stream);
+                                hipStream_t stream, float* lse = nullptr);
 
 }  // namespace sla

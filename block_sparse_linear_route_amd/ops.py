@@ -445,6 +445,27 @@ def forward_save(q, k, v, crit_idx, marg_idx, h_states, z_states, alpha, *, work
     return out, ws
 
 
+def forward_save_fp8(q, k, v, q8, q_scale, k8, k_scale, v8, v_scale, crit_idx, marg_idx, h_states,
+                     z_states, alpha, *, workspace=None, out=None, stream=None):
+    """The fp8 forward for quantisation-aware training: returns (O, workspace),
+    the workspace holding the fp8 forward's O_s, O_l and normalisers for
+    ``backward_saved`` (bf16 gradients, the quantisation passed through)."""
+    k, v = _same_layout(q, k, v)
+    kc, km = int(crit_idx.shape[-1]), int(marg_idx.shape[-1])
+    p = make_problem(q, kc, km)
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    ws = workspace if workspace is not None else _workspace(p, _lib.OP_BACKWARD, q.device)
+    alpha = alpha.to(device=q.device, dtype=torch.float32).contiguous()
+    codes = [t.contiguous() for t in (q8, q_scale, k8, k_scale, v8, v_scale)]
+    _check(lib.sla_forward_save_fp8(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                    *[_ptr(t) for t in codes],
+                                    _ptr(crit_idx.contiguous()), _ptr(marg_idx.contiguous()),
+                                    _ptr(h_states), _ptr(z_states), _ptr(alpha), _ptr(out),
+                                    _ptr(ws), ws.numel(), _stream(stream)))
+    return out, ws
+
+
 def backward_saved(q, k, v, dout, crit_idx, marg_idx, alpha, workspace, *, stream=None):
     """``backward`` without its forward part: ``workspace`` is the one
     ``forward_save`` filled for the same inputs, lists and alpha."""

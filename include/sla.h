@@ -477,6 +477,27 @@ int sla_backward_saved(const sla_problem* problem, const void* q, const void* k,
                        const int32_t* marg_idx, const float* alpha, float* dq, float* dk,
                        float* dv, float* dalpha, void* ws, size_t ws_bytes, void* stream);
 
+/* Low-bit forward paired with the bf16 backward, for quantisation-aware
+ * training.  [SLA2 summary 2.C: the forward runs the sparse branch in a
+ * low-bit format while the backward stays in 16-bit]
+ * sla_forward_save_fp8 is sla_forward_fp8 (same q8 / k8 / v8 codes and
+ * scales as sla_quantize_fp8 writes, head_dim 128) that keeps, like
+ * sla_forward_save, what sla_backward_saved reads: the marginal sums, O_s
+ * and O_l of the fp8 forward (float) and each row's log2 normaliser of the
+ * fp8 sparse softmax, in ws of sla_workspace_size(SLA_OP_BACKWARD) bytes;
+ * O (bf16) goes to o.  q, k, v are the bf16 inputs the codes were made
+ * from.  sla_backward_saved on that ws then gives the bf16 gradients: they
+ * rebuild P from the bf16 scores q k^T and the fp8 forward's normaliser and
+ * take rowsum(dO_s * O_s) from the fp8 O_s, i.e. the quantisation is passed
+ * through unchanged in the backward (straight-through), and the gradients
+ * differ from those of the unquantised forward by the fp8 forward's error. */
+int sla_forward_save_fp8(const sla_problem* problem, const void* q, const void* k,
+                         const void* v, const uint8_t* q8, const float* q_scales,
+                         const uint8_t* k8, const float* k_scales, const uint8_t* v8,
+                         const float* v_scales, const int32_t* crit_idx,
+                         const int32_t* marg_idx, const void* h_states, const float* z_states,
+                         const float* alpha, void* o, void* ws, size_t ws_bytes, void* stream);
+
 /* Host: static text of a status code. */
 const char* sla_status_string(int status);
 
