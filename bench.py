@@ -351,6 +351,20 @@ def main():
         ms_r = (time.perf_counter() - t0) * 1e3 / n_r
         pr = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
                        for i in range(n_r)]).mean(axis=0)
+        # the subtraction form of the residual sums (global state minus the
+        # critical blocks' states) on the same lists and states
+        He_s, _ = sla_gpu.linear_states(k, v, feature_map="exp")
+        ws_sub = sla_gpu.residual_workspace_subtract(q, kc)
+        sla_gpu.residual_sums_subtract(q, rr["crit_idx"], He_s, ws_sub)
+        evr = [torch.cuda.Event(enable_timing=True) for _ in range(n_r + 1)]
+        torch.cuda.synchronize()
+        evr[0].record()
+        for i in range(n_r):
+            sla_gpu.residual_sums_subtract(q, rr["crit_idx"], He_s, ws_sub)
+            evr[i + 1].record()
+        torch.cuda.synchronize()
+        sub_ms = float(np.mean([evr[i].elapsed_time(evr[i + 1]) for i in range(n_r)]))
+        del He_s, ws_sub
         fr_crit, fr_lin, fr_sums = executed_flops(rr["crit_idx"].cpu().numpy(),
                                                   rr["marg_idx"].cpu().numpy(), N, d)
         fr_fwd = fr_crit + fr_lin + fr_sums
@@ -359,6 +373,7 @@ def main():
             "forward_ms": float(pr[2] + pr[3]),
             "breakdown_ms": {"route": pr[0], "linear_states_exp": pr[1],
                              "residual_sums": pr[2], "attention_rla": pr[3]},
+            "residual_sums_subtraction_form_ms": sub_ms,
             "forward_tflops": fr_fwd / ((pr[2] + pr[3]) * 1e-3) / 1e12,
             "attention_rla_tflops": (fr_crit + fr_lin) / (pr[3] * 1e-3) / 1e12,
             "note": "residual linear attention: same critical split, residual state = the "

@@ -29,6 +29,8 @@ from .ops import (  # noqa: F401
     pisa_workspace,
     quantize_fp8,
     residual_sums,
+    residual_sums_subtract,
+    residual_workspace_subtract,
     route,
     route_noalloc,
     validate_lists,

@@ -21,7 +21,7 @@ SLA_ERR_NO_DEVICE = -5
 SLA_F32, SLA_BF16 = 0, 1
 SLA_STATIC_SCRATCH_BYTES = 64 << 20
 (OP_ROUTE, OP_LINEAR_STATES, OP_FORWARD, OP_QUANTIZE_FP8, OP_FORWARD_FP8, OP_ROUTE_TAYLOR,
- OP_FORWARD_PISA, OP_BACKWARD, OP_ROUTE_PISA) = range(9)
+ OP_FORWARD_PISA, OP_BACKWARD, OP_ROUTE_PISA, OP_RESIDUAL_SUBTRACT) = range(10)
 
 
 class Problem(ctypes.Structure):
@@ -63,6 +63,7 @@ SIGNATURES = {
     "sla_forward_attend_fp8": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                               _vp, _vp, _vp, _vp, _sz, _vp]),
     "sla_linear_states_exp": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp]),
+    "sla_residual_sums_subtract": (ctypes.c_int, [_P, _vp, _vp, _vp, _sz, _vp]),
     "sla_residual_sums": (ctypes.c_int, [_P, _vp, _vp, _vp, _sz, _vp]),
     "sla_forward_attend_rla": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                               _sz, _vp]),

@@ -325,6 +325,7 @@ int sla_workspace_size(const sla_problem* problem, int op, size_t* bytes) {
     case SLA_OP_FORWARD_PISA: *bytes = pisa_ws(g); return SLA_OK;
     case SLA_OP_BACKWARD: *bytes = backward_ws(g); return SLA_OK;
     case SLA_OP_ROUTE_PISA: *bytes = route_pisa_ws(g); return SLA_OK;
+    case SLA_OP_RESIDUAL_SUBTRACT: *bytes = forward_ws(g) + align_up(sla::residual_total_bytes(g)); return SLA_OK;
     default: return fail(SLA_ERR_INVALID_ARGUMENT, "unknown op %d", op);
   }
 }
@@ -685,6 +686,24 @@ int sla_residual_sums(const sla_problem* problem, const int32_t* crit_idx, const
                                             nullptr, w.s_sum, nullptr, w.bits, w.zhl, true,
                                             static_cast<hipStream_t>(stream)),
                   "residual-sum launch");
+}
+
+int sla_residual_sums_subtract(const sla_problem* problem, const int32_t* crit_idx,
+                               const void* h_states, void* ws, size_t ws_bytes, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_TRY(check_rla_counts(problem));
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  if (problem->k_marg > 0) SLA_REQ(h_states, 16);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, forward_ws(g) + align_up(sla::residual_total_bytes(g))));
+  SLA_TRY(check_device());
+  if (g.k_marg == 0) return SLA_OK;
+  const FwdWs w = carve_forward_ws(g, ws);
+  float* tot = reinterpret_cast<float*>(static_cast<char*>(ws) + forward_ws(g));
+  return launched(sla::launch_residual_subtract(g, crit_idx, static_cast<const uint16_t*>(h_states),
+                                                w.s_sum, w.bits, tot,
+                                                static_cast<hipStream_t>(stream)),
+                  "residual-sum (subtraction form) launch");
 }
 
 int sla_forward_attend_rla(const sla_problem* problem, const void* q, const void* k, const void* v,

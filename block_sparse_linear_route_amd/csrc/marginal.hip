@@ -41,6 +41,7 @@ constexpr int kGN = 64;                   // S columns per GEMM workgroup
 constexpr int kGK = 64;                   // KV blocks per chunk
 constexpr int kStages = 3;                // 3 to 6
 constexpr int kHBytes = kGK * kGN * 2;    // H chunk bytes (8 KB)
+constexpr int kTotParts = 4;              // row ranges of the global-state partial sums
 
 // grid (ceil(nq / RPB), B*H), RPB = 256 / D query blocks per workgroup,
 // thread (row, feature a):
@@ -51,10 +52,13 @@ constexpr int kHBytes = kGK * kGN * 2;    // H chunk bytes (8 KB)
 //    32-feature group x as [hi of 32x .. 32x+31 | lo of the same], so that
 //    one 64-column tile of the product carries both parts of 32 features.
 //
-// COMPL: the list is each row's critical list (k_crit entries) and the bit
-// row written is its complement over the valid KV blocks (the residual set of
-// residual linear attention: every block that is not critical); no z.
-template <int D, bool COMPL>
+// MODE 0: the marginal lists, and the z parts.  MODE 1: the list is each
+// row's critical list (k_crit entries) and the bit row written is its
+// complement over the valid KV blocks (the residual set of residual linear
+// attention: every block that is not critical); no z.  MODE 2: the critical
+// lists as they are (the selected set whose states the subtraction form of
+// residual linear attention removes from the global state); no z.
+template <int D, int MODE>
 __global__ void __launch_bounds__(kThreads)
 marg_prep_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __restrict__ zs,
                  uint16_t* __restrict__ zhl, uint32_t* __restrict__ bits, int nchunks,
@@ -69,7 +73,8 @@ marg_prep_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __re
   for (int e = threadIdx.x; e < RPB * nw; e += kThreads) sbits[e] = 0u;
   __syncthreads();
 
-  const int km = COMPL ? g.k_crit : g.k_marg;
+  constexpr bool COMPL = MODE == 1;
+  const int km = MODE == 0 ? g.k_marg : g.k_crit;
   const bool row_ok = i < g.nq;
   const int32_t* __restrict__ mrow = marg + (static_cast<int64_t>(bh) * g.nq + min(i, g.nq - 1)) * km;
   if (row_ok) {
@@ -78,7 +83,7 @@ marg_prep_kernel(Geometry g, const int32_t* __restrict__ marg, const float* __re
       atomicOr(&sbits[r * nw + (j >> 5)], 1u << (j & 31));
     }
   }
-  if constexpr (!COMPL) {
+  if constexpr (MODE == 0) {
     if (i < g.nkb) {
       const float z = zs[(static_cast<int64_t>(bh) * g.nkb + i) * D + a];
       const uint16_t hi = f32_to_bf16_bits(z);
@@ -119,11 +124,15 @@ __device__ __forceinline__ int hslot(int r, int c16) { return c16 ^ (4 * ((r >> 
 // ZC: past the RS / 64 column tiles of the states, 2 D / 64 more tiles
 // read the bf16 hi / lo parts of z (zhl, rows of 2 D) and write
 // sigma = hi + lo sums as float32 [B,H,nq,D].
-template <int D, int NT, int RS = D * D, bool ZC = false>
+// SUB: each output is T[e] - (the product), T[e] = the sum of the kTotParts
+// float32 partial totals tot[bh][part][e] (the global state of the head), so
+// the row holds the sum over the blocks its bits leave out.
+template <int D, int NT, int RS = D * D, bool ZC = false, bool SUB = false>
 __global__ void __launch_bounds__(kThreads, 2)
 marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int rows_pad,
                  int row0, int tiles, const uint16_t* __restrict__ hs, uint16_t* __restrict__ s_out,
-                 const uint16_t* __restrict__ zhl = nullptr, float* __restrict__ sigma = nullptr) {
+                 const uint16_t* __restrict__ zhl = nullptr, float* __restrict__ sigma = nullptr,
+                 const float* __restrict__ tot = nullptr) {
   constexpr int DD = RS;
   constexpr int kNT = NT;
   constexpr int kGM = 128 * NT;
@@ -338,6 +347,22 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
     }
     return;
   }
+  if constexpr (SUB) {
+    // global state entries of this lane's columns e, partial totals summed in
+    // a fixed order
+    const float* tb = tot + static_cast<int64_t>(bh) * kTotParts * DD;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int e = kGN * ct + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
+        float tv = tb[e];
+#pragma unroll
+        for (int pp = 1; pp < kTotParts; ++pp) tv += tb[pp * DD + e];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) acc[mt][nt][r] = tv - acc[mt][nt][r];
+      }
+  }
   // Output: acc[mt][nt][r] = S^T[e = 64 ct + 32 mt + 8(r/4) + 4hh + r%4]
   //                              [i = i0 + 128w + 32nt + l32].
   // Each wave stages 32 rows x 128 bytes at a time in its own 4 KB of the
@@ -370,6 +395,43 @@ marg_gemm_kernel(Geometry g, const uint32_t* __restrict__ bits, int nchunks, int
   }
 }
 
+// The global state of each head (the sum of every block's state) as
+// kTotParts float32 partial sums over consecutive KV block ranges: grid
+// (RS / 2048, kTotParts, B*H), thread t of column slice cs sums elements
+// 2048 cs + 8 t .. +7 over its part's blocks, four rows in flight at a time,
+// in ascending block order.
+template <int RS>
+__global__ void __launch_bounds__(kThreads)
+state_total_kernel(Geometry g, const uint16_t* __restrict__ hs, float* __restrict__ tot) {
+  const int cs = blockIdx.x, part = blockIdx.y, bh = blockIdx.z;
+  const int per = (g.nkb + kTotParts - 1) / kTotParts;
+  const int j0 = min(part * per, g.nkb), j1 = min(j0 + per, g.nkb);
+  const int e0 = 2048 * cs + 8 * threadIdx.x;
+  const uint16_t* src = hs + static_cast<int64_t>(bh) * g.nkb * RS + e0;
+  float a[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) a[x] = 0.0f;
+  int j = j0;
+  for (; j + 4 <= j1; j += 4) {
+    float f[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8_f32(src + static_cast<int64_t>(j + u) * RS, f[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) a[x] += f[u][x];
+  }
+  for (; j < j1; ++j) {
+    float f[8];
+    load8_f32(src + static_cast<int64_t>(j) * RS, f);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) a[x] += f[x];
+  }
+  float* dst = tot + (static_cast<int64_t>(bh) * kTotParts + part) * RS + e0;
+  *reinterpret_cast<f32x4*>(dst) = f32x4{a[0], a[1], a[2], a[3]};
+  *reinterpret_cast<f32x4*>(dst + 4) = f32x4{a[4], a[5], a[6], a[7]};
+}
+
 }  // namespace
 
 hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const uint16_t* h_states,
@@ -380,18 +442,18 @@ hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const ui
   const int rpb = kThreads / g.D;
   dim3 gs((g.nq + rpb - 1) / rpb, g.B * g.H);
   const size_t lds1 = static_cast<size_t>(rpb) * 2 * nchunks * sizeof(uint32_t);
-  auto prep = [&](auto dc, auto cc) {
+  auto prep = [&](auto dc, auto mc) {
     constexpr int DK = decltype(dc)::value;
-    constexpr bool CK = decltype(cc)::value;
-    hipLaunchKernelGGL((marg_prep_kernel<DK, CK>), gs, dim3(kThreads), lds1, stream, g, marg,
+    constexpr int MK = decltype(mc)::value;
+    hipLaunchKernelGGL((marg_prep_kernel<DK, MK>), gs, dim3(kThreads), lds1, stream, g, marg,
                        z_states, zhl, bits, nchunks, rows_pad);
   };
   if (g.D == 128) {
-    if (complement) prep(std::integral_constant<int, 128>(), std::true_type());
-    else prep(std::integral_constant<int, 128>(), std::false_type());
+    if (complement) prep(std::integral_constant<int, 128>(), std::integral_constant<int, 1>());
+    else prep(std::integral_constant<int, 128>(), std::integral_constant<int, 0>());
   } else {
-    if (complement) prep(std::integral_constant<int, 64>(), std::true_type());
-    else prep(std::integral_constant<int, 64>(), std::false_type());
+    if (complement) prep(std::integral_constant<int, 64>(), std::integral_constant<int, 1>());
+    else prep(std::integral_constant<int, 64>(), std::integral_constant<int, 0>());
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -401,7 +463,7 @@ hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const ui
 
 hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint16_t* h_states,
                             uint16_t* s_sum, hipStream_t stream, bool with_vector,
-                            const uint16_t* zhl, float* sigma) {
+                            const uint16_t* zhl, float* sigma, const float* tot) {
   const int nchunks = marginal_chunks(g);
   const int rows_pad = marginal_rows_pad(g);
   // 512-row tiles, and a 256-row tile for a remainder of at most 256 rows
@@ -414,6 +476,11 @@ hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint1
       dim3 g2(tiles * ((DK * DK + DK) / kGN) * g.B * g.H);
       hipLaunchKernelGGL((marg_gemm_kernel<DK, NTK, DK * DK + DK>), g2, dim3(kThreads), 0, stream,
                          g, bits, nchunks, rows_pad, row0, tiles, h_states, s_sum);
+    } else if (tot) {
+      dim3 g2(tiles * (DK * DK / kGN) * g.B * g.H);
+      hipLaunchKernelGGL((marg_gemm_kernel<DK, NTK, DK * DK, false, true>), g2, dim3(kThreads), 0,
+                         stream, g, bits, nchunks, rows_pad, row0, tiles, h_states, s_sum, nullptr,
+                         nullptr, tot);
     } else if (zhl) {
       dim3 g2(tiles * ((DK * DK + 2 * DK) / kGN) * g.B * g.H);
       hipLaunchKernelGGL((marg_gemm_kernel<DK, NTK, DK * DK, true>), g2, dim3(kThreads), 0, stream,
@@ -434,6 +501,39 @@ hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint1
       gemm(std::integral_constant<int, 64>(), std::integral_constant<int, 2>(), 1, 512 * full);
   }
   return hipGetLastError();
+}
+
+}  // namespace sla
+
+namespace sla {
+
+hipError_t launch_residual_subtract(const Geometry& g, const int32_t* crit, const uint16_t* h_states,
+                                    uint16_t* s_sum, uint32_t* bits, float* tot,
+                                    hipStream_t stream) {
+  const int nchunks = marginal_chunks(g);
+  const int rows_pad = marginal_rows_pad(g);
+  const int rpb = kThreads / g.D;
+  dim3 gs((g.nq + rpb - 1) / rpb, g.B * g.H);
+  const size_t lds1 = static_cast<size_t>(rpb) * 2 * nchunks * sizeof(uint32_t);
+  const int rs = g.D * g.D;
+  if (g.D == 128) {
+    hipLaunchKernelGGL((marg_prep_kernel<128, 2>), gs, dim3(kThreads), lds1, stream, g, crit,
+                       nullptr, nullptr, bits, nchunks, rows_pad);
+    hipLaunchKernelGGL((state_total_kernel<128 * 128>), dim3(rs / 2048, kTotParts, g.B * g.H),
+                       dim3(kThreads), 0, stream, g, h_states, tot);
+  } else {
+    hipLaunchKernelGGL((marg_prep_kernel<64, 2>), gs, dim3(kThreads), lds1, stream, g, crit,
+                       nullptr, nullptr, bits, nchunks, rows_pad);
+    hipLaunchKernelGGL((state_total_kernel<64 * 64>), dim3(rs / 2048, kTotParts, g.B * g.H),
+                       dim3(kThreads), 0, stream, g, h_states, tot);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_mask_gemm(g, bits, h_states, s_sum, stream, false, nullptr, nullptr, tot);
+}
+
+size_t residual_total_bytes(const Geometry& g) {
+  return static_cast<size_t>(g.B) * g.H * kTotParts * g.D * g.D * sizeof(float);
 }
 
 }  // namespace sla

@@ -71,7 +71,16 @@ hipError_t launch_marginal_sums(const Geometry& g, const int32_t* marg, const ui
 // sigma = M (hi + lo) of the bf16 parts of z, rows of 2 d.
 hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint16_t* h_states,
                             uint16_t* s_sum, hipStream_t stream, bool with_vector = false,
-                            const uint16_t* zhl = nullptr, float* sigma = nullptr);
+                            const uint16_t* zhl = nullptr, float* sigma = nullptr,
+                            const float* tot = nullptr);
+
+// Residual sums in the subtraction form: the global state of each head (as
+// float32 partial sums in tot, residual_total_bytes) minus the product of
+// the critical-block bits with the states, rounded to bf16 into s_sum.
+hipError_t launch_residual_subtract(const Geometry& g, const int32_t* crit, const uint16_t* h_states,
+                                    uint16_t* s_sum, uint32_t* bits, float* tot,
+                                    hipStream_t stream);
+size_t residual_total_bytes(const Geometry& g);
 
 // rla: residual linear attention epilogue (s_sum holds every non-critical
 // block's exponential-map state; RMS norm in place of the sigma denominator).

@@ -293,6 +293,24 @@ def residual_sums(q, crit_idx, h_states, workspace, *, stream=None):
                                  _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
+def residual_workspace_subtract(q, k_crit: int):
+    """Workspace of ``residual_sums_subtract`` (its leading part is the
+    forward workspace ``forward_attend_rla`` reads)."""
+    p = make_problem(q, k_crit, num_blocks(q.shape[2]) - k_crit)
+    return _workspace(p, _lib.OP_RESIDUAL_SUBTRACT, q.device)
+
+
+def residual_sums_subtract(q, crit_idx, h_states, workspace, *, stream=None):
+    """``residual_sums`` in the subtraction form: the head's global state
+    minus the critical blocks' states (workspace from
+    ``residual_workspace_subtract``)."""
+    kc = int(crit_idx.shape[-1])
+    p = make_problem(q, kc, num_blocks(q.shape[2]) - kc)
+    _check(lib.sla_residual_sums_subtract(ctypes.byref(p), _ptr(crit_idx.contiguous()),
+                                          _ptr(h_states), _ptr(workspace), workspace.numel(),
+                                          _stream(stream)))
+
+
 def forward_attend_rla(q, k, v, crit_idx, alpha, workspace, *, branches: bool = False, out=None,
                        stream=None):
     """Second phase of ``forward_rla``: exact sparse branch, RMS-normalised

@@ -94,7 +94,8 @@ typedef enum sla_op {
   SLA_OP_ROUTE_TAYLOR = 5,
   SLA_OP_FORWARD_PISA = 6,
   SLA_OP_BACKWARD = 7,
-  SLA_OP_ROUTE_PISA = 8
+  SLA_OP_ROUTE_PISA = 8,
+  SLA_OP_RESIDUAL_SUBTRACT = 9
 } sla_op;
 
 /* Problem description (host struct, read only during the call).
@@ -344,12 +345,26 @@ int sla_forward_attend_fp8(const sla_problem* problem, const void* q,
  *   forward workspace (sla_workspace_size(SLA_OP_FORWARD) bytes) from the
  *   critical lists and the exponential-map states; the sigma region is not
  *   written.
+ * sla_residual_sums_subtract: the same S_i in the page's subtraction form,
+ *   S_i = (sum of every block's H_j) - (sum over the critical blocks of
+ *   H_j): the global state of the head (float32, four partial sums over
+ *   block ranges added in a fixed order) minus the product of the
+ *   critical-block bits with the states (float32), rounded once to bf16.
+ *   So phi(q) S_i = o_bar - o_tilde with o_bar from one global state and
+ *   o_tilde from the selected blocks only; the unselected blocks are read
+ *   only through the global state.  Its workspace is
+ *   sla_workspace_size(SLA_OP_RESIDUAL_SUBTRACT) bytes, whose leading
+ *   sla_workspace_size(SLA_OP_FORWARD) bytes are the forward workspace that
+ *   sla_forward_attend_rla reads.  Same S_i as sla_residual_sums up to
+ *   float32 summation order.
  * sla_forward_attend_rla: the fused forward reading S_i from that workspace;
  *   o_linear (when not NULL) receives RMSNorm(phi(Q) S_i).
  * sla_forward_rla: sla_residual_sums then sla_forward_attend_rla on one
  *   stream. */
 int sla_linear_states_exp(const sla_problem* problem, const void* k, const void* v,
                           void* h_states, float* z_states, void* stream);
+int sla_residual_sums_subtract(const sla_problem* problem, const int32_t* crit_idx,
+                               const void* h_states, void* ws, size_t ws_bytes, void* stream);
 int sla_residual_sums(const sla_problem* problem, const int32_t* crit_idx,
                       const void* h_states, void* ws, size_t ws_bytes, void* stream);
 int sla_forward_attend_rla(const sla_problem* problem, const void* q, const void* k,

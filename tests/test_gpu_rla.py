@@ -48,14 +48,20 @@ def test_states_exp_parity(name, heads):
         assert max_abs(hg, H64) < 2e-2 * max(1.0, np.abs(H64).max())
 
 
-def _rla_check(w, kc, heads=None, n_sample=None, seed=0):
+def _rla_check(w, kc, heads=None, n_sample=None, seed=0, form="complement"):
     s = _s()
     q, k, v = w.q.to(DEV), w.k.to(DEV), w.v.to(DEV)
     B, H, N, d = w.shape
     nb = ora.n_blocks(N)
     r = s.route(q, k, kc, nb - kc)
     Hs, _ = s.linear_states(k, v, feature_map="exp")
-    o, o_s, o_l = s.forward_rla(q, k, v, r["crit_idx"], Hs, w.alpha, branches=True)
+    if form == "complement":
+        o, o_s, o_l = s.forward_rla(q, k, v, r["crit_idx"], Hs, w.alpha, branches=True)
+    else:
+        # the subtraction form: global state minus the critical blocks' states
+        ws = s.residual_workspace_subtract(q, kc)
+        s.residual_sums_subtract(q, r["crit_idx"], Hs, ws)
+        o, o_s, o_l = s.forward_attend_rla(q, k, v, r["crit_idx"], w.alpha, ws, branches=True)
     torch.cuda.synchronize()
     q64, k64, v64 = to64(w.q), to64(w.k), to64(w.v)
     heads = heads or [(b, h) for b in range(B) for h in range(H)]
@@ -83,7 +89,7 @@ def _rla_check(w, kc, heads=None, n_sample=None, seed=0):
     res, per = {}, {}
     for key in ("o", "s", "l"):
         res[key], per[key] = metrics_by_head(pairs[key])
-    _say(f"[rla {w.name} N={N} d={d} kc={kc} {w.q.dtype}; {len(heads)} heads] "
+    _say(f"[rla {form} {w.name} N={N} d={d} kc={kc} {w.q.dtype}; {len(heads)} heads] "
          + " ".join(f"{k_}: relL2 {v_[0]:.2e} maxabs {v_[1]:.2e}" for k_, v_ in res.items()))
     if len(heads) > 1:
         _say("  per head O relL2/maxabs: " + format_per_head(per["o"]))
@@ -122,6 +128,27 @@ def test_forward_rla_parity_shapes(N, d, dtype, kc, H, seed):
     w = make_custom(1, H, N, d, dtype=dtype, kind="fourier1d", seed=seed, k_crit=kc,
                     k_marg=nb - kc)
     _rla_check(w, kc, n_sample=None if nb <= 64 else 48)
+
+
+@pytest.mark.parametrize("name", ["tiny", "seq8k", pytest.param("video32k", marks=pytest.mark.timeout(900))])
+def test_forward_rla_subtraction_form_parity(name):
+    # SPLA summary, section 2.2: o_rla = o_bar - o_tilde with o_bar from the
+    # head's global state and o_tilde from the selected blocks only
+    w = make_workload(name)
+    _rla_check(w, w.k_crit, form="subtract")
+
+
+@pytest.mark.parametrize("N,d,dtype,kc,H,seed", [
+    (1000, 128, "bf16", 0, 2, 60),        # nothing selected: the global state alone
+    (1000, 128, "bf16", 15, 1, 61),       # one residual block left
+    (777, 64, "fp32", 3, 2, 62),
+    (300 * 64 + 17, 128, "bf16", 129, 1, 67),
+])
+def test_forward_rla_subtraction_form_shapes(N, d, dtype, kc, H, seed):
+    nb = ora.n_blocks(N)
+    w = make_custom(1, H, N, d, dtype=dtype, kind="fourier1d", seed=seed, k_crit=kc,
+                    k_marg=nb - kc)
+    _rla_check(w, kc, n_sample=None if nb <= 64 else 48, form="subtract")
 
 
 def test_forward_rla_phases_equal_fused_call():
