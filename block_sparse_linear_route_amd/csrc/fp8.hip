@@ -1,10 +1,10 @@
 // Low-bit sparse branch: per-block OCP E4M3 quantiser.
 //
 // [SLA2 technical summary, section 2.C] the sparse branch runs in a low-bit
-// format; the per-block scale and the encoding (fp8_encode.hpp) are done in
-// integer/float steps (round to nearest even, saturate to +-448, -0 kept as
-// 0x80) so that the bytes are fully specified by the OCP 8-bit
-// floating-point format rather than by a conversion instruction's modes.
+// format; the per-block scale and the encoding (fp8_encode.hpp: round to
+// nearest even, saturating at +-448 by construction of the scale, -0 kept
+// as 0x80) make the bytes those the OCP 8-bit floating-point format fixes
+// for the scaled values.
 #include "fp8_encode.hpp"
 #include "sla_internal.hpp"
 

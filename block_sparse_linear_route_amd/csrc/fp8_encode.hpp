@@ -13,22 +13,6 @@
 
 namespace sla {
 
-// E4M3 code of x, branch-free.  |x| >= 2^-6: adding 2^19 - 1 plus the kept
-// lowest bit to the float's bits and dropping 20 mantissa bits rounds to 3
-// mantissa bits, nearest even, with any carry moving into the exponent; the
-// result minus (127 - 7) << 3 is the code (exponent bias 7), and everything
-// above 448 (0x7e), infinities and NaN included, saturates to 0x7e.  Below
-// 2^-6 the codes are the multiples of 2^-9 (code 8 being 2^-6 itself).
-__device__ __forceinline__ uint32_t e4m3_encode(float x) {
-  const uint32_t bits = __float_as_uint(x);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const uint32_t ab = bits & 0x7fffffffu;
-  const uint32_t rn = (ab + 0x7ffffu + ((ab >> 20) & 1u)) >> 20;
-  const uint32_t nc = min(rn - (120u << 3), 0x7eu);
-  const uint32_t sc = static_cast<uint32_t>(rintf(__uint_as_float(ab) * 512.0f));
-  return sign | (ab < 0x3c800000u ? sc : nc);
-}
-
 // Largest of the 256 threads' values (4 waves; wmax: 4 floats of LDS).
 // Every thread returns it; contains one barrier.
 __device__ __forceinline__ float workgroup_max4(float a, float* wmax) {
@@ -49,12 +33,24 @@ __device__ __forceinline__ float e4m3_block_scale(float amax) {
   return amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
 }
 
-// Codes of 8 consecutive values, packed little-endian.
+// Codes of 8 consecutive values, packed little-endian, by the matrix-core
+// format's own conversion (v_cvt_pk_fp8_f32: OCP E4M3, round to nearest
+// even, subnormals kept, -0 as 0x80).  The scaled values lie within
+// 448 (1 + 2^-22) in magnitude (x is at most the block's absolute maximum
+// and r = fl32(448 / absmax)), below 464, the midpoint to the next
+// magnitude, so they round to at most 448 and the conversion never
+// overflows; the codes are those of rounding to nearest even with
+// saturation.  A non-finite input makes the block's scale non-finite and
+// its codes unspecified.
 __device__ __forceinline__ u32x2 e4m3_pack8(const float* v, float r) {
+  int w0 = 0, w1 = 0;
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[0], r), __fmul_rn(v[1], r), w0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[2], r), __fmul_rn(v[3], r), w0, true);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[4], r), __fmul_rn(v[5], r), w1, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[6], r), __fmul_rn(v[7], r), w1, true);
   u32x2 w;
-  w[0] = w[1] = 0u;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) w[e >> 2] |= e4m3_encode(__fmul_rn(v[e], r)) << (8 * (e & 3));
+  w[0] = static_cast<uint32_t>(w0);
+  w[1] = static_cast<uint32_t>(w1);
   return w;
 }
 
