@@ -116,7 +116,11 @@ __device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Buffer resource over [base, base + bytes): raw (unstructured) loads through
-// it are range-checked per dword, and dwords past the end read as zero.
+// it are range-checked per dword, and dwords past the end read as zero.  The
+// check covers the whole offset, the scalar (soffset) part included, for
+// loads into registers and direct loads into LDS alike (verified on gfx950
+// with offsets past the end inside a larger allocation: all zeros), so a
+// tile base passed as soffset still gets zeros past the tensor's end.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
                                            0x00020000);
