@@ -466,10 +466,11 @@ hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint1
                             const uint16_t* zhl, float* sigma, const float* tot) {
   const int nchunks = marginal_chunks(g);
   const int rows_pad = marginal_rows_pad(g);
-  // 512-row tiles, and a 256-row tile for a remainder of at most 256 rows
-  // (at nq = 1182: 1280 rows of matrix-core work instead of 1536)
-  const int full = g.nq / 512, rem = g.nq - 512 * full;
-  const int n512 = rem > 256 ? full + 1 : full;
+  // One launch covers every row of the heads, so the row tiles of one
+  // column tile (neighbours in the XCD-ordered grid) share the H slabs in
+  // L2: a single 512-row tile up to nq = 512 (a 256-row one up to 256), and
+  // 256-row tiles beyond (at nq = 1182: five tiles, 1280 rows of work, 5%
+  // faster than two 512-row tiles and a separate 256-row launch).
   auto gemm = [&](auto dc, auto ntc, int tiles, int row0) {
     constexpr int DK = decltype(dc)::value, NTK = decltype(ntc)::value;
     if (with_vector) {
@@ -491,14 +492,14 @@ hipError_t launch_mask_gemm(const Geometry& g, const uint32_t* bits, const uint1
                          nchunks, rows_pad, row0, tiles, h_states, s_sum);
     }
   };
+  const bool one512 = g.nq > 256 && g.nq <= 512;
+  const int n256 = (g.nq + 255) / 256;
   if (g.D == 128) {
-    if (n512 > 0) gemm(std::integral_constant<int, 128>(), std::integral_constant<int, 4>(), n512, 0);
-    if (rem > 0 && rem <= 256)
-      gemm(std::integral_constant<int, 128>(), std::integral_constant<int, 2>(), 1, 512 * full);
+    if (one512) gemm(std::integral_constant<int, 128>(), std::integral_constant<int, 4>(), 1, 0);
+    else gemm(std::integral_constant<int, 128>(), std::integral_constant<int, 2>(), n256, 0);
   } else {
-    if (n512 > 0) gemm(std::integral_constant<int, 64>(), std::integral_constant<int, 4>(), n512, 0);
-    if (rem > 0 && rem <= 256)
-      gemm(std::integral_constant<int, 64>(), std::integral_constant<int, 2>(), 1, 512 * full);
+    if (one512) gemm(std::integral_constant<int, 64>(), std::integral_constant<int, 4>(), 1, 0);
+    else gemm(std::integral_constant<int, 64>(), std::integral_constant<int, 2>(), n256, 0);
   }
   return hipGetLastError();
 }
