@@ -151,6 +151,7 @@ def make_step(sla_gpu, q, k, v, alpha, kc, km):
         t1 = time.perf_counter()
         parts = np.array([[events[i][p].elapsed_time(events[i][p + 1]) for p in range(5)]
                           for i in range(n_steps)])
+        timed.last_parts = parts
         return r, (t1 - t0) * 1e3 / n_steps, parts.mean(axis=0)
 
     return step, timed
@@ -283,6 +284,7 @@ def main():
     r, ms_step, parts = timed(args.steps, fp8)
     route_ms, states_ms, _, msum_ms, attn_ms = parts
     fwd_ms = msum_ms + attn_ms
+    attn_pct = np.percentile(timed.last_parts[:, 4], [10, 50, 90])
 
     crit = r["crit_idx"].cpu().numpy()
     marg = r["marg_idx"].cpu().numpy()
@@ -293,6 +295,29 @@ def main():
     achieved = attn_flops / (attn_ms * 1e-3) / 1e12
     dense_equiv = 4.0 * B * H * N * N * d
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+
+    # the sparse branch alone on the same critical lists (no marginal blocks:
+    # the fused kernel skips the linear branch), per-branch context
+    ws0 = sla_gpu.forward_workspace(q, kc, 0)
+    if fp8:
+        codes0 = (r["q8"], r["q_scale"], r["k8"], r["k_scale"],
+                  *sla_gpu.linear_states_quantize(k, v)[2:])
+
+        def kern0():
+            sla_gpu.forward_attend_fp8(q, *codes0, r["crit_idx"], alpha, ws0, k_marg=0)
+    else:
+        def kern0():
+            sla_gpu.forward_attend(q, k, v, r["crit_idx"], alpha, ws0, k_marg=0)
+    kern0()
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    ev0[0].record()
+    for i in range(args.steps):
+        kern0()
+        ev0[i + 1].record()
+    torch.cuda.synchronize()
+    sparse_only_ms = float(np.mean([ev0[i].elapsed_time(ev0[i + 1]) for i in range(args.steps)]))
+    del ws0
 
     fp8_variant = None
     if not fp8 and d == 128 and w.q.dtype == torch.bfloat16:
@@ -552,6 +577,7 @@ def main():
         torch.cuda.synchronize()
 
     c = CONFIGS[args.workload]
+    traffic = load_traffic(args.workload, fp8)
     out = {
         "metric": METRIC,
         "value": f_step / (ms_step * 1e-3) / 1e12,
@@ -593,11 +619,19 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": load_traffic(args.workload, fp8),
+            "traffic": traffic,
             "flops_per_launch": attn_flops,
             "mean_launch_ms": attn_ms,
+            "launch_ms_p10_p50_p90": [float(x) for x in attn_pct],
+            "traffic_gbs": None if traffic is None else traffic / (attn_ms * 1e-3) / 1e9,
+            "traffic_frac_hbm_peak": None if traffic is None else traffic / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         },
+        "forward_sparse_only_ms": sparse_only_ms,
+        "forward_sparse_only_note": "the fused kernel on the same critical lists with k_marg = 0 "
+                                    "(no marginal sums, no linear branch)",
     }
+    if fp8:
+        out["forward_frac_fp8_peak"] = f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS
     if fp8_variant is not None:
         out["fp8_sparse_branch"] = fp8_variant
     if rla_variant is not None:
@@ -613,6 +647,7 @@ def main():
                                 for name in others}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, kc, km, f_step, args.cpu_heads)
+        out["cpu_baseline"]["oracle_ms_over_gpu_ms"] = out["cpu_baseline"]["ms_per_step_est"] / ms_step
     print(json.dumps(out), flush=True)
 
 
