@@ -178,12 +178,18 @@ FwdWs carve_forward_ws(const sla::Geometry& g, void* ws) {
 }
 
 // Route workspace: [pooled Q f64 B*H*nq*d][pooled K^T f64 B*H*d*nkb]
-// and, for the second-order score, [key variances^T f64 B*H*d*nkb].
+// [selection keys u64, route_key_bytes] and, for the second-order score,
+// [key variances^T f64 B*H*d*nkb].
 size_t route_region(const sla::Geometry& g) {
   return align_up(static_cast<size_t>(g.B) * g.H * g.nq * g.D * 8);
 }
-size_t route_ws(const sla::Geometry& g) { return 2 * route_region(g); }
-size_t route_taylor_ws(const sla::Geometry& g) { return 3 * route_region(g); }
+size_t route_ws(const sla::Geometry& g) {
+  return 2 * route_region(g) + align_up(sla::route_key_bytes(g));
+}
+size_t route_taylor_ws(const sla::Geometry& g) { return route_ws(g) + route_region(g); }
+uint64_t* route_keys(const sla::Geometry& g, void* ws) {
+  return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + 2 * route_region(g));
+}
 
 // PISA workspace: [kbar bf16 B*H*npb*64*d][vbar bf16 B*H*npb*64*d]
 // [Hbar bf16 B*H*d*d][chunk partials f32 B*H*nchunks*d*d]
@@ -348,7 +354,8 @@ int sla_route(const sla_problem* problem, const void* q, const void* k, int32_t*
   double* kpool_t = reinterpret_cast<double*>(static_cast<char*>(ws) + route_region(g));
   return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
                                     pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr,
-                                    static_cast<hipStream_t>(stream)),
+                                    static_cast<hipStream_t>(stream), nullptr, nullptr,
+                                    route_keys(g, ws)),
                   "sla_route launch");
 }
 
@@ -376,7 +383,8 @@ int sla_route_quantize(const sla_problem* problem, const void* q, const void* k,
   const sla::Fp8Out f8{q8, q_scales, k8, k_scales};
   return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
                                     pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr,
-                                    static_cast<hipStream_t>(stream), nullptr, &f8),
+                                    static_cast<hipStream_t>(stream), nullptr, &f8,
+                                    route_keys(g, ws)),
                   "sla_route_quantize launch");
 }
 
@@ -392,7 +400,7 @@ int sla_route_noalloc(const sla_problem* problem, const void* q, const void* k, 
   SLA_OPT(pooled_q, 4);
   SLA_OPT(pooled_k, 4);
   const sla::Geometry g = geometry(problem);
-  const size_t need = route_ws(g);
+  const size_t need = 2 * route_region(g);   // pooled sums; the fused selection kernel
   if (need > sla::kStaticScratchBytes)
     return fail(SLA_ERR_WORKSPACE,
                 "routing needs %zu bytes of scratch; the static scratch holds %zu "
@@ -448,10 +456,11 @@ int sla_route_taylor(const sla_problem* problem, const void* q, const void* k, i
   char* p = static_cast<char*>(ws);
   double* qpool = reinterpret_cast<double*>(p);
   double* kpool_t = reinterpret_cast<double*>(p + route_region(g));
-  double* kvar_t = reinterpret_cast<double*>(p + 2 * route_region(g));
+  double* kvar_t = reinterpret_cast<double*>(p + route_ws(g));
   return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
                                     pooled_q, pooled_k, qpool, kpool_t, kvar_t, key_var,
-                                    static_cast<hipStream_t>(stream)),
+                                    static_cast<hipStream_t>(stream), nullptr, nullptr,
+                                    route_keys(g, ws)),
                   "sla_route_taylor launch");
 }
 
@@ -781,7 +790,8 @@ int sla_route_pisa(const sla_problem* problem, const void* q, const void* k, con
   SLA_TRY(launched(sla::launch_pisa_deviation(g, k, v, w.hbar, w.part, hbar_f32, mdev, block_dev, st),
                    "PISA block deviation launch"));
   return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
-                                    pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr, st, mdev),
+                                    pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr, st, mdev,
+                                    nullptr, route_keys(g, p)),
                   "sla_route_pisa launch");
 }
 

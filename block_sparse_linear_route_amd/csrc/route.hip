@@ -505,6 +505,196 @@ hipError_t launch_select_rk(const Geometry& g, int nkbp, const double* qpool,
   return hipGetLastError();
 }
 
+// ------------------------------------------------- split selection
+// Given workspace for them, the logits and the selection run as two kernels
+// with the keys in between in memory ([heads][nq][nkbp] u64, ~0 past nkb).
+//
+// logits_kernel: one workgroup per 64 x 64 tile of (query block, KV block)
+// pairs of one head; thread t owns rows 4 (t / 16) .. +3 and columns
+// 4 (t % 16) .. +3 of the tile.  The pooled rows go through LDS 16 features
+// at a time (the next chunk loaded into registers while the current one is
+// used), so each pooled value read from L2 serves 64 logits; in the fused
+// kernel a row group reads the head's whole pooled K for R rows.  Every
+// logit is the same float64 FMA chain over the features in ascending order
+// as in the fused kernel (then the division by sqrt(d) and, per score mode,
+// the same added term), so the keys are the fused kernel's bit for bit;
+// only the covariance score's |qbar_i| is summed here in ascending feature
+// order.
+constexpr int kLT = 64;   // tile rows and columns
+constexpr int kLA = 16;   // features per LDS chunk
+
+template <int SCORE>
+__global__ void __launch_bounds__(kThreads)
+logits_kernel(Geometry g, int nkbp, int bh0, int nbh, const double* __restrict__ qpool,
+              const double* __restrict__ kpool_t, const double* __restrict__ kvar_t,
+              const double* __restrict__ mdev, double sqrt_d, double inv_2d,
+              uint64_t* __restrict__ keys, float* __restrict__ logits_out) {
+  constexpr bool TAYLOR = SCORE == 1;
+  constexpr bool COV = SCORE == 2;
+  __shared__ __attribute__((aligned(16))) double qs[kLA][kLT];
+  __shared__ __attribute__((aligned(16))) double ks[kLA][kLT];
+  __shared__ __attribute__((aligned(16))) double vs[TAYLOR ? kLA : 1][kLT];
+  __shared__ double cq[COV ? kLT : 1];
+  const int nq = g.nq, nkb = g.nkb, D = g.D;
+  const int tr_n = (nq + kLT - 1) / kLT, tc_n = nkbp / kLT;
+  const int logical = xcd_remap(blockIdx.x, tr_n * tc_n * nbh);
+  const int ct = logical % tc_n;
+  const int rt = (logical / tc_n) % tr_n;
+  const int bhl = logical / (tc_n * tr_n);
+  const int bh = bh0 + bhl;
+  const int i0 = rt * kLT, j0 = ct * kLT;
+  const int t = threadIdx.x;
+  const int tr = t >> 4, tc = t & 15;
+
+  // staging: Q rows t / 4, features 4 (t % 4) .. +3 of the chunk (stored
+  // transposed); K^T (and variance) feature t / 16, columns 4 (t % 16) .. +3
+  const int sq_row = t >> 2, sq_a = (t & 3) * 4;
+  const double* gq = qpool + (static_cast<int64_t>(bh) * nq + min(i0 + sq_row, nq - 1)) * D + sq_a;
+  const int sk_a = t >> 4, sk_c = (t & 15) * 4;
+  int64_t kcol[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) kcol[n] = min(j0 + sk_c + n, nkb - 1);
+  const double* gk = kpool_t + (static_cast<int64_t>(bh) * D + sk_a) * nkb;
+  const double* gv = TAYLOR ? kvar_t + (static_cast<int64_t>(bh) * D + sk_a) * nkb : nullptr;
+  double rq[4], rk[4], rv[TAYLOR ? 4 : 1];
+  auto fetch = [&](int a0) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      rq[n] = gq[a0 + n];
+      rk[n] = gk[static_cast<int64_t>(a0) * nkb + kcol[n]];
+      if constexpr (TAYLOR) rv[n] = gv[static_cast<int64_t>(a0) * nkb + kcol[n]];
+    }
+  };
+
+  double acc[4][4], acc2[TAYLOR ? 4 : 1][TAYLOR ? 4 : 1];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      acc[m][n] = 0.0;
+      if constexpr (TAYLOR) acc2[m][n] = 0.0;
+    }
+  double ss = 0.0;   // COV: sum of squares of row t (t < 64)
+
+  fetch(0);
+  for (int a0 = 0; a0 < D; a0 += kLA) {
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      qs[sq_a + n][sq_row] = rq[n];
+      ks[sk_a][sk_c + n] = rk[n];
+      if constexpr (TAYLOR) vs[sk_a][sk_c + n] = rv[n];
+    }
+    __syncthreads();
+    if (a0 + kLA < D) fetch(a0 + kLA);
+    if constexpr (COV) {
+      if (t < kLT) {
+#pragma unroll
+        for (int a = 0; a < kLA; ++a) ss = fma(qs[a][t], qs[a][t], ss);
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < kLA; ++a) {
+      const f64x2 q01 = *reinterpret_cast<const f64x2*>(&qs[a][4 * tr]);
+      const f64x2 q23 = *reinterpret_cast<const f64x2*>(&qs[a][4 * tr + 2]);
+      const f64x2 k01 = *reinterpret_cast<const f64x2*>(&ks[a][4 * tc]);
+      const f64x2 k23 = *reinterpret_cast<const f64x2*>(&ks[a][4 * tc + 2]);
+      const double qv[4] = {q01[0], q01[1], q23[0], q23[1]};
+      const double kv[4] = {k01[0], k01[1], k23[0], k23[1]};
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[m][n] = fma(qv[m], kv[n], acc[m][n]);
+      if constexpr (TAYLOR) {
+        const f64x2 v01 = *reinterpret_cast<const f64x2*>(&vs[a][4 * tc]);
+        const f64x2 v23 = *reinterpret_cast<const f64x2*>(&vs[a][4 * tc + 2]);
+        const double vv[4] = {v01[0], v01[1], v23[0], v23[1]};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const double q2 = qv[m] * qv[m];
+#pragma unroll
+          for (int n = 0; n < 4; ++n) acc2[m][n] = fma(q2, vv[n], acc2[m][n]);
+        }
+      }
+    }
+  }
+  if constexpr (COV) {
+    if (t < kLT) cq[t] = sqrt(ss) * inv_2d;
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int i = i0 + 4 * tr + m;
+    if (i >= nq) continue;
+    uint64_t kr[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int j = j0 + 4 * tc + n;
+      double sv = acc[m][n] / sqrt_d;
+      if constexpr (TAYLOR) sv += log1p(acc2[m][n] * inv_2d);
+      // (the staging columns 4 (t % 16) + n are this thread's output columns)
+      if constexpr (COV) sv += log1p(cq[4 * tr + m] * mdev[static_cast<int64_t>(bh) * nkb + kcol[n]]);
+      kr[n] = j < nkb ? desc_key(sv) : ~0ull;
+      if (j < nkb && logits_out)
+        logits_out[(static_cast<int64_t>(bh) * nq + i) * nkb + j] = static_cast<float>(sv);
+    }
+    uint64_t* krow = keys + (static_cast<int64_t>(bhl) * nq + i) * nkbp + j0 + 4 * tc;
+    *reinterpret_cast<u64x2*>(krow) = u64x2{kr[0], kr[1]};
+    *reinterpret_cast<u64x2*>(krow + 2) = u64x2{kr[2], kr[3]};
+  }
+}
+
+// select_rows_kernel: one wave per row of keys written by logits_kernel
+// (select_row reading the row from memory); four rows per workgroup.
+template <int KPL>
+__global__ void __launch_bounds__(kThreads)
+select_rows_kernel(Geometry g, int nkbp, int bh0, int nbh, const uint64_t* __restrict__ keys,
+                   int32_t* __restrict__ crit, int32_t* __restrict__ marg,
+                   int8_t* __restrict__ cls) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4][128];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r = blockIdx.x * 4 + wave;
+  if (r >= nbh * g.nq) return;
+  const int bhl = r / g.nq, i = r % g.nq;
+  select_row<KPL>(keys + static_cast<int64_t>(r) * nkbp, g.nkb, lane, hist[wave], g.k_crit,
+                  g.k_marg, static_cast<int64_t>(bh0 + bhl) * g.nq + i, crit, marg, cls);
+}
+
+template <int SCORE>
+hipError_t launch_select_split(const Geometry& g, const double* qpool, const double* kpool_t,
+                               const double* kvar_t, const double* mdev, uint64_t* keys,
+                               int32_t* crit, int32_t* marg, int8_t* cls, float* logits,
+                               hipStream_t stream) {
+  const int nkbp = (g.nkb + 63) / 64 * 64;
+  const int bh_all = g.B * g.H;
+  const int chunk = route_key_heads(g);
+  const double sqrt_d = __builtin_sqrt(static_cast<double>(g.D));
+  const double inv_2d = SCORE == 2 ? 1.0 / (sqrt_d * kBlock) : 1.0 / (2.0 * g.D);
+  const int tiles = ((g.nq + kLT - 1) / kLT) * (nkbp / kLT);
+  for (int bh0 = 0; bh0 < bh_all; bh0 += chunk) {
+    const int nbh = bh_all - bh0 < chunk ? bh_all - bh0 : chunk;
+    hipLaunchKernelGGL((logits_kernel<SCORE>), dim3(tiles * nbh), dim3(kThreads), 0, stream, g,
+                       nkbp, bh0, nbh, qpool, kpool_t, kvar_t, mdev, sqrt_d, inv_2d, keys, logits);
+    const dim3 sg((nbh * g.nq + 3) / 4);
+    if (nkbp <= 128)
+      hipLaunchKernelGGL((select_rows_kernel<2>), sg, dim3(kThreads), 0, stream, g, nkbp, bh0, nbh, keys, crit, marg, cls);
+    else if (nkbp <= 512)
+      hipLaunchKernelGGL((select_rows_kernel<8>), sg, dim3(kThreads), 0, stream, g, nkbp, bh0, nbh, keys, crit, marg, cls);
+    else if (nkbp <= 1024)
+      hipLaunchKernelGGL((select_rows_kernel<16>), sg, dim3(kThreads), 0, stream, g, nkbp, bh0, nbh, keys, crit, marg, cls);
+    else if (nkbp <= 1536)
+      hipLaunchKernelGGL((select_rows_kernel<24>), sg, dim3(kThreads), 0, stream, g, nkbp, bh0, nbh, keys, crit, marg, cls);
+    else if (nkbp <= 2048)
+      hipLaunchKernelGGL((select_rows_kernel<32>), sg, dim3(kThreads), 0, stream, g, nkbp, bh0, nbh, keys, crit, marg, cls);
+    else
+      hipLaunchKernelGGL((select_rows_kernel<64>), sg, dim3(kThreads), 0, stream, g, nkbp, bh0, nbh, keys, crit, marg, cls);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 // Eight query rows per workgroup (every pooled-K value read serves eight
 // logits) up to nkb = 1024, then four and two, so that the key rows stay
 // within 64 KB of LDS and several workgroups share a CU (the kernel is
@@ -513,7 +703,10 @@ hipError_t launch_select_rk(const Geometry& g, int nkbp, const double* qpool,
 template <int SCORE>
 hipError_t launch_select(const Geometry& g, const double* qpool, const double* kpool_t,
                          const double* kvar_t, const double* mdev, int32_t* crit, int32_t* marg,
-                         int8_t* cls, float* logits, hipStream_t stream) {
+                         int8_t* cls, float* logits, hipStream_t stream, uint64_t* keys) {
+  if (keys)
+    return launch_select_split<SCORE>(g, qpool, kpool_t, kvar_t, mdev, keys, crit, marg, cls,
+                                      logits, stream);
   const int nkbp = (g.nkb + 63) / 64 * 64;
   if (nkbp <= 128)
     return launch_select_rk<8, 2, SCORE>(g, nkbp, qpool, kpool_t, kvar_t, mdev, crit, marg, cls, logits, stream);
@@ -551,7 +744,7 @@ hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t
                         int32_t* marg, int8_t* cls, float* logits, float* pooled_q,
                         float* pooled_k, double* ws_qpool, double* ws_kpool_t,
                         double* ws_kvar_t, float* key_var, hipStream_t stream,
-                        const double* block_dev, const Fp8Out* f8) {
+                        const double* block_dev, const Fp8Out* f8, uint64_t* ws_keys) {
   if (g.dtype == 1) {
     if (g.D == 128)
       launch_pool_t<uint16_t, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8);
@@ -566,10 +759,13 @@ hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ws_kvar_t)
-    return launch_select<1>(g, ws_qpool, ws_kpool_t, ws_kvar_t, nullptr, crit, marg, cls, logits, stream);
+    return launch_select<1>(g, ws_qpool, ws_kpool_t, ws_kvar_t, nullptr, crit, marg, cls, logits, stream,
+                             ws_keys);
   if (block_dev)
-    return launch_select<2>(g, ws_qpool, ws_kpool_t, nullptr, block_dev, crit, marg, cls, logits, stream);
-  return launch_select<0>(g, ws_qpool, ws_kpool_t, nullptr, nullptr, crit, marg, cls, logits, stream);
+    return launch_select<2>(g, ws_qpool, ws_kpool_t, nullptr, block_dev, crit, marg, cls, logits, stream,
+                             ws_keys);
+  return launch_select<0>(g, ws_qpool, ws_kpool_t, nullptr, nullptr, crit, marg, cls, logits, stream,
+                             ws_keys);
 }
 
 }  // namespace sla

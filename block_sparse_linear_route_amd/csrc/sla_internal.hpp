@@ -6,6 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+
 namespace sla {
 
 // Validated problem geometry (all sizes checked by the API layer).
@@ -36,11 +37,27 @@ struct Fp8Out {
   uint8_t* k8;
   float* k_scale;
 };
+// ws_keys non-null: the logits go through memory (route_key_bytes(g) of
+// workspace) and the selection runs as a kernel of its own; null: one fused
+// kernel keeps them in LDS.
+constexpr size_t kRouteKeyBytes = size_t(512) << 20;   // keys of one pass over heads, at most
+inline int route_key_nkbp(const Geometry& g) { return (g.nkb + 63) / 64 * 64; }
+// heads whose keys one pass holds (all, or as many as fit kRouteKeyBytes)
+inline int route_key_heads(const Geometry& g) {
+  const size_t per = static_cast<size_t>(g.nq) * route_key_nkbp(g) * 8;
+  const size_t fit = kRouteKeyBytes / per;
+  const size_t bh = static_cast<size_t>(g.B) * g.H;
+  return static_cast<int>(fit < 1 ? 1 : (fit < bh ? fit : bh));
+}
+inline size_t route_key_bytes(const Geometry& g) {
+  return static_cast<size_t>(route_key_heads(g)) * g.nq * route_key_nkbp(g) * 8;
+}
 hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t* crit,
                         int32_t* marg, int8_t* cls, float* logits, float* pooled_q,
                         float* pooled_k, double* ws_qpool, double* ws_kpool_t,
                         double* ws_kvar_t, float* key_var, hipStream_t stream,
-                        const double* block_dev = nullptr, const Fp8Out* f8 = nullptr);
+                        const double* block_dev = nullptr, const Fp8Out* f8 = nullptr,
+                        uint64_t* ws_keys = nullptr);
 
 // exp_map: phi(k) = exp(k) elementwise instead of the softmax over features.
 // v8 non-null (softmax map only): also the E4M3 codes and scales of V.

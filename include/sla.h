@@ -129,7 +129,9 @@ int sla_num_blocks(const sla_problem* problem, int32_t* nq, int32_t* nkb);
  * B*H*2*ceil(nkb/64)*(nq rounded up to 512) 32-bit words of marginal-mask
  * bits and bf16 [B,H,nkb,2d] parts of z, each region 256-byte aligned;
  * SLA_OP_ROUTE
- * needs float64 pooled Q and K, SLA_OP_ROUTE_TAYLOR those and float64 block
+ * needs float64 pooled Q and K and the 64-bit selection keys of one pass
+ * over heads (nq x nkb rounded up to 64 per head, as many heads as fit
+ * 512 MiB, at least one), SLA_OP_ROUTE_TAYLOR those and float64 block
  * key variances; SLA_OP_FORWARD_PISA needs bf16 block means of K and V
  * [B,H,64*ceil(nkb/64),d], a bf16 Hbar [B,H,d,d] and float32 per-chunk
  * partial sums of the first-order matrices; SLA_OP_BACKWARD needs the
@@ -150,7 +152,10 @@ int sla_workspace_size(const sla_problem* problem, int op, size_t* bytes);
  * pooled_k     out float [B,H,nb,d] or NULL: block means rounded to float32
  * ws           workspace of sla_workspace_size(SLA_OP_ROUTE) bytes.
  * Pooling and logits are evaluated in float64, so the ranking follows the
- * exact block means up to summation order. */
+ * exact block means up to summation order.  The logits go as a tiled
+ * product into the workspace's keys, then a second kernel selects; the keys,
+ * and so the lists, are those of the one-kernel path sla_route_noalloc
+ * takes. */
 int sla_route(const sla_problem* problem, const void* q, const void* k,
               int32_t* crit_idx, int32_t* marg_idx, int8_t* block_class,
               float* block_logits, float* pooled_q, float* pooled_k, void* ws,
@@ -181,8 +186,10 @@ int sla_route_quantize(const sla_problem* problem, const void* q, const void* k,
  * device array of SLA_STATIC_SCRATCH_BYTES that the library holds on every
  * GPU it runs on until the process ends (its device address is looked up
  * once per device on the first call there).  The call allocates nothing.
- * Returns SLA_ERR_WORKSPACE when sla_workspace_size(SLA_OP_ROUTE) exceeds
- * SLA_STATIC_SCRATCH_BYTES (at head_dim 128: B * H * nkb > 32768).  Every
+ * The selection runs as one fused kernel (keys in LDS), so only the pooled
+ * sums need the scratch: returns SLA_ERR_WORKSPACE when those, 16 * B * H *
+ * nkb * d bytes, exceed SLA_STATIC_SCRATCH_BYTES (at head_dim 128:
+ * B * H * nkb > 32768).  Every
  * call on one GPU shares that GPU's array, whatever the stream: calls that
  * overlap in time on one GPU race on it and must be serialised by the
  * caller (one stream, or events). */

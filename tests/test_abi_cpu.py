@@ -280,7 +280,8 @@ def test_noalloc_route_rejects_sizes_past_the_static_scratch_before_any_device_c
     fits = P(batch=32, heads=1, seq_len=64 * 1024, stride_h=64 * 1024 * 128, stride_b=64 * 1024 * 128)
     n = ctypes.c_size_t()
     assert lib.sla_workspace_size(ctypes.byref(fits), _lib.OP_ROUTE, ctypes.byref(n)) == 0
-    assert n.value == _lib.SLA_STATIC_SCRATCH_BYTES
+    # the caller workspace adds the split selection's keys to the pooled sums
+    assert n.value == _lib.SLA_STATIC_SCRATCH_BYTES + 32 * 1024 * 1024 * 8
     big = P(batch=33, heads=1, seq_len=64 * 1024, stride_h=64 * 1024 * 128, stride_b=64 * 1024 * 128)
     st = lib.sla_route_noalloc(ctypes.byref(big), fake, fake, fake, fake, None, None, None, None, None)
     assert st == _lib.SLA_ERR_WORKSPACE
@@ -304,3 +305,19 @@ def test_list_validator_without_a_device_returns_no_device():
     assert lib.sla_validate_lists(ctypes.byref(P()), fake, fake, None) == _lib.SLA_ERR_NO_DEVICE
     # a list the count makes unnecessary may be NULL
     assert lib.sla_validate_lists(ctypes.byref(P(k_crit=0)), None, fake, None) == _lib.SLA_ERR_NO_DEVICE
+
+
+def test_route_workspace_holds_the_keys_of_as_many_heads_as_fit_512_mib():
+    # pooled Q and K in float64, then u64 keys [heads][nq][nkb rounded to 64]
+    # for min(B*H, 512 MiB / per-head keys) heads (at least one)
+    n = ctypes.c_size_t()
+    for (b, h, nkb) in [(1, 12, 512), (1, 40, 1182), (2, 4, 4096), (1, 1, 4096), (1, 3, 7)]:
+        N = 64 * nkb
+        p = P(batch=b, heads=h, seq_len=N, stride_h=N * 128, stride_b=h * N * 128)
+        assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_ROUTE, ctypes.byref(n)) == 0
+        align = lambda x: (x + 255) // 256 * 256
+        pooled = align(b * h * nkb * 128 * 8)
+        nkbp = (nkb + 63) // 64 * 64
+        per = nkb * nkbp * 8
+        heads = max(1, min(b * h, (512 << 20) // per))
+        assert n.value == 2 * pooled + align(heads * per), (b, h, nkb)
