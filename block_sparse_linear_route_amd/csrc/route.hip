@@ -510,18 +510,27 @@ hipError_t launch_select_rk(const Geometry& g, int nkbp, const double* qpool,
 // with the keys in between in memory ([heads][nq][nkbp] u64, ~0 past nkb).
 //
 // logits_kernel: one workgroup per 64 x 64 tile of (query block, KV block)
-// pairs of one head; thread t owns rows 4 (t / 16) .. +3 and columns
-// 4 (t % 16) .. +3 of the tile.  The pooled rows go through LDS 16 features
-// at a time (the next chunk loaded into registers while the current one is
-// used), so each pooled value read from L2 serves 64 logits; in the fused
-// kernel a row group reads the head's whole pooled K for R rows.  Every
-// logit is the same float64 FMA chain over the features in ascending order
-// as in the fused kernel (then the division by sqrt(d) and, per score mode,
-// the same added term), so the keys are the fused kernel's bit for bit;
-// only the covariance score's |qbar_i| is summed here in ascending feature
-// order.
+// pairs of one head, each wave a 32 x 32 quarter of it as 2 x 2 products
+// on the float64 matrix cores (v_mfma_f64_16x16x4_f64).  The pooled rows go
+// through LDS 16 features at a time (the next chunk loaded into registers
+// while the current one is used), so each pooled value read from L2 serves
+// 64 logits; in the fused kernel a row group reads the head's whole pooled
+// K for R rows.  The matrix core accumulates each output as a chain of
+// fused multiply-adds over its four k-slots in ascending order (checked on
+// the device against the plain FMA chain: bit-equal on random operands
+// spanning 2^40 in magnitude, where a single-rounding four-term dot or a
+// tree of rounded products differs in ~80% of outputs), and the k-slots of
+// successive products take features in ascending order, so every logit is
+// the fused kernel's FMA chain bit for bit, then the same division by
+// sqrt(d) and added term.  Only the covariance score's |qbar_i| is summed
+// here in ascending feature order.
+//
+// Operand layouts (16 x 16 x 4): A lane l holds row l % 16 at k-slot l / 16,
+// B lane l holds k-slot l / 16 at column l % 16; the result's lane l holds
+// rows l / 16 + 4 x (x = 0..3) at column l % 16.
 constexpr int kLT = 64;   // tile rows and columns
 constexpr int kLA = 16;   // features per LDS chunk
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <int SCORE>
 __global__ void __launch_bounds__(kThreads)
@@ -543,8 +552,9 @@ logits_kernel(Geometry g, int nkbp, int bh0, int nbh, const double* __restrict__
   const int bhl = logical / (tc_n * tr_n);
   const int bh = bh0 + bhl;
   const int i0 = rt * kLT, j0 = ct * kLT;
-  const int t = threadIdx.x;
-  const int tr = t >> 4, tc = t & 15;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;   // this wave's quarter
+  const int l16 = lane & 15, kslot = lane >> 4;
 
   // staging: Q rows t / 4, features 4 (t % 4) .. +3 of the chunk (stored
   // transposed); K^T (and variance) feature t / 16, columns 4 (t % 16) .. +3
@@ -566,13 +576,13 @@ logits_kernel(Geometry g, int nkbp, int bh0, int nbh, const double* __restrict__
     }
   };
 
-  double acc[4][4], acc2[TAYLOR ? 4 : 1][TAYLOR ? 4 : 1];
+  f64x4 acc[2][2], acc2[TAYLOR ? 2 : 1][TAYLOR ? 2 : 1];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      acc[m][n] = 0.0;
-      if constexpr (TAYLOR) acc2[m][n] = 0.0;
+    for (int n = 0; n < 2; ++n) {
+      acc[m][n] = f64x4{0.0, 0.0, 0.0, 0.0};
+      if constexpr (TAYLOR) acc2[m][n] = f64x4{0.0, 0.0, 0.0, 0.0};
     }
   double ss = 0.0;   // COV: sum of squares of row t (t < 64)
 
@@ -594,26 +604,28 @@ logits_kernel(Geometry g, int nkbp, int bh0, int nbh, const double* __restrict__
       }
     }
 #pragma unroll
-    for (int a = 0; a < kLA; ++a) {
-      const f64x2 q01 = *reinterpret_cast<const f64x2*>(&qs[a][4 * tr]);
-      const f64x2 q23 = *reinterpret_cast<const f64x2*>(&qs[a][4 * tr + 2]);
-      const f64x2 k01 = *reinterpret_cast<const f64x2*>(&ks[a][4 * tc]);
-      const f64x2 k23 = *reinterpret_cast<const f64x2*>(&ks[a][4 * tc + 2]);
-      const double qv[4] = {q01[0], q01[1], q23[0], q23[1]};
-      const double kv[4] = {k01[0], k01[1], k23[0], k23[1]};
+    for (int kk = 0; kk < kLA / 4; ++kk) {
+      const int a = 4 * kk + kslot;
+      double af[2], bf[2];
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 2; ++m) af[m] = qs[a][wr + 16 * m + l16];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc[m][n] = fma(qv[m], kv[n], acc[m][n]);
+      for (int n = 0; n < 2; ++n) bf[n] = ks[a][wc + 16 * n + l16];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[m], bf[n], acc[m][n], 0, 0, 0);
       if constexpr (TAYLOR) {
-        const f64x2 v01 = *reinterpret_cast<const f64x2*>(&vs[a][4 * tc]);
-        const f64x2 v23 = *reinterpret_cast<const f64x2*>(&vs[a][4 * tc + 2]);
-        const double vv[4] = {v01[0], v01[1], v23[0], v23[1]};
+        double vf[2];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const double q2 = qv[m] * qv[m];
+        for (int n = 0; n < 2; ++n) vf[n] = vs[a][wc + 16 * n + l16];
 #pragma unroll
-          for (int n = 0; n < 4; ++n) acc2[m][n] = fma(q2, vv[n], acc2[m][n]);
+        for (int m = 0; m < 2; ++m) {
+          const double q2 = af[m] * af[m];
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+            acc2[m][n] = __builtin_amdgcn_mfma_f64_16x16x4f64(q2, vf[n], acc2[m][n], 0, 0, 0);
         }
       }
     }
@@ -624,24 +636,24 @@ logits_kernel(Geometry g, int nkbp, int bh0, int nbh, const double* __restrict__
   }
 
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int i = i0 + 4 * tr + m;
-    if (i >= nq) continue;
-    uint64_t kr[4];
+  for (int n = 0; n < 2; ++n) {
+    const int jl = wc + 16 * n + l16;
+    const int j = j0 + jl;
+    const double md = COV && j < nkb ? mdev[static_cast<int64_t>(bh) * nkb + j] : 0.0;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int j = j0 + 4 * tc + n;
-      double sv = acc[m][n] / sqrt_d;
-      if constexpr (TAYLOR) sv += log1p(acc2[m][n] * inv_2d);
-      // (the staging columns 4 (t % 16) + n are this thread's output columns)
-      if constexpr (COV) sv += log1p(cq[4 * tr + m] * mdev[static_cast<int64_t>(bh) * nkb + kcol[n]]);
-      kr[n] = j < nkb ? desc_key(sv) : ~0ull;
-      if (j < nkb && logits_out)
-        logits_out[(static_cast<int64_t>(bh) * nq + i) * nkb + j] = static_cast<float>(sv);
-    }
-    uint64_t* krow = keys + (static_cast<int64_t>(bhl) * nq + i) * nkbp + j0 + 4 * tc;
-    *reinterpret_cast<u64x2*>(krow) = u64x2{kr[0], kr[1]};
-    *reinterpret_cast<u64x2*>(krow + 2) = u64x2{kr[2], kr[3]};
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int il = wr + 16 * m + kslot + 4 * x;
+        const int i = i0 + il;
+        if (i >= nq) continue;
+        double sv = acc[m][n][x] / sqrt_d;
+        if constexpr (TAYLOR) sv += log1p(acc2[m][n][x] * inv_2d);
+        if constexpr (COV) sv += log1p(cq[il] * md);
+        keys[(static_cast<int64_t>(bhl) * nq + i) * nkbp + j] = j < nkb ? desc_key(sv) : ~0ull;
+        if (j < nkb && logits_out)
+          logits_out[(static_cast<int64_t>(bh) * nq + i) * nkb + j] = static_cast<float>(sv);
+      }
   }
 }
 
