@@ -25,8 +25,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
-typedef double f64x2 __attribute__((ext_vector_type(2)));
-typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 64;
 constexpr int kThreads = 256;

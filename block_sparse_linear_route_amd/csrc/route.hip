@@ -556,20 +556,22 @@ logits_kernel(Geometry g, int nkbp, int bh0, int nbh, const double* __restrict__
   const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;   // this wave's quarter
   const int l16 = lane & 15, kslot = lane >> 4;
 
-  // staging: Q rows t / 4, features 4 (t % 4) .. +3 of the chunk (stored
-  // transposed); K^T (and variance) feature t / 16, columns 4 (t % 16) .. +3
-  const int sq_row = t >> 2, sq_a = (t & 3) * 4;
+  // staging, kSV values per thread: Q rows t / 4, features kSV (t % 4) ..
+  // of the chunk (stored transposed); K^T (and variance) feature t / (64 /
+  // kSV), columns kSV (t % (64 / kSV)) ..
+  constexpr int kSV = kLA / 4;
+  const int sq_row = t >> 2, sq_a = (t & 3) * kSV;
   const double* gq = qpool + (static_cast<int64_t>(bh) * nq + min(i0 + sq_row, nq - 1)) * D + sq_a;
-  const int sk_a = t >> 4, sk_c = (t & 15) * 4;
-  int64_t kcol[4];
+  const int sk_a = t / (kLT / kSV), sk_c = (t % (kLT / kSV)) * kSV;
+  int64_t kcol[kSV];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) kcol[n] = min(j0 + sk_c + n, nkb - 1);
+  for (int n = 0; n < kSV; ++n) kcol[n] = min(j0 + sk_c + n, nkb - 1);
   const double* gk = kpool_t + (static_cast<int64_t>(bh) * D + sk_a) * nkb;
   const double* gv = TAYLOR ? kvar_t + (static_cast<int64_t>(bh) * D + sk_a) * nkb : nullptr;
-  double rq[4], rk[4], rv[TAYLOR ? 4 : 1];
+  double rq[kSV], rk[kSV], rv[TAYLOR ? kSV : 1];
   auto fetch = [&](int a0) {
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < kSV; ++n) {
       rq[n] = gq[a0 + n];
       rk[n] = gk[static_cast<int64_t>(a0) * nkb + kcol[n]];
       if constexpr (TAYLOR) rv[n] = gv[static_cast<int64_t>(a0) * nkb + kcol[n]];
@@ -590,7 +592,7 @@ logits_kernel(Geometry g, int nkbp, int bh0, int nbh, const double* __restrict__
   for (int a0 = 0; a0 < D; a0 += kLA) {
     __syncthreads();
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < kSV; ++n) {
       qs[sq_a + n][sq_row] = rq[n];
       ks[sk_a][sk_c + n] = rk[n];
       if constexpr (TAYLOR) vs[sk_a][sk_c + n] = rv[n];
