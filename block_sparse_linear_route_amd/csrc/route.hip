@@ -322,40 +322,35 @@ __device__ __forceinline__ void select_row(const uint64_t* rk, int nkb, int lane
   }
 }
 
-// grid (ceil(nq / R), B*H), dynamic LDS: keys [R][nkbp] u64, per-wave
-// histograms of 256 16-bit bins packed two to a word ([4][128] u32; a bin
-// never counts more than nkb <= 4096 keys).
+// The fused routing kernel (plain score; the routing path of
+// sla_route_noalloc, whose static scratch holds no key buffer).
+// One-dimensional grid of ceil(nq / R) row groups x B*H, dynamic LDS: keys
+// [R][nkbp] u64, per-wave histograms of 256 16-bit bins packed two to a word
+// ([4][128] u32; a bin never counts more than nkb <= 4096 keys).
 //
 // Phase 1 (whole workgroup): thread t owns KV blocks j = t + 512 m and
 // t + 256 + 512 m and computes the float64 logits of the R query blocks
 // against them, so each pooled-K value read serves R logits; the pooled-Q
 // rows are uniform across the workgroup and are read as scalar operands,
-// each serving two logits.  Results go to LDS as keys.
-// SCORE selects the logit: 0 the plain pooled dot product; 1 (second-order
-// score) accumulates the second-order term beside the dot product, from the
-// same scalar pooled-Q values squared and the block variances laid out like
-// the pooled K.
+// each serving two logits.  Each logit is one FMA chain over the features in
+// ascending order, divided by sqrt(d).  Results go to LDS as keys.
 // Phase 2: one wave per query block (select_row).
 constexpr int kFC = 4;
 
-template <int R, int KPL, int SCORE>
+template <int R, int KPL>
 __global__ void __launch_bounds__(kThreads)
 select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
-              const double* __restrict__ kpool_t, const double* __restrict__ kvar_t,
-              const double* __restrict__ mdev, double sqrt_d, double inv_2d,
-              int32_t* __restrict__ crit, int32_t* __restrict__ marg, int8_t* __restrict__ cls,
+              const double* __restrict__ kpool_t, double sqrt_d, int32_t* __restrict__ crit,
+              int32_t* __restrict__ marg, int8_t* __restrict__ cls,
               float* __restrict__ logits_out) {
-  constexpr bool TAYLOR = SCORE == 1;
-  constexpr bool COV = SCORE == 2;
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
-  __shared__ double cq[COV ? R : 1];
   uint64_t* keys = reinterpret_cast<uint64_t*>(dyn);                 // [R][nkbp]
   uint32_t* hist = reinterpret_cast<uint32_t*>(keys + R * nkbp);      // [4][128]
 
-  // One-dimensional grid of row groups x B*H, the row group fastest in the
-  // logical order and each XCD given a contiguous range of it: an XCD then
-  // works through its heads one at a time, and the head's pooled keys,
-  // which every row group reads in full, stay in its L2.
+  // The row group fastest in the logical order and each XCD given a
+  // contiguous range of it: an XCD then works through its heads one at a
+  // time, and the head's pooled keys, which every row group reads in full,
+  // stay in its L2.
   const int nq = g.nq, nkb = g.nkb, D = g.D;
   const int ngroups = (nq + R - 1) / R;
   const int logical = xcd_remap(blockIdx.x, ngroups * g.B * g.H);
@@ -368,56 +363,24 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
   for (int r = 0; r < R; ++r)
     qrow[r] = qpool + (static_cast<int64_t>(bh) * nq + min(i0 + r, nq - 1)) * D;
   const double* kt = kpool_t + static_cast<int64_t>(bh) * D * nkb;
-  const double* vt = TAYLOR ? kvar_t + static_cast<int64_t>(bh) * D * nkb : nullptr;
-  if constexpr (COV) {
-    // |qbar_r| / (sqrt(d) B) per row: 256 / R threads per row, then a
-    // shuffle sum over those lanes (R = 2..8: 32..128 lanes, within a wave
-    // when R >= 4)
-    constexpr int TPR = kThreads / R;
-    const int r = t / TPR, e0 = t % TPR;
-    double ss = 0.0;
-    for (int e = e0; e < D; e += TPR) ss = fma(qrow[r][e], qrow[r][e], ss);
-    if constexpr (TPR <= 64) {
-#pragma unroll
-      for (int m = TPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-      if (e0 == 0) cq[r] = sqrt(ss) * inv_2d;
-    } else {
-      // R = 2: 128 threads per row, two waves; wave sums meet in LDS
-      __shared__ double wsum[4];
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-      if (lane == 0) wsum[wave] = ss;
-      __syncthreads();
-      if (t < R) cq[t] = sqrt(wsum[2 * t] + wsum[2 * t + 1]) * inv_2d;
-    }
-    __syncthreads();
-  }
 
   // Two KV blocks per thread (j and j + 256); kFC features per step, the next
   // step's pooled-K values loaded before this step's FMAs.
   for (int j0 = t; j0 < nkbp; j0 += 2 * kThreads) {
     const int jj[2] = {j0, j0 + kThreads};
     const int64_t jl[2] = {jj[0] < nkb ? jj[0] : 0, jj[1] < nkb ? jj[1] : 0};
-    double acc[2][R], acc2[TAYLOR ? 2 : 1][TAYLOR ? R : 1];
+    double acc[2][R];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        acc[x][r] = 0.0;
-        if constexpr (TAYLOR) acc2[x][r] = 0.0;
-      }
-    const int qz = 0;
+      for (int r = 0; r < R; ++r) acc[x][r] = 0.0;
     double kv[2][kFC], qv[R][kFC];
-    double vv[TAYLOR ? 2 : 1][kFC], vn[TAYLOR ? 2 : 1][kFC];
 #pragma unroll
     for (int e = 0; e < kFC; ++e) {
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        kv[x][e] = kt[static_cast<int64_t>(e) * nkb + jl[x]];
-        if constexpr (TAYLOR) vv[x][e] = vt[static_cast<int64_t>(e) * nkb + jl[x]];
-      }
+      for (int x = 0; x < 2; ++x) kv[x][e] = kt[static_cast<int64_t>(e) * nkb + jl[x]];
 #pragma unroll
-      for (int r = 0; r < R; ++r) qv[r][e] = qrow[r][e + qz];
+      for (int r = 0; r < R; ++r) qv[r][e] = qrow[r][e];
     }
 #pragma unroll 2
     for (int a0 = 0; a0 < D; a0 += kFC) {
@@ -426,12 +389,9 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
 #pragma unroll
       for (int e = 0; e < kFC; ++e) {
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          kn[x][e] = kt[static_cast<int64_t>(an + e) * nkb + jl[x]];
-          if constexpr (TAYLOR) vn[x][e] = vt[static_cast<int64_t>(an + e) * nkb + jl[x]];
-        }
+        for (int x = 0; x < 2; ++x) kn[x][e] = kt[static_cast<int64_t>(an + e) * nkb + jl[x]];
 #pragma unroll
-        for (int r = 0; r < R; ++r) qn[r][e] = qrow[r][an + e + qz];
+        for (int r = 0; r < R; ++r) qn[r][e] = qrow[r][an + e];
       }
 #pragma unroll
       for (int r = 0; r < R; ++r)
@@ -439,19 +399,11 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
         for (int e = 0; e < kFC; ++e) {
           acc[0][r] = fma(qv[r][e], kv[0][e], acc[0][r]);
           acc[1][r] = fma(qv[r][e], kv[1][e], acc[1][r]);
-          if constexpr (TAYLOR) {
-            const double q2 = qv[r][e] * qv[r][e];
-            acc2[0][r] = fma(q2, vv[0][e], acc2[0][r]);
-            acc2[1][r] = fma(q2, vv[1][e], acc2[1][r]);
-          }
         }
 #pragma unroll
       for (int e = 0; e < kFC; ++e) {
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          kv[x][e] = kn[x][e];
-          if constexpr (TAYLOR) vv[x][e] = vn[x][e];
-        }
+        for (int x = 0; x < 2; ++x) kv[x][e] = kn[x][e];
 #pragma unroll
         for (int r = 0; r < R; ++r) qv[r][e] = qn[r][e];
       }
@@ -462,9 +414,7 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
       if (j >= nkbp) continue;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        double sv = acc[x][r] / sqrt_d;
-        if constexpr (TAYLOR) sv += log1p(acc2[x][r] * inv_2d);
-        if constexpr (COV) sv += log1p(cq[r] * mdev[static_cast<int64_t>(bh) * nkb + jl[x]]);
+        const double sv = acc[x][r] / sqrt_d;
         const bool ok = i0 + r < nq && j < nkb;
         keys[r * nkbp + j] = ok ? desc_key(sv) : ~0ull;
         if (ok && logits_out)
@@ -482,26 +432,23 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
   }
 }
 
-template <int R, int KPL, int SCORE>
+template <int R, int KPL>
 hipError_t launch_select_rk(const Geometry& g, int nkbp, const double* qpool,
-                            const double* kpool_t, const double* kvar_t, const double* mdev,
-                            int32_t* crit, int32_t* marg, int8_t* cls, float* logits,
-                            hipStream_t stream) {
+                            const double* kpool_t, int32_t* crit, int32_t* marg, int8_t* cls,
+                            float* logits, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(R) * nkbp * 8 + 4 * 128 * 4;
   if (lds > 65536) {
     // more than 64 KB of dynamic LDS has to be allowed for the kernel (on
     // the current device)
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<R, KPL, SCORE>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<R, KPL>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
   dim3 grid(((g.nq + R - 1) / R) * g.B * g.H);
   const double sqrt_d = __builtin_sqrt(static_cast<double>(g.D));
-  // second-order score: 1 / (2 d); covariance score: 1 / (sqrt(d) B)
-  const double inv_2d = SCORE == 2 ? 1.0 / (sqrt_d * kBlock) : 1.0 / (2.0 * g.D);
-  hipLaunchKernelGGL((select_kernel<R, KPL, SCORE>), grid, dim3(kThreads), lds, stream, g, nkbp,
-                     qpool, kpool_t, kvar_t, mdev, sqrt_d, inv_2d, crit, marg, cls, logits);
+  hipLaunchKernelGGL((select_kernel<R, KPL>), grid, dim3(kThreads), lds, stream, g, nkbp, qpool,
+                     kpool_t, sqrt_d, crit, marg, cls, logits);
   return hipGetLastError();
 }
 
@@ -709,11 +656,12 @@ hipError_t launch_select_split(const Geometry& g, const double* qpool, const dou
   return hipSuccess;
 }
 
-// Eight query rows per workgroup (every pooled-K value read serves eight
-// logits) up to nkb = 1024, then four and two, so that the key rows stay
-// within 64 KB of LDS and several workgroups share a CU (the kernel is
-// latency-bound; at nkb = 1182 four rows measured faster than eight).  Keys
-// per lane cover the row (nkb <= 4096).
+// With key workspace (every score mode): the split path.  Without it (the
+// plain score of sla_route_noalloc): the fused kernel, eight query rows per
+// workgroup (every pooled-K value read serves eight logits) up to
+// nkb = 1024, then four and two, so that the key rows stay within 64 KB of
+// LDS and several workgroups share a CU (at nkb = 1182 four rows measured
+// faster than eight).  Keys per lane cover the row (nkb <= 4096).
 template <int SCORE>
 hipError_t launch_select(const Geometry& g, const double* qpool, const double* kpool_t,
                          const double* kvar_t, const double* mdev, int32_t* crit, int32_t* marg,
@@ -721,16 +669,13 @@ hipError_t launch_select(const Geometry& g, const double* qpool, const double* k
   if (keys)
     return launch_select_split<SCORE>(g, qpool, kpool_t, kvar_t, mdev, keys, crit, marg, cls,
                                       logits, stream);
+  if (SCORE != 0) return hipErrorInvalidValue;   // the score modes always carry key workspace
   const int nkbp = (g.nkb + 63) / 64 * 64;
-  if (nkbp <= 128)
-    return launch_select_rk<8, 2, SCORE>(g, nkbp, qpool, kpool_t, kvar_t, mdev, crit, marg, cls, logits, stream);
-  if (nkbp <= 512)
-    return launch_select_rk<8, 8, SCORE>(g, nkbp, qpool, kpool_t, kvar_t, mdev, crit, marg, cls, logits, stream);
-  if (nkbp <= 1024)
-    return launch_select_rk<8, 16, SCORE>(g, nkbp, qpool, kpool_t, kvar_t, mdev, crit, marg, cls, logits, stream);
-  if (nkbp <= 2048)
-    return launch_select_rk<4, 32, SCORE>(g, nkbp, qpool, kpool_t, kvar_t, mdev, crit, marg, cls, logits, stream);
-  return launch_select_rk<2, 64, SCORE>(g, nkbp, qpool, kpool_t, kvar_t, mdev, crit, marg, cls, logits, stream);
+  if (nkbp <= 128) return launch_select_rk<8, 2>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+  if (nkbp <= 512) return launch_select_rk<8, 8>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+  if (nkbp <= 1024) return launch_select_rk<8, 16>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+  if (nkbp <= 2048) return launch_select_rk<4, 32>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+  return launch_select_rk<2, 64>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
 }
 
 template <typename T, int D>

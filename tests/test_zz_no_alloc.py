@@ -1,15 +1,21 @@
 """The allocation-free route (sla_route_noalloc, static device scratch)
 against sla_route with a caller workspace: identical index lists, class
 maps, logits and pooled means, on two calls in a row, the second smaller
-than the first (the scratch keeps the first call's contents)."""
+than the first (the scratch keeps the first call's contents).  The two take
+different selection paths (one fused kernel here; tiled logits through the
+workspace, then a selection kernel, in sla_route) whose logits are the same
+FMA chains, so the comparison is bit for bit at every row length the fused
+kernel has an instance for, ties and all-equal rows included."""
 import ctypes
 
+import numpy as np
 import pytest
 import torch
 
 from block_sparse_linear_route_amd import _lib
 from block_sparse_linear_route_amd._lib import lib
 from workloads import make_custom, make_workload
+from workloads.synth import Workload
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -59,6 +65,32 @@ def _check_same(w):
 def test_noalloc_route_equals_route_on_two_calls_second_smaller():
     _check_same(make_workload("video32k"))                                   # 12 heads x 512 blocks
     _check_same(make_custom(1, 2, 1000, 64, dtype="fp32", seed=7, k_crit=3, k_marg=5))
+
+
+@pytest.mark.parametrize("N, H, kc, km, kind", [
+    (64 * 2 - 5, 3, 1, 1, "rand"),        # nkb = 2: 2 keys per lane
+    (64 * 128, 2, 13, 26, "rand"),        # nkb = 128
+    (64 * 300 + 17, 2, 30, 60, "tie"),    # 8 keys per lane, heavy ties
+    (64 * 700, 1, 70, 140, "rand"),       # 16 keys per lane
+    (64 * 1500 - 3, 1, 150, 300, "tie"),  # 32 keys per lane
+    (64 * 4096, 1, 40, 80, "const"),      # 64 keys per lane, every logit equal
+])
+def test_noalloc_route_fused_path_equals_split_path(N, H, kc, km, kind):
+    if kind == "rand":
+        w = make_custom(1, H, N, 128, seed=N % 97, k_crit=kc, k_marg=km)
+    else:
+        rng = np.random.default_rng(N)
+        nkb = (N + 63) // 64
+        if kind == "tie":
+            pat = rng.standard_normal((4, 128))
+            kb = pat[rng.integers(0, 4, nkb)].repeat(64, axis=0)[:N]
+        else:
+            kb = np.ones((N, 128))
+        qv = rng.standard_normal((1, H, N, 128)) if kind == "tie" else np.ones((1, H, N, 128))
+        q = torch.tensor(qv, dtype=torch.bfloat16)
+        k = torch.tensor(np.broadcast_to(kb, (1, H, N, 128)).copy(), dtype=torch.bfloat16)
+        w = Workload(f"{kind}{N}", q, k, k, torch.ones(H), kc, km, {})
+    _check_same(w)
 
 
 def test_noalloc_route_rejects_sizes_past_the_static_scratch():
