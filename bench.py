@@ -99,6 +99,39 @@ def load_traffic(workload: str, fp8: bool = False):
     return t.get("hbm_bytes_per_launch")
 
 
+def load_forward_traffic(workload: str, fp8: bool, B: int, H: int, N: int, d: int):
+    """HBM bytes of one forward (marginal sums and the fused kernel) from the
+    same committed FETCH_SIZE / WRITE_SIZE summary, against the forward's
+    algorithmic bytes: Q, K, V read once (fp8: the E4M3 codes, plus Q in
+    bf16 for the linear branch), S_i and sigma_i once, O written once."""
+    path = os.path.join(ROOT, "profiles", f"attention_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != source_hash(ATTN_FP8_SOURCES if fp8 else ATTN_SOURCES):
+        return None
+    cal = t["copy_calibration"]
+    per = t["per_kernel_kib_raw"]
+    names = ([n for n in per if n.startswith("marg_prep_kernel<") and n.endswith(", 0>")]
+             + [n for n in per if n.startswith("marg_gemm_kernel<") and n.endswith("true, false>")]
+             + [t["kernel"]])
+    if len(names) != 3 or any(n not in per for n in names):
+        return None
+    mb = {n: (per[n]["fetch"] * cal["fetch_factor"] + per[n]["write"] * cal["write_factor"]) * 1024
+          for n in names}
+    nq = (N + 63) // 64
+    per_elem = 7 if fp8 else 8          # bytes per (token, feature) of Q, K, V and O
+    alg = B * H * (per_elem * N * d + nq * d * d * 2 + nq * d * 4)
+    total = sum(mb.values())
+    return {"bytes": total, "algorithmic_bytes": float(alg), "ratio": total / alg,
+            "per_kernel_mb": {n: v / 1e6 for n, v in mb.items()},
+            "note": "per-dispatch FETCH_SIZE + WRITE_SIZE means of the committed profile, each scaled "
+                    "by what the counter reads for a plain copy; the marginal sums write S_i and the "
+                    "fused kernel reads it back, so S_i crosses HBM twice where the algorithmic count "
+                    "has it once, and the mask product reads every state once"}
+
+
 def make_step(sla_gpu, q, k, v, alpha, kc, km):
     """(step, timed) closures over device-resident inputs.
 
@@ -626,6 +659,7 @@ def main():
             "traffic_gbs": None if traffic is None else traffic / (attn_ms * 1e-3) / 1e9,
             "traffic_frac_hbm_peak": None if traffic is None else traffic / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         },
+        "forward_traffic": load_forward_traffic(args.workload, fp8, B, H, N, d),
         "forward_sparse_only_ms": sparse_only_ms,
         "forward_sparse_only_note": "the fused kernel on the same critical lists with k_marg = 0 "
                                     "(no marginal sums, no linear branch)",
