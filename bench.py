@@ -190,7 +190,7 @@ def make_step(sla_gpu, q, k, v, alpha, kc, km):
     return step, timed
 
 
-def config_record(sla_gpu, name: str, steps: int, warmup: int):
+def config_record(sla_gpu, name: str, steps: int, warmup: int, settle_ms: float = 0.0):
     """The bf16 step on another named workload: step and forward time, the
     forward's executed TFLOP/s and the attention kernel's fraction of the
     bf16 MFMA peak (same FLOP accounting as the headline line)."""
@@ -207,6 +207,15 @@ def config_record(sla_gpu, name: str, steps: int, warmup: int):
     alpha = w.alpha.to(dev)
     del w
     step, timed = make_step(sla_gpu, q, k, v, alpha, kc, km)
+    settle_steps = 0
+    if settle_ms > 0:
+        # the GPU idled while the inputs were made: let the clocks ramp again
+        torch.cuda.synchronize()
+        t_settle = time.perf_counter()
+        while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
+            step(None, False)
+            settle_steps += 1
+            torch.cuda.synchronize()
     for _ in range(warmup):
         step(None, False)
     torch.cuda.synchronize()
@@ -221,7 +230,7 @@ def config_record(sla_gpu, name: str, steps: int, warmup: int):
     rec = {
         "workload": f"{name}: B={B} H={H} N={N} d={d} bf16, block 64, "
                     f"k_crit={kc} k_marg={km} of {(N + 63) // 64} KV blocks",
-        "steps": steps, "warmup": warmup,
+        "steps": steps, "warmup": warmup, "settle_steps": settle_steps,
         "ms_per_step": ms_step,
         "step_tflops": f_step / (ms_step * 1e-3) / 1e12,
         "forward_ms": fwd_ms,
@@ -274,6 +283,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="video32k")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed steps run for at least this long before the warm-up steps, so "
+                         "that the GPU clocks have ramped up (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=6,
                     help="heads the oracle runs for the CPU baseline (scaled to all heads)")
@@ -311,6 +323,19 @@ def main():
     alpha = w.alpha.to(dev)
     step, timed = make_step(sla_gpu, q, k, v, alpha, kc, km)
 
+    # The clocks ramp up over the first ~100 ms of GPU work: a 20-step window
+    # right after 5 warm-up steps measured 0.83 ms per step at video32k where
+    # the steady state is 0.75 ms.  Untimed whole steps first, in groups of
+    # ten, until at least settle_ms have passed on the device.
+    settle_steps = 0
+    if args.settle_ms > 0:
+        torch.cuda.synchronize()
+        t_settle = time.perf_counter()
+        while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+            for _ in range(10):
+                r, o = step(None, fp8)
+            settle_steps += 10
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         r, o = step(None, fp8)
     torch.cuda.synchronize()
@@ -618,6 +643,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -677,7 +703,7 @@ def main():
         out["backward"] = bwd_variant
     others = [x for x in args.other_configs.split(",") if x and x != args.workload]
     if others:
-        out["other_configs"] = {name: config_record(sla_gpu, name, args.other_steps, 2)
+        out["other_configs"] = {name: config_record(sla_gpu, name, args.other_steps, 2, args.settle_ms)
                                 for name in others}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, kc, km, f_step, args.cpu_heads)
