@@ -93,6 +93,16 @@ def test_noalloc_route_fused_path_equals_split_path(N, H, kc, km, kind):
     _check_same(w)
 
 
+def test_noalloc_route_fused_path_equals_split_path_over_two_head_passes():
+    # 4096 KV blocks: the keys of one head take 128 MiB, so the split path
+    # runs its logits and selection over heads 0-3, then 4-5
+    s = _s()
+    N, H = 64 * 4096, 6
+    assert s.num_blocks(N) == 4096
+    w = make_custom(1, H, N, 128, kind="iid", seed=11, k_crit=40, k_marg=80)
+    _check_same(w)
+
+
 def test_noalloc_route_rejects_sizes_past_the_static_scratch():
     s = _s()
     # B * H * nkb = 33 * 1024 > 32768 at head_dim 128: no kernel is launched
