@@ -137,9 +137,10 @@ def make_step(sla_gpu, q, k, v, alpha, kc, km):
 
     step(ev, fp8_step) runs route -> states -> marginal sums -> attention on
     torch's current stream; ev (6 events or None) brackets each op, so each
-    event pair times exactly that op's kernels.  timed(n, fp8_step) runs n
-    steps and returns the last routing, the wall ms per step and the mean
-    per-op ms (route, states, -, marginal sums, attention)."""
+    event pair times exactly that op's kernels.  timed(n, fp8_step,
+    with_events) runs n steps and returns the last routing, the wall ms per
+    step and (with events) the mean per-op ms (route, states, -, marginal
+    sums, attention)."""
     import numpy as np
     import torch
 
@@ -174,14 +175,17 @@ def make_step(sla_gpu, q, k, v, alpha, kc, km):
         mark(5)
         return r, o
 
-    def timed(n_steps, fp8_step):
-        events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_steps)]
+    def timed(n_steps, fp8_step, with_events=True):
+        events = ([[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_steps)]
+                  if with_events else [None] * n_steps)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(n_steps):
             r, o = step(events[i], fp8_step)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        if not with_events:
+            return r, (t1 - t0) * 1e3 / n_steps, None
         parts = np.array([[events[i][p].elapsed_time(events[i][p + 1]) for p in range(5)]
                           for i in range(n_steps)])
         timed.last_parts = parts
@@ -219,7 +223,8 @@ def config_record(sla_gpu, name: str, steps: int, warmup: int, settle_ms: float 
     for _ in range(warmup):
         step(None, False)
     torch.cuda.synchronize()
-    r, ms_step, parts = timed(steps, False)
+    r, ms_step, _ = timed(steps, False, with_events=False)
+    r, _, parts = timed(steps, False)
     route_ms, states_ms, _, msum_ms, attn_ms = (float(x) for x in parts)
     fwd_ms = msum_ms + attn_ms
     f_crit, f_lin, f_sums = executed_flops(r["crit_idx"].cpu().numpy(),
@@ -339,7 +344,10 @@ def main():
     for _ in range(args.warmup):
         r, o = step(None, fp8)
     torch.cuda.synchronize()
-    r, ms_step, parts = timed(args.steps, fp8)
+    # the timed steps carry no instrumentation; the per-op breakdown comes
+    # from a second pass of as many steps with an event between ops
+    r, ms_step, _ = timed(args.steps, fp8, with_events=False)
+    r, ms_step_instr, parts = timed(args.steps, fp8)
     route_ms, states_ms, _, msum_ms, attn_ms = parts
     fwd_ms = msum_ms + attn_ms
     attn_pct = np.percentile(timed.last_parts[:, 4], [10, 50, 90])
@@ -382,7 +390,8 @@ def main():
         # the fp8 sparse branch on the same inputs (reported beside the bf16 path)
         for _ in range(2):
             step(None, True)
-        _, ms8, parts8 = timed(max(3, args.steps // 2), True)
+        _, ms8, _ = timed(args.steps, True, with_events=False)
+        _, _, parts8 = timed(max(3, args.steps // 2), True)
         r8_ms, st8_ms, _, ms8_sum, ms8_attn = parts8
         fwd8 = ms8_sum + ms8_attn
         fp8_variant = {
@@ -644,6 +653,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "settle_steps": settle_steps,
+        "ms_per_step_with_op_events": ms_step_instr,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
