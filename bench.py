@@ -349,6 +349,17 @@ def main():
     r, ms_step, _ = timed(args.steps, fp8, with_events=False)
     r, ms_step_instr, parts = timed(args.steps, fp8)
     route_ms, states_ms, _, msum_ms, attn_ms = parts
+    route_states_ms = None
+    if not fp8:
+        # routing and states as one call (sla_route_states: the states pass
+        # also pools K), beside the step's two separate calls
+        ev_rs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev_rs[0].record()
+        for i in range(args.steps):
+            sla_gpu.route_states(q, k, v, kc, km)
+            ev_rs[i + 1].record()
+        torch.cuda.synchronize()
+        route_states_ms = float(np.mean([ev_rs[i].elapsed_time(ev_rs[i + 1]) for i in range(args.steps)]))
     fwd_ms = msum_ms + attn_ms
     attn_pct = np.percentile(timed.last_parts[:, 4], [10, 50, 90])
 
@@ -695,6 +706,9 @@ def main():
             "traffic_gbs": None if traffic is None else traffic / (attn_ms * 1e-3) / 1e9,
             "traffic_frac_hbm_peak": None if traffic is None else traffic / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         },
+        "route_states_ms": route_states_ms,
+        "route_states_note": "sla_route_states (route and states in one call, K read once) "
+                             "against breakdown route + linear_states",
         "forward_traffic": load_forward_traffic(args.workload, fp8, B, H, N, d),
         "forward_sparse_only_ms": sparse_only_ms,
         "forward_sparse_only_note": "the fused kernel on the same critical lists with k_marg = 0 "

@@ -33,6 +33,7 @@ from .ops import (  # noqa: F401
     residual_workspace_subtract,
     route,
     route_noalloc,
+    route_states,
     validate_lists,
     route_pisa,
     route_quantize,

@@ -48,6 +48,7 @@ SIGNATURES = {
                                           _vp, _vp, _sz, _vp]),
     "sla_linear_states_quantize": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "sla_route_noalloc": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "sla_route_states": (ctypes.c_int, [_P] + [_vp] * 12 + [_sz, _vp]),
     "sla_validate_lists": (ctypes.c_int, [_P, _vp, _vp, _vp]),
     "sla_route_taylor": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _sz, _vp]),

@@ -359,6 +359,39 @@ int sla_route(const sla_problem* problem, const void* q, const void* k, int32_t*
                   "sla_route launch");
 }
 
+int sla_route_states(const sla_problem* problem, const void* q, const void* k, const void* v,
+                     int32_t* crit_idx, int32_t* marg_idx, int8_t* block_class, float* block_logits,
+                     float* pooled_q, float* pooled_k, void* h_states, float* z_states, void* ws,
+                     size_t ws_bytes, void* stream) {
+  SLA_TRY(validate_problem(problem));
+  SLA_REQ(q, 16);
+  SLA_REQ(k, 16);
+  SLA_REQ(v, 16);
+  SLA_REQ(h_states, 16);
+  SLA_REQ(z_states, 16);
+  if (problem->k_crit > 0) SLA_REQ(crit_idx, 4);
+  if (problem->k_marg > 0) SLA_REQ(marg_idx, 4);
+  SLA_OPT(block_logits, 4);
+  SLA_OPT(pooled_q, 4);
+  SLA_OPT(pooled_k, 4);
+  const sla::Geometry g = geometry(problem);
+  SLA_TRY(check_ws(ws, ws_bytes, route_ws(g)));
+  SLA_TRY(check_device());
+  double* qpool = static_cast<double*>(ws);
+  double* kpool_t = reinterpret_cast<double*>(static_cast<char*>(ws) + route_region(g));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // bf16: the states pass also pools K; float32 inputs take the two passes
+  const bool fused = g.dtype == 1;
+  SLA_TRY(launched(sla::launch_states(g, k, v, static_cast<uint16_t*>(h_states), z_states, false, st,
+                                      nullptr, nullptr, fused ? kpool_t : nullptr,
+                                      fused ? pooled_k : nullptr),
+                   "sla_route_states states launch"));
+  return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
+                                    pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr, st,
+                                    nullptr, nullptr, route_keys(g, ws), fused),
+                  "sla_route_states route launch");
+}
+
 int sla_route_quantize(const sla_problem* problem, const void* q, const void* k, int32_t* crit_idx,
                        int32_t* marg_idx, int8_t* block_class, float* block_logits,
                        float* pooled_q, float* pooled_k, uint8_t* q8, float* q_scales,

@@ -22,7 +22,8 @@ namespace sla {
 namespace {
 
 // ---------------------------------------------------------------- pooling
-// One-dimensional grid of nb x B*H x 2 (Q, then K) blocks, the block index
+// One-dimensional grid of nb x B*H x nwhich (Q, then K when nwhich = 2;
+// Q alone when the states pass pooled K) blocks, the block index
 // fastest in the logical order and each XCD given a contiguous range of it,
 // so that neighbouring blocks of one head run on one XCD and their 8-byte
 // entries of each transposed pooled-K row meet in the same L2 lines before
@@ -36,7 +37,7 @@ namespace {
 // of the stand-alone quantiser) from the tile already in registers.
 template <typename T, int D, bool VAR, bool QNT = false>
 __global__ void __launch_bounds__(kThreads)
-pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g,
+pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g, int nwhich,
             double* __restrict__ qpool, double* __restrict__ kpool_t,
             float* __restrict__ qout, float* __restrict__ kout,
             double* __restrict__ kvar_t, float* __restrict__ vout,
@@ -49,7 +50,7 @@ pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g,
   __shared__ double mean_s[VAR ? D : 1];
 
   const int bhn = g.B * g.H;
-  const int logical = xcd_remap(blockIdx.x, g.nq * bhn * 2);
+  const int logical = xcd_remap(blockIdx.x, g.nq * bhn * nwhich);
   const int j = logical % g.nq;
   const int bh = (logical / g.nq) % bhn;
   const int which = logical / (g.nq * bhn);
@@ -681,20 +682,20 @@ hipError_t launch_select(const Geometry& g, const double* qpool, const double* k
 template <typename T, int D>
 void launch_pool_t(const Geometry& g, const void* q, const void* k, double* qpool, double* kpool_t,
                    float* qo, float* ko, double* kvar_t, float* vo, hipStream_t stream,
-                   const Fp8Out* f8) {
-  dim3 grid(g.nq * g.B * g.H * 2);
+                   const Fp8Out* f8, int nwhich) {
+  dim3 grid(g.nq * g.B * g.H * nwhich);
   if (f8)
     hipLaunchKernelGGL((pool_kernel<T, D, false, true>), grid, dim3(kThreads), 0, stream,
-                       static_cast<const T*>(q), static_cast<const T*>(k), g, qpool, kpool_t, qo,
-                       ko, nullptr, nullptr, f8->q8, f8->q_scale, f8->k8, f8->k_scale);
+                       static_cast<const T*>(q), static_cast<const T*>(k), g, nwhich, qpool, kpool_t,
+                       qo, ko, nullptr, nullptr, f8->q8, f8->q_scale, f8->k8, f8->k_scale);
   else if (kvar_t)
     hipLaunchKernelGGL((pool_kernel<T, D, true>), grid, dim3(kThreads), 0, stream,
-                       static_cast<const T*>(q), static_cast<const T*>(k), g, qpool, kpool_t, qo,
-                       ko, kvar_t, vo);
+                       static_cast<const T*>(q), static_cast<const T*>(k), g, nwhich, qpool, kpool_t,
+                       qo, ko, kvar_t, vo);
   else
     hipLaunchKernelGGL((pool_kernel<T, D, false>), grid, dim3(kThreads), 0, stream,
-                       static_cast<const T*>(q), static_cast<const T*>(k), g, qpool, kpool_t, qo,
-                       ko, nullptr, nullptr);
+                       static_cast<const T*>(q), static_cast<const T*>(k), g, nwhich, qpool, kpool_t,
+                       qo, ko, nullptr, nullptr);
 }
 
 }  // namespace
@@ -703,17 +704,20 @@ hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t
                         int32_t* marg, int8_t* cls, float* logits, float* pooled_q,
                         float* pooled_k, double* ws_qpool, double* ws_kpool_t,
                         double* ws_kvar_t, float* key_var, hipStream_t stream,
-                        const double* block_dev, const Fp8Out* f8, uint64_t* ws_keys) {
+                        const double* block_dev, const Fp8Out* f8, uint64_t* ws_keys,
+                        bool k_pooled) {
+  if (k_pooled && (f8 || ws_kvar_t || block_dev)) return hipErrorInvalidValue;
+  const int nwhich = k_pooled ? 1 : 2;
   if (g.dtype == 1) {
     if (g.D == 128)
-      launch_pool_t<uint16_t, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8);
+      launch_pool_t<uint16_t, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8, nwhich);
     else
-      launch_pool_t<uint16_t, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8);
+      launch_pool_t<uint16_t, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8, nwhich);
   } else {
     if (g.D == 128)
-      launch_pool_t<float, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8);
+      launch_pool_t<float, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8, nwhich);
     else
-      launch_pool_t<float, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8);
+      launch_pool_t<float, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8, nwhich);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

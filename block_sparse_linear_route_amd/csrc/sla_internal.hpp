@@ -39,7 +39,9 @@ struct Fp8Out {
 };
 // ws_keys non-null: the logits go through memory (route_key_bytes(g) of
 // workspace) and the selection runs as a kernel of its own; null: one fused
-// kernel keeps them in LDS.
+// kernel keeps them in LDS.  k_pooled (plain score, no f8): ws_kpool_t
+// already holds the pooled keys (launch_states with kpool_t), so only Q is
+// pooled.
 constexpr size_t kRouteKeyBytes = size_t(512) << 20;   // keys of one pass over heads, at most
 inline int route_key_nkbp(const Geometry& g) { return (g.nkb + 63) / 64 * 64; }
 // heads whose keys one pass holds (all, or as many as fit kRouteKeyBytes)
@@ -57,13 +59,17 @@ hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t
                         float* pooled_k, double* ws_qpool, double* ws_kpool_t,
                         double* ws_kvar_t, float* key_var, hipStream_t stream,
                         const double* block_dev = nullptr, const Fp8Out* f8 = nullptr,
-                        uint64_t* ws_keys = nullptr);
+                        uint64_t* ws_keys = nullptr, bool k_pooled = false);
 
 // exp_map: phi(k) = exp(k) elementwise instead of the softmax over features.
 // v8 non-null (softmax map only): also the E4M3 codes and scales of V.
+// kpool_t non-null (bf16, softmax map, no v8): also the pooled key rows of
+// the router, float64 transposed [B*H][d][nkb] as the pooling pass writes
+// them (and float32 [B,H,nkb,d] into kout when non-null).
 hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16_t* h_states,
                          float* z_states, bool exp_map, hipStream_t stream,
-                         uint8_t* v8 = nullptr, float* v_scale = nullptr);
+                         uint8_t* v8 = nullptr, float* v_scale = nullptr,
+                         double* kpool_t = nullptr, float* kout = nullptr);
 
 // Marginal-state sums S_i = sum_{j in M_i} H_j (bf16, [B,H,nq,d,d], value-major
 // like the states) and sigma_i = sum_{j in M_i} z_j (float, [B,H,nq,d]); bits

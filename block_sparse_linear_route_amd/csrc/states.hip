@@ -29,17 +29,28 @@ namespace {
 // QNT (low-bit sparse branch): also the V block's E4M3 codes and float32
 // scale ([SLA2 technical summary, section 2.C]; the bytes of the
 // stand-alone quantiser), from the V rows already in registers.
-template <typename T, int D, bool EXPMAP, bool QNT = false>
+// POOLK (bf16 inputs): also the block's pooled key row for the router
+// ([SLA2 technical summary, section 2.B]), the float64 mean of the valid
+// keys, into the transposed pooled-K rows the routing kernels read (and
+// float32 into kout when non-null), so routing needs no second pass over K.
+// The sum runs in the routing pooling kernel's order (rows r, r + RG, ...
+// per row group r, then the row groups in order), so the means are that
+// kernel's bit for bit.
+template <typename T, int D, bool EXPMAP, bool QNT = false, bool POOLK = false>
 __global__ void __launch_bounds__(kThreads)
 states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
               uint16_t* __restrict__ h_out, float* __restrict__ z_out,
-              uint8_t* __restrict__ v8 = nullptr, float* __restrict__ v_scale = nullptr) {
+              uint8_t* __restrict__ v8 = nullptr, float* __restrict__ v_scale = nullptr,
+              double* __restrict__ kpool_t = nullptr, float* __restrict__ kout = nullptr) {
   constexpr int TS = kBlock + 8;        // token stride of the transposed tiles
   constexpr int HS = D + 8;             // row stride of the staged (value-major) output tile
   constexpr int CW = D / 4;             // features per thread (4 threads per token)
   constexpr int TA = D / 32;            // 32-row tiles per dimension
   constexpr int NT = TA * TA / 4;       // output tiles per wave
-  constexpr int SMEM = (2 * D * TS > D * HS) ? 2 * D * TS : D * HS;
+  constexpr int SMEM_OP = (2 * D * TS > D * HS) ? 2 * D * TS : D * HS;
+  // POOLK: the raw key rows, then float64 partial sums [row groups][D]
+  constexpr int SMEM_PK = (64 * HS + 7) / 8 * 8 + (kThreads / (D / 8)) * D * 4;
+  constexpr int SMEM = (POOLK && SMEM_PK > SMEM_OP) ? SMEM_PK : SMEM_OP;
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
   __shared__ float zpart[4][D];
   uint16_t* phi_t = smem;               // [D][TS]: phi(K)^T
@@ -61,6 +72,49 @@ states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
   for (int c = 0; c < CW / 8; ++c) {
     load8_f32(k + off + 8 * c, kv + 8 * c);
     load8_f32(v + off + 8 * c, vv + 8 * c);
+  }
+
+  if constexpr (POOLK) {
+    // raw keys as bf16 (exact: the inputs are bf16) in the smem rows, then
+    // one thread per feature sums its column
+    static_assert(sizeof(T) == 2, "pooled keys from the states pass: bf16 inputs");
+    constexpr int PRG = kThreads / (D / 8);       // row groups of the pooling kernel
+    constexpr int PRPG = kBlock / PRG;            // rows per group
+#pragma unroll
+    for (int c = 0; c < CW; c += 2)
+      *reinterpret_cast<uint32_t*>(&smem[row * HS + part * CW + c]) =
+          static_cast<uint32_t>(f32_to_bf16_bits(kv[c])) |
+          (static_cast<uint32_t>(f32_to_bf16_bits(kv[c + 1])) << 16);
+    __syncthreads();
+    // phase 1, all threads: the partial sum of each (row group, feature) in
+    // row order, 8 row groups per thread; phase 2: one thread per feature
+    // adds its row groups in order
+    static_assert(PRG * D / kThreads == 8, "8 row groups per thread");
+    double* gsum = reinterpret_cast<double*>(smem + (64 * HS + 7) / 8 * 8);   // [PRG][D]
+    {
+      const int c = t % D, rg0 = (t / D) * 8;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int rg = rg0 + x;
+        double acc = 0.0;
+#pragma unroll
+        for (int rr = 0; rr < PRPG; ++rr) {
+          const int r = rg + rr * PRG;
+          acc += r < nj ? static_cast<double>(bf16_to_f32(smem[r * HS + c])) : 0.0;
+        }
+        gsum[rg * D + c] = acc;
+      }
+    }
+    __syncthreads();
+    if (t < D) {
+      double sum = 0.0;
+#pragma unroll
+      for (int rg = 0; rg < PRG; ++rg) sum += gsum[rg * D + t];
+      const double m = sum / static_cast<double>(nj);
+      kpool_t[(static_cast<int64_t>(bh) * D + t) * g.nkb + j] = m;
+      if (kout) kout[(static_cast<int64_t>(bh) * g.nkb + j) * D + t] = static_cast<float>(m);
+    }
+    __syncthreads();   // the rows are read before the operand tiles reuse smem
   }
 
   if constexpr (EXPMAP) {
@@ -170,8 +224,17 @@ states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
 
 template <typename T, int D>
 void launch_states_t(const Geometry& g, const void* k, const void* v, uint16_t* hs, float* zs,
-                     bool exp_map, hipStream_t stream, uint8_t* v8, float* vs) {
+                     bool exp_map, hipStream_t stream, uint8_t* v8, float* vs, double* kpool_t,
+                     float* kout) {
   dim3 grid(g.nkb, g.B * g.H);
+  if constexpr (sizeof(T) == 2) {
+    if (kpool_t) {
+      hipLaunchKernelGGL((states_kernel<T, D, false, false, true>), grid, dim3(kThreads), 0, stream,
+                         static_cast<const T*>(k), static_cast<const T*>(v), g, hs, zs, nullptr,
+                         nullptr, kpool_t, kout);
+      return;
+    }
+  }
   if (v8)
     hipLaunchKernelGGL((states_kernel<T, D, false, true>), grid, dim3(kThreads), 0, stream,
                        static_cast<const T*>(k), static_cast<const T*>(v), g, hs, zs, v8, vs);
@@ -187,13 +250,14 @@ void launch_states_t(const Geometry& g, const void* k, const void* v, uint16_t* 
 
 hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16_t* h_states,
                          float* z_states, bool exp_map, hipStream_t stream, uint8_t* v8,
-                         float* v_scale) {
+                         float* v_scale, double* kpool_t, float* kout) {
+  if (kpool_t && (g.dtype != 1 || exp_map || v8)) return hipErrorInvalidValue;
   if (g.dtype == 1) {
-    if (g.D == 128) launch_states_t<uint16_t, 128>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale);
-    else launch_states_t<uint16_t, 64>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale);
+    if (g.D == 128) launch_states_t<uint16_t, 128>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale, kpool_t, kout);
+    else launch_states_t<uint16_t, 64>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale, kpool_t, kout);
   } else {
-    if (g.D == 128) launch_states_t<float, 128>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale);
-    else launch_states_t<float, 64>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale);
+    if (g.D == 128) launch_states_t<float, 128>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale, nullptr, nullptr);
+    else launch_states_t<float, 64>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale, nullptr, nullptr);
   }
   return hipGetLastError();
 }

@@ -211,6 +211,37 @@ def route_noalloc(q: torch.Tensor, k: torch.Tensor, k_crit: int, k_marg: int, *,
     return out
 
 
+def route_states(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_crit: int, k_marg: int, *,
+                 want_class: bool = False, want_logits: bool = False, want_pooled: bool = False,
+                 stream=None) -> dict:
+    """``route`` and ``linear_states`` in one call (``sla_route_states``): the
+    routing outputs plus h_states, z_states; for bf16 inputs K is read once."""
+    (k, v) = _same_layout(q, k, v)
+    p = make_problem(q, k_crit, k_marg)
+    B, H, N, d = q.shape
+    nb = num_blocks(N)
+    dev = q.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(crit_idx=torch.empty((B, H, nb, k_crit), **i32),
+               marg_idx=torch.empty((B, H, nb, k_marg), **i32),
+               h_states=torch.empty((B, H, nb, d, d), dtype=torch.bfloat16, device=dev),
+               z_states=torch.empty((B, H, nb, d), dtype=torch.float32, device=dev))
+    if want_class:
+        out["block_class"] = torch.empty((B, H, nb, nb), dtype=torch.int8, device=dev)
+    if want_logits:
+        out["block_logits"] = torch.empty((B, H, nb, nb), dtype=torch.float32, device=dev)
+    if want_pooled:
+        out["pooled_q"] = torch.empty((B, H, nb, d), dtype=torch.float32, device=dev)
+        out["pooled_k"] = torch.empty((B, H, nb, d), dtype=torch.float32, device=dev)
+    ws = _workspace(p, _lib.OP_ROUTE, dev)
+    _check(lib.sla_route_states(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out["crit_idx"]),
+                                _ptr(out["marg_idx"]), _ptr(out.get("block_class")),
+                                _ptr(out.get("block_logits")), _ptr(out.get("pooled_q")),
+                                _ptr(out.get("pooled_k")), _ptr(out["h_states"]), _ptr(out["z_states"]),
+                                _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return out
+
+
 def linear_states(k: torch.Tensor, v: torch.Tensor, stream=None, *, feature_map: str = "softmax"):
     """Per-block states: H bf16 [B,H,nkb,d,d], z float32 [B,H,nkb,d].
 

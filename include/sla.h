@@ -175,6 +175,20 @@ int sla_route_quantize(const sla_problem* problem, const void* q, const void* k,
                        float* q_scales, uint8_t* k8, float* k_scales, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* Block routing and the per-block linear states in one call.  [SLA2
+ * summary 2.B; SLA abstract; PISA summary]  Exactly sla_route followed by
+ * sla_linear_states (same arguments, results and errors; h_states and
+ * z_states as sla_linear_states writes them; ws of
+ * sla_workspace_size(SLA_OP_ROUTE) bytes).  For bf16 inputs the states pass
+ * also forms the pooled keys from the K tiles it reads anyway, in the
+ * routing pass's summation order, so K crosses HBM once instead of twice;
+ * float32 inputs take the two passes. */
+int sla_route_states(const sla_problem* problem, const void* q, const void* k,
+                     const void* v, int32_t* crit_idx, int32_t* marg_idx,
+                     int8_t* block_class, float* block_logits, float* pooled_q,
+                     float* pooled_k, void* h_states, float* z_states, void* ws,
+                     size_t ws_bytes, void* stream);
+
 /* Bytes of device scratch the library holds per GPU for the allocation-free
  * entry points. */
 #define SLA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)

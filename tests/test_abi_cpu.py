@@ -130,6 +130,16 @@ def test_entry_points_reject_bad_arguments_before_any_device_call():
     assert st == _lib.SLA_ERR_WORKSPACE              # the plain route workspace is too small
     st = lib.sla_linear_states(ctypes.byref(p), fake, None, fake, fake, None)
     assert st == _lib.SLA_ERR_INVALID_ARGUMENT
+    # route + states: q, k, v, crit, marg, class, logits, pooled q / k, H, z, ws
+    rs = lambda *a: lib.sla_route_states(ctypes.byref(p), *a)
+    assert rs(fake, fake, None, fake, fake, None, None, None, None, fake, fake, fake, 1 << 30, None) \
+        == _lib.SLA_ERR_INVALID_ARGUMENT             # v missing
+    assert rs(fake, fake, fake, fake, fake, None, None, None, None, None, fake, fake, 1 << 30, None) \
+        == _lib.SLA_ERR_INVALID_ARGUMENT             # H missing
+    assert rs(fake, fake, fake, fake, fake, None, None, None, None, fake, odd, fake, 1 << 30, None) \
+        == _lib.SLA_ERR_INVALID_ARGUMENT             # misaligned z
+    assert rs(fake, fake, fake, fake, fake, None, None, None, None, fake, fake, fake, 16, None) \
+        == _lib.SLA_ERR_WORKSPACE
     st = lib.sla_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None, fake,
                          None, None, fake, 1 << 40, None)
     assert st == _lib.SLA_ERR_INVALID_ARGUMENT      # alpha missing
@@ -264,6 +274,9 @@ def test_valid_calls_without_a_device_return_no_device():
     assert st == _lib.SLA_ERR_NO_DEVICE
     assert lib.sla_last_error_message()
     st = lib.sla_linear_states(ctypes.byref(p), fake, fake, fake, fake, None)
+    assert st == _lib.SLA_ERR_NO_DEVICE
+    st = lib.sla_route_states(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, None, None,
+                              fake, fake, fake, n.value, None)
     assert st == _lib.SLA_ERR_NO_DEVICE
     assert lib.sla_workspace_size(ctypes.byref(p), _lib.OP_FORWARD, ctypes.byref(n)) == 0
     st = lib.sla_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,

@@ -125,6 +125,44 @@ def test_route_heavy_exact_ties(nkb, kc, km, n_patterns):
     np.testing.assert_array_equal(r["marg_idx"][0, 0].cpu().numpy(), o["marg_idx"])
 
 
+def _route_states_matches_separate_calls(q, k, v, kc, km):
+    s = _s()
+    got = s.route_states(q, k, v, kc, km, want_class=True, want_logits=True, want_pooled=True)
+    ref = s.route(q, k, kc, km, want_class=True, want_logits=True, want_pooled=True)
+    Hs, zs = s.linear_states(k, v)
+    torch.cuda.synchronize()
+    for name in ("crit_idx", "marg_idx", "block_class", "block_logits", "pooled_q", "pooled_k"):
+        assert torch.equal(got[name], ref[name]), name
+    assert torch.equal(got["h_states"], Hs) and torch.equal(got["z_states"], zs)
+
+
+@pytest.mark.parametrize("name", ["seq8k", "video32k"])
+def test_route_states_equals_route_then_states(name):
+    # bf16: the states pass pools K in the routing pass's order, bit for bit
+    w = make_workload(name)
+    _say(f"[route+states {name}]")
+    _route_states_matches_separate_calls(*_gpu(w), w.k_crit, w.k_marg)
+
+
+@pytest.mark.parametrize("N, d, dtype, kc, km, H, seed", [
+    (1000, 64, "bf16", 3, 5, 2, 81),      # ragged last block, d = 64
+    (19217, 128, "bf16", 70, 30, 1, 82),  # ragged, long lists
+    (777, 128, "fp32", 2, 4, 1, 83),      # float32: the two-pass path
+    (65, 128, "bf16", 1, 0, 3, 84),       # one full block and one of a single token
+])
+def test_route_states_equals_route_then_states_shapes(N, d, dtype, kc, km, H, seed):
+    w = make_custom(1, H, N, d, dtype=dtype, seed=seed, k_crit=kc, k_marg=km)
+    _say(f"[route+states custom N={N} d={d} {dtype}]")
+    _route_states_matches_separate_calls(*_gpu(w), kc, km)
+
+
+def test_route_states_constant_keys():
+    q = torch.randn(1, 2, 64 * 40 + 9, 128).to(torch.bfloat16).to(DEV)
+    k = torch.full_like(q, 0.375)
+    v = torch.randn_like(q.float()).to(torch.bfloat16)
+    _route_states_matches_separate_calls(q, k, v, 5, 9)
+
+
 def test_route_all_logits_equal():
     q = torch.randn(1, 1, 64 * 200, 128).to(torch.bfloat16)
     k = torch.zeros(1, 1, 64 * 200, 128, dtype=torch.bfloat16)
