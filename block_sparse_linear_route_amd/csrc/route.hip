@@ -468,10 +468,12 @@ hipError_t launch_select_rk(const Geometry& g, int nkbp, const double* qpool,
 // the device against the plain FMA chain: bit-equal on random operands
 // spanning 2^40 in magnitude, where a single-rounding four-term dot or a
 // tree of rounded products differs in ~80% of outputs), and the k-slots of
-// successive products take features in ascending order, so every logit is
-// the fused kernel's FMA chain bit for bit, then the same division by
-// sqrt(d) and added term.  Only the covariance score's |qbar_i| is summed
-// here in ascending feature order.
+// successive products take features in ascending order, so each plain
+// logit (then divided by sqrt(d)) is the fused kernel's FMA chain bit for
+// bit.  SCORE 1 adds log1p(t / 2d), t a second such chain over the squared
+// pooled queries (rounded once) and the key variances; SCORE 2 adds
+// log1p(c_i M_j) with c_i = |qbar_i| / (sqrt(d) 64), the squares of qbar_i
+// summed in ascending feature order.
 //
 // Operand layouts (16 x 16 x 4): A lane l holds row l % 16 at k-slot l / 16,
 // B lane l holds k-slot l / 16 at column l % 16; the result's lane l holds
