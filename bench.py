@@ -195,7 +195,7 @@ def make_step(sla_gpu, q, k, v, alpha, kc, km):
 
 
 def config_record(sla_gpu, name: str, steps: int, warmup: int, settle_ms: float = 0.0):
-    """The bf16 step on another named workload: step and forward time, the
+    """The step on another named workload: step and forward time, the
     forward's executed TFLOP/s and the attention kernel's fraction of the
     bf16 MFMA peak (same FLOP accounting as the headline line)."""
     import torch
@@ -233,7 +233,7 @@ def config_record(sla_gpu, name: str, steps: int, warmup: int, settle_ms: float 
     f_step = f_fwd + route_flops(B, H, N, d) + states_flops(B, H, N, d)
     attn_tf = (f_crit + f_lin) / (attn_ms * 1e-3) / 1e12
     rec = {
-        "workload": f"{name}: B={B} H={H} N={N} d={d} bf16, block 64, "
+        "workload": f"{name}: B={B} H={H} N={N} d={d} {'fp32' if q.dtype == torch.float32 else 'bf16'}, block 64, "
                     f"k_crit={kc} k_marg={km} of {(N + 63) // 64} KV blocks",
         "steps": steps, "warmup": warmup, "settle_steps": settle_steps,
         "ms_per_step": ms_step,
@@ -300,7 +300,7 @@ def main():
                     help="skip the piecewise exact-or-approximate attention side measurement")
     ap.add_argument("--no-rla", action="store_true",
                     help="skip the residual-linear-attention side measurement")
-    ap.add_argument("--other-configs", default="seq8k,video75k",
+    ap.add_argument("--other-configs", default="tiny,seq8k,video75k",
                     help="comma-separated bf16 workloads timed after the headline one "
                          "(step, forward, attention fraction of peak); empty for none")
     ap.add_argument("--other-steps", type=int, default=5)
