@@ -195,6 +195,18 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // search ends as soon as that bin holds a single key: that key is the cut.
 // If all 64 bits are consumed, the remaining rank counts equal keys, which
 // are taken in ascending KV block order.
+//
+// Histogram (wh, kHistWords u32 per wave): kHistCopies copies of 256 bins,
+// lane l counting into copy l / 16.  In the first passes most keys share one
+// or two digits (the window holds the sign and the exponent), and LDS atomics
+// on one word from many lanes are serialised; successive copies start
+// kHistStride = 264 words apart, i.e. 8 banks further on, so the four copies
+// of a bin sit in different banks and the lanes of one instruction split
+// four ways.
+constexpr int kHistBins = 256;
+constexpr int kHistCopies = 4;
+constexpr int kHistStride = kHistBins + 8;
+constexpr int kHistWords = kHistCopies * kHistStride;
 template <int KPL>
 __device__ __forceinline__ void select_row(const uint64_t* rk, int nkb, int lane, uint32_t* wh,
                                            int k_crit, int k_marg, int64_t row, int32_t* crit,
@@ -228,26 +240,30 @@ __device__ __forceinline__ void select_row(const uint64_t* rk, int nkb, int lane
 
   while (hi >= 0 && !(done[0] && done[1])) {
     const int lo = hi >= 7 ? hi - 7 : 0;
-    const uint32_t dmask = (2u << (hi - lo)) - 1u;
-    const uint64_t above = ~((2ull << hi) - 1ull);
+    // keys sharing a prefix p (bits above hi; p is zero from hi down) are
+    // those with key - p <= lim, and their digit is (key - p) >> lo < 256
+    const uint64_t lim = (2ull << hi) - 1ull;
     const uint64_t from_lo = ~((1ull << lo) - 1ull);
     const bool shared = !done[0] && !done[1] && pref[0] == pref[1];
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
       if (done[w] || (shared && w == 1)) continue;
-      *reinterpret_cast<u32x2*>(wh + 2 * lane) = u32x2{0u, 0u};
+#pragma unroll
+      for (int h = 0; h < kHistCopies; ++h)
+        *reinterpret_cast<u32x4*>(wh + h * kHistStride + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
       const uint64_t pw = pref[w];
+      uint32_t* whl = wh + (lane >> 4) * kHistStride;
 #pragma unroll
       for (int u = 0; u < KPL; ++u) {
         if (64 * u >= nkb) break;
-        if (lane + 64 * u < nkb && ((kk[u] ^ pw) & above) == 0ull) {
-          const uint32_t bin = static_cast<uint32_t>(kk[u] >> lo) & dmask;
-          atomicAdd(&wh[bin >> 1], 1u << (16 * (bin & 1)));
-        }
+        const uint64_t dk = kk[u] - pw;
+        if (lane + 64 * u < nkb && dk <= lim) atomicAdd(&whl[static_cast<uint32_t>(dk >> lo)], 1u);
       }
       lds_wait();
-      const u32x2 cw = *reinterpret_cast<const u32x2*>(wh + 2 * lane);
-      const u32x4 c = u32x4{cw[0] & 0xffffu, cw[0] >> 16, cw[1] & 0xffffu, cw[1] >> 16};
+      u32x4 c = *reinterpret_cast<const u32x4*>(wh + 4 * lane);
+#pragma unroll
+      for (int h = 1; h < kHistCopies; ++h)
+        c += *reinterpret_cast<const u32x4*>(wh + h * kHistStride + 4 * lane);
       const uint32_t tot = c[0] + c[1] + c[2] + c[3];
       const uint32_t incl = wave_incl_scan(tot, lane);
       const uint32_t excl = incl - tot;
@@ -326,8 +342,7 @@ __device__ __forceinline__ void select_row(const uint64_t* rk, int nkb, int lane
 // The fused routing kernel (plain score; the routing path of
 // sla_route_noalloc, whose static scratch holds no key buffer).
 // One-dimensional grid of ceil(nq / R) row groups x B*H, dynamic LDS: keys
-// [R][nkbp] u64, per-wave histograms of 256 16-bit bins packed two to a word
-// ([4][128] u32; a bin never counts more than nkb <= 4096 keys).
+// [R][nkbp] u64, then the four waves' histograms ([4][kHistWords] u32).
 //
 // Phase 1 (whole workgroup): thread t owns KV blocks j = t + 512 m and
 // t + 256 + 512 m and computes the float64 logits of the R query blocks
@@ -346,7 +361,7 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
               float* __restrict__ logits_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
   uint64_t* keys = reinterpret_cast<uint64_t*>(dyn);                 // [R][nkbp]
-  uint32_t* hist = reinterpret_cast<uint32_t*>(keys + R * nkbp);      // [4][128]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(keys + R * nkbp);      // [4][kHistWords]
 
   // The row group fastest in the logical order and each XCD given a
   // contiguous range of it: an XCD then works through its heads one at a
@@ -428,7 +443,7 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
   for (int r = wave; r < R; r += 4) {
     const int i = i0 + r;
     if (i >= nq) break;
-    select_row<KPL>(keys + r * nkbp, nkb, lane, hist + wave * 128, g.k_crit, g.k_marg,
+    select_row<KPL>(keys + r * nkbp, nkb, lane, hist + wave * kHistWords, g.k_crit, g.k_marg,
                     static_cast<int64_t>(bh) * nq + i, crit, marg, cls);
   }
 }
@@ -437,7 +452,7 @@ template <int R, int KPL>
 hipError_t launch_select_rk(const Geometry& g, int nkbp, const double* qpool,
                             const double* kpool_t, int32_t* crit, int32_t* marg, int8_t* cls,
                             float* logits, hipStream_t stream) {
-  const size_t lds = static_cast<size_t>(R) * nkbp * 8 + 4 * 128 * 4;
+  const size_t lds = static_cast<size_t>(R) * nkbp * 8 + 4 * kHistWords * 4;
   if (lds > 65536) {
     // more than 64 KB of dynamic LDS has to be allowed for the kernel (on
     // the current device)
@@ -616,7 +631,7 @@ __global__ void __launch_bounds__(kThreads)
 select_rows_kernel(Geometry g, int nkbp, int bh0, int nbh, const uint64_t* __restrict__ keys,
                    int32_t* __restrict__ crit, int32_t* __restrict__ marg,
                    int8_t* __restrict__ cls) {
-  __shared__ __attribute__((aligned(16))) uint32_t hist[4][128];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4][kHistWords];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int r = blockIdx.x * 4 + wave;
   if (r >= nbh * g.nq) return;
