@@ -175,12 +175,6 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
          __builtin_amdgcn_readlane(v, 32) | __builtin_amdgcn_readlane(v, 48);
 }
 
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), l);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), l);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------- selection
@@ -192,7 +186,10 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // keys differ (the bits above are common to all keys) and takes 8 bits per
 // pass.  A pass histograms the digit of the keys that share the cut's prefix,
 // a prefix scan of the bins finds the bin holding the cut's rank, and the
-// search ends as soon as that bin holds a single key: that key is the cut.
+// search ends as soon as that bin holds a single key: that key is the cut,
+// and as no other key shares its bits from the window's low end up, the cut
+// is recorded as that prefix with every lower bit set (the largest key with
+// the prefix), which ranks every key exactly as the cut itself would.
 // If all 64 bits are consumed, the remaining rank counts equal keys, which
 // are taken in ascending KV block order.
 //
@@ -243,7 +240,6 @@ __device__ __forceinline__ void select_row(const uint64_t* rk, int nkb, int lane
     // keys sharing a prefix p (bits above hi; p is zero from hi down) are
     // those with key - p <= lim, and their digit is (key - p) >> lo < 256
     const uint64_t lim = (2ull << hi) - 1ull;
-    const uint64_t from_lo = ~((1ull << lo) - 1ull);
     const bool shared = !done[0] && !done[1] && pref[0] == pref[1];
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
@@ -287,16 +283,9 @@ __device__ __forceinline__ void select_row(const uint64_t* rk, int nkb, int lane
         pref[ww] |= static_cast<uint64_t>(b_bin) << lo;
         rem[ww] -= b_cum;
         if (b_cnt == 1u) {
-          // the bin holds one key: it is the cut
-          const uint64_t pv = pref[ww];
-          uint64_t key = pv;
-#pragma unroll
-          for (int u = 0; u < KPL; ++u) {
-            if (64 * u >= nkb) break;
-            const uint64_t bm = __ballot(lane + 64 * u < nkb && ((kk[u] ^ pv) & from_lo) == 0ull);
-            if (bm) key = readlane64(kk[u], __builtin_ctzll(bm));
-          }
-          pref[ww] = key;
+          // the bin holds one key, the cut: no other key shares its bits
+          // from lo up, so the largest key with that prefix stands in for it
+          pref[ww] |= (1ull << lo) - 1ull;
           rem[ww] = 0u;
           done[ww] = true;
         }
