@@ -177,9 +177,10 @@ FwdWs carve_forward_ws(const sla::Geometry& g, void* ws) {
   return w;
 }
 
-// Route workspace: [pooled Q f64 B*H*nq*d][pooled K^T f64 B*H*d*nkb]
+// Route workspace: [pooled Q f64 B*H*nq*d][pooled K f64 B*H*nkb*d]
 // [selection keys u64, route_key_bytes] and, for the second-order score,
-// [key variances^T f64 B*H*d*nkb].
+// [key variances f64 B*H*nkb*d] (the allocation-free route keeps pooled K
+// transposed, B*H*d*nkb, in its static scratch).
 size_t route_region(const sla::Geometry& g) {
   return align_up(static_cast<size_t>(g.B) * g.H * g.nq * g.D * 8);
 }
@@ -351,9 +352,9 @@ int sla_route(const sla_problem* problem, const void* q, const void* k, int32_t*
   SLA_TRY(check_ws(ws, ws_bytes, route_ws(g)));
   SLA_TRY(check_device());
   double* qpool = static_cast<double*>(ws);
-  double* kpool_t = reinterpret_cast<double*>(static_cast<char*>(ws) + route_region(g));
+  double* kpool = reinterpret_cast<double*>(static_cast<char*>(ws) + route_region(g));
   return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
-                                    pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr,
+                                    pooled_q, pooled_k, qpool, kpool, nullptr, nullptr,
                                     static_cast<hipStream_t>(stream), nullptr, nullptr,
                                     route_keys(g, ws)),
                   "sla_route launch");
@@ -378,16 +379,16 @@ int sla_route_states(const sla_problem* problem, const void* q, const void* k, c
   SLA_TRY(check_ws(ws, ws_bytes, route_ws(g)));
   SLA_TRY(check_device());
   double* qpool = static_cast<double*>(ws);
-  double* kpool_t = reinterpret_cast<double*>(static_cast<char*>(ws) + route_region(g));
+  double* kpool = reinterpret_cast<double*>(static_cast<char*>(ws) + route_region(g));
   const hipStream_t st = static_cast<hipStream_t>(stream);
   // bf16: the states pass also pools K; float32 inputs take the two passes
   const bool fused = g.dtype == 1;
   SLA_TRY(launched(sla::launch_states(g, k, v, static_cast<uint16_t*>(h_states), z_states, false, st,
-                                      nullptr, nullptr, fused ? kpool_t : nullptr,
+                                      nullptr, nullptr, fused ? kpool : nullptr,
                                       fused ? pooled_k : nullptr),
                    "sla_route_states states launch"));
   return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
-                                    pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr, st,
+                                    pooled_q, pooled_k, qpool, kpool, nullptr, nullptr, st,
                                     nullptr, nullptr, route_keys(g, ws), fused),
                   "sla_route_states route launch");
 }
@@ -412,10 +413,10 @@ int sla_route_quantize(const sla_problem* problem, const void* q, const void* k,
   SLA_TRY(check_ws(ws, ws_bytes, route_ws(g)));
   SLA_TRY(check_device());
   double* qpool = static_cast<double*>(ws);
-  double* kpool_t = reinterpret_cast<double*>(static_cast<char*>(ws) + route_region(g));
+  double* kpool = reinterpret_cast<double*>(static_cast<char*>(ws) + route_region(g));
   const sla::Fp8Out f8{q8, q_scales, k8, k_scales};
   return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
-                                    pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr,
+                                    pooled_q, pooled_k, qpool, kpool, nullptr, nullptr,
                                     static_cast<hipStream_t>(stream), nullptr, &f8,
                                     route_keys(g, ws)),
                   "sla_route_quantize launch");
@@ -488,10 +489,10 @@ int sla_route_taylor(const sla_problem* problem, const void* q, const void* k, i
   SLA_TRY(check_device());
   char* p = static_cast<char*>(ws);
   double* qpool = reinterpret_cast<double*>(p);
-  double* kpool_t = reinterpret_cast<double*>(p + route_region(g));
-  double* kvar_t = reinterpret_cast<double*>(p + route_ws(g));
+  double* kpool = reinterpret_cast<double*>(p + route_region(g));
+  double* kvar = reinterpret_cast<double*>(p + route_ws(g));
   return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
-                                    pooled_q, pooled_k, qpool, kpool_t, kvar_t, key_var,
+                                    pooled_q, pooled_k, qpool, kpool, kvar, key_var,
                                     static_cast<hipStream_t>(stream), nullptr, nullptr,
                                     route_keys(g, ws)),
                   "sla_route_taylor launch");
@@ -814,7 +815,7 @@ int sla_route_pisa(const sla_problem* problem, const void* q, const void* k, con
   const size_t bh = static_cast<size_t>(g.B) * g.H;
   char* p = static_cast<char*>(ws) + pisa_ws(g);
   double* qpool = reinterpret_cast<double*>(p);
-  double* kpool_t = reinterpret_cast<double*>(p + route_region(g));
+  double* kpool = reinterpret_cast<double*>(p + route_region(g));
   float* hbar_f32 = reinterpret_cast<float*>(p + route_ws(g));
   double* mdev = reinterpret_cast<double*>(p + route_ws(g) + align_up(bh * g.D * g.D * 4));
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -823,7 +824,7 @@ int sla_route_pisa(const sla_problem* problem, const void* q, const void* k, con
   SLA_TRY(launched(sla::launch_pisa_deviation(g, k, v, w.hbar, w.part, hbar_f32, mdev, block_dev, st),
                    "PISA block deviation launch"));
   return launched(sla::launch_route(g, q, k, crit_idx, marg_idx, block_class, block_logits,
-                                    pooled_q, pooled_k, qpool, kpool_t, nullptr, nullptr, st, mdev,
+                                    pooled_q, pooled_k, qpool, kpool, nullptr, nullptr, st, mdev,
                                     nullptr, route_keys(g, p)),
                   "sla_route_pisa launch");
 }

@@ -24,10 +24,13 @@ namespace {
 // ---------------------------------------------------------------- pooling
 // One-dimensional grid of nb x B*H x nwhich (Q, then K when nwhich = 2;
 // Q alone when the states pass pooled K) blocks, the block index
-// fastest in the logical order and each XCD given a contiguous range of it,
-// so that neighbouring blocks of one head run on one XCD and their 8-byte
-// entries of each transposed pooled-K row meet in the same L2 lines before
-// those are written back.  One workgroup per block:
+// fastest in the logical order and each XCD given a contiguous range of it.
+// Pooled K (and the key variances) go out as rows [B*H][nkb][d] when k_rows
+// is set (the split selection, whose logits kernel stages them like pooled
+// Q: one 1 KB row per block), else transposed [B*H][d][nkb] for the fused
+// selection kernel, each of whose threads walks one block's column; there
+// the 8-byte entries of neighbouring blocks, which run on one XCD, meet in
+// the same L2 lines before those are written back.  One workgroup per block:
 // thread t reads the 16-byte chunk t % CH of rows t / CH + RG m (rows past
 // a ragged end load the block's last row and are zeroed, so every load is in
 // flight at once), then LDS sums the row groups in float64.  VAR adds, for
@@ -37,10 +40,10 @@ namespace {
 // of the stand-alone quantiser) from the tile already in registers.
 template <typename T, int D, bool VAR, bool QNT = false>
 __global__ void __launch_bounds__(kThreads)
-pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g, int nwhich,
-            double* __restrict__ qpool, double* __restrict__ kpool_t,
+pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g, int nwhich, int k_rows,
+            double* __restrict__ qpool, double* __restrict__ kpool,
             float* __restrict__ qout, float* __restrict__ kout,
-            double* __restrict__ kvar_t, float* __restrict__ vout,
+            double* __restrict__ kvar, float* __restrict__ vout,
             uint8_t* __restrict__ q8 = nullptr, float* __restrict__ q_scale = nullptr,
             uint8_t* __restrict__ k8 = nullptr, float* __restrict__ k_scale = nullptr) {
   constexpr int CH = D / 8;           // 8-element chunks per row
@@ -101,7 +104,8 @@ pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g, int nw
       qpool[o] = m;
       if (qout) qout[o] = static_cast<float>(m);
     } else {
-      kpool_t[(static_cast<int64_t>(bh) * D + t) * g.nkb + j] = m;
+      kpool[k_rows ? (static_cast<int64_t>(bh) * g.nkb + j) * D + t
+                   : (static_cast<int64_t>(bh) * D + t) * g.nkb + j] = m;
       if (kout) kout[(static_cast<int64_t>(bh) * g.nkb + j) * D + t] = static_cast<float>(m);
       if constexpr (VAR) mean_s[t] = m;
     }
@@ -126,7 +130,8 @@ pool_kernel(const T* __restrict__ q, const T* __restrict__ k, Geometry g, int nw
         double s = 0.0;
         for (int r = 0; r < RG; ++r) s += red[r][t];
         const double var = s / static_cast<double>(nj);
-        kvar_t[(static_cast<int64_t>(bh) * D + t) * g.nkb + j] = var;
+        kvar[k_rows ? (static_cast<int64_t>(bh) * g.nkb + j) * D + t
+                    : (static_cast<int64_t>(bh) * D + t) * g.nkb + j] = var;
         if (vout) vout[(static_cast<int64_t>(bh) * g.nkb + j) * D + t] = static_cast<float>(var);
       }
     }
@@ -484,19 +489,23 @@ hipError_t launch_select_rk(const Geometry& g, int nkbp, const double* qpool,
 // rows l / 16 + 4 x (x = 0..3) at column l % 16.
 constexpr int kLT = 64;   // tile rows and columns
 constexpr int kLA = 16;   // features per LDS chunk
+constexpr int kKS = kLA + 2;   // LDS row of a pooled-K chunk
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <int SCORE>
 __global__ void __launch_bounds__(kThreads)
 logits_kernel(Geometry g, int nkbp, int bh0, int nbh, const double* __restrict__ qpool,
-              const double* __restrict__ kpool_t, const double* __restrict__ kvar_t,
+              const double* __restrict__ kpool, const double* __restrict__ kvar,
               const double* __restrict__ mdev, double sqrt_d, double inv_2d,
               uint64_t* __restrict__ keys, float* __restrict__ logits_out) {
   constexpr bool TAYLOR = SCORE == 1;
   constexpr bool COV = SCORE == 2;
-  __shared__ __attribute__((aligned(16))) double qs[kLA][kLT];
-  __shared__ __attribute__((aligned(16))) double ks[kLA][kLT];
-  __shared__ __attribute__((aligned(16))) double vs[TAYLOR ? kLA : 1][kLT];
+  // pooled Q, K (and variances) row-major with rows of kKS = kLA + 2
+  // values, so a thread's four features go in as two 16-byte stores and the
+  // operand reads below spread over the banks
+  __shared__ __attribute__((aligned(16))) double qs[kLT][kKS];
+  __shared__ __attribute__((aligned(16))) double ks[kLT][kKS];
+  __shared__ __attribute__((aligned(16))) double vs[TAYLOR ? kLT : 1][kKS];
   __shared__ double cq[COV ? kLT : 1];
   const int nq = g.nq, nkb = g.nkb, D = g.D;
   const int tr_n = (nq + kLT - 1) / kLT, tc_n = nkbp / kLT;
@@ -510,25 +519,22 @@ logits_kernel(Geometry g, int nkbp, int bh0, int nbh, const double* __restrict__
   const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;   // this wave's quarter
   const int l16 = lane & 15, kslot = lane >> 4;
 
-  // staging, kSV values per thread: Q rows t / 4, features kSV (t % 4) ..
-  // of the chunk (stored transposed); K^T (and variance) feature t / (64 /
-  // kSV), columns kSV (t % (64 / kSV)) ..
+  // staging, kSV values per thread: pooled-Q row i0 + t / 4 and pooled-K
+  // (and variance) row j0 + t / 4, features kSV (t % 4) .. of the chunk;
+  // rows past the end repeat the last
   constexpr int kSV = kLA / 4;
   const int sq_row = t >> 2, sq_a = (t & 3) * kSV;
   const double* gq = qpool + (static_cast<int64_t>(bh) * nq + min(i0 + sq_row, nq - 1)) * D + sq_a;
-  const int sk_a = t / (kLT / kSV), sk_c = (t % (kLT / kSV)) * kSV;
-  int64_t kcol[kSV];
-#pragma unroll
-  for (int n = 0; n < kSV; ++n) kcol[n] = min(j0 + sk_c + n, nkb - 1);
-  const double* gk = kpool_t + (static_cast<int64_t>(bh) * D + sk_a) * nkb;
-  const double* gv = TAYLOR ? kvar_t + (static_cast<int64_t>(bh) * D + sk_a) * nkb : nullptr;
+  const int64_t krow = (static_cast<int64_t>(bh) * nkb + min(j0 + sq_row, nkb - 1)) * D + sq_a;
+  const double* gk = kpool + krow;
+  const double* gv = TAYLOR ? kvar + krow : nullptr;
   double rq[kSV], rk[kSV], rv[TAYLOR ? kSV : 1];
   auto fetch = [&](int a0) {
 #pragma unroll
     for (int n = 0; n < kSV; ++n) {
       rq[n] = gq[a0 + n];
-      rk[n] = gk[static_cast<int64_t>(a0) * nkb + kcol[n]];
-      if constexpr (TAYLOR) rv[n] = gv[static_cast<int64_t>(a0) * nkb + kcol[n]];
+      rk[n] = gk[a0 + n];
+      if constexpr (TAYLOR) rv[n] = gv[a0 + n];
     }
   };
 
@@ -547,16 +553,16 @@ logits_kernel(Geometry g, int nkbp, int bh0, int nbh, const double* __restrict__
     __syncthreads();
 #pragma unroll
     for (int n = 0; n < kSV; ++n) {
-      qs[sq_a + n][sq_row] = rq[n];
-      ks[sk_a][sk_c + n] = rk[n];
-      if constexpr (TAYLOR) vs[sk_a][sk_c + n] = rv[n];
+      qs[sq_row][sq_a + n] = rq[n];
+      ks[sq_row][sq_a + n] = rk[n];
+      if constexpr (TAYLOR) vs[sq_row][sq_a + n] = rv[n];
     }
     __syncthreads();
     if (a0 + kLA < D) fetch(a0 + kLA);
     if constexpr (COV) {
       if (t < kLT) {
 #pragma unroll
-        for (int a = 0; a < kLA; ++a) ss = fma(qs[a][t], qs[a][t], ss);
+        for (int a = 0; a < kLA; ++a) ss = fma(qs[t][a], qs[t][a], ss);
       }
     }
 #pragma unroll
@@ -564,9 +570,9 @@ logits_kernel(Geometry g, int nkbp, int bh0, int nbh, const double* __restrict__
       const int a = 4 * kk + kslot;
       double af[2], bf[2];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) af[m] = qs[a][wr + 16 * m + l16];
+      for (int m = 0; m < 2; ++m) af[m] = qs[wr + 16 * m + l16][a];
 #pragma unroll
-      for (int n = 0; n < 2; ++n) bf[n] = ks[a][wc + 16 * n + l16];
+      for (int n = 0; n < 2; ++n) bf[n] = ks[wc + 16 * n + l16][a];
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -575,7 +581,7 @@ logits_kernel(Geometry g, int nkbp, int bh0, int nbh, const double* __restrict__
       if constexpr (TAYLOR) {
         double vf[2];
 #pragma unroll
-        for (int n = 0; n < 2; ++n) vf[n] = vs[a][wc + 16 * n + l16];
+        for (int n = 0; n < 2; ++n) vf[n] = vs[wc + 16 * n + l16][a];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           const double q2 = af[m] * af[m];
@@ -630,8 +636,8 @@ select_rows_kernel(Geometry g, int nkbp, int bh0, int nbh, const uint64_t* __res
 }
 
 template <int SCORE>
-hipError_t launch_select_split(const Geometry& g, const double* qpool, const double* kpool_t,
-                               const double* kvar_t, const double* mdev, uint64_t* keys,
+hipError_t launch_select_split(const Geometry& g, const double* qpool, const double* kpool,
+                               const double* kvar, const double* mdev, uint64_t* keys,
                                int32_t* crit, int32_t* marg, int8_t* cls, float* logits,
                                hipStream_t stream) {
   const int nkbp = (g.nkb + 63) / 64 * 64;
@@ -643,7 +649,7 @@ hipError_t launch_select_split(const Geometry& g, const double* qpool, const dou
   for (int bh0 = 0; bh0 < bh_all; bh0 += chunk) {
     const int nbh = bh_all - bh0 < chunk ? bh_all - bh0 : chunk;
     hipLaunchKernelGGL((logits_kernel<SCORE>), dim3(tiles * nbh), dim3(kThreads), 0, stream, g,
-                       nkbp, bh0, nbh, qpool, kpool_t, kvar_t, mdev, sqrt_d, inv_2d, keys, logits);
+                       nkbp, bh0, nbh, qpool, kpool, kvar, mdev, sqrt_d, inv_2d, keys, logits);
     const dim3 sg((nbh * g.nq + 3) / 4);
     if (nkbp <= 128)
       hipLaunchKernelGGL((select_rows_kernel<2>), sg, dim3(kThreads), 0, stream, g, nkbp, bh0, nbh, keys, crit, marg, cls);
@@ -670,70 +676,74 @@ hipError_t launch_select_split(const Geometry& g, const double* qpool, const dou
 // LDS and several workgroups share a CU (at nkb = 1182 four rows measured
 // faster than eight).  Keys per lane cover the row (nkb <= 4096).
 template <int SCORE>
-hipError_t launch_select(const Geometry& g, const double* qpool, const double* kpool_t,
-                         const double* kvar_t, const double* mdev, int32_t* crit, int32_t* marg,
+// kpool (and kvar): rows [B*H][nkb][d] for the split path (keys non-null),
+// transposed [B*H][d][nkb] for the fused kernel
+hipError_t launch_select(const Geometry& g, const double* qpool, const double* kpool,
+                         const double* kvar, const double* mdev, int32_t* crit, int32_t* marg,
                          int8_t* cls, float* logits, hipStream_t stream, uint64_t* keys) {
   if (keys)
-    return launch_select_split<SCORE>(g, qpool, kpool_t, kvar_t, mdev, keys, crit, marg, cls,
+    return launch_select_split<SCORE>(g, qpool, kpool, kvar, mdev, keys, crit, marg, cls,
                                       logits, stream);
   if (SCORE != 0) return hipErrorInvalidValue;   // the score modes always carry key workspace
   const int nkbp = (g.nkb + 63) / 64 * 64;
-  if (nkbp <= 128) return launch_select_rk<8, 2>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
-  if (nkbp <= 512) return launch_select_rk<8, 8>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
-  if (nkbp <= 1024) return launch_select_rk<8, 16>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
-  if (nkbp <= 2048) return launch_select_rk<4, 32>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
-  return launch_select_rk<2, 64>(g, nkbp, qpool, kpool_t, crit, marg, cls, logits, stream);
+  if (nkbp <= 128) return launch_select_rk<8, 2>(g, nkbp, qpool, kpool, crit, marg, cls, logits, stream);
+  if (nkbp <= 512) return launch_select_rk<8, 8>(g, nkbp, qpool, kpool, crit, marg, cls, logits, stream);
+  if (nkbp <= 1024) return launch_select_rk<8, 16>(g, nkbp, qpool, kpool, crit, marg, cls, logits, stream);
+  if (nkbp <= 2048) return launch_select_rk<4, 32>(g, nkbp, qpool, kpool, crit, marg, cls, logits, stream);
+  return launch_select_rk<2, 64>(g, nkbp, qpool, kpool, crit, marg, cls, logits, stream);
 }
 
 template <typename T, int D>
-void launch_pool_t(const Geometry& g, const void* q, const void* k, double* qpool, double* kpool_t,
-                   float* qo, float* ko, double* kvar_t, float* vo, hipStream_t stream,
-                   const Fp8Out* f8, int nwhich) {
+void launch_pool_t(const Geometry& g, const void* q, const void* k, double* qpool, double* kpool,
+                   float* qo, float* ko, double* kvar, float* vo, hipStream_t stream,
+                   const Fp8Out* f8, int nwhich, int k_rows) {
   dim3 grid(g.nq * g.B * g.H * nwhich);
   if (f8)
     hipLaunchKernelGGL((pool_kernel<T, D, false, true>), grid, dim3(kThreads), 0, stream,
-                       static_cast<const T*>(q), static_cast<const T*>(k), g, nwhich, qpool, kpool_t,
-                       qo, ko, nullptr, nullptr, f8->q8, f8->q_scale, f8->k8, f8->k_scale);
-  else if (kvar_t)
+                       static_cast<const T*>(q), static_cast<const T*>(k), g, nwhich, k_rows, qpool,
+                       kpool, qo, ko, nullptr, nullptr, f8->q8, f8->q_scale, f8->k8, f8->k_scale);
+  else if (kvar)
     hipLaunchKernelGGL((pool_kernel<T, D, true>), grid, dim3(kThreads), 0, stream,
-                       static_cast<const T*>(q), static_cast<const T*>(k), g, nwhich, qpool, kpool_t,
-                       qo, ko, kvar_t, vo);
+                       static_cast<const T*>(q), static_cast<const T*>(k), g, nwhich, k_rows, qpool,
+                       kpool, qo, ko, kvar, vo);
   else
     hipLaunchKernelGGL((pool_kernel<T, D, false>), grid, dim3(kThreads), 0, stream,
-                       static_cast<const T*>(q), static_cast<const T*>(k), g, nwhich, qpool, kpool_t,
-                       qo, ko, nullptr, nullptr);
+                       static_cast<const T*>(q), static_cast<const T*>(k), g, nwhich, k_rows, qpool,
+                       kpool, qo, ko, nullptr, nullptr);
 }
 
 }  // namespace
 
 hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t* crit,
                         int32_t* marg, int8_t* cls, float* logits, float* pooled_q,
-                        float* pooled_k, double* ws_qpool, double* ws_kpool_t,
-                        double* ws_kvar_t, float* key_var, hipStream_t stream,
+                        float* pooled_k, double* ws_qpool, double* ws_kpool,
+                        double* ws_kvar, float* key_var, hipStream_t stream,
                         const double* block_dev, const Fp8Out* f8, uint64_t* ws_keys,
                         bool k_pooled) {
-  if (k_pooled && (f8 || ws_kvar_t || block_dev)) return hipErrorInvalidValue;
+  // the states pass writes pooled K in the split selection's row layout
+  if (k_pooled && (f8 || ws_kvar || block_dev || !ws_keys)) return hipErrorInvalidValue;
   const int nwhich = k_pooled ? 1 : 2;
+  const int k_rows = ws_keys != nullptr;
   if (g.dtype == 1) {
     if (g.D == 128)
-      launch_pool_t<uint16_t, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8, nwhich);
+      launch_pool_t<uint16_t, 128>(g, q, k, ws_qpool, ws_kpool, pooled_q, pooled_k, ws_kvar, key_var, stream, f8, nwhich, k_rows);
     else
-      launch_pool_t<uint16_t, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8, nwhich);
+      launch_pool_t<uint16_t, 64>(g, q, k, ws_qpool, ws_kpool, pooled_q, pooled_k, ws_kvar, key_var, stream, f8, nwhich, k_rows);
   } else {
     if (g.D == 128)
-      launch_pool_t<float, 128>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8, nwhich);
+      launch_pool_t<float, 128>(g, q, k, ws_qpool, ws_kpool, pooled_q, pooled_k, ws_kvar, key_var, stream, f8, nwhich, k_rows);
     else
-      launch_pool_t<float, 64>(g, q, k, ws_qpool, ws_kpool_t, pooled_q, pooled_k, ws_kvar_t, key_var, stream, f8, nwhich);
+      launch_pool_t<float, 64>(g, q, k, ws_qpool, ws_kpool, pooled_q, pooled_k, ws_kvar, key_var, stream, f8, nwhich, k_rows);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ws_kvar_t)
-    return launch_select<1>(g, ws_qpool, ws_kpool_t, ws_kvar_t, nullptr, crit, marg, cls, logits, stream,
+  if (ws_kvar)
+    return launch_select<1>(g, ws_qpool, ws_kpool, ws_kvar, nullptr, crit, marg, cls, logits, stream,
                              ws_keys);
   if (block_dev)
-    return launch_select<2>(g, ws_qpool, ws_kpool_t, nullptr, block_dev, crit, marg, cls, logits, stream,
+    return launch_select<2>(g, ws_qpool, ws_kpool, nullptr, block_dev, crit, marg, cls, logits, stream,
                              ws_keys);
-  return launch_select<0>(g, ws_qpool, ws_kpool_t, nullptr, nullptr, crit, marg, cls, logits, stream,
+  return launch_select<0>(g, ws_qpool, ws_kpool, nullptr, nullptr, crit, marg, cls, logits, stream,
                              ws_keys);
 }
 

@@ -25,9 +25,9 @@ struct Geometry {
 constexpr size_t kStaticScratchBytes = size_t(64) << 20;
 hipError_t static_scratch(void** ptr);
 
-// ws_kvar_t non-null: second-order routing score (block key variances pooled
+// ws_kvar non-null: second-order routing score (block key variances pooled
 // into it, and into key_var as float32 when that is non-null).  block_dev
-// non-null (and ws_kvar_t null): covariance-aware score, block_dev holding
+// non-null (and ws_kvar null): covariance-aware score, block_dev holding
 // the float64 deviation norms M_j [B*H][nkb].
 // f8 non-null (plain score only): the pooling pass also writes the E4M3
 // codes and scales of Q and K ([B,H,N,d] u8, [B,H,nb] float).
@@ -39,9 +39,11 @@ struct Fp8Out {
 };
 // ws_keys non-null: the logits go through memory (route_key_bytes(g) of
 // workspace) and the selection runs as a kernel of its own; null: one fused
-// kernel keeps them in LDS.  k_pooled (plain score, no f8): ws_kpool_t
-// already holds the pooled keys (launch_states with kpool_t), so only Q is
-// pooled.
+// kernel keeps them in LDS.  ws_kpool (and ws_kvar) hold pooled K (and the
+// key variances) as rows [B*H][nkb][d] on the split path, transposed
+// [B*H][d][nkb] for the fused kernel.  k_pooled (plain score, no f8, split
+// path): ws_kpool already holds the pooled keys (launch_states with kpool),
+// so only Q is pooled.
 constexpr size_t kRouteKeyBytes = size_t(512) << 20;   // keys of one pass over heads, at most
 inline int route_key_nkbp(const Geometry& g) { return (g.nkb + 63) / 64 * 64; }
 // heads whose keys one pass holds (all, or as many as fit kRouteKeyBytes)
@@ -56,20 +58,20 @@ inline size_t route_key_bytes(const Geometry& g) {
 }
 hipError_t launch_route(const Geometry& g, const void* q, const void* k, int32_t* crit,
                         int32_t* marg, int8_t* cls, float* logits, float* pooled_q,
-                        float* pooled_k, double* ws_qpool, double* ws_kpool_t,
-                        double* ws_kvar_t, float* key_var, hipStream_t stream,
+                        float* pooled_k, double* ws_qpool, double* ws_kpool,
+                        double* ws_kvar, float* key_var, hipStream_t stream,
                         const double* block_dev = nullptr, const Fp8Out* f8 = nullptr,
                         uint64_t* ws_keys = nullptr, bool k_pooled = false);
 
 // exp_map: phi(k) = exp(k) elementwise instead of the softmax over features.
 // v8 non-null (softmax map only): also the E4M3 codes and scales of V.
-// kpool_t non-null (bf16, softmax map, no v8): also the pooled key rows of
-// the router, float64 transposed [B*H][d][nkb] as the pooling pass writes
-// them (and float32 [B,H,nkb,d] into kout when non-null).
+// kpool non-null (bf16, softmax map, no v8): also the pooled key rows of
+// the router, float64 [B*H][nkb][d] as the pooling pass writes them for the
+// split selection (and float32 [B,H,nkb,d] into kout when non-null).
 hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16_t* h_states,
                          float* z_states, bool exp_map, hipStream_t stream,
                          uint8_t* v8 = nullptr, float* v_scale = nullptr,
-                         double* kpool_t = nullptr, float* kout = nullptr);
+                         double* kpool = nullptr, float* kout = nullptr);
 
 // Marginal-state sums S_i = sum_{j in M_i} H_j (bf16, [B,H,nq,d,d], value-major
 // like the states) and sigma_i = sum_{j in M_i} z_j (float, [B,H,nq,d]); bits

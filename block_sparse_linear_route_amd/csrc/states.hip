@@ -31,8 +31,9 @@ namespace {
 // stand-alone quantiser), from the V rows already in registers.
 // POOLK (bf16 inputs): also the block's pooled key row for the router
 // ([SLA2 technical summary, section 2.B]), the float64 mean of the valid
-// keys, into the transposed pooled-K rows the routing kernels read (and
-// float32 into kout when non-null), so routing needs no second pass over K.
+// keys, into the pooled-K rows [B*H][nkb][d] the split routing path reads
+// (and float32 into kout when non-null), so routing needs no second pass
+// over K.
 // The sum runs in the routing pooling kernel's order (rows r, r + RG, ...
 // per row group r, then the row groups in order), so the means are that
 // kernel's bit for bit.
@@ -41,7 +42,7 @@ __global__ void __launch_bounds__(kThreads)
 states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
               uint16_t* __restrict__ h_out, float* __restrict__ z_out,
               uint8_t* __restrict__ v8 = nullptr, float* __restrict__ v_scale = nullptr,
-              double* __restrict__ kpool_t = nullptr, float* __restrict__ kout = nullptr) {
+              double* __restrict__ kpool = nullptr, float* __restrict__ kout = nullptr) {
   constexpr int TS = kBlock + 8;        // token stride of the transposed tiles
   constexpr int HS = D + 8;             // row stride of the staged (value-major) output tile
   constexpr int CW = D / 4;             // features per thread (4 threads per token)
@@ -111,7 +112,7 @@ states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
 #pragma unroll
       for (int rg = 0; rg < PRG; ++rg) sum += gsum[rg * D + t];
       const double m = sum / static_cast<double>(nj);
-      kpool_t[(static_cast<int64_t>(bh) * D + t) * g.nkb + j] = m;
+      kpool[(static_cast<int64_t>(bh) * g.nkb + j) * D + t] = m;
       if (kout) kout[(static_cast<int64_t>(bh) * g.nkb + j) * D + t] = static_cast<float>(m);
     }
     __syncthreads();   // the rows are read before the operand tiles reuse smem
@@ -224,14 +225,14 @@ states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
 
 template <typename T, int D>
 void launch_states_t(const Geometry& g, const void* k, const void* v, uint16_t* hs, float* zs,
-                     bool exp_map, hipStream_t stream, uint8_t* v8, float* vs, double* kpool_t,
+                     bool exp_map, hipStream_t stream, uint8_t* v8, float* vs, double* kpool,
                      float* kout) {
   dim3 grid(g.nkb, g.B * g.H);
   if constexpr (sizeof(T) == 2) {
-    if (kpool_t) {
+    if (kpool) {
       hipLaunchKernelGGL((states_kernel<T, D, false, false, true>), grid, dim3(kThreads), 0, stream,
                          static_cast<const T*>(k), static_cast<const T*>(v), g, hs, zs, nullptr,
-                         nullptr, kpool_t, kout);
+                         nullptr, kpool, kout);
       return;
     }
   }
@@ -250,11 +251,11 @@ void launch_states_t(const Geometry& g, const void* k, const void* v, uint16_t* 
 
 hipError_t launch_states(const Geometry& g, const void* k, const void* v, uint16_t* h_states,
                          float* z_states, bool exp_map, hipStream_t stream, uint8_t* v8,
-                         float* v_scale, double* kpool_t, float* kout) {
-  if (kpool_t && (g.dtype != 1 || exp_map || v8)) return hipErrorInvalidValue;
+                         float* v_scale, double* kpool, float* kout) {
+  if (kpool && (g.dtype != 1 || exp_map || v8)) return hipErrorInvalidValue;
   if (g.dtype == 1) {
-    if (g.D == 128) launch_states_t<uint16_t, 128>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale, kpool_t, kout);
-    else launch_states_t<uint16_t, 64>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale, kpool_t, kout);
+    if (g.D == 128) launch_states_t<uint16_t, 128>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale, kpool, kout);
+    else launch_states_t<uint16_t, 64>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale, kpool, kout);
   } else {
     if (g.D == 128) launch_states_t<float, 128>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale, nullptr, nullptr);
     else launch_states_t<float, 64>(g, k, v, h_states, z_states, exp_map, stream, v8, v_scale, nullptr, nullptr);
