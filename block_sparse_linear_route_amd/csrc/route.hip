@@ -300,37 +300,48 @@ __device__ __forceinline__ void select_row(const uint64_t* rk, int nkb, int lane
     hi = lo - 1;
   }
 
-  // classes (equal keys ranked by ascending j) and compaction
+  // classes (equal keys ranked by ascending j) and compaction.  A cut left
+  // open when the bits ran out sits among equal keys, which need their tie
+  // ranks; a cut found as a single key (or an empty target) does not.
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-  uint32_t eq_base[2] = {0u, 0u};
-  uint32_t out_base[2] = {0u, 0u};
+  auto compact = [&](auto ties_c) {
+    constexpr bool TIES = decltype(ties_c)::value;
+    uint32_t eq_base[2] = {0u, 0u};
+    uint32_t out_base[2] = {0u, 0u};
 #pragma unroll
-  for (int u = 0; u < KPL; ++u) {
-    if (64 * u >= nkb) break;
-    const int j = lane + 64 * u;
-    const uint64_t kv = kk[u];
-    bool in_w[2];
+    for (int u = 0; u < KPL; ++u) {
+      if (64 * u >= nkb) break;
+      const int j = lane + 64 * u;
+      const uint64_t kv = kk[u];
+      bool in_w[2];
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const uint64_t eqb = __ballot(kv == pref[w] && j < nkb);
-      const uint32_t tie_rank = eq_base[w] + static_cast<uint32_t>(__popcll(eqb & lt_mask));
-      in_w[w] = target[w] > 0 && (kv < pref[w] || (kv == pref[w] && tie_rank <= rem[w]));
-      eq_base[w] += static_cast<uint32_t>(__popcll(eqb));
+      for (int w = 0; w < 2; ++w) {
+        if constexpr (TIES) {
+          const uint64_t eqb = __ballot(kv == pref[w] && j < nkb);
+          const uint32_t tie_rank = eq_base[w] + static_cast<uint32_t>(__popcll(eqb & lt_mask));
+          in_w[w] = target[w] > 0 && (kv < pref[w] || (kv == pref[w] && tie_rank <= rem[w]));
+          eq_base[w] += static_cast<uint32_t>(__popcll(eqb));
+        } else {
+          in_w[w] = target[w] > 0 && kv <= pref[w];
+        }
+      }
+      const bool ok = j < nkb;
+      const int c = !ok ? 0 : (in_w[0] ? 2 : (in_w[1] ? 1 : 0));
+      const uint64_t b2 = __ballot(c == 2);
+      const uint64_t b1 = __ballot(c == 1);
+      const uint32_t p2 = out_base[0] + static_cast<uint32_t>(__popcll(b2 & lt_mask));
+      const uint32_t p1 = out_base[1] + static_cast<uint32_t>(__popcll(b1 & lt_mask));
+      out_base[0] += static_cast<uint32_t>(__popcll(b2));
+      out_base[1] += static_cast<uint32_t>(__popcll(b1));
+      if (ok) {
+        if (cls) cls[row * nkb + j] = static_cast<int8_t>(c);
+        if (c == 2 && p2 < static_cast<uint32_t>(k_crit)) crit[row * k_crit + p2] = j;
+        else if (c == 1 && p1 < static_cast<uint32_t>(k_marg)) marg[row * k_marg + p1] = j;
+      }
     }
-    const bool ok = j < nkb;
-    const int c = !ok ? 0 : (in_w[0] ? 2 : (in_w[1] ? 1 : 0));
-    const uint64_t b2 = __ballot(c == 2);
-    const uint64_t b1 = __ballot(c == 1);
-    const uint32_t p2 = out_base[0] + static_cast<uint32_t>(__popcll(b2 & lt_mask));
-    const uint32_t p1 = out_base[1] + static_cast<uint32_t>(__popcll(b1 & lt_mask));
-    out_base[0] += static_cast<uint32_t>(__popcll(b2));
-    out_base[1] += static_cast<uint32_t>(__popcll(b1));
-    if (ok) {
-      if (cls) cls[row * nkb + j] = static_cast<int8_t>(c);
-      if (c == 2 && p2 < static_cast<uint32_t>(k_crit)) crit[row * k_crit + p2] = j;
-      else if (c == 1 && p1 < static_cast<uint32_t>(k_marg)) marg[row * k_marg + p1] = j;
-    }
-  }
+  };
+  if (done[0] && done[1]) compact(std::false_type{});
+  else compact(std::true_type{});
 }
 
 // The fused routing kernel (plain score; the routing path of
