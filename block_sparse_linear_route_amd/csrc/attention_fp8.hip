@@ -95,7 +95,8 @@ attention_fp8_kernel(AttnFp8Args A) {
   const float* sig_dummy = reinterpret_cast<const float*>(smem_raw);         // (unused sigma slot)
 
   const Geometry& g = A.g;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform (scalar)
   const int qh = wave & 1, lh = wave >> 1;
   const int l32 = lane & 31, hh = lane >> 5;
 
@@ -150,8 +151,7 @@ attention_fp8_kernel(AttnFp8Args A) {
 
   // LDS: per half [K0 | K1 | V0 | V1], 8 KB each.  Wave qh of half lh loads
   // rows 32*qh + 8*u + lane/8 of the half's tiles; lane l writes chunk slot
-  // l%8 of its row, which holds global chunk (l%8) ^ swz8(row).  Rows past
-  // the end of a short last block repeat its last row (masked in S).
+  // l%8 of its row, which holds global chunk (l%8) ^ swz8(row).
   unsigned char* hbase = smem_raw + lh * HALF_BYTES;
   uint32_t toff[4];
 #pragma unroll
@@ -159,20 +159,17 @@ attention_fp8_kernel(AttnFp8Args A) {
     const int r = 32 * qh + 8 * u + (lane >> 3);
     toff[u] = static_cast<uint32_t>(r * D + 16 * ((lane & 7) ^ swz8(r)));
   }
-  auto issue_tile = [&](const uint8_t* base, int c, unsigned char* dst) {
+  // Tiles come through a range-checked buffer resource ending at the head's
+  // last token, so rows past the end of a short last block read as zeros
+  // (their keys are masked to -inf in S, so their P is 0).
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k8p, static_cast<uint32_t>(g.N) * D);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v8p, static_cast<uint32_t>(g.N) * D);
+  auto issue_tile = [&](bool is_k, int c, unsigned char* dst) {
     const int jb = crit_at(c);
-    const int nj = min(kBlock, g.N - kBlock * jb);
-    const uint8_t* tb = base + static_cast<int64_t>(kBlock * jb) * D;
+    const uint32_t soff = static_cast<uint32_t>(kBlock * jb) * D;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r0 = 32 * qh + 8 * u;
-      uint32_t off = toff[u];
-      if (nj < kBlock) {
-        const int r = r0 + (lane >> 3);
-        off = static_cast<uint32_t>((r < nj ? r : nj - 1) * D + 16 * ((lane & 7) ^ swz8(r)));
-      }
-      load_lds16(tb + off, dst + r0 * D);
-    }
+    for (int u = 0; u < 4; ++u)
+      buffer_load_lds16(is_k ? krs : vrs, dst + (32 * qh + 8 * u) * D, toff[u], soff);
   };
 
   // K^ operand reads: row 32*tt + l32, chunks 4*cc + 2*hh + {0, 1}
@@ -230,9 +227,9 @@ attention_fp8_kernel(AttnFp8Args A) {
   s_cur[0] = zero16();
   s_cur[1] = zero16();
   if (nh > 0) {
-    issue_tile(k8p, 0, hbase);
-    issue_tile(v8p, 0, hbase + 2 * TB);
-    if (nh > 1) issue_tile(k8p, 1, hbase + TB);
+    issue_tile(true, 0, hbase);
+    issue_tile(false, 0, hbase + 2 * TB);
+    if (nh > 1) issue_tile(true, 1, hbase + TB);
   }
   wait_vmem();
   __syncthreads();
@@ -241,12 +238,43 @@ attention_fp8_kernel(AttnFp8Args A) {
 
   for (int it = 0; it < nit; ++it) {
     const int cur = it & 1;
-    if (it + 2 < nh) issue_tile(k8p, it + 2, hbase + cur * TB);
-    if (it + 1 < nh) issue_tile(v8p, it + 1, hbase + 2 * TB + (cur ^ 1) * TB);
+    // V^T fragments of this step's block (in LDS since the last barrier):
+    // all 16 transposing reads in flight together, one wait, before the
+    // tile loads for the next blocks are issued
+    u32x2 vr[4 * DT];
+    {
+      const uint32_t vt_addr = lds_addr(hbase + 2 * TB + cur * TB);
+      asm volatile(
+          "ds_read_b64_tr_b8 %0, %16\n\t"
+          "ds_read_b64_tr_b8 %1, %16 offset:2048\n\t"
+          "ds_read_b64_tr_b8 %2, %16 offset:4096\n\t"
+          "ds_read_b64_tr_b8 %3, %16 offset:6144\n\t"
+          "ds_read_b64_tr_b8 %4, %17\n\t"
+          "ds_read_b64_tr_b8 %5, %17 offset:2048\n\t"
+          "ds_read_b64_tr_b8 %6, %17 offset:4096\n\t"
+          "ds_read_b64_tr_b8 %7, %17 offset:6144\n\t"
+          "ds_read_b64_tr_b8 %8, %18\n\t"
+          "ds_read_b64_tr_b8 %9, %18 offset:2048\n\t"
+          "ds_read_b64_tr_b8 %10, %18 offset:4096\n\t"
+          "ds_read_b64_tr_b8 %11, %18 offset:6144\n\t"
+          "ds_read_b64_tr_b8 %12, %19\n\t"
+          "ds_read_b64_tr_b8 %13, %19 offset:2048\n\t"
+          "ds_read_b64_tr_b8 %14, %19 offset:4096\n\t"
+          "ds_read_b64_tr_b8 %15, %19 offset:6144\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]),
+            "=&v"(vr[6]), "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]),
+            "=&v"(vr[12]), "=&v"(vr[13]), "=&v"(vr[14]), "=&v"(vr[15])
+          : "v"(vt_addr + vofs[0]), "v"(vt_addr + vofs[1]), "v"(vt_addr + vofs[2]),
+            "v"(vt_addr + vofs[3])
+          : "memory");
+    }
+    if (it + 2 < nh) issue_tile(true, it + 2, hbase + cur * TB);
+    if (it + 1 < nh) issue_tile(false, it + 1, hbase + 2 * TB + (cur ^ 1) * TB);
+    // S of the next block (from a stale but in-bounds buffer when this half
+    // has no next block; the result is then dropped)
     f32x16 s_next[2];
-    s_next[0] = zero16();
-    s_next[1] = zero16();
-    if (it + 1 < nh) qk(hbase + (cur ^ 1) * TB, s_next);
+    qk(hbase + (cur ^ 1) * TB, s_next);
 
     if (it < nh) {
       const int o = it - ebase;
@@ -314,19 +342,9 @@ attention_fp8_kernel(AttnFp8Args A) {
       const f32x16 lsum = mfma_fp8(ones8, pk, zero16(), scale_b);
       l_run = fmaf(lsum[0], 0.5f * iv, l_run);
 
-      const uint32_t vt_addr = lds_addr(hbase + 2 * TB + cur * TB);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        u32x2 a0, a1, a2, a3;
-        asm volatile(
-            "ds_read_b64_tr_b8 %0, %4\n\t"
-            "ds_read_b64_tr_b8 %1, %4 offset:2048\n\t"
-            "ds_read_b64_tr_b8 %2, %4 offset:4096\n\t"
-            "ds_read_b64_tr_b8 %3, %4 offset:6144\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
-            : "v"(vt_addr + vofs[dt])
-            : "memory");
+        const u32x2 a0 = vr[4 * dt], a1 = vr[4 * dt + 1], a2 = vr[4 * dt + 2], a3 = vr[4 * dt + 3];
         i32x8 vf;
         vf[0] = static_cast<int>(a0[0]); vf[1] = static_cast<int>(a0[1]);
         vf[2] = static_cast<int>(a1[0]); vf[3] = static_cast<int>(a1[1]);

@@ -48,7 +48,8 @@ pisa_stats_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g, 
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int nch = gridDim.x;
   const int b = bh / g.H, h = bh % g.H;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform (scalar)
   const int row = t >> 2, prt = t & 3;
   const int l32 = lane & 31, hh = lane >> 5;
   const int j0 = chunk * G, j1 = min(j0 + G, g.nkb);
@@ -387,7 +388,8 @@ pisa_first_order_f32_kernel(const T* __restrict__ k, const T* __restrict__ v, Ge
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int nch = gridDim.x;
   const int b = bh / g.H, h = bh % g.H;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform (scalar)
   const int a0 = (t / 16) * AW, c0 = (t % 16) * AW;
   const int j0 = chunk * G, j1 = min(j0 + G, g.nkb);
   const T* kh = k + b * g.sb + h * g.sh;
@@ -484,7 +486,8 @@ pisa_reduce_kernel(const float* __restrict__ part, int nch, int nkb, uint16_t* _
                    float* __restrict__ hbar_f32) {
   __shared__ f32x4 red[4][64];
   const int bh = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
   const int e = 256 * blockIdx.x + 4 * lane;
   const float* src = part + static_cast<int64_t>(bh) * nch * D * D + e;
   f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};

@@ -377,7 +377,8 @@ select_kernel(Geometry g, int nkbp, const double* __restrict__ qpool,
   const int logical = xcd_remap(blockIdx.x, ngroups * g.B * g.H);
   const int bh = logical / ngroups;
   const int i0 = (logical % ngroups) * R;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform (scalar)
 
   const double* qrow[R];
 #pragma unroll
@@ -526,7 +527,8 @@ logits_kernel(Geometry g, int nkbp, int bh0, int nbh, const double* __restrict__
   const int bhl = logical / (tc_n * tr_n);
   const int bh = bh0 + bhl;
   const int i0 = rt * kLT, j0 = ct * kLT;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform (scalar)
   const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;   // this wave's quarter
   const int l16 = lane & 15, kslot = lane >> 4;
 
@@ -638,7 +640,8 @@ select_rows_kernel(Geometry g, int nkbp, int bh0, int nbh, const uint64_t* __res
                    int32_t* __restrict__ crit, int32_t* __restrict__ marg,
                    int8_t* __restrict__ cls) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[4][kHistWords];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform (scalar)
   const int r = blockIdx.x * 4 + wave;
   if (r >= nbh * g.nq) return;
   const int bhl = r / g.nq, i = r % g.nq;

@@ -59,7 +59,8 @@ states_kernel(const T* __restrict__ k, const T* __restrict__ v, Geometry g,
 
   const int j = blockIdx.x, bh = blockIdx.y;
   const int b = bh / g.H, h = bh % g.H;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform (scalar)
   const int row = t >> 2, part = t & 3;
   const int nj = min(kBlock, g.N - j * kBlock);
   const bool valid = row < nj;
