@@ -84,15 +84,19 @@ attention_fp8_kernel(AttnFp8Args A) {
   constexpr int NS = D / 16;
   constexpr int DT = D / 32;
   constexpr int TB = kBlock * D;               // bytes per fp8 tile
-  constexpr int HALF_BYTES = 4 * TB;           // K0, K1, V0, V1 of one list half
-  constexpr int LOOP_BYTES = 2 * HALF_BYTES;
+  // LDS: the K buffers of both list halves [0, 4 TB), then their V buffers
+  // [4 TB, 8 TB); the epilogue's merge buffers start at the V buffers and
+  // sigma_i sits past them.
+  constexpr int VREG = 4 * TB;
   constexpr int EPI_BYTES = epilogue_smem_bytes<D>();
-  constexpr int SMEM_BYTES = (LOOP_BYTES > EPI_BYTES ? LOOP_BYTES : EPI_BYTES);
+  constexpr int SIG_OFF = VREG + EPI_BYTES;
+  constexpr int SMEM_BYTES = SIG_OFF + D * 4;
+  static_assert(SIG_OFF >= 8 * TB, "sigma_i must lie past the ring");
   constexpr float kLazy = 8.0f;
   constexpr float kLog2Max = 8.807354922057604f;   // log2(448)
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM_BYTES];
-  const uint16_t* smem_u16 = reinterpret_cast<const uint16_t*>(smem_raw);   // (unused S^T slot)
-  const float* sig_dummy = reinterpret_cast<const float*>(smem_raw);         // (unused sigma slot)
+  const uint16_t* smem_u16 = reinterpret_cast<const uint16_t*>(smem_raw);
+  float* sig_lds = reinterpret_cast<float*>(smem_raw + SIG_OFF);
 
   const Geometry& g = A.g;
   const int t = threadIdx.x, lane = t & 63;
@@ -149,10 +153,12 @@ attention_fp8_kernel(AttnFp8Args A) {
     return o < 64 ? __builtin_amdgcn_readlane(ej0, o) : __builtin_amdgcn_readlane(ej1, o - 64);
   };
 
-  // LDS: per half [K0 | K1 | V0 | V1], 8 KB each.  Wave qh of half lh loads
-  // rows 32*qh + 8*u + lane/8 of the half's tiles; lane l writes chunk slot
-  // l%8 of its row, which holds global chunk (l%8) ^ swz8(row).
-  unsigned char* hbase = smem_raw + lh * HALF_BYTES;
+  // LDS ring of a half: K buffers K0, K1 at kbase, V buffers V0, V1 at
+  // vbase, 8 KB each.  Wave qh of half lh loads rows 32*qh + 8*u + lane/8 of
+  // the half's tiles; lane l writes chunk slot l%8 of its row, which holds
+  // global chunk (l%8) ^ swz8(row).
+  unsigned char* kbase = smem_raw + lh * 2 * TB;
+  unsigned char* vbase = smem_raw + VREG + lh * 2 * TB;
   uint32_t toff[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -223,27 +229,89 @@ attention_fp8_kernel(AttnFp8Args A) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = zero16();
 
+  // Epilogue operands prefetched into LDS while the last blocks compute, so
+  // the epilogue waits on no HBM load: sigma_i at the start; the value-major
+  // S_i^T half this list half finalises (rows 64*lh .. +63, a swizzled
+  // 64 x D bf16 tile) into the half's two K buffers as each falls free
+  // (K[c] takes rows 32c .. +31; K[(nh-2)&1] is free from step nh-2 on and
+  // K[(nh-1)&1] from step nh-1); bf16 Q rows 32*lh .. +31 into the half's
+  // V buffer that is free in its last step (V[(nh-2)&1]), with a 16-byte
+  // chunk swizzle row & 15.
+  const bool has_lin = g.k_marg > 0;
+  const __amdgpu_buffer_rsrc_t srs =
+      make_rsrc(A.s_sum + (static_cast<int64_t>(bh) * g.nq + i) * D * D, D * D * 2);
+  const uint16_t* __restrict__ qblk = A.q + hoff + static_cast<int64_t>(kBlock * i) * g.sn;
+  const __amdgpu_buffer_rsrc_t qrs =
+      make_rsrc(qblk, static_cast<uint32_t>(((n_i - 1) * g.sn + D) * 2));
+  if (has_lin && wave == 0 && lane < D / 4) {
+    const __amdgpu_buffer_rsrc_t sgr =
+        make_rsrc(A.sigma_sum + (static_cast<int64_t>(bh) * g.nq + i) * D, D * 4);
+    buffer_load_lds16(sgr, sig_lds, 16u * lane, 0u);
+  }
+  // Lane l of a 1 KB load covers row l/16 (of 4) at chunk slot l%16.  For
+  // S_i^T row r = 4m + l/16 the swizzle swz(r) is 4(l/16) + m%4, so the slot
+  // holds global chunk (l%16) ^ 4(l/16) ^ (m%4): one lane constant, and the
+  // row base goes into the scalar offset.  Q rows use the swizzle row & 15,
+  // i.e. chunk (l%16) ^ (l/16) ^ 4(m%4).
+  const int lr16 = lane >> 4;
+  const uint32_t s_lane = static_cast<uint32_t>(lr16 * D * 2 + 16 * ((lane & 15) ^ (4 * lr16)));
+  const uint32_t q_row = static_cast<uint32_t>(lr16 * g.sn * 2);
+  const int q_chunk = (lane & 15) ^ lr16;
+  auto issue_s_rows = [&](int piece) {
+    unsigned char* dst = kbase + piece * TB;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r0 = 32 * piece + 16 * qh + 4 * u;              // first row of this load
+      buffer_load_lds16(srs, dst + (16 * qh + 4 * u) * D * 2, s_lane ^ (16u * u),
+                        static_cast<uint32_t>((64 * lh + r0) * D * 2));
+    }
+  };
+  // the V buffer of half h that holds Q rows 32h .. +31 (free in its last step)
+  auto q_buf = [&](int nhh) { return nhh >= 1 ? (((nhh - 1) & 1) ^ 1) : 1; };
+  auto issue_q_rows = [&]() {
+    unsigned char* dst = vbase + q_buf(nh) * TB;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int rb0 = 16 * qh + 4 * u;                           // first buffer row of this load
+      buffer_load_lds16(qrs, dst + rb0 * D * 2, q_row + 16u * static_cast<uint32_t>(q_chunk ^ (4 * u)),
+                        static_cast<uint32_t>((32 * lh + rb0) * g.sn * 2));
+    }
+  };
+  auto issue_tail = [&](int it) {
+    if (nh == 0) {
+      if (it == 0) { issue_s_rows(0); issue_s_rows(1); issue_q_rows(); }
+      return;
+    }
+    if (it == nh - 2) issue_s_rows(it & 1);
+    if (it == nh - 1) {
+      issue_s_rows(it & 1);
+      if (nh == 1) issue_s_rows(1);
+      issue_q_rows();
+    }
+  };
+
   f32x16 s_cur[2];
   s_cur[0] = zero16();
   s_cur[1] = zero16();
   if (nh > 0) {
-    issue_tile(true, 0, hbase);
-    issue_tile(false, 0, hbase + 2 * TB);
-    if (nh > 1) issue_tile(true, 1, hbase + TB);
+    issue_tile(true, 0, kbase);
+    issue_tile(false, 0, vbase);
+    if (nh > 1) issue_tile(true, 1, kbase + TB);
   }
   wait_vmem();
   __syncthreads();
-  if (nh > 0) qk(hbase, s_cur);
+  if (nh > 0) qk(kbase, s_cur);
   __syncthreads();   // every wave has read K0 before the first step refills it
 
   for (int it = 0; it < nit; ++it) {
     const int cur = it & 1;
+    if (has_lin) issue_tail(it);   // into buffers that fell free at the last barrier
     // V^T fragments of this step's block (in LDS since the last barrier):
     // all 16 transposing reads in flight together, one wait, before the
     // tile loads for the next blocks are issued
     u32x2 vr[4 * DT];
     {
-      const uint32_t vt_addr = lds_addr(hbase + 2 * TB + cur * TB);
+      const uint32_t vt_addr = lds_addr(vbase + cur * TB);
       asm volatile(
           "ds_read_b64_tr_b8 %0, %16\n\t"
           "ds_read_b64_tr_b8 %1, %16 offset:2048\n\t"
@@ -269,12 +337,12 @@ attention_fp8_kernel(AttnFp8Args A) {
             "v"(vt_addr + vofs[3])
           : "memory");
     }
-    if (it + 2 < nh) issue_tile(true, it + 2, hbase + cur * TB);
-    if (it + 1 < nh) issue_tile(false, it + 1, hbase + 2 * TB + (cur ^ 1) * TB);
+    if (it + 2 < nh) issue_tile(true, it + 2, kbase + cur * TB);
+    if (it + 1 < nh) issue_tile(false, it + 1, vbase + (cur ^ 1) * TB);
     // S of the next block (from a stale but in-bounds buffer when this half
     // has no next block; the result is then dropped)
     f32x16 s_next[2];
-    qk(hbase + (cur ^ 1) * TB, s_next);
+    qk(kbase + (cur ^ 1) * TB, s_next);
 
     if (it < nh) {
       const int o = it - ebase;
@@ -365,16 +433,30 @@ attention_fp8_kernel(AttnFp8Args A) {
     __syncthreads();
   }
 
-  // bf16 Q fragments for phi(Q) in the linear branch
+  // no critical block (no loop): the epilogue operands go in now
+  if (nit == 0) {
+    if (has_lin) issue_tail(0);
+    wait_vmem();
+    __syncthreads();
+  }
+  // bf16 Q fragments for phi(Q) in the linear branch: query 32*qh + l32 from
+  // the V buffer of half qh that took Q rows 32*qh .. +31
   bf16x8 qf[NS];
-  const uint16_t* __restrict__ qp = A.q + hoff;
+  if (has_lin) {
+    const int nhq = (kc - qh + 1) / 2;
+    const uint16_t* qsrc = reinterpret_cast<const uint16_t*>(smem_raw + VREG + qh * 2 * TB + q_buf(nhq) * TB);
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    qf[s] = load8(qp + static_cast<int64_t>(kBlock * i + qr) * g.sn + 16 * s + 8 * hh);
-  __syncthreads();
-  attention_finish<uint16_t, D, false, false, false, false, LSE>(
-      smem_raw, smem_u16, sig_dummy, false, g, bh, h, i, n_i, qrow, hoff, A.s_sum, A.sigma_sum,
-      A.alpha, A.o, A.o_sparse, A.o_linear, oacc, m_run, l_run, 1.0f, qf, [](int) {}, 0.0f, A.lse);
+    for (int s = 0; s < NS; ++s)
+      qf[s] = *reinterpret_cast<const bf16x8*>(qsrc + l32 * D + 8 * ((2 * s + hh) ^ (l32 & 15)));
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = bf16x8{};
+  }
+  __syncthreads();   // every wave holds its Q before the merge buffers overwrite the V buffers
+  attention_finish<uint16_t, D, true, false, false, false, LSE>(
+      smem_raw + VREG, smem_u16 + lh * (2 * TB / 2), sig_lds, true, g, bh, h, i, n_i, qrow, hoff,
+      A.s_sum, A.sigma_sum, A.alpha, A.o, A.o_sparse, A.o_linear, oacc, m_run, l_run, 1.0f, qf,
+      [](int) {}, 0.0f, A.lse);
 }
 
 }  // namespace
