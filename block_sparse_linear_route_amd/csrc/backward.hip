@@ -683,7 +683,9 @@ bwd_kv_kernel(BwdArgs A) {
   }
   auto issue = [&](auto xc, int it) {
     constexpr int X = decltype(xc)::value;
-    const int qi = qlist[it];
+    // the list entry is the same in every lane: in a scalar register the
+    // buffer loads take it as their scalar offset directly
+    const int qi = __builtin_amdgcn_readfirstlane(qlist[it]);
     const uint32_t soff = static_cast<uint32_t>(kBlock * qi) * rowb;
     uint16_t* qd = (X ? q1 : q0) + 16 * wave * D;
     uint16_t* gd = (X ? g1 : g0) + 16 * wave * D;
@@ -734,7 +736,7 @@ bwd_kv_kernel(BwdArgs A) {
     const uint16_t* qt = X ? q1 : q0;
     const uint16_t* gt = X ? g1 : g0;
     const float* stx = X ? &st1[0][0] : &st0[0][0];
-    const int n_q = min(kBlock, g.N - kBlock * qlist[it]);
+    const int n_q = min(kBlock, g.N - kBlock * __builtin_amdgcn_readfirstlane(qlist[it]));
     // row statistics of the 16 query rows in this lane's registers
     float lse_r[16], d_r[16];
 #pragma unroll
