@@ -417,6 +417,27 @@ def test_forward_fp8_parity_shapes(N, kc, km, H, seed):
     _forward_check(w, n_sample=None if nb <= 40 else 12, fp8=True, fp8_inputs=True)
 
 
+@pytest.mark.parametrize("kc,km", [(3, 4), (6, 9)])
+def test_forward_fp8_strided_layout(kc, km):
+    # [B, N, H, d] storage viewed as [B, H, N, d]: the fp8 kernel reads the
+    # bf16 Q rows of the linear branch (prefetched into LDS during the last
+    # critical blocks) and writes O with the row stride; two batches, so the
+    # head offsets take the batch stride too
+    w = make_custom(2, 3, 900, 128, seed=25 + kc, k_crit=kc, k_marg=km)
+    s = _s()
+    q, k, v = _gpu(w)
+    qs = w.q.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+    assert qs.stride()[2] == 3 * 128
+    r = s.route(q, k, kc, km)
+    Hs, zs = s.linear_states(k, v)
+    (q8, qsc), (k8, ksc), (v8, vsc) = (s.quantize_fp8(x) for x in (q, k, v))
+    o1 = s.forward_fp8(qs, q8, qsc, k8, ksc, v8, vsc, r["crit_idx"], r["marg_idx"], Hs, zs, w.alpha)
+    o2 = s.forward_fp8(q, q8, qsc, k8, ksc, v8, vsc, r["crit_idx"], r["marg_idx"], Hs, zs, w.alpha)
+    torch.cuda.synchronize()
+    assert o1.stride() == qs.stride()
+    assert torch.equal(o1.contiguous(), o2)
+
+
 def test_forward_fp8_close_to_bf16_forward():
     """Both sparse branches see the same routing; their outputs differ by the
     quantisation error only."""
