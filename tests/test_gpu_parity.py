@@ -406,6 +406,8 @@ def test_forward_fp8_parity(name, heads, n_sample):
     (1000, 0, 16, 2, 41),        # no critical block: linear branch only
     (777, 5, 3, 1, 42),          # ragged tail block
     (64, 1, 0, 1, 43),           # one block, one list half idle
+    (1500, 2, 5, 2, 48),         # one block per half: both epilogue prefetch halves in step 0
+    (1500, 4, 6, 1, 49),         # two blocks per half
     (4095, 1, 20, 2, 44),
     (4096, 7, 9, 1, 45),         # odd critical count: halves of 4 and 3
     (300 * 64 + 17, 150, 10, 1, 46),   # half lists of 75 entries: register refill
